@@ -1,0 +1,195 @@
+"""ctypes binding of ``libgdn.so`` (the C ABI in ``include/gdn.h``).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every step of the computation runs in the library's kernels.  There is
+no fallback -- if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+STATUS = {0: "GDN_OK", 1: "GDN_E_INVALID", 2: "GDN_E_UNSUPPORTED", 3: "GDN_E_WORKSPACE", 4: "GDN_E_HIP"}
+
+_vp = ctypes.c_void_p
+
+
+class CommonArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("g", _vp), ("beta", _vp), ("h0", _vp),
+                ("scale", ctypes.c_float),
+                ("cu_seqlens", _vp), ("cu_seqlens_host", _vp),
+                ("num_seqs", ctypes.c_int32), ("cp_mode", ctypes.c_int32),
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("a", CommonArgs), ("o", _vp), ("hT", _vp)]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("a", CommonArgs), ("do_", _vp), ("dhT", _vp), ("dq", _vp), ("dk", _vp),
+                ("dv", _vp), ("dbeta", _vp), ("dg", _vp), ("dh0", _vp)]
+
+
+class GDNError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib():
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise GDNError(f"{LIB_PATH} is missing: build it with gated_deltanet_chunked_delta_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        L.gdn_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdArgs)]
+        L.gdn_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+        L.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
+        L.gdn_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+        L.gdn_chunk_fwd.argtypes = [ctypes.POINTER(FwdArgs), _vp]
+        L.gdn_chunk_fwd.restype = ctypes.c_int
+        L.gdn_chunk_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
+        L.gdn_chunk_bwd.restype = ctypes.c_int
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = lib().gdn_last_error().decode()
+        raise GDNError(f"{STATUS.get(status, status)}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise GDNError(f"unsupported dtype {t.dtype}")
+
+
+def _contig(name, t, dtype=None, device=None):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise GDNError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise GDNError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise GDNError(f"{name} must be on {device}")
+    return t
+
+
+def _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode):
+    dev = q.device
+    dt = q.dtype
+    _contig("q", q, dt, dev)
+    _contig("k", k, dt, dev)
+    _contig("v", v, dt, dev)
+    _contig("beta", beta, dt, dev)
+    _contig("g", g, torch.float32, dev)
+    _contig("h0", h0, torch.float32, dev)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if tuple(k.shape) != (B, T, H, Dk) or tuple(v.shape[:3]) != (B, T, H):
+        raise GDNError("q, k, v shapes disagree")
+    if tuple(g.shape) != (B, T, H) or tuple(beta.shape) != (B, T, H):
+        raise GDNError("g and beta must be [B, T, H]")
+    a = CommonArgs()
+    a.dtype = _dtype_code(q)
+    a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, Dk, Dv
+    a.q, a.k, a.v, a.g, a.beta, a.h0 = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0)
+    a.scale = float(scale)
+    keep = []
+    if cu_seqlens is not None:
+        _contig("cu_seqlens", cu_seqlens, torch.int32, dev)
+        if cu_seqlens_host is None:
+            cu_seqlens_host = cu_seqlens.cpu()  # synchronises; pass the host copy to avoid it
+        host = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+        keep.append(host)
+        a.cu_seqlens = cu_seqlens.data_ptr()
+        a.cu_seqlens_host = host.data_ptr()
+        a.num_seqs = host.numel() - 1
+    else:
+        a.num_seqs = B
+    a.cp_mode = int(cp_mode)
+    return a, keep
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_seqlens_host=None,
+                  output_final_state: bool = True, cp_mode: int = 0):
+    """Forward pass.  Returns (o, hT) with hT None unless output_final_state."""
+    a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode)
+    L = lib()
+    o = torch.empty(q.shape[:3] + (a.Dv,), dtype=q.dtype, device=q.device)
+    hT = (torch.empty((a.num_seqs, a.H, a.Dk, a.Dv), dtype=torch.float32, device=q.device)
+          if output_final_state else None)
+    args = FwdArgs()
+    args.a = a
+    args.o, args.hT = _ptr(o), _ptr(hT)
+    nbytes = L.gdn_chunk_fwd_workspace_size(ctypes.byref(args))
+    if nbytes == 0:
+        _check(1)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    args.a.workspace, args.a.workspace_bytes = ws.data_ptr(), nbytes
+    _check(L.gdn_chunk_fwd(ctypes.byref(args), _vp(_stream(q.device))))
+    del keep
+    return o, hT
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, scale: float, do, h0=None, dhT=None, cu_seqlens=None,
+                  cu_seqlens_host=None, cp_mode: int = 0, need_dh0: bool = True):
+    """Backward pass.  Returns (dq, dk, dv, dg, dbeta, dh0) with dh0 None unless need_dh0."""
+    a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode)
+    _contig("do", do, q.dtype, q.device)
+    _contig("dhT", dhT, torch.float32, q.device)
+    L = lib()
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dbeta = torch.empty_like(beta)
+    dg = torch.empty_like(g)
+    dh0 = (torch.empty((a.num_seqs, a.H, a.Dk, a.Dv), dtype=torch.float32, device=q.device)
+           if need_dh0 else None)
+    args = BwdArgs()
+    args.a = a
+    args.do_, args.dhT = _ptr(do), _ptr(dhT)
+    args.dq, args.dk, args.dv, args.dbeta, args.dg, args.dh0 = map(_ptr, (dq, dk, dv, dbeta, dg, dh0))
+    nbytes = L.gdn_chunk_bwd_workspace_size(ctypes.byref(args))
+    if nbytes == 0:
+        _check(1)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    args.a.workspace, args.a.workspace_bytes = ws.data_ptr(), nbytes
+    _check(L.gdn_chunk_bwd(ctypes.byref(args), _vp(_stream(q.device))))
+    del keep
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+def exported_symbols(header: Optional[str] = None) -> Sequence[str]:
+    """Function names declared in include/gdn.h."""
+    import re
+    header = header or os.path.join(os.path.dirname(HERE), "include", "gdn.h")
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))

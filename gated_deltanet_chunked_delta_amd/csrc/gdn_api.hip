@@ -1,0 +1,298 @@
+// gdn_api.hip -- host side of the C ABI declared in include/gdn.h:
+// argument validation, the segment plan's sizes, workspace layout and the
+// launch sequence on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+constexpr int CHUNK = gdn::CH;
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Compute units of the current device, cached per device.
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+struct Plan {
+  int N = 0;
+  int nchunk = 0;       // total chunks over all sequences
+  int nseg = 0;         // total segments over all sequences
+  int segc = 1;         // chunks per segment
+  bool cp = false;      // some sequence has more than one segment
+  // workspace offsets (bytes)
+  size_t o_chunk_first = 0, o_seg_first = 0, o_segs = 0, o_chunk_tab = 0;
+  size_t o_bstate = 0, o_lam = 0, o_bstate2 = 0, o_lam2 = 0, o_hs = 0, o_dhs = 0, total = 0;
+};
+
+bool supported(int dtype, int Dk, int Dv) {
+  if (dtype == GDN_BF16) return (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);
+  if (dtype == GDN_F32) return Dk == 64 && Dv == 64;
+  return false;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+gdn_status check_common(const gdn_common_args& a) {
+  if (a.dtype != GDN_F32 && a.dtype != GDN_BF16) return fail(GDN_E_UNSUPPORTED, "unknown dtype %d", a.dtype);
+  if (a.B < 1 || a.T < 0 || a.H < 1 || a.Dk < 1 || a.Dv < 1)
+    return fail(GDN_E_INVALID, "bad sizes B=%d T=%d H=%d Dk=%d Dv=%d", a.B, a.T, a.H, a.Dk, a.Dv);
+  if (!supported(a.dtype, a.Dk, a.Dv))
+    return fail(GDN_E_UNSUPPORTED, "unsupported combination dtype=%d Dk=%d Dv=%d", a.dtype, a.Dk, a.Dv);
+  const long long tokens = (long long)a.B * a.T;
+  if (tokens * a.H * std::max(a.Dk, a.Dv) >= (1LL << 40)) return fail(GDN_E_INVALID, "problem too large");
+  if (tokens > 0) {
+    if (!a.q || !a.k || !a.v || !a.g || !a.beta) return fail(GDN_E_INVALID, "null input pointer");
+    if (!aligned(a.q, 16) || !aligned(a.k, 16) || !aligned(a.v, 16))
+      return fail(GDN_E_INVALID, "q, k and v must be 16-byte aligned");
+    if (!aligned(a.g, 4) || !aligned(a.beta, a.dtype == GDN_F32 ? 4 : 2))
+      return fail(GDN_E_INVALID, "g / beta misaligned");
+  }
+  if (!aligned(a.h0, 4)) return fail(GDN_E_INVALID, "h0 misaligned");
+  if (a.cu_seqlens) {
+    if (a.B != 1) return fail(GDN_E_INVALID, "cu_seqlens requires B == 1 (got %d)", a.B);
+    if (!a.cu_seqlens_host) return fail(GDN_E_INVALID, "cu_seqlens needs its host copy cu_seqlens_host");
+    if (a.num_seqs < 1) return fail(GDN_E_INVALID, "num_seqs must be >= 1 with cu_seqlens");
+    const int32_t* cu = a.cu_seqlens_host;
+    if (cu[0] != 0) return fail(GDN_E_INVALID, "cu_seqlens[0] must be 0");
+    for (int n = 0; n < a.num_seqs; ++n)
+      if (cu[n + 1] < cu[n]) return fail(GDN_E_INVALID, "cu_seqlens must be non-decreasing (index %d)", n);
+    if (cu[a.num_seqs] != a.T) return fail(GDN_E_INVALID, "cu_seqlens[N] = %d != T = %d", cu[a.num_seqs], a.T);
+  } else if (a.cu_seqlens_host) {
+    return fail(GDN_E_INVALID, "cu_seqlens_host given without cu_seqlens");
+  } else if (a.num_seqs != a.B) {
+    return fail(GDN_E_INVALID, "num_seqs (%d) must equal B (%d) without cu_seqlens", a.num_seqs, a.B);
+  }
+  if (a.cp_mode < -1) return fail(GDN_E_INVALID, "cp_mode must be -1, 0 or a positive chunk count");
+  return GDN_OK;
+}
+
+// Segment length, totals and workspace layout.  `bwd` adds the backward's arrays.
+Plan make_plan(const gdn_common_args& a, bool bwd, int cus) {
+  Plan p;
+  p.N = a.num_seqs;
+  std::vector<int> nch(p.N);
+  long long total = 0;
+  int maxc = 0;
+  for (int n = 0; n < p.N; ++n) {
+    const int len = a.cu_seqlens ? a.cu_seqlens_host[n + 1] - a.cu_seqlens_host[n] : a.T;
+    nch[n] = (len + CHUNK - 1) / CHUNK;
+    total += nch[n];
+    maxc = std::max(maxc, nch[n]);
+  }
+  p.nchunk = (int)total;
+  if (a.cp_mode == -1) {
+    p.segc = std::max(1, maxc);
+  } else if (a.cp_mode > 0) {
+    p.segc = a.cp_mode;
+  } else {
+    // Automatic: aim for about one workgroup per compute unit, but never cut
+    // segments shorter than 8 chunks -- the boundary correction costs a few
+    // chunks of work per segment (the gate-decay horizon).
+    const long long work = total * a.H;
+    const long long per = (work + cus - 1) / std::max(1, cus);
+    p.segc = (int)std::max<long long>(8, per);
+    p.segc = std::max(1, std::min(p.segc, std::max(1, maxc)));
+  }
+  long long nseg = 0;
+  for (int n = 0; n < p.N; ++n) nseg += nch[n] == 0 ? 1 : (nch[n] + p.segc - 1) / p.segc;
+  p.nseg = (int)nseg;
+  p.cp = p.nseg > p.N;
+  const size_t SS = (size_t)a.Dk * a.Dv;
+  const size_t esz = a.dtype == GDN_BF16 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  p.o_chunk_first = take(sizeof(int) * (p.N + 1));
+  p.o_seg_first = take(sizeof(int) * (p.N + 1));
+  p.o_segs = take(sizeof(gdn::SegDesc) * p.nseg);
+  p.o_chunk_tab = take(sizeof(int2) * std::max(1, p.nchunk));
+  if (p.cp) {
+    p.o_bstate = take(sizeof(float) * SS * p.nseg * a.H);
+    p.o_lam = take(sizeof(float) * (size_t)p.nseg * a.H);
+  }
+  if (bwd) {
+    if (p.cp) {
+      p.o_bstate2 = take(sizeof(float) * SS * p.nseg * a.H);
+      p.o_lam2 = take(sizeof(float) * (size_t)p.nseg * a.H);
+    }
+    p.o_hs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
+    p.o_dhs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
+  }
+  p.total = off;
+  return p;
+}
+
+template <class T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+
+gdn_status hip_fail(hipError_t e, const char* what) {
+  return fail(GDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+gdn::SeqInfo seq_info(const gdn_common_args& a) {
+  gdn::SeqInfo s;
+  s.cu = a.cu_seqlens;
+  s.T = a.T;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_last_error(void) { return g_err.c_str(); }
+
+size_t gdn_chunk_fwd_workspace_size(const gdn_fwd_args* args) {
+  if (!args) { fail(GDN_E_INVALID, "null args"); return 0; }
+  if (check_common(args->a) != GDN_OK) return 0;
+  return make_plan(args->a, false, cu_count()).total;
+}
+
+size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args) {
+  if (!args) { fail(GDN_E_INVALID, "null args"); return 0; }
+  if (check_common(args->a) != GDN_OK) return 0;
+  return make_plan(args->a, true, cu_count()).total;
+}
+
+gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
+  if (!args) return fail(GDN_E_INVALID, "null args");
+  const gdn_common_args& a = args->a;
+  gdn_status st = check_common(a);
+  if (st != GDN_OK) return st;
+  if ((long long)a.B * a.T > 0 && !args->o) return fail(GDN_E_INVALID, "null output o");
+  if (!aligned(args->o, 16)) return fail(GDN_E_INVALID, "o must be 16-byte aligned");
+  if (!aligned(args->hT, 4)) return fail(GDN_E_INVALID, "hT misaligned");
+  const Plan pl = make_plan(a, false, cu_count());
+  if (!a.workspace || a.workspace_bytes < pl.total)
+    return fail(GDN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total,
+                a.workspace ? a.workspace_bytes : (size_t)0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = a.workspace;
+  gdn::SeqInfo sq = seq_info(a);
+  hipError_t e = gdn::launch_plan(sq, pl.N, pl.segc, at<int>(ws, pl.o_chunk_first), at<int>(ws, pl.o_seg_first),
+                                  at<gdn::SegDesc>(ws, pl.o_segs), at<int2>(ws, pl.o_chunk_tab), s);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  gdn::FwdParams p{};
+  p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta; p.h0 = a.h0;
+  p.o = args->o; p.hT = args->hT; p.scale = a.scale; p.H = a.H; p.seq = sq;
+  p.segs = at<gdn::SegDesc>(ws, pl.o_segs);
+  p.seg_first = at<int>(ws, pl.o_seg_first);
+  p.chunk_first = at<int>(ws, pl.o_chunk_first);
+  p.bstate = pl.cp ? at<float>(ws, pl.o_bstate) : nullptr;
+  p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
+  p.hs = nullptr;
+  p.phase = 1;
+  e = gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  if (pl.cp) {
+    p.phase = 3;
+    e = gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s);
+    if (e != hipSuccess) return hip_fail(e, "forward correction launch");
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
+  if (!args) return fail(GDN_E_INVALID, "null args");
+  const gdn_common_args& a = args->a;
+  gdn_status st = check_common(a);
+  if (st != GDN_OK) return st;
+  const bool any = (long long)a.B * a.T > 0;
+  if (any && (!args->do_ || !args->dq || !args->dk || !args->dv || !args->dbeta || !args->dg))
+    return fail(GDN_E_INVALID, "null gradient pointer");
+  if (!aligned(args->do_, 16) || !aligned(args->dq, 16) || !aligned(args->dk, 16) || !aligned(args->dv, 16))
+    return fail(GDN_E_INVALID, "do, dq, dk and dv must be 16-byte aligned");
+  if (!aligned(args->dg, 4) || !aligned(args->dbeta, a.dtype == GDN_F32 ? 4 : 2) || !aligned(args->dhT, 4) ||
+      !aligned(args->dh0, 4))
+    return fail(GDN_E_INVALID, "dg / dbeta / dhT / dh0 misaligned");
+  const Plan pl = make_plan(a, true, cu_count());
+  if (!a.workspace || a.workspace_bytes < pl.total)
+    return fail(GDN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total,
+                a.workspace ? a.workspace_bytes : (size_t)0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = a.workspace;
+  gdn::SeqInfo sq = seq_info(a);
+  hipError_t e = gdn::launch_plan(sq, pl.N, pl.segc, at<int>(ws, pl.o_chunk_first), at<int>(ws, pl.o_seg_first),
+                                  at<gdn::SegDesc>(ws, pl.o_segs), at<int2>(ws, pl.o_chunk_tab), s);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  // 1. forward replay: state at every chunk start
+  gdn::FwdParams p{};
+  p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta; p.h0 = a.h0;
+  p.o = nullptr; p.hT = nullptr; p.scale = a.scale; p.H = a.H; p.seq = sq;
+  p.segs = at<gdn::SegDesc>(ws, pl.o_segs);
+  p.seg_first = at<int>(ws, pl.o_seg_first);
+  p.chunk_first = at<int>(ws, pl.o_chunk_first);
+  p.bstate = pl.cp ? at<float>(ws, pl.o_bstate) : nullptr;
+  p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
+  p.hs = at<void>(ws, pl.o_hs);
+  p.phase = 1;
+  e = gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s);
+  if (e != hipSuccess) return hip_fail(e, "replay launch");
+  if (pl.cp) {
+    p.phase = 3;
+    e = gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s);
+    if (e != hipSuccess) return hip_fail(e, "replay correction launch");
+  }
+  // 2. reverse chain: state gradient at every chunk end, dh0
+  gdn::RevParams r{};
+  r.q = a.q; r.k = a.k; r.g = a.g; r.beta = a.beta; r.dout = args->do_; r.dhT = args->dhT; r.dh0 = args->dh0;
+  r.scale = a.scale; r.H = a.H; r.seq = sq;
+  r.segs = p.segs; r.seg_first = p.seg_first; r.chunk_first = p.chunk_first;
+  r.bstate = pl.cp ? at<float>(ws, pl.o_bstate2) : nullptr;
+  r.lam = pl.cp ? at<float>(ws, pl.o_lam2) : nullptr;
+  r.dhs = at<void>(ws, pl.o_dhs);
+  r.phase = 1;
+  e = gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s);
+  if (e != hipSuccess) return hip_fail(e, "reverse launch");
+  if (pl.cp) {
+    r.phase = 3;
+    e = gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s);
+    if (e != hipSuccess) return hip_fail(e, "reverse correction launch");
+  }
+  // 3. chunk-parallel gradients
+  if (pl.nchunk > 0) {
+    gdn::GradParams gp{};
+    gp.q = a.q; gp.k = a.k; gp.v = a.v; gp.g = a.g; gp.beta = a.beta; gp.dout = args->do_;
+    gp.hs = p.hs; gp.dhs = r.dhs;
+    gp.dq = args->dq; gp.dk = args->dk; gp.dv = args->dv; gp.dbeta = args->dbeta; gp.dg = args->dg;
+    gp.scale = a.scale; gp.H = a.H; gp.seq = sq;
+    gp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);
+    e = gdn::launch_grad(a.dtype, a.Dk, a.Dv, gp, pl.nchunk, s);
+    if (e != hipSuccess) return hip_fail(e, "gradient launch");
+  }
+  return GDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+// gdn_device.h -- device-side building blocks shared by the GDN kernels (gfx950).
+//
+// Matrix products run on the CDNA4 matrix cores with 16x16 output tiles:
+//   bf16 operands: v_mfma_f32_16x16x32_bf16  (one instruction per 32-deep k-block)
+//   fp32 operands: v_mfma_f32_16x16x4_f32    (eight instructions per 32-deep k-block)
+// Accumulator ("C") layout of a 16x16 fp32 tile in a wave of 64 lanes:
+//   lane l holds C[4*(l/16) + i][l % 16] in acc[i], i = 0..3.
+//
+// k-permutation.  Inside one 32-deep k-block, lane l (lane group g = l/16) feeds
+// eight operand slots j = 0..7 that stand for the logical k index
+//   kperm(g, j) = 4g + j          (j < 4)
+//               = 16 + 4g + j - 4 (j >= 4).
+// The matrix core pairs slot j of the A operand with slot j of the B operand in
+// the same lane group, so any fixed slot->k map gives the right sum as long as A
+// and B use the same one.  This particular map is chosen because it is exactly
+// what a lane already holds of two vertically stacked C tiles (rows 4g..4g+3 of
+// each): an accumulator tile pair can be fed back as an operand along k with no
+// data movement across lanes.
+//
+// Operand sources:
+//   "X" operand (A side, m = row):  row-major matrix in LDS, k contiguous.
+//   "Y" operand (B side, n = col):  the product is C = X * Y^T, Y row-major with
+//                                   k contiguous -- the "NT" form.
+//   register operand: a pair of C tiles stacked along k.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int CH = 64;  // chunk length (rows per chunk)
+
+// ln(2^-24): a boundary state whose propagated contribution is bounded by
+// exp(sum of per-token log-bounds) * |state| stops mattering once that factor
+// is below fp32's unit round-off.
+constexpr float LN_EPS = -16.635532333438686f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ---------------------------------------------------------------------------
+// Operand fragments: eight k-slots per lane.
+template <class E> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[j], b.lo[j], acc, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[j], b.hi[j], acc, 0, 0, 0);
+}
+
+// Load the eight k-slots of row `row` of a row-major LDS matrix (k contiguous),
+// for the k-block starting at k0.  Slots: [k0+4g .. +3], [k0+16+4g .. +3].
+__device__ __forceinline__ Frag<bf16> ld_frag(const bf16* base, int ld, int row, int k0) {
+  const int g = lane_id() >> 4;
+  const bf16* p = base + row * ld + k0 + 4 * g;
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+__device__ __forceinline__ Frag<float> ld_frag(const float* base, int ld, int row, int k0) {
+  const int g = lane_id() >> 4;
+  const float* p = base + row * ld + k0 + 4 * g;
+  Frag<float> f;
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 16);
+  return f;
+}
+
+// Fragment of row `row` of an fp32 row-major LDS matrix, each k-slot multiplied
+// by kscale[k] (a diagonal matrix applied on the right), converted to E.
+template <class E>
+__device__ __forceinline__ Frag<E> ld_frag_scaled(const float* base, int ld, int row, int k0,
+                                                  const float* kscale) {
+  const int g = lane_id() >> 4;
+  const float* p = base + row * ld + k0 + 4 * g;
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 16);
+  f32x4 sa = *reinterpret_cast<const f32x4*>(kscale + k0 + 4 * g);
+  f32x4 sb = *reinterpret_cast<const f32x4*>(kscale + k0 + 16 + 4 * g);
+  Frag<E> f;
+  pack_frag(f, a * sa, b * sb);
+  return f;
+}
+
+// Register operand from two accumulator tiles stacked along k (t0: k0..k0+15,
+// t1: k0+16..k0+31), each slot multiplied by a per-k scale (s0 for t0's rows,
+// s1 for t1's rows).
+__device__ __forceinline__ void pack_frag(Frag<bf16>& f, const f32x4& t0, const f32x4& t1) {
+  f.v = bf16x8{(bf16)t0[0], (bf16)t0[1], (bf16)t0[2], (bf16)t0[3],
+               (bf16)t1[0], (bf16)t1[1], (bf16)t1[2], (bf16)t1[3]};
+}
+__device__ __forceinline__ void pack_frag(Frag<float>& f, const f32x4& t0, const f32x4& t1) {
+  f.lo = t0;
+  f.hi = t1;
+}
+template <class E>
+__device__ __forceinline__ void pack_frag_scaled(Frag<E>& f, const f32x4& t0, const f32x4& t1,
+                                                 const f32x4& s0, const f32x4& s1) {
+  pack_frag(f, t0 * s0, t1 * s1);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// fp32 -> storage type
+template <class E> __device__ __forceinline__ E to_e(float x);
+template <> __device__ __forceinline__ bf16 to_e<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float to_e<float>(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+
+// Wave-wide inclusive prefix sum (64 lanes).
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    float y = __shfl_up(x, o, 64);
+    if (l >= o) x += y;
+  }
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Row-major LDS leading dimensions: 4 extra elements per row stagger rows
+// across LDS banks for the 8-/16-byte fragment reads.
+template <class E> constexpr int ldpad(int n) { return n + 4; }
+
+// Per-chunk work description, written by the plan kernel.
+struct SegDesc {
+  int n;        // sequence index
+  int c_begin;  // first chunk (index within the sequence)
+  int c_end;    // one past the last chunk
+  int s;        // segment index within the sequence
+};
+
+struct SeqInfo {
+  const int32_t* cu;   // device cu_seqlens [N+1] or nullptr for uniform length T
+  int T;               // tokens per sequence when cu == nullptr
+  __device__ __forceinline__ int64_t start(int n) const { return cu ? (int64_t)cu[n] : (int64_t)n * T; }
+  __device__ __forceinline__ int len(int n) const { return cu ? cu[n + 1] - cu[n] : T; }
+};
+
+}  // namespace gdn

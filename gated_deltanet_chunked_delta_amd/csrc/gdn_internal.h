@@ -1,0 +1,80 @@
+// gdn_internal.h -- host/device parameter blocks and launchers (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_device.h"
+
+namespace gdn {
+
+// Forward chunk loop (also the backward's forward-state replay).
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const void* beta;
+  const float* h0;         // nullable
+  void* o;                 // nullable: replay mode writes no output
+  float* hT;               // nullable
+  float scale;
+  int H;
+  SeqInfo seq;
+  const SegDesc* segs;     // [total segments]
+  const int* seg_first;    // [N+1]
+  const int* chunk_first;  // [N+1]
+  float* bstate;           // [total segments][H][DK][DV] segment end states
+  float* lam;              // [total segments][H] segment log-bounds
+  void* hs;                // nullable: [total chunks][H][DK][DV] chunk start states (dtype)
+  int phase;               // 1 = segments from zero / h0, 3 = boundary corrections
+};
+
+// Reverse state-gradient chain of the backward.
+struct RevParams {
+  const void* q;
+  const void* k;
+  const float* g;
+  const void* beta;
+  const void* dout;
+  const float* dhT;        // nullable
+  float* dh0;              // nullable
+  float scale;
+  int H;
+  SeqInfo seq;
+  const SegDesc* segs;
+  const int* seg_first;
+  const int* chunk_first;
+  float* bstate;           // [total segments][H][DK][DV] segment start gradients
+  float* lam;              // [total segments][H]
+  void* dhs;               // [total chunks][H][DK][DV] gradient at each chunk END (dtype)
+  int phase;
+};
+
+// Chunk-parallel gradients of the backward.
+struct GradParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const void* beta;
+  const void* dout;
+  const void* hs;          // chunk start states
+  const void* dhs;         // chunk end state gradients
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dbeta;
+  float* dg;
+  float scale;
+  int H;
+  SeqInfo seq;
+  const int2* chunk_tab;   // [total chunks] (sequence, chunk index within it)
+};
+
+hipError_t launch_plan(SeqInfo seq, int N, int segc, int* chunk_first, int* seg_first, SegDesc* segs,
+                       int2* chunk_tab, hipStream_t st);
+hipError_t launch_fwd(int dtype, int DK, int DV, const FwdParams& p, int nseg_total, hipStream_t st);
+hipError_t launch_rev(int dtype, int DK, int DV, const RevParams& p, int nseg_total, hipStream_t st);
+hipError_t launch_grad(int dtype, int DK, int DV, const GradParams& p, int nchunk_total, hipStream_t st);
+
+}  // namespace gdn

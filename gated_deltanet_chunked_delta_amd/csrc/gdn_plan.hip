@@ -1,0 +1,98 @@
+// gdn_plan.hip -- device-side work plan: which chunks each workgroup owns.
+//
+// Every sequence n is cut into ceil(len_n / 64) chunks (the last one may be
+// short) and its chunks into segments of `segc` chunks.  One small workgroup
+// derives, from the device copy of cu_seqlens (or the uniform length T):
+//   chunk_first[n]  first global chunk index of sequence n   ([N+1] prefix)
+//   seg_first[n]    first global segment index of sequence n ([N+1] prefix)
+//   segs[j]         (sequence, chunk range, segment index) of global segment j
+//   chunk_tab[c]    (sequence, chunk index within it) of global chunk c
+// An empty sequence gets one segment with no chunks, so that its final state
+// (h0) and its initial-state gradient (dhT) still pass through.
+#include "gdn_internal.h"
+
+namespace gdn {
+
+constexpr int PLAN_NT = 1024;
+
+__global__ __launch_bounds__(PLAN_NT) void gdn_plan_kernel(SeqInfo seq, int N, int segc, int* chunk_first,
+                                                          int* seg_first, SegDesc* segs, int2* chunk_tab) {
+  __shared__ int sc[PLAN_NT], ss[PLAN_NT];
+  __shared__ int carry_c, carry_s;
+  const int tid = threadIdx.x;
+  if (tid == 0) { carry_c = 0; carry_s = 0; }
+  __syncthreads();
+  for (int base = 0; base < N; base += PLAN_NT) {
+    const int n = base + tid;
+    int nc = 0, ns = 0;
+    if (n < N) {
+      const int len = seq.len(n);
+      nc = (len + CH - 1) / CH;
+      ns = nc == 0 ? 1 : (nc + segc - 1) / segc;
+    }
+    sc[tid] = nc;
+    ss[tid] = ns;
+    __syncthreads();
+    // inclusive Hillis-Steele scan over the tile
+    for (int o = 1; o < PLAN_NT; o <<= 1) {
+      int a = tid >= o ? sc[tid - o] : 0, b = tid >= o ? ss[tid - o] : 0;
+      __syncthreads();
+      sc[tid] += a;
+      ss[tid] += b;
+      __syncthreads();
+    }
+    if (n < N) {
+      chunk_first[n] = carry_c + sc[tid] - nc;
+      seg_first[n] = carry_s + ss[tid] - ns;
+    }
+    __syncthreads();
+    if (tid == PLAN_NT - 1) {
+      carry_c += sc[tid];
+      carry_s += ss[tid];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    chunk_first[N] = carry_c;
+    seg_first[N] = carry_s;
+  }
+  __syncthreads();
+  __threadfence();
+  const int total_s = carry_s, total_c = carry_c;
+  // fill the tables: locate the owning sequence by binary search over the prefixes
+  for (int j = tid; j < total_s; j += PLAN_NT) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seg_first[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    // skip sequences that own no segment (none do: every sequence has >= 1)
+    const int n = lo, s = j - seg_first[n];
+    const int nc = (seq.len(n) + CH - 1) / CH;
+    SegDesc d;
+    d.n = n;
+    d.s = s;
+    d.c_begin = min(nc, s * segc);
+    d.c_end = min(nc, (s + 1) * segc);
+    segs[j] = d;
+  }
+  for (int c = tid; c < total_c; c += PLAN_NT) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (chunk_first[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    // sequences with zero chunks share their prefix with the next one; the
+    // search lands on the last sequence whose first chunk is <= c, which owns c
+    chunk_tab[c] = make_int2(lo, c - chunk_first[lo]);
+  }
+}
+
+hipError_t launch_plan(SeqInfo seq, int N, int segc, int* chunk_first, int* seg_first, SegDesc* segs,
+                       int2* chunk_tab, hipStream_t st) {
+  hipLaunchKernelGGL(gdn_plan_kernel, dim3(1), dim3(PLAN_NT), 0, st, seq, N, segc, chunk_first, seg_first,
+                     segs, chunk_tab);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

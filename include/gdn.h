@@ -1,0 +1,135 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) chunked Gated DeltaNet prefill library.
+ *
+ * Operation.  The pages this library follows ("Qwen's FlashQLA targets the
+ * expensive bit of long-context AI", section "What happened"; "FlashQLA
+ * resource", section 2 "What It Actually Is") describe the forward and backward
+ * pass of Gated DeltaNet (GDN) chunked prefill.  They print no formula; the
+ * computation is the published gated delta rule, per sequence and head:
+ *
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,    S_0 = h0^T
+ *     o_t = scale * S_t q_t,                                               hT = S_T^T
+ *
+ * with S a Dv x Dk matrix, evaluated chunk by chunk (64 tokens) in the exact
+ * WY/UT form ("FlashQLA resource", section 3: an algebraic reformulation that
+ * keeps full precision).  Long sequences with few heads are split into
+ * segments that run side by side on one GPU; the exponential decay of the
+ * gates bounds how far a segment boundary's state must be propagated
+ * ("FlashQLA resource", section 3, gate-driven intra-card context parallelism;
+ * section 5 for the backward pass).  The result does not depend on the split
+ * beyond fp32 rounding.
+ *
+ * Layouts (row-major, last dimension contiguous, all pointers device memory
+ * unless stated otherwise; every tensor pointer 16-byte aligned):
+ *   q, k                [B, T, H, Dk]   dtype
+ *   v, o                [B, T, H, Dv]   dtype
+ *   beta                [B, T, H]       dtype
+ *   g                   [B, T, H]       fp32, natural-log decay (<= 0 in the tested domain)
+ *   h0, hT, dhT, dh0    [N, H, Dk, Dv]  fp32, h = S^T
+ *   do, dq, dk, dv, dbeta   like o, q, k, v, beta; dg like g (fp32)
+ * Variable-length batches: B == 1, sequences packed along T, described by
+ * cu_seqlens (int32 [N+1], cu[0] = 0, non-decreasing, cu[N] = T).  The
+ * recurrence restarts at every sequence start.  Without cu_seqlens, N = B.
+ *
+ * Supported: dtype GDN_BF16 with Dk, Dv in {64, 128}; GDN_F32 with Dk = Dv = 64.
+ *
+ * Ownership.  The caller owns every buffer, including the workspace, whose size
+ * the *_workspace_size functions report for the same arguments.  The library
+ * allocates no device memory and keeps no state besides a per-device cache of
+ * the compute-unit count and a thread-local error string.
+ *
+ * Asynchrony.  Calls enqueue kernels on the caller's HIP stream and return
+ * without synchronising.  Buffers must stay valid until the stream has passed
+ * the call.  Two calls that share a workspace must be ordered on one stream.
+ *
+ * Errors.  All argument checks run before anything is enqueued: a call that
+ * returns GDN_E_INVALID / GDN_E_UNSUPPORTED / GDN_E_WORKSPACE has written
+ * nothing.  GDN_E_HIP reports a failed launch (the message carries HIP's
+ * error string).  gdn_last_error() returns a description of the last non-OK
+ * status on the calling thread.  Nothing throws or aborts across this ABI.
+ * Non-finite inputs propagate; they are not detected.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_E_INVALID = 1,     /* null pointer, bad size, misalignment, bad cu_seqlens, ... */
+  GDN_E_UNSUPPORTED = 2, /* dtype / head-size combination not built */
+  GDN_E_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size */
+  GDN_E_HIP = 4          /* a HIP launch or query failed */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Arguments shared by forward and backward. */
+typedef struct {
+  int32_t dtype;               /* gdn_dtype of q, k, v, beta (and o, do, dq, dk, dv, dbeta) */
+  int32_t B, T, H, Dk, Dv;     /* with cu_seqlens: B == 1 and T = total packed tokens */
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const void* beta;
+  const float* h0;             /* nullable: zero initial state */
+  float scale;                 /* output scale; the usual choice is Dk^-0.5 */
+  const int32_t* cu_seqlens;   /* nullable device pointer [N+1] */
+  const int32_t* cu_seqlens_host; /* host copy of the same [N+1]; required with cu_seqlens */
+  int32_t num_seqs;            /* N: len(cu_seqlens) - 1, or B when cu_seqlens is NULL */
+  int32_t cp_mode;             /* intra-card sequence splitting: 0 = automatic,
+                                  -1 = off (one segment per sequence and head),
+                                  k > 0 = segments of k chunks (64 tokens each) */
+  void* workspace;             /* device scratch of at least workspace_bytes */
+  size_t workspace_bytes;
+} gdn_common_args;
+
+typedef struct {
+  gdn_common_args a;
+  void* o;                     /* [B,T,H,Dv] dtype, written */
+  float* hT;                   /* nullable [N,H,Dk,Dv] fp32, written */
+} gdn_fwd_args;
+
+typedef struct {
+  gdn_common_args a;           /* the forward's inputs; the backward recomputes what it needs */
+  const void* do_;             /* [B,T,H,Dv] dtype: gradient of o */
+  const float* dhT;            /* nullable [N,H,Dk,Dv]: gradient of hT (NULL = zero) */
+  void* dq;                    /* [B,T,H,Dk] dtype, written */
+  void* dk;                    /* [B,T,H,Dk] dtype, written */
+  void* dv;                    /* [B,T,H,Dv] dtype, written */
+  void* dbeta;                 /* [B,T,H] dtype, written */
+  float* dg;                   /* [B,T,H] fp32, written */
+  float* dh0;                  /* nullable [N,H,Dk,Dv] fp32, written */
+} gdn_bwd_args;
+
+/* Bytes of device workspace gdn_chunk_fwd / gdn_chunk_bwd need for these
+ * arguments (pointers other than cu_seqlens_host are not read).  Returns 0 and
+ * sets the error string when the arguments are invalid. */
+size_t gdn_chunk_fwd_workspace_size(const gdn_fwd_args* args);
+size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args);
+
+/* Forward: o and (optionally) hT.  stream is a hipStream_t (NULL = default stream). */
+gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream);
+
+/* Backward: gradients of <do, o> + <dhT, hT> with respect to q, k, v, beta, g
+ * and (optionally) h0.  It recomputes the forward states from the inputs. */
+gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char* gdn_last_error(void);
+
+/* GDN_ABI_VERSION of the library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

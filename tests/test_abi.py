@@ -1,0 +1,94 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before touching the device."""
+import ctypes
+
+import pytest
+
+from gated_deltanet_chunked_delta_amd import binding as B
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = B.exported_symbols()
+    assert {"gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_chunk_fwd_workspace_size",
+            "gdn_chunk_bwd_workspace_size", "gdn_last_error", "gdn_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.gdn_abi_version() == 1
+
+
+FAKE = 1 << 20  # a 16-byte aligned fake device address; never dereferenced
+
+
+def fwd_args(**kw):
+    a = B.CommonArgs()
+    a.dtype, a.B, a.T, a.H, a.Dk, a.Dv = B.GDN_BF16, 1, 128, 2, 128, 128
+    a.q = a.k = a.v = a.g = a.beta = FAKE
+    a.scale = 0.1
+    a.num_seqs = 1
+    a.workspace = FAKE
+    a.workspace_bytes = 1 << 30
+    for key, val in kw.items():
+        setattr(a, key, val)
+    f = B.FwdArgs()
+    f.a = a
+    f.o = FAKE
+    return f
+
+
+def call_fwd(L, f):
+    return L.gdn_chunk_fwd(ctypes.byref(f), None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q", None, 1), ("g", None, 1), ("beta", None, 1),
+    ("B", 0, 1), ("H", 0, 1), ("T", -1, 1),
+    ("Dk", 96, 2), ("Dv", 32, 2), ("dtype", 7, 2),
+    ("q", FAKE + 8, 1),          # misaligned
+    ("cp_mode", -2, 1),
+    ("num_seqs", 2, 1),          # != B without cu_seqlens
+    ("workspace_bytes", 16, 3), ("workspace", None, 3),
+])
+def test_forward_rejects_bad_arguments(L, field, value, status):
+    f = fwd_args(**{field: value})
+    assert call_fwd(L, f) == status
+    assert L.gdn_last_error()
+
+
+def test_f32_only_head_size_64(L):
+    assert call_fwd(L, fwd_args(dtype=B.GDN_F32)) == 2
+
+
+def test_cu_seqlens_validation(L):
+    import numpy as np
+    for cu, status in [([0, 5, 3, 128], 1), ([1, 64, 128], 1), ([0, 64, 100], 1)]:
+        host = np.array(cu, dtype=np.int32)
+        f = fwd_args(cu_seqlens=FAKE, cu_seqlens_host=host.ctypes.data, num_seqs=len(cu) - 1)
+        assert call_fwd(L, f) == status, cu
+    host = np.array([0, 64, 128], dtype=np.int32)
+    f = fwd_args(B=2, T=64, cu_seqlens=FAKE, cu_seqlens_host=host.ctypes.data, num_seqs=2)
+    assert call_fwd(L, f) == 1           # B != 1 with cu_seqlens
+    f = fwd_args(cu_seqlens=FAKE, num_seqs=2)
+    assert call_fwd(L, f) == 1           # host copy missing
+
+
+def test_workspace_size_query(L):
+    f = fwd_args()
+    n1 = L.gdn_chunk_fwd_workspace_size(ctypes.byref(f))
+    assert n1 > 0
+    bad = fwd_args(Dk=96)
+    assert L.gdn_chunk_fwd_workspace_size(ctypes.byref(bad)) == 0
+    b = B.BwdArgs()
+    b.a = fwd_args().a
+    assert L.gdn_chunk_bwd_workspace_size(ctypes.byref(b)) > n1
+
+
+def test_backward_rejects_missing_gradients(L):
+    b = B.BwdArgs()
+    b.a = fwd_args().a
+    b.do_ = FAKE
+    assert L.gdn_chunk_bwd(ctypes.byref(b), None) == 1

@@ -1,0 +1,122 @@
+"""Forward parity on the GPU: HIP path through the C ABI vs the fp64 oracle,
+element by element, on the same seeded inputs."""
+import sys
+
+import numpy as np
+import pytest
+
+import gdn_inputs
+from oracle import ref
+from tests.helpers import TOL, relerr, to_np, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def run_fwd(x, dev, cp_mode=0, final=True):
+    from gated_deltanet_chunked_delta_amd import gdn_chunk_fwd
+    import torch
+    t = to_torch(x, dev)
+    host = None if x.cu_seqlens is None else x.cu_seqlens.astype(np.int32)
+    o, hT = gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, h0=t["h0"],
+                          cu_seqlens=t["cu"], cu_seqlens_host=host, output_final_state=final,
+                          cp_mode=cp_mode)
+    torch.cuda.synchronize()
+    return to_np(o), to_np(hT)
+
+
+def check_fwd(x, dev, cp_mode=0, label=""):
+    print(f"[fwd] {label} T={x.q.shape[1]} H={x.q.shape[2]} Dk={x.q.shape[3]} Dv={x.v.shape[3]} "
+          f"{x.dtype} cp={cp_mode}", flush=True)
+    sys.stdout.flush()
+    o, hT = run_fwd(x, dev, cp_mode)
+    ro, rhT = ref.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0, x.cu_seqlens)
+    eo, eh = relerr(o, ro), relerr(hT, rhT)
+    print(f"    o {eo:.3e}  hT {eh:.3e}", flush=True)
+    assert eo <= TOL[x.dtype] and eh <= TOL[x.dtype], (eo, eh)
+    return o, hT
+
+
+# ------------------------------------------------------------------ small cases, many tiles + ragged tails
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 333])
+@pytest.mark.parametrize("cp_mode", [-1, 1, 2])
+def test_ragged_lengths_bf16(dev, T, cp_mode):
+    x = gdn_inputs.generate(B=2, T=T, H=3, Dk=128, Dv=128, dtype="bf16", seed=100 + T, h0_std=0.5)
+    check_fwd(x, dev, cp_mode, "ragged")
+
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 64), (64, 128), (128, 64)])
+def test_head_sizes_bf16(dev, Dk, Dv):
+    x = gdn_inputs.generate(B=1, T=300, H=2, Dk=Dk, Dv=Dv, dtype="bf16", seed=7 + Dk + Dv, h0_std=0.1)
+    for cp in (-1, 2):
+        check_fwd(x, dev, cp, "heads")
+
+
+@pytest.mark.parametrize("T,cp", [(256, -1), (256, 1), (130, 0), (700, 3)])
+def test_fp32_path(dev, T, cp):
+    x = gdn_inputs.generate(B=1, T=T, H=2, Dk=64, Dv=64, dtype="f32", seed=11 + T, h0_std=0.3)
+    check_fwd(x, dev, cp, "f32")
+
+
+def test_varlen_with_empty_and_tiny_sequences(dev):
+    rng = np.random.default_rng(5)
+    lens = [0, 1, 64, 130, 0, 77, 500, 3]
+    cu = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    y = gdn_inputs.generate(B=1, T=int(cu[-1]), H=2, Dk=128, Dv=128, dtype="bf16", seed=10)
+    y.cu_seqlens = cu
+    y.h0 = (0.3 * rng.standard_normal((len(lens), 2, 128, 128))).astype(np.float32)
+    for cp in (-1, 1, 0):
+        check_fwd(y, dev, cp, "varlen-edge")
+
+
+def test_segment_split_is_exact(dev):
+    """With fp32 arithmetic throughout, forced segment splits agree with the
+    unsplit run to fp32 rounding: the boundary correction drops nothing."""
+    x = gdn_inputs.generate(B=1, T=1000, H=2, Dk=64, Dv=64, dtype="f32", seed=3, h0_std=0.2)
+    o_ref, h_ref = run_fwd(x, dev, -1)
+    for cp in (1, 2, 5):
+        o, hT = run_fwd(x, dev, cp)
+        assert relerr(o, o_ref) < 1e-5 and relerr(hT, h_ref) < 1e-5, cp
+    # bf16 inputs: split and unsplit both sit well inside the oracle tolerance
+    y = gdn_inputs.generate(B=1, T=1000, H=2, Dk=128, Dv=128, dtype="bf16", seed=3, h0_std=0.2)
+    for cp in (-1, 1, 5):
+        check_fwd(y, dev, cp, "split-bf16")
+
+
+def test_slow_decay_falls_back_to_serial(dev):
+    """Gates near zero do not decay across a segment: the boundary certificate
+    fails and the sequence is recomputed serially -- results stay exact."""
+    x = gdn_inputs.generate(B=1, T=640, H=2, Dk=128, Dv=128, dtype="bf16", seed=4, h0_std=0.2)
+    x.g = (x.g * 1e-3).astype(np.float32)
+    for cp in (1, 3):
+        check_fwd(x, dev, cp, "no-decay")
+
+
+def test_no_final_state(dev):
+    x = gdn_inputs.generate(B=1, T=100, H=1, Dk=64, Dv=64, dtype="bf16", seed=1)
+    o, hT = run_fwd(x, dev, 0, final=False)
+    assert hT is None
+    ro, _ = ref.fwd(x.q, x.k, x.v, x.g, x.beta, x.scale)
+    assert relerr(o, ro) <= TOL["bf16"]
+
+
+def test_deterministic(dev):
+    x = gdn_inputs.generate(B=1, T=777, H=2, Dk=128, Dv=128, dtype="bf16", seed=12, h0_std=0.1)
+    a = run_fwd(x, dev, 2)
+    b = run_fwd(x, dev, 2)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ the measured workloads
+@pytest.mark.parametrize("name", ["tiny_f32", "single_bf16", "long_fewhead", "varlen", "metric_32k"])
+def test_config_forward(dev, name):
+    x = gdn_inputs.config(name, grad=False)
+    check_fwd(x, dev, 0, name)
