@@ -1,5 +1,821 @@
+// gdn_bwd.hip -- backward pass of the chunked gated delta rule on gfx950.
+//
+// The backward ("FlashQLA resource", sections 3 and 5: fused backward kernels
+// with intra-card sequence parallelism) runs in three stages after the forward
+// replay (gdn_fwd.hip in replay mode stores the state h_c at every chunk start):
+//
+//  1. Reverse chain (this file, gdn_rev_kernel): per (segment, head), from the
+//     last chunk to the first, the gradient dh' at each chunk END is stored and
+//     carried back through the chunk:
+//        dU = scale P^T dO + diag(ek) K dh'
+//        dh = scale (diag(Gam) Q)^T dO + Gam_C dh' - W^T dU
+//     The dh' chain lives in accumulator registers (wave w owns 16 columns).
+//     Long sequences are cut into segments exactly as in the forward; a
+//     segment's provisional run starts from dh' = 0 (dhT for the last one) and
+//     a correction pass propagates the true boundary gradient backwards through
+//     the last chunks of each segment until the gate-decay bound drops under
+//     fp32 round-off (the transpose of the forward transition has the same norm
+//     bound).
+//
+//  2. Chunk gradients (gdn_grad_kernel): every chunk independently, given h_c
+//     and dh'_c, evaluates the reverse-mode derivative of the chunk algebra
+//     (with D_ri = exp(gam_r - gam_i), M = D * [i <= r], ek = exp(gam_last - gam)):
+//        GP = scale (dO U^T) * [i <= r]
+//        GW = -dU h^T,  XW = T^T GW,  XU = T^T dU
+//        GT = dU (diag(beta) V)^T + GW (diag(beta Gam) K)^T
+//        GA = strict_lower(-T^T GT T^T),  E = diag(beta) (GA * D)
+//        dQ = scale diag(Gam) dO h^T + (GP*M) K
+//        dK = (GP*M)^T Q + diag(ek) U dh'^T + diag(beta Gam) XW + (E + E^T) K
+//        dV = diag(beta) XU
+//        dbeta_r = XU_r.v_r + Gam_r XW_r.k_r + sum_i GA_ri D_ri (k_r.k_i)
+//        dgam_r  = scale Gam_r q_r.(dO h^T)_r + beta_r Gam_r XW_r.k_r
+//                  + rowsum_r(GP*P) - colsum_r(GP*P) + rowsum_r(GA*A) - colsum_r(GA*A)
+//                  - ek_r k_r.(U dh'^T)_r
+//                  + [r = last] (Gam_C <h, dh'> + sum_i ek_i k_i.(U dh'^T)_i)
+//        dg = reverse cumulative sum of dgam within the chunk.
+//     A short final chunk is handled as a 64-row chunk whose extra rows have
+//     zero q, k, v, dO, beta and g, which leaves every real gradient unchanged.
+#include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_tiles.h"
+
 namespace gdn {
-hipError_t launch_rev(int, int, int, const RevParams&, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_grad(int, int, int, const GradParams&, int, hipStream_t) { return hipErrorNotSupported; }
+
+// ======================================================================== reverse chain
+
+template <class E, int DK, int DV>
+struct alignas(16) RevSmem {
+  static constexpr int LQ = ldpad<E>(DK);
+  static constexpr int LT = ldpad<E>(CH);
+  static constexpr int LA = CH + 4;
+  E Q[CH * LQ];    // row-major, X of Q K^T
+  E K[CH * LQ];    // row-major, X/Y of K K^T, X of K dh'
+  E KT[DK * LT];   // K^T, X of W^T
+  E QT[DK * LT];   // Q^T, X of (Gam Q)^T dO
+  E DOT[DV * LT];  // dO^T, Y of P^T dO and (Gam Q)^T dO
+  E WT[DK * LT];   // -W^T
+  E PT[CH * LT];   // scale * P^T
+  float A[CH * LA];
+  float T[CH * LA];
+  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], graw[CH], lam[CH], sGam[CH];
+  float GamC;
+};
+
+enum : int { R_CORR = 1 };
+
+// One chunk of the reverse chain.  dh: this wave's columns of the gradient at
+// the chunk end on entry, at the chunk start on exit.  Returns Lambda_c.
+template <class E, int DK, int DV>
+__device__ float rev_step(RevSmem<E, DK, DV>& s, const RevParams& p, int64_t tok0, int rows, int h,
+                          int mode, E* dhs_chunk, f32x4 (&dh)[DK / 16]) {
+  using Sm = RevSmem<E, DK, DV>;
+  constexpr int NW = DV / 16, NT = NW * 64;
+  constexpr int LQ = Sm::LQ, LT = Sm::LT, LA = Sm::LA;
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const bool corr = mode & R_CORR;
+  const int H = p.H;
+
+  // ---- 0. gradient at the chunk end, out
+#pragma unroll
+  for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      E* dst = dhs_chunk + (16 * t + 4 * g + i) * DV + 16 * w + c16;
+      float val = dh[t][i];
+      if (corr) val += to_f(*dst);
+      *dst = to_e<E>(val);
+    }
+
+  // ---- 1. staging
+  {
+    const E* k = static_cast<const E*>(p.k) + (tok0 * H + h) * DK;
+    stage_tile<E, DK, NT>(k, (int64_t)H * DK, rows, s.K, LQ, s.KT, LT);
+    if (!corr) {
+      const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
+      const E* d = static_cast<const E*>(p.dout) + (tok0 * H + h) * DV;
+      stage_tile<E, DK, NT>(q, (int64_t)H * DK, rows, s.Q, LQ, s.QT, LT);
+      stage_tile<E, DV, NT>(d, (int64_t)H * DV, rows, nullptr, 0, s.DOT, LT);
+    }
+    if (w == 0) {
+      const bool valid = l < rows;
+      const int64_t si = (tok0 + l) * H + h;
+      float gr = valid ? p.g[si] : 0.f;
+      float bt = valid ? to_f(static_cast<const E*>(p.beta)[si]) : 0.f;
+      float gm = wave_incl_scan(gr);
+      float gC = __shfl(gm, 63, 64);
+      float Gm = __expf(gm);
+      s.gam[l] = gm;
+      s.Gam[l] = Gm;
+      s.sGam[l] = p.scale * Gm;
+      s.ek[l] = __expf(gC - gm);
+      s.beta[l] = bt;
+      s.bg[l] = bt * Gm;
+      s.graw[l] = gr;
+      if (l == 0) s.GamC = __expf(gC);
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. K K^T -> A (+ lambda) ; Q K^T -> scale P^T
+  const int ntiles = corr ? 10 : 20;
+  for (int ti = w; ti < ntiles; ti += NW) {
+    const bool isq = ti >= 10;
+    const int tt = isq ? ti - 10 : ti;
+    int rt = 0;
+    while ((rt + 1) * (rt + 2) / 2 <= tt) ++rt;
+    const int ct = tt - rt * (rt + 1) / 2;
+    f32x4 acc = zero4();
+    const E* X = isq ? s.Q : s.K;
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb)
+      mma(acc, ld_frag(X, LQ, 16 * rt + c16, 32 * kb), ld_frag(s.K, LQ, 16 * ct + c16, 32 * kb));
+    const int c = 16 * ct + c16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rt + 4 * g + i;
+      if (!isq) {
+        float val = (c < r) ? s.beta[r] * acc[i] * __expf(s.gam[r] - s.gam[c]) : 0.f;
+        s.A[r * LA + c] = val;
+        if (r == c) s.lam[r] = s.graw[r] + __logf(fmaxf(1.f, fabsf(1.f - s.beta[r] * acc[i])));
+      } else {
+        float val = (c <= r) ? p.scale * acc[i] * __expf(s.gam[r] - s.gam[c]) : 0.f;
+        s.PT[c * LT + r] = to_e<E>(val);
+      }
+    }
+  }
+  __syncthreads();
+  const float lam_c = __shfl(wave_sum(s.lam[l]), 0, 64);
+
+  // ---- 3. T = (I + A)^-1
+  solve_T(s.A, s.T, nullptr);
+
+  // ---- 4. -W^T = -K^T diag(beta Gam) T^T
+  for (int ti = w; ti < (DK / 16) * 4; ti += NW) {
+    const int dt = ti >> 2, rt = ti & 3;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      mma(acc, ld_frag_kscaled<E>(s.KT, LT, 16 * dt + c16, 32 * kb, s.bg),
+          ld_frag_f32<E>(s.T, LA, 16 * rt + c16, 32 * kb));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s.WT[(16 * dt + 4 * g + i) * LT + 16 * rt + c16] = to_e<E>(-acc[i]);
+  }
+  __syncthreads();
+
+  // ---- 5. dU = diag(ek) K dh' + scale P^T dO ; dh = Gam_C dh' + scale (Gam Q)^T dO - W^T dU
+  f32x4 du[4];
+  {
+    Frag<E> hf[DK / 32];
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) pack_frag(hf[kb], dh[2 * kb], dh[2 * kb + 1]);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) mma(acc, ld_frag(s.K, LQ, 16 * rt + c16, 32 * kb), hf[kb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= s.ek[16 * rt + 4 * g + i];
+      if (!corr) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          mma(acc, ld_frag(s.PT, LT, 16 * rt + c16, 32 * kb), ld_frag(s.DOT, LT, 16 * w + c16, 32 * kb));
+      }
+      du[rt] = acc;
+    }
+  }
+  {
+    const float gc = s.GamC;
+    Frag<E> uf[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) pack_frag(uf[kb], du[2 * kb], du[2 * kb + 1]);
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t) {
+      dh[t] = dh[t] * gc;
+      if (!corr) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          mma(dh[t], ld_frag_kscaled<E>(s.QT, LT, 16 * t + c16, 32 * kb, s.sGam),
+              ld_frag(s.DOT, LT, 16 * w + c16, 32 * kb));
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) mma(dh[t], ld_frag(s.WT, LT, 16 * t + c16, 32 * kb), uf[kb]);
+    }
+  }
+  __syncthreads();
+  return lam_c;
 }
+
+template <class E, int DK, int DV>
+__device__ void rev_load(f32x4 (&acc)[DK / 16], const float* src) {
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+#pragma unroll
+  for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[t][i] = src ? src[(16 * t + 4 * g + i) * DV + 16 * w + c16] : 0.f;
+}
+template <class E, int DK, int DV>
+__device__ void rev_store(const f32x4 (&acc)[DK / 16], float* dst, const float* add, bool use_acc) {
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+#pragma unroll
+  for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = (16 * t + 4 * g + i) * DV + 16 * w + c16;
+      dst[e] = (use_acc ? acc[t][i] : 0.f) + (add ? add[e] : 0.f);
+    }
+}
+
+template <class E, int DK, int DV>
+__global__ __launch_bounds__(DV / 16 * 64) void gdn_rev_kernel(RevParams p) {
+  __shared__ RevSmem<E, DK, DV> s;
+  using Sm = RevSmem<E, DK, DV>;
+  const SegDesc sd = p.segs[blockIdx.x];
+  const int h = blockIdx.y, n = sd.n;
+  const int seg0 = p.seg_first[n];
+  const int nseg = p.seg_first[n + 1] - seg0;
+  const int64_t seq0 = p.seq.start(n);
+  const int len = p.seq.len(n);
+  const size_t SS = (size_t)DK * DV;
+  const int64_t chunk0 = p.chunk_first[n];
+  E* dhs = static_cast<E*>(p.dhs);
+  const float* dhT = p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr;
+  float* dh0 = p.dh0 ? p.dh0 + ((size_t)n * p.H + h) * SS : nullptr;
+  f32x4 dh[DK / 16];
+
+  // T's strictly-upper blocks and the tiles of P^T above the diagonal are never written
+  for (int e = threadIdx.x; e < CH * CH; e += blockDim.x) {
+    s.T[(e >> 6) * Sm::LA + (e & 63)] = 0.f;
+    s.PT[(e >> 6) * Sm::LT + (e & 63)] = to_e<E>(0.f);
+  }
+  __syncthreads();
+
+  auto run = [&](int cb, int ce, int mode) {
+    float lam = 0.f;
+    for (int c = ce - 1; c >= cb; --c) {
+      const int64_t tok0 = seq0 + (int64_t)c * CH;
+      const int rows = min(CH, len - c * CH);
+      lam += rev_step<E, DK, DV>(s, p, tok0, rows, h, mode, dhs + ((chunk0 + c) * p.H + h) * SS, dh);
+    }
+    return lam;
+  };
+
+  if (p.phase == 1) {
+    rev_load<E, DK, DV>(dh, sd.s == nseg - 1 ? dhT : nullptr);
+    const float lam = run(sd.c_begin, sd.c_end, 0);
+    if (nseg == 1) {
+      if (dh0) rev_store<E, DK, DV>(dh, dh0, nullptr, true);
+    } else {
+      rev_store<E, DK, DV>(dh, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, nullptr, true);
+      if (threadIdx.x == 0) p.lam[(size_t)blockIdx.x * p.H + h] = lam;
+    }
+    return;
+  }
+
+  // ---- phase 3: propagate the true end-of-segment gradient into the segment's last chunks
+  if (nseg == 1 || sd.s == nseg - 1) return;
+  bool ok = true;
+  for (int j = 1; j + 1 < nseg; ++j) ok = ok && (p.lam[(size_t)(seg0 + j) * p.H + h] <= LN_EPS);
+  if (!ok) {
+    if (sd.s != 0) return;
+    rev_load<E, DK, DV>(dh, dhT);
+    run(0, (len + CH - 1) / CH, 0);
+    if (dh0) rev_store<E, DK, DV>(dh, dh0, nullptr, true);
+    return;
+  }
+  rev_load<E, DK, DV>(dh, p.bstate + ((size_t)(blockIdx.x + 1) * p.H + h) * SS);
+  float cum = 0.f;
+  int c = sd.c_end - 1;
+  for (; c >= sd.c_begin && cum > LN_EPS; --c) {
+    const int64_t tok0 = seq0 + (int64_t)c * CH;
+    const int rows = min(CH, len - c * CH);
+    cum += rev_step<E, DK, DV>(s, p, tok0, rows, h, R_CORR, dhs + ((chunk0 + c) * p.H + h) * SS, dh);
+  }
+  if (sd.s == 0 && dh0)
+    rev_store<E, DK, DV>(dh, dh0, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, c < sd.c_begin);
+}
+
+template <class E, int DK, int DV>
+hipError_t launch_rev_t(const RevParams& p, int nseg_total, hipStream_t st) {
+  hipLaunchKernelGGL((gdn_rev_kernel<E, DK, DV>), dim3(nseg_total, p.H), dim3(DV / 16 * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rev(int dtype, int DK, int DV, const RevParams& p, int nseg_total, hipStream_t st) {
+  if (dtype == 1) {
+    if (DK == 128 && DV == 128) return launch_rev_t<bf16, 128, 128>(p, nseg_total, st);
+    if (DK == 64 && DV == 64) return launch_rev_t<bf16, 64, 64>(p, nseg_total, st);
+    if (DK == 64 && DV == 128) return launch_rev_t<bf16, 64, 128>(p, nseg_total, st);
+    if (DK == 128 && DV == 64) return launch_rev_t<bf16, 128, 64>(p, nseg_total, st);
+  } else {
+    if (DK == 64 && DV == 64) return launch_rev_t<float, 64, 64>(p, nseg_total, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ======================================================================== chunk gradients
+
+template <class E, int DK, int DV>
+struct GradLayout {
+  static constexpr int PADE = 16 / (int)sizeof(E);
+  static constexpr int LK = DK + PADE;  // row-major [64][DK] E
+  static constexpr int LV = DV + PADE;  // row-major [64][DV] E
+  static constexpr int LT = CH + 4;     // transposed [D][64] E
+  static constexpr int LA = CH + 4;     // fp32 [64][64]
+  static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+  static constexpr int SLOT = cmax(cmax(CH * LK * (int)sizeof(E), CH * LV * (int)sizeof(E)),
+                                   cmax(DK * LT * (int)sizeof(E), CH * LA * 4));
+  static constexpr int NSLOT = 9;
+};
+
+template <class E, int DK, int DV>
+struct alignas(16) GradSmem {
+  using L = GradLayout<E, DK, DV>;
+  alignas(16) char slot[L::NSLOT][L::SLOT];
+  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH];
+  float pg[4][CH], pb[4][CH], pc[4][CH];
+  float pl[4], ph[4];
+  float GamC;
+};
+
+// slot roles
+enum { SK = 0, SKT = 1, SQ = 2, SV = 3, SDO = 4, ST = 5, SKD = 6, SP = 7, SDU = 8 };
+
+template <class E, int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_grad_kernel(GradParams p) {
+  using L = GradLayout<E, DK, DV>;
+  constexpr int NT = 256;
+  constexpr int LK = L::LK, LV = L::LV, LT = L::LT, LA = L::LA;
+  constexpr int CTK = DK / 64, CTV = DV / 64;  // 16-wide column tiles per wave
+  __shared__ GradSmem<E, DK, DV> s;
+  auto slotE = [&](int i) { return reinterpret_cast<E*>(s.slot[i]); };
+  auto slotF = [&](int i) { return reinterpret_cast<float*>(s.slot[i]); };
+
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const int2 ctab = p.chunk_tab[blockIdx.x];
+  const int n = ctab.x, jc = ctab.y, h = blockIdx.y, H = p.H;
+  const int len = p.seq.len(n);
+  const int64_t tok0 = p.seq.start(n) + (int64_t)jc * CH;
+  const int rows = min(CH, len - jc * CH);
+  const size_t SS = (size_t)DK * DV;
+  const E* hs = static_cast<const E*>(p.hs) + ((size_t)blockIdx.x * H + h) * SS;
+  const E* dhs = static_cast<const E*>(p.dhs) + ((size_t)blockIdx.x * H + h) * SS;
+  const int d0 = w * (DK / 4), n0 = w * (DV / 4);
+  const float scale = p.scale;
+
+  E* sK = slotE(SK);
+  E* sKT = slotE(SKT);
+  float* sT = slotF(ST);
+  float* sKD = slotF(SKD);
+  float* sP = slotF(SP);
+  E* sDU = slotE(SDU);
+
+  // ---- P1: staging; zero T and P (their upper parts are read as zeros)
+  {
+    const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
+    const E* k = static_cast<const E*>(p.k) + (tok0 * H + h) * DK;
+    const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
+    const E* d = static_cast<const E*>(p.dout) + (tok0 * H + h) * DV;
+    stage_tile<E, DK, NT>(k, (int64_t)H * DK, rows, sK, LK, sKT, LT);
+    stage_tile<E, DK, NT>(q, (int64_t)H * DK, rows, slotE(SQ), LK, nullptr, 0);
+    stage_tile<E, DV, NT>(v, (int64_t)H * DV, rows, slotE(SV), LV, nullptr, 0);
+    stage_tile<E, DV, NT>(d, (int64_t)H * DV, rows, slotE(SDO), LV, nullptr, 0);
+    for (int e = tid; e < CH * CH; e += NT) {
+      sT[(e >> 6) * LA + (e & 63)] = 0.f;
+      sP[(e >> 6) * LA + (e & 63)] = 0.f;
+    }
+    if (w == 0) {
+      const bool valid = l < rows;
+      const int64_t si = (tok0 + l) * H + h;
+      float gr = valid ? p.g[si] : 0.f;
+      float bt = valid ? to_f(static_cast<const E*>(p.beta)[si]) : 0.f;
+      float gm = wave_incl_scan(gr);
+      float gC = __shfl(gm, 63, 64);
+      float Gm = __expf(gm);
+      s.gam[l] = gm;
+      s.Gam[l] = Gm;
+      s.ek[l] = __expf(gC - gm);
+      s.beta[l] = bt;
+      s.bg[l] = bt * Gm;
+      if (l == 0) s.GamC = __expf(gC);
+    }
+  }
+  __syncthreads();
+
+  // ---- P2: KD = strict_lower(K K^T * D), P = (Q K^T) * M
+  for (int ti = w; ti < 20; ti += 4) {
+    const bool isq = ti >= 10;
+    const int tt = isq ? ti - 10 : ti;
+    int rt = 0;
+    while ((rt + 1) * (rt + 2) / 2 <= tt) ++rt;
+    const int ct = tt - rt * (rt + 1) / 2;
+    f32x4 acc = zero4();
+    const E* X = isq ? slotE(SQ) : sK;
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb)
+      mma(acc, ld_frag(X, LK, 16 * rt + c16, 32 * kb), ld_frag(sK, LK, 16 * ct + c16, 32 * kb));
+    const int c = 16 * ct + c16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rt + 4 * g + i;
+      const float dm = __expf(s.gam[r] - s.gam[c]);
+      if (!isq) sKD[r * LA + c] = (c < r) ? acc[i] * dm : 0.f;
+      else sP[r * LA + c] = (c <= r) ? acc[i] * dm : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- P3: T = (I + diag(beta) KD)^-1
+  solve_T(sKD, sT, s.beta);
+
+  // per-lane partial sums, reduced at the end
+  f32x4 rg[4], rb[4];  // dgam / dbeta contributions of rows 16rt+4g+i from this lane's columns
+  float cc[4] = {0.f, 0.f, 0.f, 0.f};  // dgam contributions of column 16ct+c16 from this lane's rows
+  float lastsum = 0.f, hdh = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) { rg[rt] = zero4(); rb[rt] = zero4(); }
+
+  // ---- P4: Ut = T diag(beta) V (own value columns), W = T diag(beta Gam) K -> slot V
+  Frag<E> vr[2][CTV];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int nt = 0; nt < CTV; ++nt) vr[kb][nt] = ld_fragC<E>(slotE(SV), LV, 32 * kb, n0 + 16 * nt + c16);
+  f32x4 u[4][CTV];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int nt = 0; nt < CTV; ++nt) {
+      u[rt][nt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) mma(u[rt][nt], ld_frag_scaled<E>(sT, LA, 16 * rt + c16, 32 * kb, s.beta), vr[kb][nt]);
+    }
+  __syncthreads();
+  {
+    E* sW = slotE(SV);
+    for (int ti = w; ti < 4 * (DK / 16); ti += 4) {
+      const int rt = ti / (DK / 16), dt = ti % (DK / 16);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        mma(acc, ld_frag_scaled<E>(sT, LA, 16 * rt + c16, 32 * kb, s.bg), ld_frag(sKT, LT, 16 * dt + c16, 32 * kb));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sW[(16 * rt + 4 * g + i) * LK + 16 * dt + c16] = to_e<E>(acc[i]);
+    }
+  }
+  __syncthreads();
+
+  // ---- P5: U = Ut - W h (own value columns), dU = diag(ek) K dh' + scale P^T dO
+  f32x4 du[4][CTV];
+  {
+    const E* sW = slotE(SV);
+#pragma unroll
+    for (int nt = 0; nt < CTV; ++nt) {
+      Frag<E> hk[DK / 32], dk_[DK / 32];
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        hk[kb] = ld_fragC<E>(hs, DV, 32 * kb, n0 + 16 * nt + c16);
+        dk_[kb] = ld_fragC<E>(dhs, DV, 32 * kb, n0 + 16 * nt + c16);
+      }
+      Frag<E> dor[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) dor[kb] = ld_fragC<E>(slotE(SDO), LV, 32 * kb, n0 + 16 * nt + c16);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        f32x4 wh = zero4(), kd = zero4();
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          mma(wh, ld_frag(sW, LK, 16 * rt + c16, 32 * kb), hk[kb]);
+          mma(kd, ld_frag(sK, LK, 16 * rt + c16, 32 * kb), dk_[kb]);
+        }
+        u[rt][nt] = u[rt][nt] - wh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kd[i] *= s.ek[16 * rt + 4 * g + i];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) mma(kd, ld_fragT<E>(sP, LA, 16 * rt + c16, 32 * kb, scale), dor[kb]);
+        du[rt][nt] = kd;
+      }
+    }
+  }
+  __syncthreads();  // W reads done: slot V becomes U
+  {
+    E* sU = slotE(SV);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < CTV; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * g + i, c = n0 + 16 * nt + c16;
+          sU[r * LV + c] = to_e<E>(u[rt][nt][i]);
+          sDU[r * LV + c] = to_e<E>(du[rt][nt][i]);
+        }
+  }
+  __syncthreads();
+
+  // ---- P6: GW = -dU h^T, dQ1 = dO h^T, Udh = U dh'^T (own key columns)
+  Frag<E> qr[2][CTK];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int dt = 0; dt < CTK; ++dt) qr[kb][dt] = ld_fragC<E>(slotE(SQ), LK, 32 * kb, d0 + 16 * dt + c16);
+  f32x4 gw[4][CTK], dq1[4][CTK], udh[4][CTK];
+#pragma unroll
+  for (int dt = 0; dt < CTK; ++dt) {
+    Frag<E> hn[DV / 32], dhn[DV / 32];
+#pragma unroll
+    for (int kb = 0; kb < DV / 32; ++kb) {
+      hn[kb] = ld_frag(hs, DV, d0 + 16 * dt + c16, 32 * kb);
+      dhn[kb] = ld_frag(dhs, DV, d0 + 16 * dt + c16, 32 * kb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hdh += frag_at(hn[kb], j) * frag_at(dhn[kb], j);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 a = zero4(), b = zero4(), c = zero4();
+#pragma unroll
+      for (int kb = 0; kb < DV / 32; ++kb) {
+        mma(a, ld_frag(sDU, LV, 16 * rt + c16, 32 * kb), hn[kb]);
+        mma(b, ld_frag(slotE(SDO), LV, 16 * rt + c16, 32 * kb), hn[kb]);
+        mma(c, ld_frag(slotE(SV), LV, 16 * rt + c16, 32 * kb), dhn[kb]);
+      }
+      gw[rt][dt] = zero4() - a;
+      dq1[rt][dt] = b;
+      udh[rt][dt] = c;
+      const int dcol = d0 + 16 * dt + c16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        const float qv = frag_at(qr[rt >> 1][dt], (rt & 1) * 4 + i);
+        const float kv = to_f(sK[r * LK + dcol]);
+        rg[rt][i] += scale * s.Gam[r] * qv * b[i] - s.ek[r] * kv * c[i];
+        lastsum += s.ek[r] * kv * c[i];
+      }
+    }
+  }
+  __syncthreads();  // Q reads done: slot Q becomes GW
+  {
+    E* sGW = slotE(SQ);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int dt = 0; dt < CTK; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sGW[(16 * rt + 4 * g + i) * LK + d0 + 16 * dt + c16] = to_e<E>(gw[rt][dt][i]);
+  }
+
+  // ---- P7: GP = scale (dO U^T) * [i <= r]; GP*P row/column sums; P -> GP * M
+  for (int ti = w; ti < 10; ti += 4) {
+    int rt = 0;
+    while ((rt + 1) * (rt + 2) / 2 <= ti) ++rt;
+    const int ct = ti - rt * (rt + 1) / 2;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < DV / 32; ++kb)
+      mma(acc, ld_frag(slotE(SDO), LV, 16 * rt + c16, 32 * kb), ld_frag(slotE(SV), LV, 16 * ct + c16, 32 * kb));
+    const int c = 16 * ct + c16;
+    float csum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rt + 4 * g + i;
+      const float gp = (c <= r) ? scale * acc[i] : 0.f;
+      const float pv = sP[r * LA + c];
+      const float gpp = gp * pv;
+      rg[rt][i] += gpp;
+      csum += gpp;
+      sP[r * LA + c] = (c <= r) ? gp * __expf(s.gam[r] - s.gam[c]) : 0.f;
+    }
+    cc[ct] -= csum;
+  }
+  __syncthreads();
+
+  // ---- P8: XW = T^T GW, XU = T^T dU; dV; row dots; dK partial
+  f32x4 dkacc[4][CTK];
+  {
+    Frag<E> gwf[2][CTK];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int dt = 0; dt < CTK; ++dt) pack_frag(gwf[kb][dt], gw[2 * kb][dt], gw[2 * kb + 1][dt]);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int dt = 0; dt < CTK; ++dt) {
+        f32x4 xw = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) mma(xw, ld_fragT<E>(sT, LA, 16 * rt + c16, 32 * kb, 1.f), gwf[kb][dt]);
+        const int dcol = d0 + 16 * dt + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * g + i;
+          const float kv = to_f(sK[r * LK + dcol]);
+          const float xk = xw[i] * kv;
+          rb[rt][i] += s.Gam[r] * xk;
+          rg[rt][i] += s.bg[r] * xk;
+          dkacc[rt][dt][i] = s.bg[r] * xw[i] + s.ek[r] * udh[rt][dt][i];
+        }
+      }
+  }
+  {
+    Frag<E> duf[2][CTV];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int nt = 0; nt < CTV; ++nt) pack_frag(duf[kb][nt], du[2 * kb][nt], du[2 * kb + 1][nt]);
+    E* dv = static_cast<E*>(p.dv) + (tok0 * H + h) * DV;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < CTV; ++nt) {
+        f32x4 xu = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) mma(xu, ld_fragT<E>(sT, LA, 16 * rt + c16, 32 * kb, 1.f), duf[kb][nt]);
+        const int ncol = n0 + 16 * nt + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * g + i;
+          rb[rt][i] += xu[i] * frag_at(vr[rt >> 1][nt], (rt & 1) * 4 + i);
+          if (r < rows) dv[(int64_t)r * H * DV + ncol] = to_e<E>(s.beta[r] * xu[i]);
+        }
+      }
+  }
+  // slot dO is free: reload V row-major there for G_T
+  {
+    const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
+    stage_tile<E, DV, NT>(v, (int64_t)H * DV, rows, slotE(SDO), LV, nullptr, 0);
+  }
+  __syncthreads();
+
+  // ---- P9: GT = dU V^T diag(beta) + GW K^T diag(beta Gam) -> slot V (fp32)
+  {
+    float* sGT = slotF(SV);
+    for (int ti = w; ti < 16; ti += 4) {
+      const int rt = ti >> 2, ct = ti & 3;
+      f32x4 a = zero4(), b = zero4();
+#pragma unroll
+      for (int kb = 0; kb < DV / 32; ++kb)
+        mma(a, ld_frag(sDU, LV, 16 * rt + c16, 32 * kb), ld_frag(slotE(SDO), LV, 16 * ct + c16, 32 * kb));
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb)
+        mma(b, ld_frag(slotE(SQ), LK, 16 * rt + c16, 32 * kb), ld_frag(sK, LK, 16 * ct + c16, 32 * kb));
+      const int c = 16 * ct + c16;
+      // U (slot V) must not be overwritten before every wave finished P7, which the barrier above ensures
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sGT[(16 * rt + 4 * g + i) * LA + c] = s.beta[c] * a[i] + s.bg[c] * b[i];
+    }
+  }
+  __syncthreads();
+
+  // ---- P10: Z = GT T^T (own 16 columns), GA = strict_lower(-T^T Z); E -> S = E + E^T (slot KD)
+  {
+    const float* sGT = slotF(SV);
+    f32x4 z[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      z[rt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        mma(z[rt], ld_frag(sGT, LA, 16 * rt + c16, 32 * kb), ld_frag(sT, LA, 16 * w + c16, 32 * kb));
+    }
+    Frag<float> zf[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) pack_frag(zf[kb], z[2 * kb], z[2 * kb + 1]);
+    const int c = 16 * w + c16;
+    float csum = 0.f;
+    f32x4 ga[4], kdv[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) mma(acc, ld_fragT<float>(sT, LA, 16 * rt + c16, 32 * kb, -1.f), zf[kb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        const float gav = (c < r) ? acc[i] : 0.f;
+        const float kd = sKD[r * LA + c];
+        const float gaa = gav * s.beta[r] * kd;
+        rg[rt][i] += gaa;
+        csum += gaa;
+        rb[rt][i] += gav * kd;
+        ga[rt][i] = gav;
+        kdv[rt][i] = kd;
+      }
+    }
+    cc[w] -= csum;
+    __syncthreads();  // every wave has read its KD entries: slot KD becomes S
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        if (c <= r) {
+          const float ev = s.beta[r] * ga[rt][i] * __expf(s.gam[r] - s.gam[c]);
+          sKD[r * LA + c] = ev;
+          if (c < r) sKD[c * LA + r] = ev;
+        }
+      }
+    (void)kdv;
+  }
+  __syncthreads();
+
+  // ---- P11: dQ = scale diag(Gam) dQ1 + GPM K ; dK += GPM^T Q + S K
+  {
+    E* dq = static_cast<E*>(p.dq) + (tok0 * H + h) * DK;
+    E* dk = static_cast<E*>(p.dk) + (tok0 * H + h) * DK;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int dt = 0; dt < CTK; ++dt) {
+        f32x4 a = zero4(), b = dkacc[rt][dt];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const Frag<E> kt = ld_frag(sKT, LT, d0 + 16 * dt + c16, 32 * kb);
+          mma(a, ld_frag_f32<E>(sP, LA, 16 * rt + c16, 32 * kb), kt);
+          mma(b, ld_frag_f32<E>(sKD, LA, 16 * rt + c16, 32 * kb), kt);
+          mma(b, ld_fragT<E>(sP, LA, 16 * rt + c16, 32 * kb, 1.f), qr[kb][dt]);
+        }
+        const int dcol = d0 + 16 * dt + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * g + i;
+          if (r < rows) {
+            dq[(int64_t)r * H * DK + dcol] = to_e<E>(scale * s.Gam[r] * dq1[rt][dt][i] + a[i]);
+            dk[(int64_t)r * H * DK + dcol] = to_e<E>(b[i]);
+          }
+        }
+      }
+  }
+
+  // ---- P12: reductions, dbeta, dg
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float a = rg[rt][i], b = rb[rt][i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        a += __shfl_xor(a, o, 64);
+        b += __shfl_xor(b, o, 64);
+      }
+      if (c16 == 0) {
+        s.pg[w][16 * rt + 4 * g + i] = a;
+        s.pb[w][16 * rt + 4 * g + i] = b;
+      }
+    }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    float a = cc[ct];
+    a += __shfl_xor(a, 16, 64);
+    a += __shfl_xor(a, 32, 64);
+    if (g == 0) s.pc[w][16 * ct + c16] = a;
+  }
+  {
+    const float a = wave_sum(lastsum), b = wave_sum(hdh);
+    if (l == 0) { s.pl[w] = a; s.ph[w] = b; }
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int r = l;
+    float dgm = 0.f, db = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      dgm += s.pg[ww][r] + s.pc[ww][r];
+      db += s.pb[ww][r];
+    }
+    if (r == CH - 1) {
+      float extra = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) extra += s.GamC * s.ph[ww] + s.pl[ww];
+      dgm += extra;
+    }
+    // dg_r = sum_{r' >= r} dgam_r'  (suffix scan = prefix scan over reversed lanes)
+    const float rev = __shfl(dgm, CH - 1 - r, 64);
+    const float sc = wave_incl_scan(rev);
+    const float dgv = __shfl(sc, CH - 1 - r, 64);
+    if (r < rows) {
+      const int64_t si = (tok0 + r) * H + h;
+      p.dg[si] = dgv;
+      static_cast<E*>(p.dbeta)[si] = to_e<E>(db);
+    }
+  }
+}
+
+template <class E, int DK, int DV>
+hipError_t launch_grad_t(const GradParams& p, int nchunk_total, hipStream_t st) {
+  hipLaunchKernelGGL((gdn_grad_kernel<E, DK, DV>), dim3(nchunk_total, p.H), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad(int dtype, int DK, int DV, const GradParams& p, int nchunk_total, hipStream_t st) {
+  if (dtype == 1) {
+    if (DK == 128 && DV == 128) return launch_grad_t<bf16, 128, 128>(p, nchunk_total, st);
+    if (DK == 64 && DV == 64) return launch_grad_t<bf16, 64, 64>(p, nchunk_total, st);
+    if (DK == 64 && DV == 128) return launch_grad_t<bf16, 64, 128>(p, nchunk_total, st);
+    if (DK == 128 && DV == 64) return launch_grad_t<bf16, 128, 64>(p, nchunk_total, st);
+  } else {
+    if (DK == 64 && DV == 64) return launch_grad_t<float, 64, 64>(p, nchunk_total, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

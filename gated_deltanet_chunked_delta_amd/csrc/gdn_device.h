@@ -121,6 +121,72 @@ template <> __device__ __forceinline__ float to_e<float>(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
 
+// Fragment of row `row` of an fp32 row-major LDS matrix, converted to E.
+template <class E>
+__device__ __forceinline__ Frag<E> ld_frag_f32(const float* base, int ld, int row, int k0) {
+  const int g = lane_id() >> 4;
+  const float* p = base + row * ld + k0 + 4 * g;
+  Frag<E> f;
+  pack_frag(f, *reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 16));
+  return f;
+}
+
+// Fragment of row m of M^T for an fp32 row-major M (so the k-slots walk down
+// column m of M), times sc, converted to E.
+template <class E>
+__device__ __forceinline__ Frag<E> ld_fragT(const float* M, int ld, int m, int k0, float sc) {
+  const int g = lane_id() >> 4;
+  const float* p = M + (k0 + 4 * g) * ld + m;
+  f32x4 a, b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = sc * p[j * ld];
+    b[j] = sc * p[(16 + j) * ld];
+  }
+  Frag<E> f;
+  pack_frag(f, a, b);
+  return f;
+}
+
+// Fragment whose k-slots walk down column `col` of a row-major E matrix (rows
+// k0+4g.., k0+16+4g..): the operand layout of an accumulator tile pair, read
+// from memory.  Works for LDS and global pointers.
+template <class E>
+__device__ __forceinline__ Frag<E> ld_fragC(const E* base, int64_t ld, int k0, int col) {
+  const int g = lane_id() >> 4;
+  const E* p = base + (int64_t)(k0 + 4 * g) * ld + col;
+  f32x4 a, b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = to_f(p[j * ld]);
+    b[j] = to_f(p[(16 + j) * ld]);
+  }
+  Frag<E> f;
+  pack_frag(f, a, b);
+  return f;
+}
+
+// Row fragment of a row-major E matrix with each k-slot multiplied by kscale[k].
+template <class E>
+__device__ __forceinline__ Frag<E> ld_frag_kscaled(const E* base, int ld, int row, int k0,
+                                                   const float* kscale) {
+  const int g = lane_id() >> 4;
+  const E* p = base + row * ld + k0 + 4 * g;
+  f32x4 a, b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = to_f(p[j]) * kscale[k0 + 4 * g + j];
+    b[j] = to_f(p[16 + j]) * kscale[k0 + 16 + 4 * g + j];
+  }
+  Frag<E> f;
+  pack_frag(f, a, b);
+  return f;
+}
+
+// Value of k-slot j of a fragment, as fp32.
+__device__ __forceinline__ float frag_at(const Frag<bf16>& f, int j) { return (float)f.v[j]; }
+__device__ __forceinline__ float frag_at(const Frag<float>& f, int j) { return j < 4 ? f.lo[j] : f.hi[j - 4]; }
+
 // Wave-wide inclusive prefix sum (64 lanes).
 __device__ __forceinline__ float wave_incl_scan(float x) {
   const int l = lane_id();
