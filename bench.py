@@ -1,0 +1,184 @@
+"""Benchmark: chunked Gated DeltaNet prefill forward + backward on one MI355X.
+
+One step = gdn_chunk_fwd + gdn_chunk_bwd (the whole hot path) over one batch of
+synthetic inputs already resident in HBM.  Default workload: B=1, T=32768,
+H=16, dk=dv=128, chunk 64, bf16 (inputs as in gdn_inputs, h0 = 0, dhT = 0).
+
+Prints ONE JSON line with tokens/s (B*T per step, all heads), the fraction of
+the bf16 MFMA peak reached by the step's algorithmic FLOPs, per-kernel times
+measured with HIP events on the launch stream during the timed region, a
+roofline entry for the dominant kernel, and the fp64 CPU oracle timed on a
+bounded sample of the same workload on this host's cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN chunked prefill fwd+bwd tokens/s and % bf16 MFMA peak, H=16 d=128 T=32k"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+CH = 64
+
+
+def flops_per_token_head(dk, dv, C=CH):
+    """Algorithmic FLOP model (full C x C tiles, no recompute)."""
+    fwd = 6 * dk * dv + 2 * C * (3 * dk + 2 * dv) + (2.0 / 3.0) * C * C
+    bwd = 12 * dk * dv + 4 * C * (3 * dk + 2 * dv) + 4 * C * C
+    return fwd, bwd
+
+
+def kernel_models(dk, dv, esz):
+    """Per token-head algorithmic FLOPs and HBM bytes each kernel is responsible for.
+
+    fwd:  the forward chunk algebra; reads q, k, v, g, beta and writes o.
+    rev:  the state-gradient chain (diag(Gam)Q)^T dO and W^T dU; reads q, k, g, beta, dO.
+    grad: the rest of the backward; reads q, k, v, dO, g, beta, writes dq, dk, dv, dbeta, dg.
+    The replay and boundary-correction launches are recomputation and count no
+    algorithmic work.
+    """
+    fwd, bwd = flops_per_token_head(dk, dv)
+    rev = 4 * dk * dv
+    return {
+        "fwd": (fwd, (2 * dk + dv) * esz + 4 + esz + dv * esz),
+        "rev": (rev, (2 * dk + dv) * esz + 4 + esz),
+        "grad": (bwd - rev, (2 * dk + 2 * dv) * esz + 4 + esz + (2 * dk + dv) * esz + esz + 4),
+    }
+
+
+def cpu_baseline(x_full, seconds_target=15.0):
+    """Time the fp64 oracle (forward, then backward) on the first tokens of the workload."""
+    from oracle import ref
+    import gdn_inputs  # noqa: F401
+
+    def run(Ts):
+        sl = lambda a: None if a is None else np.ascontiguousarray(a[:, :Ts])
+        q, k, v, g, b, do = (sl(a) for a in (x_full.q, x_full.k, x_full.v, x_full.g, x_full.beta, x_full.do))
+        t0 = time.perf_counter()
+        ref.fwd(q, k, v, g, b, x_full.scale)
+        ref.bwd(q, k, v, g, b, x_full.scale, do)
+        return time.perf_counter() - t0
+
+    T = x_full.q.shape[1]
+    Ts = min(T, 256)
+    dt = run(Ts)
+    while dt < seconds_target / 4 and Ts < T:
+        Ts = min(T, int(Ts * min(8.0, max(2.0, seconds_target / max(dt, 1e-3)))))
+        dt = run(Ts)
+    B, _, H, _ = x_full.q.shape
+    return {"value": B * Ts / dt, "unit": "tokens/s", "cores": ref.threads(), "kind": "oracle",
+            "sample": f"first {Ts} of {T} tokens (B={B}, all {H} heads), fp64 token recurrence forward "
+                      f"then its reverse-mode backward, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="metric_32k")
+    ap.add_argument("--direction", default="fwdbwd", choices=["fwdbwd", "fwd", "bwd"])
+    ap.add_argument("--cp-mode", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    log = lambda msg: print(f"[bench] {msg}", file=sys.stderr, flush=True)
+    log("importing torch")
+    import torch
+    import gdn_inputs
+    from gated_deltanet_chunked_delta_amd import binding as gb
+
+    dev = torch.device("cuda:0")
+    log(f"generating {args.config}")
+    x = gdn_inputs.config(args.config, grad=True)
+    B, T, H, dk = x.q.shape
+    dv = x.v.shape[-1]
+    dt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    t = lambda a, d=dt: torch.from_numpy(a).to(dev).to(d).contiguous()
+    q, k, v, beta, do = (t(a) for a in (x.q, x.k, x.v, x.beta, x.do))
+    g = t(x.g, torch.float32)
+    h0 = None if x.h0 is None else t(x.h0, torch.float32)
+    cu = None if x.cu_seqlens is None else torch.from_numpy(x.cu_seqlens).to(dev)
+    host = x.cu_seqlens
+    ntok = int(B * T) if cu is None else int(x.cu_seqlens[-1])
+
+    def step():
+        if args.direction in ("fwdbwd", "fwd"):
+            gb.gdn_chunk_fwd(q, k, v, g, beta, x.scale, h0=h0, cu_seqlens=cu, cu_seqlens_host=host,
+                             cp_mode=args.cp_mode)
+        if args.direction in ("fwdbwd", "bwd"):
+            gb.gdn_chunk_bwd(q, k, v, g, beta, x.scale, do, h0=h0, cu_seqlens=cu, cu_seqlens_host=host,
+                             cp_mode=args.cp_mode, need_dh0=h0 is not None)
+
+    log("warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    gb.gdn_profile_reset()
+    gb.gdn_profile_enable(True)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gb.gdn_profile_enable(False)
+    prof = gb.gdn_profile_read()
+    log(f"timed {args.steps} steps")
+    ms = e0.elapsed_time(e1) / args.steps
+
+    fwd_f, bwd_f = flops_per_token_head(dk, dv)
+    per_th = {"fwdbwd": fwd_f + bwd_f, "fwd": fwd_f, "bwd": bwd_f}[args.direction]
+    tflops = per_th * ntok * H / (ms * 1e-3) / 1e12
+    kernels = {name: {"avg_ms": tot / n, "launches_per_step": n / args.steps}
+               for name, (tot, n) in prof.items()}
+
+    # roofline entry for the kernel with the largest share of the step
+    esz = 2 if x.dtype == "bf16" else 4
+    models = kernel_models(dk, dv, esz)
+    dom = max(prof, key=lambda nm: prof[nm][0])
+    avg_s = prof[dom][0] / prof[dom][1] * 1e-3
+    f_th, b_th = models.get(dom, (0.0, 0.0))
+    units = ntok * H
+    flop_rate = f_th * units / avg_s / 1e12
+    byte_rate = b_th * units / avg_s / 1e9
+    if f_th / max(b_th, 1) >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": flop_rate, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": byte_rate, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    roof["algorithmic_per_launch"] = {"flop": f_th * units, "bytes": b_th * units}
+
+    out = {
+        "metric": METRIC, "value": ntok * 1e3 / ms, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if x.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.config, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": CH,
+                   "direction": args.direction, "cp_mode": args.cp_mode, "tokens_per_step": ntok},
+        "tflops": tflops, "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "kernels": kernels, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

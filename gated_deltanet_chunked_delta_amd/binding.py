@@ -62,6 +62,12 @@ def lib():
         L.gdn_chunk_fwd.restype = ctypes.c_int
         L.gdn_chunk_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
         L.gdn_chunk_bwd.restype = ctypes.c_int
+        L.gdn_profile_enable.argtypes = [ctypes.c_int]
+        L.gdn_profile_enable.restype = ctypes.c_int
+        L.gdn_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                       ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+        L.gdn_profile_read.restype = ctypes.c_int
+        L.gdn_profile_reset.restype = None
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_abi_version.restype = ctypes.c_int
         _lib = L
@@ -184,6 +190,28 @@ def gdn_chunk_bwd(q, k, v, g, beta, scale: float, do, h0=None, dhT=None, cu_seql
     _check(L.gdn_chunk_bwd(ctypes.byref(args), _vp(_stream(q.device))))
     del keep
     return dq, dk, dv, dg, dbeta, dh0
+
+
+def gdn_profile_enable(on: bool) -> bool:
+    """Turn per-kernel event timing on or off; returns the previous setting."""
+    return bool(lib().gdn_profile_enable(1 if on else 0))
+
+
+def gdn_profile_reset() -> None:
+    lib().gdn_profile_reset()
+
+
+def gdn_profile_read() -> dict:
+    """{kernel name: (total ms, launches)} accumulated since the last reset (waits for the events)."""
+    L = lib()
+    cap = 32
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_double * cap)()
+    cnt = (ctypes.c_int * cap)()
+    n = L.gdn_profile_read(cap, names, ms, cnt)
+    if n < 0:
+        _check(4)
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(min(n, cap))}
 
 
 def exported_symbols(header: Optional[str] = None) -> Sequence[str]:

@@ -155,6 +155,33 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus) {
 template <class T>
 T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
 
+// ---------------------------------------------------------------- per-kernel timing
+struct ProfRec { const char* name; hipEvent_t a, b; };
+struct ProfTotal { const char* name; double ms; int n; };
+bool g_prof = false;
+std::vector<ProfRec> g_pending;
+std::vector<hipEvent_t> g_pool;
+std::vector<ProfTotal> g_totals;
+
+hipEvent_t prof_event() {
+  if (!g_pool.empty()) { hipEvent_t e = g_pool.back(); g_pool.pop_back(); return e; }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch through f() on stream s, bracketed by events when timing is enabled.
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F f) {
+  if (!g_prof) return f();
+  ProfRec r{name, prof_event(), prof_event()};
+  if (r.a) hipEventRecord(r.a, s);
+  hipError_t e = f();
+  if (r.b) hipEventRecord(r.b, s);
+  if (r.a && r.b) g_pending.push_back(r);
+  return e;
+}
+
 gdn_status hip_fail(hipError_t e, const char* what) {
   return fail(GDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -171,6 +198,46 @@ gdn::SeqInfo seq_info(const gdn_common_args& a) {
 extern "C" {
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+int gdn_profile_enable(int on) {
+  const int was = g_prof ? 1 : 0;
+  g_prof = on != 0;
+  return was;
+}
+
+void gdn_profile_reset(void) {
+  for (ProfRec& r : g_pending) {
+    hipEventSynchronize(r.b);
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_pending.clear();
+  g_totals.clear();
+}
+
+int gdn_profile_read(int max, const char** names, double* ms, int* launches) {
+  int rc = 0;
+  for (ProfRec& r : g_pending) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) rc = -1;
+    ProfTotal* tot = nullptr;
+    for (ProfTotal& x : g_totals)
+      if (std::strcmp(x.name, r.name) == 0) tot = &x;
+    if (!tot) { g_totals.push_back({r.name, 0.0, 0}); tot = &g_totals.back(); }
+    tot->ms += t;
+    tot->n += 1;
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_pending.clear();
+  if (rc) { fail(GDN_E_HIP, "profile: event query failed"); return -1; }
+  for (int i = 0; i < (int)g_totals.size() && i < max; ++i) {
+    if (names) names[i] = g_totals[i].name;
+    if (ms) ms[i] = g_totals[i].ms;
+    if (launches) launches[i] = g_totals[i].n;
+  }
+  return (int)g_totals.size();
+}
 
 const char* gdn_last_error(void) { return g_err.c_str(); }
 
@@ -201,8 +268,10 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* ws = a.workspace;
   gdn::SeqInfo sq = seq_info(a);
-  hipError_t e = gdn::launch_plan(sq, pl.N, pl.segc, at<int>(ws, pl.o_chunk_first), at<int>(ws, pl.o_seg_first),
-                                  at<gdn::SegDesc>(ws, pl.o_segs), at<int2>(ws, pl.o_chunk_tab), s);
+  hipError_t e = timed("plan", s, [&] {
+    return gdn::launch_plan(sq, pl.N, pl.segc, at<int>(ws, pl.o_chunk_first), at<int>(ws, pl.o_seg_first),
+                            at<gdn::SegDesc>(ws, pl.o_segs), at<int2>(ws, pl.o_chunk_tab), s);
+  });
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   gdn::FwdParams p{};
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta; p.h0 = a.h0;
@@ -214,11 +283,11 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
   p.hs = nullptr;
   p.phase = 1;
-  e = gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s);
+  e = timed("fwd", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   if (pl.cp) {
     p.phase = 3;
-    e = gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s);
+    e = timed("fwd_corr", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
     if (e != hipSuccess) return hip_fail(e, "forward correction launch");
   }
   return GDN_OK;
@@ -244,8 +313,10 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* ws = a.workspace;
   gdn::SeqInfo sq = seq_info(a);
-  hipError_t e = gdn::launch_plan(sq, pl.N, pl.segc, at<int>(ws, pl.o_chunk_first), at<int>(ws, pl.o_seg_first),
-                                  at<gdn::SegDesc>(ws, pl.o_segs), at<int2>(ws, pl.o_chunk_tab), s);
+  hipError_t e = timed("plan", s, [&] {
+    return gdn::launch_plan(sq, pl.N, pl.segc, at<int>(ws, pl.o_chunk_first), at<int>(ws, pl.o_seg_first),
+                            at<gdn::SegDesc>(ws, pl.o_segs), at<int2>(ws, pl.o_chunk_tab), s);
+  });
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   // 1. forward replay: state at every chunk start
   gdn::FwdParams p{};
@@ -258,11 +329,11 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
   p.hs = at<void>(ws, pl.o_hs);
   p.phase = 1;
-  e = gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s);
+  e = timed("replay", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "replay launch");
   if (pl.cp) {
     p.phase = 3;
-    e = gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s);
+    e = timed("replay_corr", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
     if (e != hipSuccess) return hip_fail(e, "replay correction launch");
   }
   // 2. reverse chain: state gradient at every chunk end, dh0
@@ -274,11 +345,11 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   r.lam = pl.cp ? at<float>(ws, pl.o_lam2) : nullptr;
   r.dhs = at<void>(ws, pl.o_dhs);
   r.phase = 1;
-  e = gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s);
+  e = timed("rev", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "reverse launch");
   if (pl.cp) {
     r.phase = 3;
-    e = gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s);
+    e = timed("rev_corr", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });
     if (e != hipSuccess) return hip_fail(e, "reverse correction launch");
   }
   // 3. chunk-parallel gradients
@@ -289,7 +360,7 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
     gp.dq = args->dq; gp.dk = args->dk; gp.dv = args->dv; gp.dbeta = args->dbeta; gp.dg = args->dg;
     gp.scale = a.scale; gp.H = a.H; gp.seq = sq;
     gp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);
-    e = gdn::launch_grad(a.dtype, a.Dk, a.Dv, gp, pl.nchunk, s);
+    e = timed("grad", s, [&] { return gdn::launch_grad(a.dtype, a.Dk, a.Dv, gp, pl.nchunk, s); });
     if (e != hipSuccess) return hip_fail(e, "gradient launch");
   }
   return GDN_OK;

@@ -1,12 +1,14 @@
 // gdn_fwd.hip -- forward chunk loop of the gated delta rule on gfx950.
 //
-// One workgroup owns one (segment, head): a run of consecutive 64-token chunks
-// of one sequence.  Wave w of the workgroup keeps columns [16w, 16w+16) of the
-// fp32 state h = S^T (Dk x Dv) in accumulator registers for the whole run, so
+// One workgroup (4 waves, one per SIMD) owns one (segment, head): a run of
+// consecutive 64-token chunks of one sequence.  Wave w keeps columns
+// [w Dv/4, (w+1) Dv/4) of the fp32 state h = S^T (Dk x Dv) in accumulator
+// registers for the whole run, so
 // the serial chain U = Ut - W h, h' = Gam_C h + Kt^T U never leaves registers.
 // Everything that does not depend on h (decay cumsum, the decay-masked K K^T,
 // the unit-lower-triangular solve, W and Ut, the masked Q K^T) is computed
-// per chunk from LDS tiles by all waves together.
+// per chunk from LDS tiles by all waves together, while the next chunk's
+// q/k/v/g/beta are already on their way from HBM into registers.
 //
 // Chunk algebra (rows r, i of one chunk; gam = inclusive cumsum of g):
 //   A  = strict_lower(diag(beta) (K K^T) * exp(gam_r - gam_i))
@@ -31,6 +33,11 @@
 // makes happen after a few chunks.  H_s = b_{s-1} is exact to that bound only
 // if every interior segment decays below it; a workgroup checks that from the
 // Lambda_s values and otherwise the (sequence, head) is recomputed serially.
+//
+// The same kernels, without an output, replay the forward for the backward
+// pass and store the state at every chunk start.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_tiles.h"
@@ -39,10 +46,10 @@ namespace gdn {
 
 template <class E, int DK, int DV>
 struct alignas(16) FwdSmem {
-  static constexpr int LQ = ldpad<E>(DK);  // sQ, sK, sW row stride
-  static constexpr int LT = ldpad<E>(CH);  // transposed tiles and 64x64 E matrices
-  static constexpr int LA = CH + 4;        // fp32 64x64 matrices
-  static constexpr int LO = ldpad<E>(DV);  // output staging
+  static constexpr int LQ = ldpad<E>(DK);                 // sQ, sK, sW row stride
+  static constexpr int LT = ldpad<E>(CH);                 // transposed tiles, P
+  static constexpr int LA = CH + 4;                       // fp32 64x64 matrices
+  static constexpr int LO = DV + 16 / (int)sizeof(E);     // output staging (16-byte rows)
   static constexpr int A_BYTES = CH * LA * 4;
   static constexpr int O_BYTES = CH * LO * (int)sizeof(E);
   E Q[CH * LQ];
@@ -56,260 +63,410 @@ struct alignas(16) FwdSmem {
     float A[CH * LA];
     E O[(O_BYTES > A_BYTES ? O_BYTES : A_BYTES) / sizeof(E)];
   };
-  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], graw[CH], lam[CH];
+  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], lam[CH];
   float GamC;
+};
+
+// ------------------------------------------------------------------ prefetch
+
+// The raw tiles of one chunk, held in registers between the global load and
+// the LDS store so that the next chunk's loads overlap the current chunk's
+// compute.  K and V move as 4-row x 16-byte blocks (K is stored row-major and
+// transposed, V transposed); Q as single 16-byte vectors (row-major).
+template <class E, int DK, int DV, int NT, bool NEED_Q, bool NEED_V>
+struct TileLoader {
+  static constexpr int VEC = 16 / (int)sizeof(E);
+  static constexpr int NBK = (CH / 4) * (DK / VEC);
+  static constexpr int NBV = NEED_V ? (CH / 4) * (DV / VEC) : 0;
+  static constexpr int NB = (NBK + NBV + NT - 1) / NT;     // blocks per thread
+  static constexpr int NQV = NEED_Q ? (CH * (DK / VEC) + NT - 1) / NT : 0;
+  typedef E vec_t __attribute__((__vector_size__(16)));
+  vec_t blk[NB > 0 ? NB : 1][4];
+  vec_t qv[NQV > 0 ? NQV : 1];
+  float gr;
+  E be;
+  int nrow;
+
+  __device__ __forceinline__ void load(const FwdParams& p, int64_t tok0, int rows, int h) {
+    load_kv(p, tok0, rows, h);
+    load_q(p, tok0, rows, h);
+  }
+
+  // K / V blocks and g / beta
+  __device__ __forceinline__ void load_kv(const FwdParams& p, int64_t tok0, int rows, int h) {
+    const int H = p.H;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int id = threadIdx.x + b * NT;
+      if (id < NBK + NBV) {
+        const bool isk = id < NBK;
+        const int loc = isk ? id : id - NBK;
+        const int D = isk ? DK : DV;
+        const int r0 = (loc / (D / VEC)) * 4, c0 = (loc % (D / VEC)) * VEC;
+        const E* src = static_cast<const E*>(isk ? p.k : p.v) + (tok0 * H + h) * D + c0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (r0 + j < rows) blk[b][j] = *reinterpret_cast<const vec_t*>(src + (int64_t)(r0 + j) * H * D);
+          else
+            for (int e = 0; e < VEC; ++e) blk[b][j][e] = (E)0.f;
+        }
+      }
+    }
+    if (threadIdx.x < 64) {
+      // unconditional load of a clamped row; rows past the chunk end are masked when used
+      const int l = threadIdx.x;
+      const int64_t si = (tok0 + min(l, rows - 1)) * H + h;
+      gr = p.g[si];
+      be = static_cast<const E*>(p.beta)[si];
+      nrow = rows;
+    }
+  }
+
+  __device__ __forceinline__ void load_q(const FwdParams& p, int64_t tok0, int rows, int h) {
+    const int H = p.H;
+#pragma unroll
+    for (int v = 0; v < NQV; ++v) {
+      const int id = threadIdx.x + v * NT;
+      if (id < CH * (DK / VEC)) {
+        const int r = id / (DK / VEC), c0 = (id % (DK / VEC)) * VEC;
+        if (r < rows) qv[v] = *reinterpret_cast<const vec_t*>(static_cast<const E*>(p.q) + ((tok0 + r) * H + h) * DK + c0);
+        else
+          for (int e = 0; e < VEC; ++e) qv[v][e] = (E)0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ float g_at(int l) const { return l < nrow ? gr : 0.f; }
+  __device__ __forceinline__ float beta_at(int l) const { return l < nrow ? to_f(be) : 0.f; }
+
+  template <class S>
+  __device__ __forceinline__ void store(S& s) const {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int id = threadIdx.x + b * NT;
+      if (id < NBK + NBV) {
+        const bool isk = id < NBK;
+        const int loc = isk ? id : id - NBK;
+        const int D = isk ? DK : DV;
+        const int r0 = (loc / (D / VEC)) * 4, c0 = (loc % (D / VEC)) * VEC;
+        E* dT = isk ? s.KT : s.VT;
+        if (isk) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4)
+              st4<E>(s.K + (r0 + j) * S::LQ + c0 + e, blk[b][j][e], blk[b][j][e + 1], blk[b][j][e + 2],
+                     blk[b][j][e + 3]);
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          st4<E>(dT + (c0 + e) * S::LT + r0, blk[b][0][e], blk[b][1][e], blk[b][2][e], blk[b][3][e]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NQV; ++v) {
+      const int id = threadIdx.x + v * NT;
+      if (id < CH * (DK / VEC)) {
+        const int r = id / (DK / VEC), c0 = (id % (DK / VEC)) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4)
+          st4<E>(s.Q + r * S::LQ + c0 + e, qv[v][e], qv[v][e + 1], qv[v][e + 2], qv[v][e + 3]);
+      }
+    }
+  }
 };
 
 // ------------------------------------------------------------------ one chunk
 
-enum : int { M_WRITE_O = 1, M_STORE_H = 2, M_CORR = 4 };
-
-template <class E, int DK, int DV>
-struct FwdCtx {
-  static constexpr int NW = DV / 16;
+// OUT:  forward (writes o) vs replay (stores the chunk-start state instead).
+// CORR: boundary correction -- the state is a propagated difference; the values
+//       v do not enter, outputs / stored states are incremented.
+template <class E, int DK, int DV, bool OUT, bool CORR>
+struct Chunk {
+  static constexpr int NW = 4;
   static constexpr int NT = NW * 64;
-  static constexpr int KT_ = DK / 16;  // state row tiles per wave
+  static constexpr int NTW = DV / 64;  // 16-column tiles of the state per wave
   using S = FwdSmem<E, DK, DV>;
-};
+  using Loader = TileLoader<E, DK, DV, NT, OUT, !CORR>;
+  using Acc = f32x4[DK / 16][DV / 64];
 
-// Process one chunk.  hacc: this wave's state columns (state at chunk start on
-// entry, at chunk end on exit).  Returns the chunk's log-bound Lambda_c.
-template <class E, int DK, int DV>
-__device__ float chunk_step(FwdSmem<E, DK, DV>& s, const FwdParams& p, int64_t tok0, int rows,
-                            int h, int mode, E* hs_chunk, f32x4 (&hacc)[DK / 16]) {
-  using C = FwdCtx<E, DK, DV>;
-  using Sm = FwdSmem<E, DK, DV>;
-  constexpr int NW = C::NW, NT = C::NT;
-  constexpr int LQ = Sm::LQ, LT = Sm::LT, LA = Sm::LA, LO = Sm::LO;
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
-  const bool corr = mode & M_CORR;
-  const bool need_q = mode & M_WRITE_O;
-  const bool need_v = !corr;
-  const int H = p.H;
+  // Process the chunk whose tiles `ld` holds; prefetch the next chunk (if any)
+  // into `ld`.  hacc: this wave's state columns (chunk start on entry, chunk end
+  // on exit).  Returns the chunk's log-bound Lambda_c.
+  __device__ static float step(S& s, const FwdParams& p, Loader& ld, int64_t tok0, int rows,
+                               int64_t ntok0, int nrows, int h, E* hs_chunk, f32x4 (&hacc)[DK / 16][DV / 64]) {
+    constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA, LO = S::LO;
+    const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+    const int H = p.H;
+    const int n0 = w * (DV / 4);  // first state column of this wave
 
-  // ---- 0. per-chunk start state out (backward replay)
-  if (hs_chunk) {
-#pragma unroll
-    for (int t = 0; t < DK / 16; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        E* dst = hs_chunk + (16 * t + 4 * g + i) * DV + 16 * w + c16;
-        float val = hacc[t][i];
-        if (corr) val += to_f(*dst);
-        *dst = to_e<E>(val);
-      }
-  }
-
-  // ---- 1. staging
-  {
-    const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
-    const E* k = static_cast<const E*>(p.k) + (tok0 * H + h) * DK;
-    const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
-    stage_tile<E, DK, NT>(k, (int64_t)H * DK, rows, s.K, LQ, s.KT, LT);
-    if (need_q) stage_tile<E, DK, NT>(q, (int64_t)H * DK, rows, s.Q, LQ, nullptr, 0);
-    if (need_v) stage_tile<E, DV, NT>(v, (int64_t)H * DV, rows, nullptr, 0, s.VT, LT);
+    // ---- 1. tiles into LDS, scalars, prefetch of the next chunk
+    ld.store(s);
     if (w == 0) {
-      const bool valid = l < rows;
-      const int64_t si = (tok0 + l) * H + h;
-      float gr = valid ? p.g[si] : 0.f;
-      float bt = valid ? to_f(static_cast<const E*>(p.beta)[si]) : 0.f;
-      float gm = wave_incl_scan(gr);
-      float gC = __shfl(gm, 63, 64);
-      float Gm = __expf(gm);
+      const float gr = ld.g_at(l), bt = ld.beta_at(l);
+      const float gm = wave_incl_scan(gr);
+      const float gC = __shfl(gm, 63, 64);
+      const float Gm = __expf(gm);
       s.gam[l] = gm;
       s.Gam[l] = Gm;
       s.ek[l] = __expf(gC - gm);
       s.beta[l] = bt;
       s.bg[l] = bt * Gm;
-      s.graw[l] = gr;
+      // per-token log-bound; the log max(1, |1 - beta |k|^2|) part is added with K K^T
+      s.lam[l] = gr;
       if (l == 0) s.GamC = __expf(gC);
     }
-  }
-  __syncthreads();
-
-  // ---- 2. K K^T (lower tiles) -> A, lambda
-  for (int ti = w; ti < 10; ti += NW) {
-    int rt = 0;
-    while ((rt + 1) * (rt + 2) / 2 <= ti) ++rt;
-    const int ct = ti - rt * (rt + 1) / 2;
-    f32x4 acc = zero4();
+    if (!OUT && hs_chunk) {
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb)
-      mma(acc, ld_frag(s.K, LQ, 16 * rt + c16, 32 * kb), ld_frag(s.K, LQ, 16 * ct + c16, 32 * kb));
-    const int c = 16 * ct + c16;
+      for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * g + i;
-      float val = (c < r) ? s.beta[r] * acc[i] * __expf(s.gam[r] - s.gam[c]) : 0.f;
-      s.A[r * LA + c] = val;
-      if (r == c) s.lam[r] = s.graw[r] + __logf(fmaxf(1.f, fabsf(1.f - s.beta[r] * acc[i])));
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            E* dst = hs_chunk + (16 * t + 4 * g + i) * DV + n0 + 16 * nt + c16;
+            float val = hacc[t][nt][i];
+            if (CORR) val += to_f(*dst);
+            *dst = to_e<E>(val);
+          }
     }
-  }
-  __syncthreads();
-  // lane 0's sum: every wave reduces the same values in the same order, so the
-  // value (and the loop decisions taken on it) is identical across the workgroup
-  const float lam_c = __shfl(wave_sum(s.lam[l]), 0, 64);
+    __syncthreads();
 
-  // ---- 3a. diagonal solve (wave 0) || Q K^T -> P and Q h (other waves)
-  f32x4 qh[4];
-  if (w == 0) solve_diag(s.A, s.T);
-  if (need_q) {
-    const int nw = NW > 1 ? NW - 1 : 1, w0 = NW > 1 ? w - 1 : w;
-    if (w0 >= 0) {
-      for (int ti = w0; ti < 10; ti += nw) {
-        int rt = 0;
-        while ((rt + 1) * (rt + 2) / 2 <= ti) ++rt;
-        const int ct = ti - rt * (rt + 1) / 2;
-        f32x4 acc = zero4();
+    // ---- 2. K K^T -> A (waves 0, 1) and Q K^T -> P (waves 2, 3).  Each wave takes a
+    //         pair of row tiles {0, 3} or {1, 2} (5 lower tiles); its A-side
+    //         fragments are loaded once per row.  Waves 0 and 1 then solve the two
+    //         diagonal blocks of T they produced.
+    {
+      const bool rows03 = (w & 1) == 0;
+      const bool isq = w >= 2;
+      if (!isq || OUT) {
+        const E* X = isq ? s.Q : s.K;
+        auto row = [&](auto RT_) {
+          constexpr int RT = decltype(RT_)::value;
+          Frag<E> xa[DK / 32];
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb)
-          mma(acc, ld_frag(s.Q, LQ, 16 * rt + c16, 32 * kb), ld_frag(s.K, LQ, 16 * ct + c16, 32 * kb));
-        const int c = 16 * ct + c16;
+          for (int kb = 0; kb < DK / 32; ++kb) xa[kb] = ld_frag(X, LQ, 16 * RT + c16, 32 * kb);
+          f32x4 gr4 = *reinterpret_cast<const f32x4*>(&s.gam[16 * RT + 4 * g]);
+          f32x4 br4 = *reinterpret_cast<const f32x4*>(&s.beta[16 * RT + 4 * g]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * g + i;
-          float val = (c <= r) ? acc[i] * __expf(s.gam[r] - s.gam[c]) : 0.f;
-          s.P[r * LT + c] = to_e<E>(val);
-        }
+          for (int ct = 0; ct <= RT; ++ct) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) mma(acc, xa[kb], ld_frag(s.K, LQ, 16 * ct + c16, 32 * kb));
+            const int c = 16 * ct + c16;
+            const float gc = s.gam[c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 16 * RT + 4 * g + i;
+              const float dm = __expf(gr4[i] - gc);
+              if (!isq) {
+                s.A[r * LA + c] = (c < r) ? br4[i] * acc[i] * dm : 0.f;
+                if (ct == RT && r == c) s.lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
+              } else {
+                s.P[r * LT + c] = to_e<E>((c <= r) ? acc[i] * dm : 0.f);
+              }
+            }
+          }
+        };
+        if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
+        else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
+        if (!isq) solve_diag_pair(s.A, s.T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
       }
     }
-    // Q h for this wave's columns
-    Frag<E> hf[DK / 32];
+    __syncthreads();
+    // lane 0's sum: every wave reduces the same values in the same order, so the
+    // value (and the loop decisions taken on it) is identical across the workgroup
+    const float lam_c = __shfl(wave_sum(s.lam[l]), 0, 64);
+
+    // next chunk's k, v, g, beta start their way from HBM (q follows later,
+    // which keeps the prefetch registers out of the busiest stretch)
+    if (nrows > 0) ld.load_kv(p, ntok0, nrows, h);
+    if (OUT && nrows > 0) ld.load_q(p, ntok0, nrows, h);
+
+    // ---- 3. off-diagonal blocks of T
+    solve_level1(s.A, s.T, w, nullptr);
+    __syncthreads();
+    solve_level2(s.A, s.T, w, nullptr);
+    __syncthreads();
+
+    // ---- 4. -W = -T diag(beta Gam) K for row tile w (all key columns);
+    //         Q h and Ut = T diag(beta) V for this wave's state columns.
+    {
+      Frag<E> xw[2];
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) pack_frag(hf[kb], hacc[2 * kb], hacc[2 * kb + 1]);
+      for (int kb = 0; kb < 2; ++kb) xw[kb] = ld_frag_scaled<E>(s.T, LA, 16 * w + c16, 32 * kb, s.bg);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      qh[rt] = zero4();
+      for (int ct = 0; ct < DK / 16; ++ct) {
+        f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) mma(qh[rt], ld_frag(s.Q, LQ, 16 * rt + c16, 32 * kb), hf[kb]);
+        for (int kb = 0; kb < 2; ++kb) mma(acc, xw[kb], ld_frag(s.KT, LT, 16 * ct + c16, 32 * kb));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.W[(16 * w + 4 * g + i) * LQ + 16 * ct + c16] = to_e<E>(-acc[i]);
+      }
     }
-  }
-  __syncthreads();
-
-  // ---- 3b. off-diagonal solve levels
-  if (w < 3) solve_offdiag(s.A, s.T, w + 1, w);
-  __syncthreads();
-  if (w < 2) solve_offdiag(s.A, s.T, w + 2, w);
-  __syncthreads();
-  if (w == 0) solve_offdiag(s.A, s.T, 3, 0);
-  __syncthreads();
-
-  // ---- 5. -W = -T diag(beta Gam) K  (all waves) ; Ut = T diag(beta) V (own columns)
-  for (int ti = w; ti < 4 * (DK / 16); ti += NW) {
-    const int rt = ti / (DK / 16), ct = ti % (DK / 16);
-    f32x4 acc = zero4();
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 u[4][NTW];
+    {
+      Frag<E> yv[NTW][2];
+      if (!CORR) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      mma(acc, ld_frag_scaled<E>(s.T, LA, 16 * rt + c16, 32 * kb, s.bg), ld_frag(s.KT, LT, 16 * ct + c16, 32 * kb));
+        for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s.W[(16 * rt + 4 * g + i) * LQ + 16 * ct + c16] = to_e<E>(-acc[i]);
-  }
-  f32x4 u[4];
+          for (int kb = 0; kb < 2; ++kb) yv[nt][kb] = ld_frag(s.VT, LT, n0 + 16 * nt + c16, 32 * kb);
+      }
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    u[rt] = zero4();
-    if (need_v) {
+      for (int rt = 0; rt < 4; ++rt) {
+        Frag<E> xb[2];
+        if (!CORR) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        mma(u[rt], ld_frag_scaled<E>(s.T, LA, 16 * rt + c16, 32 * kb, s.beta), ld_frag(s.VT, LT, 16 * w + c16, 32 * kb));
-    }
-  }
-  __syncthreads();
-
-  // ---- 6. state chain: U = Ut - W h ; O ; h' = GamC h + K^T (ek * U)
-  {
-    Frag<E> hf[DK / 32];
+          for (int kb = 0; kb < 2; ++kb) xb[kb] = ld_frag_scaled<E>(s.T, LA, 16 * rt + c16, 32 * kb, s.beta);
+        }
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) pack_frag(hf[kb], hacc[2 * kb], hacc[2 * kb + 1]);
+        for (int nt = 0; nt < NTW; ++nt) {
+          u[rt][nt] = zero4();
+          if (!CORR) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) mma(u[rt], ld_frag(s.W, LQ, 16 * rt + c16, 32 * kb), hf[kb]);
-  }
-  if (need_q) {
-    Frag<E> uf[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) pack_frag(uf[kb], u[2 * kb], u[2 * kb + 1]);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = qh[rt][i] * s.Gam[16 * rt + 4 * g + i];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mma(o, ld_frag(s.P, LT, 16 * rt + c16, 32 * kb), uf[kb]);
-      o = o * p.scale;
-      if (!corr) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s.O[(16 * rt + 4 * g + i) * LO + 16 * w + c16] = to_e<E>(o[i]);
-      } else if (mode & M_WRITE_O) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * g + i;
-          if (r < rows) {
-            E* dst = static_cast<E*>(p.o) + ((tok0 + r) * H + h) * DV + 16 * w + c16;
-            *dst = to_e<E>(to_f(*dst) + o[i]);
+            for (int kb = 0; kb < 2; ++kb) mma(u[rt][nt], xb[kb], yv[nt][kb]);
           }
         }
       }
     }
-  }
-  {
-    const float gc = s.GamC;
-    Frag<E> us[2];
+    __syncthreads();
+
+    // ---- 5. state chain: U = Ut - W h ; O = scale (diag(Gam) Q h + P U) ; h' = Gam_C h + K^T (ek * U)
+    Frag<E> hf[NTW][DK / 32];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x4 e0, e1;
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) pack_frag(hf[nt][kb], hacc[2 * kb][nt], hacc[2 * kb + 1][nt]);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      Frag<E> xw[DK / 32];
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) xw[kb] = ld_frag(s.W, LQ, 16 * rt + c16, 32 * kb);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) mma(u[rt][nt], xw[kb], hf[nt][kb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (OUT) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        Frag<E> uf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) pack_frag(uf[kb], u[2 * kb][nt], u[2 * kb + 1][nt]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          f32x4 o = zero4();
+#pragma unroll
+          for (int kb = 0; kb < DK / 32; ++kb) mma(o, ld_frag(s.Q, LQ, 16 * rt + c16, 32 * kb), hf[nt][kb]);
+          const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&s.Gam[16 * rt + 4 * g]);
+          o = o * gm4;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) mma(o, ld_frag(s.P, LT, 16 * rt + c16, 32 * kb), uf[kb]);
+          o = o * p.scale;
+          const int col = n0 + 16 * nt + c16;
+          if (!CORR) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s.O[(16 * rt + 4 * g + i) * LO + col] = to_e<E>(o[i]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 16 * rt + 4 * g + i;
+              if (r < rows) {
+                E* dst = static_cast<E*>(p.o) + ((tok0 + r) * H + h) * DV + col;
+                *dst = to_e<E>(to_f(*dst) + o[i]);
+              }
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const float gc = s.GamC;
+      f32x4 e0[2], e1[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        e0[kb] = *reinterpret_cast<const f32x4*>(&s.ek[32 * kb + 4 * g]);
+        e1[kb] = *reinterpret_cast<const f32x4*>(&s.ek[32 * kb + 16 + 4 * g]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        Frag<E> us[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) pack_frag_scaled(us[kb], u[2 * kb][nt], u[2 * kb + 1][nt], e0[kb], e1[kb]);
+#pragma unroll
+        for (int t = 0; t < DK / 16; ++t) {
+          hacc[t][nt] = hacc[t][nt] * gc;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) mma(hacc[t][nt], ld_frag(s.KT, LT, 16 * t + c16, 32 * kb), us[kb]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- 6. output tile out (coalesced); the next chunk's staging does not touch s.O
+    if (OUT && !CORR) {
+      constexpr int VEC = 16 / sizeof(E);
+      typedef E vec_t __attribute__((__vector_size__(16)));
+      for (int e = tid; e < CH * (DV / VEC); e += NT) {
+        const int r = e / (DV / VEC), c0 = (e % (DV / VEC)) * VEC;
+        if (r < rows)
+          *reinterpret_cast<vec_t*>(static_cast<E*>(p.o) + ((tok0 + r) * H + h) * DV + c0) =
+              *reinterpret_cast<const vec_t*>(&s.O[r * LO + c0]);
+      }
+    }
+    return lam_c;
+  }
+
+  // Run chunks [cb, ce) of sequence (seq0, len) from the state in hacc.
+  // CORR runs stop early once the accumulated bound falls under 2^-24; the
+  // number of chunks processed is returned through *done.
+  __device__ static float run(S& s, const FwdParams& p, int64_t seq0, int len, int64_t chunk0, int cb,
+                              int ce, int h, f32x4 (&hacc)[DK / 16][DV / 64], int* done) {
+    Loader ld;
+    float lam = 0.f;
+    int c = cb;
+    if (cb < ce) ld.load(p, seq0 + (int64_t)cb * CH, min(CH, len - cb * CH), h);
+    const size_t SS = (size_t)DK * DV;
+    E* hs = static_cast<E*>(p.hs);
+    for (; c < ce; ++c) {
+      if (CORR && lam <= LN_EPS) break;
+      const int64_t tok0 = seq0 + (int64_t)c * CH;
+      const int rows = min(CH, len - c * CH);
+      const bool more = c + 1 < ce;
+      const int nrows = more ? min(CH, len - (c + 1) * CH) : 0;
+      E* hsc = (!OUT && hs) ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
+      lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, hacc);
+    }
+    if (done) *done = c - cb;
+    return lam;
+  }
+};
+
+template <class E, int DK, int DV>
+__device__ void load_state(f32x4 (&hacc)[DK / 16][DV / 64], const float* src) {
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+#pragma unroll
+  for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+    for (int nt = 0; nt < DV / 64; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        hacc[t][nt][i] = src ? src[(16 * t + 4 * g + i) * DV + w * (DV / 4) + 16 * nt + c16] : 0.f;
+}
+template <class E, int DK, int DV>
+__device__ void store_state(const f32x4 (&hacc)[DK / 16][DV / 64], float* dst, const float* add, bool use_acc) {
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+#pragma unroll
+  for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+    for (int nt = 0; nt < DV / 64; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        e0[i] = s.ek[32 * kb + 4 * g + i];
-        e1[i] = s.ek[32 * kb + 16 + 4 * g + i];
+        const int e = (16 * t + 4 * g + i) * DV + w * (DV / 4) + 16 * nt + c16;
+        dst[e] = (use_acc ? hacc[t][nt][i] : 0.f) + (add ? add[e] : 0.f);
       }
-      pack_frag_scaled(us[kb], u[2 * kb], u[2 * kb + 1], e0, e1);
-    }
-#pragma unroll
-    for (int t = 0; t < DK / 16; ++t) {
-      hacc[t] = hacc[t] * gc;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mma(hacc[t], ld_frag(s.KT, LT, 16 * t + c16, 32 * kb), us[kb]);
-    }
-  }
-  __syncthreads();
-
-  // ---- 7. output tile out (coalesced)
-  if ((mode & M_WRITE_O) && !corr) {
-    constexpr int VEC = 16 / sizeof(E);
-    typedef E vec_t __attribute__((__vector_size__(16)));
-    for (int e = tid; e < CH * (DV / VEC); e += NT) {
-      const int r = e / (DV / VEC), c0 = (e % (DV / VEC)) * VEC;
-      if (r < rows) {
-        vec_t x;
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) x[j] = s.O[r * LO + c0 + j];
-        *reinterpret_cast<vec_t*>(static_cast<E*>(p.o) + ((tok0 + r) * H + h) * DV + c0) = x;
-      }
-    }
-  }
-  return lam_c;
-}
-
-template <class E, int DK, int DV>
-__device__ void load_state(f32x4 (&hacc)[DK / 16], const float* src) {
-  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
-#pragma unroll
-  for (int t = 0; t < DK / 16; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hacc[t][i] = src ? src[(16 * t + 4 * g + i) * DV + 16 * w + c16] : 0.f;
-}
-template <class E, int DK, int DV>
-__device__ void store_state(const f32x4 (&hacc)[DK / 16], float* dst, const float* add) {
-  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
-#pragma unroll
-  for (int t = 0; t < DK / 16; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = (16 * t + 4 * g + i) * DV + 16 * w + c16;
-      dst[e] = hacc[t][i] + (add ? add[e] : 0.f);
-    }
 }
 
 template <class E, int DK, int DV>
@@ -325,89 +482,73 @@ __device__ void init_smem(FwdSmem<E, DK, DV>& s) {
   __syncthreads();
 }
 
-template <class E, int DK, int DV>
-__global__ __launch_bounds__(DV / 16 * 64) void gdn_fwd_kernel(FwdParams p) {
+// Phase 1: every segment from zero (segment 0 from h0).
+template <class E, int DK, int DV, bool OUT>
+__global__ __launch_bounds__(256) void gdn_fwd_p1(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
-  const int h = blockIdx.y;
-  const int n = sd.n;
+  const int h = blockIdx.y, n = sd.n;
+  const int nseg = p.seg_first[n + 1] - p.seg_first[n];
+  const size_t SS = (size_t)DK * DV;
+  f32x4 hacc[DK / 16][DV / 64];
+  init_smem(s);
+  load_state<E, DK, DV>(hacc, (sd.s == 0 && p.h0) ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
+  const float lam = Chunk<E, DK, DV, OUT, false>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
+                                                      sd.c_begin, sd.c_end, h, hacc, nullptr);
+  if (nseg == 1) {
+    if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
+  } else {
+    store_state<E, DK, DV>(hacc, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, nullptr, true);
+    if (threadIdx.x == 0) p.lam[(size_t)blockIdx.x * p.H + h] = lam;
+  }
+}
+
+// Phase 3: boundary corrections (or the serial fallback).
+template <class E, int DK, int DV, bool OUT>
+__global__ __launch_bounds__(256) void gdn_fwd_p3(FwdParams p) {
+  __shared__ FwdSmem<E, DK, DV> s;
+  const SegDesc sd = p.segs[blockIdx.x];
+  const int h = blockIdx.y, n = sd.n;
   const int seg0 = p.seg_first[n];
   const int nseg = p.seg_first[n + 1] - seg0;
+  if (nseg == 1 || sd.s == 0) return;
   const int64_t seq0 = p.seq.start(n);
   const int len = p.seq.len(n);
   const size_t SS = (size_t)DK * DV;
   const int64_t chunk0 = p.chunk_first[n];
-  E* hs = static_cast<E*>(p.hs);
-  const int base_mode = (p.o ? M_WRITE_O : 0) | (hs ? M_STORE_H : 0);
-  f32x4 hacc[DK / 16];
-
-  auto run = [&](int cb, int ce, int mode) {
-    for (int c = cb; c < ce; ++c) {
-      const int64_t tok0 = seq0 + (int64_t)c * CH;
-      const int rows = min(CH, len - c * CH);
-      E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
-      chunk_step<E, DK, DV>(s, p, tok0, rows, h, mode, hsc, hacc);
-    }
-  };
-
-  if (p.phase == 1) {
-    init_smem(s);
-    load_state<E, DK, DV>(hacc, (sd.s == 0 && p.h0) ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-    float lam = 0.f;
-    for (int c = sd.c_begin; c < sd.c_end; ++c) {
-      const int64_t tok0 = seq0 + (int64_t)c * CH;
-      const int rows = min(CH, len - c * CH);
-      E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
-      lam += chunk_step<E, DK, DV>(s, p, tok0, rows, h, base_mode, hsc, hacc);
-    }
-    if (nseg == 1) {
-      if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr);
-    } else {
-      store_state<E, DK, DV>(hacc, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, nullptr);
-      if (threadIdx.x == 0) p.lam[(size_t)blockIdx.x * p.H + h] = lam;
-    }
-    return;
-  }
-
-  // ---- phase 3: boundary corrections
-  if (nseg == 1 || sd.s == 0) return;
   bool ok = true;
   for (int j = 1; j + 1 < nseg; ++j) ok = ok && (p.lam[(size_t)(seg0 + j) * p.H + h] <= LN_EPS);
+  if (!ok && sd.s != 1) return;
+  f32x4 hacc[DK / 16][DV / 64];
   init_smem(s);
   if (!ok) {
     // Gates do not decay fast enough to cut this sequence: one workgroup redoes it serially.
-    if (sd.s != 1) return;
     load_state<E, DK, DV>(hacc, p.h0 ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-    const int nch = (len + CH - 1) / CH;
-    run(0, nch, base_mode);
-    if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr);
+    Chunk<E, DK, DV, OUT, false>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc, nullptr);
+    if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
     return;
   }
   load_state<E, DK, DV>(hacc, p.bstate + ((size_t)(blockIdx.x - 1) * p.H + h) * SS);
-  float cum = 0.f;
-  int c = sd.c_begin;
-  for (; c < sd.c_end && cum > LN_EPS; ++c) {
-    const int64_t tok0 = seq0 + (int64_t)c * CH;
-    const int rows = min(CH, len - c * CH);
-    E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
-    cum += chunk_step<E, DK, DV>(s, p, tok0, rows, h, base_mode | M_CORR, hsc, hacc);
-  }
+  int done = 0;
+  Chunk<E, DK, DV, OUT, true>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done);
   if (sd.s == nseg - 1 && p.hT) {
     // hT = b_last + (the correction propagated through the whole last segment, if it got there)
     const float* b = p.bstate + ((size_t)blockIdx.x * p.H + h) * SS;
-    if (c == sd.c_end) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, b);
-    else {
-      f32x4 z[DK / 16];
-      for (int t = 0; t < DK / 16; ++t) z[t] = zero4();
-      store_state<E, DK, DV>(z, p.hT + ((size_t)n * p.H + h) * SS, b);
-    }
+    store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, b, done == sd.c_end - sd.c_begin);
   }
 }
 
 template <class E, int DK, int DV>
 hipError_t launch_fwd_t(const FwdParams& p, int nseg_total, hipStream_t st) {
-  dim3 grid(nseg_total, p.H), block(DV / 16 * 64);
-  hipLaunchKernelGGL((gdn_fwd_kernel<E, DK, DV>), grid, block, 0, st, p);
+  dim3 grid(nseg_total, p.H), block(256);
+  const bool out = p.o != nullptr;
+  if (p.phase == 1) {
+    if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false>), grid, block, 0, st, p);
+  } else {
+    if (out) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, false>), grid, block, 0, st, p);
+  }
   return hipGetLastError();
 }
 

@@ -112,6 +112,95 @@ __device__ __forceinline__ void stage_tile(const E* __restrict__ src, int64_t gl
 }
 
 
+// One diagonal 16x16 block b of T = (I + A)^-1 by forward substitution, done by
+// one wave: lane (j = l%16, g = l/16) owns rows 4g..4g+3 of column j.  Step i
+// finalises row i (broadcast from its owner lane) and removes A_ri T_ij from
+// every later row r.  A = diag(rs) Araw (rs may be null).
+__device__ __forceinline__ void solve_diag_block(const float* A, float* T, int b, const float* rs) {
+  constexpr int LA = CH + 4;
+  const int l = lane_id(), j = l & 15, g = l >> 4;
+  const float* Ab = A + (16 * b) * LA + 16 * b;
+  float t[4], sc[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    t[ii] = (4 * g + ii == j) ? 1.f : 0.f;
+    sc[ii] = rs ? rs[16 * b + 4 * g + ii] : 1.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 15; ++i) {
+    const float ti = __shfl(t[i & 3], 16 * (i >> 2) + j, 64);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int r = 4 * g + ii;
+      const float a = sc[ii] * Ab[r * LA + i];
+      t[ii] = (r > i) ? t[ii] - a * ti : t[ii];
+    }
+  }
+  float* Tb = T + (16 * b) * LA + 16 * b;
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) Tb[(4 * g + ii) * LA + j] = t[ii];
+}
+
+// Two diagonal 16x16 blocks (ba, bb) of T by forward substitution in one wave,
+// with no cross-lane traffic: lane j (< 16) owns column j of block ba, lane
+// 16 + j column j of block bb (lanes 32..63 repeat lanes 0..31 and write
+// nothing).  T_rj = d_rj - sum_{i<r} A_ri T_ij, applied right-looking: once
+// row i is final, A_ri T_ij is removed from every later row r.
+__device__ __forceinline__ void solve_diag_pair(const float* A, float* T, int ba, int bb, const float* rs) {
+  constexpr int LA = CH + 4;
+  const int l = lane_id(), j = l & 15;
+  const int b = (l & 16) ? bb : ba;
+  const float* Ab = A + (16 * b) * LA + 16 * b;
+  float t[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) t[r] = (r == j) ? 1.f : 0.f;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) {
+#pragma unroll
+    for (int r = i + 1; r < 16; ++r) t[r] -= (rs ? rs[16 * b + r] : 1.f) * Ab[r * LA + i] * t[i];
+  }
+  if (l < 32) {
+    float* Tb = T + (16 * b) * LA + 16 * b;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Tb[r * LA + j] = t[r];
+  }
+}
+
+// First off-diagonal level (after all diagonal blocks): wave 0 -> T_10, wave 1 -> T_32.
+__device__ __forceinline__ void solve_level1(const float* A, float* T, int w, const float* rs) {
+  if (w == 0) solve_offdiag(A, T, 1, 0, rs);
+  else if (w == 1) solve_offdiag(A, T, 3, 2, rs);
+}
+
+// Second level: the lower-left 32x32 block of T from the two 32x32 diagonal
+// inverses,  T_ll = -T_bot * A_ll * T_top  (waves 0..3 -> T_20, T_21, T_30, T_31).
+__device__ __forceinline__ void solve_level2(const float* A, float* T, int w, const float* rs) {
+  constexpr int LA = CH + 4;
+  if (w > 3) return;
+  const int I = 2 + (w >> 1), J = w & 1;
+  f32x4 out = zero4();
+  for (int K = 2; K <= I; ++K) {
+    f32x4 y = zero4();
+    for (int M = J; M <= 1; ++M) mm16_xy(y, A, LA, 16 * K, 16 * M, T, LA, 16 * M, 16 * J, rs);
+    mm16_xreg(out, T, LA, 16 * I, 16 * K, y);
+  }
+  const int l = lane_id(), g = l >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) T[(16 * I + 4 * g + i) * LA + 16 * J + (l & 15)] = -out[i];
+}
+
+// Full solve with 3 barriers, for kernels with at least 4 waves.  T's
+// strictly-upper blocks must already be zero; complete after the final barrier.
+__device__ __forceinline__ void solve_T4(const float* A, float* T, const float* rs) {
+  const int w = wave_id();
+  if (w < 4) solve_diag_block(A, T, w, rs);
+  __syncthreads();
+  solve_level1(A, T, w, rs);
+  __syncthreads();
+  solve_level2(A, T, w, rs);
+  __syncthreads();
+}
+
 // Solve T = (I + diag(rs) Araw)^-1 for a 64x64 strictly-lower Araw (fp32, row
 // stride CH+4) into T, using waves 0..2 of the workgroup.  Must be called by
 // every thread (it contains barriers); T's strictly-upper blocks must already

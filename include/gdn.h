@@ -123,6 +123,18 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream);
  * and (optionally) h0.  It recomputes the forward states from the inputs. */
 gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream);
 
+/* Per-kernel timing, for benchmarks (off by default).  While enabled, every
+ * kernel the library launches is bracketed by a pair of HIP events recorded on
+ * the call's stream.  gdn_profile_read waits for the recorded events, adds
+ * their elapsed times to per-kernel totals and writes up to `max` entries:
+ * the kernel's name (static storage), total milliseconds and launch count.
+ * It returns the number of distinct kernels seen since the last reset (or -1
+ * on a HIP error).  gdn_profile_reset clears the totals.  Not thread-safe with
+ * respect to concurrent calls on other threads. */
+int gdn_profile_enable(int on);
+int gdn_profile_read(int max, const char** names, double* ms, int* launches);
+void gdn_profile_reset(void);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* gdn_last_error(void);
 
