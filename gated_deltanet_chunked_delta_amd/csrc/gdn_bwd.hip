@@ -34,7 +34,11 @@
 //                  + [r = last] (Gam_C <h, dh'> + sum_i ek_i k_i.(U dh'^T)_i)
 //        dg = reverse cumulative sum of dgam within the chunk.
 //     A short final chunk is handled as a 64-row chunk whose extra rows have
-//     zero q, k, v, dO, beta and g, which leaves every real gradient unchanged.
+//     zero beta and g (and, in the chunk-gradient kernel, zero q, k, v, dO);
+//     the reverse chain loads copies of the last real row there and masks the
+//     two terms that would see them, which leaves every real gradient unchanged.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_tiles.h"
@@ -57,246 +61,341 @@ struct alignas(16) RevSmem {
   E PT[CH * LT];   // scale * P^T
   float A[CH * LA];
   float T[CH * LA];
-  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], graw[CH], lam[CH], sGam[CH];
+  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], lam[CH], sGam[CH];
   float GamC;
 };
 
-enum : int { R_CORR = 1 };
+// One chunk of the reverse chain (4 waves; wave w owns Dv/4 columns of the
+// state gradient).  CORR: propagation of a boundary difference only (dO
+// does not enter, stored gradients are incremented).
+template <class E, int DK, int DV, bool CORR>
+struct RevChunk {
+  static constexpr int NW = 4, NT = 256, NTW = DV / 64;
+  using S = RevSmem<E, DK, DV>;
+  struct Loader {
+    TilePart<E, NT, DK> k;
+    TilePart<E, NT, CORR ? 0 : DK> q;
+    TilePart<E, NT, CORR ? 0 : DV> d;
+    ScalarPart<E> sc;
+  };
 
-// One chunk of the reverse chain.  dh: this wave's columns of the gradient at
-// the chunk end on entry, at the chunk start on exit.  Returns Lambda_c.
-template <class E, int DK, int DV>
-__device__ float rev_step(RevSmem<E, DK, DV>& s, const RevParams& p, int64_t tok0, int rows, int h,
-                          int mode, E* dhs_chunk, f32x4 (&dh)[DK / 16]) {
-  using Sm = RevSmem<E, DK, DV>;
-  constexpr int NW = DV / 16, NT = NW * 64;
-  constexpr int LQ = Sm::LQ, LT = Sm::LT, LA = Sm::LA;
-  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
-  const bool corr = mode & R_CORR;
-  const int H = p.H;
-
-  // ---- 0. gradient at the chunk end, out
-#pragma unroll
-  for (int t = 0; t < DK / 16; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      E* dst = dhs_chunk + (16 * t + 4 * g + i) * DV + 16 * w + c16;
-      float val = dh[t][i];
-      if (corr) val += to_f(*dst);
-      *dst = to_e<E>(val);
+  __device__ static void issue(Loader& ld, const RevParams& p, int64_t tok0, int rows, int h) {
+    const int H = p.H;
+    ld.k.load(static_cast<const E*>(p.k) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
+    if (!CORR) {
+      ld.q.load(static_cast<const E*>(p.q) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
+      ld.d.load(static_cast<const E*>(p.dout) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
     }
+    ld.sc.load(p.g, static_cast<const E*>(p.beta), tok0, H, h, rows);
+  }
 
-  // ---- 1. staging
-  {
-    const E* k = static_cast<const E*>(p.k) + (tok0 * H + h) * DK;
-    stage_tile<E, DK, NT>(k, (int64_t)H * DK, rows, s.K, LQ, s.KT, LT);
-    if (!corr) {
-      const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
-      const E* d = static_cast<const E*>(p.dout) + (tok0 * H + h) * DV;
-      stage_tile<E, DK, NT>(q, (int64_t)H * DK, rows, s.Q, LQ, s.QT, LT);
-      stage_tile<E, DV, NT>(d, (int64_t)H * DV, rows, nullptr, 0, s.DOT, LT);
+  // dh: gradient at the chunk end on entry, at the chunk start on exit.
+  // Prefetches chunk (ntok0, nrows) into ld (nrows = 0: none).  Returns Lambda_c.
+  __device__ static float step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows,
+                               int h, E* dhs_chunk, f32x4 (&dh)[DK / 16][DV / 64]) {
+    constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
+    const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+    const int n0 = w * (DV / 4);
+
+    // ---- 1. gradient at the chunk end out; tiles into LDS; scalars
+    S* sp = lds_opaque(&s0);
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          E* dst = dhs_chunk + (16 * t + 4 * g + i) * DV + n0 + 16 * nt + c16;
+          float val = dh[t][nt][i];
+          if (CORR) val += to_f(*dst);
+          *dst = to_e<E>(val);
+        }
+    S& s1 = *sp;
+    ld.k.store(s1.K, LQ, s1.KT, LT);
+    if (!CORR) {
+      ld.q.store(s1.Q, LQ, s1.QT, LT);
+      ld.d.store(nullptr, 0, s1.DOT, LT);
     }
     if (w == 0) {
-      const bool valid = l < rows;
-      const int64_t si = (tok0 + l) * H + h;
-      float gr = valid ? p.g[si] : 0.f;
-      float bt = valid ? to_f(static_cast<const E*>(p.beta)[si]) : 0.f;
-      float gm = wave_incl_scan(gr);
-      float gC = __shfl(gm, 63, 64);
-      float Gm = __expf(gm);
+      S& s = s1;
+      const float gr = ld.sc.g_at(l), bt = ld.sc.beta_at(l);
+      const float gm = wave_incl_scan(gr);
+      const float gC = __shfl(gm, 63, 64);
+      const float Gm = __expf(gm);
       s.gam[l] = gm;
       s.Gam[l] = Gm;
-      s.sGam[l] = p.scale * Gm;
+      s.sGam[l] = l < rows ? p.scale * Gm : 0.f;  // rows past the end carry copies of the last
       s.ek[l] = __expf(gC - gm);
       s.beta[l] = bt;
       s.bg[l] = bt * Gm;
-      s.graw[l] = gr;
+      s.lam[l] = gr;
       if (l == 0) s.GamC = __expf(gC);
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- 2. K K^T -> A (+ lambda) ; Q K^T -> scale P^T
-  const int ntiles = corr ? 10 : 20;
-  for (int ti = w; ti < ntiles; ti += NW) {
-    const bool isq = ti >= 10;
-    const int tt = isq ? ti - 10 : ti;
-    int rt = 0;
-    while ((rt + 1) * (rt + 2) / 2 <= tt) ++rt;
-    const int ct = tt - rt * (rt + 1) / 2;
-    f32x4 acc = zero4();
-    const E* X = isq ? s.Q : s.K;
+    // ---- 2. K K^T -> A (waves 0, 1, row pairs) + diagonal blocks of T;
+    //         Q K^T -> scale P^T (waves 2, 3)
+    {
+      S& s = *lds_opaque(&s0);
+      const bool rows03 = (w & 1) == 0;
+      const bool isq = w >= 2;
+      if (!isq || !CORR) {
+        const E* X = isq ? s.Q : s.K;
+        auto row = [&](auto RT_) {
+          constexpr int RT = decltype(RT_)::value;
+          Frag<E> xa[DK / 32];
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb)
-      mma(acc, ld_frag(X, LQ, 16 * rt + c16, 32 * kb), ld_frag(s.K, LQ, 16 * ct + c16, 32 * kb));
-    const int c = 16 * ct + c16;
+          for (int kb = 0; kb < DK / 32; ++kb) xa[kb] = ld_frag(X, LQ, 16 * RT + c16, 32 * kb);
+          const f32x4 gr4 = *reinterpret_cast<const f32x4*>(&s.gam[16 * RT + 4 * g]);
+          const f32x4 br4 = *reinterpret_cast<const f32x4*>(&s.beta[16 * RT + 4 * g]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * g + i;
-      if (!isq) {
-        float val = (c < r) ? s.beta[r] * acc[i] * __expf(s.gam[r] - s.gam[c]) : 0.f;
-        s.A[r * LA + c] = val;
-        if (r == c) s.lam[r] = s.graw[r] + __logf(fmaxf(1.f, fabsf(1.f - s.beta[r] * acc[i])));
-      } else {
-        float val = (c <= r) ? p.scale * acc[i] * __expf(s.gam[r] - s.gam[c]) : 0.f;
-        s.PT[c * LT + r] = to_e<E>(val);
+          for (int ct = 0; ct <= RT; ++ct) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) mma(acc, xa[kb], ld_frag(s.K, LQ, 16 * ct + c16, 32 * kb));
+            const int c = 16 * ct + c16;
+            const float gc = s.gam[c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 16 * RT + 4 * g + i;
+              const float dm = __expf(gr4[i] - gc);
+              if (!isq) {
+                s.A[r * LA + c] = (c < r) ? br4[i] * acc[i] * dm : 0.f;
+                if (ct == RT && r == c) s.lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
+              } else {
+                s.PT[c * LT + r] = to_e<E>((c <= r && r < rows) ? p.scale * acc[i] * dm : 0.f);
+              }
+            }
+          }
+        };
+        if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
+        else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
+        if (!isq) solve_diag_pair(s.A, s.T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
       }
     }
-  }
-  __syncthreads();
-  const float lam_c = __shfl(wave_sum(s.lam[l]), 0, 64);
+    __syncthreads();
+    const float lam_c = __shfl(wave_sum(lds_opaque(&s0)->lam[l]), 0, 64);
+    if (nrows > 0) issue(ld, p, ntok0, nrows, h);
 
-  // ---- 3. T = (I + A)^-1
-  solve_T(s.A, s.T, nullptr);
-
-  // ---- 4. -W^T = -K^T diag(beta Gam) T^T
-  for (int ti = w; ti < (DK / 16) * 4; ti += NW) {
-    const int dt = ti >> 2, rt = ti & 3;
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      mma(acc, ld_frag_kscaled<E>(s.KT, LT, 16 * dt + c16, 32 * kb, s.bg),
-          ld_frag_f32<E>(s.T, LA, 16 * rt + c16, 32 * kb));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s.WT[(16 * dt + 4 * g + i) * LT + 16 * rt + c16] = to_e<E>(-acc[i]);
-  }
-  __syncthreads();
-
-  // ---- 5. dU = diag(ek) K dh' + scale P^T dO ; dh = Gam_C dh' + scale (Gam Q)^T dO - W^T dU
-  f32x4 du[4];
-  {
-    Frag<E> hf[DK / 32];
-#pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) pack_frag(hf[kb], dh[2 * kb], dh[2 * kb + 1]);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) mma(acc, ld_frag(s.K, LQ, 16 * rt + c16, 32 * kb), hf[kb]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= s.ek[16 * rt + 4 * g + i];
-      if (!corr) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          mma(acc, ld_frag(s.PT, LT, 16 * rt + c16, 32 * kb), ld_frag(s.DOT, LT, 16 * w + c16, 32 * kb));
-      }
-      du[rt] = acc;
+    // ---- 3. off-diagonal blocks of T
+    {
+      S& s = *lds_opaque(&s0);
+      solve_level1(s.A, s.T, w, nullptr);
     }
-  }
-  {
-    const float gc = s.GamC;
-    Frag<E> uf[2];
+    __syncthreads();
+    {
+      S& s = *lds_opaque(&s0);
+      solve_level2(s.A, s.T, w, nullptr);
+    }
+    __syncthreads();
+
+    // ---- 4. -W^T = -K^T diag(beta Gam) T^T; wave w takes key rows [w Dk/4, (w+1) Dk/4)
+    {
+      S& s = *lds_opaque(&s0);
+      Frag<E> yt[4][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) pack_frag(uf[kb], du[2 * kb], du[2 * kb + 1]);
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int t = 0; t < DK / 16; ++t) {
-      dh[t] = dh[t] * gc;
-      if (!corr) {
+        for (int kb = 0; kb < 2; ++kb) yt[rt][kb] = ld_frag_f32<E>(s.T, LA, 16 * rt + c16, 32 * kb);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          mma(dh[t], ld_frag_kscaled<E>(s.QT, LT, 16 * t + c16, 32 * kb, s.sGam),
-              ld_frag(s.DOT, LT, 16 * w + c16, 32 * kb));
+      for (int dd = 0; dd < DK / 64; ++dd) {
+        const int dt = w * (DK / 64) + dd;
+        Frag<E> xk[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) xk[kb] = ld_frag_kscaled<E>(s.KT, LT, 16 * dt + c16, 32 * kb, s.bg);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) mma(acc, xk[kb], yt[rt][kb]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s.WT[(16 * dt + 4 * g + i) * LT + 16 * rt + c16] = to_e<E>(-acc[i]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- 5. dU = diag(ek) K dh' + scale P^T dO ;  dh = Gam_C dh' + scale (Gam Q)^T dO - W^T dU
+    f32x4 du[4][NTW];
+    {
+      S& s = *lds_opaque(&s0);
+      Frag<E> hf[NTW][DK / 32];
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) pack_frag(hf[nt][kb], dh[2 * kb][nt], dh[2 * kb + 1][nt]);
+      Frag<E> yd[NTW][2];
+      if (!CORR) {
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) yd[nt][kb] = ld_frag(s.DOT, LT, n0 + 16 * nt + c16, 32 * kb);
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mma(dh[t], ld_frag(s.WT, LT, 16 * t + c16, 32 * kb), uf[kb]);
+      for (int rt = 0; rt < 4; ++rt) {
+        Frag<E> xk[DK / 32];
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) xk[kb] = ld_frag(s.K, LQ, 16 * rt + c16, 32 * kb);
+        const f32x4 e4 = *reinterpret_cast<const f32x4*>(&s.ek[16 * rt + 4 * g]);
+        Frag<E> xp[2];
+        if (!CORR) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) xp[kb] = ld_frag(s.PT, LT, 16 * rt + c16, 32 * kb);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb < DK / 32; ++kb) mma(acc, xk[kb], hf[nt][kb]);
+          acc = acc * e4;
+          if (!CORR) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) mma(acc, xp[kb], yd[nt][kb]);
+          }
+          du[rt][nt] = acc;
+        }
+      }
+      const float gc = s.GamC;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        Frag<E> uf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) pack_frag(uf[kb], du[2 * kb][nt], du[2 * kb + 1][nt]);
+#pragma unroll
+        for (int t = 0; t < DK / 16; ++t) {
+          dh[t][nt] = dh[t][nt] * gc;
+          if (!CORR) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+              mma(dh[t][nt], ld_frag_kscaled<E>(s.QT, LT, 16 * t + c16, 32 * kb, s.sGam), yd[nt][kb]);
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) mma(dh[t][nt], ld_frag(s.WT, LT, 16 * t + c16, 32 * kb), uf[kb]);
+        }
+      }
     }
+    __syncthreads();
+    return lam_c;
   }
-  __syncthreads();
-  return lam_c;
-}
+
+  // Chunks ce-1 down to cb; CORR stops once the accumulated bound is below 2^-24.
+  // Returns Lambda over the processed chunks; *lowest = last chunk processed.
+  __device__ static float run(S& s, const RevParams& p, int64_t seq0, int len, int64_t chunk0, int cb, int ce,
+                              int h, f32x4 (&dh)[DK / 16][DV / 64], int* lowest) {
+    Loader ld;
+    float lam = 0.f;
+    int c = ce - 1;
+    if (c >= cb) issue(ld, p, seq0 + (int64_t)c * CH, min(CH, len - c * CH), h);
+    const size_t SS = (size_t)DK * DV;
+    E* dhs = static_cast<E*>(p.dhs);
+    for (; c >= cb; --c) {
+      if (CORR && lam <= LN_EPS) break;
+      const int rows = min(CH, len - c * CH);
+      const bool more = c - 1 >= cb;
+      const int64_t ntok0 = seq0 + (int64_t)(c - 1) * CH;
+      const int nrows = more ? min(CH, len - (c - 1) * CH) : 0;
+      lam += step(s, p, ld, rows, ntok0, nrows, h, dhs + ((chunk0 + c) * p.H + h) * SS, dh);
+    }
+    if (lowest) *lowest = c + 1;
+    return lam;
+  }
+};
 
 template <class E, int DK, int DV>
-__device__ void rev_load(f32x4 (&acc)[DK / 16], const float* src) {
+__device__ void rev_load(f32x4 (&acc)[DK / 16][DV / 64], const float* src) {
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
 #pragma unroll
   for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] = src ? src[(16 * t + 4 * g + i) * DV + 16 * w + c16] : 0.f;
+    for (int nt = 0; nt < DV / 64; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[t][nt][i] = src ? src[(16 * t + 4 * g + i) * DV + w * (DV / 4) + 16 * nt + c16] : 0.f;
 }
 template <class E, int DK, int DV>
-__device__ void rev_store(const f32x4 (&acc)[DK / 16], float* dst, const float* add, bool use_acc) {
+__device__ void rev_store(const f32x4 (&acc)[DK / 16][DV / 64], float* dst, const float* add, bool use_acc) {
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
 #pragma unroll
   for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = (16 * t + 4 * g + i) * DV + 16 * w + c16;
-      dst[e] = (use_acc ? acc[t][i] : 0.f) + (add ? add[e] : 0.f);
-    }
+    for (int nt = 0; nt < DV / 64; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = (16 * t + 4 * g + i) * DV + w * (DV / 4) + 16 * nt + c16;
+        dst[e] = (use_acc ? acc[t][nt][i] : 0.f) + (add ? add[e] : 0.f);
+      }
 }
 
 template <class E, int DK, int DV>
-__global__ __launch_bounds__(DV / 16 * 64) void gdn_rev_kernel(RevParams p) {
-  __shared__ RevSmem<E, DK, DV> s;
+__device__ void rev_init_smem(RevSmem<E, DK, DV>& s) {
   using Sm = RevSmem<E, DK, DV>;
-  const SegDesc sd = p.segs[blockIdx.x];
-  const int h = blockIdx.y, n = sd.n;
-  const int seg0 = p.seg_first[n];
-  const int nseg = p.seg_first[n + 1] - seg0;
-  const int64_t seq0 = p.seq.start(n);
-  const int len = p.seq.len(n);
-  const size_t SS = (size_t)DK * DV;
-  const int64_t chunk0 = p.chunk_first[n];
-  E* dhs = static_cast<E*>(p.dhs);
-  const float* dhT = p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr;
-  float* dh0 = p.dh0 ? p.dh0 + ((size_t)n * p.H + h) * SS : nullptr;
-  f32x4 dh[DK / 16];
-
   // T's strictly-upper blocks and the tiles of P^T above the diagonal are never written
   for (int e = threadIdx.x; e < CH * CH; e += blockDim.x) {
     s.T[(e >> 6) * Sm::LA + (e & 63)] = 0.f;
     s.PT[(e >> 6) * Sm::LT + (e & 63)] = to_e<E>(0.f);
   }
   __syncthreads();
+}
 
-  auto run = [&](int cb, int ce, int mode) {
-    float lam = 0.f;
-    for (int c = ce - 1; c >= cb; --c) {
-      const int64_t tok0 = seq0 + (int64_t)c * CH;
-      const int rows = min(CH, len - c * CH);
-      lam += rev_step<E, DK, DV>(s, p, tok0, rows, h, mode, dhs + ((chunk0 + c) * p.H + h) * SS, dh);
-    }
-    return lam;
-  };
-
-  if (p.phase == 1) {
-    rev_load<E, DK, DV>(dh, sd.s == nseg - 1 ? dhT : nullptr);
-    const float lam = run(sd.c_begin, sd.c_end, 0);
-    if (nseg == 1) {
-      if (dh0) rev_store<E, DK, DV>(dh, dh0, nullptr, true);
-    } else {
-      rev_store<E, DK, DV>(dh, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, nullptr, true);
-      if (threadIdx.x == 0) p.lam[(size_t)blockIdx.x * p.H + h] = lam;
-    }
-    return;
+// Phase 1: every segment from dh' = 0 (the last segment of a sequence from dhT).
+template <class E, int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_rev_p1(RevParams p) {
+  __shared__ RevSmem<E, DK, DV> s;
+  const SegDesc sd = p.segs[blockIdx.x];
+  const int h = blockIdx.y, n = sd.n;
+  const int nseg = p.seg_first[n + 1] - p.seg_first[n];
+  const size_t SS = (size_t)DK * DV;
+  const float* dhT = p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr;
+  f32x4 dh[DK / 16][DV / 64];
+  rev_init_smem(s);
+  rev_load<E, DK, DV>(dh, sd.s == nseg - 1 ? dhT : nullptr);
+  const float lam = RevChunk<E, DK, DV, false>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
+                                                    sd.c_begin, sd.c_end, h, dh, nullptr);
+  if (nseg == 1) {
+    if (p.dh0) rev_store<E, DK, DV>(dh, p.dh0 + ((size_t)n * p.H + h) * SS, nullptr, true);
+  } else {
+    rev_store<E, DK, DV>(dh, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, nullptr, true);
+    if (threadIdx.x == 0) p.lam[(size_t)blockIdx.x * p.H + h] = lam;
   }
+}
 
-  // ---- phase 3: propagate the true end-of-segment gradient into the segment's last chunks
+// Phase 3: propagate the true end-of-segment gradient into each segment's last
+// chunks (or recompute the sequence serially when the certificate fails).
+template <class E, int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_rev_p3(RevParams p) {
+  __shared__ RevSmem<E, DK, DV> s;
+  const SegDesc sd = p.segs[blockIdx.x];
+  const int h = blockIdx.y, n = sd.n;
+  const int seg0 = p.seg_first[n];
+  const int nseg = p.seg_first[n + 1] - seg0;
   if (nseg == 1 || sd.s == nseg - 1) return;
+  const int64_t seq0 = p.seq.start(n);
+  const int len = p.seq.len(n);
+  const size_t SS = (size_t)DK * DV;
+  const int64_t chunk0 = p.chunk_first[n];
+  float* dh0 = p.dh0 ? p.dh0 + ((size_t)n * p.H + h) * SS : nullptr;
   bool ok = true;
   for (int j = 1; j + 1 < nseg; ++j) ok = ok && (p.lam[(size_t)(seg0 + j) * p.H + h] <= LN_EPS);
+  if (!ok && sd.s != 0) return;
+  f32x4 dh[DK / 16][DV / 64];
+  rev_init_smem(s);
   if (!ok) {
-    if (sd.s != 0) return;
-    rev_load<E, DK, DV>(dh, dhT);
-    run(0, (len + CH - 1) / CH, 0);
+    rev_load<E, DK, DV>(dh, p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr);
+    RevChunk<E, DK, DV, false>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, dh, nullptr);
     if (dh0) rev_store<E, DK, DV>(dh, dh0, nullptr, true);
     return;
   }
   rev_load<E, DK, DV>(dh, p.bstate + ((size_t)(blockIdx.x + 1) * p.H + h) * SS);
-  float cum = 0.f;
-  int c = sd.c_end - 1;
-  for (; c >= sd.c_begin && cum > LN_EPS; --c) {
-    const int64_t tok0 = seq0 + (int64_t)c * CH;
-    const int rows = min(CH, len - c * CH);
-    cum += rev_step<E, DK, DV>(s, p, tok0, rows, h, R_CORR, dhs + ((chunk0 + c) * p.H + h) * SS, dh);
-  }
+  int lowest = sd.c_end;
+  RevChunk<E, DK, DV, true>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, dh, &lowest);
   if (sd.s == 0 && dh0)
-    rev_store<E, DK, DV>(dh, dh0, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, c < sd.c_begin);
+    rev_store<E, DK, DV>(dh, dh0, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, lowest == sd.c_begin);
 }
 
 template <class E, int DK, int DV>
 hipError_t launch_rev_t(const RevParams& p, int nseg_total, hipStream_t st) {
-  hipLaunchKernelGGL((gdn_rev_kernel<E, DK, DV>), dim3(nseg_total, p.H), dim3(DV / 16 * 64), 0, st, p);
+  if (p.phase == 1) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV>), dim3(nseg_total, p.H), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV>), dim3(nseg_total, p.H), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -41,6 +41,20 @@ constexpr int CH = 64;  // chunk length (rows per chunk)
 constexpr float LN_EPS = -16.635532333438686f;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Returns the LDS pointer p unchanged while hiding its value from the
+// optimizer: address arithmetic derived from the result cannot be hoisted
+// above or shared across this point.  Kernels whose LDS exceeds the 64 KiB
+// reach of a ds instruction's immediate offset call it at each phase, so that
+// per-lane LDS addresses are formed where they are used instead of being
+// precomputed once and held (or spilled) across the whole chunk loop.
+template <class T>
+__device__ __forceinline__ T* lds_opaque(T* p) {
+  uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) T*)p);
+  asm volatile("" : "+s"(a));
+  return (T*)((__attribute__((address_space(3))) T*)(uintptr_t)a);
+}
+
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // ---------------------------------------------------------------------------

@@ -192,7 +192,7 @@ struct Chunk {
   // Process the chunk whose tiles `ld` holds; prefetch the next chunk (if any)
   // into `ld`.  hacc: this wave's state columns (chunk start on entry, chunk end
   // on exit).  Returns the chunk's log-bound Lambda_c.
-  __device__ static float step(S& s, const FwdParams& p, Loader& ld, int64_t tok0, int rows,
+  __device__ static float step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows,
                                int64_t ntok0, int nrows, int h, E* hs_chunk, f32x4 (&hacc)[DK / 16][DV / 64]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA, LO = S::LO;
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
@@ -200,20 +200,21 @@ struct Chunk {
     const int n0 = w * (DV / 4);  // first state column of this wave
 
     // ---- 1. tiles into LDS, scalars, prefetch of the next chunk
-    ld.store(s);
+    S* sp = lds_opaque(&s0);
+    ld.store(*sp);
     if (w == 0) {
       const float gr = ld.g_at(l), bt = ld.beta_at(l);
       const float gm = wave_incl_scan(gr);
       const float gC = __shfl(gm, 63, 64);
       const float Gm = __expf(gm);
-      s.gam[l] = gm;
-      s.Gam[l] = Gm;
-      s.ek[l] = __expf(gC - gm);
-      s.beta[l] = bt;
-      s.bg[l] = bt * Gm;
+      sp->gam[l] = gm;
+      sp->Gam[l] = Gm;
+      sp->ek[l] = __expf(gC - gm);
+      sp->beta[l] = bt;
+      sp->bg[l] = bt * Gm;
       // per-token log-bound; the log max(1, |1 - beta |k|^2|) part is added with K K^T
-      s.lam[l] = gr;
-      if (l == 0) s.GamC = __expf(gC);
+      sp->lam[l] = gr;
+      if (l == 0) sp->GamC = __expf(gC);
     }
     if (!OUT && hs_chunk) {
 #pragma unroll
@@ -229,6 +230,7 @@ struct Chunk {
           }
     }
     __syncthreads();
+    sp = lds_opaque(sp);
 
     // ---- 2. K K^T -> A (waves 0, 1) and Q K^T -> P (waves 2, 3).  Each wave takes a
     //         pair of row tiles {0, 3} or {1, 2} (5 lower tiles); its A-side
@@ -238,43 +240,44 @@ struct Chunk {
       const bool rows03 = (w & 1) == 0;
       const bool isq = w >= 2;
       if (!isq || OUT) {
-        const E* X = isq ? s.Q : s.K;
+        const E* X = isq ? sp->Q : sp->K;
         auto row = [&](auto RT_) {
           constexpr int RT = decltype(RT_)::value;
           Frag<E> xa[DK / 32];
 #pragma unroll
           for (int kb = 0; kb < DK / 32; ++kb) xa[kb] = ld_frag(X, LQ, 16 * RT + c16, 32 * kb);
-          f32x4 gr4 = *reinterpret_cast<const f32x4*>(&s.gam[16 * RT + 4 * g]);
-          f32x4 br4 = *reinterpret_cast<const f32x4*>(&s.beta[16 * RT + 4 * g]);
+          f32x4 gr4 = *reinterpret_cast<const f32x4*>(&sp->gam[16 * RT + 4 * g]);
+          f32x4 br4 = *reinterpret_cast<const f32x4*>(&sp->beta[16 * RT + 4 * g]);
 #pragma unroll
           for (int ct = 0; ct <= RT; ++ct) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) mma(acc, xa[kb], ld_frag(s.K, LQ, 16 * ct + c16, 32 * kb));
+            for (int kb = 0; kb < DK / 32; ++kb) mma(acc, xa[kb], ld_frag(sp->K, LQ, 16 * ct + c16, 32 * kb));
             const int c = 16 * ct + c16;
-            const float gc = s.gam[c];
+            const float gc = sp->gam[c];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = 16 * RT + 4 * g + i;
               const float dm = __expf(gr4[i] - gc);
               if (!isq) {
-                s.A[r * LA + c] = (c < r) ? br4[i] * acc[i] * dm : 0.f;
-                if (ct == RT && r == c) s.lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
+                sp->A[r * LA + c] = (c < r) ? br4[i] * acc[i] * dm : 0.f;
+                if (ct == RT && r == c) sp->lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
               } else {
-                s.P[r * LT + c] = to_e<E>((c <= r) ? acc[i] * dm : 0.f);
+                sp->P[r * LT + c] = to_e<E>((c <= r) ? acc[i] * dm : 0.f);
               }
             }
           }
         };
         if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
         else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
-        if (!isq) solve_diag_pair(s.A, s.T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
+        if (!isq) solve_diag_pair(sp->A, sp->T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
       }
     }
     __syncthreads();
+    sp = lds_opaque(sp);
     // lane 0's sum: every wave reduces the same values in the same order, so the
     // value (and the loop decisions taken on it) is identical across the workgroup
-    const float lam_c = __shfl(wave_sum(s.lam[l]), 0, 64);
+    const float lam_c = __shfl(wave_sum(sp->lam[l]), 0, 64);
 
     // next chunk's k, v, g, beta start their way from HBM (q follows later,
     // which keeps the prefetch registers out of the busiest stretch)
@@ -282,27 +285,30 @@ struct Chunk {
     if (OUT && nrows > 0) ld.load_q(p, ntok0, nrows, h);
 
     // ---- 3. off-diagonal blocks of T
-    solve_level1(s.A, s.T, w, nullptr);
+    solve_level1(sp->A, sp->T, w, nullptr);
     __syncthreads();
-    solve_level2(s.A, s.T, w, nullptr);
+    sp = lds_opaque(sp);
+    solve_level2(sp->A, sp->T, w, nullptr);
     __syncthreads();
+    sp = lds_opaque(sp);
 
     // ---- 4. -W = -T diag(beta Gam) K for row tile w (all key columns);
     //         Q h and Ut = T diag(beta) V for this wave's state columns.
     {
       Frag<E> xw[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) xw[kb] = ld_frag_scaled<E>(s.T, LA, 16 * w + c16, 32 * kb, s.bg);
+      for (int kb = 0; kb < 2; ++kb) xw[kb] = ld_frag_scaled<E>(sp->T, LA, 16 * w + c16, 32 * kb, sp->bg);
 #pragma unroll
       for (int ct = 0; ct < DK / 16; ++ct) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(acc, xw[kb], ld_frag(s.KT, LT, 16 * ct + c16, 32 * kb));
+        for (int kb = 0; kb < 2; ++kb) mma(acc, xw[kb], ld_frag(sp->KT, LT, 16 * ct + c16, 32 * kb));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s.W[(16 * w + 4 * g + i) * LQ + 16 * ct + c16] = to_e<E>(-acc[i]);
+        for (int i = 0; i < 4; ++i) sp->W[(16 * w + 4 * g + i) * LQ + 16 * ct + c16] = to_e<E>(-acc[i]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    sp = lds_opaque(sp);
     f32x4 u[4][NTW];
     {
       Frag<E> yv[NTW][2];
@@ -310,14 +316,14 @@ struct Chunk {
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) yv[nt][kb] = ld_frag(s.VT, LT, n0 + 16 * nt + c16, 32 * kb);
+          for (int kb = 0; kb < 2; ++kb) yv[nt][kb] = ld_frag(sp->VT, LT, n0 + 16 * nt + c16, 32 * kb);
       }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         Frag<E> xb[2];
         if (!CORR) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) xb[kb] = ld_frag_scaled<E>(s.T, LA, 16 * rt + c16, 32 * kb, s.beta);
+          for (int kb = 0; kb < 2; ++kb) xb[kb] = ld_frag_scaled<E>(sp->T, LA, 16 * rt + c16, 32 * kb, sp->beta);
         }
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
@@ -330,6 +336,7 @@ struct Chunk {
       }
     }
     __syncthreads();
+    sp = lds_opaque(sp);
 
     // ---- 5. state chain: U = Ut - W h ; O = scale (diag(Gam) Q h + P U) ; h' = Gam_C h + K^T (ek * U)
     Frag<E> hf[NTW][DK / 32];
@@ -341,13 +348,14 @@ struct Chunk {
     for (int rt = 0; rt < 4; ++rt) {
       Frag<E> xw[DK / 32];
 #pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) xw[kb] = ld_frag(s.W, LQ, 16 * rt + c16, 32 * kb);
+      for (int kb = 0; kb < DK / 32; ++kb) xw[kb] = ld_frag(sp->W, LQ, 16 * rt + c16, 32 * kb);
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) mma(u[rt][nt], xw[kb], hf[nt][kb]);
     }
     __builtin_amdgcn_sched_barrier(0);
+    sp = lds_opaque(sp);
     if (OUT) {
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
@@ -358,16 +366,16 @@ struct Chunk {
         for (int rt = 0; rt < 4; ++rt) {
           f32x4 o = zero4();
 #pragma unroll
-          for (int kb = 0; kb < DK / 32; ++kb) mma(o, ld_frag(s.Q, LQ, 16 * rt + c16, 32 * kb), hf[nt][kb]);
-          const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&s.Gam[16 * rt + 4 * g]);
+          for (int kb = 0; kb < DK / 32; ++kb) mma(o, ld_frag(sp->Q, LQ, 16 * rt + c16, 32 * kb), hf[nt][kb]);
+          const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&sp->Gam[16 * rt + 4 * g]);
           o = o * gm4;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) mma(o, ld_frag(s.P, LT, 16 * rt + c16, 32 * kb), uf[kb]);
+          for (int kb = 0; kb < 2; ++kb) mma(o, ld_frag(sp->P, LT, 16 * rt + c16, 32 * kb), uf[kb]);
           o = o * p.scale;
           const int col = n0 + 16 * nt + c16;
           if (!CORR) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s.O[(16 * rt + 4 * g + i) * LO + col] = to_e<E>(o[i]);
+            for (int i = 0; i < 4; ++i) sp->O[(16 * rt + 4 * g + i) * LO + col] = to_e<E>(o[i]);
           } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -382,13 +390,14 @@ struct Chunk {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    sp = lds_opaque(sp);
     {
-      const float gc = s.GamC;
+      const float gc = sp->GamC;
       f32x4 e0[2], e1[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        e0[kb] = *reinterpret_cast<const f32x4*>(&s.ek[32 * kb + 4 * g]);
-        e1[kb] = *reinterpret_cast<const f32x4*>(&s.ek[32 * kb + 16 + 4 * g]);
+        e0[kb] = *reinterpret_cast<const f32x4*>(&sp->ek[32 * kb + 4 * g]);
+        e1[kb] = *reinterpret_cast<const f32x4*>(&sp->ek[32 * kb + 16 + 4 * g]);
       }
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
@@ -399,13 +408,14 @@ struct Chunk {
         for (int t = 0; t < DK / 16; ++t) {
           hacc[t][nt] = hacc[t][nt] * gc;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) mma(hacc[t][nt], ld_frag(s.KT, LT, 16 * t + c16, 32 * kb), us[kb]);
+          for (int kb = 0; kb < 2; ++kb) mma(hacc[t][nt], ld_frag(sp->KT, LT, 16 * t + c16, 32 * kb), us[kb]);
         }
       }
     }
     __syncthreads();
+    sp = lds_opaque(sp);
 
-    // ---- 6. output tile out (coalesced); the next chunk's staging does not touch s.O
+    // ---- 6. output tile out (coalesced); the next chunk's staging does not touch sp->O
     if (OUT && !CORR) {
       constexpr int VEC = 16 / sizeof(E);
       typedef E vec_t __attribute__((__vector_size__(16)));
@@ -413,7 +423,7 @@ struct Chunk {
         const int r = e / (DV / VEC), c0 = (e % (DV / VEC)) * VEC;
         if (r < rows)
           *reinterpret_cast<vec_t*>(static_cast<E*>(p.o) + ((tok0 + r) * H + h) * DV + c0) =
-              *reinterpret_cast<const vec_t*>(&s.O[r * LO + c0]);
+              *reinterpret_cast<const vec_t*>(&sp->O[r * LO + c0]);
       }
     }
     return lam_c;

@@ -218,3 +218,77 @@ __device__ __forceinline__ void solve_T(const float* A, float* T, const float* r
 }
 
 }  // namespace gdn
+
+namespace gdn {
+
+// Register prefetch of up to three [CH x D_t] tiles of one chunk (D_t = 0:
+// tensor absent), moved as 4-row x 16-byte blocks so that each block can be
+// written to LDS row-major and/or transposed.  Every tensor has its own
+// compile-time block loop, so no pointer or stride is ever selected at run
+// time.  Rows at or past `rows` are loaded from the last valid row (finite
+// data); the kernels mask those rows through beta = 0, g = 0 and their output
+// masks, which leaves every real result unchanged.  load() only issues global
+// loads; store() consumes them.
+template <class E, int NT, int D>
+struct TilePart {
+  static constexpr int VEC = 16 / (int)sizeof(E);
+  static constexpr int NBLK = D > 0 ? (CH / 4) * (D / VEC) : 0;
+  static constexpr int NB = (NBLK + NT - 1) / NT;
+  static constexpr int BPR = D > 0 ? D / VEC : 1;  // blocks per 4-row group
+  typedef E vec_t __attribute__((__vector_size__(16)));
+  vec_t blk[NB > 0 ? NB : 1][4];
+
+  __device__ __forceinline__ void load(const E* src, int64_t gld, int rows) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int id = threadIdx.x + b * NT;
+      if (NB * NT == NBLK || id < NBLK) {
+        const int r0 = (id / BPR) * 4, c0 = (id % BPR) * VEC;
+        const E* p = src + c0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) blk[b][j] = *reinterpret_cast<const vec_t*>(p + (int64_t)min(r0 + j, rows - 1) * gld);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(E* dst, int ld, E* dstT, int ldT) const {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int id = threadIdx.x + b * NT;
+      if (NB * NT == NBLK || id < NBLK) {
+        const int r0 = (id / BPR) * 4, c0 = (id % BPR) * VEC;
+        if (dst) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4)
+              st4<E>(dst + (r0 + j) * ld + c0 + e, blk[b][j][e], blk[b][j][e + 1], blk[b][j][e + 2], blk[b][j][e + 3]);
+        }
+        if (dstT) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e)
+            st4<E>(dstT + (c0 + e) * ldT + r0, blk[b][0][e], blk[b][1][e], blk[b][2][e], blk[b][3][e]);
+        }
+      }
+    }
+  }
+};
+
+// g / beta of one chunk for threads 0..63 (one row each), masked at use.
+template <class E>
+struct ScalarPart {
+  float gr;
+  E be;
+  int nrow;
+  __device__ __forceinline__ void load(const float* g, const E* beta, int64_t tok0, int H, int h, int rows) {
+    if (threadIdx.x < 64) {
+      const int64_t si = (tok0 + min((int)threadIdx.x, rows - 1)) * H + h;
+      gr = g[si];
+      be = beta[si];
+      nrow = rows;
+    }
+  }
+  __device__ __forceinline__ float g_at(int l) const { return l < nrow ? gr : 0.f; }
+  __device__ __forceinline__ float beta_at(int l) const { return l < nrow ? to_f(be) : 0.f; }
+};
+
+}  // namespace gdn
