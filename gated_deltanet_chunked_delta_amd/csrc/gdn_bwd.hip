@@ -99,17 +99,16 @@ struct RevChunk {
 
     // ---- 1. gradient at the chunk end out; tiles into LDS; scalars
     S* sp = lds_opaque(&s0);
+    // stored transposed, [DV][DK]: the lane's four rows of one column are contiguous
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          E* dst = dhs_chunk + (16 * t + 4 * g + i) * DV + n0 + 16 * nt + c16;
-          float val = dh[t][nt][i];
-          if (CORR) val += to_f(*dst);
-          *dst = to_e<E>(val);
-        }
+      for (int nt = 0; nt < NTW; ++nt) {
+        E* dst = dhs_chunk + (n0 + 16 * nt + c16) * DK + 16 * t + 4 * g;
+        f32x4 val = dh[t][nt];
+        if (CORR) val = val + ld4f<E>(dst);
+        st4f<E>(dst, val);
+      }
     S& s1 = *sp;
     ld.k.store(s1.K, LQ, s1.KT, LT);
     if (!CORR) {
@@ -431,34 +430,44 @@ struct alignas(16) GradSmem {
   using L = GradLayout<E, DK, DV>;
   alignas(16) char slot[L::NSLOT][L::SLOT];
   alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH];
-  float pg[4][CH], pb[4][CH], pc[4][CH];
-  float pl[4], ph[4];
+  float pg[4][CH], pb[4][CH];  // row sums of the per-wave dgam / dbeta terms, by column group
+  float p7[4][CH], c7[4][CH];  // row sums of GP*P by column tile, column sums by row tile
+  float c10[2][CH];            // column sums of GA*A by row half
+  float pl[8], ph[8];
   float GamC;
 };
 
 // slot roles
 enum { SK = 0, SKT = 1, SQ = 2, SV = 3, SDO = 4, ST = 5, SKD = 6, SP = 7, SDU = 8 };
 
+// One chunk per workgroup of 8 waves.  Wave w works on column group cw = w % 4
+// (key columns [cw Dk/4, (cw+1) Dk/4), value columns [cw Dv/4, ...)) and row
+// half rh = w / 4 (row tiles 2 rh, 2 rh + 1) of every per-row product, so two
+// waves share each SIMD and every accumulator array is half the size it would
+// be with four waves.  Sums over rows or columns that cross those halves go
+// through small LDS arrays with a single writer per entry (deterministic).
 template <class E, int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_grad_kernel(GradParams p) {
+__global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   using L = GradLayout<E, DK, DV>;
-  constexpr int NT = 256;
+  constexpr int NT = 512;
   constexpr int LK = L::LK, LV = L::LV, LT = L::LT, LA = L::LA;
-  constexpr int CTK = DK / 64, CTV = DV / 64;  // 16-wide column tiles per wave
+  constexpr int CTK = DK / 64, CTV = DV / 64;  // 16-wide column tiles per column group
   __shared__ GradSmem<E, DK, DV> s;
   auto slotE = [&](int i) { return reinterpret_cast<E*>(s.slot[i]); };
   auto slotF = [&](int i) { return reinterpret_cast<float*>(s.slot[i]); };
 
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const int cw = w & 3, rh = w >> 2;
   const int2 ctab = p.chunk_tab[blockIdx.x];
   const int n = ctab.x, jc = ctab.y, h = blockIdx.y, H = p.H;
   const int len = p.seq.len(n);
   const int64_t tok0 = p.seq.start(n) + (int64_t)jc * CH;
   const int rows = min(CH, len - jc * CH);
   const size_t SS = (size_t)DK * DV;
+  // h_c and dh'_c of this chunk, both stored transposed ([DV][DK] row-major)
   const E* hs = static_cast<const E*>(p.hs) + ((size_t)blockIdx.x * H + h) * SS;
   const E* dhs = static_cast<const E*>(p.dhs) + ((size_t)blockIdx.x * H + h) * SS;
-  const int d0 = w * (DK / 4), n0 = w * (DV / 4);
+  const int d0 = cw * (DK / 4), n0 = cw * (DV / 4);
   const float scale = p.scale;
 
   E* sK = slotE(SK);
@@ -468,19 +477,41 @@ __global__ __launch_bounds__(256) void gdn_grad_kernel(GradParams p) {
   float* sP = slotF(SP);
   E* sDU = slotE(SDU);
 
-  // ---- P1: staging; zero T and P (their upper parts are read as zeros)
+  // ---- P1: staging (all four tiles in flight at once; rows past the end are
+  //          zero); zero T, P and the cross-wave sum arrays.  h and dh' down this
+  //          wave's value columns (the operands of P5) are requested right
+  //          after the tiles and stay in flight until P5.
+  Frag<E> hk[CTV][DK / 32], dk_[CTV][DK / 32];
   {
     const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
     const E* k = static_cast<const E*>(p.k) + (tok0 * H + h) * DK;
     const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
     const E* d = static_cast<const E*>(p.dout) + (tok0 * H + h) * DV;
-    stage_tile<E, DK, NT>(k, (int64_t)H * DK, rows, sK, LK, sKT, LT);
-    stage_tile<E, DK, NT>(q, (int64_t)H * DK, rows, slotE(SQ), LK, nullptr, 0);
-    stage_tile<E, DV, NT>(v, (int64_t)H * DV, rows, slotE(SV), LV, nullptr, 0);
-    stage_tile<E, DV, NT>(d, (int64_t)H * DV, rows, slotE(SDO), LV, nullptr, 0);
-    for (int e = tid; e < CH * CH; e += NT) {
-      sT[(e >> 6) * LA + (e & 63)] = 0.f;
-      sP[(e >> 6) * LA + (e & 63)] = 0.f;
+    // waves 0..3 bring K and Q, waves 4..7 V and dO
+    const int ht = tid & (NT / 2 - 1);
+    TilePart<E, NT / 2, DK> tk, tq;
+    TilePart<E, NT / 2, DV> tv, td;
+    if (rh == 0) {
+      tk.template load<true>(k, (int64_t)H * DK, rows, ht);
+      tq.template load<true>(q, (int64_t)H * DK, rows, ht);
+    } else {
+      tv.template load<true>(v, (int64_t)H * DV, rows, ht);
+      td.template load<true>(d, (int64_t)H * DV, rows, ht);
+    }
+#pragma unroll
+    for (int nt = 0; nt < CTV; ++nt)
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        hk[nt][kb] = ld_frag(hs, DK, n0 + 16 * nt + c16, 32 * kb);
+        dk_[nt][kb] = ld_frag(dhs, DK, n0 + 16 * nt + c16, 32 * kb);
+      }
+    for (int e = 4 * tid; e < CH * CH; e += 4 * NT) {
+      *reinterpret_cast<f32x4*>(&sT[(e >> 6) * LA + (e & 63)]) = zero4();
+      *reinterpret_cast<f32x4*>(&sP[(e >> 6) * LA + (e & 63)]) = zero4();
+    }
+    for (int e = tid; e < 4 * CH; e += NT) {
+      (&s.p7[0][0])[e] = 0.f;
+      (&s.c7[0][0])[e] = 0.f;
     }
     if (w == 0) {
       const bool valid = l < rows;
@@ -497,11 +528,18 @@ __global__ __launch_bounds__(256) void gdn_grad_kernel(GradParams p) {
       s.bg[l] = bt * Gm;
       if (l == 0) s.GamC = __expf(gC);
     }
+    if (rh == 0) {
+      tk.store(sK, LK, sKT, LT, ht);
+      tq.store(slotE(SQ), LK, nullptr, 0, ht);
+    } else {
+      tv.store(slotE(SV), LV, nullptr, 0, ht);
+      td.store(slotE(SDO), LV, nullptr, 0, ht);
+    }
   }
   __syncthreads();
 
-  // ---- P2: KD = strict_lower(K K^T * D), P = (Q K^T) * M
-  for (int ti = w; ti < 20; ti += 4) {
+  // ---- P2: KD = strict_lower(K K^T * D), P = (Q K^T) * M  (20 lower tiles)
+  for (int ti = w; ti < 20; ti += 8) {
     const bool isq = ti >= 10;
     const int tt = isq ? ti - 10 : ti;
     int rt = 0;
@@ -524,74 +562,76 @@ __global__ __launch_bounds__(256) void gdn_grad_kernel(GradParams p) {
   __syncthreads();
 
   // ---- P3: T = (I + diag(beta) KD)^-1
-  solve_T(sKD, sT, s.beta);
+  if (w < 2) solve_diag_pair(sKD, sT, w, 3 - w, s.beta);
+  __syncthreads();
+  solve_level1(sKD, sT, w, s.beta);
+  __syncthreads();
+  solve_level2(sKD, sT, w, s.beta);
+  __syncthreads();
 
-  // per-lane partial sums, reduced at the end
-  f32x4 rg[4], rb[4];  // dgam / dbeta contributions of rows 16rt+4g+i from this lane's columns
-  float cc[4] = {0.f, 0.f, 0.f, 0.f};  // dgam contributions of column 16ct+c16 from this lane's rows
+  // per-lane partial sums of this wave's rows (row tiles 2 rh + j)
+  f32x4 rg[2], rb[2];  // dgam / dbeta terms
   float lastsum = 0.f, hdh = 0.f;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) { rg[rt] = zero4(); rb[rt] = zero4(); }
+  for (int j = 0; j < 2; ++j) { rg[j] = zero4(); rb[j] = zero4(); }
 
-  // ---- P4: Ut = T diag(beta) V (own value columns), W = T diag(beta Gam) K -> slot V
+  // ---- P4: Ut = T diag(beta) V (own rows and value columns); then W = T diag(beta Gam) K -> slot V
   Frag<E> vr[2][CTV];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int nt = 0; nt < CTV; ++nt) vr[kb][nt] = ld_fragC<E>(slotE(SV), LV, 32 * kb, n0 + 16 * nt + c16);
-  f32x4 u[4][CTV];
+    for (int nt = 0; nt < CTV; ++nt) vr[kb][nt] = ld_fragC_q<E>(slotE(SV), LV, 32 * kb, n0 + 16 * nt);
+  f32x4 u[2][CTV];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int nt = 0; nt < CTV; ++nt) {
-      u[rt][nt] = zero4();
+      const int rt = 2 * rh + j;
+      u[j][nt] = zero4();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mma(u[rt][nt], ld_frag_scaled<E>(sT, LA, 16 * rt + c16, 32 * kb, s.beta), vr[kb][nt]);
+      for (int kb = 0; kb < 2; ++kb) mma(u[j][nt], ld_frag_scaled<E>(sT, LA, 16 * rt + c16, 32 * kb, s.beta), vr[kb][nt]);
     }
+  // the V entries of this wave's rows, for dbeta in P8
+  Frag<E> vown[CTV];
+#pragma unroll
+  for (int nt = 0; nt < CTV; ++nt) vown[nt] = rh ? vr[1][nt] : vr[0][nt];
   __syncthreads();
   {
     E* sW = slotE(SV);
-    for (int ti = w; ti < 4 * (DK / 16); ti += 4) {
+    for (int ti = w; ti < 4 * (DK / 16); ti += 8) {
       const int rt = ti / (DK / 16), dt = ti % (DK / 16);
       f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         mma(acc, ld_frag_scaled<E>(sT, LA, 16 * rt + c16, 32 * kb, s.bg), ld_frag(sKT, LT, 16 * dt + c16, 32 * kb));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sW[(16 * rt + 4 * g + i) * LK + 16 * dt + c16] = to_e<E>(acc[i]);
+      st_tile_rows<E>(sW, LK, 16 * rt, 16 * dt, acc);
     }
   }
   __syncthreads();
 
-  // ---- P5: U = Ut - W h (own value columns), dU = diag(ek) K dh' + scale P^T dO
-  f32x4 du[4][CTV];
+  // ---- P5: U = Ut - W h, dU = diag(ek) K dh' + scale P^T dO (own rows and value columns)
+  f32x4 du[2][CTV];
   {
     const E* sW = slotE(SV);
 #pragma unroll
     for (int nt = 0; nt < CTV; ++nt) {
-      Frag<E> hk[DK / 32], dk_[DK / 32];
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) {
-        hk[kb] = ld_fragC<E>(hs, DV, 32 * kb, n0 + 16 * nt + c16);
-        dk_[kb] = ld_fragC<E>(dhs, DV, 32 * kb, n0 + 16 * nt + c16);
-      }
       Frag<E> dor[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) dor[kb] = ld_fragC<E>(slotE(SDO), LV, 32 * kb, n0 + 16 * nt + c16);
+      for (int kb = 0; kb < 2; ++kb) dor[kb] = ld_fragC_q<E>(slotE(SDO), LV, 32 * kb, n0 + 16 * nt);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+      for (int j = 0; j < 2; ++j) {
+        const int rt = 2 * rh + j;
         f32x4 wh = zero4(), kd = zero4();
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
-          mma(wh, ld_frag(sW, LK, 16 * rt + c16, 32 * kb), hk[kb]);
-          mma(kd, ld_frag(sK, LK, 16 * rt + c16, 32 * kb), dk_[kb]);
+          mma(wh, ld_frag(sW, LK, 16 * rt + c16, 32 * kb), hk[nt][kb]);
+          mma(kd, ld_frag(sK, LK, 16 * rt + c16, 32 * kb), dk_[nt][kb]);
         }
-        u[rt][nt] = u[rt][nt] - wh;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kd[i] *= s.ek[16 * rt + 4 * g + i];
+        u[j][nt] = u[j][nt] - wh;
+        kd = kd * *reinterpret_cast<const f32x4*>(&s.ek[16 * rt + 4 * g]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) mma(kd, ld_fragT<E>(sP, LA, 16 * rt + c16, 32 * kb, scale), dor[kb]);
-        du[rt][nt] = kd;
+        du[j][nt] = kd;
       }
     }
   }
@@ -599,37 +639,38 @@ __global__ __launch_bounds__(256) void gdn_grad_kernel(GradParams p) {
   {
     E* sU = slotE(SV);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int nt = 0; nt < CTV; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * g + i, c = n0 + 16 * nt + c16;
-          sU[r * LV + c] = to_e<E>(u[rt][nt][i]);
-          sDU[r * LV + c] = to_e<E>(du[rt][nt][i]);
-        }
+      for (int nt = 0; nt < CTV; ++nt) {
+        st_tile_rows<E>(sU, LV, 16 * (2 * rh + j), n0 + 16 * nt, u[j][nt]);
+        st_tile_rows<E>(sDU, LV, 16 * (2 * rh + j), n0 + 16 * nt, du[j][nt]);
+      }
   }
   __syncthreads();
 
-  // ---- P6: GW = -dU h^T, dQ1 = dO h^T, Udh = U dh'^T (own key columns)
-  Frag<E> qr[2][CTK];
+  // ---- P6: GW = -dU h^T, dQ1 = dO h^T, Udh = U dh'^T (own rows and key columns)
+  Frag<E> qr[2][CTK];  // Q down the own key columns, all rows
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int dt = 0; dt < CTK; ++dt) qr[kb][dt] = ld_fragC<E>(slotE(SQ), LK, 32 * kb, d0 + 16 * dt + c16);
-  f32x4 gw[4][CTK], dq1[4][CTK], udh[4][CTK];
+    for (int dt = 0; dt < CTK; ++dt) qr[kb][dt] = ld_fragC_q<E>(slotE(SQ), LK, 32 * kb, d0 + 16 * dt);
+  f32x4 gw[2][CTK], dq1[2][CTK], udh[2][CTK];
 #pragma unroll
   for (int dt = 0; dt < CTK; ++dt) {
     Frag<E> hn[DV / 32], dhn[DV / 32];
 #pragma unroll
     for (int kb = 0; kb < DV / 32; ++kb) {
-      hn[kb] = ld_frag(hs, DV, d0 + 16 * dt + c16, 32 * kb);
-      dhn[kb] = ld_frag(dhs, DV, d0 + 16 * dt + c16, 32 * kb);
+      hn[kb] = ld_fragC_q<E>(hs, DK, 32 * kb, d0 + 16 * dt);
+      dhn[kb] = ld_fragC_q<E>(dhs, DK, 32 * kb, d0 + 16 * dt);
+      if (rh == 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) hdh += frag_at(hn[kb], j) * frag_at(dhn[kb], j);
+        for (int jj = 0; jj < 8; ++jj) hdh += frag_at(hn[kb], jj) * frag_at(dhn[kb], jj);
+      }
     }
+    const Frag<E> qown = rh ? qr[1][dt] : qr[0][dt];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int j = 0; j < 2; ++j) {
+      const int rt = 2 * rh + j;
       f32x4 a = zero4(), b = zero4(), c = zero4();
 #pragma unroll
       for (int kb = 0; kb < DV / 32; ++kb) {
@@ -637,34 +678,35 @@ __global__ __launch_bounds__(256) void gdn_grad_kernel(GradParams p) {
         mma(b, ld_frag(slotE(SDO), LV, 16 * rt + c16, 32 * kb), hn[kb]);
         mma(c, ld_frag(slotE(SV), LV, 16 * rt + c16, 32 * kb), dhn[kb]);
       }
-      gw[rt][dt] = zero4() - a;
-      dq1[rt][dt] = b;
-      udh[rt][dt] = c;
+      gw[j][dt] = zero4() - a;
+      dq1[j][dt] = b;
+      udh[j][dt] = c;
       const int dcol = d0 + 16 * dt + c16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
-        const float qv = frag_at(qr[rt >> 1][dt], (rt & 1) * 4 + i);
+        const float qv = frag_at(qown, 4 * j + i);
         const float kv = to_f(sK[r * LK + dcol]);
-        rg[rt][i] += scale * s.Gam[r] * qv * b[i] - s.ek[r] * kv * c[i];
+        rg[j][i] += scale * s.Gam[r] * qv * b[i] - s.ek[r] * kv * c[i];
         lastsum += s.ek[r] * kv * c[i];
       }
     }
   }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) { pin(rg[j]); pin(rb[j]); }
+  pin(lastsum);
+  pin(hdh);
   __syncthreads();  // Q reads done: slot Q becomes GW
   {
     E* sGW = slotE(SQ);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int dt = 0; dt < CTK; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sGW[(16 * rt + 4 * g + i) * LK + d0 + 16 * dt + c16] = to_e<E>(gw[rt][dt][i]);
+      for (int dt = 0; dt < CTK; ++dt) st_tile_rows<E>(sGW, LK, 16 * (2 * rh + j), d0 + 16 * dt, gw[j][dt]);
   }
 
-  // ---- P7: GP = scale (dO U^T) * [i <= r]; GP*P row/column sums; P -> GP * M
-  for (int ti = w; ti < 10; ti += 4) {
+  // ---- P7: GP = scale (dO U^T) * [i <= r]; GP*P row / column sums; P -> GP * M
+  for (int ti = w; ti < 10; ti += 8) {
     int rt = 0;
     while ((rt + 1) * (rt + 2) / 2 <= ti) ++rt;
     const int ct = ti - rt * (rt + 1) / 2;
@@ -673,99 +715,131 @@ __global__ __launch_bounds__(256) void gdn_grad_kernel(GradParams p) {
     for (int kb = 0; kb < DV / 32; ++kb)
       mma(acc, ld_frag(slotE(SDO), LV, 16 * rt + c16, 32 * kb), ld_frag(slotE(SV), LV, 16 * ct + c16, 32 * kb));
     const int c = 16 * ct + c16;
+    f32x4 rs4;
     float csum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rt + 4 * g + i;
       const float gp = (c <= r) ? scale * acc[i] : 0.f;
-      const float pv = sP[r * LA + c];
-      const float gpp = gp * pv;
-      rg[rt][i] += gpp;
+      const float gpp = gp * sP[r * LA + c];
+      rs4[i] = gpp;
       csum += gpp;
       sP[r * LA + c] = (c <= r) ? gp * __expf(s.gam[r] - s.gam[c]) : 0.f;
     }
-    cc[ct] -= csum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs4[i] = row16_sum(rs4[i]);
+    csum += __shfl_xor(csum, 16, 64);
+    csum += __shfl_xor(csum, 32, 64);
+    if (c16 == 0) *reinterpret_cast<f32x4*>(&s.p7[ct][16 * rt + 4 * g]) = rs4;
+    if (g == 0) s.c7[rt][c] = -csum;
   }
   __syncthreads();
 
-  // ---- P8: XW = T^T GW, XU = T^T dU; dV; row dots; dK partial
-  f32x4 dkacc[4][CTK];
+  // ---- P8: XW = T^T GW (own rows); row dots; dK partial (with GPM^T Q); dQ
+  f32x4 dkacc[2][CTK];
   {
-    Frag<E> gwf[2][CTK];
+    const E* sGW = slotE(SQ);
+    // K is re-read here: an opaque pointer keeps the compiler from holding the
+    // values read in P6 in registers (or scratch) until now
+    const E* sKr = lds_opaque(sK);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int dt = 0; dt < CTK; ++dt) {
+      Frag<E> gwf[2];
 #pragma unroll
-      for (int dt = 0; dt < CTK; ++dt) pack_frag(gwf[kb][dt], gw[2 * kb][dt], gw[2 * kb + 1][dt]);
+      for (int kb = 0; kb < 2; ++kb) gwf[kb] = ld_fragC_q<E>(sGW, LK, 32 * kb, d0 + 16 * dt);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int dt = 0; dt < CTK; ++dt) {
+      for (int j = 0; j < 2; ++j) {
+        const int rt = 2 * rh + j;
         f32x4 xw = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(xw, ld_fragT<E>(sT, LA, 16 * rt + c16, 32 * kb, 1.f), gwf[kb][dt]);
+        for (int kb = 0; kb < 2; ++kb) mma(xw, ld_fragT<E>(sT, LA, 16 * rt + c16, 32 * kb, 1.f), gwf[kb]);
         const int dcol = d0 + 16 * dt + c16;
+        f32x4 pq = zero4();  // GPM^T Q (GPM is final since P7)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) mma(pq, ld_fragT<E>(sP, LA, 16 * rt + c16, 32 * kb, 1.f), qr[kb][dt]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * g + i;
-          const float kv = to_f(sK[r * LK + dcol]);
+          const float kv = to_f(sKr[r * LK + dcol]);
           const float xk = xw[i] * kv;
-          rb[rt][i] += s.Gam[r] * xk;
-          rg[rt][i] += s.bg[r] * xk;
-          dkacc[rt][dt][i] = s.bg[r] * xw[i] + s.ek[r] * udh[rt][dt][i];
+          rb[j][i] += s.Gam[r] * xk;
+          rg[j][i] += s.bg[r] * xk;
+          dkacc[j][dt][i] = s.bg[r] * xw[i] + s.ek[r] * udh[j][dt][i] + pq[i];
         }
       }
+    }
   }
+  // dQ = scale diag(Gam) dQ1 + GPM K, final here (slot dO was last read in P7)
   {
-    Frag<E> duf[2][CTV];
+    E* sDQ = slotE(SDO);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int nt = 0; nt < CTV; ++nt) pack_frag(duf[kb][nt], du[2 * kb][nt], du[2 * kb + 1][nt]);
-    E* dv = static_cast<E*>(p.dv) + (tok0 * H + h) * DV;
+      for (int dt = 0; dt < CTK; ++dt) {
+        const int rt = 2 * rh + j;
+        f32x4 a = zero4();
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int nt = 0; nt < CTV; ++nt) {
-        f32x4 xu = zero4();
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(xu, ld_fragT<E>(sT, LA, 16 * rt + c16, 32 * kb, 1.f), duf[kb][nt]);
-        const int ncol = n0 + 16 * nt + c16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * g + i;
-          rb[rt][i] += xu[i] * frag_at(vr[rt >> 1][nt], (rt & 1) * 4 + i);
-          if (r < rows) dv[(int64_t)r * H * DV + ncol] = to_e<E>(s.beta[r] * xu[i]);
-        }
+        for (int kb = 0; kb < 2; ++kb)
+          mma(a, ld_frag_f32<E>(sP, LA, 16 * rt + c16, 32 * kb), ld_frag(sKT, LT, d0 + 16 * dt + c16, 32 * kb));
+        const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&s.Gam[16 * rt + 4 * g]);
+        st_tile_rows<E>(sDQ, LK, 16 * rt, d0 + 16 * dt, dq1[j][dt] * gm4 * scale + a);
       }
-  }
-  // slot dO is free: reload V row-major there for G_T
-  {
-    const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
-    stage_tile<E, DV, NT>(v, (int64_t)H * DV, rows, slotE(SDO), LV, nullptr, 0);
   }
   __syncthreads();
 
   // ---- P9: GT = dU V^T diag(beta) + GW K^T diag(beta Gam) -> slot V (fp32)
   {
+    // every tile of this wave has column tile cw, so it needs V rows 16 cw..
+    // only: read them from global (rows past the end are copies of the last
+    // one; beta = 0 there removes them)
+    Frag<E> vf[DV / 32];
+    {
+      const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
+      const int vrow = min(16 * cw + c16, rows - 1);
+#pragma unroll
+      for (int kb = 0; kb < DV / 32; ++kb) vf[kb] = ld_frag(v + (int64_t)vrow * H * DV, 0, 0, 32 * kb);
+    }
     float* sGT = slotF(SV);
-    for (int ti = w; ti < 16; ti += 4) {
-      const int rt = ti >> 2, ct = ti & 3;
+    const int c = 16 * cw + c16;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rt = rh + 2 * j;
       f32x4 a = zero4(), b = zero4();
 #pragma unroll
-      for (int kb = 0; kb < DV / 32; ++kb)
-        mma(a, ld_frag(sDU, LV, 16 * rt + c16, 32 * kb), ld_frag(slotE(SDO), LV, 16 * ct + c16, 32 * kb));
+      for (int kb = 0; kb < DV / 32; ++kb) mma(a, ld_frag(sDU, LV, 16 * rt + c16, 32 * kb), vf[kb]);
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb)
-        mma(b, ld_frag(slotE(SQ), LK, 16 * rt + c16, 32 * kb), ld_frag(sK, LK, 16 * ct + c16, 32 * kb));
-      const int c = 16 * ct + c16;
-      // U (slot V) must not be overwritten before every wave finished P7, which the barrier above ensures
+        mma(b, ld_frag(slotE(SQ), LK, 16 * rt + c16, 32 * kb), ld_frag(sK, LK, c, 32 * kb));
+      // U (slot V) is no longer read: every wave finished P7 before the barrier above
 #pragma unroll
       for (int i = 0; i < 4; ++i) sGT[(16 * rt + 4 * g + i) * LA + c] = s.beta[c] * a[i] + s.bg[c] * b[i];
     }
   }
   __syncthreads();
 
-  // ---- P10: Z = GT T^T (own 16 columns), GA = strict_lower(-T^T Z); E -> S = E + E^T (slot KD)
+  // ---- P10: Z = GT T^T (column tile cw, all rows), GA = strict_lower(-T^T Z) (own
+  //           rows); E -> S = E + E^T (slot KD)
+  // XU = T^T dU (own rows and value columns) -> dV into slot Q (GW was last read in P9)
+  {
+    E* sDV = slotE(SQ);
+#pragma unroll
+    for (int nt = 0; nt < CTV; ++nt) {
+      Frag<E> duf[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) duf[kb] = ld_fragC_q<E>(sDU, LV, 32 * kb, n0 + 16 * nt);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rt = 2 * rh + j;
+        f32x4 xu = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) mma(xu, ld_fragT<E>(sT, LA, 16 * rt + c16, 32 * kb, 1.f), duf[kb]);
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s.beta[16 * rt + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rb[j][i] += xu[i] * frag_at(vown[nt], 4 * j + i);
+        st_tile_rows<E>(sDV, LV, 16 * rt, n0 + 16 * nt, xu * b4);
+      }
+    }
+  }
   {
     const float* sGT = slotF(SV);
     f32x4 z[4];
@@ -774,16 +848,17 @@ __global__ __launch_bounds__(256) void gdn_grad_kernel(GradParams p) {
       z[rt] = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        mma(z[rt], ld_frag(sGT, LA, 16 * rt + c16, 32 * kb), ld_frag(sT, LA, 16 * w + c16, 32 * kb));
+        mma(z[rt], ld_frag(sGT, LA, 16 * rt + c16, 32 * kb), ld_frag(sT, LA, 16 * cw + c16, 32 * kb));
     }
     Frag<float> zf[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) pack_frag(zf[kb], z[2 * kb], z[2 * kb + 1]);
-    const int c = 16 * w + c16;
+    const int c = 16 * cw + c16;
     float csum = 0.f;
-    f32x4 ga[4], kdv[4];
+    f32x4 ga[2];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int j = 0; j < 2; ++j) {
+      const int rt = 2 * rh + j;
       f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) mma(acc, ld_fragT<float>(sT, LA, 16 * rt + c16, 32 * kb, -1.f), zf[kb]);
@@ -793,98 +868,82 @@ __global__ __launch_bounds__(256) void gdn_grad_kernel(GradParams p) {
         const float gav = (c < r) ? acc[i] : 0.f;
         const float kd = sKD[r * LA + c];
         const float gaa = gav * s.beta[r] * kd;
-        rg[rt][i] += gaa;
+        rg[j][i] += gaa;
         csum += gaa;
-        rb[rt][i] += gav * kd;
-        ga[rt][i] = gav;
-        kdv[rt][i] = kd;
+        rb[j][i] += gav * kd;
+        ga[j][i] = gav;
       }
     }
-    cc[w] -= csum;
+    csum += __shfl_xor(csum, 16, 64);
+    csum += __shfl_xor(csum, 32, 64);
+    if (g == 0) s.c10[rh][c] = -csum;
     __syncthreads();  // every wave has read its KD entries: slot KD becomes S
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
+        const int r = 16 * (2 * rh + j) + 4 * g + i;
         if (c <= r) {
-          const float ev = s.beta[r] * ga[rt][i] * __expf(s.gam[r] - s.gam[c]);
+          const float ev = s.beta[r] * ga[j][i] * __expf(s.gam[r] - s.gam[c]);
           sKD[r * LA + c] = ev;
           if (c < r) sKD[c * LA + r] = ev;
         }
       }
-    (void)kdv;
   }
   __syncthreads();
 
-  // ---- P11: dQ = scale diag(Gam) dQ1 + GPM K ; dK += GPM^T Q + S K
+  // ---- P11: dK = dK partial + S K (own rows and key columns) -> slot K
+  //           (free since P9).  The three gradient tiles are written out after
+  //           the last barrier, so that no load of this kernel waits behind a store.
   {
-    E* dq = static_cast<E*>(p.dq) + (tok0 * H + h) * DK;
-    E* dk = static_cast<E*>(p.dk) + (tok0 * H + h) * DK;
+    E* sDK = slotE(SK);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int dt = 0; dt < CTK; ++dt) {
-        f32x4 a = zero4(), b = dkacc[rt][dt];
+        const int rt = 2 * rh + j;
+        f32x4 b = dkacc[j][dt];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const Frag<E> kt = ld_frag(sKT, LT, d0 + 16 * dt + c16, 32 * kb);
-          mma(a, ld_frag_f32<E>(sP, LA, 16 * rt + c16, 32 * kb), kt);
-          mma(b, ld_frag_f32<E>(sKD, LA, 16 * rt + c16, 32 * kb), kt);
-          mma(b, ld_fragT<E>(sP, LA, 16 * rt + c16, 32 * kb, 1.f), qr[kb][dt]);
-        }
-        const int dcol = d0 + 16 * dt + c16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * g + i;
-          if (r < rows) {
-            dq[(int64_t)r * H * DK + dcol] = to_e<E>(scale * s.Gam[r] * dq1[rt][dt][i] + a[i]);
-            dk[(int64_t)r * H * DK + dcol] = to_e<E>(b[i]);
-          }
-        }
+        for (int kb = 0; kb < 2; ++kb)
+          mma(b, ld_frag_f32<E>(sKD, LA, 16 * rt + c16, 32 * kb), ld_frag(sKT, LT, d0 + 16 * dt + c16, 32 * kb));
+        st_tile_rows<E>(sDK, LK, 16 * rt, d0 + 16 * dt, b);
       }
   }
 
   // ---- P12: reductions, dbeta, dg
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int j = 0; j < 2; ++j) {
+    f32x4 a = rg[j], b = rb[j];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float a = rg[rt][i], b = rb[rt][i];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        a += __shfl_xor(a, o, 64);
-        b += __shfl_xor(b, o, 64);
-      }
-      if (c16 == 0) {
-        s.pg[w][16 * rt + 4 * g + i] = a;
-        s.pb[w][16 * rt + 4 * g + i] = b;
-      }
+      a[i] = row16_sum(a[i]);
+      b[i] = row16_sum(b[i]);
     }
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    float a = cc[ct];
-    a += __shfl_xor(a, 16, 64);
-    a += __shfl_xor(a, 32, 64);
-    if (g == 0) s.pc[w][16 * ct + c16] = a;
+    if (c16 == 0) {
+      *reinterpret_cast<f32x4*>(&s.pg[cw][16 * (2 * rh + j) + 4 * g]) = a;
+      *reinterpret_cast<f32x4*>(&s.pb[cw][16 * (2 * rh + j) + 4 * g]) = b;
+    }
   }
   {
     const float a = wave_sum(lastsum), b = wave_sum(hdh);
     if (l == 0) { s.pl[w] = a; s.ph[w] = b; }
   }
   __syncthreads();
+  store_tile<E, DV, NT>(slotE(SQ), LV, static_cast<E*>(p.dv) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
+  store_tile<E, DK, NT>(slotE(SDO), LK, static_cast<E*>(p.dq) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
+  store_tile<E, DK, NT>(slotE(SK), LK, static_cast<E*>(p.dk) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
   if (w == 0) {
     const int r = l;
-    float dgm = 0.f, db = 0.f;
+    float dgm = s.c10[0][r] + s.c10[1][r], db = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      dgm += s.pg[ww][r] + s.pc[ww][r];
+      dgm += s.pg[ww][r] + s.p7[ww][r] + s.c7[ww][r];
       db += s.pb[ww][r];
     }
     if (r == CH - 1) {
       float extra = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) extra += s.GamC * s.ph[ww] + s.pl[ww];
+      for (int ww = 0; ww < 8; ++ww) extra += s.GamC * s.ph[ww] + s.pl[ww];
       dgm += extra;
     }
     // dg_r = sum_{r' >= r} dgam_r'  (suffix scan = prefix scan over reversed lanes)
@@ -901,7 +960,7 @@ __global__ __launch_bounds__(256) void gdn_grad_kernel(GradParams p) {
 
 template <class E, int DK, int DV>
 hipError_t launch_grad_t(const GradParams& p, int nchunk_total, hipStream_t st) {
-  hipLaunchKernelGGL((gdn_grad_kernel<E, DK, DV>), dim3(nchunk_total, p.H), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((gdn_grad_kernel<E, DK, DV>), dim3(nchunk_total, p.H), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 

@@ -180,6 +180,153 @@ __device__ __forceinline__ Frag<E> ld_fragC(const E* base, int64_t ld, int k0, i
   return f;
 }
 
+// Four consecutive E values as fp32, and the reverse.
+template <class E>
+__device__ __forceinline__ f32x4 ld4f(const E* p);
+template <>
+__device__ __forceinline__ f32x4 ld4f<bf16>(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+template <>
+__device__ __forceinline__ f32x4 ld4f<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <class E>
+__device__ __forceinline__ void st4f(E* p, const f32x4& v);
+template <>
+__device__ __forceinline__ void st4f<bf16>(bf16* p, const f32x4& v) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+template <>
+__device__ __forceinline__ void st4f<float>(float* p, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// x from lane (lane ^ X) of the same quad (DPP quad permutation, no LDS).
+template <int X>
+__device__ __forceinline__ float quad_xor(float x) {
+  constexpr int ctrl = (0 ^ X) | ((1 ^ X) << 2) | ((2 ^ X) << 4) | ((3 ^ X) << 6);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false));
+}
+
+// Forces x to be computed here: the compiler may not sink the arithmetic that
+// produces it past this point (which would keep its inputs alive instead).
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(f32x4& x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float t = x[i];
+    asm volatile("" : "+v"(t));
+    x[i] = t;
+  }
+}
+
+// Sum over the 16 lanes of each DPP row (lanes 16r .. 16r+15), in every lane.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += quad_xor<1>(x);
+  x += quad_xor<2>(x);
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));  // half-row mirror
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));  // row mirror
+  return x;
+}
+
+// 4x4 transpose across each aligned quad of lanes: lane b of the quad holds
+// column b of a 4x4 block (v[i] = M[i][b]) and gets row b (v[j] = M[b][j]);
+// applied to rows it gives columns.  Two butterfly stages: 2x2 blocks are
+// exchanged with lane b^2, then single entries with lane b^1.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 v) {
+  const int b = threadIdx.x & 3;
+  {
+    const bool lo = (b & 2) == 0;
+    const float r0 = quad_xor<2>(lo ? v[2] : v[0]);
+    const float r1 = quad_xor<2>(lo ? v[3] : v[1]);
+    v = lo ? f32x4{v[0], v[1], r0, r1} : f32x4{r0, r1, v[2], v[3]};
+  }
+  {
+    const bool lo = (b & 1) == 0;
+    const float r0 = quad_xor<1>(lo ? v[1] : v[0]);
+    const float r1 = quad_xor<1>(lo ? v[3] : v[2]);
+    v = lo ? f32x4{v[0], r0, v[2], r1} : f32x4{r0, v[1], r1, v[3]};
+  }
+  return v;
+}
+
+// quad_transpose for four 16-bit values held as two packed dwords
+// (d0 = v0 | v1 << 16, d1 = v2 | v3 << 16).
+template <int X>
+__device__ __forceinline__ uint32_t quad_xor_u(uint32_t x) {
+  constexpr int ctrl = (0 ^ X) | ((1 ^ X) << 2) | ((2 ^ X) << 4) | ((3 ^ X) << 6);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, 0xF, 0xF, false);
+}
+__device__ __forceinline__ void quad_transpose16(uint32_t& d0, uint32_t& d1) {
+  const int b = threadIdx.x & 3;
+  {  // 2x2 blocks with lane b^2: dwords move whole
+    const bool lo = (b & 2) == 0;
+    const uint32_t r = quad_xor_u<2>(lo ? d1 : d0);
+    if (lo) d1 = r; else d0 = r;
+  }
+  {  // single entries with lane b^1: halves move
+    const bool lo = (b & 1) == 0;
+    const uint32_t snd = lo ? __builtin_amdgcn_perm(d1, d0, 0x07060302u) : __builtin_amdgcn_perm(d1, d0, 0x05040100u);
+    const uint32_t r = quad_xor_u<1>(snd);
+    if (lo) {
+      d0 = __builtin_amdgcn_perm(r, d0, 0x05040100u);
+      d1 = __builtin_amdgcn_perm(r, d1, 0x07060100u);
+    } else {
+      d0 = __builtin_amdgcn_perm(d0, r, 0x07060100u);
+      d1 = __builtin_amdgcn_perm(d1, r, 0x07060302u);
+    }
+  }
+}
+
+// Same fragment as ld_fragC(base, ld, k0, col0 + lane%16) (k-slots walking
+// down a column of a row-major E matrix), read as 4-element row pieces and
+// turned into column pieces by quad transposes.  col0 must be a multiple of 4.
+template <class E>
+__device__ __forceinline__ Frag<E> ld_fragC_q(const E* base, int ld, int k0, int col0);
+template <>
+__device__ __forceinline__ Frag<bf16> ld_fragC_q<bf16>(const bf16* base, int ld, int k0, int col0) {
+  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+  const bf16* p = base + (k0 + 4 * g + b) * ld + col0 + 4 * q;
+  typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+  typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+  u32x2 x = *reinterpret_cast<const u32x2*>(p);
+  u32x2 y = *reinterpret_cast<const u32x2*>(p + 16 * ld);
+  uint32_t x0 = x[0], x1 = x[1], y0 = y[0], y1 = y[1];
+  quad_transpose16(x0, x1);
+  quad_transpose16(y0, y1);
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, u32x4{x0, x1, y0, y1});
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> ld_fragC_q<float>(const float* base, int ld, int k0, int col0) {
+  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+  const float* p = base + (k0 + 4 * g + b) * ld + col0 + 4 * q;
+  Frag<float> f;
+  f.lo = quad_transpose(*reinterpret_cast<const f32x4*>(p));
+  f.hi = quad_transpose(*reinterpret_cast<const f32x4*>(p + 16 * ld));
+  return f;
+}
+
+// Four fp32 values of a C-layout column piece -> E, quad-transposed into a row
+// piece and stored (4 consecutive columns of row `row`).
+template <class E>
+__device__ __forceinline__ void st4_transposed(E* p, const f32x4& v);
+template <>
+__device__ __forceinline__ void st4_transposed<bf16>(bf16* p, const f32x4& v) {
+  typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+  u32x2 x = __builtin_bit_cast(u32x2, bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]});
+  uint32_t x0 = x[0], x1 = x[1];
+  quad_transpose16(x0, x1);
+  *reinterpret_cast<u32x2*>(p) = u32x2{x0, x1};
+}
+template <>
+__device__ __forceinline__ void st4_transposed<float>(float* p, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(p) = quad_transpose(v);
+}
+
 // Row fragment of a row-major E matrix with each k-slot multiplied by kscale[k].
 template <class E>
 __device__ __forceinline__ Frag<E> ld_frag_kscaled(const E* base, int ld, int row, int k0,

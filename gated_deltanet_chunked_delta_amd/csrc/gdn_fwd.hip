@@ -217,17 +217,16 @@ struct Chunk {
       if (l == 0) sp->GamC = __expf(gC);
     }
     if (!OUT && hs_chunk) {
+      // stored transposed, [DV][DK]: the lane's four rows of one column are contiguous
 #pragma unroll
       for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            E* dst = hs_chunk + (16 * t + 4 * g + i) * DV + n0 + 16 * nt + c16;
-            float val = hacc[t][nt][i];
-            if (CORR) val += to_f(*dst);
-            *dst = to_e<E>(val);
-          }
+        for (int nt = 0; nt < NTW; ++nt) {
+          E* dst = hs_chunk + (n0 + 16 * nt + c16) * DK + 16 * t + 4 * g;
+          f32x4 val = hacc[t][nt];
+          if (CORR) val = val + ld4f<E>(dst);
+          st4f<E>(dst, val);
+        }
     }
     __syncthreads();
     sp = lds_opaque(sp);

@@ -144,8 +144,10 @@ __device__ __forceinline__ void solve_diag_block(const float* A, float* T, int b
 // Two diagonal 16x16 blocks (ba, bb) of T by forward substitution in one wave,
 // with no cross-lane traffic: lane j (< 16) owns column j of block ba, lane
 // 16 + j column j of block bb (lanes 32..63 repeat lanes 0..31 and write
-// nothing).  T_rj = d_rj - sum_{i<r} A_ri T_ij, applied right-looking: once
-// row i is final, A_ri T_ij is removed from every later row r.
+// nothing).  Left-looking: row r of the block is
+//   T_rj = [r = j] - rs_r sum_{i<r} A_ri T_ij,
+// with A's rows read as 16-byte vectors so the reads run ahead of the
+// dependent dot products.
 __device__ __forceinline__ void solve_diag_pair(const float* A, float* T, int ba, int bb, const float* rs) {
   constexpr int LA = CH + 4;
   const int l = lane_id(), j = l & 15;
@@ -155,9 +157,17 @@ __device__ __forceinline__ void solve_diag_pair(const float* A, float* T, int ba
 #pragma unroll
   for (int r = 0; r < 16; ++r) t[r] = (r == j) ? 1.f : 0.f;
 #pragma unroll
-  for (int i = 0; i < 15; ++i) {
+  for (int r = 1; r < 16; ++r) {
+    f32x4 a[4];
 #pragma unroll
-    for (int r = i + 1; r < 16; ++r) t[r] -= (rs ? rs[16 * b + r] : 1.f) * Ab[r * LA + i] * t[i];
+    for (int q = 0; q < (r + 3) / 4; ++q) a[q] = *reinterpret_cast<const f32x4*>(Ab + r * LA + 4 * q);
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < r; ++i) {
+      if (i & 1) acc1 += a[i >> 2][i & 3] * t[i];
+      else acc0 += a[i >> 2][i & 3] * t[i];
+    }
+    t[r] -= (rs ? rs[16 * b + r] : 1.f) * (acc0 + acc1);
   }
   if (l < 32) {
     float* Tb = T + (16 * b) * LA + 16 * b;
@@ -238,22 +248,31 @@ struct TilePart {
   typedef E vec_t __attribute__((__vector_size__(16)));
   vec_t blk[NB > 0 ? NB : 1][4];
 
-  __device__ __forceinline__ void load(const E* src, int64_t gld, int rows) {
+  // ZFILL: rows at or past `rows` become zero instead of copies of the last row.
+  template <bool ZFILL = false>
+  __device__ __forceinline__ void load(const E* src, int64_t gld, int rows, int tid = threadIdx.x) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int id = threadIdx.x + b * NT;
+      const int id = tid + b * NT;
       if (NB * NT == NBLK || id < NBLK) {
         const int r0 = (id / BPR) * 4, c0 = (id % BPR) * VEC;
         const E* p = src + c0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) blk[b][j] = *reinterpret_cast<const vec_t*>(p + (int64_t)min(r0 + j, rows - 1) * gld);
+        for (int j = 0; j < 4; ++j) {
+          if (ZFILL) {
+            blk[b][j] = vec_t{};
+            if (r0 + j < rows) blk[b][j] = *reinterpret_cast<const vec_t*>(p + (int64_t)(r0 + j) * gld);
+          } else {
+            blk[b][j] = *reinterpret_cast<const vec_t*>(p + (int64_t)min(r0 + j, rows - 1) * gld);
+          }
+        }
       }
     }
   }
-  __device__ __forceinline__ void store(E* dst, int ld, E* dstT, int ldT) const {
+  __device__ __forceinline__ void store(E* dst, int ld, E* dstT, int ldT, int tid = threadIdx.x) const {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int id = threadIdx.x + b * NT;
+      const int id = tid + b * NT;
       if (NB * NT == NBLK || id < NBLK) {
         const int r0 = (id / BPR) * 4, c0 = (id % BPR) * VEC;
         if (dst) {
@@ -272,6 +291,27 @@ struct TilePart {
     }
   }
 };
+
+// Copy rows [0, rows) of a [CH x D] row-major LDS tile (row stride ld) to
+// global memory (row stride gld) in 16-byte pieces.
+template <class E, int D, int NT>
+__device__ __forceinline__ void store_tile(const E* src, int ld, E* dst, int64_t gld, int rows) {
+  constexpr int VEC = 16 / (int)sizeof(E);
+  typedef E vec_t __attribute__((__vector_size__(16)));
+  for (int e = threadIdx.x; e < rows * (D / VEC); e += NT) {
+    const int r = e / (D / VEC), c0 = (e % (D / VEC)) * VEC;
+    *reinterpret_cast<vec_t*>(dst + (int64_t)r * gld + c0) = *reinterpret_cast<const vec_t*>(src + r * ld + c0);
+  }
+}
+
+// Write a C-layout accumulator tile (lane: rows r0+4g..+3 of column c0+lane%16)
+// into a row-major E matrix, four consecutive columns per lane after a quad
+// transpose.
+template <class E>
+__device__ __forceinline__ void st_tile_rows(E* base, int ld, int r0, int c0, const f32x4& acc) {
+  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+  st4_transposed<E>(base + (r0 + 4 * g + b) * ld + c0 + 4 * q, acc);
+}
 
 // g / beta of one chunk for threads 0..63 (one row each), masked at use.
 template <class E>
