@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--config", default="metric_32k")
     ap.add_argument("--direction", default="fwdbwd", choices=["fwdbwd", "fwd", "bwd"])
     ap.add_argument("--cp-mode", type=int, default=0)
+    ap.add_argument("--save-states", action="store_true",
+                    help="the forward keeps the chunk states and the backward reads them (no replay)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -113,32 +115,57 @@ def main():
     host = x.cu_seqlens
     ntok = int(B * T) if cu is None else int(x.cu_seqlens[-1])
 
+    # The step follows the backward as specified: it takes the forward's inputs
+    # and replays the forward states.  --save-states times the alternative in
+    # which the forward keeps the chunk states (Dk*Dv values per 64 tokens and
+    # head) for the backward; the default run also reports that variant in a
+    # separate, labelled object.
+    keep = False
+
     def step():
+        states = None
         if args.direction in ("fwdbwd", "fwd"):
-            gb.gdn_chunk_fwd(q, k, v, g, beta, x.scale, h0=h0, cu_seqlens=cu, cu_seqlens_host=host,
-                             cp_mode=args.cp_mode)
+            res = gb.gdn_chunk_fwd(q, k, v, g, beta, x.scale, h0=h0, cu_seqlens=cu, cu_seqlens_host=host,
+                                   cp_mode=args.cp_mode, save_states=keep)
+            states = res[2] if keep else None
         if args.direction in ("fwdbwd", "bwd"):
             gb.gdn_chunk_bwd(q, k, v, g, beta, x.scale, do, h0=h0, cu_seqlens=cu, cu_seqlens_host=host,
-                             cp_mode=args.cp_mode, need_dh0=h0 is not None)
+                             cp_mode=args.cp_mode, need_dh0=h0 is not None, states=states)
 
-    log("warmup")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    gb.gdn_profile_reset()
-    gb.gdn_profile_enable(True)
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    gb.gdn_profile_enable(False)
-    prof = gb.gdn_profile_read()
+
+    def timed_run(profile):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        if profile:
+            gb.gdn_profile_reset()
+            gb.gdn_profile_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        prof = None
+        if profile:
+            gb.gdn_profile_enable(False)
+            prof = gb.gdn_profile_read()
+        return e0.elapsed_time(e1) / args.steps, prof
+
+    log("warmup + timed steps")
+    keep = args.save_states and args.direction == "fwdbwd"
+    ms, prof = timed_run(True)
     log(f"timed {args.steps} steps")
-    ms = e0.elapsed_time(e1) / args.steps
+    variant = None
+    if args.direction == "fwdbwd" and not args.save_states:
+        keep = True
+        ms_v, _ = timed_run(False)
+        keep = False
+        variant = {"states": "saved by fwd (no replay in bwd)", "ms_per_step": ms_v, "value": ntok * 1e3 / ms_v,
+                   "unit": "tokens/s"}
+        log(f"timed {args.steps} steps with saved states")
 
     fwd_f, bwd_f = flops_per_token_head(dk, dv)
     per_th = {"fwdbwd": fwd_f + bwd_f, "fwd": fwd_f, "bwd": bwd_f}[args.direction]
@@ -170,10 +197,13 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if x.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": args.config, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": CH,
-                   "direction": args.direction, "cp_mode": args.cp_mode, "tokens_per_step": ntok},
+                   "direction": args.direction, "cp_mode": args.cp_mode, "tokens_per_step": ntok,
+                   "states": "saved by fwd" if args.save_states else "recomputed in bwd"},
         "tflops": tflops, "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "kernels": kernels, "roofline": roof,
     }
+    if variant is not None:
+        out["variant_saved_states"] = variant
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)

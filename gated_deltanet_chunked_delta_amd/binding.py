@@ -32,11 +32,11 @@ class CommonArgs(ctypes.Structure):
 
 
 class FwdArgs(ctypes.Structure):
-    _fields_ = [("a", CommonArgs), ("o", _vp), ("hT", _vp)]
+    _fields_ = [("a", CommonArgs), ("o", _vp), ("hT", _vp), ("h_save", _vp)]
 
 
 class BwdArgs(ctypes.Structure):
-    _fields_ = [("a", CommonArgs), ("do_", _vp), ("dhT", _vp), ("dq", _vp), ("dk", _vp),
+    _fields_ = [("a", CommonArgs), ("h_saved", _vp), ("do_", _vp), ("dhT", _vp), ("dq", _vp), ("dk", _vp),
                 ("dv", _vp), ("dbeta", _vp), ("dg", _vp), ("dh0", _vp)]
 
 
@@ -58,6 +58,8 @@ def lib():
         L.gdn_chunk_fwd_workspace_size.restype = ctypes.c_size_t
         L.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
         L.gdn_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+        L.gdn_chunk_states_bytes.argtypes = [ctypes.POINTER(CommonArgs)]
+        L.gdn_chunk_states_bytes.restype = ctypes.c_size_t
         L.gdn_chunk_fwd.argtypes = [ctypes.POINTER(FwdArgs), _vp]
         L.gdn_chunk_fwd.restype = ctypes.c_int
         L.gdn_chunk_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
@@ -145,16 +147,22 @@ def _stream(dev):
 
 
 def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_seqlens_host=None,
-                  output_final_state: bool = True, cp_mode: int = 0):
-    """Forward pass.  Returns (o, hT) with hT None unless output_final_state."""
+                  output_final_state: bool = True, cp_mode: int = 0, save_states: bool = False):
+    """Forward pass.  Returns (o, hT) with hT None unless output_final_state; with
+    save_states, (o, hT, states) where states (the state at every chunk start, for
+    gdn_chunk_bwd) is a flat tensor of the input dtype."""
     a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode)
     L = lib()
     o = torch.empty(q.shape[:3] + (a.Dv,), dtype=q.dtype, device=q.device)
     hT = (torch.empty((a.num_seqs, a.H, a.Dk, a.Dv), dtype=torch.float32, device=q.device)
           if output_final_state else None)
+    states = None
+    if save_states:
+        nb = L.gdn_chunk_states_bytes(ctypes.byref(a))
+        states = torch.empty(max(nb, 16) // q.element_size(), dtype=q.dtype, device=q.device)
     args = FwdArgs()
     args.a = a
-    args.o, args.hT = _ptr(o), _ptr(hT)
+    args.o, args.hT, args.h_save = _ptr(o), _ptr(hT), _ptr(states)
     nbytes = L.gdn_chunk_fwd_workspace_size(ctypes.byref(args))
     if nbytes == 0:
         _check(1)
@@ -162,15 +170,20 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_s
     args.a.workspace, args.a.workspace_bytes = ws.data_ptr(), nbytes
     _check(L.gdn_chunk_fwd(ctypes.byref(args), _vp(_stream(q.device))))
     del keep
-    return o, hT
+    return (o, hT, states) if save_states else (o, hT)
 
 
 def gdn_chunk_bwd(q, k, v, g, beta, scale: float, do, h0=None, dhT=None, cu_seqlens=None,
-                  cu_seqlens_host=None, cp_mode: int = 0, need_dh0: bool = True):
-    """Backward pass.  Returns (dq, dk, dv, dg, dbeta, dh0) with dh0 None unless need_dh0."""
+                  cu_seqlens_host=None, cp_mode: int = 0, need_dh0: bool = True, states=None):
+    """Backward pass.  Returns (dq, dk, dv, dg, dbeta, dh0) with dh0 None unless need_dh0.
+    states: the forward's saved chunk states (gdn_chunk_fwd(..., save_states=True)); when
+    given the backward does not recompute them."""
     a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode)
     _contig("do", do, q.dtype, q.device)
     _contig("dhT", dhT, torch.float32, q.device)
+    _contig("states", states, q.dtype, q.device)
+    if states is not None and states.numel() * states.element_size() < lib().gdn_chunk_states_bytes(ctypes.byref(a)):
+        raise GDNError("states is smaller than gdn_chunk_states_bytes")
     L = lib()
     dq, dk = torch.empty_like(q), torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -180,6 +193,7 @@ def gdn_chunk_bwd(q, k, v, g, beta, scale: float, do, h0=None, dhT=None, cu_seql
            if need_dh0 else None)
     args = BwdArgs()
     args.a = a
+    args.h_saved = _ptr(states)
     args.do_, args.dhT = _ptr(do), _ptr(dhT)
     args.dq, args.dk, args.dv, args.dbeta, args.dg, args.dh0 = map(_ptr, (dq, dk, dv, dbeta, dg, dh0))
     nbytes = L.gdn_chunk_bwd_workspace_size(ctypes.byref(args))

@@ -97,8 +97,9 @@ gdn_status check_common(const gdn_common_args& a) {
   return GDN_OK;
 }
 
-// Segment length, totals and workspace layout.  `bwd` adds the backward's arrays.
-Plan make_plan(const gdn_common_args& a, bool bwd, int cus) {
+// Segment length, totals and workspace layout.  `bwd` adds the backward's arrays
+// (without the chunk states when the caller provides them: `saved`).
+Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false) {
   Plan p;
   p.N = a.num_seqs;
   std::vector<int> nch(p.N);
@@ -145,7 +146,7 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus) {
       p.o_bstate2 = take(sizeof(float) * SS * p.nseg * a.H);
       p.o_lam2 = take(sizeof(float) * (size_t)p.nseg * a.H);
     }
-    p.o_hs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
+    if (!saved) p.o_hs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
     p.o_dhs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
   }
   p.total = off;
@@ -250,7 +251,19 @@ size_t gdn_chunk_fwd_workspace_size(const gdn_fwd_args* args) {
 size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args) {
   if (!args) { fail(GDN_E_INVALID, "null args"); return 0; }
   if (check_common(args->a) != GDN_OK) return 0;
-  return make_plan(args->a, true, cu_count()).total;
+  return make_plan(args->a, true, cu_count(), args->h_saved != nullptr).total;
+}
+
+size_t gdn_chunk_states_bytes(const gdn_common_args* a) {
+  if (!a) { fail(GDN_E_INVALID, "null args"); return 0; }
+  if (check_common(*a) != GDN_OK) return 0;
+  long long chunks = 0;
+  for (int n = 0; n < a->num_seqs; ++n) {
+    const int len = a->cu_seqlens ? a->cu_seqlens_host[n + 1] - a->cu_seqlens_host[n] : a->T;
+    chunks += (len + CHUNK - 1) / CHUNK;
+  }
+  const size_t esz = a->dtype == GDN_BF16 ? 2 : 4;
+  return (size_t)chunks * a->H * a->Dk * a->Dv * esz;
 }
 
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
@@ -261,6 +274,7 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   if ((long long)a.B * a.T > 0 && !args->o) return fail(GDN_E_INVALID, "null output o");
   if (!aligned(args->o, 16)) return fail(GDN_E_INVALID, "o must be 16-byte aligned");
   if (!aligned(args->hT, 4)) return fail(GDN_E_INVALID, "hT misaligned");
+  if (!aligned(args->h_save, 16)) return fail(GDN_E_INVALID, "h_save must be 16-byte aligned");
   const Plan pl = make_plan(a, false, cu_count());
   if (!a.workspace || a.workspace_bytes < pl.total)
     return fail(GDN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total,
@@ -281,7 +295,7 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   p.chunk_first = at<int>(ws, pl.o_chunk_first);
   p.bstate = pl.cp ? at<float>(ws, pl.o_bstate) : nullptr;
   p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
-  p.hs = nullptr;
+  p.hs = args->h_save;  // nullable: the chunk states are stored only on request
   p.phase = 1;
   e = timed("fwd", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
@@ -306,7 +320,9 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   if (!aligned(args->dg, 4) || !aligned(args->dbeta, a.dtype == GDN_F32 ? 4 : 2) || !aligned(args->dhT, 4) ||
       !aligned(args->dh0, 4))
     return fail(GDN_E_INVALID, "dg / dbeta / dhT / dh0 misaligned");
-  const Plan pl = make_plan(a, true, cu_count());
+  if (!aligned(args->h_saved, 16)) return fail(GDN_E_INVALID, "h_saved must be 16-byte aligned");
+  const bool saved = args->h_saved != nullptr;
+  const Plan pl = make_plan(a, true, cu_count(), saved);
   if (!a.workspace || a.workspace_bytes < pl.total)
     return fail(GDN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total,
                 a.workspace ? a.workspace_bytes : (size_t)0);
@@ -318,7 +334,7 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
                             at<gdn::SegDesc>(ws, pl.o_segs), at<int2>(ws, pl.o_chunk_tab), s);
   });
   if (e != hipSuccess) return hip_fail(e, "plan launch");
-  // 1. forward replay: state at every chunk start
+  // 1. forward replay: state at every chunk start (unless the forward saved them)
   gdn::FwdParams p{};
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta; p.h0 = a.h0;
   p.o = nullptr; p.hT = nullptr; p.scale = a.scale; p.H = a.H; p.seq = sq;
@@ -327,14 +343,18 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   p.chunk_first = at<int>(ws, pl.o_chunk_first);
   p.bstate = pl.cp ? at<float>(ws, pl.o_bstate) : nullptr;
   p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
-  p.hs = at<void>(ws, pl.o_hs);
-  p.phase = 1;
-  e = timed("replay", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
-  if (e != hipSuccess) return hip_fail(e, "replay launch");
-  if (pl.cp) {
-    p.phase = 3;
-    e = timed("replay_corr", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
-    if (e != hipSuccess) return hip_fail(e, "replay correction launch");
+  if (saved) {
+    p.hs = const_cast<void*>(args->h_saved);
+  } else {
+    p.hs = at<void>(ws, pl.o_hs);
+    p.phase = 1;
+    e = timed("replay", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
+    if (e != hipSuccess) return hip_fail(e, "replay launch");
+    if (pl.cp) {
+      p.phase = 3;
+      e = timed("replay_corr", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
+      if (e != hipSuccess) return hip_fail(e, "replay correction launch");
+    }
   }
   // 2. reverse chain: state gradient at every chunk end, dh0
   gdn::RevParams r{};

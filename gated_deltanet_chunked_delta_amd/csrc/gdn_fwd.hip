@@ -177,7 +177,8 @@ struct TileLoader {
 
 // ------------------------------------------------------------------ one chunk
 
-// OUT:  forward (writes o) vs replay (stores the chunk-start state instead).
+// OUT:  forward (writes o) vs replay (no output).  Either stores the chunk-start
+//       state when p.hs is set.
 // CORR: boundary correction -- the state is a propagated difference; the values
 //       v do not enter, outputs / stored states are incremented.
 template <class E, int DK, int DV, bool OUT, bool CORR>
@@ -216,7 +217,7 @@ struct Chunk {
       sp->lam[l] = gr;
       if (l == 0) sp->GamC = __expf(gC);
     }
-    if (!OUT && hs_chunk) {
+    if (hs_chunk) {
       // stored transposed, [DV][DK]: the lane's four rows of one column are contiguous
 #pragma unroll
       for (int t = 0; t < DK / 16; ++t)
@@ -445,7 +446,7 @@ struct Chunk {
       const int rows = min(CH, len - c * CH);
       const bool more = c + 1 < ce;
       const int nrows = more ? min(CH, len - (c + 1) * CH) : 0;
-      E* hsc = (!OUT && hs) ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
+      E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
       lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, hacc);
     }
     if (done) *done = c - cb;

@@ -25,7 +25,7 @@ struct FwdParams {
   const int* chunk_first;  // [N+1]
   float* bstate;           // [total segments][H][DK][DV] segment end states
   float* lam;              // [total segments][H] segment log-bounds
-  void* hs;                // nullable: [total chunks][H][DK][DV] chunk start states (dtype)
+  void* hs;                // nullable: [total chunks][H][DV][DK] chunk start states S (dtype)
   int phase;               // 1 = segments from zero / h0, 3 = boundary corrections
 };
 
@@ -46,7 +46,7 @@ struct RevParams {
   const int* chunk_first;
   float* bstate;           // [total segments][H][DK][DV] segment start gradients
   float* lam;              // [total segments][H]
-  void* dhs;               // [total chunks][H][DK][DV] gradient at each chunk END (dtype)
+  void* dhs;               // [total chunks][H][DV][DK] gradient at each chunk END, transposed (dtype)
   int phase;
 };
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
   GDN_OK = 0,
@@ -96,10 +96,16 @@ typedef struct {
   gdn_common_args a;
   void* o;                     /* [B,T,H,Dv] dtype, written */
   float* hT;                   /* nullable [N,H,Dk,Dv] fp32, written */
+  void* h_save;                /* nullable, 16-byte aligned, gdn_chunk_states_bytes(&a) bytes: the
+                                  state at the start of every 64-token chunk, written for a later
+                                  gdn_chunk_bwd (layout below) */
 } gdn_fwd_args;
 
 typedef struct {
   gdn_common_args a;           /* the forward's inputs; the backward recomputes what it needs */
+  const void* h_saved;         /* nullable: h_save of a gdn_chunk_fwd call on the same inputs;
+                                  given, the backward reads the chunk states instead of
+                                  recomputing them (no forward replay) */
   const void* do_;             /* [B,T,H,Dv] dtype: gradient of o */
   const float* dhT;            /* nullable [N,H,Dk,Dv]: gradient of hT (NULL = zero) */
   void* dq;                    /* [B,T,H,Dk] dtype, written */
@@ -111,16 +117,28 @@ typedef struct {
 } gdn_bwd_args;
 
 /* Bytes of device workspace gdn_chunk_fwd / gdn_chunk_bwd need for these
- * arguments (pointers other than cu_seqlens_host are not read).  Returns 0 and
- * sets the error string when the arguments are invalid. */
+ * arguments (pointers other than cu_seqlens_host are not read, except that the
+ * backward needs less when h_saved is non-NULL).  Returns 0 and sets the error
+ * string when the arguments are invalid. */
 size_t gdn_chunk_fwd_workspace_size(const gdn_fwd_args* args);
 size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args);
 
-/* Forward: o and (optionally) hT.  stream is a hipStream_t (NULL = default stream). */
+/* Bytes of the saved chunk states (h_save / h_saved) for these arguments:
+ * C * H * Dk * Dv elements of the input dtype, C = sum over sequences of
+ * ceil(len / 64).  Element [c][h][j][i] is h[i][j] (= S[j][i]) at the start of
+ * chunk c (chunks numbered sequence after sequence), i.e. each state is stored
+ * as S, Dv x Dk row-major, rounded to the dtype.  Returns 0 and sets the error
+ * string for invalid arguments (and returns 0 without error when there are no
+ * tokens). */
+size_t gdn_chunk_states_bytes(const gdn_common_args* a);
+
+/* Forward: o and (optionally) hT and the chunk states.  stream is a
+ * hipStream_t (NULL = default stream). */
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream);
 
 /* Backward: gradients of <do, o> + <dhT, hT> with respect to q, k, v, beta, g
- * and (optionally) h0.  It recomputes the forward states from the inputs. */
+ * and (optionally) h0.  It recomputes the forward states from the inputs
+ * unless h_saved provides them. */
 gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream);
 
 /* Per-kernel timing, for benchmarks (off by default).  While enabled, every

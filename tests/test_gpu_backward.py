@@ -134,3 +134,38 @@ def test_euler_identities_on_gpu_output(dev):
 def test_config_backward(dev, name):
     x = gdn_inputs.config(name)
     check_bwd(x, dev, 0, name)
+
+
+@pytest.mark.parametrize("cp_mode", [-1, 2, 0])
+def test_saved_states_match_replay(dev, cp_mode):
+    """The backward fed with the forward's saved chunk states gives the same
+    gradients as the backward that replays the forward (same kernels, same
+    arithmetic order), and the forward's outputs do not change by saving them."""
+    import torch
+    from gated_deltanet_chunked_delta_amd import gdn_chunk_bwd, gdn_chunk_fwd
+    rng = np.random.default_rng(9)
+    lens = [0, 70, 300, 1, 129]
+    cu = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    x = gdn_inputs.generate(B=1, T=int(cu[-1]), H=2, Dk=128, Dv=128, dtype="bf16", seed=91, grad=True)
+    x.cu_seqlens = cu
+    x.h0 = (0.3 * rng.standard_normal((len(lens), 2, 128, 128))).astype(np.float32)
+    x.dhT = rng.standard_normal((len(lens), 2, 128, 128)).astype(np.float32)
+    print(f"[bwd] saved-states varlen cp={cp_mode}", flush=True)
+    t = to_torch(x, dev)
+    kw = dict(h0=t["h0"], cu_seqlens=t["cu"], cu_seqlens_host=cu, cp_mode=cp_mode)
+    o1, hT1 = gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, **kw)
+    o2, hT2, states = gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, save_states=True, **kw)
+    g1 = gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, t["do"], dhT=t["dhT"], **kw)
+    g2 = gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, t["do"], dhT=t["dhT"],
+                       states=states, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(hT1, hT2)
+    for name, a, b in zip(NAMES, g1, g2):
+        da, db = to_np(a), to_np(b)
+        err = relerr(db, da)
+        print(f"    {name} {err:.3e}", flush=True)
+        assert err <= 1e-6, (name, err)
+    want = ref.bwd(x.q, x.k, x.v, x.g, x.beta, x.scale, x.do, x.h0, x.dhT, x.cu_seqlens)
+    for name, b in zip(NAMES, g2):
+        assert relerr(to_np(b), want[name]) <= TOL[x.dtype], name
