@@ -179,12 +179,7 @@ struct RevChunk {
     // ---- 3. off-diagonal blocks of T
     {
       S& s = *lds_opaque(&s0);
-      solve_level1(s.A, s.T, w, nullptr);
-    }
-    __syncthreads();
-    {
-      S& s = *lds_opaque(&s0);
-      solve_level2(s.A, s.T, w, nullptr);
+      solve_columns(s.A, s.T, w, nullptr);
     }
     __syncthreads();
 
@@ -564,9 +559,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   // ---- P3: T = (I + diag(beta) KD)^-1
   if (w < 2) solve_diag_pair(sKD, sT, w, 3 - w, s.beta);
   __syncthreads();
-  solve_level1(sKD, sT, w, s.beta);
-  __syncthreads();
-  solve_level2(sKD, sT, w, s.beta);
+  solve_columns(sKD, sT, w, s.beta);
   __syncthreads();
 
   // per-lane partial sums of this wave's rows (row tiles 2 rh + j)

@@ -181,24 +181,28 @@ struct TileLoader {
 //       state when p.hs is set.
 // CORR: boundary correction -- the state is a propagated difference; the values
 //       v do not enter, outputs / stored states are incremented.
+// Waves per workgroup: 8 when the state has 128 value columns (one 16-column
+// tile per wave, two waves per SIMD), else 4.
+template <int DV>
+struct FwdWaves { static constexpr int NW = DV == 128 ? 8 : 4; };
+
 template <class E, int DK, int DV, bool OUT, bool CORR>
 struct Chunk {
-  static constexpr int NW = 4;
+  static constexpr int NW = FwdWaves<DV>::NW;
   static constexpr int NT = NW * 64;
-  static constexpr int NTW = DV / 64;  // 16-column tiles of the state per wave
+  static constexpr int NTW = DV / (16 * NW);  // 16-column tiles of the state per wave
   using S = FwdSmem<E, DK, DV>;
   using Loader = TileLoader<E, DK, DV, NT, OUT, !CORR>;
-  using Acc = f32x4[DK / 16][DV / 64];
 
   // Process the chunk whose tiles `ld` holds; prefetch the next chunk (if any)
   // into `ld`.  hacc: this wave's state columns (chunk start on entry, chunk end
   // on exit).  Returns the chunk's log-bound Lambda_c.
   __device__ static float step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows,
-                               int64_t ntok0, int nrows, int h, E* hs_chunk, f32x4 (&hacc)[DK / 16][DV / 64]) {
+                               int64_t ntok0, int nrows, int h, E* hs_chunk, f32x4 (&hacc)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA, LO = S::LO;
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
     const int H = p.H;
-    const int n0 = w * (DV / 4);  // first state column of this wave
+    const int n0 = w * (DV / NW);  // first state column of this wave
 
     // ---- 1. tiles into LDS, scalars, prefetch of the next chunk
     S* sp = lds_opaque(&s0);
@@ -232,13 +236,13 @@ struct Chunk {
     __syncthreads();
     sp = lds_opaque(sp);
 
-    // ---- 2. K K^T -> A (waves 0, 1) and Q K^T -> P (waves 2, 3).  Each wave takes a
-    //         pair of row tiles {0, 3} or {1, 2} (5 lower tiles); its A-side
-    //         fragments are loaded once per row.  Waves 0 and 1 then solve the two
-    //         diagonal blocks of T they produced.
+    // ---- 2. K K^T -> A and Q K^T -> P, lower 16x16 tiles.  Four waves: each takes a
+    //         pair of row tiles {0, 3} or {1, 2} of one product (waves 0, 1: A; 2, 3: P).
+    //         Eight waves: wave r < 4 takes row tile r of A, wave 4 + r row tile r of P.
+    //         A wave's row-side fragments are loaded once per row; the waves that
+    //         produced A's rows then solve the diagonal blocks of T they hold.
     {
-      const bool rows03 = (w & 1) == 0;
-      const bool isq = w >= 2;
+      const bool isq = NW == 8 ? w >= 4 : w >= 2;
       if (!isq || OUT) {
         const E* X = isq ? sp->Q : sp->K;
         auto row = [&](auto RT_) {
@@ -268,9 +272,19 @@ struct Chunk {
             }
           }
         };
-        if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
-        else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
-        if (!isq) solve_diag_pair(sp->A, sp->T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
+        if constexpr (NW == 8) {
+          const int rw = w & 3;
+          if (rw == 0) row(std::integral_constant<int, 0>{});
+          else if (rw == 1) row(std::integral_constant<int, 1>{});
+          else if (rw == 2) row(std::integral_constant<int, 2>{});
+          else row(std::integral_constant<int, 3>{});
+          if (!isq) solve_diag_pair(sp->A, sp->T, rw, rw, nullptr);
+        } else {
+          const bool rows03 = (w & 1) == 0;
+          if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
+          else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
+          if (!isq) solve_diag_pair(sp->A, sp->T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
+        }
       }
     }
     __syncthreads();
@@ -284,27 +298,28 @@ struct Chunk {
     if (nrows > 0) ld.load_kv(p, ntok0, nrows, h);
     if (OUT && nrows > 0) ld.load_q(p, ntok0, nrows, h);
 
-    // ---- 3. off-diagonal blocks of T
-    solve_level1(sp->A, sp->T, w, nullptr);
-    __syncthreads();
-    sp = lds_opaque(sp);
-    solve_level2(sp->A, sp->T, w, nullptr);
+    // ---- 3. off-diagonal blocks of T (one block column per wave)
+    solve_columns(sp->A, sp->T, w, nullptr);
     __syncthreads();
     sp = lds_opaque(sp);
 
-    // ---- 4. -W = -T diag(beta Gam) K for row tile w (all key columns);
-    //         Q h and Ut = T diag(beta) V for this wave's state columns.
+    // ---- 4. -W = -T diag(beta Gam) K for row tile w % 4 (key column tiles split
+    //         between w / 4 = 0, 1 with eight waves); Ut = T diag(beta) V for this
+    //         wave's state columns.
     {
+      constexpr int CTW = (DK / 16) / (NW / 4);
+      const int rt = w & 3, ct0 = (w >> 2) * CTW;
       Frag<E> xw[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) xw[kb] = ld_frag_scaled<E>(sp->T, LA, 16 * w + c16, 32 * kb, sp->bg);
+      for (int kb = 0; kb < 2; ++kb) xw[kb] = ld_frag_scaled<E>(sp->T, LA, 16 * rt + c16, 32 * kb, sp->bg);
 #pragma unroll
-      for (int ct = 0; ct < DK / 16; ++ct) {
+      for (int cc = 0; cc < CTW; ++cc) {
+        const int ct = ct0 + cc;
         f32x4 acc = zero4();
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) mma(acc, xw[kb], ld_frag(sp->KT, LT, 16 * ct + c16, 32 * kb));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sp->W[(16 * w + 4 * g + i) * LQ + 16 * ct + c16] = to_e<E>(-acc[i]);
+        for (int i = 0; i < 4; ++i) sp->W[(16 * rt + 4 * g + i) * LQ + 16 * ct + c16] = to_e<E>(-acc[i]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -433,7 +448,7 @@ struct Chunk {
   // CORR runs stop early once the accumulated bound falls under 2^-24; the
   // number of chunks processed is returned through *done.
   __device__ static float run(S& s, const FwdParams& p, int64_t seq0, int len, int64_t chunk0, int cb,
-                              int ce, int h, f32x4 (&hacc)[DK / 16][DV / 64], int* done) {
+                              int ce, int h, f32x4 (&hacc)[DK / 16][NTW], int* done) {
     Loader ld;
     float lam = 0.f;
     int c = cb;
@@ -454,27 +469,31 @@ struct Chunk {
   }
 };
 
+// State h = S^T (fp32 [DK][DV]) <-> this wave's accumulator tiles (its DV/NW columns).
 template <class E, int DK, int DV>
-__device__ void load_state(f32x4 (&hacc)[DK / 16][DV / 64], const float* src) {
+__device__ void load_state(f32x4 (&hacc)[DK / 16][DV / (16 * FwdWaves<DV>::NW)], const float* src) {
+  constexpr int NW = FwdWaves<DV>::NW, NTW = DV / (16 * NW);
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
 #pragma unroll
   for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-    for (int nt = 0; nt < DV / 64; ++nt)
+    for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        hacc[t][nt][i] = src ? src[(16 * t + 4 * g + i) * DV + w * (DV / 4) + 16 * nt + c16] : 0.f;
+        hacc[t][nt][i] = src ? src[(16 * t + 4 * g + i) * DV + w * (DV / NW) + 16 * nt + c16] : 0.f;
 }
 template <class E, int DK, int DV>
-__device__ void store_state(const f32x4 (&hacc)[DK / 16][DV / 64], float* dst, const float* add, bool use_acc) {
+__device__ void store_state(const f32x4 (&hacc)[DK / 16][DV / (16 * FwdWaves<DV>::NW)], float* dst,
+                            const float* add, bool use_acc) {
+  constexpr int NW = FwdWaves<DV>::NW, NTW = DV / (16 * NW);
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
 #pragma unroll
   for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-    for (int nt = 0; nt < DV / 64; ++nt)
+    for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int e = (16 * t + 4 * g + i) * DV + w * (DV / 4) + 16 * nt + c16;
+        const int e = (16 * t + 4 * g + i) * DV + w * (DV / NW) + 16 * nt + c16;
         dst[e] = (use_acc ? hacc[t][nt][i] : 0.f) + (add ? add[e] : 0.f);
       }
 }
@@ -494,13 +513,13 @@ __device__ void init_smem(FwdSmem<E, DK, DV>& s) {
 
 // Phase 1: every segment from zero (segment 0 from h0).
 template <class E, int DK, int DV, bool OUT>
-__global__ __launch_bounds__(256) void gdn_fwd_p1(FwdParams p) {
+__global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
   const int h = blockIdx.y, n = sd.n;
   const int nseg = p.seg_first[n + 1] - p.seg_first[n];
   const size_t SS = (size_t)DK * DV;
-  f32x4 hacc[DK / 16][DV / 64];
+  f32x4 hacc[DK / 16][DV / (16 * FwdWaves<DV>::NW)];
   init_smem(s);
   load_state<E, DK, DV>(hacc, (sd.s == 0 && p.h0) ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
   const float lam = Chunk<E, DK, DV, OUT, false>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
@@ -515,7 +534,7 @@ __global__ __launch_bounds__(256) void gdn_fwd_p1(FwdParams p) {
 
 // Phase 3: boundary corrections (or the serial fallback).
 template <class E, int DK, int DV, bool OUT>
-__global__ __launch_bounds__(256) void gdn_fwd_p3(FwdParams p) {
+__global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p3(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
   const int h = blockIdx.y, n = sd.n;
@@ -529,7 +548,7 @@ __global__ __launch_bounds__(256) void gdn_fwd_p3(FwdParams p) {
   bool ok = true;
   for (int j = 1; j + 1 < nseg; ++j) ok = ok && (p.lam[(size_t)(seg0 + j) * p.H + h] <= LN_EPS);
   if (!ok && sd.s != 1) return;
-  f32x4 hacc[DK / 16][DV / 64];
+  f32x4 hacc[DK / 16][DV / (16 * FwdWaves<DV>::NW)];
   init_smem(s);
   if (!ok) {
     // Gates do not decay fast enough to cut this sequence: one workgroup redoes it serially.
@@ -550,7 +569,7 @@ __global__ __launch_bounds__(256) void gdn_fwd_p3(FwdParams p) {
 
 template <class E, int DK, int DV>
 hipError_t launch_fwd_t(const FwdParams& p, int nseg_total, hipStream_t st) {
-  dim3 grid(nseg_total, p.H), block(256);
+  dim3 grid(nseg_total, p.H), block(64 * FwdWaves<DV>::NW);
   const bool out = p.o != nullptr;
   if (p.phase == 1) {
     if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true>), grid, block, 0, st, p);

@@ -18,6 +18,17 @@ __device__ __forceinline__ void mm16_xreg(f32x4& acc, const float* X, int ldx, i
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, yreg[i], acc, 0, 0, 0);
   }
 }
+// acc += diag(rs) X[xr0.., xk0..] * Y with Y in registers as above (rs may be null).
+__device__ __forceinline__ void mm16_xreg_scaled(f32x4& acc, const float* X, int ldx, int xr0, int xk0,
+                                                 const f32x4& yreg, const float* rs) {
+  const int l = lane_id(), g = l >> 4;
+  const float sc = rs ? rs[xr0 + (l & 15)] : 1.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = sc * X[(xr0 + (l & 15)) * ldx + xk0 + 4 * g + i];
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, yreg[i], acc, 0, 0, 0);
+  }
+}
 // acc += diag(rs) X[xr0.., xk0..] * Y[yk0.., yc0..], both fp32 row-major in LDS
 // (16x16x16); rs (a row scale of X) may be null.
 __device__ __forceinline__ void mm16_xy(f32x4& acc, const float* X, int ldx, int xr0, int xk0,
@@ -197,6 +208,37 @@ __device__ __forceinline__ void solve_level2(const float* A, float* T, int w, co
   const int l = lane_id(), g = l >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) T[(16 * I + 4 * g + i) * LA + 16 * J + (l & 15)] = -out[i];
+}
+
+// All off-diagonal 16x16 blocks of T (after the diagonal blocks), one block
+// column per wave: wave J (< 3) forms T_IJ for I = J+1 .. 3 in order,
+//   T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ,
+// keeping the blocks it has finished in registers (in accumulator layout,
+// which is the B-operand layout of the 16x16x4 fp32 product) so that no
+// barrier separates them.  Complete after the caller's next barrier.
+template <int J>
+__device__ __forceinline__ void solve_column(const float* A, float* T, const float* rs) {
+  constexpr int LA = CH + 4;
+  const int l = lane_id(), g = l >> 4;
+  f32x4 tk[3];  // tk[I - J - 1] = T_IJ
+#pragma unroll
+  for (int I = J + 1; I < 4; ++I) {
+    f32x4 y = zero4();
+    mm16_xy(y, A, LA, 16 * I, 16 * J, T, LA, 16 * J, 16 * J, rs);
+#pragma unroll
+    for (int K = J + 1; K < I; ++K) mm16_xreg_scaled(y, A, LA, 16 * I, 16 * K, tk[K - J - 1], rs);
+    f32x4 t = zero4();
+    mm16_xreg(t, T, LA, 16 * I, 16 * I, y);
+    t = zero4() - t;
+    tk[I - J - 1] = t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) T[(16 * I + 4 * g + i) * LA + 16 * J + (l & 15)] = t[i];
+  }
+}
+__device__ __forceinline__ void solve_columns(const float* A, float* T, int w, const float* rs) {
+  if (w == 0) solve_column<0>(A, T, rs);
+  else if (w == 1) solve_column<1>(A, T, rs);
+  else if (w == 2) solve_column<2>(A, T, rs);
 }
 
 // Full solve with 3 barriers, for kernels with at least 4 waves.  T's
