@@ -65,12 +65,17 @@ struct alignas(16) RevSmem {
   float GamC;
 };
 
-// One chunk of the reverse chain (4 waves; wave w owns Dv/4 columns of the
-// state gradient).  CORR: propagation of a boundary difference only (dO
-// does not enter, stored gradients are incremented).
+// Waves per workgroup of the reverse chain: 8 when the state gradient has 128
+// value columns (one 16-column tile per wave, two waves per SIMD), else 4.
+template <int DV>
+struct RevWaves { static constexpr int NW = DV == 128 ? 8 : 4; };
+
+// One chunk of the reverse chain (wave w owns Dv/NW columns of the state
+// gradient).  CORR: propagation of a boundary difference only (dO does not
+// enter, stored gradients are incremented).
 template <class E, int DK, int DV, bool CORR>
 struct RevChunk {
-  static constexpr int NW = 4, NT = 256, NTW = DV / 64;
+  static constexpr int NW = RevWaves<DV>::NW, NT = 64 * NW, NTW = DV / (16 * NW);
   using S = RevSmem<E, DK, DV>;
   struct Loader {
     TilePart<E, NT, DK> k;
@@ -92,10 +97,10 @@ struct RevChunk {
   // dh: gradient at the chunk end on entry, at the chunk start on exit.
   // Prefetches chunk (ntok0, nrows) into ld (nrows = 0: none).  Returns Lambda_c.
   __device__ static float step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows,
-                               int h, E* dhs_chunk, f32x4 (&dh)[DK / 16][DV / 64]) {
+                               int h, E* dhs_chunk, f32x4 (&dh)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
     const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
-    const int n0 = w * (DV / 4);
+    const int n0 = w * (DV / NW);
 
     // ---- 1. gradient at the chunk end out; tiles into LDS; scalars
     S* sp = lds_opaque(&s0);
@@ -132,12 +137,12 @@ struct RevChunk {
     }
     __syncthreads();
 
-    // ---- 2. K K^T -> A (waves 0, 1, row pairs) + diagonal blocks of T;
-    //         Q K^T -> scale P^T (waves 2, 3)
+    // ---- 2. K K^T -> A + diagonal blocks of T; Q K^T -> scale P^T.  Four waves:
+    //         row-tile pairs {0, 3} / {1, 2} (waves 0, 1: A; 2, 3: P^T).  Eight waves:
+    //         wave r < 4 row tile r of A (then its diagonal block), wave 4 + r of P^T.
     {
       S& s = *lds_opaque(&s0);
-      const bool rows03 = (w & 1) == 0;
-      const bool isq = w >= 2;
+      const bool isq = NW == 8 ? w >= 4 : w >= 2;
       if (!isq || !CORR) {
         const E* X = isq ? s.Q : s.K;
         auto row = [&](auto RT_) {
@@ -167,9 +172,19 @@ struct RevChunk {
             }
           }
         };
-        if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
-        else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
-        if (!isq) solve_diag_pair(s.A, s.T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
+        if constexpr (NW == 8) {
+          const int rw = w & 3;
+          if (rw == 0) row(std::integral_constant<int, 0>{});
+          else if (rw == 1) row(std::integral_constant<int, 1>{});
+          else if (rw == 2) row(std::integral_constant<int, 2>{});
+          else row(std::integral_constant<int, 3>{});
+          if (!isq) solve_diag_pair(s.A, s.T, rw, rw, nullptr);
+        } else {
+          const bool rows03 = (w & 1) == 0;
+          if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
+          else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
+          if (!isq) solve_diag_pair(s.A, s.T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
+        }
       }
     }
     __syncthreads();
@@ -183,27 +198,32 @@ struct RevChunk {
     }
     __syncthreads();
 
-    // ---- 4. -W^T = -K^T diag(beta Gam) T^T; wave w takes key rows [w Dk/4, (w+1) Dk/4)
+    // ---- 4. -W^T = -K^T diag(beta Gam) T^T: (Dk/16) x 4 tiles, KTW key tiles x
+    //         RTW chunk-row tiles per wave
     {
       S& s = *lds_opaque(&s0);
-      Frag<E> yt[4][2];
+      constexpr int NKT = DK / 16;
+      constexpr int KTW = NKT >= NW ? NKT / NW : 1;
+      constexpr int RTW = NKT >= NW ? 4 : 4 * NKT / NW;
+      const int kt0 = (w % (NKT / KTW)) * KTW, rt0 = (w / (NKT / KTW)) * RTW;
+      Frag<E> yt[RTW][2];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      for (int rr = 0; rr < RTW; ++rr)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) yt[rt][kb] = ld_frag_f32<E>(s.T, LA, 16 * rt + c16, 32 * kb);
+        for (int kb = 0; kb < 2; ++kb) yt[rr][kb] = ld_frag_f32<E>(s.T, LA, 16 * (rt0 + rr) + c16, 32 * kb);
 #pragma unroll
-      for (int dd = 0; dd < DK / 64; ++dd) {
-        const int dt = w * (DK / 64) + dd;
+      for (int dd = 0; dd < KTW; ++dd) {
+        const int dt = kt0 + dd;
         Frag<E> xk[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) xk[kb] = ld_frag_kscaled<E>(s.KT, LT, 16 * dt + c16, 32 * kb, s.bg);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        for (int rr = 0; rr < RTW; ++rr) {
           f32x4 acc = zero4();
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) mma(acc, xk[kb], yt[rt][kb]);
+          for (int kb = 0; kb < 2; ++kb) mma(acc, xk[kb], yt[rr][kb]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s.WT[(16 * dt + 4 * g + i) * LT + 16 * rt + c16] = to_e<E>(-acc[i]);
+          for (int i = 0; i < 4; ++i) s.WT[(16 * dt + 4 * g + i) * LT + 16 * (rt0 + rr) + c16] = to_e<E>(-acc[i]);
         }
       }
     }
@@ -275,7 +295,7 @@ struct RevChunk {
   // Chunks ce-1 down to cb; CORR stops once the accumulated bound is below 2^-24.
   // Returns Lambda over the processed chunks; *lowest = last chunk processed.
   __device__ static float run(S& s, const RevParams& p, int64_t seq0, int len, int64_t chunk0, int cb, int ce,
-                              int h, f32x4 (&dh)[DK / 16][DV / 64], int* lowest) {
+                              int h, f32x4 (&dh)[DK / 16][DV / (16 * RevWaves<DV>::NW)], int* lowest) {
     Loader ld;
     float lam = 0.f;
     int c = ce - 1;
@@ -296,26 +316,29 @@ struct RevChunk {
 };
 
 template <class E, int DK, int DV>
-__device__ void rev_load(f32x4 (&acc)[DK / 16][DV / 64], const float* src) {
+__device__ void rev_load(f32x4 (&acc)[DK / 16][DV / (16 * RevWaves<DV>::NW)], const float* src) {
+  constexpr int NW = RevWaves<DV>::NW, NTW = DV / (16 * NW);
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
 #pragma unroll
   for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-    for (int nt = 0; nt < DV / 64; ++nt)
+    for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        acc[t][nt][i] = src ? src[(16 * t + 4 * g + i) * DV + w * (DV / 4) + 16 * nt + c16] : 0.f;
+        acc[t][nt][i] = src ? src[(16 * t + 4 * g + i) * DV + w * (DV / NW) + 16 * nt + c16] : 0.f;
 }
 template <class E, int DK, int DV>
-__device__ void rev_store(const f32x4 (&acc)[DK / 16][DV / 64], float* dst, const float* add, bool use_acc) {
+__device__ void rev_store(const f32x4 (&acc)[DK / 16][DV / (16 * RevWaves<DV>::NW)], float* dst, const float* add,
+                          bool use_acc) {
+  constexpr int NW = RevWaves<DV>::NW, NTW = DV / (16 * NW);
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
 #pragma unroll
   for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-    for (int nt = 0; nt < DV / 64; ++nt)
+    for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int e = (16 * t + 4 * g + i) * DV + w * (DV / 4) + 16 * nt + c16;
+        const int e = (16 * t + 4 * g + i) * DV + w * (DV / NW) + 16 * nt + c16;
         dst[e] = (use_acc ? acc[t][nt][i] : 0.f) + (add ? add[e] : 0.f);
       }
 }
@@ -333,14 +356,14 @@ __device__ void rev_init_smem(RevSmem<E, DK, DV>& s) {
 
 // Phase 1: every segment from dh' = 0 (the last segment of a sequence from dhT).
 template <class E, int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_rev_p1(RevParams p) {
+__global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p1(RevParams p) {
   __shared__ RevSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
   const int h = blockIdx.y, n = sd.n;
   const int nseg = p.seg_first[n + 1] - p.seg_first[n];
   const size_t SS = (size_t)DK * DV;
   const float* dhT = p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr;
-  f32x4 dh[DK / 16][DV / 64];
+  f32x4 dh[DK / 16][DV / (16 * RevWaves<DV>::NW)];
   rev_init_smem(s);
   rev_load<E, DK, DV>(dh, sd.s == nseg - 1 ? dhT : nullptr);
   const float lam = RevChunk<E, DK, DV, false>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
@@ -356,7 +379,7 @@ __global__ __launch_bounds__(256) void gdn_rev_p1(RevParams p) {
 // Phase 3: propagate the true end-of-segment gradient into each segment's last
 // chunks (or recompute the sequence serially when the certificate fails).
 template <class E, int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_rev_p3(RevParams p) {
+__global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p3(RevParams p) {
   __shared__ RevSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
   const int h = blockIdx.y, n = sd.n;
@@ -371,7 +394,7 @@ __global__ __launch_bounds__(256) void gdn_rev_p3(RevParams p) {
   bool ok = true;
   for (int j = 1; j + 1 < nseg; ++j) ok = ok && (p.lam[(size_t)(seg0 + j) * p.H + h] <= LN_EPS);
   if (!ok && sd.s != 0) return;
-  f32x4 dh[DK / 16][DV / 64];
+  f32x4 dh[DK / 16][DV / (16 * RevWaves<DV>::NW)];
   rev_init_smem(s);
   if (!ok) {
     rev_load<E, DK, DV>(dh, p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr);
@@ -388,8 +411,9 @@ __global__ __launch_bounds__(256) void gdn_rev_p3(RevParams p) {
 
 template <class E, int DK, int DV>
 hipError_t launch_rev_t(const RevParams& p, int nseg_total, hipStream_t st) {
-  if (p.phase == 1) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV>), dim3(nseg_total, p.H), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV>), dim3(nseg_total, p.H), dim3(256), 0, st, p);
+  const dim3 block(64 * RevWaves<DV>::NW);
+  if (p.phase == 1) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV>), dim3(nseg_total, p.H), block, 0, st, p);
+  else hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV>), dim3(nseg_total, p.H), block, 0, st, p);
   return hipGetLastError();
 }
 
