@@ -52,6 +52,33 @@ def kernel_models(dk, dv, esz):
     }
 
 
+def kernel_sources_sha256():
+    """Digest of the HIP sources (the key under which measured counters stay valid)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "gated_deltanet_chunked_delta_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(d, "*.hip")) + glob.glob(os.path.join(d, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    record (already scaled by the copy-kernel reference), or None if there is no record or the
+    kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def cpu_baseline(x_full, seconds_target=15.0):
     """Time the fp64 oracle (forward, then backward) on the first tokens of the workload."""
     from oracle import ref
@@ -88,6 +115,9 @@ def main():
     ap.add_argument("--save-states", action="store_true",
                     help="the forward keeps the chunk states and the backward reads them (no replay)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run a plain device copy (out = x * 1, fp32) of this many MiB three "
+                         "times: the reference kernel that scales HBM byte counters under rocprofv3 --pmc")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -188,7 +218,7 @@ def main():
         roof = {"bound": "hbm", "achieved": byte_rate, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = dom
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom, args.config)
     roof["algorithmic_per_launch"] = {"flop": f_th * units, "bytes": b_th * units}
 
     out = {
@@ -204,6 +234,16 @@ def main():
     }
     if variant is not None:
         out["variant_saved_states"] = variant
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy reference: 3 x {args.copy_mib} MiB read + {args.copy_mib} MiB written")
+        del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
