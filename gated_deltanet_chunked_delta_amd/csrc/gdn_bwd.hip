@@ -94,6 +94,35 @@ struct RevChunk {
     ld.sc.load(p.g, static_cast<const E*>(p.beta), tok0, H, h, rows);
   }
 
+  // One lower 16x16 tile (rt, ct) of A = strict_lower(diag(beta) (K K^T) * D)
+  // (ISQ false; the diagonal tile also adds the log-bound terms) or of
+  // scale P^T, P = (Q K^T) * M with the rows past the sequence end masked (ISQ true).
+  template <bool ISQ>
+  __device__ __forceinline__ static void kk_tile(S* sp, const RevParams& p, int rt, int ct, int g, int c16,
+                                                 int rows) {
+    constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
+    const E* X = ISQ ? sp->Q : sp->K;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb)
+      mma(acc, ld_frag(X, LQ, 16 * rt + c16, 32 * kb), ld_frag(sp->K, LQ, 16 * ct + c16, 32 * kb));
+    const f32x4 gr4 = *reinterpret_cast<const f32x4*>(&sp->gam[16 * rt + 4 * g]);
+    const f32x4 br4 = *reinterpret_cast<const f32x4*>(&sp->beta[16 * rt + 4 * g]);
+    const int c = 16 * ct + c16;
+    const float gc = sp->gam[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rt + 4 * g + i;
+      const float dm = __expf(gr4[i] - gc);
+      if (!ISQ) {
+        sp->A[r * LA + c] = (c < r) ? br4[i] * acc[i] * dm : 0.f;
+        if (r == c) sp->lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
+      } else {
+        sp->PT[c * LT + r] = to_e<E>((c <= r && r < rows) ? p.scale * acc[i] * dm : 0.f);
+      }
+    }
+  }
+
   // dh: gradient at the chunk end on entry, at the chunk start on exit.
   // Prefetches chunk (ntok0, nrows) into ld (nrows = 0: none).  Returns Lambda_c.
   __device__ static float step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows,
@@ -139,11 +168,36 @@ struct RevChunk {
 
     // ---- 2. K K^T -> A + diagonal blocks of T; Q K^T -> scale P^T.  Four waves:
     //         row-tile pairs {0, 3} / {1, 2} (waves 0, 1: A; 2, 3: P^T).  Eight waves:
-    //         wave r < 4 row tile r of A (then its diagonal block), wave 4 + r of P^T.
+    //         wave r < 4 forms the diagonal tile A_rr and solves block r of T at once
+    //         (the critical path); waves 4..7 share the six off-diagonal tiles of A
+    //         and the ten of P^T.
+    if constexpr (NW == 8) {
+      S* sq = lds_opaque(&s0);
+      if (w < 4) {
+        kk_tile<false>(sq, p, w, w, g, c16, rows);
+        solve_diag_pair(sq->A, sq->T, w, w, nullptr);
+      } else {
+        const int wq = w - 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int id = wq + 4 * j;  // 0..5: A tiles below the diagonal, 6..15: P^T tiles
+          if (id < 6) {
+            const int rt = id < 1 ? 1 : (id < 3 ? 2 : 3);
+            const int ct = id - (rt * (rt - 1)) / 2;
+            kk_tile<false>(sq, p, rt, ct, g, c16, rows);
+          } else if (!CORR) {
+            const int pid = id - 6;
+            const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
+            const int ct = pid - (rt * (rt + 1)) / 2;
+            kk_tile<true>(sq, p, rt, ct, g, c16, rows);
+          }
+        }
+      }
+    }
     {
       S& s = *lds_opaque(&s0);
       const bool isq = NW == 8 ? w >= 4 : w >= 2;
-      if (!isq || !CORR) {
+      if (NW == 4 && (!isq || !CORR)) {
         const E* X = isq ? s.Q : s.K;
         auto row = [&](auto RT_) {
           constexpr int RT = decltype(RT_)::value;
@@ -173,12 +227,7 @@ struct RevChunk {
           }
         };
         if constexpr (NW == 8) {
-          const int rw = w & 3;
-          if (rw == 0) row(std::integral_constant<int, 0>{});
-          else if (rw == 1) row(std::integral_constant<int, 1>{});
-          else if (rw == 2) row(std::integral_constant<int, 2>{});
-          else row(std::integral_constant<int, 3>{});
-          if (!isq) solve_diag_pair(s.A, s.T, rw, rw, nullptr);
+          (void)row;
         } else {
           const bool rows03 = (w & 1) == 0;
           if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }

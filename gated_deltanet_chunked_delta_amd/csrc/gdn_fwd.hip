@@ -194,6 +194,35 @@ struct Chunk {
   using S = FwdSmem<E, DK, DV>;
   using Loader = TileLoader<E, DK, DV, NT, OUT, !CORR>;
 
+  // One lower 16x16 tile (rt, ct) of A = strict_lower(diag(beta) (K K^T) * D)
+  // (ISQ false; the diagonal tile also adds the log-bound terms) or of
+  // P = (Q K^T) * M (ISQ true).
+  template <bool ISQ>
+  __device__ __forceinline__ static void kk_tile(S* sp, int rt, int ct, int g, int c16, int rows) {
+    constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
+    (void)rows;
+    const E* X = ISQ ? sp->Q : sp->K;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb)
+      mma(acc, ld_frag(X, LQ, 16 * rt + c16, 32 * kb), ld_frag(sp->K, LQ, 16 * ct + c16, 32 * kb));
+    const f32x4 gr4 = *reinterpret_cast<const f32x4*>(&sp->gam[16 * rt + 4 * g]);
+    const f32x4 br4 = *reinterpret_cast<const f32x4*>(&sp->beta[16 * rt + 4 * g]);
+    const int c = 16 * ct + c16;
+    const float gc = sp->gam[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rt + 4 * g + i;
+      const float dm = __expf(gr4[i] - gc);
+      if (!ISQ) {
+        sp->A[r * LA + c] = (c < r) ? br4[i] * acc[i] * dm : 0.f;
+        if (r == c) sp->lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
+      } else {
+        sp->P[r * LT + c] = to_e<E>((c <= r) ? acc[i] * dm : 0.f);
+      }
+    }
+  }
+
   // Process the chunk whose tiles `ld` holds; prefetch the next chunk (if any)
   // into `ld`.  hacc: this wave's state columns (chunk start on entry, chunk end
   // on exit).  Returns the chunk's log-bound Lambda_c.
@@ -237,13 +266,36 @@ struct Chunk {
     sp = lds_opaque(sp);
 
     // ---- 2. K K^T -> A and Q K^T -> P, lower 16x16 tiles.  Four waves: each takes a
-    //         pair of row tiles {0, 3} or {1, 2} of one product (waves 0, 1: A; 2, 3: P).
-    //         Eight waves: wave r < 4 takes row tile r of A, wave 4 + r row tile r of P.
-    //         A wave's row-side fragments are loaded once per row; the waves that
-    //         produced A's rows then solve the diagonal blocks of T they hold.
+    //         pair of row tiles {0, 3} or {1, 2} of one product (waves 0, 1: A; 2, 3: P),
+    //         loading its row-side fragments once per row; waves 0, 1 then solve the
+    //         diagonal blocks of T they hold.  Eight waves: wave r < 4 forms only the
+    //         diagonal tile A_rr and solves block r of T at once (the critical path);
+    //         waves 4..7 share the six off-diagonal tiles of A and the ten of P.
+    if constexpr (NW == 8) {
+      if (w < 4) {
+        kk_tile<false>(sp, w, w, g, c16, rows);
+        solve_diag_pair(sp->A, sp->T, w, w, nullptr);
+      } else {
+        const int wq = w - 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int id = wq + 4 * j;  // 0..5: A tiles below the diagonal, 6..15: P tiles
+          if (id < 6) {
+            const int rt = id < 1 ? 1 : (id < 3 ? 2 : 3);
+            const int ct = id - (rt * (rt - 1)) / 2;
+            kk_tile<false>(sp, rt, ct, g, c16, rows);
+          } else if (OUT) {
+            const int pid = id - 6;
+            const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
+            const int ct = pid - (rt * (rt + 1)) / 2;
+            kk_tile<true>(sp, rt, ct, g, c16, rows);
+          }
+        }
+      }
+    }
     {
       const bool isq = NW == 8 ? w >= 4 : w >= 2;
-      if (!isq || OUT) {
+      if (NW == 4 && (!isq || OUT)) {
         const E* X = isq ? sp->Q : sp->K;
         auto row = [&](auto RT_) {
           constexpr int RT = decltype(RT_)::value;
@@ -273,12 +325,7 @@ struct Chunk {
           }
         };
         if constexpr (NW == 8) {
-          const int rw = w & 3;
-          if (rw == 0) row(std::integral_constant<int, 0>{});
-          else if (rw == 1) row(std::integral_constant<int, 1>{});
-          else if (rw == 2) row(std::integral_constant<int, 2>{});
-          else row(std::integral_constant<int, 3>{});
-          if (!isq) solve_diag_pair(sp->A, sp->T, rw, rw, nullptr);
+          (void)row;
         } else {
           const bool rows03 = (w & 1) == 0;
           if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
