@@ -9,9 +9,9 @@ from __future__ import annotations
 
 import torch
 
-from .binding import GDNError, gdn_chunk_bwd, gdn_chunk_fwd, lib  # noqa: F401
+from .binding import GDNError, gdn_chunk_bwd, gdn_chunk_fwd, gdn_decode_step, lib  # noqa: F401
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_bwd", "chunk_gated_delta_rule", "GDNError", "lib"]
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_decode_step", "chunk_gated_delta_rule", "GDNError", "lib"]
 
 
 class _ChunkGatedDeltaRule(torch.autograd.Function):

@@ -40,6 +40,14 @@ class BwdArgs(ctypes.Structure):
                 ("dv", _vp), ("dbeta", _vp), ("dg", _vp), ("dh0", _vp)]
 
 
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("N", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("g", _vp), ("beta", _vp),
+                ("scale", ctypes.c_float), ("state", _vp), ("state_idx", _vp),
+                ("num_slots", ctypes.c_int32), ("o", _vp)]
+
+
 class GDNError(RuntimeError):
     pass
 
@@ -64,6 +72,8 @@ def lib():
         L.gdn_chunk_fwd.restype = ctypes.c_int
         L.gdn_chunk_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
         L.gdn_chunk_bwd.restype = ctypes.c_int
+        L.gdn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+        L.gdn_decode_step.restype = ctypes.c_int
         L.gdn_profile_enable.argtypes = [ctypes.c_int]
         L.gdn_profile_enable.restype = ctypes.c_int
         L.gdn_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -204,6 +214,32 @@ def gdn_chunk_bwd(q, k, v, g, beta, scale: float, do, h0=None, dhT=None, cu_seql
     _check(L.gdn_chunk_bwd(ctypes.byref(args), _vp(_stream(q.device))))
     del keep
     return dq, dk, dv, dg, dbeta, dh0
+
+
+def gdn_decode_step(q, k, v, g, beta, scale: float, state, state_idx=None, o=None):
+    """One recurrent step for N sequences: q, k [N, H, Dk], v [N, H, Dv], g, beta [N, H];
+    state [S, H, Dk, Dv] fp32 is updated in place (sequence n uses slot n, or state_idx[n]
+    when given; out-of-range indices mark padding).  Returns o [N, H, Dv]."""
+    dev = q.device
+    dt = q.dtype
+    for name, t, d in (("q", q, dt), ("k", k, dt), ("v", v, dt), ("beta", beta, dt),
+                       ("g", g, torch.float32), ("state", state, torch.float32)):
+        _contig(name, t, d, dev)
+    _contig("state_idx", state_idx, torch.int32, dev)
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if tuple(k.shape) != (N, H, Dk) or tuple(v.shape[:2]) != (N, H) or tuple(g.shape) != (N, H) \
+            or tuple(beta.shape) != (N, H) or tuple(state.shape[1:]) != (H, Dk, Dv):
+        raise GDNError("decode shapes disagree")
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=dt, device=dev)
+    a = DecodeArgs()
+    a.dtype, a.N, a.H, a.Dk, a.Dv = _dtype_code(q), N, H, Dk, Dv
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.scale = float(scale)
+    a.state, a.state_idx, a.num_slots, a.o = _ptr(state), _ptr(state_idx), state.shape[0], _ptr(o)
+    _check(lib().gdn_decode_step(ctypes.byref(a), _vp(_stream(dev))))
+    return o
 
 
 def gdn_profile_enable(on: bool) -> bool:

@@ -386,4 +386,31 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   return GDN_OK;
 }
 
+gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream) {
+  if (!args) return fail(GDN_E_INVALID, "null args");
+  const gdn_decode_args& a = *args;
+  if (a.dtype != GDN_F32 && a.dtype != GDN_BF16) return fail(GDN_E_UNSUPPORTED, "unknown dtype %d", a.dtype);
+  if (a.N < 0 || a.H < 1 || a.Dk < 1 || a.Dv < 1)
+    return fail(GDN_E_INVALID, "bad sizes N=%d H=%d Dk=%d Dv=%d", a.N, a.H, a.Dk, a.Dv);
+  if (!((a.Dk == 64 || a.Dk == 128) && (a.Dv == 64 || a.Dv == 128)))
+    return fail(GDN_E_UNSUPPORTED, "unsupported head sizes Dk=%d Dv=%d", a.Dk, a.Dv);
+  if ((long long)a.N * a.H >= (1LL << 31)) return fail(GDN_E_INVALID, "problem too large");
+  if (a.N == 0) return GDN_OK;
+  if (!a.q || !a.k || !a.v || !a.g || !a.beta || !a.state || !a.o) return fail(GDN_E_INVALID, "null pointer");
+  if (!aligned(a.q, 16) || !aligned(a.k, 16) || !aligned(a.v, 16) || !aligned(a.o, 16) || !aligned(a.state, 16))
+    return fail(GDN_E_INVALID, "q, k, v, o and state must be 16-byte aligned");
+  if (!aligned(a.g, 4) || !aligned(a.beta, a.dtype == GDN_F32 ? 4 : 2) || !aligned(a.state_idx, 4))
+    return fail(GDN_E_INVALID, "g / beta / state_idx misaligned");
+  if (a.num_slots < (a.state_idx ? 0 : a.N))
+    return fail(GDN_E_INVALID, "num_slots (%d) must be >= N (%d) without state_idx", a.num_slots, a.N);
+  gdn::DecodeParams p{};
+  p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta;
+  p.state = a.state; p.state_idx = a.state_idx; p.num_slots = a.num_slots;
+  p.o = a.o; p.scale = a.scale; p.N = a.N; p.H = a.H;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("decode", s, [&] { return gdn::launch_decode(a.dtype, a.Dk, a.Dv, p, s); });
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return GDN_OK;
+}
+
 }  // extern "C"

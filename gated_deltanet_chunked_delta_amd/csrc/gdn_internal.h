@@ -71,10 +71,26 @@ struct GradParams {
   const int2* chunk_tab;   // [total chunks] (sequence, chunk index within it)
 };
 
+// One recurrent decode step: N sequences x H heads, one token each.
+struct DecodeParams {
+  const void* q;              // [N, H, DK]
+  const void* k;              // [N, H, DK]
+  const void* v;              // [N, H, DV]
+  const float* g;             // [N, H]
+  const void* beta;           // [N, H]
+  float* state;               // [num_slots, H, DK, DV] fp32 h = S^T, updated in place
+  const int32_t* state_idx;   // nullable [N]: state slot of sequence n (out of range: skipped)
+  int num_slots;
+  void* o;                    // [N, H, DV]
+  float scale;
+  int N, H;
+};
+
 hipError_t launch_plan(SeqInfo seq, int N, int segc, int* chunk_first, int* seg_first, SegDesc* segs,
                        int2* chunk_tab, hipStream_t st);
 hipError_t launch_fwd(int dtype, int DK, int DV, const FwdParams& p, int nseg_total, hipStream_t st);
 hipError_t launch_rev(int dtype, int DK, int DV, const RevParams& p, int nseg_total, hipStream_t st);
 hipError_t launch_grad(int dtype, int DK, int DV, const GradParams& p, int nchunk_total, hipStream_t st);
+hipError_t launch_decode(int dtype, int DK, int DV, const DecodeParams& p, hipStream_t st);
 
 }  // namespace gdn

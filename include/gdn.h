@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
   GDN_OK = 0,
@@ -140,6 +140,42 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream);
  * and (optionally) h0.  It recomputes the forward states from the inputs
  * unless h_saved provides them. */
 gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream);
+
+/* One recurrent decode step: every listed sequence takes one new token and
+ * advances its state in place.  The pages present the kernels as serving
+ * training and inference ("Qwen's FlashQLA targets the expensive bit of
+ * long-context AI", section "What happened"; "FlashQLA resource", section 4);
+ * after a prefill (gdn_chunk_fwd with hT) the state continues token by token
+ * with the same recurrence, per sequence n and head:
+ *     S <- exp(g) S (I - beta k k^T) + beta v k^T,      o = scale * S q
+ * with the state stored as h = S^T (fp32 [Dk, Dv], as hT of the forward).
+ *
+ * Layouts (row-major, last dimension contiguous, device memory, every pointer
+ * 16-byte aligned except g and beta):
+ *   q, k [N, H, Dk], v, o [N, H, Dv] dtype;  g [N, H] fp32;  beta [N, H] dtype;
+ *   state [num_slots, H, Dk, Dv] fp32, read and written in place.
+ * state_idx (nullable int32 [N], device): sequence n uses slot state_idx[n];
+ * an index outside [0, num_slots) marks a padding entry, which is skipped
+ * (its o is not written).  NULL means slot n (num_slots >= N).  Two
+ * sequences of one call must not share a slot.
+ * Supported: bf16 and fp32 with Dk, Dv in {64, 128}.  Errors as for the chunk
+ * calls (checked before anything is enqueued); asynchronous on `stream`. */
+typedef struct {
+  int32_t dtype;               /* gdn_dtype of q, k, v, beta, o */
+  int32_t N, H, Dk, Dv;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const void* beta;
+  float scale;
+  float* state;
+  const int32_t* state_idx;
+  int32_t num_slots;
+  void* o;
+} gdn_decode_args;
+
+gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream);
 
 /* Per-kernel timing, for benchmarks (off by default).  While enabled, every
  * kernel the library launches is bracketed by a pair of HIP events recorded on

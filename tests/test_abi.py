@@ -18,7 +18,7 @@ def test_exports_every_declared_symbol(L):
             "gdn_chunk_bwd_workspace_size", "gdn_last_error", "gdn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdn_abi_version() == 2
+    assert L.gdn_abi_version() == 3
 
 
 FAKE = 1 << 20  # a 16-byte aligned fake device address; never dereferenced
@@ -119,3 +119,31 @@ def test_misaligned_saved_states_rejected(L):
     f = fwd_args()
     f.h_save = FAKE + 8
     assert call_fwd(L, f) == 1
+
+
+def dec_args(**kw):
+    a = B.DecodeArgs()
+    a.dtype, a.N, a.H, a.Dk, a.Dv = B.GDN_BF16, 4, 2, 128, 128
+    a.q = a.k = a.v = a.g = a.beta = a.state = a.o = FAKE
+    a.scale = 0.1
+    a.num_slots = 4
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q", None, 1), ("state", None, 1), ("o", None, 1), ("H", 0, 1), ("N", -1, 1),
+    ("Dk", 96, 2), ("Dv", 32, 2), ("dtype", 5, 2),
+    ("state", FAKE + 4, 1), ("q", FAKE + 8, 1),
+    ("num_slots", 3, 1),          # fewer slots than sequences without state_idx
+])
+def test_decode_rejects_bad_arguments(L, field, value, status):
+    a = dec_args(**{field: value})
+    assert L.gdn_decode_step(ctypes.byref(a), None) == status
+    assert L.gdn_last_error()
+
+
+def test_decode_empty_batch_is_a_no_op(L):
+    a = dec_args(N=0, q=None, k=None, v=None, state=None, o=None)
+    assert L.gdn_decode_step(ctypes.byref(a), None) == 0
