@@ -13,7 +13,8 @@
 // row of the slice read as one 128-byte segment), the two column sums p and o
 // are reduced over the row groups through LDS, and the updated slice is
 // written back in place.  The step is bound by HBM: the fp32 state is read and
-// written once (2 Dk Dv 4 bytes per sequence and head).
+// written once (2 Dk Dv 4 bytes per sequence and head), with non-temporal
+// accesses since nothing reuses it within the step.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(DEC_NT) void gdn_decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int i = tr + 32 * m;
-    hv[m] = *reinterpret_cast<const f32x4*>(hs + (int64_t)i * DV + c0);
+    hv[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hs + (int64_t)i * DV + c0));
     kv[m] = ld1<E>(p.k, qk + i);
     qv[m] = ld1<E>(p.q, qk + i);
   }
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(DEC_NT) void gdn_decode_kernel(DecodeParams p) {
   for (int m = 0; m < RPT; ++m) {
     const int i = tr + 32 * m;
     const f32x4 hn = hv[m] * a + u4 * kv[m];
-    *reinterpret_cast<f32x4*>(hs + (int64_t)i * DV + c0) = hn;
+    __builtin_nontemporal_store(hn, reinterpret_cast<f32x4*>(hs + (int64_t)i * DV + c0));
     part = part + hn * qv[m];
   }
 #pragma unroll
