@@ -548,7 +548,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   // ---- P1: staging (all four tiles in flight at once; rows past the end are
   //          zero); zero T, P and the cross-wave sum arrays.  h and dh' down this
   //          wave's value columns (the operands of P5) are requested right
-  //          after the tiles and stay in flight until P5.
+  //          after the tiles and stay in flight until P5; their products use the
+  //          contiguous k-slot order (one 16-byte read per fragment).
   Frag<E> hk[CTV][DK / 32], dk_[CTV][DK / 32];
   {
     const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
@@ -570,8 +571,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     for (int nt = 0; nt < CTV; ++nt)
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb) {
-        hk[nt][kb] = ld_frag(hs, DK, n0 + 16 * nt + c16, 32 * kb);
-        dk_[nt][kb] = ld_frag(dhs, DK, n0 + 16 * nt + c16, 32 * kb);
+        hk[nt][kb] = ld_frag8(hs, DK, n0 + 16 * nt + c16, 32 * kb);
+        dk_[nt][kb] = ld_frag8(dhs, DK, n0 + 16 * nt + c16, 32 * kb);
       }
     for (int e = 4 * tid; e < CH * CH; e += 4 * NT) {
       *reinterpret_cast<f32x4*>(&sT[(e >> 6) * LA + (e & 63)]) = zero4();
@@ -690,8 +691,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         f32x4 wh = zero4(), kd = zero4();
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
-          mma(wh, ld_frag(sW, LK, 16 * rt + c16, 32 * kb), hk[nt][kb]);
-          mma(kd, ld_frag(sK, LK, 16 * rt + c16, 32 * kb), dk_[nt][kb]);
+          mma(wh, ld_frag8(sW, LK, 16 * rt + c16, 32 * kb), hk[nt][kb]);
+          mma(kd, ld_frag8(sK, LK, 16 * rt + c16, 32 * kb), dk_[nt][kb]);
         }
         u[j][nt] = u[j][nt] - wh;
         kd = kd * *reinterpret_cast<const f32x4*>(&s.ek[16 * rt + 4 * g]);

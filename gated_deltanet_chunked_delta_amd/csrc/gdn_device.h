@@ -93,6 +93,25 @@ __device__ __forceinline__ Frag<float> ld_frag(const float* base, int ld, int ro
   return f;
 }
 
+// Fragment of row `row` of a row-major E matrix (LDS or global) in the
+// "contiguous" k-slot order: slot j of lane group g is k0 + 8g + j, one 16-byte
+// read per lane.  Both operands of a product must use the same order; this one
+// serves products whose operands both come from memory.
+__device__ __forceinline__ Frag<bf16> ld_frag8(const bf16* base, int ld, int row, int k0) {
+  const int g = lane_id() >> 4;
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(base + row * ld + k0 + 8 * g);
+  return f;
+}
+__device__ __forceinline__ Frag<float> ld_frag8(const float* base, int ld, int row, int k0) {
+  const int g = lane_id() >> 4;
+  const float* p = base + row * ld + k0 + 8 * g;
+  Frag<float> f;
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f;
+}
+
 // Fragment of row `row` of an fp32 row-major LDS matrix, each k-slot multiplied
 // by kscale[k] (a diagonal matrix applied on the right), converted to E.
 template <class E>
