@@ -176,10 +176,15 @@ template <class F>
 hipError_t timed(const char* name, hipStream_t s, F f) {
   if (!g_prof) return f();
   ProfRec r{name, prof_event(), prof_event()};
-  if (r.a) hipEventRecord(r.a, s);
+  const bool ok_a = r.a && hipEventRecord(r.a, s) == hipSuccess;
   hipError_t e = f();
-  if (r.b) hipEventRecord(r.b, s);
-  if (r.a && r.b) g_pending.push_back(r);
+  const bool ok_b = r.b && hipEventRecord(r.b, s) == hipSuccess;
+  if (ok_a && ok_b) {
+    g_pending.push_back(r);
+  } else {  // an unrecorded pair is not timed; its events go back to the pool
+    if (r.a) g_pool.push_back(r.a);
+    if (r.b) g_pool.push_back(r.b);
+  }
   return e;
 }
 
@@ -208,7 +213,7 @@ int gdn_profile_enable(int on) {
 
 void gdn_profile_reset(void) {
   for (ProfRec& r : g_pending) {
-    hipEventSynchronize(r.b);
+    (void)hipEventSynchronize(r.b);
     g_pool.push_back(r.a);
     g_pool.push_back(r.b);
   }

@@ -181,24 +181,6 @@ __device__ __forceinline__ Frag<E> ld_fragT(const float* M, int ld, int m, int k
   return f;
 }
 
-// Fragment whose k-slots walk down column `col` of a row-major E matrix (rows
-// k0+4g.., k0+16+4g..): the operand layout of an accumulator tile pair, read
-// from memory.  Works for LDS and global pointers.
-template <class E>
-__device__ __forceinline__ Frag<E> ld_fragC(const E* base, int64_t ld, int k0, int col) {
-  const int g = lane_id() >> 4;
-  const E* p = base + (int64_t)(k0 + 4 * g) * ld + col;
-  f32x4 a, b;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    a[j] = to_f(p[j * ld]);
-    b[j] = to_f(p[(16 + j) * ld]);
-  }
-  Frag<E> f;
-  pack_frag(f, a, b);
-  return f;
-}
-
 // Four consecutive E values as fp32, and the reverse.
 template <class E>
 __device__ __forceinline__ f32x4 ld4f(const E* p);
@@ -299,9 +281,10 @@ __device__ __forceinline__ void quad_transpose16(uint32_t& d0, uint32_t& d1) {
   }
 }
 
-// Same fragment as ld_fragC(base, ld, k0, col0 + lane%16) (k-slots walking
-// down a column of a row-major E matrix), read as 4-element row pieces and
-// turned into column pieces by quad transposes.  col0 must be a multiple of 4.
+// Fragment whose k-slots walk down column col0 + lane%16 of a row-major E
+// matrix (rows k0+4g.., k0+16+4g..: the operand layout of an accumulator tile
+// pair), read as 4-element row pieces and turned into column pieces by quad
+// transposes.  col0 must be a multiple of 4; all 64 lanes must take part.
 template <class E>
 __device__ __forceinline__ Frag<E> ld_fragC_q(const E* base, int ld, int k0, int col0);
 template <>

@@ -1,5 +1,6 @@
 // gdn_tiles.h -- LDS tile helpers shared by the forward and backward kernels:
-// the 64x64 unit-lower-triangular solve and global->LDS tile staging.
+// the 64x64 unit-lower-triangular solve, register prefetch of chunk tiles and
+// their stores into LDS, and coalesced tile writes.
 #pragma once
 #include "gdn_device.h"
 
@@ -44,39 +45,6 @@ __device__ __forceinline__ void mm16_xy(f32x4& acc, const float* X, int ldx, int
   }
 }
 
-// Off-diagonal 16x16 block of T = (I + A)^-1 (block rows/cols of 16):
-//   T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ
-// with A = diag(rs) Araw (rs null: A = Araw).
-__device__ void solve_offdiag(const float* A, float* T, int I, int J, const float* rs = nullptr) {
-  constexpr int LA = CH + 4;
-  f32x4 y = zero4();
-  for (int K = J; K < I; ++K) mm16_xy(y, A, LA, 16 * I, 16 * K, T, LA, 16 * K, 16 * J, rs);
-  f32x4 t = zero4();
-  mm16_xreg(t, T, LA, 16 * I, 16 * I, y);
-  const int l = lane_id(), g = l >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) T[(16 * I + 4 * g + i) * LA + 16 * J + (l & 15)] = -t[i];
-}
-
-// Diagonal 16x16 blocks of T by forward substitution; one wave, lane = 16*b + j
-// owns column j of block b.  (I + A) T = I  =>  T_rj = d_rj - sum_{i<r} A_ri T_ij.
-__device__ void solve_diag(const float* A, float* T, const float* rs = nullptr) {
-  constexpr int LA = CH + 4;
-  const int l = lane_id(), b = l >> 4, j = l & 15;
-  const float* Ab = A + (16 * b) * LA + 16 * b;
-  float t[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) t[r] = (r == j) ? 1.f : 0.f;
-#pragma unroll
-  for (int i = 0; i < 15; ++i) {
-#pragma unroll
-    for (int r = i + 1; r < 16; ++r) t[r] -= (rs ? rs[16 * b + r] : 1.f) * Ab[r * LA + i] * t[i];
-  }
-  float* Tb = T + (16 * b) * LA + 16 * b;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) Tb[r * LA + j] = t[r];
-}
-
 // ------------------------------------------------------------------ staging
 
 template <class E>
@@ -88,68 +56,6 @@ __device__ __forceinline__ void st4<bf16>(bf16* dst, bf16 a, bf16 b, bf16 c, bf1
 template <>
 __device__ __forceinline__ void st4<float>(float* dst, float a, float b, float c, float d) {
   *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
-}
-
-// Copy a [CH x D] tile (rows >= rows are zero) from global (row stride gld
-// elements) into LDS row-major (dst, ld) and/or transposed (dstT, ldT).
-template <class E, int D, int NT>
-__device__ __forceinline__ void stage_tile(const E* __restrict__ src, int64_t gld, int rows,
-                                           E* dst, int ld, E* dstT, int ldT) {
-  constexpr int VEC = 16 / sizeof(E);
-  constexpr int CG = D / VEC;          // vector columns per row
-  constexpr int NB = (CH / 4) * CG;    // 4-row blocks
-  typedef E vec_t __attribute__((__vector_size__(16)));
-  for (int blk = threadIdx.x; blk < NB; blk += NT) {
-    const int r0 = (blk / CG) * 4, c0 = (blk % CG) * VEC;
-    vec_t x[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (r0 + j < rows) x[j] = *reinterpret_cast<const vec_t*>(src + (int64_t)(r0 + j) * gld + c0);
-      else
-        for (int e = 0; e < VEC; ++e) x[j][e] = (E)0.f;
-    }
-    if (dst) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4)
-          st4<E>(dst + (r0 + j) * ld + c0 + e, x[j][e], x[j][e + 1], x[j][e + 2], x[j][e + 3]);
-    }
-    if (dstT) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) st4<E>(dstT + (c0 + e) * ldT + r0, x[0][e], x[1][e], x[2][e], x[3][e]);
-    }
-  }
-}
-
-
-// One diagonal 16x16 block b of T = (I + A)^-1 by forward substitution, done by
-// one wave: lane (j = l%16, g = l/16) owns rows 4g..4g+3 of column j.  Step i
-// finalises row i (broadcast from its owner lane) and removes A_ri T_ij from
-// every later row r.  A = diag(rs) Araw (rs may be null).
-__device__ __forceinline__ void solve_diag_block(const float* A, float* T, int b, const float* rs) {
-  constexpr int LA = CH + 4;
-  const int l = lane_id(), j = l & 15, g = l >> 4;
-  const float* Ab = A + (16 * b) * LA + 16 * b;
-  float t[4], sc[4];
-#pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    t[ii] = (4 * g + ii == j) ? 1.f : 0.f;
-    sc[ii] = rs ? rs[16 * b + 4 * g + ii] : 1.f;
-  }
-#pragma unroll
-  for (int i = 0; i < 15; ++i) {
-    const float ti = __shfl(t[i & 3], 16 * (i >> 2) + j, 64);
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int r = 4 * g + ii;
-      const float a = sc[ii] * Ab[r * LA + i];
-      t[ii] = (r > i) ? t[ii] - a * ti : t[ii];
-    }
-  }
-  float* Tb = T + (16 * b) * LA + 16 * b;
-#pragma unroll
-  for (int ii = 0; ii < 4; ++ii) Tb[(4 * g + ii) * LA + j] = t[ii];
 }
 
 // Two diagonal 16x16 blocks (ba, bb) of T by forward substitution in one wave,
@@ -187,29 +93,6 @@ __device__ __forceinline__ void solve_diag_pair(const float* A, float* T, int ba
   }
 }
 
-// First off-diagonal level (after all diagonal blocks): wave 0 -> T_10, wave 1 -> T_32.
-__device__ __forceinline__ void solve_level1(const float* A, float* T, int w, const float* rs) {
-  if (w == 0) solve_offdiag(A, T, 1, 0, rs);
-  else if (w == 1) solve_offdiag(A, T, 3, 2, rs);
-}
-
-// Second level: the lower-left 32x32 block of T from the two 32x32 diagonal
-// inverses,  T_ll = -T_bot * A_ll * T_top  (waves 0..3 -> T_20, T_21, T_30, T_31).
-__device__ __forceinline__ void solve_level2(const float* A, float* T, int w, const float* rs) {
-  constexpr int LA = CH + 4;
-  if (w > 3) return;
-  const int I = 2 + (w >> 1), J = w & 1;
-  f32x4 out = zero4();
-  for (int K = 2; K <= I; ++K) {
-    f32x4 y = zero4();
-    for (int M = J; M <= 1; ++M) mm16_xy(y, A, LA, 16 * K, 16 * M, T, LA, 16 * M, 16 * J, rs);
-    mm16_xreg(out, T, LA, 16 * I, 16 * K, y);
-  }
-  const int l = lane_id(), g = l >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) T[(16 * I + 4 * g + i) * LA + 16 * J + (l & 15)] = -out[i];
-}
-
 // All off-diagonal 16x16 blocks of T (after the diagonal blocks), one block
 // column per wave: wave J (< 3) forms T_IJ for I = J+1 .. 3 in order,
 //   T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ,
@@ -239,34 +122,6 @@ __device__ __forceinline__ void solve_columns(const float* A, float* T, int w, c
   if (w == 0) solve_column<0>(A, T, rs);
   else if (w == 1) solve_column<1>(A, T, rs);
   else if (w == 2) solve_column<2>(A, T, rs);
-}
-
-// Full solve with 3 barriers, for kernels with at least 4 waves.  T's
-// strictly-upper blocks must already be zero; complete after the final barrier.
-__device__ __forceinline__ void solve_T4(const float* A, float* T, const float* rs) {
-  const int w = wave_id();
-  if (w < 4) solve_diag_block(A, T, w, rs);
-  __syncthreads();
-  solve_level1(A, T, w, rs);
-  __syncthreads();
-  solve_level2(A, T, w, rs);
-  __syncthreads();
-}
-
-// Solve T = (I + diag(rs) Araw)^-1 for a 64x64 strictly-lower Araw (fp32, row
-// stride CH+4) into T, using waves 0..2 of the workgroup.  Must be called by
-// every thread (it contains barriers); T's strictly-upper blocks must already
-// be zero.  On return (after the final barrier) T is complete.
-__device__ __forceinline__ void solve_T(const float* A, float* T, const float* rs) {
-  const int w = wave_id();
-  if (w == 0) solve_diag(A, T, rs);
-  __syncthreads();
-  if (w < 3) solve_offdiag(A, T, w + 1, w, rs);
-  __syncthreads();
-  if (w < 2) solve_offdiag(A, T, w + 2, w, rs);
-  __syncthreads();
-  if (w == 0) solve_offdiag(A, T, 3, 0, rs);
-  __syncthreads();
 }
 
 }  // namespace gdn
