@@ -191,6 +191,9 @@ def main():
                          "(its own JSON line; not the headline metric)")
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--cp-mode", type=int, default=0)
+    ap.add_argument("--prep", action="store_true",
+                    help="in-kernel pre-processing: raw q, k (rescaled rows) normalised inside the kernels, "
+                         "gate and beta passed as logits (g = -0.1 softplus(a), beta = sigmoid(b))")
     ap.add_argument("--save-states", action="store_true",
                     help="the forward keeps the chunk states and the backward reads them (no replay)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -215,6 +218,17 @@ def main():
     dev = torch.device("cuda:0")
     log(f"generating {args.config}")
     x = gdn_inputs.config(args.config, grad=True)
+    prep_kw = {}
+    if args.prep:
+        # raw inputs of the same workload: rows rescaled, gate / beta as logits
+        rng = np.random.default_rng(12345)
+        rnd = gdn_inputs.round_bf16 if x.dtype == "bf16" else (lambda a: a.astype(np.float32))
+        x.q = rnd(x.q * rng.uniform(0.25, 4.0, size=x.q.shape[:-1] + (1,)))
+        x.k = rnd(x.k * rng.uniform(0.25, 4.0, size=x.k.shape[:-1] + (1,)))
+        x.g = rng.standard_normal(x.g.shape).astype(np.float32)
+        x.beta = rnd(rng.standard_normal(x.beta.shape))
+        prep_kw = dict(qk_norm=True, gate_act=True,
+                       gate_scale=torch.full((x.q.shape[2],), 0.1, dtype=torch.float32, device=dev))
     B, T, H, dk = x.q.shape
     dv = x.v.shape[-1]
     dt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
@@ -237,11 +251,11 @@ def main():
         states = None
         if args.direction in ("fwdbwd", "fwd"):
             res = gb.gdn_chunk_fwd(q, k, v, g, beta, x.scale, h0=h0, cu_seqlens=cu, cu_seqlens_host=host,
-                                   cp_mode=args.cp_mode, save_states=keep)
+                                   cp_mode=args.cp_mode, save_states=keep, **prep_kw)
             states = res[2] if keep else None
         if args.direction in ("fwdbwd", "bwd"):
             gb.gdn_chunk_bwd(q, k, v, g, beta, x.scale, do, h0=h0, cu_seqlens=cu, cu_seqlens_host=host,
-                             cp_mode=args.cp_mode, need_dh0=h0 is not None, states=states)
+                             cp_mode=args.cp_mode, need_dh0=h0 is not None, states=states, **prep_kw)
 
     stream = torch.cuda.current_stream(dev)
 
@@ -309,7 +323,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": CH,
                    "direction": args.direction, "cp_mode": args.cp_mode, "tokens_per_step": ntok,
-                   "states": "saved by fwd" if args.save_states else "recomputed in bwd"},
+                   "states": "saved by fwd" if args.save_states else "recomputed in bwd",
+                   "preprocessing": "in-kernel q/k L2 norm + gate/beta activation" if args.prep else "none"},
         "tflops": tflops, "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "kernels": kernels, "roofline": roof,
     }

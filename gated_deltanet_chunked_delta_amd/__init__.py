@@ -16,38 +16,46 @@ __all__ = ["gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_decode_step", "chunk_gated_del
 
 class _ChunkGatedDeltaRule(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, h0, scale, cu_seqlens, cu_seqlens_host, cp_mode, save_states):
+    def forward(ctx, q, k, v, g, beta, h0, scale, cu_seqlens, cu_seqlens_host, cp_mode, save_states,
+                qk_norm, gate_act, gate_scale):
         res = gdn_chunk_fwd(q, k, v, g, beta, scale, h0=h0, cu_seqlens=cu_seqlens,
                             cu_seqlens_host=cu_seqlens_host, output_final_state=True, cp_mode=cp_mode,
-                            save_states=save_states)
+                            save_states=save_states, qk_norm=qk_norm, gate_act=gate_act, gate_scale=gate_scale)
         o, hT = res[0], res[1]
         states = res[2] if save_states else None
-        ctx.save_for_backward(q, k, v, g, beta, h0, cu_seqlens, states)
+        ctx.save_for_backward(q, k, v, g, beta, h0, cu_seqlens, states, gate_scale)
         ctx.scale, ctx.cu_host, ctx.cp_mode = scale, cu_seqlens_host, cp_mode
+        ctx.qk_norm, ctx.gate_act = qk_norm, gate_act
         return o, hT
 
     @staticmethod
     def backward(ctx, do, dhT):
-        q, k, v, g, beta, h0, cu, states = ctx.saved_tensors
+        q, k, v, g, beta, h0, cu, states, gate_scale = ctx.saved_tensors
         dq, dk, dv, dg, dbeta, dh0 = gdn_chunk_bwd(
             q, k, v, g, beta, ctx.scale, do.contiguous(), h0=h0,
             dhT=None if dhT is None else dhT.contiguous(), cu_seqlens=cu,
-            cu_seqlens_host=ctx.cu_host, cp_mode=ctx.cp_mode, need_dh0=h0 is not None, states=states)
-        return dq, dk, dv, dg, dbeta, dh0, None, None, None, None, None
+            cu_seqlens_host=ctx.cu_host, cp_mode=ctx.cp_mode, need_dh0=h0 is not None, states=states,
+            qk_norm=ctx.qk_norm, gate_act=ctx.gate_act, gate_scale=gate_scale)
+        return dq, dk, dv, dg, dbeta, dh0, None, None, None, None, None, None, None, None
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
-                           cu_seqlens=None, cu_seqlens_host=None, cp_mode: int = 0, save_states: bool = True):
+                           cu_seqlens=None, cu_seqlens_host=None, cp_mode: int = 0, save_states: bool = True,
+                           qk_norm: bool = False, gate_act: bool = False, gate_scale=None):
     """o, (hT) for the gated delta rule over [B, T, H, D] inputs, differentiable.
 
     g is the fp32 natural-log decay [B, T, H]; beta has the dtype of q.  With
     save_states (the default) the forward keeps the state at every chunk start
     (Dk * Dv values per 64 tokens and head, in the input dtype) so that the
     backward does not recompute them; pass False to trade that memory for a
-    forward replay inside the backward.
+    forward replay inside the backward.  qk_norm: q and k are raw and normalised
+    inside the kernels; gate_act: g and beta are logits, g = -gate_scale[h]
+    softplus(g), beta = sigmoid(beta) inside the kernels (gate_scale is not
+    differentiated).
     """
     if scale is None:
         scale = q.shape[-1] ** -0.5
     o, hT = _ChunkGatedDeltaRule.apply(q, k, v, g, beta, initial_state, float(scale), cu_seqlens,
-                                       cu_seqlens_host, int(cp_mode), bool(save_states))
+                                       cu_seqlens_host, int(cp_mode), bool(save_states), bool(qk_norm),
+                                       bool(gate_act), gate_scale)
     return (o, hT) if output_final_state else o

@@ -28,7 +28,8 @@ class CommonArgs(ctypes.Structure):
                 ("scale", ctypes.c_float),
                 ("cu_seqlens", _vp), ("cu_seqlens_host", _vp),
                 ("num_seqs", ctypes.c_int32), ("cp_mode", ctypes.c_int32),
-                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+                ("qk_norm", ctypes.c_int32), ("gate_act", ctypes.c_int32), ("gate_scale", _vp)]
 
 
 class FwdArgs(ctypes.Structure):
@@ -45,7 +46,8 @@ class DecodeArgs(ctypes.Structure):
                 ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32),
                 ("q", _vp), ("k", _vp), ("v", _vp), ("g", _vp), ("beta", _vp),
                 ("scale", ctypes.c_float), ("state", _vp), ("state_idx", _vp),
-                ("num_slots", ctypes.c_int32), ("o", _vp)]
+                ("num_slots", ctypes.c_int32), ("o", _vp),
+                ("qk_norm", ctypes.c_int32), ("gate_act", ctypes.c_int32), ("gate_scale", _vp)]
 
 
 class GDNError(RuntimeError):
@@ -116,7 +118,18 @@ def _contig(name, t, dtype=None, device=None):
     return t
 
 
-def _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode):
+def _prep(a, q, qk_norm, gate_act, gate_scale):
+    """Fill the pre-processing fields of an argument struct."""
+    a.qk_norm, a.gate_act = int(bool(qk_norm)), int(bool(gate_act))
+    if gate_scale is not None:
+        _contig("gate_scale", gate_scale, torch.float32, q.device)
+        if gate_scale.numel() != a.H:
+            raise GDNError("gate_scale must have H entries")
+    a.gate_scale = _ptr(gate_scale)
+
+
+def _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode,
+            qk_norm=False, gate_act=False, gate_scale=None):
     dev = q.device
     dt = q.dtype
     _contig("q", q, dt, dev)
@@ -149,6 +162,7 @@ def _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode):
     else:
         a.num_seqs = B
     a.cp_mode = int(cp_mode)
+    _prep(a, q, qk_norm, gate_act, gate_scale)
     return a, keep
 
 
@@ -157,11 +171,14 @@ def _stream(dev):
 
 
 def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_seqlens_host=None,
-                  output_final_state: bool = True, cp_mode: int = 0, save_states: bool = False):
+                  output_final_state: bool = True, cp_mode: int = 0, save_states: bool = False,
+                  qk_norm: bool = False, gate_act: bool = False, gate_scale=None):
     """Forward pass.  Returns (o, hT) with hT None unless output_final_state; with
     save_states, (o, hT, states) where states (the state at every chunk start, for
-    gdn_chunk_bwd) is a flat tensor of the input dtype."""
-    a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode)
+    gdn_chunk_bwd) is a flat tensor of the input dtype.  qk_norm / gate_act select the
+    in-kernel pre-processing (raw q, k; gate and beta logits, see include/gdn.h)."""
+    a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode,
+                      qk_norm, gate_act, gate_scale)
     L = lib()
     o = torch.empty(q.shape[:3] + (a.Dv,), dtype=q.dtype, device=q.device)
     hT = (torch.empty((a.num_seqs, a.H, a.Dk, a.Dv), dtype=torch.float32, device=q.device)
@@ -184,11 +201,14 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_s
 
 
 def gdn_chunk_bwd(q, k, v, g, beta, scale: float, do, h0=None, dhT=None, cu_seqlens=None,
-                  cu_seqlens_host=None, cp_mode: int = 0, need_dh0: bool = True, states=None):
+                  cu_seqlens_host=None, cp_mode: int = 0, need_dh0: bool = True, states=None,
+                  qk_norm: bool = False, gate_act: bool = False, gate_scale=None):
     """Backward pass.  Returns (dq, dk, dv, dg, dbeta, dh0) with dh0 None unless need_dh0.
     states: the forward's saved chunk states (gdn_chunk_fwd(..., save_states=True)); when
-    given the backward does not recompute them."""
-    a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode)
+    given the backward does not recompute them.  With qk_norm / gate_act the gradients
+    are with respect to the raw inputs."""
+    a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode,
+                      qk_norm, gate_act, gate_scale)
     _contig("do", do, q.dtype, q.device)
     _contig("dhT", dhT, torch.float32, q.device)
     _contig("states", states, q.dtype, q.device)
@@ -216,7 +236,8 @@ def gdn_chunk_bwd(q, k, v, g, beta, scale: float, do, h0=None, dhT=None, cu_seql
     return dq, dk, dv, dg, dbeta, dh0
 
 
-def gdn_decode_step(q, k, v, g, beta, scale: float, state, state_idx=None, o=None):
+def gdn_decode_step(q, k, v, g, beta, scale: float, state, state_idx=None, o=None,
+                    qk_norm: bool = False, gate_act: bool = False, gate_scale=None):
     """One recurrent step for N sequences: q, k [N, H, Dk], v [N, H, Dv], g, beta [N, H];
     state [S, H, Dk, Dv] fp32 is updated in place (sequence n uses slot n, or state_idx[n]
     when given; out-of-range indices mark padding).  Returns o [N, H, Dv]."""
@@ -238,6 +259,7 @@ def gdn_decode_step(q, k, v, g, beta, scale: float, state, state_idx=None, o=Non
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
     a.scale = float(scale)
     a.state, a.state_idx, a.num_slots, a.o = _ptr(state), _ptr(state_idx), state.shape[0], _ptr(o)
+    _prep(a, q, qk_norm, gate_act, gate_scale)
     _check(lib().gdn_decode_step(ctypes.byref(a), _vp(_stream(dev))))
     return o
 

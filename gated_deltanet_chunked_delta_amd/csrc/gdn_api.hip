@@ -63,6 +63,14 @@ bool supported(int dtype, int Dk, int Dv) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+gdn_status check_prep(int qk_norm, int gate_act, const float* gate_scale) {
+  if ((qk_norm != 0 && qk_norm != 1) || (gate_act != 0 && gate_act != 1))
+    return fail(GDN_E_INVALID, "qk_norm and gate_act must be 0 or 1");
+  if (gate_scale && !gate_act) return fail(GDN_E_INVALID, "gate_scale is only used with gate_act");
+  if (!aligned(gate_scale, 4)) return fail(GDN_E_INVALID, "gate_scale misaligned");
+  return GDN_OK;
+}
+
 gdn_status check_common(const gdn_common_args& a) {
   if (a.dtype != GDN_F32 && a.dtype != GDN_BF16) return fail(GDN_E_UNSUPPORTED, "unknown dtype %d", a.dtype);
   if (a.B < 1 || a.T < 0 || a.H < 1 || a.Dk < 1 || a.Dv < 1)
@@ -94,7 +102,15 @@ gdn_status check_common(const gdn_common_args& a) {
     return fail(GDN_E_INVALID, "num_seqs (%d) must equal B (%d) without cu_seqlens", a.num_seqs, a.B);
   }
   if (a.cp_mode < -1) return fail(GDN_E_INVALID, "cp_mode must be -1, 0 or a positive chunk count");
-  return GDN_OK;
+  return check_prep(a.qk_norm, a.gate_act, a.gate_scale);
+}
+
+gdn::PrepParams prep_of(int qk_norm, int gate_act, const float* gate_scale) {
+  gdn::PrepParams pp;
+  pp.qk_norm = qk_norm;
+  pp.gate_act = gate_act;
+  pp.gate_scale = gate_scale;
+  return pp;
 }
 
 // Segment length, totals and workspace layout.  `bwd` adds the backward's arrays
@@ -301,6 +317,7 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   p.bstate = pl.cp ? at<float>(ws, pl.o_bstate) : nullptr;
   p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
   p.hs = args->h_save;  // nullable: the chunk states are stored only on request
+  p.prep = prep_of(a.qk_norm, a.gate_act, a.gate_scale);
   p.phase = 1;
   e = timed("fwd", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
@@ -341,6 +358,7 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   // 1. forward replay: state at every chunk start (unless the forward saved them)
   gdn::FwdParams p{};
+  p.prep = prep_of(a.qk_norm, a.gate_act, a.gate_scale);
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta; p.h0 = a.h0;
   p.o = nullptr; p.hT = nullptr; p.scale = a.scale; p.H = a.H; p.seq = sq;
   p.segs = at<gdn::SegDesc>(ws, pl.o_segs);
@@ -369,6 +387,7 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   r.bstate = pl.cp ? at<float>(ws, pl.o_bstate2) : nullptr;
   r.lam = pl.cp ? at<float>(ws, pl.o_lam2) : nullptr;
   r.dhs = at<void>(ws, pl.o_dhs);
+  r.prep = p.prep;
   r.phase = 1;
   e = timed("rev", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "reverse launch");
@@ -385,6 +404,7 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
     gp.dq = args->dq; gp.dk = args->dk; gp.dv = args->dv; gp.dbeta = args->dbeta; gp.dg = args->dg;
     gp.scale = a.scale; gp.H = a.H; gp.seq = sq;
     gp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);
+    gp.prep = p.prep;
     e = timed("grad", s, [&] { return gdn::launch_grad(a.dtype, a.Dk, a.Dv, gp, pl.nchunk, s); });
     if (e != hipSuccess) return hip_fail(e, "gradient launch");
   }
@@ -408,10 +428,12 @@ gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream) {
     return fail(GDN_E_INVALID, "g / beta / state_idx misaligned");
   if (a.num_slots < (a.state_idx ? 0 : a.N))
     return fail(GDN_E_INVALID, "num_slots (%d) must be >= N (%d) without state_idx", a.num_slots, a.N);
+  if (gdn_status ps = check_prep(a.qk_norm, a.gate_act, a.gate_scale); ps != GDN_OK) return ps;
   gdn::DecodeParams p{};
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta;
   p.state = a.state; p.state_idx = a.state_idx; p.num_slots = a.num_slots;
   p.o = a.o; p.scale = a.scale; p.N = a.N; p.H = a.H;
+  p.prep = prep_of(a.qk_norm, a.gate_act, a.gate_scale);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = timed("decode", s, [&] { return gdn::launch_decode(a.dtype, a.Dk, a.Dv, p, s); });
   if (e != hipSuccess) return hip_fail(e, "decode launch");

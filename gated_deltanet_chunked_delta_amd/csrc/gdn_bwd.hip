@@ -73,7 +73,7 @@ struct RevWaves { static constexpr int NW = DV == 128 ? 8 : 4; };
 // One chunk of the reverse chain (wave w owns Dv/NW columns of the state
 // gradient).  CORR: propagation of a boundary difference only (dO does not
 // enter, stored gradients are incremented).
-template <class E, int DK, int DV, bool CORR>
+template <class E, int DK, int DV, bool CORR, bool PREP>
 struct RevChunk {
   static constexpr int NW = RevWaves<DV>::NW, NT = 64 * NW, NTW = DV / (16 * NW);
   using S = RevSmem<E, DK, DV>;
@@ -144,6 +144,10 @@ struct RevChunk {
         st4f<E>(dst, val);
       }
     S& s1 = *sp;
+    if (PREP && p.prep.qk_norm) {
+      ld.k.normalize_rows();
+      if (!CORR) ld.q.normalize_rows();
+    }
     ld.k.store(s1.K, LQ, s1.KT, LT);
     if (!CORR) {
       ld.q.store(s1.Q, LQ, s1.QT, LT);
@@ -151,7 +155,8 @@ struct RevChunk {
     }
     if (w == 0) {
       S& s = s1;
-      const float gr = ld.sc.g_at(l), bt = ld.sc.beta_at(l);
+      float gr, bt;
+      ld.sc.template gb_at<PREP>(l, p.prep, h, gr, bt);
       const float gm = wave_incl_scan(gr);
       const float gC = __shfl(gm, 63, 64);
       const float Gm = __expf(gm);
@@ -404,7 +409,7 @@ __device__ void rev_init_smem(RevSmem<E, DK, DV>& s) {
 }
 
 // Phase 1: every segment from dh' = 0 (the last segment of a sequence from dhT).
-template <class E, int DK, int DV>
+template <class E, int DK, int DV, bool PREP>
 __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p1(RevParams p) {
   __shared__ RevSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p1(RevParams p)
   f32x4 dh[DK / 16][DV / (16 * RevWaves<DV>::NW)];
   rev_init_smem(s);
   rev_load<E, DK, DV>(dh, sd.s == nseg - 1 ? dhT : nullptr);
-  const float lam = RevChunk<E, DK, DV, false>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
+  const float lam = RevChunk<E, DK, DV, false, PREP>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
                                                     sd.c_begin, sd.c_end, h, dh, nullptr);
   if (nseg == 1) {
     if (p.dh0) rev_store<E, DK, DV>(dh, p.dh0 + ((size_t)n * p.H + h) * SS, nullptr, true);
@@ -427,7 +432,7 @@ __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p1(RevParams p)
 
 // Phase 3: propagate the true end-of-segment gradient into each segment's last
 // chunks (or recompute the sequence serially when the certificate fails).
-template <class E, int DK, int DV>
+template <class E, int DK, int DV, bool PREP>
 __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p3(RevParams p) {
   __shared__ RevSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
@@ -447,13 +452,13 @@ __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p3(RevParams p)
   rev_init_smem(s);
   if (!ok) {
     rev_load<E, DK, DV>(dh, p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr);
-    RevChunk<E, DK, DV, false>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, dh, nullptr);
+    RevChunk<E, DK, DV, false, PREP>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, dh, nullptr);
     if (dh0) rev_store<E, DK, DV>(dh, dh0, nullptr, true);
     return;
   }
   rev_load<E, DK, DV>(dh, p.bstate + ((size_t)(blockIdx.x + 1) * p.H + h) * SS);
   int lowest = sd.c_end;
-  RevChunk<E, DK, DV, true>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, dh, &lowest);
+  RevChunk<E, DK, DV, true, PREP>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, dh, &lowest);
   if (sd.s == 0 && dh0)
     rev_store<E, DK, DV>(dh, dh0, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, lowest == sd.c_begin);
 }
@@ -461,8 +466,14 @@ __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p3(RevParams p)
 template <class E, int DK, int DV>
 hipError_t launch_rev_t(const RevParams& p, int nseg_total, hipStream_t st) {
   const dim3 block(64 * RevWaves<DV>::NW);
-  if (p.phase == 1) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV>), dim3(nseg_total, p.H), block, 0, st, p);
-  else hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV>), dim3(nseg_total, p.H), block, 0, st, p);
+  const dim3 grid(nseg_total, p.H);
+  if (p.prep.qk_norm || p.prep.gate_act) {
+    if (p.phase == 1) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV, true>), grid, block, 0, st, p);
+  } else {
+    if (p.phase == 1) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV, false>), grid, block, 0, st, p);
+  }
   return hipGetLastError();
 }
 
@@ -514,7 +525,7 @@ enum { SK = 0, SKT = 1, SQ = 2, SV = 3, SDO = 4, ST = 5, SKD = 6, SP = 7, SDU = 
 // waves share each SIMD and every accumulator array is half the size it would
 // be with four waves.  Sums over rows or columns that cross those halves go
 // through small LDS arrays with a single writer per entry (deterministic).
-template <class E, int DK, int DV>
+template <class E, int DK, int DV, bool PREP>
 __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   using L = GradLayout<E, DK, DV>;
   constexpr int NT = 512;
@@ -587,6 +598,10 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       const int64_t si = (tok0 + l) * H + h;
       float gr = valid ? p.g[si] : 0.f;
       float bt = valid ? to_f(static_cast<const E*>(p.beta)[si]) : 0.f;
+      if (PREP && p.prep.gate_act && valid) {
+        gr = -(p.prep.gate_scale ? p.prep.gate_scale[h] : 1.f) * softplus_f(gr);
+        bt = sigmoid_f(bt);
+      }
       float gm = wave_incl_scan(gr);
       float gC = __shfl(gm, 63, 64);
       float Gm = __expf(gm);
@@ -596,6 +611,10 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       s.beta[l] = bt;
       s.bg[l] = bt * Gm;
       if (l == 0) s.GamC = __expf(gC);
+    }
+    if (PREP && p.prep.qk_norm && rh == 0) {
+      tk.normalize_rows(ht);
+      tq.normalize_rows(ht);
     }
     if (rh == 0) {
       tk.store(sK, LK, sKT, LT, ht);
@@ -997,8 +1016,16 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   __syncthreads();
   store_tile<E, DV, NT>(slotE(SQ), LV, static_cast<E*>(p.dv) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
-  store_tile<E, DK, NT>(slotE(SDO), LK, static_cast<E*>(p.dq) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
-  store_tile<E, DK, NT>(slotE(SK), LK, static_cast<E*>(p.dk) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
+  if (PREP && p.prep.qk_norm) {
+    // gradients with respect to the raw q and k (the kernel saw them normalised)
+    store_tile_unnorm<E, DK, NT>(slotE(SDO), LK, static_cast<const E*>(p.q) + (tok0 * H + h) * DK, (int64_t)H * DK,
+                                 static_cast<E*>(p.dq) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
+    store_tile_unnorm<E, DK, NT>(slotE(SK), LK, static_cast<const E*>(p.k) + (tok0 * H + h) * DK, (int64_t)H * DK,
+                                 static_cast<E*>(p.dk) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
+  } else {
+    store_tile<E, DK, NT>(slotE(SDO), LK, static_cast<E*>(p.dq) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
+    store_tile<E, DK, NT>(slotE(SK), LK, static_cast<E*>(p.dk) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
+  }
   if (w == 0) {
     const int r = l;
     float dgm = s.c10[0][r] + s.c10[1][r], db = 0.f;
@@ -1019,15 +1046,26 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     const float dgv = __shfl(sc, CH - 1 - r, 64);
     if (r < rows) {
       const int64_t si = (tok0 + r) * H + h;
-      p.dg[si] = dgv;
-      static_cast<E*>(p.dbeta)[si] = to_e<E>(db);
+      if (PREP && p.prep.gate_act) {
+        // chain rule through g = -s softplus(a) and beta = sigmoid(b)
+        const float s_h = p.prep.gate_scale ? p.prep.gate_scale[h] : 1.f;
+        const float bs = sigmoid_f(to_f(static_cast<const E*>(p.beta)[si]));
+        p.dg[si] = -s_h * sigmoid_f(p.g[si]) * dgv;
+        static_cast<E*>(p.dbeta)[si] = to_e<E>(db * bs * (1.f - bs));
+      } else {
+        p.dg[si] = dgv;
+        static_cast<E*>(p.dbeta)[si] = to_e<E>(db);
+      }
     }
   }
 }
 
 template <class E, int DK, int DV>
 hipError_t launch_grad_t(const GradParams& p, int nchunk_total, hipStream_t st) {
-  hipLaunchKernelGGL((gdn_grad_kernel<E, DK, DV>), dim3(nchunk_total, p.H), dim3(512), 0, st, p);
+  if (p.prep.qk_norm || p.prep.gate_act)
+    hipLaunchKernelGGL((gdn_grad_kernel<E, DK, DV, true>), dim3(nchunk_total, p.H), dim3(512), 0, st, p);
+  else
+    hipLaunchKernelGGL((gdn_grad_kernel<E, DK, DV, false>), dim3(nchunk_total, p.H), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 

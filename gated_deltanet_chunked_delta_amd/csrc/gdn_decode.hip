@@ -6,6 +6,8 @@
 // serve training and inference).  With h = S^T (Dk x Dv) the step is
 //     p = h^T k,   u = beta (v - e^g p),   h' = e^g h + k u^T,   o = scale h'^T q,
 // the same algebra as S' = e^g S (I - beta k k^T) + beta v k^T, o = scale S' q.
+// With the optional pre-processing, q and k are first divided by their L2
+// norms and g, beta are formed from logits (as in the chunk kernels).
 //
 // Every column j of h evolves independently given (q, k, v_j, g, beta): a
 // workgroup owns a 32-column slice of one (sequence, head) state.  Its 256
@@ -43,8 +45,32 @@ __global__ __launch_bounds__(DEC_NT) void gdn_decode_kernel(DecodeParams p) {
   float* hs = p.state + ((int64_t)slot * p.H + h) * DK * DV;
   const int64_t qk = (int64_t)nh * DK;
 
-  const float gl = p.g[nh];
-  const float a = __expf(gl), bt = ld1<E>(p.beta, nh);
+  float gl = p.g[nh], bt = ld1<E>(p.beta, nh);
+  if (p.prep.gate_act) {
+    gl = -(p.prep.gate_scale ? p.prep.gate_scale[h] : 1.f) * softplus_f(gl);
+    bt = sigmoid_f(bt);
+  }
+  const float a = __expf(gl);
+  // optional L2 normalisation of q and k: wave 0 forms both norms
+  __shared__ float inv_norm[2];
+  if (p.prep.qk_norm) {
+    if (tid < 64) {
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int i = tid; i < DK; i += 64) {
+        const float kk = ld1<E>(p.k, qk + i), qq = ld1<E>(p.q, qk + i);
+        sk += kk * kk;
+        sq += qq * qq;
+      }
+      sk = wave_sum(sk);
+      sq = wave_sum(sq);
+      if (tid == 0) {
+        inv_norm[0] = rsqrtf(sk + QK_NORM_EPS);
+        inv_norm[1] = rsqrtf(sq + QK_NORM_EPS);
+      }
+    }
+    __syncthreads();
+  }
 
   // own rows of the slice and the matching k, q entries
   f32x4 hv[RPT];
@@ -55,6 +81,15 @@ __global__ __launch_bounds__(DEC_NT) void gdn_decode_kernel(DecodeParams p) {
     hv[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hs + (int64_t)i * DV + c0));
     kv[m] = ld1<E>(p.k, qk + i);
     qv[m] = ld1<E>(p.q, qk + i);
+  }
+
+  if (p.prep.qk_norm) {
+    const float ik = inv_norm[0], iq = inv_norm[1];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      kv[m] *= ik;
+      qv[m] *= iq;
+    }
   }
 
   // p_j = sum_i h_ij k_i over this thread's rows, then over the 32 row groups

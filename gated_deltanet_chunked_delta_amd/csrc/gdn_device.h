@@ -232,6 +232,26 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Sum over each aligned group of N (8 or 16) consecutive lanes, in every lane
+// of the group.  Every lane of the wave must execute it.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(N == 8 || N == 16, "lane groups of 8 or 16");
+  x += quad_xor<1>(x);
+  x += quad_xor<2>(x);
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  if (N == 16)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// Input pre-processing (see PrepParams): 1 / sqrt(sum of squares + eps) for the
+// L2 normalisation of q and k, and the gate / beta activations with their
+// derivatives.
+constexpr float QK_NORM_EPS = 1e-6f;
+__device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log1pf(__expf(x)); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+
 // 4x4 transpose across each aligned quad of lanes: lane b of the quad holds
 // column b of a 4x4 block (v[i] = M[i][b]) and gets row b (v[j] = M[b][j]);
 // applied to rows it gives columns.  Two butterfly stages: 2x2 blocks are

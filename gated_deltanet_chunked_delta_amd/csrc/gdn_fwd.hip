@@ -73,7 +73,7 @@ struct alignas(16) FwdSmem {
 // the LDS store so that the next chunk's loads overlap the current chunk's
 // compute.  K and V move as 4-row x 16-byte blocks (K is stored row-major and
 // transposed, V transposed); Q as single 16-byte vectors (row-major).
-template <class E, int DK, int DV, int NT, bool NEED_Q, bool NEED_V>
+template <class E, int DK, int DV, int NT, bool NEED_Q, bool NEED_V, bool PREP>
 struct TileLoader {
   static constexpr int VEC = 16 / (int)sizeof(E);
   static constexpr int NBK = (CH / 4) * (DK / VEC);
@@ -83,8 +83,8 @@ struct TileLoader {
   typedef E vec_t __attribute__((__vector_size__(16)));
   vec_t blk[NB > 0 ? NB : 1][4];
   vec_t qv[NQV > 0 ? NQV : 1];
-  float gr;
-  E be;
+  float gr;  // raw values: converted where they are used, so that nothing waits
+  E be;      // for these loads while the next chunk's tiles are in flight
   int nrow;
 
   __device__ __forceinline__ void load(const FwdParams& p, int64_t tok0, int rows, int h) {
@@ -135,8 +135,51 @@ struct TileLoader {
       }
     }
   }
-  __device__ __forceinline__ float g_at(int l) const { return l < nrow ? gr : 0.f; }
-  __device__ __forceinline__ float beta_at(int l) const { return l < nrow ? to_f(be) : 0.f; }
+  // g and beta of row l of the chunk (zero past its end), after the optional
+  // gate / beta activation.
+  __device__ __forceinline__ void gb_at(int l, const PrepParams& pp, int h, float& g, float& b) const {
+    g = gr;
+    b = to_f(be);
+    if (PREP && pp.gate_act) {
+      g = -(pp.gate_scale ? pp.gate_scale[h] : 1.f) * softplus_f(g);
+      b = sigmoid_f(b);
+    }
+    if (l >= nrow) g = b = 0.f;
+  }
+
+  // Divide every row of K and Q by its L2 norm (q / k pre-processing).  A row's
+  // DK/VEC vectors sit on consecutive lanes, and K / V blocks never share a
+  // wave; every lane of the workgroup must call this.
+  __device__ __forceinline__ void normalize() {
+    constexpr int BPR = DK / VEC;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const bool isk = threadIdx.x + b * NT < NBK;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) ss += to_f(blk[b][j][e]) * to_f(blk[b][j][e]);
+        ss = lane_group_sum<BPR>(isk ? ss : 0.f);
+        const float sc = rsqrtf(ss + QK_NORM_EPS);
+        if (isk) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) blk[b][j][e] = to_e<E>(to_f(blk[b][j][e]) * sc);
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NQV; ++v) {
+      const bool valid = threadIdx.x + v * NT < CH * (DK / VEC);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) ss += to_f(qv[v][e]) * to_f(qv[v][e]);
+      ss = lane_group_sum<BPR>(valid ? ss : 0.f);
+      const float sc = rsqrtf(ss + QK_NORM_EPS);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) qv[v][e] = to_e<E>(to_f(qv[v][e]) * sc);
+    }
+  }
 
   template <class S>
   __device__ __forceinline__ void store(S& s) const {
@@ -186,13 +229,13 @@ struct TileLoader {
 template <int DV>
 struct FwdWaves { static constexpr int NW = DV == 128 ? 8 : 4; };
 
-template <class E, int DK, int DV, bool OUT, bool CORR>
+template <class E, int DK, int DV, bool OUT, bool CORR, bool PREP>
 struct Chunk {
   static constexpr int NW = FwdWaves<DV>::NW;
   static constexpr int NT = NW * 64;
   static constexpr int NTW = DV / (16 * NW);  // 16-column tiles of the state per wave
   using S = FwdSmem<E, DK, DV>;
-  using Loader = TileLoader<E, DK, DV, NT, OUT, !CORR>;
+  using Loader = TileLoader<E, DK, DV, NT, OUT, !CORR, PREP>;
 
   // One lower 16x16 tile (rt, ct) of A = strict_lower(diag(beta) (K K^T) * D)
   // (ISQ false; the diagonal tile also adds the log-bound terms) or of
@@ -235,9 +278,11 @@ struct Chunk {
 
     // ---- 1. tiles into LDS, scalars, prefetch of the next chunk
     S* sp = lds_opaque(&s0);
+    if (PREP && p.prep.qk_norm) ld.normalize();
     ld.store(*sp);
     if (w == 0) {
-      const float gr = ld.g_at(l), bt = ld.beta_at(l);
+      float gr, bt;
+      ld.gb_at(l, p.prep, h, gr, bt);
       const float gm = wave_incl_scan(gr);
       const float gC = __shfl(gm, 63, 64);
       const float Gm = __expf(gm);
@@ -559,7 +604,7 @@ __device__ void init_smem(FwdSmem<E, DK, DV>& s) {
 }
 
 // Phase 1: every segment from zero (segment 0 from h0).
-template <class E, int DK, int DV, bool OUT>
+template <class E, int DK, int DV, bool OUT, bool PREP>
 __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
@@ -569,7 +614,7 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p)
   f32x4 hacc[DK / 16][DV / (16 * FwdWaves<DV>::NW)];
   init_smem(s);
   load_state<E, DK, DV>(hacc, (sd.s == 0 && p.h0) ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-  const float lam = Chunk<E, DK, DV, OUT, false>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
+  const float lam = Chunk<E, DK, DV, OUT, false, PREP>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
                                                       sd.c_begin, sd.c_end, h, hacc, nullptr);
   if (nseg == 1) {
     if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
@@ -580,7 +625,7 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p)
 }
 
 // Phase 3: boundary corrections (or the serial fallback).
-template <class E, int DK, int DV, bool OUT>
+template <class E, int DK, int DV, bool OUT, bool PREP>
 __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p3(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
@@ -600,13 +645,13 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p3(FwdParams p)
   if (!ok) {
     // Gates do not decay fast enough to cut this sequence: one workgroup redoes it serially.
     load_state<E, DK, DV>(hacc, p.h0 ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-    Chunk<E, DK, DV, OUT, false>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc, nullptr);
+    Chunk<E, DK, DV, OUT, false, PREP>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc, nullptr);
     if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
     return;
   }
   load_state<E, DK, DV>(hacc, p.bstate + ((size_t)(blockIdx.x - 1) * p.H + h) * SS);
   int done = 0;
-  Chunk<E, DK, DV, OUT, true>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done);
+  Chunk<E, DK, DV, OUT, true, PREP>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done);
   if (sd.s == nseg - 1 && p.hT) {
     // hT = b_last + (the correction propagated through the whole last segment, if it got there)
     const float* b = p.bstate + ((size_t)blockIdx.x * p.H + h) * SS;
@@ -618,12 +663,23 @@ template <class E, int DK, int DV>
 hipError_t launch_fwd_t(const FwdParams& p, int nseg_total, hipStream_t st) {
   dim3 grid(nseg_total, p.H), block(64 * FwdWaves<DV>::NW);
   const bool out = p.o != nullptr;
+  const bool prep = p.prep.qk_norm || p.prep.gate_act;
   if (p.phase == 1) {
-    if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false>), grid, block, 0, st, p);
+    if (prep) {
+      if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true>), grid, block, 0, st, p);
+    } else {
+      if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false>), grid, block, 0, st, p);
+    }
   } else {
-    if (out) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, false>), grid, block, 0, st, p);
+    if (prep) {
+      if (out) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, false, true>), grid, block, 0, st, p);
+    } else {
+      if (out) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, false>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, false, false>), grid, block, 0, st, p);
+    }
   }
   return hipGetLastError();
 }

@@ -8,6 +8,15 @@
 namespace gdn {
 
 // Forward chunk loop (also the backward's forward-state replay).
+// Optional input pre-processing applied inside the kernels: q and k divided by
+// their L2 norm over the head dimension (qk_norm), and gate / beta given as
+// logits (gate_act): g = -gate_scale[h] softplus(a), beta = sigmoid(b).
+struct PrepParams {
+  int qk_norm;
+  int gate_act;
+  const float* gate_scale;  // nullable [H]: 1
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -27,6 +36,7 @@ struct FwdParams {
   float* lam;              // [total segments][H] segment log-bounds
   void* hs;                // nullable: [total chunks][H][DV][DK] chunk start states S (dtype)
   int phase;               // 1 = segments from zero / h0, 3 = boundary corrections
+  PrepParams prep;
 };
 
 // Reverse state-gradient chain of the backward.
@@ -48,6 +58,7 @@ struct RevParams {
   float* lam;              // [total segments][H]
   void* dhs;               // [total chunks][H][DV][DK] gradient at each chunk END, transposed (dtype)
   int phase;
+  PrepParams prep;
 };
 
 // Chunk-parallel gradients of the backward.
@@ -69,6 +80,7 @@ struct GradParams {
   int H;
   SeqInfo seq;
   const int2* chunk_tab;   // [total chunks] (sequence, chunk index within it)
+  PrepParams prep;
 };
 
 // One recurrent decode step: N sequences x H heads, one token each.
@@ -84,6 +96,7 @@ struct DecodeParams {
   void* o;                    // [N, H, DV]
   float scale;
   int N, H;
+  PrepParams prep;
 };
 
 hipError_t launch_plan(SeqInfo seq, int N, int segc, int* chunk_first, int* seg_first, SegDesc* segs,

@@ -3,6 +3,7 @@
 // their stores into LDS, and coalesced tile writes.
 #pragma once
 #include "gdn_device.h"
+#include "gdn_internal.h"
 
 namespace gdn {
 
@@ -166,6 +167,29 @@ struct TilePart {
       }
     }
   }
+  // Divide every row by its L2 norm (q / k pre-processing).  A row's D/VEC
+  // blocks sit on consecutive lanes; every lane of the wave must call this.
+  __device__ __forceinline__ void normalize_rows(int tid = threadIdx.x) {
+    if constexpr (NB > 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const bool valid = NB * NT == NBLK || tid + b * NT < NBLK;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float x = to_f(blk[b][j][e]);
+            ss += x * x;
+          }
+          ss = lane_group_sum<BPR>(valid ? ss : 0.f);
+          const float sc = rsqrtf(ss + QK_NORM_EPS);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) blk[b][j][e] = to_e<E>(to_f(blk[b][j][e]) * sc);
+        }
+      }
+    }
+  }
   __device__ __forceinline__ void store(E* dst, int ld, E* dstT, int ldT, int tid = threadIdx.x) const {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -213,8 +237,8 @@ __device__ __forceinline__ void st_tile_rows(E* base, int ld, int r0, int c0, co
 // g / beta of one chunk for threads 0..63 (one row each), masked at use.
 template <class E>
 struct ScalarPart {
-  float gr;
-  E be;
+  float gr;  // raw values: converted where they are used, so that nothing waits
+  E be;      // for these loads while the next chunk's tiles are in flight
   int nrow;
   __device__ __forceinline__ void load(const float* g, const E* beta, int64_t tok0, int H, int h, int rows) {
     if (threadIdx.x < 64) {
@@ -224,8 +248,51 @@ struct ScalarPart {
       nrow = rows;
     }
   }
-  __device__ __forceinline__ float g_at(int l) const { return l < nrow ? gr : 0.f; }
-  __device__ __forceinline__ float beta_at(int l) const { return l < nrow ? to_f(be) : 0.f; }
+  // g and beta of row l (zero past the chunk end), after the optional activation.
+  template <bool PREP>
+  __device__ __forceinline__ void gb_at(int l, const PrepParams& pp, int h, float& g, float& b) const {
+    g = gr;
+    b = to_f(be);
+    if (PREP && pp.gate_act) {
+      g = -(pp.gate_scale ? pp.gate_scale[h] : 1.f) * softplus_f(g);
+      b = sigmoid_f(b);
+    }
+    if (l >= nrow) g = b = 0.f;
+  }
 };
+
+// Gradient of a row-normalised input: rows of `grad` (LDS, row stride ld) are
+// the gradient with respect to x / sqrt(|x|^2 + eps); `raw` (global, row stride
+// gld) holds x.  Writes dx = (grad - x (x.grad) / n^2) / n, n^2 = |x|^2 + eps,
+// for rows [0, rows) to dst (global) in 16-byte pieces.
+template <class E, int D, int NT>
+__device__ __forceinline__ void store_tile_unnorm(const E* grad, int ld, const E* raw, int64_t gld, E* dst,
+                                                  int64_t dgld, int rows) {
+  constexpr int VEC = 16 / (int)sizeof(E), BPR = D / VEC;
+  typedef E vec_t __attribute__((__vector_size__(16)));
+  static_assert((CH * BPR) % NT == 0 || NT % (CH * BPR) == 0, "whole lane groups per pass");
+  for (int e = threadIdx.x; e < CH * BPR; e += NT) {
+    const int r = e / BPR, c0 = (e % BPR) * VEC;
+    const bool valid = r < rows;
+    vec_t x = vec_t{}, d = vec_t{};
+    if (valid) {
+      x = *reinterpret_cast<const vec_t*>(raw + (int64_t)r * gld + c0);
+      d = *reinterpret_cast<const vec_t*>(grad + r * ld + c0);
+    }
+    float ss = 0.f, dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      ss += to_f(x[i]) * to_f(x[i]);
+      dot += to_f(x[i]) * to_f(d[i]);
+    }
+    ss = lane_group_sum<BPR>(ss) + QK_NORM_EPS;
+    dot = lane_group_sum<BPR>(dot);
+    const float inv = rsqrtf(ss), proj = dot / ss;
+    vec_t out;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) out[i] = to_e<E>((to_f(d[i]) - to_f(x[i]) * proj) * inv);
+    if (valid) *reinterpret_cast<vec_t*>(dst + (int64_t)r * dgld + c0) = out;
+  }
+}
 
 }  // namespace gdn

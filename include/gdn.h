@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
   GDN_OK = 0,
@@ -90,6 +90,16 @@ typedef struct {
                                   k > 0 = segments of k chunks (64 tokens each) */
   void* workspace;             /* device scratch of at least workspace_bytes */
   size_t workspace_bytes;
+  /* Optional input pre-processing inside the kernels (0 = off):
+   *   qk_norm:  q and k are raw; each (token, head) vector is divided by
+   *             sqrt(|x|^2 + 1e-6) before use;
+   *   gate_act: g and beta hold logits a, b; the kernels use
+   *             g = -gate_scale[h] * softplus(a) and beta = sigmoid(b).
+   * The backward then returns dq, dk, dg, dbeta with respect to these raw
+   * inputs.  Outputs o, hT and the states are unchanged in meaning. */
+  int32_t qk_norm;
+  int32_t gate_act;
+  const float* gate_scale;     /* nullable [H] fp32 (1 when NULL); only with gate_act */
 } gdn_common_args;
 
 typedef struct {
@@ -173,6 +183,9 @@ typedef struct {
   const int32_t* state_idx;
   int32_t num_slots;
   void* o;
+  int32_t qk_norm;             /* as in gdn_common_args */
+  int32_t gate_act;
+  const float* gate_scale;
 } gdn_decode_args;
 
 gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream);

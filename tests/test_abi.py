@@ -18,7 +18,7 @@ def test_exports_every_declared_symbol(L):
             "gdn_chunk_bwd_workspace_size", "gdn_last_error", "gdn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdn_abi_version() == 3
+    assert L.gdn_abi_version() == 4
 
 
 FAKE = 1 << 20  # a 16-byte aligned fake device address; never dereferenced
