@@ -740,41 +740,54 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int dt = 0; dt < CTK; ++dt) qr[kb][dt] = ld_fragC_q<E>(slotE(SQ), LK, 32 * kb, d0 + 16 * dt);
+  // (the state operands come from memory on both sides of these products, so
+  //  they use the contiguous k-slot order: one 16-byte LDS read per fragment,
+  //  each loaded once and used for both key-column tiles)
   f32x4 gw[2][CTK], dq1[2][CTK], udh[2][CTK];
+  Frag<E> hn[CTK][DV / 32], dhn[CTK][DV / 32];
 #pragma unroll
-  for (int dt = 0; dt < CTK; ++dt) {
-    Frag<E> hn[DV / 32], dhn[DV / 32];
+  for (int dt = 0; dt < CTK; ++dt)
 #pragma unroll
     for (int kb = 0; kb < DV / 32; ++kb) {
-      hn[kb] = ld_fragC_q<E>(hs, DK, 32 * kb, d0 + 16 * dt);
-      dhn[kb] = ld_fragC_q<E>(dhs, DK, 32 * kb, d0 + 16 * dt);
+      hn[dt][kb] = ld_fragC_q8<E>(hs, DK, 32 * kb, d0 + 16 * dt);
+      dhn[dt][kb] = ld_fragC_q8<E>(dhs, DK, 32 * kb, d0 + 16 * dt);
       if (rh == 0) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) hdh += frag_at(hn[kb], jj) * frag_at(dhn[kb], jj);
+        for (int jj = 0; jj < 8; ++jj) hdh += frag_at(hn[dt][kb], jj) * frag_at(dhn[dt][kb], jj);
       }
     }
-    const Frag<E> qown = rh ? qr[1][dt] : qr[0][dt];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int rt = 2 * rh + j;
-      f32x4 a = zero4(), b = zero4(), c = zero4();
+  for (int j = 0; j < 2; ++j) {
+    const int rt = 2 * rh + j;
+    f32x4 a[CTK], b[CTK], c[CTK];
 #pragma unroll
-      for (int kb = 0; kb < DV / 32; ++kb) {
-        mma(a, ld_frag(sDU, LV, 16 * rt + c16, 32 * kb), hn[kb]);
-        mma(b, ld_frag(slotE(SDO), LV, 16 * rt + c16, 32 * kb), hn[kb]);
-        mma(c, ld_frag(slotE(SV), LV, 16 * rt + c16, 32 * kb), dhn[kb]);
+    for (int dt = 0; dt < CTK; ++dt) a[dt] = b[dt] = c[dt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < DV / 32; ++kb) {
+      const Frag<E> xdu = ld_frag8(sDU, LV, 16 * rt + c16, 32 * kb);
+      const Frag<E> xdo = ld_frag8(slotE(SDO), LV, 16 * rt + c16, 32 * kb);
+      const Frag<E> xu = ld_frag8(slotE(SV), LV, 16 * rt + c16, 32 * kb);
+#pragma unroll
+      for (int dt = 0; dt < CTK; ++dt) {
+        mma(a[dt], xdu, hn[dt][kb]);
+        mma(b[dt], xdo, hn[dt][kb]);
+        mma(c[dt], xu, dhn[dt][kb]);
       }
-      gw[j][dt] = zero4() - a;
-      dq1[j][dt] = b;
-      udh[j][dt] = c;
+    }
+#pragma unroll
+    for (int dt = 0; dt < CTK; ++dt) {
+      const Frag<E> qown = rh ? qr[1][dt] : qr[0][dt];
+      gw[j][dt] = zero4() - a[dt];
+      dq1[j][dt] = b[dt];
+      udh[j][dt] = c[dt];
       const int dcol = d0 + 16 * dt + c16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
         const float qv = frag_at(qown, 4 * j + i);
         const float kv = to_f(sK[r * LK + dcol]);
-        rg[j][i] += scale * s.Gam[r] * qv * b[i] - s.ek[r] * kv * c[i];
-        lastsum += s.ek[r] * kv * c[i];
+        rg[j][i] += scale * s.Gam[r] * qv * b[dt][i] - s.ek[r] * kv * c[dt][i];
+        lastsum += s.ek[r] * kv * c[dt][i];
       }
     }
   }
@@ -928,17 +941,41 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   {
     const float* sGT = slotF(SV);
+    // both products are fp32 x fp32: true fp32 products for fp32 inputs, the
+    // three-term bf16 split for bf16 inputs
+    constexpr bool SPLIT = std::is_same<E, bf16>::value;
     f32x4 z[4];
+    if constexpr (SPLIT) {
+      Frag<bf16> th[2], tl[2];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      z[rt] = zero4();
+      for (int kb = 0; kb < 2; ++kb) split_frag(ld_frag(sT, LA, 16 * cw + c16, 32 * kb), th[kb], tl[kb]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        mma(z[rt], ld_frag(sGT, LA, 16 * rt + c16, 32 * kb), ld_frag(sT, LA, 16 * cw + c16, 32 * kb));
+      for (int rt = 0; rt < 4; ++rt) {
+        z[rt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          Frag<bf16> xh, xl;
+          split_frag(ld_frag(sGT, LA, 16 * rt + c16, 32 * kb), xh, xl);
+          mma3(z[rt], xh, xl, th[kb], tl[kb]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        z[rt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          mma(z[rt], ld_frag(sGT, LA, 16 * rt + c16, 32 * kb), ld_frag(sT, LA, 16 * cw + c16, 32 * kb));
+      }
     }
     Frag<float> zf[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) pack_frag(zf[kb], z[2 * kb], z[2 * kb + 1]);
+    Frag<bf16> zh[2], zl[2];
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) split_frag(zf[kb], zh[kb], zl[kb]);
+    }
     const int c = 16 * cw + c16;
     float csum = 0.f;
     f32x4 ga[2];
@@ -947,7 +984,16 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       const int rt = 2 * rh + j;
       f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mma(acc, ld_fragT<float>(sT, LA, 16 * rt + c16, 32 * kb, -1.f), zf[kb]);
+      for (int kb = 0; kb < 2; ++kb) {
+        const Frag<float> tt = ld_fragT<float>(sT, LA, 16 * rt + c16, 32 * kb, -1.f);
+        if constexpr (SPLIT) {
+          Frag<bf16> xh, xl;
+          split_frag(tt, xh, xl);
+          mma3(acc, xh, xl, zh[kb], zl[kb]);
+        } else {
+          mma(acc, tt, zf[kb]);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;

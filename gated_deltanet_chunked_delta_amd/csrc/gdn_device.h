@@ -332,6 +332,35 @@ __device__ __forceinline__ Frag<float> ld_fragC_q<float>(const float* base, int 
   return f;
 }
 
+// ld_fragC_q in the contiguous k-slot order (slots k0+8g .. k0+8g+7), to pair
+// with ld_frag8.
+template <class E>
+__device__ __forceinline__ Frag<E> ld_fragC_q8(const E* base, int ld, int k0, int col0);
+template <>
+__device__ __forceinline__ Frag<bf16> ld_fragC_q8<bf16>(const bf16* base, int ld, int k0, int col0) {
+  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+  const bf16* p = base + (k0 + 8 * g + b) * ld + col0 + 4 * q;
+  typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+  typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+  u32x2 x = *reinterpret_cast<const u32x2*>(p);
+  u32x2 y = *reinterpret_cast<const u32x2*>(p + 4 * ld);
+  uint32_t x0 = x[0], x1 = x[1], y0 = y[0], y1 = y[1];
+  quad_transpose16(x0, x1);
+  quad_transpose16(y0, y1);
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, u32x4{x0, x1, y0, y1});
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> ld_fragC_q8<float>(const float* base, int ld, int k0, int col0) {
+  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+  const float* p = base + (k0 + 8 * g + b) * ld + col0 + 4 * q;
+  Frag<float> f;
+  f.lo = quad_transpose(*reinterpret_cast<const f32x4*>(p));
+  f.hi = quad_transpose(*reinterpret_cast<const f32x4*>(p + 4 * ld));
+  return f;
+}
+
 // Four fp32 values of a C-layout column piece -> E, quad-transposed into a row
 // piece and stored (4 consecutive columns of row `row`).
 template <class E>
@@ -364,6 +393,27 @@ __device__ __forceinline__ Frag<E> ld_frag_kscaled(const E* base, int ld, int ro
   Frag<E> f;
   pack_frag(f, a, b);
   return f;
+}
+
+// fp32 operands on bf16 matrix cores: x = hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi), and X Y ~ Xhi Yhi + Xhi Ylo + Xlo Yhi (the dropped
+// Xlo Ylo term and the rounding of lo leave about 16 significant bits, three
+// bf16 products in place of eight fp32 16x16x4 ones per 32-deep block).
+__device__ __forceinline__ void split_frag(const Frag<float>& f, Frag<bf16>& hi, Frag<bf16>& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16 a = (bf16)f.lo[i], b = (bf16)f.hi[i];
+    hi.v[i] = a;
+    hi.v[4 + i] = b;
+    lo.v[i] = (bf16)(f.lo[i] - (float)a);
+    lo.v[4 + i] = (bf16)(f.hi[i] - (float)b);
+  }
+}
+__device__ __forceinline__ void mma3(f32x4& acc, const Frag<bf16>& xh, const Frag<bf16>& xl, const Frag<bf16>& yh,
+                                     const Frag<bf16>& yl) {
+  mma(acc, xl, yh);
+  mma(acc, xh, yl);
+  mma(acc, xh, yh);
 }
 
 // Value of k-slot j of a fragment, as fp32.
