@@ -133,12 +133,12 @@ struct RevChunk {
 
     // ---- 1. gradient at the chunk end out; tiles into LDS; scalars
     S* sp = lds_opaque(&s0);
-    // stored transposed, [DV][DK]: the lane's four rows of one column are contiguous
+    // stored as S (Dv x Dk) in 4 x 16 blocks: the lane's four rows of one column are contiguous
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
-        E* dst = dhs_chunk + (n0 + 16 * nt + c16) * DK + 16 * t + 4 * g;
+        E* dst = dhs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK);
         f32x4 val = dh[t][nt];
         if (CORR) val = val + ld4f<E>(dst);
         st4f<E>(dst, val);
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   const int64_t tok0 = p.seq.start(n) + (int64_t)jc * CH;
   const int rows = min(CH, len - jc * CH);
   const size_t SS = (size_t)DK * DV;
-  // h_c and dh'_c of this chunk, both stored transposed ([DV][DK] row-major)
+  // h_c and dh'_c of this chunk, both stored as S-shaped (Dv x Dk) matrices in 4 x 16 blocks (st_blk)
   const E* hs = static_cast<const E*>(p.hs) + ((size_t)blockIdx.x * H + h) * SS;
   const E* dhs = static_cast<const E*>(p.dhs) + ((size_t)blockIdx.x * H + h) * SS;
   const int d0 = cw * (DK / 4), n0 = cw * (DV / 4);
@@ -582,8 +582,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     for (int nt = 0; nt < CTV; ++nt)
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb) {
-        hk[nt][kb] = ld_frag8(hs, DK, n0 + 16 * nt + c16, 32 * kb);
-        dk_[nt][kb] = ld_frag8(dhs, DK, n0 + 16 * nt + c16, 32 * kb);
+        hk[nt][kb] = ld_frag8_st(hs, DK, n0 + 16 * nt + c16, 32 * kb);
+        dk_[nt][kb] = ld_frag8_st(dhs, DK, n0 + 16 * nt + c16, 32 * kb);
       }
     for (int e = 4 * tid; e < CH * CH; e += 4 * NT) {
       *reinterpret_cast<f32x4*>(&sT[(e >> 6) * LA + (e & 63)]) = zero4();
@@ -749,8 +749,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   for (int dt = 0; dt < CTK; ++dt)
 #pragma unroll
     for (int kb = 0; kb < DV / 32; ++kb) {
-      hn[dt][kb] = ld_fragC_q8<E>(hs, DK, 32 * kb, d0 + 16 * dt);
-      dhn[dt][kb] = ld_fragC_q8<E>(dhs, DK, 32 * kb, d0 + 16 * dt);
+      hn[dt][kb] = ld_fragC_q8_st<E>(hs, DK, 32 * kb, d0 + 16 * dt);
+      dhn[dt][kb] = ld_fragC_q8_st<E>(dhs, DK, 32 * kb, d0 + 16 * dt);
       if (rh == 0) {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) hdh += frag_at(hn[dt][kb], jj) * frag_at(dhn[dt][kb], jj);

@@ -332,18 +332,48 @@ __device__ __forceinline__ Frag<float> ld_fragC_q<float>(const float* base, int 
   return f;
 }
 
-// ld_fragC_q in the contiguous k-slot order (slots k0+8g .. k0+8g+7), to pair
-// with ld_frag8.
+// Element offset of S[v][k] inside one stored chunk state (v < Dv value row,
+// k < Dk key column).  The Dv x Dk matrix is kept as 4 x 16 blocks, each
+// row-major and contiguous (64 elements: one 128-byte line for bf16), blocks in
+// row-major order.  Four consecutive keys of one row, eight consecutive keys of
+// one row, and four consecutive rows of a 16-key column block all fall into
+// whole lines, so the state can be read down its rows and across them (after
+// a quad transpose) with every fetched line fully used.
+__host__ __device__ constexpr int64_t st_blk(int v, int k, int DK) {
+  return ((int64_t)(v >> 2) * (DK >> 4) + (k >> 4)) * 64 + ((v & 3) << 4) + (k & 15);
+}
+
+// ld_frag8 from a blocked chunk state: row v, keys k0 + 8g .. k0 + 8g + 7
+// (k0 a multiple of 16).
+__device__ __forceinline__ Frag<bf16> ld_frag8_st(const bf16* base, int DK, int v, int k0) {
+  const int g = lane_id() >> 4;
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(base + st_blk(v, k0 + 8 * g, DK));
+  return f;
+}
+__device__ __forceinline__ Frag<float> ld_frag8_st(const float* base, int DK, int v, int k0) {
+  const int g = lane_id() >> 4;
+  const float* p = base + st_blk(v, k0 + 8 * g, DK);
+  Frag<float> f;
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f;
+}
+
+// ld_fragC_q in the contiguous k-slot order (pairs with ld_frag8), from a
+// blocked chunk state: k-slots walk down key column
+// col0 + lane%16 (col0 a multiple of 16) over value rows k0 + 8g .. k0 + 8g + 7
+// (k0 a multiple of 8); each 4-row piece is one block row of 16 keys.
 template <class E>
-__device__ __forceinline__ Frag<E> ld_fragC_q8(const E* base, int ld, int k0, int col0);
+__device__ __forceinline__ Frag<E> ld_fragC_q8_st(const E* base, int DK, int k0, int col0);
 template <>
-__device__ __forceinline__ Frag<bf16> ld_fragC_q8<bf16>(const bf16* base, int ld, int k0, int col0) {
+__device__ __forceinline__ Frag<bf16> ld_fragC_q8_st<bf16>(const bf16* base, int DK, int k0, int col0) {
   const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
-  const bf16* p = base + (k0 + 8 * g + b) * ld + col0 + 4 * q;
+  const bf16* p = base + st_blk(k0 + 8 * g + b, col0 + 4 * q, DK);
   typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
   typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
   u32x2 x = *reinterpret_cast<const u32x2*>(p);
-  u32x2 y = *reinterpret_cast<const u32x2*>(p + 4 * ld);
+  u32x2 y = *reinterpret_cast<const u32x2*>(p + DK * 4);  // four rows down: the next block row
   uint32_t x0 = x[0], x1 = x[1], y0 = y[0], y1 = y[1];
   quad_transpose16(x0, x1);
   quad_transpose16(y0, y1);
@@ -352,12 +382,12 @@ __device__ __forceinline__ Frag<bf16> ld_fragC_q8<bf16>(const bf16* base, int ld
   return f;
 }
 template <>
-__device__ __forceinline__ Frag<float> ld_fragC_q8<float>(const float* base, int ld, int k0, int col0) {
+__device__ __forceinline__ Frag<float> ld_fragC_q8_st<float>(const float* base, int DK, int k0, int col0) {
   const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
-  const float* p = base + (k0 + 8 * g + b) * ld + col0 + 4 * q;
+  const float* p = base + st_blk(k0 + 8 * g + b, col0 + 4 * q, DK);
   Frag<float> f;
   f.lo = quad_transpose(*reinterpret_cast<const f32x4*>(p));
-  f.hi = quad_transpose(*reinterpret_cast<const f32x4*>(p + 4 * ld));
+  f.hi = quad_transpose(*reinterpret_cast<const f32x4*>(p + DK * 4));
   return f;
 }
 

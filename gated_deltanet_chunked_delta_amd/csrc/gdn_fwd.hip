@@ -296,12 +296,12 @@ struct Chunk {
       if (l == 0) sp->GamC = __expf(gC);
     }
     if (hs_chunk) {
-      // stored transposed, [DV][DK]: the lane's four rows of one column are contiguous
+      // stored as S (Dv x Dk) in 4 x 16 blocks: the lane's four rows of one column are contiguous
 #pragma unroll
       for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
-          E* dst = hs_chunk + (n0 + 16 * nt + c16) * DK + 16 * t + 4 * g;
+          E* dst = hs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK);
           f32x4 val = hacc[t][nt];
           if (CORR) val = val + ld4f<E>(dst);
           st4f<E>(dst, val);

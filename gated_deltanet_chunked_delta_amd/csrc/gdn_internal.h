@@ -34,7 +34,7 @@ struct FwdParams {
   const int* chunk_first;  // [N+1]
   float* bstate;           // [total segments][H][DK][DV] segment end states
   float* lam;              // [total segments][H] segment log-bounds
-  void* hs;                // nullable: [total chunks][H][DV][DK] chunk start states S (dtype)
+  void* hs;                // nullable: [total chunks][H] chunk start states S, Dv x Dk in st_blk order (dtype)
   int phase;               // 1 = segments from zero / h0, 3 = boundary corrections
   PrepParams prep;
 };
@@ -56,7 +56,7 @@ struct RevParams {
   const int* chunk_first;
   float* bstate;           // [total segments][H][DK][DV] segment start gradients
   float* lam;              // [total segments][H]
-  void* dhs;               // [total chunks][H][DV][DK] gradient at each chunk END, transposed (dtype)
+  void* dhs;               // [total chunks][H] gradient at each chunk END, S-shaped, st_blk order (dtype)
   int phase;
   PrepParams prep;
 };

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum {
   GDN_OK = 0,
@@ -135,11 +135,14 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args);
 
 /* Bytes of the saved chunk states (h_save / h_saved) for these arguments:
  * C * H * Dk * Dv elements of the input dtype, C = sum over sequences of
- * ceil(len / 64).  Element [c][h][j][i] is h[i][j] (= S[j][i]) at the start of
- * chunk c (chunks numbered sequence after sequence), i.e. each state is stored
- * as S, Dv x Dk row-major, rounded to the dtype.  Returns 0 and sets the error
- * string for invalid arguments (and returns 0 without error when there are no
- * tokens). */
+ * ceil(len / 64).  State (c, h) is S (= h^T, Dv x Dk) at the start of chunk c
+ * (chunks numbered sequence after sequence), rounded to the dtype, stored at
+ * element offset (c * H + h) * Dk * Dv in 4 x 16 blocks: S[j][i] sits at
+ *     ((j / 4) * (Dk / 16) + i / 16) * 64 + (j % 4) * 16 + i % 16
+ * (each block row-major and contiguous, blocks in row-major order), so that
+ * the state can be read both along and across its rows in whole cache lines.
+ * Returns 0 and sets the error string for invalid arguments (and returns 0
+ * without error when there are no tokens). */
 size_t gdn_chunk_states_bytes(const gdn_common_args* a);
 
 /* Forward: o and (optionally) hT and the chunk states.  stream is a

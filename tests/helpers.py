@@ -29,3 +29,13 @@ def to_torch(x, dev):
 
 def to_np(t):
     return None if t is None else t.float().cpu().numpy()
+
+
+def unblock_states(flat, C, H, Dk, Dv):
+    """Chunk states as saved by gdn_chunk_fwd (flat, C * H * Dk * Dv elements; each
+    state S = h^T, Dv x Dk, in 4 x 16 blocks as include/gdn.h states) -> numpy
+    [C, H, Dk, Dv] holding h."""
+    a = np.asarray(flat, dtype=np.float64)[:C * H * Dk * Dv]
+    # [C, H, Dv/4, Dk/16, 4, 16] -> S[c, h, j, i] with j = 4 jb + jr, i = 16 ib + ir
+    S = a.reshape(C, H, Dv // 4, Dk // 16, 4, 16).transpose(0, 1, 2, 4, 3, 5).reshape(C, H, Dv, Dk)
+    return S.transpose(0, 1, 3, 2)

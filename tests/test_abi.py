@@ -2,6 +2,7 @@
 header declares, and rejects bad arguments before touching the device."""
 import ctypes
 
+import numpy as np
 import pytest
 
 from gated_deltanet_chunked_delta_amd import binding as B
@@ -18,7 +19,7 @@ def test_exports_every_declared_symbol(L):
             "gdn_chunk_bwd_workspace_size", "gdn_last_error", "gdn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdn_abi_version() == 4
+    assert L.gdn_abi_version() == 5
 
 
 FAKE = 1 << 20  # a 16-byte aligned fake device address; never dereferenced
@@ -147,3 +148,17 @@ def test_decode_rejects_bad_arguments(L, field, value, status):
 def test_decode_empty_batch_is_a_no_op(L):
     a = dec_args(N=0, q=None, k=None, v=None, state=None, o=None)
     assert L.gdn_decode_step(ctypes.byref(a), None) == 0
+
+
+def test_state_block_layout_is_a_permutation():
+    """The saved-state block order (include/gdn.h) maps every (j, i) of a Dv x Dk
+    state to its own offset below Dk * Dv, and unblock_states inverts it."""
+    from tests.helpers import unblock_states
+    for Dk, Dv in ((128, 128), (64, 128), (128, 64), (64, 64)):
+        j, i = np.meshgrid(np.arange(Dv), np.arange(Dk), indexing="ij")
+        off = ((j // 4) * (Dk // 16) + i // 16) * 64 + (j % 4) * 16 + i % 16
+        assert np.array_equal(np.sort(off.ravel()), np.arange(Dk * Dv))
+        S = np.random.default_rng(Dk + Dv).standard_normal((Dv, Dk))
+        flat = np.empty(Dk * Dv)
+        flat[off] = S
+        assert np.array_equal(unblock_states(flat, 1, 1, Dk, Dv)[0, 0], S.T)

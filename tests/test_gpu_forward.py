@@ -120,3 +120,38 @@ def test_deterministic(dev):
 def test_config_forward(dev, name):
     x = gdn_inputs.config(name, grad=False)
     check_fwd(x, dev, 0, name)
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv,cp", [("bf16", 128, 128, 0), ("bf16", 64, 128, 2), ("bf16", 128, 64, -1),
+                                           ("f32", 64, 64, 3)])
+def test_saved_states_are_chunk_start_states(dev, dtype, Dk, Dv, cp):
+    """Every saved state equals the oracle's state after the first 64 c tokens of
+    its sequence (the initial state for c = 0), read back through the documented
+    block layout."""
+    import torch
+    from gated_deltanet_chunked_delta_amd import gdn_chunk_fwd
+    from tests.helpers import unblock_states
+    lens = [130, 0, 64, 257, 5]
+    cu = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    x = gdn_inputs.generate(B=1, T=int(cu[-1]), H=2, Dk=Dk, Dv=Dv, dtype=dtype, seed=41 + Dk + Dv)
+    x.cu_seqlens = cu
+    x.h0 = (0.3 * np.random.default_rng(4).standard_normal((len(lens), 2, Dk, Dv))).astype(np.float32)
+    print(f"[fwd] saved states {dtype} Dk={Dk} Dv={Dv} cp={cp}", flush=True)
+    t = to_torch(x, dev)
+    _, _, states = gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, h0=t["h0"],
+                                 cu_seqlens=t["cu"], cu_seqlens_host=cu, cp_mode=cp, save_states=True)
+    torch.cuda.synchronize()
+    C = sum((n + 63) // 64 for n in lens)
+    got = unblock_states(to_np(states), C, 2, Dk, Dv)
+    c = 0
+    for n, ln in enumerate(lens):
+        s0 = int(cu[n])
+        for j in range((ln + 63) // 64):
+            sl = slice(s0, s0 + 64 * j)
+            want = x.h0[n] if j == 0 else ref.fwd(x.q[:, sl], x.k[:, sl], x.v[:, sl], x.g[:, sl], x.beta[:, sl],
+                                                  x.scale, x.h0[n:n + 1])[1][0]
+            err = relerr(got[c], want)
+            assert err <= TOL[dtype], (n, j, err)
+            c += 1
+    assert c == C
