@@ -558,9 +558,9 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 
   // ---- P1: staging (all four tiles in flight at once; rows past the end are
   //          zero); zero T, P and the cross-wave sum arrays.  h and dh' down this
-  //          wave's value columns (the operands of P5) are requested right
-  //          after the tiles and stay in flight until P5; their products use the
-  //          contiguous k-slot order (one 16-byte read per fragment).
+  //          wave's value columns (the operands of P5) are requested after the
+  //          tiles have landed and stay in flight until P5; their products use
+  //          the contiguous k-slot order (one 16-byte read per fragment).
   Frag<E> hk[CTV][DK / 32], dk_[CTV][DK / 32];
   {
     const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
@@ -578,13 +578,6 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       tv.template load<true>(v, (int64_t)H * DV, rows, ht);
       td.template load<true>(d, (int64_t)H * DV, rows, ht);
     }
-#pragma unroll
-    for (int nt = 0; nt < CTV; ++nt)
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) {
-        hk[nt][kb] = ld_frag8_st(hs, DK, n0 + 16 * nt + c16, 32 * kb);
-        dk_[nt][kb] = ld_frag8_st(dhs, DK, n0 + 16 * nt + c16, 32 * kb);
-      }
     for (int e = 4 * tid; e < CH * CH; e += 4 * NT) {
       *reinterpret_cast<f32x4*>(&sT[(e >> 6) * LA + (e & 63)]) = zero4();
       *reinterpret_cast<f32x4*>(&sP[(e >> 6) * LA + (e & 63)]) = zero4();
@@ -625,6 +618,16 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     }
   }
   __syncthreads();
+  // h and dh' down this wave's value columns (the operands of P5), requested
+  // only now: every workgroup stages its tiles at about the same time, and the
+  // tiles arrive sooner without the states queued beside them
+#pragma unroll
+  for (int nt = 0; nt < CTV; ++nt)
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      hk[nt][kb] = ld_frag8_st(hs, DK, n0 + 16 * nt + c16, 32 * kb);
+      dk_[nt][kb] = ld_frag8_st(dhs, DK, n0 + 16 * nt + c16, 32 * kb);
+    }
 
   // ---- P2: KD = strict_lower(K K^T * D), P = (Q K^T) * M  (20 lower tiles)
   for (int ti = w; ti < 20; ti += 8) {
