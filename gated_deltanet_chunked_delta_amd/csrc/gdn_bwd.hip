@@ -754,10 +754,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     for (int kb = 0; kb < DV / 32; ++kb) {
       hn[dt][kb] = ld_fragC_q8_st<E>(hs, DK, 32 * kb, d0 + 16 * dt);
       dhn[dt][kb] = ld_fragC_q8_st<E>(dhs, DK, 32 * kb, d0 + 16 * dt);
-      if (rh == 0) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) hdh += frag_at(hn[dt][kb], jj) * frag_at(dhn[dt][kb], jj);
-      }
+      // <h, dh'> over the whole state: the two row halves share each column group's part
+      if ((kb & 1) == rh) hdh = frag_dot(hn[dt][kb], dhn[dt][kb], hdh);
     }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -919,11 +917,22 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   __syncthreads();
 
-  // ---- P10: Z = GT T^T (column tile cw, all rows), GA = strict_lower(-T^T Z) (own
-  //           rows); E -> S = E + E^T (slot KD)
+  // ---- P10: Z = GT T^T (own row tiles, column tile cw) -> slot P (last read in
+  //           P8), GA = strict_lower(-T^T Z) (own rows); E -> S = E + E^T (slot KD)
   // XU = T^T dU (own rows and value columns) -> dV into slot Q (GW was last read in P9)
+  // The rows of T^T for this wave's row tiles serve XU (in E) and GA (in fp32).
+  Frag<float> ttf[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) ttf[j][kb] = ld_fragT<float>(sT, LA, 16 * (2 * rh + j) + c16, 32 * kb, 1.f);
   {
     E* sDV = slotE(SQ);
+    Frag<E> tte[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) pack_frag(tte[j][kb], ttf[j][kb].lo, ttf[j][kb].hi);
 #pragma unroll
     for (int nt = 0; nt < CTV; ++nt) {
       Frag<E> duf[2];
@@ -934,7 +943,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         const int rt = 2 * rh + j;
         f32x4 xu = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(xu, ld_fragT<E>(sT, LA, 16 * rt + c16, 32 * kb, 1.f), duf[kb]);
+        for (int kb = 0; kb < 2; ++kb) mma(xu, tte[j][kb], duf[kb]);
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s.beta[16 * rt + 4 * g]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) rb[j][i] += xu[i] * frag_at(vown[nt], 4 * j + i);
@@ -943,42 +952,28 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     }
   }
   {
+    // both products are fp32 x fp32 (fp32 matrix-core products); the two row
+    // halves of a column group each form half of Z and exchange it through LDS,
+    // stored transposed so that Z's columns read back as rows
     const float* sGT = slotF(SV);
-    // both products are fp32 x fp32: true fp32 products for fp32 inputs, the
-    // three-term bf16 split for bf16 inputs
-    constexpr bool SPLIT = std::is_same<E, bf16>::value;
-    f32x4 z[4];
-    if constexpr (SPLIT) {
-      Frag<bf16> th[2], tl[2];
+    float* sZT = slotF(SP);
+    {
+      Frag<float> tcol[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) split_frag(ld_frag(sT, LA, 16 * cw + c16, 32 * kb), th[kb], tl[kb]);
+      for (int kb = 0; kb < 2; ++kb) tcol[kb] = ld_frag(sT, LA, 16 * cw + c16, 32 * kb);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        z[rt] = zero4();
+      for (int j = 0; j < 2; ++j) {
+        const int rt = 2 * rh + j;
+        f32x4 z = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          Frag<bf16> xh, xl;
-          split_frag(ld_frag(sGT, LA, 16 * rt + c16, 32 * kb), xh, xl);
-          mma3(z[rt], xh, xl, th[kb], tl[kb]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        z[rt] = zero4();
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          mma(z[rt], ld_frag(sGT, LA, 16 * rt + c16, 32 * kb), ld_frag(sT, LA, 16 * cw + c16, 32 * kb));
+        for (int kb = 0; kb < 2; ++kb) mma(z, ld_frag(sGT, LA, 16 * rt + c16, 32 * kb), tcol[kb]);
+        *reinterpret_cast<f32x4*>(&sZT[(16 * cw + c16) * LA + 16 * rt + 4 * g]) = z;
       }
     }
+    __syncthreads();
     Frag<float> zf[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) pack_frag(zf[kb], z[2 * kb], z[2 * kb + 1]);
-    Frag<bf16> zh[2], zl[2];
-    if constexpr (SPLIT) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) split_frag(zf[kb], zh[kb], zl[kb]);
-    }
+    for (int kb = 0; kb < 2; ++kb) zf[kb] = ld_frag(static_cast<const float*>(sZT), LA, 16 * cw + c16, 32 * kb);
     const int c = 16 * cw + c16;
     float csum = 0.f;
     f32x4 ga[2];
@@ -987,20 +982,11 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       const int rt = 2 * rh + j;
       f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const Frag<float> tt = ld_fragT<float>(sT, LA, 16 * rt + c16, 32 * kb, -1.f);
-        if constexpr (SPLIT) {
-          Frag<bf16> xh, xl;
-          split_frag(tt, xh, xl);
-          mma3(acc, xh, xl, zh[kb], zl[kb]);
-        } else {
-          mma(acc, tt, zf[kb]);
-        }
-      }
+      for (int kb = 0; kb < 2; ++kb) mma(acc, ttf[j][kb], zf[kb]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
-        const float gav = (c < r) ? acc[i] : 0.f;
+        const float gav = (c < r) ? -acc[i] : 0.f;
         const float kd = sKD[r * LA + c];
         const float gaa = gav * s.beta[r] * kd;
         rg[j][i] += gaa;

@@ -204,11 +204,22 @@ __device__ __forceinline__ void st4f<float>(float* p, const f32x4& v) {
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// DPP move within rows of 16 lanes (quad permutations and row mirrors, whose
+// source lanes always exist, so no fill value is needed and none is set up).
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, dpp_mov<CTRL>(__builtin_bit_cast(int, x)));
+}
+
 // x from lane (lane ^ X) of the same quad (DPP quad permutation, no LDS).
 template <int X>
 __device__ __forceinline__ float quad_xor(float x) {
   constexpr int ctrl = (0 ^ X) | ((1 ^ X) << 2) | ((2 ^ X) << 4) | ((3 ^ X) << 6);
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false));
+  return dpp_mov<ctrl>(x);
 }
 
 // Forces x to be computed here: the compiler may not sink the arithmetic that
@@ -227,8 +238,8 @@ __device__ __forceinline__ void pin(f32x4& x) {
 __device__ __forceinline__ float row16_sum(float x) {
   x += quad_xor<1>(x);
   x += quad_xor<2>(x);
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));  // half-row mirror
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));  // row mirror
+  x += dpp_mov<0x141>(x);  // half-row mirror
+  x += dpp_mov<0x140>(x);  // row mirror
   return x;
 }
 
@@ -239,9 +250,8 @@ __device__ __forceinline__ float lane_group_sum(float x) {
   static_assert(N == 8 || N == 16, "lane groups of 8 or 16");
   x += quad_xor<1>(x);
   x += quad_xor<2>(x);
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
-  if (N == 16)
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  x += dpp_mov<0x141>(x);
+  if (N == 16) x += dpp_mov<0x140>(x);
   return x;
 }
 
@@ -278,27 +288,22 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 v) {
 template <int X>
 __device__ __forceinline__ uint32_t quad_xor_u(uint32_t x) {
   constexpr int ctrl = (0 ^ X) | ((1 ^ X) << 2) | ((2 ^ X) << 4) | ((3 ^ X) << 6);
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, 0xF, 0xF, false);
+  return (uint32_t)dpp_mov<ctrl>((int)x);
 }
 __device__ __forceinline__ void quad_transpose16(uint32_t& d0, uint32_t& d1) {
   const int b = threadIdx.x & 3;
-  {  // 2x2 blocks with lane b^2: dwords move whole
-    const bool lo = (b & 2) == 0;
-    const uint32_t r = quad_xor_u<2>(lo ? d1 : d0);
-    if (lo) d1 = r; else d0 = r;
-  }
-  {  // single entries with lane b^1: halves move
-    const bool lo = (b & 1) == 0;
-    const uint32_t snd = lo ? __builtin_amdgcn_perm(d1, d0, 0x07060302u) : __builtin_amdgcn_perm(d1, d0, 0x05040100u);
-    const uint32_t r = quad_xor_u<1>(snd);
-    if (lo) {
-      d0 = __builtin_amdgcn_perm(r, d0, 0x05040100u);
-      d1 = __builtin_amdgcn_perm(r, d1, 0x07060100u);
-    } else {
-      d0 = __builtin_amdgcn_perm(d0, r, 0x07060100u);
-      d1 = __builtin_amdgcn_perm(d1, r, 0x07060302u);
-    }
-  }
+  // 2x2 blocks with lane b^2: lanes 0, 1 take the partner's first dword as
+  // their second, lanes 2, 3 the partner's second dword as their first
+  const uint32_t a = quad_xor_u<2>(d0), c = quad_xor_u<2>(d1);
+  const bool lo = (b & 2) == 0;
+  const uint32_t n0 = lo ? d0 : c, n1 = lo ? a : d1;
+  // single entries with lane b^1: even lanes keep their low halves and append
+  // the partner's, odd lanes put the partner's high half below their own (one
+  // byte permute with a per-lane selector)
+  const uint32_t sel = (b & 1) ? 0x03020706u : 0x05040100u;
+  const uint32_t x0 = quad_xor_u<1>(n0), x1 = quad_xor_u<1>(n1);
+  d0 = __builtin_amdgcn_perm(x0, n0, sel);
+  d1 = __builtin_amdgcn_perm(x1, n1, sel);
 }
 
 // Fragment whose k-slots walk down column col0 + lane%16 of a row-major E
@@ -425,25 +430,20 @@ __device__ __forceinline__ Frag<E> ld_frag_kscaled(const E* base, int ld, int ro
   return f;
 }
 
-// fp32 operands on bf16 matrix cores: x = hi + lo with hi = bf16(x) and
-// lo = bf16(x - hi), and X Y ~ Xhi Yhi + Xhi Ylo + Xlo Yhi (the dropped
-// Xlo Ylo term and the rounding of lo leave about 16 significant bits, three
-// bf16 products in place of eight fp32 16x16x4 ones per 32-deep block).
-__device__ __forceinline__ void split_frag(const Frag<float>& f, Frag<bf16>& hi, Frag<bf16>& lo) {
+// acc + sum over the eight k-slots of a[j] * b[j] (bf16 pairs on the dot
+// product unit, fp32 accumulation).
+__device__ __forceinline__ float frag_dot(const Frag<bf16>& a, const Frag<bf16>& b, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  struct Pairs { bf16x2_t p[4]; };
+  const Pairs pa = __builtin_bit_cast(Pairs, a.v), pb = __builtin_bit_cast(Pairs, b.v);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16 a = (bf16)f.lo[i], b = (bf16)f.hi[i];
-    hi.v[i] = a;
-    hi.v[4 + i] = b;
-    lo.v[i] = (bf16)(f.lo[i] - (float)a);
-    lo.v[4 + i] = (bf16)(f.hi[i] - (float)b);
-  }
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(pa.p[i], pb.p[i], acc, false);
+  return acc;
 }
-__device__ __forceinline__ void mma3(f32x4& acc, const Frag<bf16>& xh, const Frag<bf16>& xl, const Frag<bf16>& yh,
-                                     const Frag<bf16>& yl) {
-  mma(acc, xl, yh);
-  mma(acc, xh, yl);
-  mma(acc, xh, yh);
+__device__ __forceinline__ float frag_dot(const Frag<float>& a, const Frag<float>& b, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc += a.lo[i] * b.lo[i] + a.hi[i] * b.hi[i];
+  return acc;
 }
 
 // Value of k-slot j of a fragment, as fp32.
