@@ -77,20 +77,24 @@ template <class E, int DK, int DV, bool CORR, bool PREP>
 struct RevChunk {
   static constexpr int NW = RevWaves<DV>::NW, NT = 64 * NW, NTW = DV / (16 * NW);
   using S = RevSmem<E, DK, DV>;
+  // The next chunk's tiles, in flight in registers during the current chunk.
+  // With dO needed, the first half of the threads holds K and the second half
+  // Q (one register set, kq), and dO sits on the first NT / 2 * (DV / DK)
+  // threads; without it (CORR) K is spread over all threads.
+  static constexpr int KQT = CORR ? NT : NT / 2;  // threads per K (or Q) tile
   struct Loader {
-    TilePart<E, NT, DK> k;
-    TilePart<E, NT, CORR ? 0 : DK> q;
+    TilePart<E, KQT, DK> kq;
     TilePart<E, NT, CORR ? 0 : DV> d;
     ScalarPart<E> sc;
   };
+  __device__ __forceinline__ static bool q_half() { return !CORR && threadIdx.x >= KQT; }
+  __device__ __forceinline__ static int kq_tid() { return threadIdx.x & (KQT - 1); }
 
   __device__ static void issue(Loader& ld, const RevParams& p, int64_t tok0, int rows, int h) {
     const int H = p.H;
-    ld.k.load(static_cast<const E*>(p.k) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
-    if (!CORR) {
-      ld.q.load(static_cast<const E*>(p.q) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
-      ld.d.load(static_cast<const E*>(p.dout) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
-    }
+    const void* src = q_half() ? p.q : p.k;
+    ld.kq.load(static_cast<const E*>(src) + (tok0 * H + h) * DK, (int64_t)H * DK, rows, kq_tid());
+    if (!CORR) ld.d.load(static_cast<const E*>(p.dout) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
     ld.sc.load(p.g, static_cast<const E*>(p.beta), tok0, H, h, rows);
   }
 
@@ -144,15 +148,12 @@ struct RevChunk {
         st4f<E>(dst, val);
       }
     S& s1 = *sp;
-    if (PREP && p.prep.qk_norm) {
-      ld.k.normalize_rows();
-      if (!CORR) ld.q.normalize_rows();
+    if (PREP && p.prep.qk_norm) ld.kq.normalize_rows(kq_tid());
+    {
+      const bool qh = q_half();
+      ld.kq.store(qh ? s1.Q : s1.K, LQ, qh ? s1.QT : s1.KT, LT, kq_tid());
     }
-    ld.k.store(s1.K, LQ, s1.KT, LT);
-    if (!CORR) {
-      ld.q.store(s1.Q, LQ, s1.QT, LT);
-      ld.d.store(nullptr, 0, s1.DOT, LT);
-    }
+    if (!CORR) ld.d.store(nullptr, 0, s1.DOT, LT);
     if (w == 0) {
       S& s = s1;
       float gr, bt;
