@@ -52,7 +52,7 @@ struct Plan {
   bool cp = false;      // some sequence has more than one segment
   // workspace offsets (bytes)
   size_t o_chunk_first = 0, o_seg_first = 0, o_segs = 0, o_chunk_tab = 0;
-  size_t o_bstate = 0, o_lam = 0, o_bstate2 = 0, o_lam2 = 0, o_hs = 0, o_dhs = 0, total = 0;
+  size_t o_bstate = 0, o_lam = 0, o_bstate2 = 0, o_lam2 = 0, o_hs = 0, o_dhs = 0, o_ts = 0, total = 0;
 };
 
 bool supported(int dtype, int Dk, int Dv) {
@@ -163,6 +163,9 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false) 
       p.o_lam2 = take(sizeof(float) * (size_t)p.nseg * a.H);
     }
     if (!saved) p.o_hs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
+    // the chunk matrices T, solved once (by the replay, else by the reverse
+    // chain) and read by the later kernels
+    p.o_ts = take(sizeof(float) * CHUNK * CHUNK * (size_t)std::max(1, p.nchunk) * a.H);
     p.o_dhs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
   }
   p.total = off;
@@ -366,13 +369,20 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   p.chunk_first = at<int>(ws, pl.o_chunk_first);
   p.bstate = pl.cp ? at<float>(ws, pl.o_bstate) : nullptr;
   p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
+  // chunk matrices T: solved by the first kernel over the chunks (the replay, or
+  // without it the reverse chain), read by the later ones
+  float* ts = at<float>(ws, pl.o_ts);
+  const bool replay = !saved;
   if (saved) {
     p.hs = const_cast<void*>(args->h_saved);
   } else {
     p.hs = at<void>(ws, pl.o_hs);
+    p.t_out = at<float>(ws, pl.o_ts);
     p.phase = 1;
     e = timed("replay", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
     if (e != hipSuccess) return hip_fail(e, "replay launch");
+    p.t_out = nullptr;
+    p.t_in = ts;
     if (pl.cp) {
       p.phase = 3;
       e = timed("replay_corr", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
@@ -387,10 +397,14 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   r.bstate = pl.cp ? at<float>(ws, pl.o_bstate2) : nullptr;
   r.lam = pl.cp ? at<float>(ws, pl.o_lam2) : nullptr;
   r.dhs = at<void>(ws, pl.o_dhs);
+  r.t_in = replay ? ts : nullptr;
+  r.t_out = replay ? nullptr : ts;
   r.prep = p.prep;
   r.phase = 1;
   e = timed("rev", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "reverse launch");
+  r.t_in = ts;
+  r.t_out = nullptr;
   if (pl.cp) {
     r.phase = 3;
     e = timed("rev_corr", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });
@@ -400,7 +414,7 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   if (pl.nchunk > 0) {
     gdn::GradParams gp{};
     gp.q = a.q; gp.k = a.k; gp.v = a.v; gp.g = a.g; gp.beta = a.beta; gp.dout = args->do_;
-    gp.hs = p.hs; gp.dhs = r.dhs;
+    gp.hs = p.hs; gp.dhs = r.dhs; gp.t_in = ts;
     gp.dq = args->dq; gp.dk = args->dk; gp.dv = args->dv; gp.dbeta = args->dbeta; gp.dg = args->dg;
     gp.scale = a.scale; gp.H = a.H; gp.seq = sq;
     gp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);

@@ -73,7 +73,8 @@ struct RevWaves { static constexpr int NW = DV == 128 ? 8 : 4; };
 // One chunk of the reverse chain (wave w owns Dv/NW columns of the state
 // gradient).  CORR: propagation of a boundary difference only (dO does not
 // enter, stored gradients are incremented).
-template <class E, int DK, int DV, bool CORR, bool PREP>
+// TLOAD: every chunk's T is read (p.t_in) instead of solved.
+template <class E, int DK, int DV, bool CORR, bool PREP, bool TLOAD>
 struct RevChunk {
   static constexpr int NW = RevWaves<DV>::NW, NT = 64 * NW, NTW = DV / (16 * NW);
   using S = RevSmem<E, DK, DV>;
@@ -129,11 +130,15 @@ struct RevChunk {
 
   // dh: gradient at the chunk end on entry, at the chunk start on exit.
   // Prefetches chunk (ntok0, nrows) into ld (nrows = 0: none).  Returns Lambda_c.
+  // t_in: this chunk's T when TLOAD; t_out: where to write the solved T
+  // (nullable).
   __device__ static float step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows,
-                               int h, E* dhs_chunk, f32x4 (&dh)[DK / 16][NTW]) {
+                               int h, E* dhs_chunk, const float* t_in, float* t_out, f32x4 (&dh)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
-    const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+    constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
+    const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
     const int n0 = w * (DV / NW);
+    constexpr bool tload = TLOAD;
 
     // ---- 1. gradient at the chunk end out; tiles into LDS; scalars
     S* sp = lds_opaque(&s0);
@@ -177,11 +182,19 @@ struct RevChunk {
     //         wave r < 4 forms the diagonal tile A_rr and solves block r of T at once
     //         (the critical path); waves 4..7 share the six off-diagonal tiles of A
     //         and the ten of P^T.
+    // T (when given) is requested now, past the staging, and lands in LDS at the
+    // end of this phase
+    f32x4 tv[TPT];
+    if (tload) {
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
+    }
     if constexpr (NW == 8) {
       S* sq = lds_opaque(&s0);
       if (w < 4) {
+        // (with T given, the diagonal tiles are still formed for the log-bound)
         kk_tile<false>(sq, p, w, w, g, c16, rows);
-        solve_diag_pair(sq->A, sq->T, w, w, nullptr);
+        if (!tload) solve_diag_pair(sq->A, sq->T, w, w, nullptr);
       } else {
         const int wq = w - 4;
 #pragma unroll
@@ -190,7 +203,7 @@ struct RevChunk {
           if (id < 6) {
             const int rt = id < 1 ? 1 : (id < 3 ? 2 : 3);
             const int ct = id - (rt * (rt - 1)) / 2;
-            kk_tile<false>(sq, p, rt, ct, g, c16, rows);
+            if (!tload) kk_tile<false>(sq, p, rt, ct, g, c16, rows);
           } else if (!CORR) {
             const int pid = id - 6;
             const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
@@ -238,20 +251,41 @@ struct RevChunk {
           const bool rows03 = (w & 1) == 0;
           if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
           else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
-          if (!isq) solve_diag_pair(s.A, s.T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
+          if (!isq && !tload) solve_diag_pair(s.A, s.T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
+        }
+      }
+      if (tload) {
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+          const int e = 4 * (tid + i * NT);
+          *reinterpret_cast<f32x4*>(&s.T[(e / CH) * LA + e % CH]) = tv[i];
         }
       }
     }
     __syncthreads();
     const float lam_c = __shfl(wave_sum(lds_opaque(&s0)->lam[l]), 0, 64);
-    if (nrows > 0) issue(ld, p, ntok0, nrows, h);
 
-    // ---- 3. off-diagonal blocks of T
-    {
-      S& s = *lds_opaque(&s0);
-      solve_columns(s.A, s.T, w, nullptr);
+    // ---- 3. off-diagonal blocks of T (when solved here), T out.  The next
+    //         chunk's tiles start their way from HBM after the T store, so that
+    //         nothing below waits behind them.
+    if constexpr (tload) {
+      if (nrows > 0) issue(ld, p, ntok0, nrows, h);
+    } else {
+      {
+        S& s = *lds_opaque(&s0);
+        solve_columns(s.A, s.T, w, nullptr);
+      }
+      __syncthreads();
+      if (t_out) {
+        const S& s = *lds_opaque(&s0);
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+          const int e = 4 * (tid + i * NT);
+          *reinterpret_cast<f32x4*>(t_out + e) = *reinterpret_cast<const f32x4*>(&s.T[(e / CH) * LA + e % CH]);
+        }
+      }
+      if (nrows > 0) issue(ld, p, ntok0, nrows, h);
     }
-    __syncthreads();
 
     // ---- 4. -W^T = -K^T diag(beta Gam) T^T: (Dk/16) x 4 tiles, KTW key tiles x
     //         RTW chunk-row tiles per wave
@@ -363,7 +397,10 @@ struct RevChunk {
       const bool more = c - 1 >= cb;
       const int64_t ntok0 = seq0 + (int64_t)(c - 1) * CH;
       const int nrows = more ? min(CH, len - (c - 1) * CH) : 0;
-      lam += step(s, p, ld, rows, ntok0, nrows, h, dhs + ((chunk0 + c) * p.H + h) * SS, dh);
+      const size_t toff = ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
+      const float* tin = TLOAD ? p.t_in + toff : nullptr;
+      float* tout = (!CORR && !TLOAD && p.t_out) ? p.t_out + toff : nullptr;
+      lam += step(s, p, ld, rows, ntok0, nrows, h, dhs + ((chunk0 + c) * p.H + h) * SS, tin, tout, dh);
     }
     if (lowest) *lowest = c + 1;
     return lam;
@@ -410,7 +447,7 @@ __device__ void rev_init_smem(RevSmem<E, DK, DV>& s) {
 }
 
 // Phase 1: every segment from dh' = 0 (the last segment of a sequence from dhT).
-template <class E, int DK, int DV, bool PREP>
+template <class E, int DK, int DV, bool PREP, bool TLOAD>
 __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p1(RevParams p) {
   __shared__ RevSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
@@ -421,7 +458,7 @@ __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p1(RevParams p)
   f32x4 dh[DK / 16][DV / (16 * RevWaves<DV>::NW)];
   rev_init_smem(s);
   rev_load<E, DK, DV>(dh, sd.s == nseg - 1 ? dhT : nullptr);
-  const float lam = RevChunk<E, DK, DV, false, PREP>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
+  const float lam = RevChunk<E, DK, DV, false, PREP, TLOAD>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
                                                     sd.c_begin, sd.c_end, h, dh, nullptr);
   if (nseg == 1) {
     if (p.dh0) rev_store<E, DK, DV>(dh, p.dh0 + ((size_t)n * p.H + h) * SS, nullptr, true);
@@ -453,13 +490,13 @@ __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p3(RevParams p)
   rev_init_smem(s);
   if (!ok) {
     rev_load<E, DK, DV>(dh, p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr);
-    RevChunk<E, DK, DV, false, PREP>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, dh, nullptr);
+    RevChunk<E, DK, DV, false, PREP, true>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, dh, nullptr);
     if (dh0) rev_store<E, DK, DV>(dh, dh0, nullptr, true);
     return;
   }
   rev_load<E, DK, DV>(dh, p.bstate + ((size_t)(blockIdx.x + 1) * p.H + h) * SS);
   int lowest = sd.c_end;
-  RevChunk<E, DK, DV, true, PREP>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, dh, &lowest);
+  RevChunk<E, DK, DV, true, PREP, true>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, dh, &lowest);
   if (sd.s == 0 && dh0)
     rev_store<E, DK, DV>(dh, dh0, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, lowest == sd.c_begin);
 }
@@ -468,12 +505,17 @@ template <class E, int DK, int DV>
 hipError_t launch_rev_t(const RevParams& p, int nseg_total, hipStream_t st) {
   const dim3 block(64 * RevWaves<DV>::NW);
   const dim3 grid(nseg_total, p.H);
+  // phase 3 always reads T (written by the replay or by phase 1)
+  if (p.phase != 1 && !p.t_in) return hipErrorInvalidValue;
+  const bool tl = p.t_in != nullptr;
   if (p.prep.qk_norm || p.prep.gate_act) {
-    if (p.phase == 1) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV, true>), grid, block, 0, st, p);
+    if (p.phase != 1) hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV, true>), grid, block, 0, st, p);
+    else if (tl) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, true, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, true, false>), grid, block, 0, st, p);
   } else {
-    if (p.phase == 1) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, false>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV, false>), grid, block, 0, st, p);
+    if (p.phase != 1) hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV, false>), grid, block, 0, st, p);
+    else if (tl) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, false, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, false, false>), grid, block, 0, st, p);
   }
   return hipGetLastError();
 }
@@ -579,8 +621,18 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       tv.template load<true>(v, (int64_t)H * DV, rows, ht);
       td.template load<true>(d, (int64_t)H * DV, rows, ht);
     }
-    for (int e = 4 * tid; e < CH * CH; e += 4 * NT) {
-      *reinterpret_cast<f32x4*>(&sT[(e >> 6) * LA + (e & 63)]) = zero4();
+    // T, when given, replaces the solve below (requested after the tiles)
+    constexpr int TPT = CH * CH / (4 * NT);
+    const float* tin = p.t_in ? p.t_in + ((size_t)blockIdx.x * H + h) * (CH * CH) : nullptr;
+    f32x4 tvals[TPT];
+    if (tin) {
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) tvals[i] = *reinterpret_cast<const f32x4*>(tin + 4 * (tid + i * NT));
+    }
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int e = 4 * (tid + i * NT);
+      if (!tin) *reinterpret_cast<f32x4*>(&sT[(e >> 6) * LA + (e & 63)]) = zero4();
       *reinterpret_cast<f32x4*>(&sP[(e >> 6) * LA + (e & 63)]) = zero4();
     }
     for (int e = tid; e < 4 * CH; e += NT) {
@@ -617,7 +669,15 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       tv.store(slotE(SV), LV, nullptr, 0, ht);
       td.store(slotE(SDO), LV, nullptr, 0, ht);
     }
+    if (tin) {
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const int e = 4 * (tid + i * NT);
+        *reinterpret_cast<f32x4*>(&sT[(e >> 6) * LA + (e & 63)]) = tvals[i];
+      }
+    }
   }
+  const bool tload = p.t_in != nullptr;
   __syncthreads();
   // h and dh' down this wave's value columns (the operands of P5), requested
   // only now: every workgroup stages its tiles at about the same time, and the
@@ -653,11 +713,13 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   __syncthreads();
 
-  // ---- P3: T = (I + diag(beta) KD)^-1
-  if (w < 2) solve_diag_pair(sKD, sT, w, 3 - w, s.beta);
-  __syncthreads();
-  solve_columns(sKD, sT, w, s.beta);
-  __syncthreads();
+  // ---- P3: T = (I + diag(beta) KD)^-1 (unless given)
+  if (!tload) {
+    if (w < 2) solve_diag_pair(sKD, sT, w, 3 - w, s.beta);
+    __syncthreads();
+    solve_columns(sKD, sT, w, s.beta);
+    __syncthreads();
+  }
 
   // per-lane partial sums of this wave's rows (row tiles 2 rh + j)
   f32x4 rg[2], rb[2];  // dgam / dbeta terms

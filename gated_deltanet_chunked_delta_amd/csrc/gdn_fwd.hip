@@ -269,12 +269,26 @@ struct Chunk {
   // Process the chunk whose tiles `ld` holds; prefetch the next chunk (if any)
   // into `ld`.  hacc: this wave's state columns (chunk start on entry, chunk end
   // on exit).  Returns the chunk's log-bound Lambda_c.
+  // t_in: this chunk's T, read instead of solved by the replay's corrections;
+  // t_out: where the replay's first phase writes the solved T (nullable).  The
+  // forward proper neither reads nor writes T.
   __device__ static float step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows,
-                               int64_t ntok0, int nrows, int h, E* hs_chunk, f32x4 (&hacc)[DK / 16][NTW]) {
+                               int64_t ntok0, int nrows, int h, E* hs_chunk, const float* t_in, float* t_out,
+                               f32x4 (&hacc)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA, LO = S::LO;
+    constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
     const int H = p.H;
     const int n0 = w * (DV / NW);  // first state column of this wave
+    // the replay's corrections read T (solved by its first phase)
+    constexpr bool tload = !OUT && CORR;
+
+    // T (when given) is requested first and lands in LDS at the end of phase 2
+    f32x4 tv[TPT];
+    if (tload) {
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
+    }
 
     // ---- 1. tiles into LDS, scalars, prefetch of the next chunk
     S* sp = lds_opaque(&s0);
@@ -318,8 +332,9 @@ struct Chunk {
     //         waves 4..7 share the six off-diagonal tiles of A and the ten of P.
     if constexpr (NW == 8) {
       if (w < 4) {
+        // (with T given, the diagonal tiles are still formed for the log-bound)
         kk_tile<false>(sp, w, w, g, c16, rows);
-        solve_diag_pair(sp->A, sp->T, w, w, nullptr);
+        if (!tload) solve_diag_pair(sp->A, sp->T, w, w, nullptr);
       } else {
         const int wq = w - 4;
 #pragma unroll
@@ -328,7 +343,7 @@ struct Chunk {
           if (id < 6) {
             const int rt = id < 1 ? 1 : (id < 3 ? 2 : 3);
             const int ct = id - (rt * (rt - 1)) / 2;
-            kk_tile<false>(sp, rt, ct, g, c16, rows);
+            if (!tload) kk_tile<false>(sp, rt, ct, g, c16, rows);
           } else if (OUT) {
             const int pid = id - 6;
             const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
@@ -375,8 +390,15 @@ struct Chunk {
           const bool rows03 = (w & 1) == 0;
           if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
           else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
-          if (!isq) solve_diag_pair(sp->A, sp->T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
+          if (!isq && !tload) solve_diag_pair(sp->A, sp->T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
         }
+      }
+    }
+    if (tload) {
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const int e = 4 * (tid + i * NT);
+        *reinterpret_cast<f32x4*>(&sp->T[(e / CH) * LA + e % CH]) = tv[i];
       }
     }
     __syncthreads();
@@ -386,14 +408,26 @@ struct Chunk {
     const float lam_c = __shfl(wave_sum(sp->lam[l]), 0, 64);
 
     // next chunk's k, v, g, beta start their way from HBM (q follows later,
-    // which keeps the prefetch registers out of the busiest stretch)
-    if (nrows > 0) ld.load_kv(p, ntok0, nrows, h);
-    if (OUT && nrows > 0) ld.load_q(p, ntok0, nrows, h);
+    // which keeps the prefetch registers out of the busiest stretch); the
+    // replay requests them after its T store below, so that nothing waits
+    // behind them
+    if (OUT && nrows > 0) {
+      ld.load_kv(p, ntok0, nrows, h);
+      ld.load_q(p, ntok0, nrows, h);
+    }
 
     // ---- 3. off-diagonal blocks of T (one block column per wave)
-    solve_columns(sp->A, sp->T, w, nullptr);
+    if (!tload) solve_columns(sp->A, sp->T, w, nullptr);
     __syncthreads();
     sp = lds_opaque(sp);
+    if (t_out) {
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const int e = 4 * (tid + i * NT);
+        *reinterpret_cast<f32x4*>(t_out + e) = *reinterpret_cast<const f32x4*>(&sp->T[(e / CH) * LA + e % CH]);
+      }
+    }
+    if (!OUT && nrows > 0) ld.load_kv(p, ntok0, nrows, h);
 
     // ---- 4. -W = -T diag(beta Gam) K for row tile w % 4 (key column tiles split
     //         between w / 4 = 0, 1 with eight waves); Ut = T diag(beta) V for this
@@ -554,7 +588,10 @@ struct Chunk {
       const bool more = c + 1 < ce;
       const int nrows = more ? min(CH, len - (c + 1) * CH) : 0;
       E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
-      lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, hacc);
+      const size_t toff = ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
+      const float* tin = (!OUT && CORR) ? p.t_in + toff : nullptr;
+      float* tout = (!OUT && !CORR && p.t_out) ? p.t_out + toff : nullptr;
+      lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, tout, hacc);
     }
     if (done) *done = c - cb;
     return lam;
@@ -664,6 +701,8 @@ hipError_t launch_fwd_t(const FwdParams& p, int nseg_total, hipStream_t st) {
   dim3 grid(nseg_total, p.H), block(64 * FwdWaves<DV>::NW);
   const bool out = p.o != nullptr;
   const bool prep = p.prep.qk_norm || p.prep.gate_act;
+  // the replay's corrections read T (written by its first phase)
+  if (p.phase != 1 && !out && !p.t_in) return hipErrorInvalidValue;
   if (p.phase == 1) {
     if (prep) {
       if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true>), grid, block, 0, st, p);

@@ -35,6 +35,9 @@ struct FwdParams {
   float* bstate;           // [total segments][H][DK][DV] segment end states
   float* lam;              // [total segments][H] segment log-bounds
   void* hs;                // nullable: [total chunks][H] chunk start states S, Dv x Dk in st_blk order (dtype)
+  // [total chunks][H][CH][CH] fp32 row-major T = (I + diag(beta) A)^-1 of each chunk:
+  const float* t_in;       // nullable: read instead of solved (replay and corrections only)
+  float* t_out;            // nullable: written where solved (phase 1)
   int phase;               // 1 = segments from zero / h0, 3 = boundary corrections
   PrepParams prep;
 };
@@ -57,6 +60,8 @@ struct RevParams {
   float* bstate;           // [total segments][H][DK][DV] segment start gradients
   float* lam;              // [total segments][H]
   void* dhs;               // [total chunks][H] gradient at each chunk END, S-shaped, st_blk order (dtype)
+  const float* t_in;       // nullable: chunk matrices T (as FwdParams), read instead of solved
+  float* t_out;            // nullable: written where solved (phase 1)
   int phase;
   PrepParams prep;
 };
@@ -71,6 +76,7 @@ struct GradParams {
   const void* dout;
   const void* hs;          // chunk start states
   const void* dhs;         // chunk end state gradients
+  const float* t_in;       // nullable: chunk matrices T (as FwdParams), read instead of solved
   void* dq;
   void* dk;
   void* dv;

@@ -147,21 +147,26 @@ struct TilePart {
   vec_t blk[NB > 0 ? NB : 1][4];
 
   // ZFILL: rows at or past `rows` become zero instead of copies of the last row.
+  // src is the same for every lane; each load is addressed as src + a 32-bit
+  // byte offset (the host keeps 64 rows of a tile under 2 GiB), one address
+  // register per load.
   template <bool ZFILL = false>
   __device__ __forceinline__ void load(const E* src, int64_t gld, int rows, int tid = threadIdx.x) {
+    const char* base = reinterpret_cast<const char*>(src);
+    const uint32_t ldb = (uint32_t)gld * (uint32_t)sizeof(E);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int id = tid + b * NT;
       if (NB * NT == NBLK || id < NBLK) {
         const int r0 = (id / BPR) * 4, c0 = (id % BPR) * VEC;
-        const E* p = src + c0;
+        const uint32_t cb = (uint32_t)c0 * (uint32_t)sizeof(E);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if (ZFILL) {
             blk[b][j] = vec_t{};
-            if (r0 + j < rows) blk[b][j] = *reinterpret_cast<const vec_t*>(p + (int64_t)(r0 + j) * gld);
+            if (r0 + j < rows) blk[b][j] = *reinterpret_cast<const vec_t*>(base + ((uint32_t)(r0 + j) * ldb + cb));
           } else {
-            blk[b][j] = *reinterpret_cast<const vec_t*>(p + (int64_t)min(r0 + j, rows - 1) * gld);
+            blk[b][j] = *reinterpret_cast<const vec_t*>(base + ((uint32_t)min(r0 + j, rows - 1) * ldb + cb));
           }
         }
       }
@@ -242,9 +247,11 @@ struct ScalarPart {
   int nrow;
   __device__ __forceinline__ void load(const float* g, const E* beta, int64_t tok0, int H, int h, int rows) {
     if (threadIdx.x < 64) {
-      const int64_t si = (tok0 + min((int)threadIdx.x, rows - 1)) * H + h;
-      gr = g[si];
-      be = beta[si];
+      // uniform row base + a 32-bit per-lane offset
+      const int64_t s0 = tok0 * H + h;
+      const uint32_t si = (uint32_t)min((int)threadIdx.x, rows - 1) * (uint32_t)H;
+      gr = (g + s0)[si];
+      be = (beta + s0)[si];
       nrow = rows;
     }
   }
