@@ -196,6 +196,8 @@ def main():
                          "gate and beta passed as logits (g = -0.1 softplus(a), beta = sigmoid(b))")
     ap.add_argument("--save-states", action="store_true",
                     help="the forward keeps the chunk states and the backward reads them (no replay)")
+    ap.add_argument("--no-save-t", action="store_true",
+                    help="the forward does not keep the chunk matrices T; the backward solves for them")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy (out = x * 1, fp32) of this many MiB three "
@@ -241,21 +243,26 @@ def main():
     ntok = int(B * T) if cu is None else int(x.cu_seqlens[-1])
 
     # The step follows the backward as specified: it takes the forward's inputs
-    # and replays the forward states.  --save-states times the alternative in
-    # which the forward keeps the chunk states (Dk*Dv values per 64 tokens and
-    # head) for the backward; the default run also reports that variant in a
-    # separate, labelled object.
+    # and replays the forward states; the forward keeps every chunk's matrix T
+    # (64 x 64 fp32 per 64 tokens and head) for it, as the autograd wrapper does
+    # (--no-save-t: the backward solves for T itself).  --save-states times the
+    # alternative in which the forward also keeps the chunk states (Dk*Dv
+    # values per 64 tokens and head) for the backward; the default run also
+    # reports that variant in a separate, labelled object.
     keep = False
+    save_t = not args.no_save_t and args.direction == "fwdbwd"
 
     def step():
-        states = None
+        states = chunk_t = None
         if args.direction in ("fwdbwd", "fwd"):
             res = gb.gdn_chunk_fwd(q, k, v, g, beta, x.scale, h0=h0, cu_seqlens=cu, cu_seqlens_host=host,
-                                   cp_mode=args.cp_mode, save_states=keep, **prep_kw)
+                                   cp_mode=args.cp_mode, save_states=keep, save_t=save_t, **prep_kw)
             states = res[2] if keep else None
+            chunk_t = res[-1] if save_t else None
         if args.direction in ("fwdbwd", "bwd"):
             gb.gdn_chunk_bwd(q, k, v, g, beta, x.scale, do, h0=h0, cu_seqlens=cu, cu_seqlens_host=host,
-                             cp_mode=args.cp_mode, need_dh0=h0 is not None, states=states, **prep_kw)
+                             cp_mode=args.cp_mode, need_dh0=h0 is not None, states=states, chunk_t=chunk_t,
+                             **prep_kw)
 
     stream = torch.cuda.current_stream(dev)
 
@@ -288,8 +295,9 @@ def main():
         keep = True
         ms_v, _ = timed_run(False)
         keep = False
-        variant = {"states": "saved by fwd (no replay in bwd)", "ms_per_step": ms_v, "value": ntok * 1e3 / ms_v,
-                   "unit": "tokens/s"}
+        variant = {"states": "saved by fwd (no replay in bwd)",
+                   "chunk_T": "saved by fwd" if save_t else "solved in bwd",
+                   "ms_per_step": ms_v, "value": ntok * 1e3 / ms_v, "unit": "tokens/s"}
         log(f"timed {args.steps} steps with saved states")
 
     fwd_f, bwd_f = flops_per_token_head(dk, dv)
@@ -324,6 +332,7 @@ def main():
         "config": {"workload": args.config, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": CH,
                    "direction": args.direction, "cp_mode": args.cp_mode, "tokens_per_step": ntok,
                    "states": "saved by fwd" if args.save_states else "recomputed in bwd",
+                   "chunk_T": "saved by fwd" if save_t else "solved in bwd",
                    "preprocessing": "in-kernel q/k L2 norm + gate/beta activation" if args.prep else "none"},
         "tflops": tflops, "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "kernels": kernels, "roofline": roof,

@@ -20,22 +20,24 @@ class _ChunkGatedDeltaRule(torch.autograd.Function):
                 qk_norm, gate_act, gate_scale):
         res = gdn_chunk_fwd(q, k, v, g, beta, scale, h0=h0, cu_seqlens=cu_seqlens,
                             cu_seqlens_host=cu_seqlens_host, output_final_state=True, cp_mode=cp_mode,
-                            save_states=save_states, qk_norm=qk_norm, gate_act=gate_act, gate_scale=gate_scale)
+                            save_states=save_states, save_t=True, qk_norm=qk_norm, gate_act=gate_act,
+                            gate_scale=gate_scale)
         o, hT = res[0], res[1]
         states = res[2] if save_states else None
-        ctx.save_for_backward(q, k, v, g, beta, h0, cu_seqlens, states, gate_scale)
+        chunk_t = res[-1]
+        ctx.save_for_backward(q, k, v, g, beta, h0, cu_seqlens, states, chunk_t, gate_scale)
         ctx.scale, ctx.cu_host, ctx.cp_mode = scale, cu_seqlens_host, cp_mode
         ctx.qk_norm, ctx.gate_act = qk_norm, gate_act
         return o, hT
 
     @staticmethod
     def backward(ctx, do, dhT):
-        q, k, v, g, beta, h0, cu, states, gate_scale = ctx.saved_tensors
+        q, k, v, g, beta, h0, cu, states, chunk_t, gate_scale = ctx.saved_tensors
         dq, dk, dv, dg, dbeta, dh0 = gdn_chunk_bwd(
             q, k, v, g, beta, ctx.scale, do.contiguous(), h0=h0,
             dhT=None if dhT is None else dhT.contiguous(), cu_seqlens=cu,
             cu_seqlens_host=ctx.cu_host, cp_mode=ctx.cp_mode, need_dh0=h0 is not None, states=states,
-            qk_norm=ctx.qk_norm, gate_act=ctx.gate_act, gate_scale=gate_scale)
+            chunk_t=chunk_t, qk_norm=ctx.qk_norm, gate_act=ctx.gate_act, gate_scale=gate_scale)
         return dq, dk, dv, dg, dbeta, dh0, None, None, None, None, None, None, None, None
 
 
@@ -44,11 +46,12 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, out
                            qk_norm: bool = False, gate_act: bool = False, gate_scale=None):
     """o, (hT) for the gated delta rule over [B, T, H, D] inputs, differentiable.
 
-    g is the fp32 natural-log decay [B, T, H]; beta has the dtype of q.  With
-    save_states (the default) the forward keeps the state at every chunk start
-    (Dk * Dv values per 64 tokens and head, in the input dtype) so that the
-    backward does not recompute them; pass False to trade that memory for a
-    forward replay inside the backward.  qk_norm: q and k are raw and normalised
+    g is the fp32 natural-log decay [B, T, H]; beta has the dtype of q.  The
+    forward keeps every chunk's matrix T (64 x 64 fp32 per 64 tokens and head)
+    for the backward.  With save_states (the default) it also keeps the state
+    at every chunk start (Dk * Dv values per 64 tokens and head, in the input
+    dtype) so that the backward does not recompute them; pass False to trade
+    that memory for a forward replay inside the backward.  qk_norm: q and k are raw and normalised
     inside the kernels; gate_act: g and beta are logits, g = -gate_scale[h]
     softplus(g), beta = sigmoid(beta) inside the kernels (gate_scale is not
     differentiated).

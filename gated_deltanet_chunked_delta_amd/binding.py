@@ -33,11 +33,12 @@ class CommonArgs(ctypes.Structure):
 
 
 class FwdArgs(ctypes.Structure):
-    _fields_ = [("a", CommonArgs), ("o", _vp), ("hT", _vp), ("h_save", _vp)]
+    _fields_ = [("a", CommonArgs), ("o", _vp), ("hT", _vp), ("h_save", _vp), ("t_save", _vp)]
 
 
 class BwdArgs(ctypes.Structure):
-    _fields_ = [("a", CommonArgs), ("h_saved", _vp), ("do_", _vp), ("dhT", _vp), ("dq", _vp), ("dk", _vp),
+    _fields_ = [("a", CommonArgs), ("h_saved", _vp), ("t_saved", _vp), ("do_", _vp), ("dhT", _vp), ("dq", _vp),
+                ("dk", _vp),
                 ("dv", _vp), ("dbeta", _vp), ("dg", _vp), ("dh0", _vp)]
 
 
@@ -70,6 +71,8 @@ def lib():
         L.gdn_chunk_bwd_workspace_size.restype = ctypes.c_size_t
         L.gdn_chunk_states_bytes.argtypes = [ctypes.POINTER(CommonArgs)]
         L.gdn_chunk_states_bytes.restype = ctypes.c_size_t
+        L.gdn_chunk_t_bytes.argtypes = [ctypes.POINTER(CommonArgs)]
+        L.gdn_chunk_t_bytes.restype = ctypes.c_size_t
         L.gdn_chunk_fwd.argtypes = [ctypes.POINTER(FwdArgs), _vp]
         L.gdn_chunk_fwd.restype = ctypes.c_int
         L.gdn_chunk_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
@@ -172,11 +175,12 @@ def _stream(dev):
 
 def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_seqlens_host=None,
                   output_final_state: bool = True, cp_mode: int = 0, save_states: bool = False,
-                  qk_norm: bool = False, gate_act: bool = False, gate_scale=None):
-    """Forward pass.  Returns (o, hT) with hT None unless output_final_state; with
-    save_states, (o, hT, states) where states (the state at every chunk start, for
-    gdn_chunk_bwd) is a flat tensor of the input dtype.  qk_norm / gate_act select the
-    in-kernel pre-processing (raw q, k; gate and beta logits, see include/gdn.h)."""
+                  save_t: bool = False, qk_norm: bool = False, gate_act: bool = False, gate_scale=None):
+    """Forward pass.  Returns (o, hT) with hT None unless output_final_state, followed by
+    states if save_states (the state at every chunk start, a flat tensor of the input
+    dtype) and chunk_t if save_t (every chunk's matrix T, a flat fp32 tensor); both are
+    for gdn_chunk_bwd.  qk_norm / gate_act select the in-kernel pre-processing (raw q,
+    k; gate and beta logits, see include/gdn.h)."""
     a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode,
                       qk_norm, gate_act, gate_scale)
     L = lib()
@@ -187,9 +191,13 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_s
     if save_states:
         nb = L.gdn_chunk_states_bytes(ctypes.byref(a))
         states = torch.empty(max(nb, 16) // q.element_size(), dtype=q.dtype, device=q.device)
+    chunk_t = None
+    if save_t:
+        nb = L.gdn_chunk_t_bytes(ctypes.byref(a))
+        chunk_t = torch.empty(max(nb, 16) // 4, dtype=torch.float32, device=q.device)
     args = FwdArgs()
     args.a = a
-    args.o, args.hT, args.h_save = _ptr(o), _ptr(hT), _ptr(states)
+    args.o, args.hT, args.h_save, args.t_save = _ptr(o), _ptr(hT), _ptr(states), _ptr(chunk_t)
     nbytes = L.gdn_chunk_fwd_workspace_size(ctypes.byref(args))
     if nbytes == 0:
         _check(1)
@@ -197,16 +205,17 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_s
     args.a.workspace, args.a.workspace_bytes = ws.data_ptr(), nbytes
     _check(L.gdn_chunk_fwd(ctypes.byref(args), _vp(_stream(q.device))))
     del keep
-    return (o, hT, states) if save_states else (o, hT)
+    return (o, hT) + ((states,) if save_states else ()) + ((chunk_t,) if save_t else ())
 
 
 def gdn_chunk_bwd(q, k, v, g, beta, scale: float, do, h0=None, dhT=None, cu_seqlens=None,
                   cu_seqlens_host=None, cp_mode: int = 0, need_dh0: bool = True, states=None,
-                  qk_norm: bool = False, gate_act: bool = False, gate_scale=None):
+                  chunk_t=None, qk_norm: bool = False, gate_act: bool = False, gate_scale=None):
     """Backward pass.  Returns (dq, dk, dv, dg, dbeta, dh0) with dh0 None unless need_dh0.
-    states: the forward's saved chunk states (gdn_chunk_fwd(..., save_states=True)); when
-    given the backward does not recompute them.  With qk_norm / gate_act the gradients
-    are with respect to the raw inputs."""
+    states / chunk_t: the forward's saved chunk states and chunk matrices T
+    (gdn_chunk_fwd(..., save_states=True / save_t=True)); what is given is not
+    recomputed.  With qk_norm / gate_act the gradients are with respect to the raw
+    inputs."""
     a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode,
                       qk_norm, gate_act, gate_scale)
     _contig("do", do, q.dtype, q.device)
@@ -214,6 +223,9 @@ def gdn_chunk_bwd(q, k, v, g, beta, scale: float, do, h0=None, dhT=None, cu_seql
     _contig("states", states, q.dtype, q.device)
     if states is not None and states.numel() * states.element_size() < lib().gdn_chunk_states_bytes(ctypes.byref(a)):
         raise GDNError("states is smaller than gdn_chunk_states_bytes")
+    _contig("chunk_t", chunk_t, torch.float32, q.device)
+    if chunk_t is not None and chunk_t.numel() * 4 < lib().gdn_chunk_t_bytes(ctypes.byref(a)):
+        raise GDNError("chunk_t is smaller than gdn_chunk_t_bytes")
     L = lib()
     dq, dk = torch.empty_like(q), torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -223,7 +235,7 @@ def gdn_chunk_bwd(q, k, v, g, beta, scale: float, do, h0=None, dhT=None, cu_seql
            if need_dh0 else None)
     args = BwdArgs()
     args.a = a
-    args.h_saved = _ptr(states)
+    args.h_saved, args.t_saved = _ptr(states), _ptr(chunk_t)
     args.do_, args.dhT = _ptr(do), _ptr(dhT)
     args.dq, args.dk, args.dv, args.dbeta, args.dg, args.dh0 = map(_ptr, (dq, dk, dv, dbeta, dg, dh0))
     nbytes = L.gdn_chunk_bwd_workspace_size(ctypes.byref(args))

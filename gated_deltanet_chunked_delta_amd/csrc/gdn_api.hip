@@ -114,8 +114,10 @@ gdn::PrepParams prep_of(int qk_norm, int gate_act, const float* gate_scale) {
 }
 
 // Segment length, totals and workspace layout.  `bwd` adds the backward's arrays
-// (without the chunk states when the caller provides them: `saved`).
-Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false) {
+// (without the chunk states when the caller provides them: `saved`).  `t_given`:
+// the caller provides (forward: takes) the chunk matrices T, which otherwise live
+// in the workspace (the forward needs them only to correct segments).
+Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false, bool t_given = false) {
   Plan p;
   p.N = a.num_seqs;
   std::vector<int> nch(p.N);
@@ -157,6 +159,8 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false) 
     p.o_bstate = take(sizeof(float) * SS * p.nseg * a.H);
     p.o_lam = take(sizeof(float) * (size_t)p.nseg * a.H);
   }
+  const size_t tbytes = sizeof(float) * CHUNK * CHUNK * (size_t)std::max(1, p.nchunk) * a.H;
+  if (!bwd && p.cp && !t_given) p.o_ts = take(tbytes);
   if (bwd) {
     if (p.cp) {
       p.o_bstate2 = take(sizeof(float) * SS * p.nseg * a.H);
@@ -165,7 +169,7 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false) 
     if (!saved) p.o_hs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
     // the chunk matrices T, solved once (by the replay, else by the reverse
     // chain) and read by the later kernels
-    p.o_ts = take(sizeof(float) * CHUNK * CHUNK * (size_t)std::max(1, p.nchunk) * a.H);
+    if (!t_given) p.o_ts = take(tbytes);
     p.o_dhs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
   }
   p.total = off;
@@ -269,13 +273,13 @@ const char* gdn_last_error(void) { return g_err.c_str(); }
 size_t gdn_chunk_fwd_workspace_size(const gdn_fwd_args* args) {
   if (!args) { fail(GDN_E_INVALID, "null args"); return 0; }
   if (check_common(args->a) != GDN_OK) return 0;
-  return make_plan(args->a, false, cu_count()).total;
+  return make_plan(args->a, false, cu_count(), false, args->t_save != nullptr).total;
 }
 
 size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args) {
   if (!args) { fail(GDN_E_INVALID, "null args"); return 0; }
   if (check_common(args->a) != GDN_OK) return 0;
-  return make_plan(args->a, true, cu_count(), args->h_saved != nullptr).total;
+  return make_plan(args->a, true, cu_count(), args->h_saved != nullptr, args->t_saved != nullptr).total;
 }
 
 size_t gdn_chunk_states_bytes(const gdn_common_args* a) {
@@ -290,6 +294,17 @@ size_t gdn_chunk_states_bytes(const gdn_common_args* a) {
   return (size_t)chunks * a->H * a->Dk * a->Dv * esz;
 }
 
+size_t gdn_chunk_t_bytes(const gdn_common_args* a) {
+  if (!a) { fail(GDN_E_INVALID, "null args"); return 0; }
+  if (check_common(*a) != GDN_OK) return 0;
+  long long chunks = 0;
+  for (int n = 0; n < a->num_seqs; ++n) {
+    const int len = a->cu_seqlens ? a->cu_seqlens_host[n + 1] - a->cu_seqlens_host[n] : a->T;
+    chunks += (len + CHUNK - 1) / CHUNK;
+  }
+  return (size_t)chunks * a->H * CHUNK * CHUNK * sizeof(float);
+}
+
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   if (!args) return fail(GDN_E_INVALID, "null args");
   const gdn_common_args& a = args->a;
@@ -299,7 +314,8 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   if (!aligned(args->o, 16)) return fail(GDN_E_INVALID, "o must be 16-byte aligned");
   if (!aligned(args->hT, 4)) return fail(GDN_E_INVALID, "hT misaligned");
   if (!aligned(args->h_save, 16)) return fail(GDN_E_INVALID, "h_save must be 16-byte aligned");
-  const Plan pl = make_plan(a, false, cu_count());
+  if (!aligned(args->t_save, 16)) return fail(GDN_E_INVALID, "t_save must be 16-byte aligned");
+  const Plan pl = make_plan(a, false, cu_count(), false, args->t_save != nullptr);
   if (!a.workspace || a.workspace_bytes < pl.total)
     return fail(GDN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total,
                 a.workspace ? a.workspace_bytes : (size_t)0);
@@ -321,10 +337,14 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
   p.hs = args->h_save;  // nullable: the chunk states are stored only on request
   p.prep = prep_of(a.qk_norm, a.gate_act, a.gate_scale);
+  // T: for the caller, or for the segment corrections (which read it back)
+  p.t_out = args->t_save ? args->t_save : (pl.cp ? at<float>(ws, pl.o_ts) : nullptr);
   p.phase = 1;
   e = timed("fwd", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   if (pl.cp) {
+    p.t_in = p.t_out;
+    p.t_out = nullptr;
     p.phase = 3;
     e = timed("fwd_corr", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
     if (e != hipSuccess) return hip_fail(e, "forward correction launch");
@@ -346,8 +366,10 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
       !aligned(args->dh0, 4))
     return fail(GDN_E_INVALID, "dg / dbeta / dhT / dh0 misaligned");
   if (!aligned(args->h_saved, 16)) return fail(GDN_E_INVALID, "h_saved must be 16-byte aligned");
+  if (!aligned(args->t_saved, 16)) return fail(GDN_E_INVALID, "t_saved must be 16-byte aligned");
   const bool saved = args->h_saved != nullptr;
-  const Plan pl = make_plan(a, true, cu_count(), saved);
+  const bool t_given = args->t_saved != nullptr;
+  const Plan pl = make_plan(a, true, cu_count(), saved, t_given);
   if (!a.workspace || a.workspace_bytes < pl.total)
     return fail(GDN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total,
                 a.workspace ? a.workspace_bytes : (size_t)0);
@@ -369,15 +391,16 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   p.chunk_first = at<int>(ws, pl.o_chunk_first);
   p.bstate = pl.cp ? at<float>(ws, pl.o_bstate) : nullptr;
   p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
-  // chunk matrices T: solved by the first kernel over the chunks (the replay, or
-  // without it the reverse chain), read by the later ones
-  float* ts = at<float>(ws, pl.o_ts);
+  // chunk matrices T: the caller's, else solved by the first kernel over the
+  // chunks (the replay, or without it the reverse chain) and read by the later ones
+  const float* ts = t_given ? args->t_saved : at<float>(ws, pl.o_ts);
   const bool replay = !saved;
   if (saved) {
     p.hs = const_cast<void*>(args->h_saved);
   } else {
     p.hs = at<void>(ws, pl.o_hs);
-    p.t_out = at<float>(ws, pl.o_ts);
+    if (t_given) p.t_in = ts;
+    else p.t_out = at<float>(ws, pl.o_ts);
     p.phase = 1;
     e = timed("replay", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
     if (e != hipSuccess) return hip_fail(e, "replay launch");
@@ -397,8 +420,9 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   r.bstate = pl.cp ? at<float>(ws, pl.o_bstate2) : nullptr;
   r.lam = pl.cp ? at<float>(ws, pl.o_lam2) : nullptr;
   r.dhs = at<void>(ws, pl.o_dhs);
-  r.t_in = replay ? ts : nullptr;
-  r.t_out = replay ? nullptr : ts;
+  const bool rev_solves = !replay && !t_given;
+  r.t_in = rev_solves ? nullptr : ts;
+  r.t_out = rev_solves ? at<float>(ws, pl.o_ts) : nullptr;
   r.prep = p.prep;
   r.phase = 1;
   e = timed("rev", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });

@@ -229,7 +229,8 @@ struct TileLoader {
 template <int DV>
 struct FwdWaves { static constexpr int NW = DV == 128 ? 8 : 4; };
 
-template <class E, int DK, int DV, bool OUT, bool CORR, bool PREP>
+// TLOAD: every chunk's T is read (p.t_in) instead of solved.
+template <class E, int DK, int DV, bool OUT, bool CORR, bool PREP, bool TLOAD>
 struct Chunk {
   static constexpr int NW = FwdWaves<DV>::NW;
   static constexpr int NT = NW * 64;
@@ -269,9 +270,8 @@ struct Chunk {
   // Process the chunk whose tiles `ld` holds; prefetch the next chunk (if any)
   // into `ld`.  hacc: this wave's state columns (chunk start on entry, chunk end
   // on exit).  Returns the chunk's log-bound Lambda_c.
-  // t_in: this chunk's T, read instead of solved by the replay's corrections;
-  // t_out: where the replay's first phase writes the solved T (nullable).  The
-  // forward proper neither reads nor writes T.
+  // t_in: this chunk's T when TLOAD; t_out: where to write the solved T
+  // (nullable).
   __device__ static float step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows,
                                int64_t ntok0, int nrows, int h, E* hs_chunk, const float* t_in, float* t_out,
                                f32x4 (&hacc)[DK / 16][NTW]) {
@@ -280,8 +280,7 @@ struct Chunk {
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
     const int H = p.H;
     const int n0 = w * (DV / NW);  // first state column of this wave
-    // the replay's corrections read T (solved by its first phase)
-    constexpr bool tload = !OUT && CORR;
+    constexpr bool tload = TLOAD;
 
     // T (when given) is requested first and lands in LDS at the end of phase 2
     f32x4 tv[TPT];
@@ -407,27 +406,25 @@ struct Chunk {
     // value (and the loop decisions taken on it) is identical across the workgroup
     const float lam_c = __shfl(wave_sum(sp->lam[l]), 0, 64);
 
-    // next chunk's k, v, g, beta start their way from HBM (q follows later,
-    // which keeps the prefetch registers out of the busiest stretch); the
-    // replay requests them after its T store below, so that nothing waits
-    // behind them
-    if (OUT && nrows > 0) {
+    // ---- 3. off-diagonal blocks of T (one block column per wave, when solved
+    //         here), T out.  The next chunk's k, v, g, beta (and q) start their
+    //         way from HBM before the solve.
+    if (nrows > 0) {
       ld.load_kv(p, ntok0, nrows, h);
-      ld.load_q(p, ntok0, nrows, h);
+      if (OUT) ld.load_q(p, ntok0, nrows, h);
     }
-
-    // ---- 3. off-diagonal blocks of T (one block column per wave)
-    if (!tload) solve_columns(sp->A, sp->T, w, nullptr);
-    __syncthreads();
-    sp = lds_opaque(sp);
-    if (t_out) {
+    if constexpr (!tload) {
+      solve_columns(sp->A, sp->T, w, nullptr);
+      __syncthreads();
+      sp = lds_opaque(sp);
+      if (t_out) {
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) {
-        const int e = 4 * (tid + i * NT);
-        *reinterpret_cast<f32x4*>(t_out + e) = *reinterpret_cast<const f32x4*>(&sp->T[(e / CH) * LA + e % CH]);
+        for (int i = 0; i < TPT; ++i) {
+          const int e = 4 * (tid + i * NT);
+          *reinterpret_cast<f32x4*>(t_out + e) = *reinterpret_cast<const f32x4*>(&sp->T[(e / CH) * LA + e % CH]);
+        }
       }
     }
-    if (!OUT && nrows > 0) ld.load_kv(p, ntok0, nrows, h);
 
     // ---- 4. -W = -T diag(beta Gam) K for row tile w % 4 (key column tiles split
     //         between w / 4 = 0, 1 with eight waves); Ut = T diag(beta) V for this
@@ -589,8 +586,8 @@ struct Chunk {
       const int nrows = more ? min(CH, len - (c + 1) * CH) : 0;
       E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
       const size_t toff = ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
-      const float* tin = (!OUT && CORR) ? p.t_in + toff : nullptr;
-      float* tout = (!OUT && !CORR && p.t_out) ? p.t_out + toff : nullptr;
+      const float* tin = TLOAD ? p.t_in + toff : nullptr;
+      float* tout = (!TLOAD && p.t_out) ? p.t_out + toff : nullptr;
       lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, tout, hacc);
     }
     if (done) *done = c - cb;
@@ -641,7 +638,7 @@ __device__ void init_smem(FwdSmem<E, DK, DV>& s) {
 }
 
 // Phase 1: every segment from zero (segment 0 from h0).
-template <class E, int DK, int DV, bool OUT, bool PREP>
+template <class E, int DK, int DV, bool OUT, bool PREP, bool TLOAD>
 __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
@@ -651,7 +648,7 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p)
   f32x4 hacc[DK / 16][DV / (16 * FwdWaves<DV>::NW)];
   init_smem(s);
   load_state<E, DK, DV>(hacc, (sd.s == 0 && p.h0) ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-  const float lam = Chunk<E, DK, DV, OUT, false, PREP>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
+  const float lam = Chunk<E, DK, DV, OUT, false, PREP, TLOAD>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
                                                       sd.c_begin, sd.c_end, h, hacc, nullptr);
   if (nseg == 1) {
     if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
@@ -682,13 +679,13 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p3(FwdParams p)
   if (!ok) {
     // Gates do not decay fast enough to cut this sequence: one workgroup redoes it serially.
     load_state<E, DK, DV>(hacc, p.h0 ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-    Chunk<E, DK, DV, OUT, false, PREP>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc, nullptr);
+    Chunk<E, DK, DV, OUT, false, PREP, true>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc, nullptr);
     if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
     return;
   }
   load_state<E, DK, DV>(hacc, p.bstate + ((size_t)(blockIdx.x - 1) * p.H + h) * SS);
   int done = 0;
-  Chunk<E, DK, DV, OUT, true, PREP>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done);
+  Chunk<E, DK, DV, OUT, true, PREP, true>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done);
   if (sd.s == nseg - 1 && p.hT) {
     // hT = b_last + (the correction propagated through the whole last segment, if it got there)
     const float* b = p.bstate + ((size_t)blockIdx.x * p.H + h) * SS;
@@ -701,15 +698,20 @@ hipError_t launch_fwd_t(const FwdParams& p, int nseg_total, hipStream_t st) {
   dim3 grid(nseg_total, p.H), block(64 * FwdWaves<DV>::NW);
   const bool out = p.o != nullptr;
   const bool prep = p.prep.qk_norm || p.prep.gate_act;
-  // the replay's corrections read T (written by its first phase)
-  if (p.phase != 1 && !out && !p.t_in) return hipErrorInvalidValue;
+  // phase 3 always reads T (written by phase 1); phase 1 reads it only in the
+  // replay, when the forward saved it
+  if (p.phase != 1 && !p.t_in) return hipErrorInvalidValue;
+  if (p.phase == 1 && out && p.t_in) return hipErrorInvalidValue;
+  const bool tl = p.t_in != nullptr;
   if (p.phase == 1) {
     if (prep) {
-      if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true>), grid, block, 0, st, p);
+      if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true, false>), grid, block, 0, st, p);
+      else if (tl) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true, false>), grid, block, 0, st, p);
     } else {
-      if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false>), grid, block, 0, st, p);
+      if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false, false>), grid, block, 0, st, p);
+      else if (tl) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false, false>), grid, block, 0, st, p);
     }
   } else {
     if (prep) {

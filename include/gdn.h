@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum {
   GDN_OK = 0,
@@ -109,6 +109,8 @@ typedef struct {
   void* h_save;                /* nullable, 16-byte aligned, gdn_chunk_states_bytes(&a) bytes: the
                                   state at the start of every 64-token chunk, written for a later
                                   gdn_chunk_bwd (layout below) */
+  float* t_save;               /* nullable, 16-byte aligned, gdn_chunk_t_bytes(&a) bytes: every
+                                  chunk's matrix T (below), written for a later gdn_chunk_bwd */
 } gdn_fwd_args;
 
 typedef struct {
@@ -116,6 +118,9 @@ typedef struct {
   const void* h_saved;         /* nullable: h_save of a gdn_chunk_fwd call on the same inputs;
                                   given, the backward reads the chunk states instead of
                                   recomputing them (no forward replay) */
+  const float* t_saved;        /* nullable: t_save of a gdn_chunk_fwd call on the same inputs;
+                                  given, the backward reads every chunk's T instead of solving
+                                  for it once itself */
   const void* do_;             /* [B,T,H,Dv] dtype: gradient of o */
   const float* dhT;            /* nullable [N,H,Dk,Dv]: gradient of hT (NULL = zero) */
   void* dq;                    /* [B,T,H,Dk] dtype, written */
@@ -128,8 +133,9 @@ typedef struct {
 
 /* Bytes of device workspace gdn_chunk_fwd / gdn_chunk_bwd need for these
  * arguments (pointers other than cu_seqlens_host are not read, except that the
- * backward needs less when h_saved is non-NULL).  Returns 0 and sets the error
- * string when the arguments are invalid. */
+ * forward needs less when t_save is non-NULL and the backward less when
+ * h_saved or t_saved is).  Returns 0 and sets the error string when the
+ * arguments are invalid. */
 size_t gdn_chunk_fwd_workspace_size(const gdn_fwd_args* args);
 size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args);
 
@@ -145,13 +151,27 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args);
  * without error when there are no tokens). */
 size_t gdn_chunk_states_bytes(const gdn_common_args* a);
 
-/* Forward: o and (optionally) hT and the chunk states.  stream is a
- * hipStream_t (NULL = default stream). */
+/* Bytes of the saved chunk matrices (t_save / t_saved): C * H * 64 * 64 fp32
+ * values, C as above.  Entry (c, h) at element offset (c * H + h) * 4096 is the
+ * 64 x 64 row-major lower-triangular matrix
+ *     T = (I + diag(beta) strict_lower((K K^T) * D))^-1,   D[r][i] = exp(G_r - G_i),
+ * of chunk c and head h (K: the chunk's 64 keys as rows, after the optional
+ * normalisation; beta after the optional activation; G_r the running sum of
+ * g over the chunk up to row r), the inverse of the chunk's unit lower-
+ * triangular system in the WY/UT form ("FlashQLA resource", section 3).  Rows
+ * past a sequence's end have beta = 0 (rows of the identity).  Returns 0 and
+ * sets the error string for invalid arguments (and returns 0 without error
+ * when there are no tokens). */
+size_t gdn_chunk_t_bytes(const gdn_common_args* a);
+
+/* Forward: o and (optionally) hT, the chunk states and the chunk matrices T.
+ * stream is a hipStream_t (NULL = default stream). */
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream);
 
 /* Backward: gradients of <do, o> + <dhT, hT> with respect to q, k, v, beta, g
  * and (optionally) h0.  It recomputes the forward states from the inputs
- * unless h_saved provides them. */
+ * unless h_saved provides them, and solves for each chunk's T once unless
+ * t_saved provides them. */
 gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream);
 
 /* One recurrent decode step: every listed sequence takes one new token and

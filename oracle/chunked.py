@@ -42,6 +42,25 @@ def _chunk_consts(Kc, g, b):
     return gam, Gam, Dm, A, T
 
 
+def chunk_t(k, g, beta, cu_seqlens=None, C=64):
+    """Every chunk's T = (I + A)^{-1} of the lines above, float64 [chunks, H, C, C],
+    chunks numbered sequence after sequence.  A short last chunk is completed with
+    identity rows and columns (its missing rows carry beta = 0)."""
+    k, g, beta = (np.asarray(x, dtype=np.float64) for x in (k, g, beta))
+    B, T, H, Dk = k.shape
+    cu = _cu(B, T, cu_seqlens)
+    kf, gf, bf = k.reshape(B * T, H, Dk), g.reshape(B * T, H), beta.reshape(B * T, H)
+    out = []
+    for n in range(len(cu) - 1):
+        for t0 in range(cu[n], cu[n + 1], C):
+            t1 = min(t0 + C, cu[n + 1])
+            ts = np.tile(np.eye(C), (H, 1, 1))
+            for hh in range(H):
+                ts[hh, :t1 - t0, :t1 - t0] = _chunk_consts(kf[t0:t1, hh], gf[t0:t1, hh], bf[t0:t1, hh])[4]
+            out.append(ts)
+    return np.stack(out) if out else np.zeros((0, H, C, C))
+
+
 def fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, C=64):
     """Chunked forward; returns (o, hT) in float64 (same shapes as ``ref.fwd``)."""
     q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))

@@ -136,11 +136,13 @@ def test_config_backward(dev, name):
     check_bwd(x, dev, 0, name)
 
 
-@pytest.mark.parametrize("cp_mode", [-1, 2, 0])
-def test_saved_states_match_replay(dev, cp_mode):
-    """The backward fed with the forward's saved chunk states gives the same
-    gradients as the backward that replays the forward (same kernels, same
-    arithmetic order), and the forward's outputs do not change by saving them."""
+@pytest.mark.parametrize("cp_mode,save_s,save_t", [(-1, True, False), (2, True, False), (0, True, False),
+                                                   (2, False, True), (0, True, True)])
+def test_saved_states_match_replay(dev, cp_mode, save_s, save_t):
+    """The backward fed with the forward's saved chunk states and / or chunk
+    matrices T gives the same gradients as the backward that recomputes them
+    (same kernels, same arithmetic order), and the forward's outputs do not
+    change by saving them."""
     import torch
     from gated_deltanet_chunked_delta_amd import gdn_chunk_bwd, gdn_chunk_fwd
     rng = np.random.default_rng(9)
@@ -151,14 +153,18 @@ def test_saved_states_match_replay(dev, cp_mode):
     x.cu_seqlens = cu
     x.h0 = (0.3 * rng.standard_normal((len(lens), 2, 128, 128))).astype(np.float32)
     x.dhT = rng.standard_normal((len(lens), 2, 128, 128)).astype(np.float32)
-    print(f"[bwd] saved-states varlen cp={cp_mode}", flush=True)
+    print(f"[bwd] saved states={save_s} T={save_t} varlen cp={cp_mode}", flush=True)
     t = to_torch(x, dev)
     kw = dict(h0=t["h0"], cu_seqlens=t["cu"], cu_seqlens_host=cu, cp_mode=cp_mode)
     o1, hT1 = gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, **kw)
-    o2, hT2, states = gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, save_states=True, **kw)
+    res = gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, save_states=save_s, save_t=save_t,
+                        **kw)
+    o2, hT2 = res[0], res[1]
+    states = res[2] if save_s else None
+    chunk_t = res[-1] if save_t else None
     g1 = gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, t["do"], dhT=t["dhT"], **kw)
     g2 = gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, t["do"], dhT=t["dhT"],
-                       states=states, **kw)
+                       states=states, chunk_t=chunk_t, **kw)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(hT1, hT2)
     for name, a, b in zip(NAMES, g1, g2):

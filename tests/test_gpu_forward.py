@@ -155,3 +155,27 @@ def test_saved_states_are_chunk_start_states(dev, dtype, Dk, Dv, cp):
             assert err <= TOL[dtype], (n, j, err)
             c += 1
     assert c == C
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv,cp", [("bf16", 128, 128, 0), ("bf16", 64, 128, 3), ("f32", 64, 64, -1)])
+def test_saved_t_matches_oracle(dev, dtype, Dk, Dv, cp):
+    """Every saved chunk matrix T equals the oracle's (the chunked form's T,
+    completed with the identity past a sequence end), entry by entry."""
+    import torch
+    from gated_deltanet_chunked_delta_amd import gdn_chunk_fwd
+    from oracle import chunked
+    lens = [130, 0, 64, 257, 5]
+    cu = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    x = gdn_inputs.generate(B=1, T=int(cu[-1]), H=2, Dk=Dk, Dv=Dv, dtype=dtype, seed=52 + Dk + Dv)
+    x.cu_seqlens = cu
+    print(f"[fwd] saved T {dtype} Dk={Dk} Dv={Dv} cp={cp}", flush=True)
+    t = to_torch(x, dev)
+    res = gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, cu_seqlens=t["cu"],
+                        cu_seqlens_host=cu, cp_mode=cp, save_t=True)
+    torch.cuda.synchronize()
+    want = chunked.chunk_t(x.k, x.g, x.beta, cu)
+    got = res[2].cpu().numpy().astype(np.float64)[:want.size].reshape(want.shape)
+    err = relerr(got, want)
+    print(f"    T {err:.3e}", flush=True)
+    assert err <= 1e-3

@@ -68,7 +68,8 @@ def test_forward_and_backward(dev, dtype, Dk, Dv, T, cp):
 
 
 def test_saved_states_with_preprocessing(dev):
-    """The forward's saved states feed the pre-processing backward like the replay does."""
+    """The forward's saved states and chunk matrices T feed the pre-processing
+    backward like the recomputation does."""
     import torch
     from gated_deltanet_chunked_delta_amd import gdn_chunk_bwd, gdn_chunk_fwd
     x = gdn_inputs.generate(B=1, T=333, H=2, Dk=128, Dv=128, dtype="bf16", seed=611, grad=True)
@@ -76,14 +77,19 @@ def test_saved_states_with_preprocessing(dev):
     print("[prep] saved states", flush=True)
     t = to_torch(x, dev)
     kw = kw_torch(gs, dev)
-    _, _, states = gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, cp_mode=2, save_states=True,
-                                 **kw)
+    _, _, states, chunk_t = gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, cp_mode=2,
+                                          save_states=True, save_t=True, **kw)
     g1 = gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, t["do"], cp_mode=2, need_dh0=False, **kw)
     g2 = gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, t["do"], cp_mode=2, need_dh0=False,
                        states=states, **kw)
+    g3 = gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, t["do"], cp_mode=2, need_dh0=False,
+                       states=states, chunk_t=chunk_t, **kw)
+    g4 = gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, t["do"], cp_mode=2, need_dh0=False,
+                       chunk_t=chunk_t, **kw)
     torch.cuda.synchronize()
-    for n, a, b in zip(NAMES[:5], g1, g2):
-        assert relerr(to_np(b), to_np(a)) <= 1e-6, n
+    for other in (g2, g3, g4):
+        for n, a, b in zip(NAMES[:5], g1, other):
+            assert relerr(to_np(b), to_np(a)) <= 1e-6, n
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -248,3 +248,26 @@ def test_pins_catch_a_transposed_initial_state():
     o, _ = ref.fwd(q, k, v, g, beta, 1.0, h0)
     o_t, _ = ref.fwd(q, k, v, g, beta, 1.0, np.swapaxes(h0, -1, -2).copy())
     assert relerr(o_t, o) > 1e-3
+
+
+def test_chunk_t_is_the_forward_chunk_matrix():
+    """chunked.chunk_t returns the T that chunked.fwd uses (pinned to the token
+    recurrence above): with a zero initial state, one chunk's end state is
+    K~^T T diag(beta) V, compared here with the recurrence's hT; short chunks are
+    completed with the identity."""
+    q, k, v, g, beta, _ = rand_case(9, B=1, T=70, Dk=5, Dv=4)
+    C = 16
+    ts = chunked.chunk_t(k, g, beta, C=C)
+    assert ts.shape == (5, 2, C, C)
+    for c in range(5):
+        t0, t1 = 16 * c, min(16 * c + 16, 70)
+        n = t1 - t0
+        _, hT = ref.fwd(q[:, t0:t1], k[:, t0:t1], v[:, t0:t1], g[:, t0:t1], beta[:, t0:t1], 0.6)
+        for hh in range(2):
+            K, V = k[0, t0:t1, hh], v[0, t0:t1, hh]
+            gam = np.cumsum(g[0, t0:t1, hh])
+            Kt = np.exp(gam[-1] - gam)[:, None] * K
+            U = ts[c, hh, :n, :n] @ (beta[0, t0:t1, hh][:, None] * V)
+            assert relerr(Kt.T @ U, hT[0, hh]) < 1e-12
+            assert np.array_equal(ts[c, hh, n:, n:], np.eye(C - n))
+            assert not np.any(ts[c, hh, :n, n:]) and not np.any(ts[c, hh, n:, :n])
