@@ -898,6 +898,19 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   __syncthreads();
 
+  // V rows 16 cw .. 16 cw + 15, the operand of P9 (every tile of a wave there
+  // has column tile cw; slot V holds U by then): read from global now so that
+  // the loads are in flight during P8 (rows past the end are copies of the last
+  // one; beta = 0 there removes them).  Contiguous k order, one 16-byte read
+  // per fragment.
+  Frag<E> vf[DV / 32];
+  {
+    const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
+    const int vrow = min(16 * cw + c16, rows - 1);
+#pragma unroll
+    for (int kb = 0; kb < DV / 32; ++kb) vf[kb] = ld_frag8(v + (int64_t)vrow * H * DV, 0, 0, 32 * kb);
+  }
+
   // ---- P8: XW = T^T GW (own rows); row dots; dK partial (with GPM^T Q); dQ
   f32x4 dkacc[2][CTK];
   {
@@ -952,16 +965,6 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 
   // ---- P9: GT = dU V^T diag(beta) + GW K^T diag(beta Gam) -> slot V (fp32)
   {
-    // every tile of this wave has column tile cw, so it needs V rows 16 cw..
-    // only: read them from global (rows past the end are copies of the last
-    // one; beta = 0 there removes them)
-    Frag<E> vf[DV / 32];
-    {
-      const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
-      const int vrow = min(16 * cw + c16, rows - 1);
-#pragma unroll
-      for (int kb = 0; kb < DV / 32; ++kb) vf[kb] = ld_frag(v + (int64_t)vrow * H * DV, 0, 0, 32 * kb);
-    }
     float* sGT = slotF(SV);
     const int c = 16 * cw + c16;
 #pragma unroll
@@ -969,7 +972,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       const int rt = rh + 2 * j;
       f32x4 a = zero4(), b = zero4();
 #pragma unroll
-      for (int kb = 0; kb < DV / 32; ++kb) mma(a, ld_frag(sDU, LV, 16 * rt + c16, 32 * kb), vf[kb]);
+      for (int kb = 0; kb < DV / 32; ++kb) mma(a, ld_frag8(sDU, LV, 16 * rt + c16, 32 * kb), vf[kb]);
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb)
         mma(b, ld_frag(slotE(SQ), LK, 16 * rt + c16, 32 * kb), ld_frag(sK, LK, c, 32 * kb));
