@@ -52,7 +52,7 @@ struct Plan {
   bool cp = false;      // some sequence has more than one segment
   // workspace offsets (bytes)
   size_t o_chunk_first = 0, o_seg_first = 0, o_segs = 0, o_chunk_tab = 0;
-  size_t o_bstate = 0, o_lam = 0, o_bstate2 = 0, o_lam2 = 0, o_hs = 0, o_dhs = 0, o_ts = 0, total = 0;
+  size_t o_bstate = 0, o_lam = 0, o_bstate2 = 0, o_lam2 = 0, o_hs = 0, o_us = 0, o_dhs = 0, o_ts = 0, total = 0;
 };
 
 bool supported(int dtype, int Dk, int Dv) {
@@ -166,7 +166,10 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false, 
       p.o_bstate2 = take(sizeof(float) * SS * p.nseg * a.H);
       p.o_lam2 = take(sizeof(float) * (size_t)p.nseg * a.H);
     }
-    if (!saved) p.o_hs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
+    if (!saved) {
+      p.o_hs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
+      p.o_us = take(esz * CHUNK * (size_t)a.Dv * std::max(1, p.nchunk) * a.H);
+    }
     // the chunk matrices T, solved once (by the replay, else by the reverse
     // chain) and read by the later kernels
     if (!t_given) p.o_ts = take(tbytes);
@@ -220,6 +223,20 @@ gdn::SeqInfo seq_info(const gdn_common_args& a) {
   s.cu = a.cu_seqlens;
   s.T = a.T;
   return s;
+}
+
+long long count_chunks(const gdn_common_args& a) {
+  long long chunks = 0;
+  for (int n = 0; n < a.num_seqs; ++n) {
+    const int len = a.cu_seqlens ? a.cu_seqlens_host[n + 1] - a.cu_seqlens_host[n] : a.T;
+    chunks += (len + CHUNK - 1) / CHUNK;
+  }
+  return chunks;
+}
+
+// The saved-states buffer: the chunk states, then every chunk's U.
+size_t states_part_bytes(const gdn_common_args& a) {
+  return (size_t)count_chunks(a) * a.H * a.Dk * a.Dv * (a.dtype == GDN_BF16 ? 2 : 4);
 }
 
 }  // namespace
@@ -285,24 +302,14 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args) {
 size_t gdn_chunk_states_bytes(const gdn_common_args* a) {
   if (!a) { fail(GDN_E_INVALID, "null args"); return 0; }
   if (check_common(*a) != GDN_OK) return 0;
-  long long chunks = 0;
-  for (int n = 0; n < a->num_seqs; ++n) {
-    const int len = a->cu_seqlens ? a->cu_seqlens_host[n + 1] - a->cu_seqlens_host[n] : a->T;
-    chunks += (len + CHUNK - 1) / CHUNK;
-  }
   const size_t esz = a->dtype == GDN_BF16 ? 2 : 4;
-  return (size_t)chunks * a->H * a->Dk * a->Dv * esz;
+  return states_part_bytes(*a) + (size_t)count_chunks(*a) * a->H * CHUNK * a->Dv * esz;
 }
 
 size_t gdn_chunk_t_bytes(const gdn_common_args* a) {
   if (!a) { fail(GDN_E_INVALID, "null args"); return 0; }
   if (check_common(*a) != GDN_OK) return 0;
-  long long chunks = 0;
-  for (int n = 0; n < a->num_seqs; ++n) {
-    const int len = a->cu_seqlens ? a->cu_seqlens_host[n + 1] - a->cu_seqlens_host[n] : a->T;
-    chunks += (len + CHUNK - 1) / CHUNK;
-  }
-  return (size_t)chunks * a->H * CHUNK * CHUNK * sizeof(float);
+  return (size_t)count_chunks(*a) * a->H * CHUNK * CHUNK * sizeof(float);
 }
 
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
@@ -335,7 +342,8 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   p.chunk_first = at<int>(ws, pl.o_chunk_first);
   p.bstate = pl.cp ? at<float>(ws, pl.o_bstate) : nullptr;
   p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
-  p.hs = args->h_save;  // nullable: the chunk states are stored only on request
+  p.hs = args->h_save;  // nullable: the chunk states (and U) are stored only on request
+  p.us = args->h_save ? static_cast<char*>(args->h_save) + states_part_bytes(a) : nullptr;
   p.prep = prep_of(a.qk_norm, a.gate_act, a.gate_scale);
   // T: for the caller, or for the segment corrections (which read it back)
   p.t_out = args->t_save ? args->t_save : (pl.cp ? at<float>(ws, pl.o_ts) : nullptr);
@@ -397,8 +405,10 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   const bool replay = !saved;
   if (saved) {
     p.hs = const_cast<void*>(args->h_saved);
+    p.us = static_cast<char*>(const_cast<void*>(args->h_saved)) + states_part_bytes(a);
   } else {
     p.hs = at<void>(ws, pl.o_hs);
+    p.us = at<void>(ws, pl.o_us);
     if (t_given) p.t_in = ts;
     else p.t_out = at<float>(ws, pl.o_ts);
     p.phase = 1;
@@ -438,7 +448,7 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   if (pl.nchunk > 0) {
     gdn::GradParams gp{};
     gp.q = a.q; gp.k = a.k; gp.v = a.v; gp.g = a.g; gp.beta = a.beta; gp.dout = args->do_;
-    gp.hs = p.hs; gp.dhs = r.dhs; gp.t_in = ts;
+    gp.hs = p.hs; gp.dhs = r.dhs; gp.us = p.us; gp.t_in = ts;
     gp.dq = args->dq; gp.dk = args->dk; gp.dv = args->dv; gp.dbeta = args->dbeta; gp.dg = args->dg;
     gp.scale = a.scale; gp.H = a.H; gp.seq = sq;
     gp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);

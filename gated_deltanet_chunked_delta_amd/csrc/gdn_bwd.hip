@@ -600,25 +600,33 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   E* sDU = slotE(SDU);
 
   // ---- P1: staging (all four tiles in flight at once; rows past the end are
-  //          zero); zero T, P and the cross-wave sum arrays.  h and dh' down this
-  //          wave's value columns (the operands of P5) are requested after the
-  //          tiles have landed and stay in flight until P5; their products use
-  //          the contiguous k-slot order (one 16-byte read per fragment).
-  Frag<E> hk[CTV][DK / 32], dk_[CTV][DK / 32];
+  //          zero); zero T (unless given), P and the cross-wave sum arrays.
+  //          dh' down this wave's value columns (the operand of P5) is
+  //          requested after the tiles have landed and stays in flight until
+  //          P5; its products use the contiguous k-slot order (one 16-byte
+  //          read per fragment).
+  Frag<E> dk_[CTV][DK / 32];
   {
     const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
     const E* k = static_cast<const E*>(p.k) + (tok0 * H + h) * DK;
-    const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
+    // U of this chunk as the forward (or its replay) formed it: DV/16 column
+    // blocks of [CH][16], zero past the end; contiguous, so 16-byte piece i
+    // of the whole [CH x DV] matrix sits at element 16 i / sizeof(E)
+    const E* u = static_cast<const E*>(p.us) + ((size_t)blockIdx.x * H + h) * (CH * DV);
     const E* d = static_cast<const E*>(p.dout) + (tok0 * H + h) * DV;
-    // waves 0..3 bring K and Q, waves 4..7 V and dO
+    // waves 0..3 bring K and Q, waves 4..7 U and dO
     const int ht = tid & (NT / 2 - 1);
     TilePart<E, NT / 2, DK> tk, tq;
-    TilePart<E, NT / 2, DV> tv, td;
+    TilePart<E, NT / 2, DV> td;
+    typedef E vec_t __attribute__((__vector_size__(16)));
+    constexpr int UVEC = 16 / (int)sizeof(E), UPC = CH * DV / UVEC / (NT / 2);  // pieces per thread
+    vec_t upc[UPC];
     if (rh == 0) {
       tk.template load<true>(k, (int64_t)H * DK, rows, ht);
       tq.template load<true>(q, (int64_t)H * DK, rows, ht);
     } else {
-      tv.template load<true>(v, (int64_t)H * DV, rows, ht);
+#pragma unroll
+      for (int i = 0; i < UPC; ++i) upc[i] = *reinterpret_cast<const vec_t*>(u + (ht + i * (NT / 2)) * UVEC);
       td.template load<true>(d, (int64_t)H * DV, rows, ht);
     }
     // T, when given, replaces the solve below (requested after the tiles)
@@ -666,7 +674,13 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       tk.store(sK, LK, sKT, LT, ht);
       tq.store(slotE(SQ), LK, nullptr, 0, ht);
     } else {
-      tv.store(slotE(SV), LV, nullptr, 0, ht);
+#pragma unroll
+      for (int i = 0; i < UPC; ++i) {
+        const int pc = ht + i * (NT / 2);            // piece index
+        const int blk = pc / (CH * 16 / UVEC);       // column block
+        const int r = (pc % (CH * 16 / UVEC)) / (16 / UVEC), c = blk * 16 + (pc % (16 / UVEC)) * UVEC;
+        *reinterpret_cast<vec_t*>(slotE(SV) + r * LV + c) = upc[i];
+      }
       td.store(slotE(SDO), LV, nullptr, 0, ht);
     }
     if (tin) {
@@ -679,16 +693,13 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   const bool tload = p.t_in != nullptr;
   __syncthreads();
-  // h and dh' down this wave's value columns (the operands of P5), requested
-  // only now: every workgroup stages its tiles at about the same time, and the
-  // tiles arrive sooner without the states queued beside them
+  // dh' down this wave's value columns (the operand of P5), requested only
+  // now: every workgroup stages its tiles at about the same time, and the tiles
+  // arrive sooner without the state queued beside them
 #pragma unroll
   for (int nt = 0; nt < CTV; ++nt)
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) {
-      hk[nt][kb] = ld_frag8_st(hs, DK, n0 + 16 * nt + c16, 32 * kb);
-      dk_[nt][kb] = ld_frag8_st(dhs, DK, n0 + 16 * nt + c16, 32 * kb);
-    }
+    for (int kb = 0; kb < DK / 32; ++kb) dk_[nt][kb] = ld_frag8_st(dhs, DK, n0 + 16 * nt + c16, 32 * kb);
 
   // ---- P2: KD = strict_lower(K K^T * D), P = (Q K^T) * M  (20 lower tiles)
   for (int ti = w; ti < 20; ti += 8) {
@@ -727,44 +738,31 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) { rg[j] = zero4(); rb[j] = zero4(); }
 
-  // ---- P4: Ut = T diag(beta) V (own rows and value columns); then W = T diag(beta Gam) K -> slot V
-  Frag<E> vr[2][CTV];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int nt = 0; nt < CTV; ++nt) vr[kb][nt] = ld_fragC_q<E>(slotE(SV), LV, 32 * kb, n0 + 16 * nt);
-  f32x4 u[2][CTV];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int nt = 0; nt < CTV; ++nt) {
-      const int rt = 2 * rh + j;
-      u[j][nt] = zero4();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mma(u[j][nt], ld_frag_scaled<E>(sT, LA, 16 * rt + c16, 32 * kb, s.beta), vr[kb][nt]);
-    }
-  // the V entries of this wave's rows, for dbeta in P8
+  // ---- P4: the V entries of this wave's rows and value columns, for dbeta in
+  //          P10, from global (rows past the end are copies of the last one;
+  //          their dbeta is not stored): the k-slots of vown[nt] walk down
+  //          column n0 + 16 nt + lane%16 over rows 32 rh + 4g.., 32 rh + 16 + 4g..
   Frag<E> vown[CTV];
-#pragma unroll
-  for (int nt = 0; nt < CTV; ++nt) vown[nt] = rh ? vr[1][nt] : vr[0][nt];
-  __syncthreads();
   {
-    E* sW = slotE(SV);
-    for (int ti = w; ti < 4 * (DK / 16); ti += 8) {
-      const int rt = ti / (DK / 16), dt = ti % (DK / 16);
-      f32x4 acc = zero4();
+    const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        mma(acc, ld_frag_scaled<E>(sT, LA, 16 * rt + c16, 32 * kb, s.bg), ld_frag(sKT, LT, 16 * dt + c16, 32 * kb));
-      st_tile_rows<E>(sW, LK, 16 * rt, 16 * dt, acc);
-    }
+    for (int nt = 0; nt < CTV; ++nt) vown[nt] = ld_fragC_q_rows<E>(v, (int64_t)H * DV, 32 * rh, n0 + 16 * nt, rows);
   }
-  __syncthreads();
 
-  // ---- P5: U = Ut - W h, dU = diag(ek) K dh' + scale P^T dO (own rows and value columns)
+  // h and dh' down this wave's key columns (the operands of P6): requested now,
+  // in flight during P5, quad-transposed in P6
+  RawFrag<E> hraw[CTK][DV / 32], dhraw[CTK][DV / 32];
+#pragma unroll
+  for (int dt = 0; dt < CTK; ++dt)
+#pragma unroll
+    for (int kb = 0; kb < DV / 32; ++kb) {
+      hraw[dt][kb] = raw_fragC_q8_st<E>(hs, DK, 32 * kb, d0 + 16 * dt);
+      dhraw[dt][kb] = raw_fragC_q8_st<E>(dhs, DK, 32 * kb, d0 + 16 * dt);
+    }
+
+  // ---- P5: dU = diag(ek) K dh' + scale P^T dO (own rows and value columns)
   f32x4 du[2][CTV];
   {
-    const E* sW = slotE(SV);
 #pragma unroll
     for (int nt = 0; nt < CTV; ++nt) {
       Frag<E> dor[2];
@@ -773,13 +771,9 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int rt = 2 * rh + j;
-        f32x4 wh = zero4(), kd = zero4();
+        f32x4 kd = zero4();
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-          mma(wh, ld_frag8(sW, LK, 16 * rt + c16, 32 * kb), hk[nt][kb]);
-          mma(kd, ld_frag8(sK, LK, 16 * rt + c16, 32 * kb), dk_[nt][kb]);
-        }
-        u[j][nt] = u[j][nt] - wh;
+        for (int kb = 0; kb < DK / 32; ++kb) mma(kd, ld_frag8(sK, LK, 16 * rt + c16, 32 * kb), dk_[nt][kb]);
         kd = kd * *reinterpret_cast<const f32x4*>(&s.ek[16 * rt + 4 * g]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) mma(kd, ld_fragT<E>(sP, LA, 16 * rt + c16, 32 * kb, scale), dor[kb]);
@@ -787,17 +781,10 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       }
     }
   }
-  __syncthreads();  // W reads done: slot V becomes U
-  {
-    E* sU = slotE(SV);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int nt = 0; nt < CTV; ++nt) {
-        st_tile_rows<E>(sU, LV, 16 * (2 * rh + j), n0 + 16 * nt, u[j][nt]);
-        st_tile_rows<E>(sDU, LV, 16 * (2 * rh + j), n0 + 16 * nt, du[j][nt]);
-      }
-  }
+    for (int nt = 0; nt < CTV; ++nt) st_tile_rows<E>(sDU, LV, 16 * (2 * rh + j), n0 + 16 * nt, du[j][nt]);
   __syncthreads();
 
   // ---- P6: GW = -dU h^T, dQ1 = dO h^T, Udh = U dh'^T (own rows and key columns)
@@ -815,8 +802,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   for (int dt = 0; dt < CTK; ++dt)
 #pragma unroll
     for (int kb = 0; kb < DV / 32; ++kb) {
-      hn[dt][kb] = ld_fragC_q8_st<E>(hs, DK, 32 * kb, d0 + 16 * dt);
-      dhn[dt][kb] = ld_fragC_q8_st<E>(dhs, DK, 32 * kb, d0 + 16 * dt);
+      hn[dt][kb] = finish_frag(hraw[dt][kb]);
+      dhn[dt][kb] = finish_frag(dhraw[dt][kb]);
       // <h, dh'> over the whole state: the two row halves share each column group's part
       if ((kb & 1) == rh) hdh = frag_dot(hn[dt][kb], dhn[dt][kb], hdh);
     }

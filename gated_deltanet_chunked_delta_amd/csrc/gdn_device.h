@@ -24,6 +24,8 @@
 //   register operand: a pair of C tiles stacked along k.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 namespace gdn {
@@ -365,6 +367,41 @@ __device__ __forceinline__ Frag<float> ld_frag8_st(const float* base, int DK, in
   return f;
 }
 
+// ld_fragC_q8_st split in two: the loads (issued early, kept in flight) and the
+// quad transposes (once the data is needed).
+template <class E> struct RawFrag;
+template <> struct RawFrag<bf16> { uint32_t x0, x1, y0, y1; };
+template <> struct RawFrag<float> { f32x4 lo, hi; };
+template <class E>
+__device__ __forceinline__ RawFrag<E> raw_fragC_q8_st(const E* base, int DK, int k0, int col0) {
+  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+  const E* p = base + st_blk(k0 + 8 * g + b, col0 + 4 * q, DK);
+  RawFrag<E> r;
+  if constexpr (std::is_same<E, bf16>::value) {
+    typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+    const u32x2 x = *reinterpret_cast<const u32x2*>(p), y = *reinterpret_cast<const u32x2*>(p + DK * 4);
+    r.x0 = x[0]; r.x1 = x[1]; r.y0 = y[0]; r.y1 = y[1];
+  } else {
+    r.lo = *reinterpret_cast<const f32x4*>(p);
+    r.hi = *reinterpret_cast<const f32x4*>(p + DK * 4);
+  }
+  return r;
+}
+__device__ __forceinline__ Frag<bf16> finish_frag(RawFrag<bf16> r) {
+  typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+  quad_transpose16(r.x0, r.x1);
+  quad_transpose16(r.y0, r.y1);
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, u32x4{r.x0, r.x1, r.y0, r.y1});
+  return f;
+}
+__device__ __forceinline__ Frag<float> finish_frag(const RawFrag<float>& r) {
+  Frag<float> f;
+  f.lo = quad_transpose(r.lo);
+  f.hi = quad_transpose(r.hi);
+  return f;
+}
+
 // ld_fragC_q in the contiguous k-slot order (pairs with ld_frag8), from a
 // blocked chunk state: k-slots walk down key column
 // col0 + lane%16 (col0 a multiple of 16) over value rows k0 + 8g .. k0 + 8g + 7
@@ -394,6 +431,62 @@ __device__ __forceinline__ Frag<float> ld_fragC_q8_st<float>(const float* base, 
   f.lo = quad_transpose(*reinterpret_cast<const f32x4*>(p));
   f.hi = quad_transpose(*reinterpret_cast<const f32x4*>(p + DK * 4));
   return f;
+}
+
+// ld_fragC_q over rows of a global tile (row stride ld) of which only rows
+// [0, rows) exist: rows at or past the end read the last row instead.
+template <class E>
+__device__ __forceinline__ Frag<E> ld_fragC_q_rows(const E* base, int64_t ld, int k0, int col0, int rows);
+template <>
+__device__ __forceinline__ Frag<bf16> ld_fragC_q_rows<bf16>(const bf16* base, int64_t ld, int k0, int col0, int rows) {
+  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+  typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+  typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+  const int r0 = min(k0 + 4 * g + b, rows - 1), r1 = min(k0 + 16 + 4 * g + b, rows - 1);
+  u32x2 x = *reinterpret_cast<const u32x2*>(base + r0 * ld + col0 + 4 * q);
+  u32x2 y = *reinterpret_cast<const u32x2*>(base + r1 * ld + col0 + 4 * q);
+  uint32_t x0 = x[0], x1 = x[1], y0 = y[0], y1 = y[1];
+  quad_transpose16(x0, x1);
+  quad_transpose16(y0, y1);
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, u32x4{x0, x1, y0, y1});
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> ld_fragC_q_rows<float>(const float* base, int64_t ld, int k0, int col0,
+                                                              int rows) {
+  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+  const int r0 = min(k0 + 4 * g + b, rows - 1), r1 = min(k0 + 16 + 4 * g + b, rows - 1);
+  Frag<float> f;
+  f.lo = quad_transpose(*reinterpret_cast<const f32x4*>(base + r0 * ld + col0 + 4 * q));
+  f.hi = quad_transpose(*reinterpret_cast<const f32x4*>(base + r1 * ld + col0 + 4 * q));
+  return f;
+}
+
+// The inverse of ld_fragC_q: a fragment whose k-slots walk down column
+// col0 + lane%16 (rows k0+4g.., k0+16+4g..) stored into a row-major E matrix as
+// two quad-transposed 4-column row pieces.  All 64 lanes must take part.
+template <class E>
+__device__ __forceinline__ void st_fragC_q(E* base, int ld, int k0, int col0, const Frag<E>& f);
+template <>
+__device__ __forceinline__ void st_fragC_q<bf16>(bf16* base, int ld, int k0, int col0, const Frag<bf16>& f) {
+  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+  typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+  typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+  const u32x4 v = __builtin_bit_cast(u32x4, f.v);
+  uint32_t x0 = v[0], x1 = v[1], y0 = v[2], y1 = v[3];
+  quad_transpose16(x0, x1);
+  quad_transpose16(y0, y1);
+  bf16* p = base + (k0 + 4 * g + b) * ld + col0 + 4 * q;
+  *reinterpret_cast<u32x2*>(p) = u32x2{x0, x1};
+  *reinterpret_cast<u32x2*>(p + 16 * ld) = u32x2{y0, y1};
+}
+template <>
+__device__ __forceinline__ void st_fragC_q<float>(float* base, int ld, int k0, int col0, const Frag<float>& f) {
+  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+  float* p = base + (k0 + 4 * g + b) * ld + col0 + 4 * q;
+  *reinterpret_cast<f32x4*>(p) = quad_transpose(f.lo);
+  *reinterpret_cast<f32x4*>(p + 16 * ld) = quad_transpose(f.hi);
 }
 
 // Four fp32 values of a C-layout column piece -> E, quad-transposed into a row

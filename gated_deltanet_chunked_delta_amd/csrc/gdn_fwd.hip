@@ -230,7 +230,8 @@ template <int DV>
 struct FwdWaves { static constexpr int NW = DV == 128 ? 8 : 4; };
 
 // TLOAD: every chunk's T is read (p.t_in) instead of solved.
-template <class E, int DK, int DV, bool OUT, bool CORR, bool PREP, bool TLOAD>
+// USAVE: every chunk's U is written to p.us (CORR: its correction added).
+template <class E, int DK, int DV, bool OUT, bool CORR, bool PREP, bool TLOAD, bool USAVE>
 struct Chunk {
   static constexpr int NW = FwdWaves<DV>::NW;
   static constexpr int NT = NW * 64;
@@ -272,9 +273,11 @@ struct Chunk {
   // on exit).  Returns the chunk's log-bound Lambda_c.
   // t_in: this chunk's T when TLOAD; t_out: where to write the solved T
   // (nullable).
+  // us_chunk: where this chunk's U = Ut - W h goes (nullable; CORR adds its
+  // correction).
   __device__ static float step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows,
                                int64_t ntok0, int nrows, int h, E* hs_chunk, const float* t_in, float* t_out,
-                               f32x4 (&hacc)[DK / 16][NTW]) {
+                               E* us_chunk, f32x4 (&hacc)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA, LO = S::LO;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
@@ -494,12 +497,29 @@ struct Chunk {
     }
     __builtin_amdgcn_sched_barrier(0);
     sp = lds_opaque(sp);
+    // U out as DV/16 column blocks of [CH][16], each contiguous (a wave's
+    // stores fill whole lines; rows past the end are zero: beta = 0 there);
+    // the forward proper writes the rounded operand fragments it forms anyway
+    if (USAVE && (CORR || !OUT)) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          E* blk = us_chunk + (n0 + 16 * nt) * CH;
+          if (CORR) st_tile_rows_add<E>(blk, 16, 16 * rt, 0, u[rt][nt]);
+          else st_tile_rows<E>(blk, 16, 16 * rt, 0, u[rt][nt]);
+        }
+    }
     if (OUT) {
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         Frag<E> uf[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) pack_frag(uf[kb], u[2 * kb][nt], u[2 * kb + 1][nt]);
+        if (USAVE && !CORR) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) st_fragC_q<E>(us_chunk + (n0 + 16 * nt) * CH, 16, 32 * kb, 0, uf[kb]);
+        }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           f32x4 o = zero4();
@@ -588,7 +608,8 @@ struct Chunk {
       const size_t toff = ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
       const float* tin = TLOAD ? p.t_in + toff : nullptr;
       float* tout = (!TLOAD && p.t_out) ? p.t_out + toff : nullptr;
-      lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, tout, hacc);
+      E* usc = USAVE ? static_cast<E*>(p.us) + ((chunk0 + c) * p.H + h) * (size_t)(CH * DV) : nullptr;
+      lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, tout, usc, hacc);
     }
     if (done) *done = c - cb;
     return lam;
@@ -638,7 +659,7 @@ __device__ void init_smem(FwdSmem<E, DK, DV>& s) {
 }
 
 // Phase 1: every segment from zero (segment 0 from h0).
-template <class E, int DK, int DV, bool OUT, bool PREP, bool TLOAD>
+template <class E, int DK, int DV, bool OUT, bool PREP, bool TLOAD, bool USAVE>
 __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
@@ -648,7 +669,7 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p)
   f32x4 hacc[DK / 16][DV / (16 * FwdWaves<DV>::NW)];
   init_smem(s);
   load_state<E, DK, DV>(hacc, (sd.s == 0 && p.h0) ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-  const float lam = Chunk<E, DK, DV, OUT, false, PREP, TLOAD>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
+  const float lam = Chunk<E, DK, DV, OUT, false, PREP, TLOAD, USAVE>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
                                                       sd.c_begin, sd.c_end, h, hacc, nullptr);
   if (nseg == 1) {
     if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
@@ -659,7 +680,7 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p)
 }
 
 // Phase 3: boundary corrections (or the serial fallback).
-template <class E, int DK, int DV, bool OUT, bool PREP>
+template <class E, int DK, int DV, bool OUT, bool PREP, bool USAVE>
 __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p3(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
@@ -679,13 +700,14 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p3(FwdParams p)
   if (!ok) {
     // Gates do not decay fast enough to cut this sequence: one workgroup redoes it serially.
     load_state<E, DK, DV>(hacc, p.h0 ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-    Chunk<E, DK, DV, OUT, false, PREP, true>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc, nullptr);
+    Chunk<E, DK, DV, OUT, false, PREP, true, USAVE>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc,
+                                                          nullptr);
     if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
     return;
   }
   load_state<E, DK, DV>(hacc, p.bstate + ((size_t)(blockIdx.x - 1) * p.H + h) * SS);
   int done = 0;
-  Chunk<E, DK, DV, OUT, true, PREP, true>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done);
+  Chunk<E, DK, DV, OUT, true, PREP, true, USAVE>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done);
   if (sd.s == nseg - 1 && p.hT) {
     // hT = b_last + (the correction propagated through the whole last segment, if it got there)
     const float* b = p.bstate + ((size_t)blockIdx.x * p.H + h) * SS;
@@ -699,27 +721,33 @@ hipError_t launch_fwd_t(const FwdParams& p, int nseg_total, hipStream_t st) {
   const bool out = p.o != nullptr;
   const bool prep = p.prep.qk_norm || p.prep.gate_act;
   // phase 3 always reads T (written by phase 1); phase 1 reads it only in the
-  // replay, when the forward saved it
+  // replay, when the forward saved it.  The replay always writes U; the
+  // forward proper on request.
   if (p.phase != 1 && !p.t_in) return hipErrorInvalidValue;
   if (p.phase == 1 && out && p.t_in) return hipErrorInvalidValue;
-  const bool tl = p.t_in != nullptr;
+  if (!out && !p.us) return hipErrorInvalidValue;
+  const bool tl = p.t_in != nullptr, us = p.us != nullptr;
   if (p.phase == 1) {
     if (prep) {
-      if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true, false>), grid, block, 0, st, p);
-      else if (tl) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true, false>), grid, block, 0, st, p);
+      if (out && us) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true, false, true>), grid, block, 0, st, p);
+      else if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true, false, false>), grid, block, 0, st, p);
+      else if (tl) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true, true, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true, false, true>), grid, block, 0, st, p);
     } else {
-      if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false, false>), grid, block, 0, st, p);
-      else if (tl) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false, false>), grid, block, 0, st, p);
+      if (out && us) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false, false, true>), grid, block, 0, st, p);
+      else if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false, false, false>), grid, block, 0, st, p);
+      else if (tl) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false, true, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false, false, true>), grid, block, 0, st, p);
     }
   } else {
     if (prep) {
-      if (out) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, false, true>), grid, block, 0, st, p);
+      if (out && us) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, true, true>), grid, block, 0, st, p);
+      else if (out) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, true, false>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, false, true, true>), grid, block, 0, st, p);
     } else {
-      if (out) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, false>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, false, false>), grid, block, 0, st, p);
+      if (out && us) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, false, true>), grid, block, 0, st, p);
+      else if (out) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, false, false>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, false, false, true>), grid, block, 0, st, p);
     }
   }
   return hipGetLastError();

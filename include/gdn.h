@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum {
   GDN_OK = 0,
@@ -140,13 +140,20 @@ size_t gdn_chunk_fwd_workspace_size(const gdn_fwd_args* args);
 size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args);
 
 /* Bytes of the saved chunk states (h_save / h_saved) for these arguments:
- * C * H * Dk * Dv elements of the input dtype, C = sum over sequences of
- * ceil(len / 64).  State (c, h) is S (= h^T, Dv x Dk) at the start of chunk c
- * (chunks numbered sequence after sequence), rounded to the dtype, stored at
- * element offset (c * H + h) * Dk * Dv in 4 x 16 blocks: S[j][i] sits at
+ * C * H * (Dk * Dv + 64 * Dv) elements of the input dtype, C = sum over
+ * sequences of ceil(len / 64).  The first C * H * Dk * Dv elements are the
+ * states: state (c, h) is S (= h^T, Dv x Dk) at the start of chunk c (chunks
+ * numbered sequence after sequence), rounded to the dtype, stored at element
+ * offset (c * H + h) * Dk * Dv in 4 x 16 blocks: S[j][i] sits at
  *     ((j / 4) * (Dk / 16) + i / 16) * 64 + (j % 4) * 16 + i % 16
  * (each block row-major and contiguous, blocks in row-major order), so that
  * the state can be read both along and across its rows in whole cache lines.
+ * Then, at element offset C * H * Dk * Dv + (c * H + h) * 64 * Dv, each
+ * chunk's value residual U = T (diag(beta) V - diag(beta Gam) K h), 64 x Dv
+ * (h the chunk-start state, Gam_r = exp(G_r), T and G as for
+ * gdn_chunk_t_bytes; rows past a sequence's end are zero), stored as Dv / 16
+ * column blocks of 64 x 16, each row-major and contiguous: U[r][j] sits at
+ *     (j / 16) * 1024 + r * 16 + j % 16.
  * Returns 0 and sets the error string for invalid arguments (and returns 0
  * without error when there are no tokens). */
 size_t gdn_chunk_states_bytes(const gdn_common_args* a);

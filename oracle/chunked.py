@@ -61,6 +61,34 @@ def chunk_t(k, g, beta, cu_seqlens=None, C=64):
     return np.stack(out) if out else np.zeros((0, H, C, C))
 
 
+def chunk_u(k, v, g, beta, h0=None, cu_seqlens=None, C=64):
+    """Every chunk's U = Ut - W h of the lines above (h the state at the chunk
+    start), float64 [chunks, H, C, Dv], chunks numbered sequence after sequence;
+    a short last chunk's missing rows are zero."""
+    k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (k, v, g, beta))
+    B, T, H, Dk = k.shape
+    Dv = v.shape[-1]
+    cu = _cu(B, T, cu_seqlens)
+    kf, vf = k.reshape(B * T, H, Dk), v.reshape(B * T, H, Dv)
+    gf, bf = g.reshape(B * T, H), beta.reshape(B * T, H)
+    out = []
+    for n in range(len(cu) - 1):
+        hs = [np.zeros((Dk, Dv)) if h0 is None else np.array(h0[n, hh], dtype=np.float64) for hh in range(H)]
+        for t0 in range(cu[n], cu[n + 1], C):
+            t1 = min(t0 + C, cu[n + 1])
+            us = np.zeros((H, C, Dv))
+            for hh in range(H):
+                K, V = kf[t0:t1, hh], vf[t0:t1, hh]
+                gc, bc = gf[t0:t1, hh], bf[t0:t1, hh]
+                gam, Gam, Dm, A, Tm = _chunk_consts(K, gc, bc)
+                U = Tm @ (bc[:, None] * V) - Tm @ ((bc * Gam)[:, None] * K) @ hs[hh]
+                us[hh, :t1 - t0] = U
+                Kt = np.exp(gam[-1] - gam)[:, None] * K
+                hs[hh] = np.exp(gam[-1]) * hs[hh] + Kt.T @ U
+            out.append(us)
+    return np.stack(out) if out else np.zeros((0, H, C, Dv))
+
+
 def fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, C=64):
     """Chunked forward; returns (o, hT) in float64 (same shapes as ``ref.fwd``)."""
     q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))

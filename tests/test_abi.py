@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(L):
             "gdn_chunk_bwd_workspace_size", "gdn_last_error", "gdn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdn_abi_version() == 6
+    assert L.gdn_abi_version() == 7
 
 
 FAKE = 1 << 20  # a 16-byte aligned fake device address; never dereferenced
@@ -98,12 +98,13 @@ def test_backward_rejects_missing_gradients(L):
 def test_states_bytes(L):
     import numpy as np
     f = fwd_args()                                        # B=1, T=128, H=2, 128 x 128, bf16
-    assert L.gdn_chunk_states_bytes(ctypes.byref(f.a)) == 2 * 2 * 128 * 128 * 2
+    per = (128 * 128 + 64 * 128) * 2                      # state + U per chunk and head
+    assert L.gdn_chunk_states_bytes(ctypes.byref(f.a)) == 2 * 2 * per
     host = np.array([0, 1, 64, 65, 128], dtype=np.int32)  # lengths 1, 63, 1, 63: one chunk each
     f = fwd_args(cu_seqlens=FAKE, cu_seqlens_host=host.ctypes.data, num_seqs=4)
-    assert L.gdn_chunk_states_bytes(ctypes.byref(f.a)) == (1 + 1 + 1 + 1) * 2 * 128 * 128 * 2
+    assert L.gdn_chunk_states_bytes(ctypes.byref(f.a)) == (1 + 1 + 1 + 1) * 2 * per
     f = fwd_args(dtype=B.GDN_F32, Dk=64, Dv=64, T=129)
-    assert L.gdn_chunk_states_bytes(ctypes.byref(f.a)) == 3 * 2 * 64 * 64 * 4
+    assert L.gdn_chunk_states_bytes(ctypes.byref(f.a)) == 3 * 2 * (64 * 64 + 64 * 64) * 4
     assert L.gdn_chunk_states_bytes(ctypes.byref(fwd_args(Dk=96).a)) == 0
 
 

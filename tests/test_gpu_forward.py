@@ -127,7 +127,7 @@ def test_config_forward(dev, name):
 def test_saved_states_are_chunk_start_states(dev, dtype, Dk, Dv, cp):
     """Every saved state equals the oracle's state after the first 64 c tokens of
     its sequence (the initial state for c = 0), read back through the documented
-    block layout."""
+    block layout, and every saved U (after the states) the oracle's chunk U."""
     import torch
     from gated_deltanet_chunked_delta_amd import gdn_chunk_fwd
     from tests.helpers import unblock_states
@@ -155,6 +155,15 @@ def test_saved_states_are_chunk_start_states(dev, dtype, Dk, Dv, cp):
             assert err <= TOL[dtype], (n, j, err)
             c += 1
     assert c == C
+    from oracle import chunked
+    want_u = chunked.chunk_u(x.k, x.v, x.g, x.beta, x.h0, cu)
+    flat = to_np(states).astype(np.float64)
+    # [C, H, Dv/16, 64, 16] column blocks -> [C, H, 64, Dv]
+    got_u = flat[C * 2 * Dk * Dv:C * 2 * Dk * Dv + want_u.size].reshape(C, 2, Dv // 16, 64, 16)
+    got_u = got_u.transpose(0, 1, 3, 2, 4).reshape(want_u.shape)
+    err = relerr(got_u, want_u)
+    print(f"    U {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype,Dk,Dv,cp", [("bf16", 128, 128, 0), ("bf16", 64, 128, 3), ("f32", 64, 64, -1)])

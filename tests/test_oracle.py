@@ -271,3 +271,24 @@ def test_chunk_t_is_the_forward_chunk_matrix():
             assert relerr(Kt.T @ U, hT[0, hh]) < 1e-12
             assert np.array_equal(ts[c, hh, n:, n:], np.eye(C - n))
             assert not np.any(ts[c, hh, :n, n:]) and not np.any(ts[c, hh, n:, :n])
+
+
+def test_chunk_u_advances_the_recurrence():
+    """chunked.chunk_u gives, for every chunk, the state update of the token
+    recurrence: h_end = exp(G_last) h_start + K~^T U (h from ref.fwd on the
+    prefixes), with a nonzero initial state; short chunks are zero-padded."""
+    q, k, v, g, beta, h0 = rand_case(10, B=1, T=45, Dk=5, Dv=4)
+    C = 16
+    us = chunked.chunk_u(k, v, g, beta, h0, C=C)
+    assert us.shape == (3, 2, C, 4)
+    sl = lambda a, t: a[:, :t]
+    for c in range(3):
+        t0, t1 = C * c, min(C * c + C, 45)
+        h_start = h0 if t0 == 0 else ref.fwd(sl(q, t0), sl(k, t0), sl(v, t0), sl(g, t0), sl(beta, t0), 0.6, h0)[1]
+        h_end = ref.fwd(sl(q, t1), sl(k, t1), sl(v, t1), sl(g, t1), sl(beta, t1), 0.6, h0)[1]
+        for hh in range(2):
+            gam = np.cumsum(g[0, t0:t1, hh])
+            Kt = np.exp(gam[-1] - gam)[:, None] * k[0, t0:t1, hh]
+            want = np.exp(gam[-1]) * h_start[0, hh] + Kt.T @ us[c, hh, :t1 - t0]
+            assert relerr(want, h_end[0, hh]) < 1e-12
+        assert not np.any(us[c, :, t1 - t0:])
