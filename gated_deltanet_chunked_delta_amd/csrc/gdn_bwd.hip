@@ -142,15 +142,19 @@ struct RevChunk {
 
     // ---- 1. gradient at the chunk end out; tiles into LDS; scalars
     S* sp = lds_opaque(&s0);
-    // stored as S (Dv x Dk) in 4 x 16 blocks: the lane's four rows of one column are contiguous
+    // stored as S (Dv x Dk) in 4 x 16 blocks: the lane's four rows of one
+    // column are contiguous.  A correction adds to the stored gradient: it
+    // requests the current values here and writes the sums after phase 4 (dh
+    // in registers changes only in phase 5).
+    typedef E e4_t __attribute__((__vector_size__(4 * sizeof(E))));
+    e4_t hold[DK / 16][NTW];
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         E* dst = dhs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK);
-        f32x4 val = dh[t][nt];
-        if (CORR) val = val + ld4f<E>(dst);
-        st4f<E>(dst, val);
+        if (CORR) hold[t][nt] = *reinterpret_cast<const e4_t*>(dst);
+        else st4f<E>(dst, dh[t][nt]);
       }
     S& s1 = *sp;
     if (PREP && p.prep.qk_norm) ld.kq.normalize_rows(kq_tid());
@@ -317,6 +321,17 @@ struct RevChunk {
       }
     }
     __syncthreads();
+
+    if constexpr (CORR) {
+#pragma unroll
+      for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const e4_t o = hold[t][nt];
+          st4f<E>(dhs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK),
+                  dh[t][nt] + f32x4{to_f(o[0]), to_f(o[1]), to_f(o[2]), to_f(o[3])});
+        }
+    }
 
     // ---- 5. dU = diag(ek) K dh' + scale P^T dO ;  dh = Gam_C dh' + scale (Gam Q)^T dO - W^T dU
     f32x4 du[4][NTW];

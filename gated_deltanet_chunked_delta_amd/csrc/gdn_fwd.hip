@@ -291,6 +291,19 @@ struct Chunk {
 #pragma unroll
       for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
     }
+    // a correction adds to the stored U: its current pieces are requested now and
+    // consumed at the end of the chain (no load latency inside it)
+    typedef E e4_t __attribute__((__vector_size__(4 * sizeof(E))));
+    e4_t uold[4][NTW];
+    if constexpr (CORR && USAVE) {
+      const int q = (l >> 2) & 3, b = l & 3;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+          uold[rt][nt] = *reinterpret_cast<const e4_t*>(us_chunk + (n0 + 16 * nt) * CH + (16 * rt + 4 * g + b) * 16 +
+                                                        4 * q);
+    }
 
     // ---- 1. tiles into LDS, scalars, prefetch of the next chunk
     S* sp = lds_opaque(&s0);
@@ -311,16 +324,19 @@ struct Chunk {
       sp->lam[l] = gr;
       if (l == 0) sp->GamC = __expf(gC);
     }
+    // chunk-start state out, as S (Dv x Dk) in 4 x 16 blocks: the lane's four
+    // rows of one column are contiguous.  A correction adds to the stored
+    // state: it requests the current values here and writes the sums after
+    // phase 4 (the state in registers changes only in phase 5).
+    e4_t hold[DK / 16][NTW];
     if (hs_chunk) {
-      // stored as S (Dv x Dk) in 4 x 16 blocks: the lane's four rows of one column are contiguous
 #pragma unroll
       for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
           E* dst = hs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK);
-          f32x4 val = hacc[t][nt];
-          if (CORR) val = val + ld4f<E>(dst);
-          st4f<E>(dst, val);
+          if (CORR) hold[t][nt] = *reinterpret_cast<const e4_t*>(dst);
+          else st4f<E>(dst, hacc[t][nt]);
         }
     }
     __syncthreads();
@@ -479,6 +495,17 @@ struct Chunk {
     __syncthreads();
     sp = lds_opaque(sp);
 
+    if (CORR && hs_chunk) {
+#pragma unroll
+      for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const e4_t o = hold[t][nt];
+          st4f<E>(hs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK),
+                  hacc[t][nt] + f32x4{to_f(o[0]), to_f(o[1]), to_f(o[2]), to_f(o[3])});
+        }
+    }
+
     // ---- 5. state chain: U = Ut - W h ; O = scale (diag(Gam) Q h + P U) ; h' = Gam_C h + K^T (ek * U)
     Frag<E> hf[NTW][DK / 32];
 #pragma unroll
@@ -506,8 +533,14 @@ struct Chunk {
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
           E* blk = us_chunk + (n0 + 16 * nt) * CH;
-          if (CORR) st_tile_rows_add<E>(blk, 16, 16 * rt, 0, u[rt][nt]);
-          else st_tile_rows<E>(blk, 16, 16 * rt, 0, u[rt][nt]);
+          if constexpr (CORR) {
+            const int q = (l >> 2) & 3, b = l & 3;
+            const e4_t o = uold[rt][nt];
+            st4f<E>(blk + (16 * rt + 4 * g + b) * 16 + 4 * q,
+                    quad_transpose(u[rt][nt]) + f32x4{to_f(o[0]), to_f(o[1]), to_f(o[2]), to_f(o[3])});
+          } else {
+            st_tile_rows<E>(blk, 16, 16 * rt, 0, u[rt][nt]);
+          }
         }
     }
     if (OUT) {

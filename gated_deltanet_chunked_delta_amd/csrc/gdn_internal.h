@@ -35,7 +35,7 @@ struct FwdParams {
   float* bstate;           // [total segments][H][DK][DV] segment end states
   float* lam;              // [total segments][H] segment log-bounds
   void* hs;                // nullable: [total chunks][H] chunk start states S, Dv x Dk in st_blk order (dtype)
-  void* us;                // nullable: [total chunks][H][CH][DV] row-major U = Ut - W h of each chunk (dtype)
+  void* us;                // nullable: [total chunks][H][DV/16][CH][16] U = Ut - W h of each chunk in 16-column blocks (dtype)
   // [total chunks][H][CH][CH] fp32 row-major T = (I + diag(beta) A)^-1 of each chunk:
   const float* t_in;       // nullable: read instead of solved (replay and corrections only)
   float* t_out;            // nullable: written where solved (phase 1)
@@ -77,7 +77,7 @@ struct GradParams {
   const void* dout;
   const void* hs;          // chunk start states
   const void* dhs;         // chunk end state gradients
-  const void* us;          // each chunk's U = Ut - W h ([total chunks][H][CH][DV] row-major, dtype)
+  const void* us;          // each chunk's U = Ut - W h ([total chunks][H][DV/16][CH][16] column blocks, dtype)
   const float* t_in;       // nullable: chunk matrices T (as FwdParams), read instead of solved
   void* dq;
   void* dk;

@@ -239,15 +239,6 @@ __device__ __forceinline__ void st_tile_rows(E* base, int ld, int r0, int c0, co
   st4_transposed<E>(base + (r0 + 4 * g + b) * ld + c0 + 4 * q, acc);
 }
 
-// st_tile_rows that adds the tile to what the destination holds (fp32 sum,
-// rounded once).
-template <class E>
-__device__ __forceinline__ void st_tile_rows_add(E* base, int ld, int r0, int c0, const f32x4& acc) {
-  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
-  E* p = base + (r0 + 4 * g + b) * ld + c0 + 4 * q;
-  st4f<E>(p, quad_transpose(acc) + ld4f<E>(p));
-}
-
 // g / beta of one chunk for threads 0..63 (one row each), masked at use.
 template <class E>
 struct ScalarPart {
