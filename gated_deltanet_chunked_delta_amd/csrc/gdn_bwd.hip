@@ -569,6 +569,7 @@ struct alignas(16) GradSmem {
   alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH];
   float pg[4][CH], pb[4][CH];  // row sums of the per-wave dgam / dbeta terms, by column group
   float p7[4][CH], c7[4][CH];  // row sums of GP*P by column tile, column sums by row tile
+  float c9[2][CH];             // column sums of T * (dU V^T) by row half
   float c10[2][CH];            // column sums of GA*A by row half
   float pl[8], ph[8];
   float GamC;
@@ -752,17 +753,6 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   float lastsum = 0.f, hdh = 0.f;
 #pragma unroll
   for (int j = 0; j < 2; ++j) { rg[j] = zero4(); rb[j] = zero4(); }
-
-  // ---- P4: the V entries of this wave's rows and value columns, for dbeta in
-  //          P10, from global (rows past the end are copies of the last one;
-  //          their dbeta is not stored): the k-slots of vown[nt] walk down
-  //          column n0 + 16 nt + lane%16 over rows 32 rh + 4g.., 32 rh + 16 + 4g..
-  Frag<E> vown[CTV];
-  {
-    const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
-#pragma unroll
-    for (int nt = 0; nt < CTV; ++nt) vown[nt] = ld_fragC_q_rows<E>(v, (int64_t)H * DV, 32 * rh, n0 + 16 * nt, rows);
-  }
 
   // h and dh' down this wave's key columns (the operands of P6): requested now,
   // in flight during P5, quad-transposed in P6
@@ -965,10 +955,13 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   __syncthreads();
 
-  // ---- P9: GT = dU V^T diag(beta) + GW K^T diag(beta Gam) -> slot V (fp32)
+  // ---- P9: GT = dU V^T diag(beta) + GW K^T diag(beta Gam) -> slot V (fp32).
+  //          The dbeta term sum_c (T^T dU)[r][c] V[r][c] is the column sum
+  //          sum_i T[i][r] (dU V^T)[i][r], taken here from the first product.
   {
     float* sGT = slotF(SV);
     const int c = 16 * cw + c16;
+    float tm = 0.f;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int rt = rh + 2 * j;
@@ -980,8 +973,15 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         mma(b, ld_frag(slotE(SQ), LK, 16 * rt + c16, 32 * kb), ld_frag(sK, LK, c, 32 * kb));
       // U (slot V) is no longer read: every wave finished P7 before the barrier above
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sGT[(16 * rt + 4 * g + i) * LA + c] = s.beta[c] * a[i] + s.bg[c] * b[i];
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        sGT[r * LA + c] = s.beta[c] * a[i] + s.bg[c] * b[i];
+        tm += sT[r * LA + c] * a[i];
+      }
     }
+    tm += __shfl_xor(tm, 16, 64);
+    tm += __shfl_xor(tm, 32, 64);
+    if (g == 0) s.c9[rh][c] = tm;
   }
   __syncthreads();
 
@@ -1013,8 +1013,6 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) mma(xu, tte[j][kb], duf[kb]);
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s.beta[16 * rt + 4 * g]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rb[j][i] += xu[i] * frag_at(vown[nt], 4 * j + i);
         st_tile_rows<E>(sDV, LV, 16 * rt, n0 + 16 * nt, xu * b4);
       }
     }
@@ -1131,7 +1129,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   if (w == 0) {
     const int r = l;
-    float dgm = s.c10[0][r] + s.c10[1][r], db = 0.f;
+    float dgm = s.c10[0][r] + s.c10[1][r], db = s.c9[0][r] + s.c9[1][r];
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
       dgm += s.pg[ww][r] + s.p7[ww][r] + s.c7[ww][r];

@@ -433,36 +433,6 @@ __device__ __forceinline__ Frag<float> ld_fragC_q8_st<float>(const float* base, 
   return f;
 }
 
-// ld_fragC_q over rows of a global tile (row stride ld) of which only rows
-// [0, rows) exist: rows at or past the end read the last row instead.
-template <class E>
-__device__ __forceinline__ Frag<E> ld_fragC_q_rows(const E* base, int64_t ld, int k0, int col0, int rows);
-template <>
-__device__ __forceinline__ Frag<bf16> ld_fragC_q_rows<bf16>(const bf16* base, int64_t ld, int k0, int col0, int rows) {
-  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
-  typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
-  typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
-  const int r0 = min(k0 + 4 * g + b, rows - 1), r1 = min(k0 + 16 + 4 * g + b, rows - 1);
-  u32x2 x = *reinterpret_cast<const u32x2*>(base + r0 * ld + col0 + 4 * q);
-  u32x2 y = *reinterpret_cast<const u32x2*>(base + r1 * ld + col0 + 4 * q);
-  uint32_t x0 = x[0], x1 = x[1], y0 = y[0], y1 = y[1];
-  quad_transpose16(x0, x1);
-  quad_transpose16(y0, y1);
-  Frag<bf16> f;
-  f.v = __builtin_bit_cast(bf16x8, u32x4{x0, x1, y0, y1});
-  return f;
-}
-template <>
-__device__ __forceinline__ Frag<float> ld_fragC_q_rows<float>(const float* base, int64_t ld, int k0, int col0,
-                                                              int rows) {
-  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
-  const int r0 = min(k0 + 4 * g + b, rows - 1), r1 = min(k0 + 16 + 4 * g + b, rows - 1);
-  Frag<float> f;
-  f.lo = quad_transpose(*reinterpret_cast<const f32x4*>(base + r0 * ld + col0 + 4 * q));
-  f.hi = quad_transpose(*reinterpret_cast<const f32x4*>(base + r1 * ld + col0 + 4 * q));
-  return f;
-}
-
 // The inverse of ld_fragC_q: a fragment whose k-slots walk down column
 // col0 + lane%16 (rows k0+4g.., k0+16+4g..) stored into a row-major E matrix as
 // two quad-transposed 4-column row pieces.  All 64 lanes must take part.
