@@ -590,6 +590,12 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   constexpr int NT = 512;
   constexpr int LK = L::LK, LV = L::LV, LT = L::LT, LA = L::LA;
   constexpr int CTK = DK / 64, CTV = DV / 64;  // 16-wide column tiles per column group
+  // P5 (dU) partition: with at least eight 16-wide value tiles every wave takes
+  // its own value tiles over all four row tiles, so no two waves request the
+  // same dh' fragments; otherwise the column group / row half split of the
+  // other products
+  constexpr bool P5ALL = (DV / 16) % 8 == 0;
+  constexpr int P5C = P5ALL ? DV / 128 : CTV, P5R = P5ALL ? 4 : 2;
   __shared__ GradSmem<E, DK, DV> s;
   auto slotE = [&](int i) { return reinterpret_cast<E*>(s.slot[i]); };
   auto slotF = [&](int i) { return reinterpret_cast<float*>(s.slot[i]); };
@@ -606,6 +612,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   const E* hs = static_cast<const E*>(p.hs) + ((size_t)blockIdx.x * H + h) * SS;
   const E* dhs = static_cast<const E*>(p.dhs) + ((size_t)blockIdx.x * H + h) * SS;
   const int d0 = cw * (DK / 4), n0 = cw * (DV / 4);
+  const int p5n0 = P5ALL ? w * (DV / 8) : n0, p5r0 = P5ALL ? 0 : 2 * rh;
   const float scale = p.scale;
 
   E* sK = slotE(SK);
@@ -621,7 +628,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   //          requested after the tiles have landed and stays in flight until
   //          P5; its products use the contiguous k-slot order (one 16-byte
   //          read per fragment).
-  Frag<E> dk_[CTV][DK / 32];
+  Frag<E> dk_[P5C][DK / 32];
   {
     const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
     const E* k = static_cast<const E*>(p.k) + (tok0 * H + h) * DK;
@@ -709,13 +716,13 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   const bool tload = p.t_in != nullptr;
   __syncthreads();
-  // dh' down this wave's value columns (the operand of P5), requested only
-  // now: every workgroup stages its tiles at about the same time, and the tiles
-  // arrive sooner without the state queued beside them
+  // dh' down this wave's P5 value columns, requested only now: every
+  // workgroup stages its tiles at about the same time, and the tiles arrive
+  // sooner without the state queued beside them
 #pragma unroll
-  for (int nt = 0; nt < CTV; ++nt)
+  for (int nt = 0; nt < P5C; ++nt)
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) dk_[nt][kb] = ld_frag8_st(dhs, DK, n0 + 16 * nt + c16, 32 * kb);
+    for (int kb = 0; kb < DK / 32; ++kb) dk_[nt][kb] = ld_frag8_st(dhs, DK, p5n0 + 16 * nt + c16, 32 * kb);
 
   // ---- P2: KD = strict_lower(K K^T * D), P = (Q K^T) * M  (20 lower tiles)
   for (int ti = w; ti < 20; ti += 8) {
@@ -765,17 +772,17 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       dhraw[dt][kb] = raw_fragC_q8_st<E>(dhs, DK, 32 * kb, d0 + 16 * dt);
     }
 
-  // ---- P5: dU = diag(ek) K dh' + scale P^T dO (own rows and value columns)
-  f32x4 du[2][CTV];
+  // ---- P5: dU = diag(ek) K dh' + scale P^T dO (P5 rows and value columns)
+  f32x4 du[P5R][P5C];
   {
 #pragma unroll
-    for (int nt = 0; nt < CTV; ++nt) {
+    for (int nt = 0; nt < P5C; ++nt) {
       Frag<E> dor[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) dor[kb] = ld_fragC_q<E>(slotE(SDO), LV, 32 * kb, n0 + 16 * nt);
+      for (int kb = 0; kb < 2; ++kb) dor[kb] = ld_fragC_q<E>(slotE(SDO), LV, 32 * kb, p5n0 + 16 * nt);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int rt = 2 * rh + j;
+      for (int j = 0; j < P5R; ++j) {
+        const int rt = p5r0 + j;
         f32x4 kd = zero4();
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) mma(kd, ld_frag8(sK, LK, 16 * rt + c16, 32 * kb), dk_[nt][kb]);
@@ -787,9 +794,9 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     }
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < P5R; ++j)
 #pragma unroll
-    for (int nt = 0; nt < CTV; ++nt) st_tile_rows<E>(sDU, LV, 16 * (2 * rh + j), n0 + 16 * nt, du[j][nt]);
+    for (int nt = 0; nt < P5C; ++nt) st_tile_rows<E>(sDU, LV, 16 * (p5r0 + j), p5n0 + 16 * nt, du[j][nt]);
   __syncthreads();
 
   // ---- P6: GW = -dU h^T, dQ1 = dO h^T, Udh = U dh'^T (own rows and key columns)
