@@ -198,6 +198,9 @@ def main():
                     help="the forward keeps the chunk states and the backward reads them (no replay)")
     ap.add_argument("--no-save-t", action="store_true",
                     help="the forward does not keep the chunk matrices T; the backward solves for them")
+    ap.add_argument("--api", default="abi", choices=["abi", "fla"],
+                    help="abi: the library's entry points; fla: the FLA-convention autograd entry "
+                         "(fla_compat.chunk_gated_delta_rule forward + torch.autograd.grad)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy (out = x * 1, fp32) of this many MiB three "
@@ -252,7 +255,19 @@ def main():
     keep = False
     save_t = not args.no_save_t and args.direction == "fwdbwd"
 
+    if args.api == "fla":
+        if args.direction != "fwdbwd" or args.prep or args.no_save_t:
+            sys.exit("--api fla times the forward + backward of the default workload only")
+        from gated_deltanet_chunked_delta_amd.fla_compat import chunk_gated_delta_rule as fla_entry
+        leaves = [a.detach().requires_grad_(True) for a in (q, k, v, g, beta)]
+
+    def step_fla():
+        o, _ = fla_entry(*leaves, scale=x.scale, cu_seqlens=cu)
+        torch.autograd.grad([o], leaves, [do])
+
     def step():
+        if args.api == "fla":
+            return step_fla()
         states = chunk_t = None
         if args.direction in ("fwdbwd", "fwd"):
             res = gb.gdn_chunk_fwd(q, k, v, g, beta, x.scale, h0=h0, cu_seqlens=cu, cu_seqlens_host=host,
@@ -291,7 +306,7 @@ def main():
     ms, prof = timed_run(True)
     log(f"timed {args.steps} steps")
     variant = None
-    if args.direction == "fwdbwd" and not args.save_states:
+    if args.direction == "fwdbwd" and not args.save_states and args.api == "abi":
         keep = True
         ms_v, _ = timed_run(False)
         keep = False
@@ -331,7 +346,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": CH,
                    "direction": args.direction, "cp_mode": args.cp_mode, "tokens_per_step": ntok,
-                   "states": "saved by fwd" if args.save_states else "recomputed in bwd",
+                   "states": "saved by fwd" if (args.save_states or args.api == "fla") else "recomputed in bwd",
+                   "api": "fla_compat autograd" if args.api == "fla" else "C ABI",
                    "chunk_T": "saved by fwd" if save_t else "solved in bwd",
                    "preprocessing": "in-kernel q/k L2 norm + gate/beta activation" if args.prep else "none"},
         "tflops": tflops, "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
