@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
 OBJ = os.path.join(HERE, "_build")
-SOURCES = ["gdn_api.hip", "gdn_plan.hip", "gdn_fwd.hip", "gdn_bwd.hip", "gdn_decode.hip"]
+SOURCES = ["gdn_api.hip", "gdn_plan.hip", "gdn_tsolve.hip", "gdn_fwd.hip", "gdn_bwd.hip", "gdn_decode.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INC, "-I", CSRC,

@@ -116,7 +116,7 @@ gdn::PrepParams prep_of(int qk_norm, int gate_act, const float* gate_scale) {
 // Segment length, totals and workspace layout.  `bwd` adds the backward's arrays
 // (without the chunk states when the caller provides them: `saved`).  `t_given`:
 // the caller provides (forward: takes) the chunk matrices T, which otherwise live
-// in the workspace (the forward needs them only to correct segments).
+// in the workspace (solved first, read by every later kernel).
 Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false, bool t_given = false) {
   Plan p;
   p.N = a.num_seqs;
@@ -160,7 +160,7 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false, 
     p.o_lam = take(sizeof(float) * (size_t)p.nseg * a.H);
   }
   const size_t tbytes = sizeof(float) * CHUNK * CHUNK * (size_t)std::max(1, p.nchunk) * a.H;
-  if (!bwd && p.cp && !t_given) p.o_ts = take(tbytes);
+  if (!bwd && !t_given) p.o_ts = take(tbytes);
   if (bwd) {
     if (p.cp) {
       p.o_bstate2 = take(sizeof(float) * SS * p.nseg * a.H);
@@ -170,8 +170,7 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false, 
       p.o_hs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
       p.o_us = take(esz * CHUNK * (size_t)a.Dv * std::max(1, p.nchunk) * a.H);
     }
-    // the chunk matrices T, solved once (by the replay, else by the reverse
-    // chain) and read by the later kernels
+    // the chunk matrices T, solved once and read by the later kernels
     if (!t_given) p.o_ts = take(tbytes);
     p.o_dhs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
   }
@@ -345,14 +344,22 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   p.hs = args->h_save;  // nullable: the chunk states (and U) are stored only on request
   p.us = args->h_save ? static_cast<char*>(args->h_save) + states_part_bytes(a) : nullptr;
   p.prep = prep_of(a.qk_norm, a.gate_act, a.gate_scale);
-  // T: for the caller, or for the segment corrections (which read it back)
-  p.t_out = args->t_save ? args->t_save : (pl.cp ? at<float>(ws, pl.o_ts) : nullptr);
+  // every chunk's T, solved chunk-parallel (into the caller's buffer when it
+  // keeps T) and read by the chunk chain and the segment corrections
+  float* ts = args->t_save ? args->t_save : at<float>(ws, pl.o_ts);
+  if (pl.nchunk > 0) {
+    gdn::TSolveParams tp{};
+    tp.k = a.k; tp.g = a.g; tp.beta = a.beta; tp.t_out = ts; tp.H = a.H; tp.seq = sq;
+    tp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);
+    tp.prep = p.prep;
+    e = timed("tsolve", s, [&] { return gdn::launch_tsolve(a.dtype, a.Dk, tp, pl.nchunk, s); });
+    if (e != hipSuccess) return hip_fail(e, "T solve launch");
+  }
+  p.t_in = ts;
   p.phase = 1;
   e = timed("fwd", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   if (pl.cp) {
-    p.t_in = p.t_out;
-    p.t_out = nullptr;
     p.phase = 3;
     e = timed("fwd_corr", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
     if (e != hipSuccess) return hip_fail(e, "forward correction launch");
@@ -399,23 +406,27 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   p.chunk_first = at<int>(ws, pl.o_chunk_first);
   p.bstate = pl.cp ? at<float>(ws, pl.o_bstate) : nullptr;
   p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
-  // chunk matrices T: the caller's, else solved by the first kernel over the
-  // chunks (the replay, or without it the reverse chain) and read by the later ones
+  // chunk matrices T: the caller's, else solved chunk-parallel here (the same
+  // kernel as the forward's, so the same values); every later kernel reads them
   const float* ts = t_given ? args->t_saved : at<float>(ws, pl.o_ts);
-  const bool replay = !saved;
+  if (!t_given && pl.nchunk > 0) {
+    gdn::TSolveParams tp{};
+    tp.k = a.k; tp.g = a.g; tp.beta = a.beta; tp.t_out = at<float>(ws, pl.o_ts); tp.H = a.H; tp.seq = sq;
+    tp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);
+    tp.prep = p.prep;
+    e = timed("tsolve", s, [&] { return gdn::launch_tsolve(a.dtype, a.Dk, tp, pl.nchunk, s); });
+    if (e != hipSuccess) return hip_fail(e, "T solve launch");
+  }
+  p.t_in = ts;
   if (saved) {
     p.hs = const_cast<void*>(args->h_saved);
     p.us = static_cast<char*>(const_cast<void*>(args->h_saved)) + states_part_bytes(a);
   } else {
     p.hs = at<void>(ws, pl.o_hs);
     p.us = at<void>(ws, pl.o_us);
-    if (t_given) p.t_in = ts;
-    else p.t_out = at<float>(ws, pl.o_ts);
     p.phase = 1;
     e = timed("replay", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
     if (e != hipSuccess) return hip_fail(e, "replay launch");
-    p.t_out = nullptr;
-    p.t_in = ts;
     if (pl.cp) {
       p.phase = 3;
       e = timed("replay_corr", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
@@ -430,15 +441,11 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   r.bstate = pl.cp ? at<float>(ws, pl.o_bstate2) : nullptr;
   r.lam = pl.cp ? at<float>(ws, pl.o_lam2) : nullptr;
   r.dhs = at<void>(ws, pl.o_dhs);
-  const bool rev_solves = !replay && !t_given;
-  r.t_in = rev_solves ? nullptr : ts;
-  r.t_out = rev_solves ? at<float>(ws, pl.o_ts) : nullptr;
+  r.t_in = ts;
   r.prep = p.prep;
   r.phase = 1;
   e = timed("rev", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "reverse launch");
-  r.t_in = ts;
-  r.t_out = nullptr;
   if (pl.cp) {
     r.phase = 3;
     e = timed("rev_corr", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });

@@ -59,7 +59,6 @@ struct alignas(16) RevSmem {
   E DOT[DV * LT];  // dO^T, Y of P^T dO and (Gam Q)^T dO
   E WT[DK * LT];   // -W^T
   E PT[CH * LT];   // scale * P^T
-  float A[CH * LA];
   float T[CH * LA];
   alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], lam[CH], sGam[CH];
   float GamC;
@@ -73,8 +72,8 @@ struct RevWaves { static constexpr int NW = DV == 128 ? 8 : 4; };
 // One chunk of the reverse chain (wave w owns Dv/NW columns of the state
 // gradient).  CORR: propagation of a boundary difference only (dO does not
 // enter, stored gradients are incremented).
-// TLOAD: every chunk's T is read (p.t_in) instead of solved.
-template <class E, int DK, int DV, bool CORR, bool PREP, bool TLOAD>
+// Every chunk's T is read from p.t_in (solved chunk-parallel beforehand).
+template <class E, int DK, int DV, bool CORR, bool PREP>
 struct RevChunk {
   static constexpr int NW = RevWaves<DV>::NW, NT = 64 * NW, NTW = DV / (16 * NW);
   using S = RevSmem<E, DK, DV>;
@@ -99,13 +98,14 @@ struct RevChunk {
     ld.sc.load(p.g, static_cast<const E*>(p.beta), tok0, H, h, rows);
   }
 
-  // One lower 16x16 tile (rt, ct) of A = strict_lower(diag(beta) (K K^T) * D)
-  // (ISQ false; the diagonal tile also adds the log-bound terms) or of
-  // scale P^T, P = (Q K^T) * M with the rows past the sequence end masked (ISQ true).
+  // ISQ false: the diagonal 16x16 tile rt = ct of K K^T, whose diagonal gives
+  // the log-bound terms log max(1, |1 - beta |k|^2|); ISQ true: one lower tile
+  // (rt, ct) of scale P^T, P = (Q K^T) * M with the rows past the sequence end
+  // masked.
   template <bool ISQ>
   __device__ __forceinline__ static void kk_tile(S* sp, const RevParams& p, int rt, int ct, int g, int c16,
                                                  int rows) {
-    constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
+    constexpr int LQ = S::LQ, LT = S::LT;
     const E* X = ISQ ? sp->Q : sp->K;
     f32x4 acc = zero4();
 #pragma unroll
@@ -120,7 +120,6 @@ struct RevChunk {
       const int r = 16 * rt + 4 * g + i;
       const float dm = __expf(gr4[i] - gc);
       if (!ISQ) {
-        sp->A[r * LA + c] = (c < r) ? br4[i] * acc[i] * dm : 0.f;
         if (r == c) sp->lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
       } else {
         sp->PT[c * LT + r] = to_e<E>((c <= r && r < rows) ? p.scale * acc[i] * dm : 0.f);
@@ -130,15 +129,13 @@ struct RevChunk {
 
   // dh: gradient at the chunk end on entry, at the chunk start on exit.
   // Prefetches chunk (ntok0, nrows) into ld (nrows = 0: none).  Returns Lambda_c.
-  // t_in: this chunk's T when TLOAD; t_out: where to write the solved T
-  // (nullable).
+  // t_in: this chunk's T.
   __device__ static float step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows,
-                               int h, E* dhs_chunk, const float* t_in, float* t_out, f32x4 (&dh)[DK / 16][NTW]) {
+                               int h, E* dhs_chunk, const float* t_in, f32x4 (&dh)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
     const int n0 = w * (DV / NW);
-    constexpr bool tload = TLOAD;
 
     // ---- 1. gradient at the chunk end out; tiles into LDS; scalars
     S* sp = lds_opaque(&s0);
@@ -181,39 +178,26 @@ struct RevChunk {
     }
     __syncthreads();
 
-    // ---- 2. K K^T -> A + diagonal blocks of T; Q K^T -> scale P^T.  Four waves:
-    //         row-tile pairs {0, 3} / {1, 2} (waves 0, 1: A; 2, 3: P^T).  Eight waves:
-    //         wave r < 4 forms the diagonal tile A_rr and solves block r of T at once
-    //         (the critical path); waves 4..7 share the six off-diagonal tiles of A
-    //         and the ten of P^T.
-    // T (when given) is requested now, past the staging, and lands in LDS at the
-    // end of this phase
+    // ---- 2. the diagonal tiles of K K^T (log-bound); Q K^T -> scale P^T.  Eight
+    //         waves: wave r < 4 forms K K^T's tile r; P^T tile j goes to wave
+    //         (j + 4) % 8 (at most two tiles a wave).  Four waves: waves 0, 1 take
+    //         the diagonal tiles of row tiles {0, 3} and {1, 2}, waves 2, 3 the rows
+    //         of P^T for those row tiles.
+    // T is requested now, past the staging, and lands in LDS at the end of
+    // this phase
     f32x4 tv[TPT];
-    if (tload) {
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
-    }
+    for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
     if constexpr (NW == 8) {
       S* sq = lds_opaque(&s0);
-      if (w < 4) {
-        // (with T given, the diagonal tiles are still formed for the log-bound)
-        kk_tile<false>(sq, p, w, w, g, c16, rows);
-        if (!tload) solve_diag_pair(sq->A, sq->T, w, w, nullptr);
-      } else {
-        const int wq = w - 4;
+      if (w < 4) kk_tile<false>(sq, p, w, w, g, c16, rows);
+      if (!CORR) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int id = wq + 4 * j;  // 0..5: A tiles below the diagonal, 6..15: P^T tiles
-          if (id < 6) {
-            const int rt = id < 1 ? 1 : (id < 3 ? 2 : 3);
-            const int ct = id - (rt * (rt - 1)) / 2;
-            if (!tload) kk_tile<false>(sq, p, rt, ct, g, c16, rows);
-          } else if (!CORR) {
-            const int pid = id - 6;
-            const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
-            const int ct = pid - (rt * (rt + 1)) / 2;
-            kk_tile<true>(sq, p, rt, ct, g, c16, rows);
-          }
+        for (int j = 0; j < 2; ++j) {
+          const int pid = ((w + 4) & 7) + 8 * j;
+          const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
+          const int ct = pid - (rt * (rt + 1)) / 2;
+          if (pid < 10) kk_tile<true>(sq, p, rt, ct, g, c16, rows);
         }
       }
     }
@@ -231,6 +215,7 @@ struct RevChunk {
           const f32x4 br4 = *reinterpret_cast<const f32x4*>(&s.beta[16 * RT + 4 * g]);
 #pragma unroll
           for (int ct = 0; ct <= RT; ++ct) {
+            if (!isq && ct != RT) continue;  // K K^T: the diagonal tile only
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb) mma(acc, xa[kb], ld_frag(s.K, LQ, 16 * ct + c16, 32 * kb));
@@ -241,8 +226,7 @@ struct RevChunk {
               const int r = 16 * RT + 4 * g + i;
               const float dm = __expf(gr4[i] - gc);
               if (!isq) {
-                s.A[r * LA + c] = (c < r) ? br4[i] * acc[i] * dm : 0.f;
-                if (ct == RT && r == c) s.lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
+                if (r == c) s.lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
               } else {
                 s.PT[c * LT + r] = to_e<E>((c <= r && r < rows) ? p.scale * acc[i] * dm : 0.f);
               }
@@ -255,41 +239,19 @@ struct RevChunk {
           const bool rows03 = (w & 1) == 0;
           if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
           else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
-          if (!isq && !tload) solve_diag_pair(s.A, s.T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
         }
       }
-      if (tload) {
 #pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-          const int e = 4 * (tid + i * NT);
-          *reinterpret_cast<f32x4*>(&s.T[(e / CH) * LA + e % CH]) = tv[i];
-        }
+      for (int i = 0; i < TPT; ++i) {
+        const int e = 4 * (tid + i * NT);
+        *reinterpret_cast<f32x4*>(&s.T[(e / CH) * LA + e % CH]) = tv[i];
       }
     }
     __syncthreads();
     const float lam_c = __shfl(wave_sum(lds_opaque(&s0)->lam[l]), 0, 64);
 
-    // ---- 3. off-diagonal blocks of T (when solved here), T out.  The next
-    //         chunk's tiles start their way from HBM after the T store, so that
-    //         nothing below waits behind them.
-    if constexpr (tload) {
-      if (nrows > 0) issue(ld, p, ntok0, nrows, h);
-    } else {
-      {
-        S& s = *lds_opaque(&s0);
-        solve_columns(s.A, s.T, w, nullptr);
-      }
-      __syncthreads();
-      if (t_out) {
-        const S& s = *lds_opaque(&s0);
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-          const int e = 4 * (tid + i * NT);
-          *reinterpret_cast<f32x4*>(t_out + e) = *reinterpret_cast<const f32x4*>(&s.T[(e / CH) * LA + e % CH]);
-        }
-      }
-      if (nrows > 0) issue(ld, p, ntok0, nrows, h);
-    }
+    // ---- 3. the next chunk's tiles start their way from HBM
+    if (nrows > 0) issue(ld, p, ntok0, nrows, h);
 
     // ---- 4. -W^T = -K^T diag(beta Gam) T^T: (Dk/16) x 4 tiles, KTW key tiles x
     //         RTW chunk-row tiles per wave
@@ -413,9 +375,7 @@ struct RevChunk {
       const int64_t ntok0 = seq0 + (int64_t)(c - 1) * CH;
       const int nrows = more ? min(CH, len - (c - 1) * CH) : 0;
       const size_t toff = ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
-      const float* tin = TLOAD ? p.t_in + toff : nullptr;
-      float* tout = (!CORR && !TLOAD && p.t_out) ? p.t_out + toff : nullptr;
-      lam += step(s, p, ld, rows, ntok0, nrows, h, dhs + ((chunk0 + c) * p.H + h) * SS, tin, tout, dh);
+      lam += step(s, p, ld, rows, ntok0, nrows, h, dhs + ((chunk0 + c) * p.H + h) * SS, p.t_in + toff, dh);
     }
     if (lowest) *lowest = c + 1;
     return lam;
@@ -462,7 +422,7 @@ __device__ void rev_init_smem(RevSmem<E, DK, DV>& s) {
 }
 
 // Phase 1: every segment from dh' = 0 (the last segment of a sequence from dhT).
-template <class E, int DK, int DV, bool PREP, bool TLOAD>
+template <class E, int DK, int DV, bool PREP>
 __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p1(RevParams p) {
   __shared__ RevSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
@@ -473,7 +433,7 @@ __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p1(RevParams p)
   f32x4 dh[DK / 16][DV / (16 * RevWaves<DV>::NW)];
   rev_init_smem(s);
   rev_load<E, DK, DV>(dh, sd.s == nseg - 1 ? dhT : nullptr);
-  const float lam = RevChunk<E, DK, DV, false, PREP, TLOAD>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
+  const float lam = RevChunk<E, DK, DV, false, PREP>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
                                                     sd.c_begin, sd.c_end, h, dh, nullptr);
   if (nseg == 1) {
     if (p.dh0) rev_store<E, DK, DV>(dh, p.dh0 + ((size_t)n * p.H + h) * SS, nullptr, true);
@@ -505,13 +465,13 @@ __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p3(RevParams p)
   rev_init_smem(s);
   if (!ok) {
     rev_load<E, DK, DV>(dh, p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr);
-    RevChunk<E, DK, DV, false, PREP, true>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, dh, nullptr);
+    RevChunk<E, DK, DV, false, PREP>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, dh, nullptr);
     if (dh0) rev_store<E, DK, DV>(dh, dh0, nullptr, true);
     return;
   }
   rev_load<E, DK, DV>(dh, p.bstate + ((size_t)(blockIdx.x + 1) * p.H + h) * SS);
   int lowest = sd.c_end;
-  RevChunk<E, DK, DV, true, PREP, true>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, dh, &lowest);
+  RevChunk<E, DK, DV, true, PREP>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, dh, &lowest);
   if (sd.s == 0 && dh0)
     rev_store<E, DK, DV>(dh, dh0, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, lowest == sd.c_begin);
 }
@@ -520,17 +480,14 @@ template <class E, int DK, int DV>
 hipError_t launch_rev_t(const RevParams& p, int nseg_total, hipStream_t st) {
   const dim3 block(64 * RevWaves<DV>::NW);
   const dim3 grid(nseg_total, p.H);
-  // phase 3 always reads T (written by the replay or by phase 1)
-  if (p.phase != 1 && !p.t_in) return hipErrorInvalidValue;
-  const bool tl = p.t_in != nullptr;
+  // every phase reads T (solved beforehand)
+  if (!p.t_in) return hipErrorInvalidValue;
   if (p.prep.qk_norm || p.prep.gate_act) {
     if (p.phase != 1) hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV, true>), grid, block, 0, st, p);
-    else if (tl) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, true, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, true, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, true>), grid, block, 0, st, p);
   } else {
     if (p.phase != 1) hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV, false>), grid, block, 0, st, p);
-    else if (tl) hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, false, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, false, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, false>), grid, block, 0, st, p);
   }
   return hipGetLastError();
 }
@@ -652,18 +609,15 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       for (int i = 0; i < UPC; ++i) upc[i] = *reinterpret_cast<const vec_t*>(u + (ht + i * (NT / 2)) * UVEC);
       td.template load<true>(d, (int64_t)H * DV, rows, ht);
     }
-    // T, when given, replaces the solve below (requested after the tiles)
+    // T (requested after the tiles)
     constexpr int TPT = CH * CH / (4 * NT);
-    const float* tin = p.t_in ? p.t_in + ((size_t)blockIdx.x * H + h) * (CH * CH) : nullptr;
+    const float* tin = p.t_in + ((size_t)blockIdx.x * H + h) * (CH * CH);
     f32x4 tvals[TPT];
-    if (tin) {
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) tvals[i] = *reinterpret_cast<const f32x4*>(tin + 4 * (tid + i * NT));
-    }
+    for (int i = 0; i < TPT; ++i) tvals[i] = *reinterpret_cast<const f32x4*>(tin + 4 * (tid + i * NT));
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int e = 4 * (tid + i * NT);
-      if (!tin) *reinterpret_cast<f32x4*>(&sT[(e >> 6) * LA + (e & 63)]) = zero4();
       *reinterpret_cast<f32x4*>(&sP[(e >> 6) * LA + (e & 63)]) = zero4();
     }
     for (int e = tid; e < 4 * CH; e += NT) {
@@ -706,15 +660,12 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       }
       td.store(slotE(SDO), LV, nullptr, 0, ht);
     }
-    if (tin) {
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) {
-        const int e = 4 * (tid + i * NT);
-        *reinterpret_cast<f32x4*>(&sT[(e >> 6) * LA + (e & 63)]) = tvals[i];
-      }
+    for (int i = 0; i < TPT; ++i) {
+      const int e = 4 * (tid + i * NT);
+      *reinterpret_cast<f32x4*>(&sT[(e >> 6) * LA + (e & 63)]) = tvals[i];
     }
   }
-  const bool tload = p.t_in != nullptr;
   __syncthreads();
   // dh' down this wave's P5 value columns, requested only now: every
   // workgroup stages its tiles at about the same time, and the tiles arrive
@@ -746,14 +697,6 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     }
   }
   __syncthreads();
-
-  // ---- P3: T = (I + diag(beta) KD)^-1 (unless given)
-  if (!tload) {
-    if (w < 2) solve_diag_pair(sKD, sT, w, 3 - w, s.beta);
-    __syncthreads();
-    solve_columns(sKD, sT, w, s.beta);
-    __syncthreads();
-  }
 
   // per-lane partial sums of this wave's rows (row tiles 2 rh + j)
   f32x4 rg[2], rb[2];  // dgam / dbeta terms

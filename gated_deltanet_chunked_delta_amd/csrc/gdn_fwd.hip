@@ -50,8 +50,6 @@ struct alignas(16) FwdSmem {
   static constexpr int LT = ldpad<E>(CH);                 // transposed tiles, P
   static constexpr int LA = CH + 4;                       // fp32 64x64 matrices
   static constexpr int LO = DV + 16 / (int)sizeof(E);     // output staging (16-byte rows)
-  static constexpr int A_BYTES = CH * LA * 4;
-  static constexpr int O_BYTES = CH * LO * (int)sizeof(E);
   E Q[CH * LQ];
   E K[CH * LQ];
   E KT[DK * LT];
@@ -59,10 +57,7 @@ struct alignas(16) FwdSmem {
   E W[CH * LQ];   // holds -W
   E P[CH * LT];
   float T[CH * LA];
-  union {
-    float A[CH * LA];
-    E O[(O_BYTES > A_BYTES ? O_BYTES : A_BYTES) / sizeof(E)];
-  };
+  E O[CH * LO];
   alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], lam[CH];
   float GamC;
 };
@@ -229,9 +224,9 @@ struct TileLoader {
 template <int DV>
 struct FwdWaves { static constexpr int NW = DV == 128 ? 8 : 4; };
 
-// TLOAD: every chunk's T is read (p.t_in) instead of solved.
+// Every chunk's T is read from p.t_in (solved chunk-parallel beforehand).
 // USAVE: every chunk's U is written to p.us (CORR: its correction added).
-template <class E, int DK, int DV, bool OUT, bool CORR, bool PREP, bool TLOAD, bool USAVE>
+template <class E, int DK, int DV, bool OUT, bool CORR, bool PREP, bool USAVE>
 struct Chunk {
   static constexpr int NW = FwdWaves<DV>::NW;
   static constexpr int NT = NW * 64;
@@ -239,13 +234,12 @@ struct Chunk {
   using S = FwdSmem<E, DK, DV>;
   using Loader = TileLoader<E, DK, DV, NT, OUT, !CORR, PREP>;
 
-  // One lower 16x16 tile (rt, ct) of A = strict_lower(diag(beta) (K K^T) * D)
-  // (ISQ false; the diagonal tile also adds the log-bound terms) or of
-  // P = (Q K^T) * M (ISQ true).
+  // ISQ false: the diagonal 16x16 tile rt = ct of K K^T, whose diagonal gives
+  // the log-bound terms log max(1, |1 - beta |k|^2|); ISQ true: one lower tile
+  // (rt, ct) of P = (Q K^T) * M.
   template <bool ISQ>
-  __device__ __forceinline__ static void kk_tile(S* sp, int rt, int ct, int g, int c16, int rows) {
-    constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
-    (void)rows;
+  __device__ __forceinline__ static void kk_tile(S* sp, int rt, int ct, int g, int c16) {
+    constexpr int LQ = S::LQ, LT = S::LT;
     const E* X = ISQ ? sp->Q : sp->K;
     f32x4 acc = zero4();
 #pragma unroll
@@ -260,7 +254,6 @@ struct Chunk {
       const int r = 16 * rt + 4 * g + i;
       const float dm = __expf(gr4[i] - gc);
       if (!ISQ) {
-        sp->A[r * LA + c] = (c < r) ? br4[i] * acc[i] * dm : 0.f;
         if (r == c) sp->lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
       } else {
         sp->P[r * LT + c] = to_e<E>((c <= r) ? acc[i] * dm : 0.f);
@@ -271,26 +264,22 @@ struct Chunk {
   // Process the chunk whose tiles `ld` holds; prefetch the next chunk (if any)
   // into `ld`.  hacc: this wave's state columns (chunk start on entry, chunk end
   // on exit).  Returns the chunk's log-bound Lambda_c.
-  // t_in: this chunk's T when TLOAD; t_out: where to write the solved T
-  // (nullable).
+  // t_in: this chunk's T.
   // us_chunk: where this chunk's U = Ut - W h goes (nullable; CORR adds its
   // correction).
   __device__ static float step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows,
-                               int64_t ntok0, int nrows, int h, E* hs_chunk, const float* t_in, float* t_out,
+                               int64_t ntok0, int nrows, int h, E* hs_chunk, const float* t_in,
                                E* us_chunk, f32x4 (&hacc)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA, LO = S::LO;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
     const int H = p.H;
     const int n0 = w * (DV / NW);  // first state column of this wave
-    constexpr bool tload = TLOAD;
 
-    // T (when given) is requested first and lands in LDS at the end of phase 2
+    // T is requested first and lands in LDS at the end of phase 2
     f32x4 tv[TPT];
-    if (tload) {
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
-    }
+    for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
     // a correction adds to the stored U: its current pieces are requested now and
     // consumed at the end of the chain (no load latency inside it)
     typedef E e4_t __attribute__((__vector_size__(4 * sizeof(E))));
@@ -342,32 +331,21 @@ struct Chunk {
     __syncthreads();
     sp = lds_opaque(sp);
 
-    // ---- 2. K K^T -> A and Q K^T -> P, lower 16x16 tiles.  Four waves: each takes a
-    //         pair of row tiles {0, 3} or {1, 2} of one product (waves 0, 1: A; 2, 3: P),
-    //         loading its row-side fragments once per row; waves 0, 1 then solve the
-    //         diagonal blocks of T they hold.  Eight waves: wave r < 4 forms only the
-    //         diagonal tile A_rr and solves block r of T at once (the critical path);
-    //         waves 4..7 share the six off-diagonal tiles of A and the ten of P.
+    // ---- 2. the diagonal tiles of K K^T (log-bound) and, for the output, the
+    //         lower 16x16 tiles of P = (Q K^T) * M.  Eight waves: wave r < 4 forms
+    //         K K^T's tile r; P tile j goes to wave (j + 4) % 8 (at most two tiles a
+    //         wave).  Four waves: waves 0, 1 take the diagonal tiles of row tiles
+    //         {0, 3} and {1, 2}, waves 2, 3 the rows of P for those row tiles,
+    //         loading their row-side fragments once per row.
     if constexpr (NW == 8) {
-      if (w < 4) {
-        // (with T given, the diagonal tiles are still formed for the log-bound)
-        kk_tile<false>(sp, w, w, g, c16, rows);
-        if (!tload) solve_diag_pair(sp->A, sp->T, w, w, nullptr);
-      } else {
-        const int wq = w - 4;
+      if (w < 4) kk_tile<false>(sp, w, w, g, c16);
+      if (OUT) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int id = wq + 4 * j;  // 0..5: A tiles below the diagonal, 6..15: P tiles
-          if (id < 6) {
-            const int rt = id < 1 ? 1 : (id < 3 ? 2 : 3);
-            const int ct = id - (rt * (rt - 1)) / 2;
-            if (!tload) kk_tile<false>(sp, rt, ct, g, c16, rows);
-          } else if (OUT) {
-            const int pid = id - 6;
-            const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
-            const int ct = pid - (rt * (rt + 1)) / 2;
-            kk_tile<true>(sp, rt, ct, g, c16, rows);
-          }
+        for (int j = 0; j < 2; ++j) {
+          const int pid = ((w + 4) & 7) + 8 * j;
+          const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
+          const int ct = pid - (rt * (rt + 1)) / 2;
+          if (pid < 10) kk_tile<true>(sp, rt, ct, g, c16);
         }
       }
     }
@@ -384,6 +362,7 @@ struct Chunk {
           f32x4 br4 = *reinterpret_cast<const f32x4*>(&sp->beta[16 * RT + 4 * g]);
 #pragma unroll
           for (int ct = 0; ct <= RT; ++ct) {
+            if (!isq && ct != RT) continue;  // K K^T: the diagonal tile only
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb) mma(acc, xa[kb], ld_frag(sp->K, LQ, 16 * ct + c16, 32 * kb));
@@ -394,8 +373,7 @@ struct Chunk {
               const int r = 16 * RT + 4 * g + i;
               const float dm = __expf(gr4[i] - gc);
               if (!isq) {
-                sp->A[r * LA + c] = (c < r) ? br4[i] * acc[i] * dm : 0.f;
-                if (ct == RT && r == c) sp->lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
+                if (r == c) sp->lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
               } else {
                 sp->P[r * LT + c] = to_e<E>((c <= r) ? acc[i] * dm : 0.f);
               }
@@ -408,16 +386,13 @@ struct Chunk {
           const bool rows03 = (w & 1) == 0;
           if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
           else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
-          if (!isq && !tload) solve_diag_pair(sp->A, sp->T, rows03 ? 0 : 1, rows03 ? 3 : 2, nullptr);
         }
       }
     }
-    if (tload) {
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) {
-        const int e = 4 * (tid + i * NT);
-        *reinterpret_cast<f32x4*>(&sp->T[(e / CH) * LA + e % CH]) = tv[i];
-      }
+    for (int i = 0; i < TPT; ++i) {
+      const int e = 4 * (tid + i * NT);
+      *reinterpret_cast<f32x4*>(&sp->T[(e / CH) * LA + e % CH]) = tv[i];
     }
     __syncthreads();
     sp = lds_opaque(sp);
@@ -425,24 +400,10 @@ struct Chunk {
     // value (and the loop decisions taken on it) is identical across the workgroup
     const float lam_c = __shfl(wave_sum(sp->lam[l]), 0, 64);
 
-    // ---- 3. off-diagonal blocks of T (one block column per wave, when solved
-    //         here), T out.  The next chunk's k, v, g, beta (and q) start their
-    //         way from HBM before the solve.
+    // ---- 3. the next chunk's k, v, g, beta (and q) start their way from HBM
     if (nrows > 0) {
       ld.load_kv(p, ntok0, nrows, h);
       if (OUT) ld.load_q(p, ntok0, nrows, h);
-    }
-    if constexpr (!tload) {
-      solve_columns(sp->A, sp->T, w, nullptr);
-      __syncthreads();
-      sp = lds_opaque(sp);
-      if (t_out) {
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-          const int e = 4 * (tid + i * NT);
-          *reinterpret_cast<f32x4*>(t_out + e) = *reinterpret_cast<const f32x4*>(&sp->T[(e / CH) * LA + e % CH]);
-        }
-      }
     }
 
     // ---- 4. -W = -T diag(beta Gam) K for row tile w % 4 (key column tiles split
@@ -639,10 +600,8 @@ struct Chunk {
       const int nrows = more ? min(CH, len - (c + 1) * CH) : 0;
       E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
       const size_t toff = ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
-      const float* tin = TLOAD ? p.t_in + toff : nullptr;
-      float* tout = (!TLOAD && p.t_out) ? p.t_out + toff : nullptr;
       E* usc = USAVE ? static_cast<E*>(p.us) + ((chunk0 + c) * p.H + h) * (size_t)(CH * DV) : nullptr;
-      lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, tout, usc, hacc);
+      lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, p.t_in + toff, usc, hacc);
     }
     if (done) *done = c - cb;
     return lam;
@@ -692,7 +651,7 @@ __device__ void init_smem(FwdSmem<E, DK, DV>& s) {
 }
 
 // Phase 1: every segment from zero (segment 0 from h0).
-template <class E, int DK, int DV, bool OUT, bool PREP, bool TLOAD, bool USAVE>
+template <class E, int DK, int DV, bool OUT, bool PREP, bool USAVE>
 __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
@@ -702,7 +661,7 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p)
   f32x4 hacc[DK / 16][DV / (16 * FwdWaves<DV>::NW)];
   init_smem(s);
   load_state<E, DK, DV>(hacc, (sd.s == 0 && p.h0) ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-  const float lam = Chunk<E, DK, DV, OUT, false, PREP, TLOAD, USAVE>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
+  const float lam = Chunk<E, DK, DV, OUT, false, PREP, USAVE>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
                                                       sd.c_begin, sd.c_end, h, hacc, nullptr);
   if (nseg == 1) {
     if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
@@ -733,14 +692,14 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p3(FwdParams p)
   if (!ok) {
     // Gates do not decay fast enough to cut this sequence: one workgroup redoes it serially.
     load_state<E, DK, DV>(hacc, p.h0 ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-    Chunk<E, DK, DV, OUT, false, PREP, true, USAVE>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc,
+    Chunk<E, DK, DV, OUT, false, PREP, USAVE>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc,
                                                           nullptr);
     if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
     return;
   }
   load_state<E, DK, DV>(hacc, p.bstate + ((size_t)(blockIdx.x - 1) * p.H + h) * SS);
   int done = 0;
-  Chunk<E, DK, DV, OUT, true, PREP, true, USAVE>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done);
+  Chunk<E, DK, DV, OUT, true, PREP, USAVE>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done);
   if (sd.s == nseg - 1 && p.hT) {
     // hT = b_last + (the correction propagated through the whole last segment, if it got there)
     const float* b = p.bstate + ((size_t)blockIdx.x * p.H + h) * SS;
@@ -753,24 +712,20 @@ hipError_t launch_fwd_t(const FwdParams& p, int nseg_total, hipStream_t st) {
   dim3 grid(nseg_total, p.H), block(64 * FwdWaves<DV>::NW);
   const bool out = p.o != nullptr;
   const bool prep = p.prep.qk_norm || p.prep.gate_act;
-  // phase 3 always reads T (written by phase 1); phase 1 reads it only in the
-  // replay, when the forward saved it.  The replay always writes U; the
-  // forward proper on request.
-  if (p.phase != 1 && !p.t_in) return hipErrorInvalidValue;
-  if (p.phase == 1 && out && p.t_in) return hipErrorInvalidValue;
+  // every phase reads T (solved beforehand); the replay always writes U, the
+  // forward proper on request
+  if (!p.t_in) return hipErrorInvalidValue;
   if (!out && !p.us) return hipErrorInvalidValue;
-  const bool tl = p.t_in != nullptr, us = p.us != nullptr;
+  const bool us = p.us != nullptr;
   if (p.phase == 1) {
     if (prep) {
-      if (out && us) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true, false, true>), grid, block, 0, st, p);
-      else if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true, false, false>), grid, block, 0, st, p);
-      else if (tl) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true, true, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true, false, true>), grid, block, 0, st, p);
+      if (out && us) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true, true>), grid, block, 0, st, p);
+      else if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true, false>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true, true>), grid, block, 0, st, p);
     } else {
-      if (out && us) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false, false, true>), grid, block, 0, st, p);
-      else if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false, false, false>), grid, block, 0, st, p);
-      else if (tl) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false, true, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false, false, true>), grid, block, 0, st, p);
+      if (out && us) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false, true>), grid, block, 0, st, p);
+      else if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false, false>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false, true>), grid, block, 0, st, p);
     }
   } else {
     if (prep) {

@@ -36,10 +36,21 @@ struct FwdParams {
   float* lam;              // [total segments][H] segment log-bounds
   void* hs;                // nullable: [total chunks][H] chunk start states S, Dv x Dk in st_blk order (dtype)
   void* us;                // nullable: [total chunks][H][DV/16][CH][16] U = Ut - W h of each chunk in 16-column blocks (dtype)
-  // [total chunks][H][CH][CH] fp32 row-major T = (I + diag(beta) A)^-1 of each chunk:
-  const float* t_in;       // nullable: read instead of solved (replay and corrections only)
-  float* t_out;            // nullable: written where solved (phase 1)
+  // [total chunks][H][CH][CH] fp32 row-major T = (I + diag(beta) A)^-1 of each chunk
+  const float* t_in;
   int phase;               // 1 = segments from zero / h0, 3 = boundary corrections
+  PrepParams prep;
+};
+
+// Every chunk's T = (I + diag(beta) strict_lower(K K^T * D))^-1, chunk-parallel.
+struct TSolveParams {
+  const void* k;
+  const float* g;
+  const void* beta;
+  float* t_out;            // [total chunks][H][CH][CH] fp32 row-major
+  int H;
+  SeqInfo seq;
+  const int2* chunk_tab;   // [total chunks] (sequence, chunk index within it)
   PrepParams prep;
 };
 
@@ -61,8 +72,7 @@ struct RevParams {
   float* bstate;           // [total segments][H][DK][DV] segment start gradients
   float* lam;              // [total segments][H]
   void* dhs;               // [total chunks][H] gradient at each chunk END, S-shaped, st_blk order (dtype)
-  const float* t_in;       // nullable: chunk matrices T (as FwdParams), read instead of solved
-  float* t_out;            // nullable: written where solved (phase 1)
+  const float* t_in;       // chunk matrices T (as FwdParams)
   int phase;
   PrepParams prep;
 };
@@ -78,7 +88,7 @@ struct GradParams {
   const void* hs;          // chunk start states
   const void* dhs;         // chunk end state gradients
   const void* us;          // each chunk's U = Ut - W h ([total chunks][H][DV/16][CH][16] column blocks, dtype)
-  const float* t_in;       // nullable: chunk matrices T (as FwdParams), read instead of solved
+  const float* t_in;       // chunk matrices T (as FwdParams)
   void* dq;
   void* dk;
   void* dv;
@@ -109,6 +119,7 @@ struct DecodeParams {
 
 hipError_t launch_plan(SeqInfo seq, int N, int segc, int* chunk_first, int* seg_first, SegDesc* segs,
                        int2* chunk_tab, hipStream_t st);
+hipError_t launch_tsolve(int dtype, int DK, const TSolveParams& p, int nchunk_total, hipStream_t st);
 hipError_t launch_fwd(int dtype, int DK, int DV, const FwdParams& p, int nseg_total, hipStream_t st);
 hipError_t launch_rev(int dtype, int DK, int DV, const RevParams& p, int nseg_total, hipStream_t st);
 hipError_t launch_grad(int dtype, int DK, int DV, const GradParams& p, int nchunk_total, hipStream_t st);
