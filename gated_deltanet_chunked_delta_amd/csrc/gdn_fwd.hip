@@ -293,6 +293,19 @@ struct Chunk {
           uold[rt][nt] = *reinterpret_cast<const e4_t*>(us_chunk + (n0 + 16 * nt) * CH + (16 * rt + 4 * g + b) * 16 +
                                                         4 * q);
     }
+    // likewise the output a correction adds to: the 16-byte row pieces this
+    // thread writes in phase 6
+    constexpr int OVEC = 16 / (int)sizeof(E), NOP = CH * (DV / OVEC) / NT;
+    typedef E ovec_t __attribute__((__vector_size__(16)));
+    ovec_t oold[NOP];
+    if constexpr (CORR && OUT) {
+#pragma unroll
+      for (int j = 0; j < NOP; ++j) {
+        const int e = tid + j * NT, r = e / (DV / OVEC), c0 = (e % (DV / OVEC)) * OVEC;
+        oold[j] = ovec_t{};
+        if (r < rows) oold[j] = *reinterpret_cast<const ovec_t*>(static_cast<const E*>(p.o) + ((tok0 + r) * H + h) * DV + c0);
+      }
+    }
 
     // ---- 1. tiles into LDS, scalars, prefetch of the next chunk
     S* sp = lds_opaque(&s0);
@@ -525,19 +538,8 @@ struct Chunk {
           for (int kb = 0; kb < 2; ++kb) mma(o, ld_frag(sp->P, LT, 16 * rt + c16, 32 * kb), uf[kb]);
           o = o * p.scale;
           const int col = n0 + 16 * nt + c16;
-          if (!CORR) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sp->O[(16 * rt + 4 * g + i) * LO + col] = to_e<E>(o[i]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 16 * rt + 4 * g + i;
-              if (r < rows) {
-                E* dst = static_cast<E*>(p.o) + ((tok0 + r) * H + h) * DV + col;
-                *dst = to_e<E>(to_f(*dst) + o[i]);
-              }
-            }
-          }
+          for (int i = 0; i < 4; ++i) sp->O[(16 * rt + 4 * g + i) * LO + col] = to_e<E>(o[i]);
         }
       }
     }
@@ -567,15 +569,21 @@ struct Chunk {
     __syncthreads();
     sp = lds_opaque(sp);
 
-    // ---- 6. output tile out (coalesced); the next chunk's staging does not touch sp->O
-    if (OUT && !CORR) {
-      constexpr int VEC = 16 / sizeof(E);
-      typedef E vec_t __attribute__((__vector_size__(16)));
-      for (int e = tid; e < CH * (DV / VEC); e += NT) {
-        const int r = e / (DV / VEC), c0 = (e % (DV / VEC)) * VEC;
-        if (r < rows)
-          *reinterpret_cast<vec_t*>(static_cast<E*>(p.o) + ((tok0 + r) * H + h) * DV + c0) =
-              *reinterpret_cast<const vec_t*>(&sp->O[r * LO + c0]);
+    // ---- 6. output tile out (coalesced); the next chunk's staging does not
+    //         touch sp->O.  A correction adds its tile to the stored values.
+    if constexpr (OUT) {
+#pragma unroll
+      for (int j = 0; j < NOP; ++j) {
+        const int e = tid + j * NT, r = e / (DV / OVEC), c0 = (e % (DV / OVEC)) * OVEC;
+        if (r < rows) {
+          ovec_t val;
+          val = *reinterpret_cast<const ovec_t*>(&sp->O[r * LO + c0]);
+          if constexpr (CORR) {
+#pragma unroll
+            for (int i = 0; i < OVEC; ++i) val[i] = to_e<E>(to_f(oold[j][i]) + to_f(val[i]));
+          }
+          *reinterpret_cast<ovec_t*>(static_cast<E*>(p.o) + ((tok0 + r) * H + h) * DV + c0) = val;
+        }
       }
     }
     return lam_c;
