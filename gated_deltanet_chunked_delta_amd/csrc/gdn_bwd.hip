@@ -938,19 +938,15 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   // ---- P10: Z = GT T^T (own row tiles, column tile cw) -> slot P (last read in
   //           P8), GA = strict_lower(-T^T Z) (own rows); E -> S = E + E^T (slot KD)
   // XU = T^T dU (own rows and value columns) -> dV into slot Q (GW was last read in P9)
-  // The rows of T^T for this wave's row tiles serve XU (in E) and GA (in fp32).
-  Frag<float> ttf[2][2];
+  // The rows of T^T for this wave's row tiles serve XU (in E) and GA (near fp32).
+  PFrag<E> ttp[2][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) ttf[j][kb] = ld_fragT<float>(sT, LA, 16 * (2 * rh + j) + c16, 32 * kb, 1.f);
+    for (int kb = 0; kb < 2; ++kb)
+      ttp[j][kb] = PFrag<E>(ld_fragT<float>(sT, LA, 16 * (2 * rh + j) + c16, 32 * kb, 1.f));
   {
     E* sDV = slotE(SQ);
-    Frag<E> tte[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) pack_frag(tte[j][kb], ttf[j][kb].lo, ttf[j][kb].hi);
 #pragma unroll
     for (int nt = 0; nt < CTV; ++nt) {
       Frag<E> duf[2];
@@ -961,35 +957,35 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         const int rt = 2 * rh + j;
         f32x4 xu = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(xu, tte[j][kb], duf[kb]);
+        for (int kb = 0; kb < 2; ++kb) mma(xu, e_part(ttp[j][kb]), duf[kb]);
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s.beta[16 * rt + 4 * g]);
         st_tile_rows<E>(sDV, LV, 16 * rt, n0 + 16 * nt, xu * b4);
       }
     }
   }
   {
-    // both products are fp32 x fp32 (fp32 matrix-core products); the two row
-    // halves of a column group each form half of Z and exchange it through LDS,
-    // stored transposed so that Z's columns read back as rows
+    // both products take fp32 operands (PFrag: near-fp32 products); the two
+    // row halves of a column group each form half of Z and exchange it through
+    // LDS, stored transposed so that Z's columns read back as rows
     const float* sGT = slotF(SV);
     float* sZT = slotF(SP);
     {
-      Frag<float> tcol[2];
+      PFrag<E> tcol[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) tcol[kb] = ld_frag(sT, LA, 16 * cw + c16, 32 * kb);
+      for (int kb = 0; kb < 2; ++kb) tcol[kb] = PFrag<E>(ld_frag(sT, LA, 16 * cw + c16, 32 * kb));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int rt = 2 * rh + j;
         f32x4 z = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(z, ld_frag(sGT, LA, 16 * rt + c16, 32 * kb), tcol[kb]);
+        for (int kb = 0; kb < 2; ++kb) mma(z, PFrag<E>(ld_frag(sGT, LA, 16 * rt + c16, 32 * kb)), tcol[kb]);
         *reinterpret_cast<f32x4*>(&sZT[(16 * cw + c16) * LA + 16 * rt + 4 * g]) = z;
       }
     }
     __syncthreads();
-    Frag<float> zf[2];
+    PFrag<E> zf[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) zf[kb] = ld_frag(static_cast<const float*>(sZT), LA, 16 * cw + c16, 32 * kb);
+    for (int kb = 0; kb < 2; ++kb) zf[kb] = PFrag<E>(ld_frag(static_cast<const float*>(sZT), LA, 16 * cw + c16, 32 * kb));
     const int c = 16 * cw + c16;
     float csum = 0.f;
     f32x4 ga[2];
@@ -998,7 +994,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       const int rt = 2 * rh + j;
       f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mma(acc, ttf[j][kb], zf[kb]);
+      for (int kb = 0; kb < 2; ++kb) mma(acc, ttp[j][kb], zf[kb]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;

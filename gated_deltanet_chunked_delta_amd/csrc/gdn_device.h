@@ -149,6 +149,42 @@ __device__ __forceinline__ void pack_frag_scaled(Frag<E>& f, const f32x4& t0, co
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Operand of a near-fp32 product, from an fp32 fragment.  For E = float it is
+// that fragment (fp32 matrix-core products).  For E = bf16 it is the pair
+// x = hi + lo of bf16 fragments (hi = x rounded, lo = the exact residual x - hi
+// rounded): the product hi*hi + hi*lo + lo*hi (lo*lo dropped) carries about 16
+// significant bits of each operand, with three bf16 instructions per 32-deep
+// k-block in place of eight fp32 ones.
+template <class E> struct PFrag;
+template <> struct PFrag<float> {
+  Frag<float> f;
+  __device__ __forceinline__ explicit PFrag(const Frag<float>& x) : f(x) {}
+  __device__ __forceinline__ PFrag() {}
+};
+template <> struct PFrag<bf16> {
+  Frag<bf16> hi, lo;
+  __device__ __forceinline__ PFrag() {}
+  __device__ __forceinline__ explicit PFrag(const Frag<float>& x) {
+    pack_frag(hi, x.lo, x.hi);
+    f32x4 rl, rh;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rl[i] = x.lo[i] - (float)hi.v[i];
+      rh[i] = x.hi[i] - (float)hi.v[4 + i];
+    }
+    pack_frag(lo, rl, rh);
+  }
+};
+__device__ __forceinline__ void mma(f32x4& acc, const PFrag<float>& a, const PFrag<float>& b) { mma(acc, a.f, b.f); }
+__device__ __forceinline__ void mma(f32x4& acc, const PFrag<bf16>& a, const PFrag<bf16>& b) {
+  mma(acc, a.lo, b.hi);
+  mma(acc, a.hi, b.lo);
+  mma(acc, a.hi, b.hi);
+}
+// The E-operand part of a PFrag (the rounded value for bf16).
+__device__ __forceinline__ const Frag<float>& e_part(const PFrag<float>& a) { return a.f; }
+__device__ __forceinline__ const Frag<bf16>& e_part(const PFrag<bf16>& a) { return a.hi; }
+
 // fp32 -> storage type
 template <class E> __device__ __forceinline__ E to_e(float x);
 template <> __device__ __forceinline__ bf16 to_e<bf16>(float x) { return (bf16)x; }
