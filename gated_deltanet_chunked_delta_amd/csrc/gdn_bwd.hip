@@ -675,25 +675,49 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb) dk_[nt][kb] = ld_frag8_st(dhs, DK, p5n0 + 16 * nt + c16, 32 * kb);
 
-  // ---- P2: KD = strict_lower(K K^T * D), P = (Q K^T) * M  (20 lower tiles)
-  for (int ti = w; ti < 20; ti += 8) {
-    const bool isq = ti >= 10;
-    const int tt = isq ? ti - 10 : ti;
-    int rt = 0;
-    while ((rt + 1) * (rt + 2) / 2 <= tt) ++rt;
-    const int ct = tt - rt * (rt + 1) / 2;
-    f32x4 acc = zero4();
-    const E* X = isq ? slotE(SQ) : sK;
+  // ---- P2: KD = strict_lower(K K^T * D), P = (Q K^T) * M  (20 lower tiles:
+  //          tile w + 8j for wave w, all fragment reads issued before the products)
+  {
+    constexpr int NJ = 3;
+    f32x4 acc[NJ];
+    Frag<E> xr[NJ][DK / 32], xc[NJ][DK / 32];
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb)
-      mma(acc, ld_frag(X, LK, 16 * rt + c16, 32 * kb), ld_frag(sK, LK, 16 * ct + c16, 32 * kb));
-    const int c = 16 * ct + c16;
+    for (int j = 0; j < NJ; ++j) {
+      const int ti = w + 8 * j, tt = ti >= 10 ? ti - 10 : ti;
+      const int rt = tt < 1 ? 0 : (tt < 3 ? 1 : (tt < 6 ? 2 : 3)), ct = tt - rt * (rt + 1) / 2;
+      const E* X = ti >= 10 ? slotE(SQ) : sK;
+      if (ti < 20) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * g + i;
-      const float dm = __expf(s.gam[r] - s.gam[c]);
-      if (!isq) sKD[r * LA + c] = (c < r) ? acc[i] * dm : 0.f;
-      else sP[r * LA + c] = (c <= r) ? acc[i] * dm : 0.f;
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          xr[j][kb] = ld_frag(X, LK, 16 * rt + c16, 32 * kb);
+          xc[j][kb] = ld_frag(sK, LK, 16 * ct + c16, 32 * kb);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      acc[j] = zero4();
+      if (w + 8 * j < 20) {
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) mma(acc[j], xr[j][kb], xc[j][kb]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int ti = w + 8 * j, tt = ti >= 10 ? ti - 10 : ti;
+      const int rt = tt < 1 ? 0 : (tt < 3 ? 1 : (tt < 6 ? 2 : 3)), ct = tt - rt * (rt + 1) / 2;
+      if (ti < 20) {
+        const int c = 16 * ct + c16;
+        const float gc = s.gam[c];
+        const f32x4 gr4 = *reinterpret_cast<const f32x4*>(&s.gam[16 * rt + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * g + i;
+          const float dm = __expf(gr4[i] - gc);
+          if (ti < 10) sKD[r * LA + c] = (c < r) ? acc[j][i] * dm : 0.f;
+          else sP[r * LA + c] = (c <= r) ? acc[j][i] * dm : 0.f;
+        }
+      }
     }
   }
   __syncthreads();
