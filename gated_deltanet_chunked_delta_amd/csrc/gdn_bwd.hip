@@ -535,6 +535,72 @@ struct alignas(16) GradSmem {
 // slot roles
 enum { SK = 0, SKT = 1, SQ = 2, SV = 3, SDO = 4, ST = 5, SKD = 6, SP = 7, SDU = 8 };
 
+// A 64 x 64 fp32 matrix in one LDS slot, kept for near-fp32 products (PFrag).
+// E = float stores it as is (row stride LA).  E = bf16 stores its bf16 hi and
+// lo parts (x = hi + lo, lo the rounded residual) as two planes of row stride
+// LP: each value is split once, when written, and fragments load ready to
+// multiply.  row(): k-slots along row r; col(): k-slots down column c0 + lane%16.
+template <class E> struct PMat;
+template <> struct PMat<float> {
+  static constexpr int LA = CH + 4;
+  float* m;
+  __device__ __forceinline__ explicit PMat(void* slot) : m(static_cast<float*>(slot)) {}
+  __device__ __forceinline__ void put(int r, int c, float x) const { m[r * LA + c] = x; }
+  __device__ __forceinline__ void put4(int r, int c0, const f32x4& x) const {
+    *reinterpret_cast<f32x4*>(&m[r * LA + c0]) = x;
+  }
+  __device__ __forceinline__ float at(int r, int c) const { return m[r * LA + c]; }
+  __device__ __forceinline__ Frag<float> row_e(int r, int k0) const { return ld_frag(m, LA, r, k0); }
+  __device__ __forceinline__ PFrag<float> row(int r, int k0) const { return PFrag<float>(ld_frag(m, LA, r, k0)); }
+  __device__ __forceinline__ PFrag<float> col(int k0, int c0) const {
+    return PFrag<float>(ld_fragT<float>(m, LA, c0 + (lane_id() & 15), k0, 1.f));
+  }
+};
+template <> struct PMat<bf16> {
+  static constexpr int LP = CH + 4;  // bf16 elements per row: 8-byte aligned rows
+  bf16* hi;
+  bf16* lo;
+  typedef bf16 b4_t __attribute__((__vector_size__(8)));
+  __device__ __forceinline__ explicit PMat(void* slot)
+      : hi(static_cast<bf16*>(slot)), lo(static_cast<bf16*>(slot) + CH * LP) {}
+  __device__ __forceinline__ static void split(float x, bf16& h, bf16& l) {
+    h = (bf16)x;
+    l = (bf16)(x - (float)h);
+  }
+  __device__ __forceinline__ void put(int r, int c, float x) const {
+    bf16 h, l;
+    split(x, h, l);
+    hi[r * LP + c] = h;
+    lo[r * LP + c] = l;
+  }
+  __device__ __forceinline__ void put4(int r, int c0, const f32x4& x) const {
+    b4_t h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16 a, b;
+      split(x[i], a, b);
+      h[i] = a;
+      l[i] = b;
+    }
+    *reinterpret_cast<b4_t*>(&hi[r * LP + c0]) = h;
+    *reinterpret_cast<b4_t*>(&lo[r * LP + c0]) = l;
+  }
+  __device__ __forceinline__ float at(int r, int c) const { return (float)hi[r * LP + c] + (float)lo[r * LP + c]; }
+  __device__ __forceinline__ Frag<bf16> row_e(int r, int k0) const { return ld_frag(hi, LP, r, k0); }
+  __device__ __forceinline__ PFrag<bf16> row(int r, int k0) const {
+    PFrag<bf16> f;
+    f.hi = ld_frag(hi, LP, r, k0);
+    f.lo = ld_frag(lo, LP, r, k0);
+    return f;
+  }
+  __device__ __forceinline__ PFrag<bf16> col(int k0, int c0) const {
+    PFrag<bf16> f;
+    f.hi = ld_fragC_q<bf16>(hi, LP, k0, c0);
+    f.lo = ld_fragC_q<bf16>(lo, LP, k0, c0);
+    return f;
+  }
+};
+
 // One chunk per workgroup of 8 waves.  Wave w works on column group cw = w % 4
 // (key columns [cw Dk/4, (cw+1) Dk/4), value columns [cw Dv/4, ...)) and row
 // half rh = w / 4 (row tiles 2 rh, 2 rh + 1) of every per-row product, so two
@@ -574,7 +640,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 
   E* sK = slotE(SK);
   E* sKT = slotE(SKT);
-  float* sT = slotF(ST);
+  const PMat<E> TT(s.slot[ST]);  // T^T (so that T^T's rows, the most read, load as rows)
   float* sKD = slotF(SKD);
   float* sP = slotF(SP);
   E* sDU = slotE(SDU);
@@ -663,7 +729,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int e = 4 * (tid + i * NT);
-      *reinterpret_cast<f32x4*>(&sT[(e >> 6) * LA + (e & 63)]) = tvals[i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) TT.put((e & 63) + q, e >> 6, tvals[i][q]);
     }
   }
   __syncthreads();
@@ -894,7 +961,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         const int rt = 2 * rh + j;
         f32x4 xw = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(xw, ld_fragT<E>(sT, LA, 16 * rt + c16, 32 * kb, 1.f), gwf[kb]);
+        for (int kb = 0; kb < 2; ++kb) mma(xw, TT.row_e(16 * rt + c16, 32 * kb), gwf[kb]);
         const int dcol = d0 + 16 * dt + c16;
         f32x4 pq = zero4();  // GPM^T Q (GPM is final since P7)
 #pragma unroll
@@ -929,11 +996,11 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   __syncthreads();
 
-  // ---- P9: GT = dU V^T diag(beta) + GW K^T diag(beta Gam) -> slot V (fp32).
+  // ---- P9: GT = dU V^T diag(beta) + GW K^T diag(beta Gam) -> slot V (PMat).
   //          The dbeta term sum_c (T^T dU)[r][c] V[r][c] is the column sum
   //          sum_i T[i][r] (dU V^T)[i][r], taken here from the first product.
+  const PMat<E> GTm(s.slot[SV]);
   {
-    float* sGT = slotF(SV);
     const int c = 16 * cw + c16;
     float tm = 0.f;
 #pragma unroll
@@ -949,8 +1016,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
-        sGT[r * LA + c] = s.beta[c] * a[i] + s.bg[c] * b[i];
-        tm += sT[r * LA + c] * a[i];
+        GTm.put(r, c, s.beta[c] * a[i] + s.bg[c] * b[i]);
+        tm += TT.at(c, r) * a[i];
       }
     }
     tm += __shfl_xor(tm, 16, 64);
@@ -968,7 +1035,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      ttp[j][kb] = PFrag<E>(ld_fragT<float>(sT, LA, 16 * (2 * rh + j) + c16, 32 * kb, 1.f));
+      ttp[j][kb] = TT.row(16 * (2 * rh + j) + c16, 32 * kb);
   {
     E* sDV = slotE(SQ);
 #pragma unroll
@@ -991,25 +1058,24 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     // both products take fp32 operands (PFrag: near-fp32 products); the two
     // row halves of a column group each form half of Z and exchange it through
     // LDS, stored transposed so that Z's columns read back as rows
-    const float* sGT = slotF(SV);
-    float* sZT = slotF(SP);
+    const PMat<E> ZT(s.slot[SP]);
     {
-      PFrag<E> tcol[2];
+      PFrag<E> tcol[2];  // rows 16 cw.. of T
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) tcol[kb] = PFrag<E>(ld_frag(sT, LA, 16 * cw + c16, 32 * kb));
+      for (int kb = 0; kb < 2; ++kb) tcol[kb] = TT.col(32 * kb, 16 * cw);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int rt = 2 * rh + j;
         f32x4 z = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(z, PFrag<E>(ld_frag(sGT, LA, 16 * rt + c16, 32 * kb)), tcol[kb]);
-        *reinterpret_cast<f32x4*>(&sZT[(16 * cw + c16) * LA + 16 * rt + 4 * g]) = z;
+        for (int kb = 0; kb < 2; ++kb) mma(z, GTm.row(16 * rt + c16, 32 * kb), tcol[kb]);
+        ZT.put4(16 * cw + c16, 16 * rt + 4 * g, z);
       }
     }
     __syncthreads();
     PFrag<E> zf[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) zf[kb] = PFrag<E>(ld_frag(static_cast<const float*>(sZT), LA, 16 * cw + c16, 32 * kb));
+    for (int kb = 0; kb < 2; ++kb) zf[kb] = ZT.row(16 * cw + c16, 32 * kb);
     const int c = 16 * cw + c16;
     float csum = 0.f;
     f32x4 ga[2];
