@@ -159,7 +159,8 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false, 
     p.o_bstate = take(sizeof(float) * SS * p.nseg * a.H);
     p.o_lam = take(sizeof(float) * (size_t)p.nseg * a.H);
   }
-  const size_t tbytes = sizeof(float) * CHUNK * CHUNK * (size_t)std::max(1, p.nchunk) * a.H;
+  // T of every chunk, then every chunk's scalar record
+  const size_t tbytes = sizeof(float) * (CHUNK * CHUNK + gdn::RECF) * (size_t)std::max(1, p.nchunk) * a.H;
   if (!bwd && !t_given) p.o_ts = take(tbytes);
   if (bwd) {
     if (p.cp) {
@@ -308,7 +309,7 @@ size_t gdn_chunk_states_bytes(const gdn_common_args* a) {
 size_t gdn_chunk_t_bytes(const gdn_common_args* a) {
   if (!a) { fail(GDN_E_INVALID, "null args"); return 0; }
   if (check_common(*a) != GDN_OK) return 0;
-  return (size_t)count_chunks(*a) * a->H * CHUNK * CHUNK * sizeof(float);
+  return (size_t)count_chunks(*a) * a->H * (CHUNK * CHUNK + gdn::RECF) * sizeof(float);
 }
 
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
@@ -347,15 +348,17 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   // every chunk's T, solved chunk-parallel (into the caller's buffer when it
   // keeps T) and read by the chunk chain and the segment corrections
   float* ts = args->t_save ? args->t_save : at<float>(ws, pl.o_ts);
+  float* rec = ts + (size_t)pl.nchunk * a.H * CHUNK * CHUNK;  // the chunks' scalar records
   if (pl.nchunk > 0) {
     gdn::TSolveParams tp{};
-    tp.k = a.k; tp.g = a.g; tp.beta = a.beta; tp.t_out = ts; tp.H = a.H; tp.seq = sq;
+    tp.k = a.k; tp.g = a.g; tp.beta = a.beta; tp.t_out = ts; tp.rec_out = rec; tp.H = a.H; tp.seq = sq;
     tp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);
     tp.prep = p.prep;
     e = timed("tsolve", s, [&] { return gdn::launch_tsolve(a.dtype, a.Dk, tp, pl.nchunk, s); });
     if (e != hipSuccess) return hip_fail(e, "T solve launch");
   }
   p.t_in = ts;
+  p.rec = rec;
   p.phase = 1;
   e = timed("fwd", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
@@ -409,15 +412,18 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   // chunk matrices T: the caller's, else solved chunk-parallel here (the same
   // kernel as the forward's, so the same values); every later kernel reads them
   const float* ts = t_given ? args->t_saved : at<float>(ws, pl.o_ts);
+  const float* rec = ts + (size_t)pl.nchunk * a.H * CHUNK * CHUNK;  // the chunks' scalar records
   if (!t_given && pl.nchunk > 0) {
     gdn::TSolveParams tp{};
-    tp.k = a.k; tp.g = a.g; tp.beta = a.beta; tp.t_out = at<float>(ws, pl.o_ts); tp.H = a.H; tp.seq = sq;
+    tp.k = a.k; tp.g = a.g; tp.beta = a.beta; tp.t_out = at<float>(ws, pl.o_ts);
+    tp.rec_out = at<float>(ws, pl.o_ts) + (size_t)pl.nchunk * a.H * CHUNK * CHUNK; tp.H = a.H; tp.seq = sq;
     tp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);
     tp.prep = p.prep;
     e = timed("tsolve", s, [&] { return gdn::launch_tsolve(a.dtype, a.Dk, tp, pl.nchunk, s); });
     if (e != hipSuccess) return hip_fail(e, "T solve launch");
   }
   p.t_in = ts;
+  p.rec = rec;
   if (saved) {
     p.hs = const_cast<void*>(args->h_saved);
     p.us = static_cast<char*>(const_cast<void*>(args->h_saved)) + states_part_bytes(a);
@@ -442,6 +448,7 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   r.lam = pl.cp ? at<float>(ws, pl.o_lam2) : nullptr;
   r.dhs = at<void>(ws, pl.o_dhs);
   r.t_in = ts;
+  r.rec = rec;
   r.prep = p.prep;
   r.phase = 1;
   e = timed("rev", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });

@@ -39,6 +39,8 @@
 //     two terms that would see them, which leaves every real gradient unchanged.
 #include <type_traits>
 
+#include <cstddef>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_tiles.h"
@@ -60,8 +62,9 @@ struct alignas(16) RevSmem {
   E WT[DK * LT];   // -W^T
   E PT[CH * LT];   // scale * P^T
   float T[CH * LA];
-  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], lam[CH], sGam[CH];
-  float GamC;
+  // the chunk's scalar record, as laid out in memory (tail: Lambda_c, Gam_C)
+  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], tail[4];
+  alignas(16) float sGam[CH];  // scale Gam, zero past the sequence end
 };
 
 // Waves per workgroup of the reverse chain: 8 when the state gradient has 128
@@ -85,53 +88,44 @@ struct RevChunk {
   struct Loader {
     TilePart<E, KQT, DK> kq;
     TilePart<E, NT, CORR ? 0 : DV> d;
-    ScalarPart<E> sc;
+    RecordPart rec;
   };
   __device__ __forceinline__ static bool q_half() { return !CORR && threadIdx.x >= KQT; }
   __device__ __forceinline__ static int kq_tid() { return threadIdx.x & (KQT - 1); }
 
-  __device__ static void issue(Loader& ld, const RevParams& p, int64_t tok0, int rows, int h) {
+  __device__ static void issue(Loader& ld, const RevParams& p, int64_t tok0, int rows, int h, const float* rec) {
     const int H = p.H;
     const void* src = q_half() ? p.q : p.k;
     ld.kq.load(static_cast<const E*>(src) + (tok0 * H + h) * DK, (int64_t)H * DK, rows, kq_tid());
     if (!CORR) ld.d.load(static_cast<const E*>(p.dout) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
-    ld.sc.load(p.g, static_cast<const E*>(p.beta), tok0, H, h, rows);
+    ld.rec.load(rec);
   }
 
-  // ISQ false: the diagonal 16x16 tile rt = ct of K K^T, whose diagonal gives
-  // the log-bound terms log max(1, |1 - beta |k|^2|); ISQ true: one lower tile
-  // (rt, ct) of scale P^T, P = (Q K^T) * M with the rows past the sequence end
-  // masked.
-  template <bool ISQ>
-  __device__ __forceinline__ static void kk_tile(S* sp, const RevParams& p, int rt, int ct, int g, int c16,
+  // One lower 16x16 tile (rt, ct) of scale P^T, P = (Q K^T) * M, with the rows
+  // past the sequence end masked.
+  __device__ __forceinline__ static void pt_tile(S* sp, const RevParams& p, int rt, int ct, int g, int c16,
                                                  int rows) {
     constexpr int LQ = S::LQ, LT = S::LT;
-    const E* X = ISQ ? sp->Q : sp->K;
     f32x4 acc = zero4();
 #pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb)
-      mma(acc, ld_frag(X, LQ, 16 * rt + c16, 32 * kb), ld_frag(sp->K, LQ, 16 * ct + c16, 32 * kb));
+      mma(acc, ld_frag(sp->Q, LQ, 16 * rt + c16, 32 * kb), ld_frag(sp->K, LQ, 16 * ct + c16, 32 * kb));
     const f32x4 gr4 = *reinterpret_cast<const f32x4*>(&sp->gam[16 * rt + 4 * g]);
-    const f32x4 br4 = *reinterpret_cast<const f32x4*>(&sp->beta[16 * rt + 4 * g]);
     const int c = 16 * ct + c16;
     const float gc = sp->gam[c];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rt + 4 * g + i;
-      const float dm = __expf(gr4[i] - gc);
-      if (!ISQ) {
-        if (r == c) sp->lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
-      } else {
-        sp->PT[c * LT + r] = to_e<E>((c <= r && r < rows) ? p.scale * acc[i] * dm : 0.f);
-      }
+      sp->PT[c * LT + r] = to_e<E>((c <= r && r < rows) ? p.scale * acc[i] * __expf(gr4[i] - gc) : 0.f);
     }
   }
 
   // dh: gradient at the chunk end on entry, at the chunk start on exit.
   // Prefetches chunk (ntok0, nrows) into ld (nrows = 0: none).  Returns Lambda_c.
-  // t_in: this chunk's T.
+  // t_in: this chunk's T; nrec: the next chunk's scalar record.
   __device__ static float step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows,
-                               int h, E* dhs_chunk, const float* t_in, f32x4 (&dh)[DK / 16][NTW]) {
+                               int h, E* dhs_chunk, const float* t_in, const float* nrec,
+                               f32x4 (&dh)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
@@ -160,87 +154,36 @@ struct RevChunk {
       ld.kq.store(qh ? s1.Q : s1.K, LQ, qh ? s1.QT : s1.KT, LT, kq_tid());
     }
     if (!CORR) ld.d.store(nullptr, 0, s1.DOT, LT);
-    if (w == 0) {
-      S& s = s1;
-      float gr, bt;
-      ld.sc.template gb_at<PREP>(l, p.prep, h, gr, bt);
-      const float gm = wave_incl_scan(gr);
-      const float gC = __shfl(gm, 63, 64);
-      const float Gm = __expf(gm);
-      s.gam[l] = gm;
-      s.Gam[l] = Gm;
-      s.sGam[l] = l < rows ? p.scale * Gm : 0.f;  // rows past the end carry copies of the last
-      s.ek[l] = __expf(gC - gm);
-      s.beta[l] = bt;
-      s.bg[l] = bt * Gm;
-      s.lam[l] = gr;
-      if (l == 0) s.GamC = __expf(gC);
+    static_assert(offsetof(S, tail) == offsetof(S, gam) + 5 * CH * sizeof(float), "record layout");
+    ld.rec.store(s1.gam);
+    if (tid >= CH / 4 && tid < CH / 2) {
+      // the threads that hold Gam form scale Gam, zero past the sequence end
+      const int r0 = 4 * tid - CH;
+      f32x4 sg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sg[i] = r0 + i < rows ? p.scale * ld.rec.rv[i] : 0.f;
+      *reinterpret_cast<f32x4*>(&s1.sGam[r0]) = sg;
     }
     __syncthreads();
 
-    // ---- 2. the diagonal tiles of K K^T (log-bound); Q K^T -> scale P^T.  Eight
-    //         waves: wave r < 4 forms K K^T's tile r; P^T tile j goes to wave
-    //         (j + 4) % 8 (at most two tiles a wave).  Four waves: waves 0, 1 take
-    //         the diagonal tiles of row tiles {0, 3} and {1, 2}, waves 2, 3 the rows
-    //         of P^T for those row tiles.
-    // T is requested now, past the staging, and lands in LDS at the end of
-    // this phase
+    // ---- 2. Q K^T -> scale P^T: the ten lower 16x16 tiles, tile j on wave j % NW
+    //         (at most two tiles a wave with eight waves).  T is requested now,
+    //         past the staging, and lands in LDS at the end of this phase.
     f32x4 tv[TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
-    if constexpr (NW == 8) {
+    if constexpr (!CORR) {
       S* sq = lds_opaque(&s0);
-      if (w < 4) kk_tile<false>(sq, p, w, w, g, c16, rows);
-      if (!CORR) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int pid = ((w + 4) & 7) + 8 * j;
-          const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
-          const int ct = pid - (rt * (rt + 1)) / 2;
-          if (pid < 10) kk_tile<true>(sq, p, rt, ct, g, c16, rows);
-        }
+      for (int j = 0; j < (10 + NW - 1) / NW; ++j) {
+        const int pid = w + NW * j;
+        const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
+        const int ct = pid - (rt * (rt + 1)) / 2;
+        if (pid < 10) pt_tile(sq, p, rt, ct, g, c16, rows);
       }
     }
     {
       S& s = *lds_opaque(&s0);
-      const bool isq = NW == 8 ? w >= 4 : w >= 2;
-      if (NW == 4 && (!isq || !CORR)) {
-        const E* X = isq ? s.Q : s.K;
-        auto row = [&](auto RT_) {
-          constexpr int RT = decltype(RT_)::value;
-          Frag<E> xa[DK / 32];
-#pragma unroll
-          for (int kb = 0; kb < DK / 32; ++kb) xa[kb] = ld_frag(X, LQ, 16 * RT + c16, 32 * kb);
-          const f32x4 gr4 = *reinterpret_cast<const f32x4*>(&s.gam[16 * RT + 4 * g]);
-          const f32x4 br4 = *reinterpret_cast<const f32x4*>(&s.beta[16 * RT + 4 * g]);
-#pragma unroll
-          for (int ct = 0; ct <= RT; ++ct) {
-            if (!isq && ct != RT) continue;  // K K^T: the diagonal tile only
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) mma(acc, xa[kb], ld_frag(s.K, LQ, 16 * ct + c16, 32 * kb));
-            const int c = 16 * ct + c16;
-            const float gc = s.gam[c];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 16 * RT + 4 * g + i;
-              const float dm = __expf(gr4[i] - gc);
-              if (!isq) {
-                if (r == c) s.lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
-              } else {
-                s.PT[c * LT + r] = to_e<E>((c <= r && r < rows) ? p.scale * acc[i] * dm : 0.f);
-              }
-            }
-          }
-        };
-        if constexpr (NW == 8) {
-          (void)row;
-        } else {
-          const bool rows03 = (w & 1) == 0;
-          if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
-          else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
-        }
-      }
 #pragma unroll
       for (int i = 0; i < TPT; ++i) {
         const int e = 4 * (tid + i * NT);
@@ -248,10 +191,10 @@ struct RevChunk {
       }
     }
     __syncthreads();
-    const float lam_c = __shfl(wave_sum(lds_opaque(&s0)->lam[l]), 0, 64);
+    const float lam_c = lds_opaque(&s0)->tail[0];  // the same value on every wave
 
     // ---- 3. the next chunk's tiles start their way from HBM
-    if (nrows > 0) issue(ld, p, ntok0, nrows, h);
+    if (nrows > 0) issue(ld, p, ntok0, nrows, h, nrec);
 
     // ---- 4. -W^T = -K^T diag(beta Gam) T^T: (Dk/16) x 4 tiles, KTW key tiles x
     //         RTW chunk-row tiles per wave
@@ -335,7 +278,7 @@ struct RevChunk {
           du[rt][nt] = acc;
         }
       }
-      const float gc = s.GamC;
+      const float gc = s.tail[1];
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         Frag<E> uf[2];
@@ -365,7 +308,7 @@ struct RevChunk {
     Loader ld;
     float lam = 0.f;
     int c = ce - 1;
-    if (c >= cb) issue(ld, p, seq0 + (int64_t)c * CH, min(CH, len - c * CH), h);
+    if (c >= cb) issue(ld, p, seq0 + (int64_t)c * CH, min(CH, len - c * CH), h, p.rec + ((chunk0 + c) * p.H + h) * RECF);
     const size_t SS = (size_t)DK * DV;
     E* dhs = static_cast<E*>(p.dhs);
     for (; c >= cb; --c) {
@@ -375,7 +318,8 @@ struct RevChunk {
       const int64_t ntok0 = seq0 + (int64_t)(c - 1) * CH;
       const int nrows = more ? min(CH, len - (c - 1) * CH) : 0;
       const size_t toff = ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
-      lam += step(s, p, ld, rows, ntok0, nrows, h, dhs + ((chunk0 + c) * p.H + h) * SS, p.t_in + toff, dh);
+      const float* nrec = more ? p.rec + ((chunk0 + c - 1) * p.H + h) * RECF : nullptr;
+      lam += step(s, p, ld, rows, ntok0, nrows, h, dhs + ((chunk0 + c) * p.H + h) * SS, p.t_in + toff, nrec, dh);
     }
     if (lowest) *lowest = c + 1;
     return lam;
@@ -699,9 +643,9 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         gr = -(p.prep.gate_scale ? p.prep.gate_scale[h] : 1.f) * softplus_f(gr);
         bt = sigmoid_f(bt);
       }
-      float gm = wave_incl_scan(gr);
-      float gC = __shfl(gm, 63, 64);
-      float Gm = __expf(gm);
+      const float gm = wave_incl_scan(gr);
+      const float gC = __shfl(gm, 63, 64);
+      const float Gm = __expf(gm);
       s.gam[l] = gm;
       s.Gam[l] = Gm;
       s.ek[l] = __expf(gC - gm);

@@ -38,6 +38,8 @@
 // pass and store the state at every chunk start.
 #include <type_traits>
 
+#include <cstddef>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_tiles.h"
@@ -58,8 +60,8 @@ struct alignas(16) FwdSmem {
   E P[CH * LT];
   float T[CH * LA];
   E O[CH * LO];
-  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], lam[CH];
-  float GamC;
+  // the chunk's scalar record, as laid out in memory (tail: Lambda_c, Gam_C)
+  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], tail[4];
 };
 
 // ------------------------------------------------------------------ prefetch
@@ -78,17 +80,15 @@ struct TileLoader {
   typedef E vec_t __attribute__((__vector_size__(16)));
   vec_t blk[NB > 0 ? NB : 1][4];
   vec_t qv[NQV > 0 ? NQV : 1];
-  float gr;  // raw values: converted where they are used, so that nothing waits
-  E be;      // for these loads while the next chunk's tiles are in flight
-  int nrow;
+  f32x4 rv;  // this thread's piece of the chunk's scalar record (threads < RECF / 4)
 
-  __device__ __forceinline__ void load(const FwdParams& p, int64_t tok0, int rows, int h) {
-    load_kv(p, tok0, rows, h);
+  __device__ __forceinline__ void load(const FwdParams& p, int64_t tok0, int rows, int h, const float* rec) {
+    load_kv(p, tok0, rows, h, rec);
     load_q(p, tok0, rows, h);
   }
 
-  // K / V blocks and g / beta
-  __device__ __forceinline__ void load_kv(const FwdParams& p, int64_t tok0, int rows, int h) {
+  // K / V blocks and the scalar record
+  __device__ __forceinline__ void load_kv(const FwdParams& p, int64_t tok0, int rows, int h, const float* rec) {
     const int H = p.H;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -107,14 +107,7 @@ struct TileLoader {
         }
       }
     }
-    if (threadIdx.x < 64) {
-      // unconditional load of a clamped row; rows past the chunk end are masked when used
-      const int l = threadIdx.x;
-      const int64_t si = (tok0 + min(l, rows - 1)) * H + h;
-      gr = p.g[si];
-      be = static_cast<const E*>(p.beta)[si];
-      nrow = rows;
-    }
+    if (threadIdx.x < RECF / 4) rv = *reinterpret_cast<const f32x4*>(rec + 4 * threadIdx.x);
   }
 
   __device__ __forceinline__ void load_q(const FwdParams& p, int64_t tok0, int rows, int h) {
@@ -130,16 +123,11 @@ struct TileLoader {
       }
     }
   }
-  // g and beta of row l of the chunk (zero past its end), after the optional
-  // gate / beta activation.
-  __device__ __forceinline__ void gb_at(int l, const PrepParams& pp, int h, float& g, float& b) const {
-    g = gr;
-    b = to_f(be);
-    if (PREP && pp.gate_act) {
-      g = -(pp.gate_scale ? pp.gate_scale[h] : 1.f) * softplus_f(g);
-      b = sigmoid_f(b);
-    }
-    if (l >= nrow) g = b = 0.f;
+  // the scalar record into LDS (gam .. tail are contiguous there as in memory)
+  template <class S>
+  __device__ __forceinline__ void store_rec(S& s) const {
+    static_assert(offsetof(S, tail) == offsetof(S, gam) + 5 * CH * sizeof(float), "record layout");
+    if (threadIdx.x < RECF / 4) *reinterpret_cast<f32x4*>(&s.gam[4 * threadIdx.x]) = rv;
   }
 
   // Divide every row of K and Q by its L2 norm (q / k pre-processing).  A row's
@@ -234,42 +222,32 @@ struct Chunk {
   using S = FwdSmem<E, DK, DV>;
   using Loader = TileLoader<E, DK, DV, NT, OUT, !CORR, PREP>;
 
-  // ISQ false: the diagonal 16x16 tile rt = ct of K K^T, whose diagonal gives
-  // the log-bound terms log max(1, |1 - beta |k|^2|); ISQ true: one lower tile
-  // (rt, ct) of P = (Q K^T) * M.
-  template <bool ISQ>
-  __device__ __forceinline__ static void kk_tile(S* sp, int rt, int ct, int g, int c16) {
+  // One lower 16x16 tile (rt, ct) of P = (Q K^T) * M.
+  __device__ __forceinline__ static void p_tile(S* sp, int rt, int ct, int g, int c16) {
     constexpr int LQ = S::LQ, LT = S::LT;
-    const E* X = ISQ ? sp->Q : sp->K;
     f32x4 acc = zero4();
 #pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb)
-      mma(acc, ld_frag(X, LQ, 16 * rt + c16, 32 * kb), ld_frag(sp->K, LQ, 16 * ct + c16, 32 * kb));
+      mma(acc, ld_frag(sp->Q, LQ, 16 * rt + c16, 32 * kb), ld_frag(sp->K, LQ, 16 * ct + c16, 32 * kb));
     const f32x4 gr4 = *reinterpret_cast<const f32x4*>(&sp->gam[16 * rt + 4 * g]);
-    const f32x4 br4 = *reinterpret_cast<const f32x4*>(&sp->beta[16 * rt + 4 * g]);
     const int c = 16 * ct + c16;
     const float gc = sp->gam[c];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rt + 4 * g + i;
-      const float dm = __expf(gr4[i] - gc);
-      if (!ISQ) {
-        if (r == c) sp->lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
-      } else {
-        sp->P[r * LT + c] = to_e<E>((c <= r) ? acc[i] * dm : 0.f);
-      }
+      sp->P[r * LT + c] = to_e<E>((c <= r) ? acc[i] * __expf(gr4[i] - gc) : 0.f);
     }
   }
 
   // Process the chunk whose tiles `ld` holds; prefetch the next chunk (if any)
   // into `ld`.  hacc: this wave's state columns (chunk start on entry, chunk end
   // on exit).  Returns the chunk's log-bound Lambda_c.
-  // t_in: this chunk's T.
+  // t_in: this chunk's T; nrec: the next chunk's scalar record.
   // us_chunk: where this chunk's U = Ut - W h goes (nullable; CORR adds its
   // correction).
   __device__ static float step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows,
                                int64_t ntok0, int nrows, int h, E* hs_chunk, const float* t_in,
-                               E* us_chunk, f32x4 (&hacc)[DK / 16][NTW]) {
+                               const float* nrec, E* us_chunk, f32x4 (&hacc)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA, LO = S::LO;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
@@ -311,21 +289,7 @@ struct Chunk {
     S* sp = lds_opaque(&s0);
     if (PREP && p.prep.qk_norm) ld.normalize();
     ld.store(*sp);
-    if (w == 0) {
-      float gr, bt;
-      ld.gb_at(l, p.prep, h, gr, bt);
-      const float gm = wave_incl_scan(gr);
-      const float gC = __shfl(gm, 63, 64);
-      const float Gm = __expf(gm);
-      sp->gam[l] = gm;
-      sp->Gam[l] = Gm;
-      sp->ek[l] = __expf(gC - gm);
-      sp->beta[l] = bt;
-      sp->bg[l] = bt * Gm;
-      // per-token log-bound; the log max(1, |1 - beta |k|^2|) part is added with K K^T
-      sp->lam[l] = gr;
-      if (l == 0) sp->GamC = __expf(gC);
-    }
+    ld.store_rec(*sp);
     // chunk-start state out, as S (Dv x Dk) in 4 x 16 blocks: the lane's four
     // rows of one column are contiguous.  A correction adds to the stored
     // state: it requests the current values here and writes the sums after
@@ -344,62 +308,15 @@ struct Chunk {
     __syncthreads();
     sp = lds_opaque(sp);
 
-    // ---- 2. the diagonal tiles of K K^T (log-bound) and, for the output, the
-    //         lower 16x16 tiles of P = (Q K^T) * M.  Eight waves: wave r < 4 forms
-    //         K K^T's tile r; P tile j goes to wave (j + 4) % 8 (at most two tiles a
-    //         wave).  Four waves: waves 0, 1 take the diagonal tiles of row tiles
-    //         {0, 3} and {1, 2}, waves 2, 3 the rows of P for those row tiles,
-    //         loading their row-side fragments once per row.
-    if constexpr (NW == 8) {
-      if (w < 4) kk_tile<false>(sp, w, w, g, c16);
-      if (OUT) {
+    // ---- 2. for the output, the ten lower 16x16 tiles of P = (Q K^T) * M, tile j
+    //         on wave j % NW (at most two tiles a wave with eight waves)
+    if constexpr (OUT) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int pid = ((w + 4) & 7) + 8 * j;
-          const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
-          const int ct = pid - (rt * (rt + 1)) / 2;
-          if (pid < 10) kk_tile<true>(sp, rt, ct, g, c16);
-        }
-      }
-    }
-    {
-      const bool isq = NW == 8 ? w >= 4 : w >= 2;
-      if (NW == 4 && (!isq || OUT)) {
-        const E* X = isq ? sp->Q : sp->K;
-        auto row = [&](auto RT_) {
-          constexpr int RT = decltype(RT_)::value;
-          Frag<E> xa[DK / 32];
-#pragma unroll
-          for (int kb = 0; kb < DK / 32; ++kb) xa[kb] = ld_frag(X, LQ, 16 * RT + c16, 32 * kb);
-          f32x4 gr4 = *reinterpret_cast<const f32x4*>(&sp->gam[16 * RT + 4 * g]);
-          f32x4 br4 = *reinterpret_cast<const f32x4*>(&sp->beta[16 * RT + 4 * g]);
-#pragma unroll
-          for (int ct = 0; ct <= RT; ++ct) {
-            if (!isq && ct != RT) continue;  // K K^T: the diagonal tile only
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) mma(acc, xa[kb], ld_frag(sp->K, LQ, 16 * ct + c16, 32 * kb));
-            const int c = 16 * ct + c16;
-            const float gc = sp->gam[c];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 16 * RT + 4 * g + i;
-              const float dm = __expf(gr4[i] - gc);
-              if (!isq) {
-                if (r == c) sp->lam[r] += __logf(fmaxf(1.f, fabsf(1.f - br4[i] * acc[i])));
-              } else {
-                sp->P[r * LT + c] = to_e<E>((c <= r) ? acc[i] * dm : 0.f);
-              }
-            }
-          }
-        };
-        if constexpr (NW == 8) {
-          (void)row;
-        } else {
-          const bool rows03 = (w & 1) == 0;
-          if (rows03) { row(std::integral_constant<int, 0>{}); row(std::integral_constant<int, 3>{}); }
-          else { row(std::integral_constant<int, 1>{}); row(std::integral_constant<int, 2>{}); }
-        }
+      for (int j = 0; j < (10 + NW - 1) / NW; ++j) {
+        const int pid = w + NW * j;
+        const int rt = pid < 1 ? 0 : (pid < 3 ? 1 : (pid < 6 ? 2 : 3));
+        const int ct = pid - (rt * (rt + 1)) / 2;
+        if (pid < 10) p_tile(sp, rt, ct, g, c16);
       }
     }
 #pragma unroll
@@ -409,13 +326,11 @@ struct Chunk {
     }
     __syncthreads();
     sp = lds_opaque(sp);
-    // lane 0's sum: every wave reduces the same values in the same order, so the
-    // value (and the loop decisions taken on it) is identical across the workgroup
-    const float lam_c = __shfl(wave_sum(sp->lam[l]), 0, 64);
+    const float lam_c = sp->tail[0];  // the same value on every wave
 
-    // ---- 3. the next chunk's k, v, g, beta (and q) start their way from HBM
+    // ---- 3. the next chunk's k, v, scalar record (and q) start their way from HBM
     if (nrows > 0) {
-      ld.load_kv(p, ntok0, nrows, h);
+      ld.load_kv(p, ntok0, nrows, h, nrec);
       if (OUT) ld.load_q(p, ntok0, nrows, h);
     }
 
@@ -546,7 +461,7 @@ struct Chunk {
     __builtin_amdgcn_sched_barrier(0);
     sp = lds_opaque(sp);
     {
-      const float gc = sp->GamC;
+      const float gc = sp->tail[1];
       f32x4 e0[2], e1[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -597,7 +512,7 @@ struct Chunk {
     Loader ld;
     float lam = 0.f;
     int c = cb;
-    if (cb < ce) ld.load(p, seq0 + (int64_t)cb * CH, min(CH, len - cb * CH), h);
+    if (cb < ce) ld.load(p, seq0 + (int64_t)cb * CH, min(CH, len - cb * CH), h, p.rec + ((chunk0 + cb) * p.H + h) * RECF);
     const size_t SS = (size_t)DK * DV;
     E* hs = static_cast<E*>(p.hs);
     for (; c < ce; ++c) {
@@ -609,7 +524,8 @@ struct Chunk {
       E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
       const size_t toff = ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
       E* usc = USAVE ? static_cast<E*>(p.us) + ((chunk0 + c) * p.H + h) * (size_t)(CH * DV) : nullptr;
-      lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, p.t_in + toff, usc, hacc);
+      const float* nrec = more ? p.rec + ((chunk0 + c + 1) * p.H + h) * RECF : nullptr;
+      lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, p.t_in + toff, nrec, usc, hacc);
     }
     if (done) *done = c - cb;
     return lam;

@@ -38,9 +38,20 @@ struct FwdParams {
   void* us;                // nullable: [total chunks][H][DV/16][CH][16] U = Ut - W h of each chunk in 16-column blocks (dtype)
   // [total chunks][H][CH][CH] fp32 row-major T = (I + diag(beta) A)^-1 of each chunk
   const float* t_in;
+  const float* rec;        // [total chunks][H][RECF] scalar records
   int phase;               // 1 = segments from zero / h0, 3 = boundary corrections
   PrepParams prep;
 };
+
+// Scalar record of a chunk (fp32, RECF values, 16-byte multiple), written by
+// the T solve beside T and read by the chunk chains in place of g and beta:
+//   [0, 64)    gam_r = sum_{i<=r} g_i         [64, 128)  Gam_r = exp(gam_r)
+//   [128, 192) ek_r = exp(gam_63 - gam_r)      [192, 256) beta_r
+//   [256, 320) bg_r = beta_r Gam_r             320: Lambda_c, 321: exp(gam_63), 322..323: 0
+// (g, beta after the optional activation; rows past a sequence end have g = 0,
+// beta = 0).  Lambda_c = sum_r [g_r + log max(1, |1 - beta_r |k_r|^2|)] is the
+// chunk's log-bound on the norm of its state transition.
+constexpr int RECF = 5 * CH + 4;
 
 // Every chunk's T = (I + diag(beta) strict_lower(K K^T * D))^-1, chunk-parallel.
 struct TSolveParams {
@@ -48,6 +59,7 @@ struct TSolveParams {
   const float* g;
   const void* beta;
   float* t_out;            // [total chunks][H][CH][CH] fp32 row-major
+  float* rec_out;          // [total chunks][H][RECF] scalar records
   int H;
   SeqInfo seq;
   const int2* chunk_tab;   // [total chunks] (sequence, chunk index within it)
@@ -73,6 +85,7 @@ struct RevParams {
   float* lam;              // [total segments][H]
   void* dhs;               // [total chunks][H] gradient at each chunk END, S-shaped, st_blk order (dtype)
   const float* t_in;       // chunk matrices T (as FwdParams)
+  const float* rec;        // scalar records (as FwdParams)
   int phase;
   PrepParams prep;
 };

@@ -239,32 +239,16 @@ __device__ __forceinline__ void st_tile_rows(E* base, int ld, int r0, int c0, co
   st4_transposed<E>(base + (r0 + 4 * g + b) * ld + c0 + 4 * q, acc);
 }
 
-// g / beta of one chunk for threads 0..63 (one row each), masked at use.
-template <class E>
-struct ScalarPart {
-  float gr;  // raw values: converted where they are used, so that nothing waits
-  E be;      // for these loads while the next chunk's tiles are in flight
-  int nrow;
-  __device__ __forceinline__ void load(const float* g, const E* beta, int64_t tok0, int H, int h, int rows) {
-    if (threadIdx.x < 64) {
-      // uniform row base + a 32-bit per-lane offset
-      const int64_t s0 = tok0 * H + h;
-      const uint32_t si = (uint32_t)min((int)threadIdx.x, rows - 1) * (uint32_t)H;
-      gr = (g + s0)[si];
-      be = (beta + s0)[si];
-      nrow = rows;
-    }
+// This thread's 16-byte piece of a chunk's scalar record (threads < RECF / 4),
+// prefetched with the chunk's tiles; store() writes it to LDS, where the
+// record's arrays lie as in memory.
+struct RecordPart {
+  f32x4 rv;
+  __device__ __forceinline__ void load(const float* rec) {
+    if (threadIdx.x < RECF / 4) rv = *reinterpret_cast<const f32x4*>(rec + 4 * threadIdx.x);
   }
-  // g and beta of row l (zero past the chunk end), after the optional activation.
-  template <bool PREP>
-  __device__ __forceinline__ void gb_at(int l, const PrepParams& pp, int h, float& g, float& b) const {
-    g = gr;
-    b = to_f(be);
-    if (PREP && pp.gate_act) {
-      g = -(pp.gate_scale ? pp.gate_scale[h] : 1.f) * softplus_f(g);
-      b = sigmoid_f(b);
-    }
-    if (l >= nrow) g = b = 0.f;
+  __device__ __forceinline__ void store(float* dst) const {
+    if (threadIdx.x < RECF / 4) *reinterpret_cast<f32x4*>(dst + 4 * threadIdx.x) = rv;
   }
 };
 

@@ -13,7 +13,10 @@
 // (T takes the place of K once K K^T is formed), so four workgroups share a
 // compute unit and one's solve overlaps another's loads.
 // Rows past a sequence end are zero in K and carry beta = 0, so their rows and
-// columns of T are those of the identity.
+// columns of T are those of the identity.  Beside T it writes the chunk's
+// scalar record (decay cumsum and exponentials, beta, the log-bound; layout in
+// gdn_internal.h), which the chunk chains and the gradient kernel read instead
+// of g and beta.
 #include "gdn_internal.h"
 #include "gdn_tiles.h"
 
@@ -27,7 +30,7 @@ struct TSolveSmem {
   static constexpr int KB = CH * LK * (int)sizeof(E), TB = CH * LA * 4;
   alignas(16) char kt[KB > TB ? KB : TB];  // K, then T
   alignas(16) float KD[CH * LA];
-  float gam[CH], beta[CH];
+  float gam[CH], beta[CH], graw[CH], kk[CH];  // kk: |k_r|^2
   __device__ E* K() { return reinterpret_cast<E*>(kt); }
   __device__ float* T() { return reinterpret_cast<float*>(kt); }
 };
@@ -57,6 +60,7 @@ __global__ __launch_bounds__(192) void gdn_tsolve(TSolveParams p) {
     }
     s.gam[l] = wave_incl_scan(gr);
     s.beta[l] = bt;
+    s.graw[l] = gr;
   }
   if (PREP && p.prep.qk_norm) tk.normalize_rows(tid);
   tk.store(s.K(), LK, nullptr, 0, tid);
@@ -102,6 +106,11 @@ __global__ __launch_bounds__(192) void gdn_tsolve(TSolveParams p) {
           const int r = 16 * rt + 4 * g + i;
           s.KD[r * LA + c] = (c < r) ? acc[j][i] * __expf(gr4[i] - gc) : 0.f;
         }
+        if (rt == ctl) {  // a diagonal tile (wave-uniform): |k_r|^2, for the log-bound
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * rt + 4 * g + i == c) s.kk[c] = acc[j][i];
+        }
       }
     }
   }
@@ -114,7 +123,21 @@ __global__ __launch_bounds__(192) void gdn_tsolve(TSolveParams p) {
     const int I = blk < 3 ? 0 : (blk < 5 ? 1 : 2), J = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
     *reinterpret_cast<f32x4*>(&sT[(16 * I + (q >> 2)) * LA + 16 * J + 4 * (q & 3)]) = zero4();
   }
-  if (w < 2) solve_diag_pair(s.KD, sT, w, 3 - w, s.beta);
+  if (w < 2) {
+    solve_diag_pair(s.KD, sT, w, 3 - w, s.beta);
+  } else {
+    // the scalar record, while waves 0 and 1 solve
+    float* rec = p.rec_out + ((size_t)blockIdx.x * H + h) * RECF;
+    const float gm = s.gam[l], gC = s.gam[CH - 1], bt = s.beta[l];
+    const float Gm = __expf(gm);
+    rec[l] = gm;
+    rec[CH + l] = Gm;
+    rec[2 * CH + l] = __expf(gC - gm);
+    rec[3 * CH + l] = bt;
+    rec[4 * CH + l] = bt * Gm;
+    const float lam = __shfl(wave_sum(s.graw[l] + __logf(fmaxf(1.f, fabsf(1.f - bt * s.kk[l])))), 0, 64);
+    if (l < 4) rec[5 * CH + l] = l == 0 ? lam : (l == 1 ? __expf(gC) : 0.f);
+  }
   __syncthreads();
   solve_columns(s.KD, sT, w, s.beta);
   __syncthreads();

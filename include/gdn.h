@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 typedef enum {
   GDN_OK = 0,
@@ -158,17 +158,22 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args);
  * without error when there are no tokens). */
 size_t gdn_chunk_states_bytes(const gdn_common_args* a);
 
-/* Bytes of the saved chunk matrices (t_save / t_saved): C * H * 64 * 64 fp32
- * values, C as above.  Entry (c, h) at element offset (c * H + h) * 4096 is the
- * 64 x 64 row-major lower-triangular matrix
+/* Bytes of the saved chunk matrices (t_save / t_saved): C * H * (64 * 64 + 324)
+ * fp32 values, C as above.  Entry (c, h) at element offset (c * H + h) * 4096 is
+ * the 64 x 64 row-major lower-triangular matrix
  *     T = (I + diag(beta) strict_lower((K K^T) * D))^-1,   D[r][i] = exp(G_r - G_i),
  * of chunk c and head h (K: the chunk's 64 keys as rows, after the optional
  * normalisation; beta after the optional activation; G_r the running sum of
  * g over the chunk up to row r), the inverse of the chunk's unit lower-
  * triangular system in the WY/UT form ("FlashQLA resource", section 3).  Rows
- * past a sequence's end have beta = 0 (rows of the identity).  Returns 0 and
- * sets the error string for invalid arguments (and returns 0 without error
- * when there are no tokens). */
+ * past a sequence's end have beta = 0 (rows of the identity).  After the
+ * C * H matrices, at element offset C * H * 4096 + (c * H + h) * 324, the
+ * chunk's scalar record (g, beta after the optional activation; rows past a
+ * sequence end have g = beta = 0): G_r (64 values), exp(G_r), exp(G_63 - G_r),
+ * beta_r, beta_r exp(G_r), then Lambda = sum_r [g_r + log max(1, |1 - beta_r
+ * |k_r|^2|)] (the log-bound on the chunk's state transition), exp(G_63), 0, 0.
+ * Returns 0 and sets the error string for invalid arguments (and returns 0
+ * without error when there are no tokens). */
 size_t gdn_chunk_t_bytes(const gdn_common_args* a);
 
 /* Forward: o and (optionally) hT, the chunk states and the chunk matrices T.

@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(L):
             "gdn_chunk_bwd_workspace_size", "gdn_last_error", "gdn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdn_abi_version() == 7
+    assert L.gdn_abi_version() == 8
 
 
 FAKE = 1 << 20  # a 16-byte aligned fake device address; never dereferenced
@@ -126,11 +126,14 @@ def test_misaligned_saved_states_rejected(L):
     assert call_fwd(L, f) == 1
 
 
+REC = 5 * 64 + 4   # floats of a chunk's scalar record
+
+
 def test_t_bytes(L):
     f = fwd_args()                                        # B=1, T=128, H=2
-    assert L.gdn_chunk_t_bytes(ctypes.byref(f.a)) == 2 * 2 * 64 * 64 * 4
+    assert L.gdn_chunk_t_bytes(ctypes.byref(f.a)) == 2 * 2 * (64 * 64 + REC) * 4
     f = fwd_args(dtype=B.GDN_F32, Dk=64, Dv=64, T=129)
-    assert L.gdn_chunk_t_bytes(ctypes.byref(f.a)) == 3 * 2 * 64 * 64 * 4
+    assert L.gdn_chunk_t_bytes(ctypes.byref(f.a)) == 3 * 2 * (64 * 64 + REC) * 4
     assert L.gdn_chunk_t_bytes(ctypes.byref(fwd_args(Dk=96).a)) == 0
 
 
@@ -141,10 +144,10 @@ def test_saved_t_shrinks_workspaces(L):
     full = L.gdn_chunk_bwd_workspace_size(ctypes.byref(b))
     b.t_saved = FAKE
     assert full - L.gdn_chunk_bwd_workspace_size(ctypes.byref(b)) >= 2 * 2 * 64 * 64 * 4
-    f = fwd_args(T=4096, cp_mode=8)                       # segments: the corrections read T
+    f = fwd_args(T=4096)
     full = L.gdn_chunk_fwd_workspace_size(ctypes.byref(f))
     f.t_save = FAKE
-    assert full - L.gdn_chunk_fwd_workspace_size(ctypes.byref(f)) >= 64 * 2 * 64 * 64 * 4
+    assert full - L.gdn_chunk_fwd_workspace_size(ctypes.byref(f)) >= 64 * 2 * (64 * 64 + REC) * 4
 
 
 def dec_args(**kw):

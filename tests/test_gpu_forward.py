@@ -188,3 +188,52 @@ def test_saved_t_matches_oracle(dev, dtype, Dk, Dv, cp):
     err = relerr(got, want)
     print(f"    T {err:.3e}", flush=True)
     assert err <= 1e-3
+
+
+@pytest.mark.parametrize("cp", [-1, 2])
+def test_saved_scalar_record(dev, cp):
+    """The scalar record saved after the chunk matrices (gdn_chunk_t_bytes):
+    decay cumsum G and its exponentials, beta, beta exp(G), the log-bound Lambda
+    and exp(G_63) of every chunk, against their definitions in float64."""
+    import torch
+    from gated_deltanet_chunked_delta_amd import gdn_chunk_fwd
+    lens = [130, 0, 64, 257, 5]
+    cu = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    H = 2
+    x = gdn_inputs.generate(B=1, T=int(cu[-1]), H=H, Dk=128, Dv=128, dtype="bf16", seed=57)
+    x.cu_seqlens = cu
+    print(f"[fwd] saved scalar record cp={cp}", flush=True)
+    t = to_torch(x, dev)
+    res = gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], x.scale, cu_seqlens=t["cu"],
+                        cu_seqlens_host=cu, cp_mode=cp, save_t=True)
+    torch.cuda.synchronize()
+    flat = res[2].cpu().numpy().astype(np.float64)
+    nch = sum((n + 63) // 64 for n in lens)
+    rec = flat[nch * H * 4096:nch * H * (4096 + 324)].reshape(nch, H, 324)
+    g, beta, k = (np.asarray(a, dtype=np.float64) for a in (x.g[0], x.beta[0], x.k[0]))
+    want = np.zeros_like(rec)
+    c = 0
+    for n, L in enumerate(lens):
+        for j in range((L + 63) // 64):
+            rows = min(64, L - 64 * j)
+            s0 = cu[n] + 64 * j
+            for h in range(H):
+                gg = np.zeros(64); bb = np.zeros(64); kk2 = np.zeros(64)
+                gg[:rows] = g[s0:s0 + rows, h]
+                bb[:rows] = beta[s0:s0 + rows, h]
+                kk2[:rows] = np.sum(k[s0:s0 + rows, h] ** 2, axis=-1)
+                G = np.cumsum(gg)
+                want[c, h, 0:64] = G
+                want[c, h, 64:128] = np.exp(G)
+                want[c, h, 128:192] = np.exp(G[63] - G)
+                want[c, h, 192:256] = bb
+                want[c, h, 256:320] = bb * np.exp(G)
+                want[c, h, 320] = np.sum(gg + np.log(np.maximum(1.0, np.abs(1.0 - bb * kk2))))
+                want[c, h, 321] = np.exp(G[63])
+            c += 1
+    for lo, hi, name in ((0, 64, "G"), (64, 128, "exp G"), (128, 192, "exp(G_C - G)"), (192, 256, "beta"),
+                         (256, 320, "beta exp G"), (320, 321, "Lambda"), (321, 324, "exp G_C, 0, 0")):
+        err = relerr(rec[..., lo:hi], want[..., lo:hi])
+        print(f"    {name} {err:.3e}", flush=True)
+        assert err <= 1e-5, name
