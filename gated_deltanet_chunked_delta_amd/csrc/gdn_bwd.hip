@@ -303,12 +303,18 @@ struct RevChunk {
 
   // Chunks ce-1 down to cb; CORR stops once the accumulated bound is below 2^-24.
   // Returns Lambda over the processed chunks; *lowest = last chunk processed.
+  // Issue the loads of chunk ce - 1, the first of a run (before the state
+  // gradient is loaded, so that the two are in flight together).
+  __device__ static void prime(Loader& ld, const RevParams& p, int64_t seq0, int len, int64_t chunk0, int cb, int ce,
+                               int h) {
+    const int c = ce - 1;
+    if (c >= cb) issue(ld, p, seq0 + (int64_t)c * CH, min(CH, len - c * CH), h, p.rec + ((chunk0 + c) * p.H + h) * RECF);
+  }
+  // ld: primed for chunk ce - 1.
   __device__ static float run(S& s, const RevParams& p, int64_t seq0, int len, int64_t chunk0, int cb, int ce,
-                              int h, f32x4 (&dh)[DK / 16][DV / (16 * RevWaves<DV>::NW)], int* lowest) {
-    Loader ld;
+                              int h, f32x4 (&dh)[DK / 16][DV / (16 * RevWaves<DV>::NW)], int* lowest, Loader& ld) {
     float lam = 0.f;
     int c = ce - 1;
-    if (c >= cb) issue(ld, p, seq0 + (int64_t)c * CH, min(CH, len - c * CH), h, p.rec + ((chunk0 + c) * p.H + h) * RECF);
     const size_t SS = (size_t)DK * DV;
     E* dhs = static_cast<E*>(p.dhs);
     for (; c >= cb; --c) {
@@ -375,10 +381,13 @@ __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p1(RevParams p)
   const size_t SS = (size_t)DK * DV;
   const float* dhT = p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr;
   f32x4 dh[DK / 16][DV / (16 * RevWaves<DV>::NW)];
+  using C = RevChunk<E, DK, DV, false, PREP>;
+  typename C::Loader ld;
+  C::prime(ld, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n], sd.c_begin, sd.c_end, h);
   rev_init_smem(s);
   rev_load<E, DK, DV>(dh, sd.s == nseg - 1 ? dhT : nullptr);
-  const float lam = RevChunk<E, DK, DV, false, PREP>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
-                                                    sd.c_begin, sd.c_end, h, dh, nullptr);
+  const float lam = C::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n], sd.c_begin, sd.c_end, h, dh,
+                           nullptr, ld);
   if (nseg == 1) {
     if (p.dh0) rev_store<E, DK, DV>(dh, p.dh0 + ((size_t)n * p.H + h) * SS, nullptr, true);
   } else {
@@ -402,20 +411,25 @@ __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p3(RevParams p)
   const size_t SS = (size_t)DK * DV;
   const int64_t chunk0 = p.chunk_first[n];
   float* dh0 = p.dh0 ? p.dh0 + ((size_t)n * p.H + h) * SS : nullptr;
-  bool ok = true;
-  for (int j = 1; j + 1 < nseg; ++j) ok = ok && (p.lam[(size_t)(seg0 + j) * p.H + h] <= LN_EPS);
+  const bool ok = interior_segments_decay(p.lam, seg0, nseg, p.H, h, LN_EPS);
   if (!ok && sd.s != 0) return;
   f32x4 dh[DK / 16][DV / (16 * RevWaves<DV>::NW)];
   rev_init_smem(s);
   if (!ok) {
+    using C = RevChunk<E, DK, DV, false, PREP>;
+    typename C::Loader ld;
+    C::prime(ld, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h);
     rev_load<E, DK, DV>(dh, p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr);
-    RevChunk<E, DK, DV, false, PREP>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, dh, nullptr);
+    C::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, dh, nullptr, ld);
     if (dh0) rev_store<E, DK, DV>(dh, dh0, nullptr, true);
     return;
   }
+  using C = RevChunk<E, DK, DV, true, PREP>;
+  typename C::Loader ld;
+  C::prime(ld, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h);
   rev_load<E, DK, DV>(dh, p.bstate + ((size_t)(blockIdx.x + 1) * p.H + h) * SS);
   int lowest = sd.c_end;
-  RevChunk<E, DK, DV, true, PREP>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, dh, &lowest);
+  C::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, dh, &lowest, ld);
   if (sd.s == 0 && dh0)
     rev_store<E, DK, DV>(dh, dh0, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, lowest == sd.c_begin);
 }

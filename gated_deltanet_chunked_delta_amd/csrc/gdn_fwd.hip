@@ -507,12 +507,17 @@ struct Chunk {
   // Run chunks [cb, ce) of sequence (seq0, len) from the state in hacc.
   // CORR runs stop early once the accumulated bound falls under 2^-24; the
   // number of chunks processed is returned through *done.
+  // Issue the loads of chunk cb, the first of a run (before the state is loaded,
+  // so that the two are in flight together).
+  __device__ static void prime(Loader& ld, const FwdParams& p, int64_t seq0, int len, int64_t chunk0, int cb,
+                               int ce, int h) {
+    if (cb < ce) ld.load(p, seq0 + (int64_t)cb * CH, min(CH, len - cb * CH), h, p.rec + ((chunk0 + cb) * p.H + h) * RECF);
+  }
+  // ld: primed for chunk cb.
   __device__ static float run(S& s, const FwdParams& p, int64_t seq0, int len, int64_t chunk0, int cb,
-                              int ce, int h, f32x4 (&hacc)[DK / 16][NTW], int* done) {
-    Loader ld;
+                              int ce, int h, f32x4 (&hacc)[DK / 16][NTW], int* done, Loader& ld) {
     float lam = 0.f;
     int c = cb;
-    if (cb < ce) ld.load(p, seq0 + (int64_t)cb * CH, min(CH, len - cb * CH), h, p.rec + ((chunk0 + cb) * p.H + h) * RECF);
     const size_t SS = (size_t)DK * DV;
     E* hs = static_cast<E*>(p.hs);
     for (; c < ce; ++c) {
@@ -583,10 +588,13 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p)
   const int nseg = p.seg_first[n + 1] - p.seg_first[n];
   const size_t SS = (size_t)DK * DV;
   f32x4 hacc[DK / 16][DV / (16 * FwdWaves<DV>::NW)];
+  using C = Chunk<E, DK, DV, OUT, false, PREP, USAVE>;
+  typename C::Loader ld;
+  C::prime(ld, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n], sd.c_begin, sd.c_end, h);
   init_smem(s);
   load_state<E, DK, DV>(hacc, (sd.s == 0 && p.h0) ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-  const float lam = Chunk<E, DK, DV, OUT, false, PREP, USAVE>::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n],
-                                                      sd.c_begin, sd.c_end, h, hacc, nullptr);
+  const float lam = C::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n], sd.c_begin, sd.c_end, h, hacc,
+                           nullptr, ld);
   if (nseg == 1) {
     if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
   } else {
@@ -608,22 +616,26 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p3(FwdParams p)
   const int len = p.seq.len(n);
   const size_t SS = (size_t)DK * DV;
   const int64_t chunk0 = p.chunk_first[n];
-  bool ok = true;
-  for (int j = 1; j + 1 < nseg; ++j) ok = ok && (p.lam[(size_t)(seg0 + j) * p.H + h] <= LN_EPS);
+  const bool ok = interior_segments_decay(p.lam, seg0, nseg, p.H, h, LN_EPS);
   if (!ok && sd.s != 1) return;
   f32x4 hacc[DK / 16][DV / (16 * FwdWaves<DV>::NW)];
   init_smem(s);
   if (!ok) {
     // Gates do not decay fast enough to cut this sequence: one workgroup redoes it serially.
+    using C = Chunk<E, DK, DV, OUT, false, PREP, USAVE>;
+    typename C::Loader ld;
+    C::prime(ld, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h);
     load_state<E, DK, DV>(hacc, p.h0 ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-    Chunk<E, DK, DV, OUT, false, PREP, USAVE>::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc,
-                                                          nullptr);
+    C::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc, nullptr, ld);
     if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
     return;
   }
+  using C = Chunk<E, DK, DV, OUT, true, PREP, USAVE>;
+  typename C::Loader ld;
+  C::prime(ld, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h);
   load_state<E, DK, DV>(hacc, p.bstate + ((size_t)(blockIdx.x - 1) * p.H + h) * SS);
   int done = 0;
-  Chunk<E, DK, DV, OUT, true, PREP, USAVE>::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done);
+  C::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done, ld);
   if (sd.s == nseg - 1 && p.hT) {
     // hT = b_last + (the correction propagated through the whole last segment, if it got there)
     const float* b = p.bstate + ((size_t)blockIdx.x * p.H + h) * SS;
