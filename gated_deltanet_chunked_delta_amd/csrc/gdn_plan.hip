@@ -15,11 +15,77 @@ namespace gdn {
 
 constexpr int PLAN_NT = 1024;
 
+// Up to 64 sequences: one wave scans the counts with lane shuffles, and the
+// prefixes stay in LDS for the table fill (no barrier-stepped block scan, no
+// round trip through global memory).
+constexpr int PLAN_SMALL = 64;
+
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (l >= o) x += y;
+  }
+  return x;
+}
+
 __global__ __launch_bounds__(PLAN_NT) void gdn_plan_kernel(SeqInfo seq, int N, int segc, int* chunk_first,
                                                           int* seg_first, SegDesc* segs, int2* chunk_tab) {
   __shared__ int sc[PLAN_NT], ss[PLAN_NT];
   __shared__ int carry_c, carry_s;
   const int tid = threadIdx.x;
+  if (N <= PLAN_SMALL) {
+    // sc[n] / ss[n]: first chunk / segment of sequence n, n <= N
+    if (tid < 64) {
+      int nc = 0, ns = 0;
+      if (tid < N) {
+        nc = (seq.len(tid) + CH - 1) / CH;
+        ns = nc == 0 ? 1 : (nc + segc - 1) / segc;
+      }
+      const int ic = wave_incl_scan_i(nc), is = wave_incl_scan_i(ns);
+      if (tid < N) {
+        sc[tid] = ic - nc;
+        ss[tid] = is - ns;
+        chunk_first[tid] = ic - nc;
+        seg_first[tid] = is - ns;
+      }
+      if (tid == 63) {
+        sc[N] = ic;
+        ss[N] = is;
+        chunk_first[N] = ic;
+        seg_first[N] = is;
+      }
+    }
+    __syncthreads();
+    const int total_s = ss[N], total_c = sc[N];
+    for (int j = tid; j < total_s; j += PLAN_NT) {
+      int n = 0, hi = N - 1;
+      while (n < hi) {
+        const int mid = (n + hi + 1) >> 1;
+        if (ss[mid] <= j) n = mid; else hi = mid - 1;
+      }
+      const int s = j - ss[n];
+      const int nc = sc[n + 1] - sc[n];
+      SegDesc d;
+      d.n = n;
+      d.s = s;
+      d.c_begin = min(nc, s * segc);
+      d.c_end = min(nc, (s + 1) * segc);
+      segs[j] = d;
+    }
+    for (int c = tid; c < total_c; c += PLAN_NT) {
+      // the last sequence whose first chunk is <= c owns c (empty sequences share
+      // their prefix with the next one)
+      int n = 0, hi = N - 1;
+      while (n < hi) {
+        const int mid = (n + hi + 1) >> 1;
+        if (sc[mid] <= c) n = mid; else hi = mid - 1;
+      }
+      chunk_tab[c] = make_int2(n, c - sc[n]);
+    }
+    return;
+  }
   if (tid == 0) { carry_c = 0; carry_s = 0; }
   __syncthreads();
   for (int base = 0; base < N; base += PLAN_NT) {

@@ -77,6 +77,22 @@ def test_varlen_with_empty_and_tiny_sequences(dev):
         check_fwd(y, dev, cp, "varlen-edge")
 
 
+@pytest.mark.parametrize("nseq", [64, 65, 300])
+def test_many_sequences(dev, nseq):
+    """Batches around and above 64 sequences (the plan's one-wave and block
+    scans), with empty sequences among them."""
+    rng = np.random.default_rng(nseq)
+    lens = rng.integers(0, 90, size=nseq)
+    lens[::7] = 0
+    cu = np.zeros(nseq + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    y = gdn_inputs.generate(B=1, T=int(cu[-1]), H=1, Dk=64, Dv=64, dtype="bf16", seed=11)
+    y.cu_seqlens = cu
+    y.h0 = (0.3 * rng.standard_normal((nseq, 1, 64, 64))).astype(np.float32)
+    for cp in (-1, 1):
+        check_fwd(y, dev, cp, f"{nseq} sequences")
+
+
 def test_segment_split_is_exact(dev):
     """With fp32 arithmetic throughout, forced segment splits agree with the
     unsplit run to fp32 rounding: the boundary correction drops nothing."""
