@@ -52,7 +52,7 @@ struct Plan {
   bool cp = false;      // some sequence has more than one segment
   // workspace offsets (bytes)
   size_t o_chunk_first = 0, o_seg_first = 0, o_segs = 0, o_chunk_tab = 0;
-  size_t o_bstate = 0, o_lam = 0, o_bstate2 = 0, o_lam2 = 0, o_hs = 0, o_us = 0, o_dhs = 0, o_ts = 0, total = 0;
+  size_t o_hs = 0, o_us = 0, o_dhs = 0, o_ts = 0, total = 0;
 };
 
 bool supported(int dtype, int Dk, int Dv) {
@@ -136,8 +136,9 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false, 
     p.segc = a.cp_mode;
   } else {
     // Automatic: aim for about one workgroup per compute unit, but never cut
-    // segments shorter than 8 chunks -- the boundary correction costs a few
-    // chunks of work per segment (the gate-decay horizon).
+    // segments shorter than 8 chunks -- each segment but a sequence's first
+    // (last, in the reverse chain) runs a few lead-in chunks before its own
+    // (the gate-decay horizon).
     const long long work = total * a.H;
     const long long per = (work + cus - 1) / std::max(1, cus);
     p.segc = (int)std::max<long long>(8, per);
@@ -155,18 +156,10 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false, 
   p.o_seg_first = take(sizeof(int) * (p.N + 1));
   p.o_segs = take(sizeof(gdn::SegDesc) * p.nseg);
   p.o_chunk_tab = take(sizeof(int2) * std::max(1, p.nchunk));
-  if (p.cp) {
-    p.o_bstate = take(sizeof(float) * SS * p.nseg * a.H);
-    p.o_lam = take(sizeof(float) * (size_t)p.nseg * a.H);
-  }
   // T of every chunk, then every chunk's scalar record
   const size_t tbytes = sizeof(float) * (CHUNK * CHUNK + gdn::RECF) * (size_t)std::max(1, p.nchunk) * a.H;
   if (!bwd && !t_given) p.o_ts = take(tbytes);
   if (bwd) {
-    if (p.cp) {
-      p.o_bstate2 = take(sizeof(float) * SS * p.nseg * a.H);
-      p.o_lam2 = take(sizeof(float) * (size_t)p.nseg * a.H);
-    }
     if (!saved) {
       p.o_hs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
       p.o_us = take(esz * CHUNK * (size_t)a.Dv * std::max(1, p.nchunk) * a.H);
@@ -340,13 +333,11 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   p.segs = at<gdn::SegDesc>(ws, pl.o_segs);
   p.seg_first = at<int>(ws, pl.o_seg_first);
   p.chunk_first = at<int>(ws, pl.o_chunk_first);
-  p.bstate = pl.cp ? at<float>(ws, pl.o_bstate) : nullptr;
-  p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
   p.hs = args->h_save;  // nullable: the chunk states (and U) are stored only on request
   p.us = args->h_save ? static_cast<char*>(args->h_save) + states_part_bytes(a) : nullptr;
   p.prep = prep_of(a.qk_norm, a.gate_act, a.gate_scale);
   // every chunk's T, solved chunk-parallel (into the caller's buffer when it
-  // keeps T) and read by the chunk chain and the segment corrections
+  // keeps T) and read by the chunk chain
   float* ts = args->t_save ? args->t_save : at<float>(ws, pl.o_ts);
   float* rec = ts + (size_t)pl.nchunk * a.H * CHUNK * CHUNK;  // the chunks' scalar records
   if (pl.nchunk > 0) {
@@ -359,14 +350,8 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   }
   p.t_in = ts;
   p.rec = rec;
-  p.phase = 1;
   e = timed("fwd", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
-  if (pl.cp) {
-    p.phase = 3;
-    e = timed("fwd_corr", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
-    if (e != hipSuccess) return hip_fail(e, "forward correction launch");
-  }
   return GDN_OK;
 }
 
@@ -407,8 +392,6 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   p.segs = at<gdn::SegDesc>(ws, pl.o_segs);
   p.seg_first = at<int>(ws, pl.o_seg_first);
   p.chunk_first = at<int>(ws, pl.o_chunk_first);
-  p.bstate = pl.cp ? at<float>(ws, pl.o_bstate) : nullptr;
-  p.lam = pl.cp ? at<float>(ws, pl.o_lam) : nullptr;
   // chunk matrices T: the caller's, else solved chunk-parallel here (the same
   // kernel as the forward's, so the same values); every later kernel reads them
   const float* ts = t_given ? args->t_saved : at<float>(ws, pl.o_ts);
@@ -430,34 +413,20 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   } else {
     p.hs = at<void>(ws, pl.o_hs);
     p.us = at<void>(ws, pl.o_us);
-    p.phase = 1;
     e = timed("replay", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
     if (e != hipSuccess) return hip_fail(e, "replay launch");
-    if (pl.cp) {
-      p.phase = 3;
-      e = timed("replay_corr", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
-      if (e != hipSuccess) return hip_fail(e, "replay correction launch");
-    }
   }
   // 2. reverse chain: state gradient at every chunk end, dh0
   gdn::RevParams r{};
   r.q = a.q; r.k = a.k; r.g = a.g; r.beta = a.beta; r.dout = args->do_; r.dhT = args->dhT; r.dh0 = args->dh0;
   r.scale = a.scale; r.H = a.H; r.seq = sq;
   r.segs = p.segs; r.seg_first = p.seg_first; r.chunk_first = p.chunk_first;
-  r.bstate = pl.cp ? at<float>(ws, pl.o_bstate2) : nullptr;
-  r.lam = pl.cp ? at<float>(ws, pl.o_lam2) : nullptr;
   r.dhs = at<void>(ws, pl.o_dhs);
   r.t_in = ts;
   r.rec = rec;
   r.prep = p.prep;
-  r.phase = 1;
   e = timed("rev", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "reverse launch");
-  if (pl.cp) {
-    r.phase = 3;
-    e = timed("rev_corr", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });
-    if (e != hipSuccess) return hip_fail(e, "reverse correction launch");
-  }
   // 3. chunk-parallel gradients
   if (pl.nchunk > 0) {
     gdn::GradParams gp{};

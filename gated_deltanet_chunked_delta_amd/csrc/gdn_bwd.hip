@@ -4,18 +4,17 @@
 // with intra-card sequence parallelism) runs in three stages after the forward
 // replay (gdn_fwd.hip in replay mode stores the state h_c at every chunk start):
 //
-//  1. Reverse chain (this file, gdn_rev_kernel): per (segment, head), from the
+//  1. Reverse chain (this file, gdn_rev_seg): per (segment, head), from the
 //     last chunk to the first, the gradient dh' at each chunk END is stored and
 //     carried back through the chunk:
 //        dU = scale P^T dO + diag(ek) K dh'
 //        dh = scale (diag(Gam) Q)^T dO + Gam_C dh' - W^T dU
 //     The dh' chain lives in accumulator registers (wave w owns 16 columns).
 //     Long sequences are cut into segments exactly as in the forward; a
-//     segment's provisional run starts from dh' = 0 (dhT for the last one) and
-//     a correction pass propagates the true boundary gradient backwards through
-//     the last chunks of each segment until the gate-decay bound drops under
-//     fp32 round-off (the transpose of the forward transition has the same norm
-//     bound).
+//     segment that does not end its sequence starts from dh' = 0 some chunks
+//     after its end (the lead-in, until the chunks' log-bounds sum to
+//     ln 2^-24 or less -- the transpose of the forward transition has the same
+//     norm bound), else from the sequence end and dhT.
 //
 //  2. Chunk gradients (gdn_grad_kernel): every chunk independently, given h_c
 //     and dh'_c, evaluates the reverse-mode derivative of the chunk algebra
@@ -73,31 +72,29 @@ template <int DV>
 struct RevWaves { static constexpr int NW = DV == 128 ? 8 : 4; };
 
 // One chunk of the reverse chain (wave w owns Dv/NW columns of the state
-// gradient).  CORR: propagation of a boundary difference only (dO does not
-// enter, stored gradients are incremented).
-// Every chunk's T is read from p.t_in (solved chunk-parallel beforehand).
-template <class E, int DK, int DV, bool CORR, bool PREP>
+// gradient).  Every chunk's T and scalar record are read from p.t_in / p.rec
+// (written by the chunk-parallel T solve beforehand).
+template <class E, int DK, int DV, bool PREP>
 struct RevChunk {
   static constexpr int NW = RevWaves<DV>::NW, NT = 64 * NW, NTW = DV / (16 * NW);
   using S = RevSmem<E, DK, DV>;
-  // The next chunk's tiles, in flight in registers during the current chunk.
-  // With dO needed, the first half of the threads holds K and the second half
-  // Q (one register set, kq), and dO sits on the first NT / 2 * (DV / DK)
-  // threads; without it (CORR) K is spread over all threads.
-  static constexpr int KQT = CORR ? NT : NT / 2;  // threads per K (or Q) tile
+  // The next chunk's tiles, in flight in registers during the current chunk:
+  // the first half of the threads holds K and the second half Q (one register
+  // set, kq), and dO sits on the first NT / 2 * (DV / DK) threads.
+  static constexpr int KQT = NT / 2;  // threads per K (or Q) tile
   struct Loader {
     TilePart<E, KQT, DK> kq;
-    TilePart<E, NT, CORR ? 0 : DV> d;
+    TilePart<E, NT, DV> d;
     RecordPart rec;
   };
-  __device__ __forceinline__ static bool q_half() { return !CORR && threadIdx.x >= KQT; }
+  __device__ __forceinline__ static bool q_half() { return threadIdx.x >= KQT; }
   __device__ __forceinline__ static int kq_tid() { return threadIdx.x & (KQT - 1); }
 
   __device__ static void issue(Loader& ld, const RevParams& p, int64_t tok0, int rows, int h, const float* rec) {
     const int H = p.H;
     const void* src = q_half() ? p.q : p.k;
     ld.kq.load(static_cast<const E*>(src) + (tok0 * H + h) * DK, (int64_t)H * DK, rows, kq_tid());
-    if (!CORR) ld.d.load(static_cast<const E*>(p.dout) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
+    ld.d.load(static_cast<const E*>(p.dout) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
     ld.rec.load(rec);
   }
 
@@ -122,10 +119,12 @@ struct RevChunk {
 
   // dh: gradient at the chunk end on entry, at the chunk start on exit.
   // Prefetches chunk (ntok0, nrows) into ld (nrows = 0: none).  Returns Lambda_c.
-  // t_in: this chunk's T; nrec: the next chunk's scalar record.
-  __device__ static float step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows,
-                               int h, E* dhs_chunk, const float* t_in, const float* nrec,
-                               f32x4 (&dh)[DK / 16][NTW]) {
+  // t_in: this chunk's T; nrec: the next chunk's scalar record.  LEAD: a
+  // lead-in chunk after the segment proper, which only advances the gradient
+  // (nothing is written).
+  template <bool LEAD>
+  __device__ static void step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows, int h,
+                              E* dhs_chunk, const float* t_in, const float* nrec, f32x4 (&dh)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
@@ -134,26 +133,20 @@ struct RevChunk {
     // ---- 1. gradient at the chunk end out; tiles into LDS; scalars
     S* sp = lds_opaque(&s0);
     // stored as S (Dv x Dk) in 4 x 16 blocks: the lane's four rows of one
-    // column are contiguous.  A correction adds to the stored gradient: it
-    // requests the current values here and writes the sums after phase 4 (dh
-    // in registers changes only in phase 5).
-    typedef E e4_t __attribute__((__vector_size__(4 * sizeof(E))));
-    e4_t hold[DK / 16][NTW];
+    // column are contiguous
+    if constexpr (!LEAD) {
 #pragma unroll
-    for (int t = 0; t < DK / 16; ++t)
+      for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        E* dst = dhs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK);
-        if (CORR) hold[t][nt] = *reinterpret_cast<const e4_t*>(dst);
-        else st4f<E>(dst, dh[t][nt]);
-      }
+        for (int nt = 0; nt < NTW; ++nt) st4f<E>(dhs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK), dh[t][nt]);
+    }
     S& s1 = *sp;
     if (PREP && p.prep.qk_norm) ld.kq.normalize_rows(kq_tid());
     {
       const bool qh = q_half();
       ld.kq.store(qh ? s1.Q : s1.K, LQ, qh ? s1.QT : s1.KT, LT, kq_tid());
     }
-    if (!CORR) ld.d.store(nullptr, 0, s1.DOT, LT);
+    ld.d.store(nullptr, 0, s1.DOT, LT);
     static_assert(offsetof(S, tail) == offsetof(S, gam) + 5 * CH * sizeof(float), "record layout");
     ld.rec.store(s1.gam);
     if (tid >= CH / 4 && tid < CH / 2) {
@@ -172,7 +165,7 @@ struct RevChunk {
     f32x4 tv[TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
-    if constexpr (!CORR) {
+    {
       S* sq = lds_opaque(&s0);
 #pragma unroll
       for (int j = 0; j < (10 + NW - 1) / NW; ++j) {
@@ -191,7 +184,6 @@ struct RevChunk {
       }
     }
     __syncthreads();
-    const float lam_c = lds_opaque(&s0)->tail[0];  // the same value on every wave
 
     // ---- 3. the next chunk's tiles start their way from HBM
     if (nrows > 0) issue(ld, p, ntok0, nrows, h, nrec);
@@ -227,17 +219,6 @@ struct RevChunk {
     }
     __syncthreads();
 
-    if constexpr (CORR) {
-#pragma unroll
-      for (int t = 0; t < DK / 16; ++t)
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          const e4_t o = hold[t][nt];
-          st4f<E>(dhs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK),
-                  dh[t][nt] + f32x4{to_f(o[0]), to_f(o[1]), to_f(o[2]), to_f(o[3])});
-        }
-    }
-
     // ---- 5. dU = diag(ek) K dh' + scale P^T dO ;  dh = Gam_C dh' + scale (Gam Q)^T dO - W^T dU
     f32x4 du[4][NTW];
     {
@@ -248,12 +229,10 @@ struct RevChunk {
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) pack_frag(hf[nt][kb], dh[2 * kb][nt], dh[2 * kb + 1][nt]);
       Frag<E> yd[NTW][2];
-      if (!CORR) {
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
+      for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) yd[nt][kb] = ld_frag(s.DOT, LT, n0 + 16 * nt + c16, 32 * kb);
-      }
+        for (int kb = 0; kb < 2; ++kb) yd[nt][kb] = ld_frag(s.DOT, LT, n0 + 16 * nt + c16, 32 * kb);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         Frag<E> xk[DK / 32];
@@ -261,20 +240,16 @@ struct RevChunk {
         for (int kb = 0; kb < DK / 32; ++kb) xk[kb] = ld_frag(s.K, LQ, 16 * rt + c16, 32 * kb);
         const f32x4 e4 = *reinterpret_cast<const f32x4*>(&s.ek[16 * rt + 4 * g]);
         Frag<E> xp[2];
-        if (!CORR) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) xp[kb] = ld_frag(s.PT, LT, 16 * rt + c16, 32 * kb);
-        }
+        for (int kb = 0; kb < 2; ++kb) xp[kb] = ld_frag(s.PT, LT, 16 * rt + c16, 32 * kb);
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
           f32x4 acc = zero4();
 #pragma unroll
           for (int kb = 0; kb < DK / 32; ++kb) mma(acc, xk[kb], hf[nt][kb]);
           acc = acc * e4;
-          if (!CORR) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) mma(acc, xp[kb], yd[nt][kb]);
-          }
+          for (int kb = 0; kb < 2; ++kb) mma(acc, xp[kb], yd[nt][kb]);
           du[rt][nt] = acc;
         }
       }
@@ -287,48 +262,45 @@ struct RevChunk {
 #pragma unroll
         for (int t = 0; t < DK / 16; ++t) {
           dh[t][nt] = dh[t][nt] * gc;
-          if (!CORR) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-              mma(dh[t][nt], ld_frag_kscaled<E>(s.QT, LT, 16 * t + c16, 32 * kb, s.sGam), yd[nt][kb]);
-          }
+          for (int kb = 0; kb < 2; ++kb)
+            mma(dh[t][nt], ld_frag_kscaled<E>(s.QT, LT, 16 * t + c16, 32 * kb, s.sGam), yd[nt][kb]);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) mma(dh[t][nt], ld_frag(s.WT, LT, 16 * t + c16, 32 * kb), uf[kb]);
         }
       }
     }
     __syncthreads();
-    return lam_c;
   }
 
-  // Chunks ce-1 down to cb; CORR stops once the accumulated bound is below 2^-24.
-  // Returns Lambda over the processed chunks; *lowest = last chunk processed.
-  // Issue the loads of chunk ce - 1, the first of a run (before the state
+  // Issue the loads of chunk we - 1, the first of a run (before the state
   // gradient is loaded, so that the two are in flight together).
-  __device__ static void prime(Loader& ld, const RevParams& p, int64_t seq0, int len, int64_t chunk0, int cb, int ce,
+  __device__ static void prime(Loader& ld, const RevParams& p, int64_t seq0, int len, int64_t chunk0, int cb, int we,
                                int h) {
-    const int c = ce - 1;
+    const int c = we - 1;
     if (c >= cb) issue(ld, p, seq0 + (int64_t)c * CH, min(CH, len - c * CH), h, p.rec + ((chunk0 + c) * p.H + h) * RECF);
   }
-  // ld: primed for chunk ce - 1.
-  __device__ static float run(S& s, const RevParams& p, int64_t seq0, int len, int64_t chunk0, int cb, int ce,
-                              int h, f32x4 (&dh)[DK / 16][DV / (16 * RevWaves<DV>::NW)], int* lowest, Loader& ld) {
-    float lam = 0.f;
-    int c = ce - 1;
+  // Chunks we-1 down to cb from the gradient in dh: chunks at or after ce are
+  // the lead-in (the gradient advances, nothing is written), chunks below ce
+  // write their chunk-end gradients.  ld: primed for chunk we - 1.
+  __device__ static void run(S& s, const RevParams& p, int64_t seq0, int len, int64_t chunk0, int cb, int ce, int we,
+                             int h, f32x4 (&dh)[DK / 16][DV / (16 * RevWaves<DV>::NW)], Loader& ld) {
     const size_t SS = (size_t)DK * DV;
     E* dhs = static_cast<E*>(p.dhs);
-    for (; c >= cb; --c) {
-      if (CORR && lam <= LN_EPS) break;
+    // the lead-in and the segment proper as two loops, each with its own
+    // register allocation
+    auto chunk = [&](auto lead, int c) {
       const int rows = min(CH, len - c * CH);
       const bool more = c - 1 >= cb;
       const int64_t ntok0 = seq0 + (int64_t)(c - 1) * CH;
       const int nrows = more ? min(CH, len - (c - 1) * CH) : 0;
-      const size_t toff = ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
+      const float* tin = p.t_in + ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
       const float* nrec = more ? p.rec + ((chunk0 + c - 1) * p.H + h) * RECF : nullptr;
-      lam += step(s, p, ld, rows, ntok0, nrows, h, dhs + ((chunk0 + c) * p.H + h) * SS, p.t_in + toff, nrec, dh);
-    }
-    if (lowest) *lowest = c + 1;
-    return lam;
+      if constexpr (decltype(lead)::value) step<true>(s, p, ld, rows, ntok0, nrows, h, nullptr, tin, nrec, dh);
+      else step<false>(s, p, ld, rows, ntok0, nrows, h, dhs + ((chunk0 + c) * p.H + h) * SS, tin, nrec, dh);
+    };
+    for (int c = we - 1; c >= ce; --c) chunk(std::true_type{}, c);
+    for (int c = ce - 1; c >= cb; --c) chunk(std::false_type{}, c);
   }
 };
 
@@ -345,8 +317,7 @@ __device__ void rev_load(f32x4 (&acc)[DK / 16][DV / (16 * RevWaves<DV>::NW)], co
         acc[t][nt][i] = src ? src[(16 * t + 4 * g + i) * DV + w * (DV / NW) + 16 * nt + c16] : 0.f;
 }
 template <class E, int DK, int DV>
-__device__ void rev_store(const f32x4 (&acc)[DK / 16][DV / (16 * RevWaves<DV>::NW)], float* dst, const float* add,
-                          bool use_acc) {
+__device__ void rev_store(const f32x4 (&acc)[DK / 16][DV / (16 * RevWaves<DV>::NW)], float* dst) {
   constexpr int NW = RevWaves<DV>::NW, NTW = DV / (16 * NW);
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
 #pragma unroll
@@ -356,7 +327,7 @@ __device__ void rev_store(const f32x4 (&acc)[DK / 16][DV / (16 * RevWaves<DV>::N
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = (16 * t + 4 * g + i) * DV + w * (DV / NW) + 16 * nt + c16;
-        dst[e] = (use_acc ? acc[t][nt][i] : 0.f) + (add ? add[e] : 0.f);
+        dst[e] = acc[t][nt][i];
       }
 }
 
@@ -371,82 +342,37 @@ __device__ void rev_init_smem(RevSmem<E, DK, DV>& s) {
   __syncthreads();
 }
 
-// Phase 1: every segment from dh' = 0 (the last segment of a sequence from dhT).
+// One segment of the reverse chain.  A segment that ends before its sequence
+// does starts from dh' = 0 a few chunks later (the lead-in, until the chunks'
+// log-bounds sum to ln 2^-24 or less; else from the sequence end and dhT), so
+// every segment runs independently of the others.
 template <class E, int DK, int DV, bool PREP>
-__global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p1(RevParams p) {
+__global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_seg(RevParams p) {
   __shared__ RevSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
   const int h = blockIdx.y, n = sd.n;
-  const int nseg = p.seg_first[n + 1] - p.seg_first[n];
+  const int64_t seq0 = p.seq.start(n), chunk0 = p.chunk_first[n];
+  const int len = p.seq.len(n), nch = (len + CH - 1) / CH;
   const size_t SS = (size_t)DK * DV;
-  const float* dhT = p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr;
+  const int we = sd.c_end < nch ? lead_in_end(p.rec, chunk0, p.H, h, sd.c_end, nch) : nch;
   f32x4 dh[DK / 16][DV / (16 * RevWaves<DV>::NW)];
-  using C = RevChunk<E, DK, DV, false, PREP>;
+  using C = RevChunk<E, DK, DV, PREP>;
   typename C::Loader ld;
-  C::prime(ld, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n], sd.c_begin, sd.c_end, h);
+  C::prime(ld, p, seq0, len, chunk0, sd.c_begin, we, h);
   rev_init_smem(s);
-  rev_load<E, DK, DV>(dh, sd.s == nseg - 1 ? dhT : nullptr);
-  const float lam = C::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n], sd.c_begin, sd.c_end, h, dh,
-                           nullptr, ld);
-  if (nseg == 1) {
-    if (p.dh0) rev_store<E, DK, DV>(dh, p.dh0 + ((size_t)n * p.H + h) * SS, nullptr, true);
-  } else {
-    rev_store<E, DK, DV>(dh, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, nullptr, true);
-    if (threadIdx.x == 0) p.lam[(size_t)blockIdx.x * p.H + h] = lam;
-  }
-}
-
-// Phase 3: propagate the true end-of-segment gradient into each segment's last
-// chunks (or recompute the sequence serially when the certificate fails).
-template <class E, int DK, int DV, bool PREP>
-__global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_p3(RevParams p) {
-  __shared__ RevSmem<E, DK, DV> s;
-  const SegDesc sd = p.segs[blockIdx.x];
-  const int h = blockIdx.y, n = sd.n;
-  const int seg0 = p.seg_first[n];
-  const int nseg = p.seg_first[n + 1] - seg0;
-  if (nseg == 1 || sd.s == nseg - 1) return;
-  const int64_t seq0 = p.seq.start(n);
-  const int len = p.seq.len(n);
-  const size_t SS = (size_t)DK * DV;
-  const int64_t chunk0 = p.chunk_first[n];
-  float* dh0 = p.dh0 ? p.dh0 + ((size_t)n * p.H + h) * SS : nullptr;
-  const bool ok = interior_segments_decay(p.lam, seg0, nseg, p.H, h, LN_EPS);
-  if (!ok && sd.s != 0) return;
-  f32x4 dh[DK / 16][DV / (16 * RevWaves<DV>::NW)];
-  rev_init_smem(s);
-  if (!ok) {
-    using C = RevChunk<E, DK, DV, false, PREP>;
-    typename C::Loader ld;
-    C::prime(ld, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h);
-    rev_load<E, DK, DV>(dh, p.dhT ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr);
-    C::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, dh, nullptr, ld);
-    if (dh0) rev_store<E, DK, DV>(dh, dh0, nullptr, true);
-    return;
-  }
-  using C = RevChunk<E, DK, DV, true, PREP>;
-  typename C::Loader ld;
-  C::prime(ld, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h);
-  rev_load<E, DK, DV>(dh, p.bstate + ((size_t)(blockIdx.x + 1) * p.H + h) * SS);
-  int lowest = sd.c_end;
-  C::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, dh, &lowest, ld);
-  if (sd.s == 0 && dh0)
-    rev_store<E, DK, DV>(dh, dh0, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, lowest == sd.c_begin);
+  rev_load<E, DK, DV>(dh, (we == nch && p.dhT) ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr);
+  C::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, we, h, dh, ld);
+  if (sd.c_begin == 0 && p.dh0) rev_store<E, DK, DV>(dh, p.dh0 + ((size_t)n * p.H + h) * SS);
 }
 
 template <class E, int DK, int DV>
 hipError_t launch_rev_t(const RevParams& p, int nseg_total, hipStream_t st) {
   const dim3 block(64 * RevWaves<DV>::NW);
   const dim3 grid(nseg_total, p.H);
-  // every phase reads T (solved beforehand)
-  if (!p.t_in) return hipErrorInvalidValue;
-  if (p.prep.qk_norm || p.prep.gate_act) {
-    if (p.phase != 1) hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, true>), grid, block, 0, st, p);
-  } else {
-    if (p.phase != 1) hipLaunchKernelGGL((gdn_rev_p3<E, DK, DV, false>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((gdn_rev_p1<E, DK, DV, false>), grid, block, 0, st, p);
-  }
+  // T and the scalar records are solved beforehand
+  if (!p.t_in || !p.rec) return hipErrorInvalidValue;
+  if (p.prep.qk_norm || p.prep.gate_act) hipLaunchKernelGGL((gdn_rev_seg<E, DK, DV, true>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((gdn_rev_seg<E, DK, DV, false>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 

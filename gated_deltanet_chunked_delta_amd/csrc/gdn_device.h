@@ -559,18 +559,6 @@ __device__ __forceinline__ float wave_incl_scan(float x) {
   }
   return x;
 }
-// Whether every interior segment j (1 <= j < nseg - 1) of a sequence has its
-// log-bound lam[(seg0 + j) * H + h] at or below LN_EPS: each lane reads its own
-// segments and the wave votes, so the loads are all in flight together.  The
-// same value on every lane and wave.
-__device__ __forceinline__ bool interior_segments_decay(const float* lam, int seg0, int nseg, int H, int h,
-                                                        float ln_eps) {
-  bool ok = true;
-  for (int j = 1 + (int)(threadIdx.x & 63); j + 1 < nseg; j += 64)
-    ok = ok & (lam[(size_t)(seg0 + j) * H + h] <= ln_eps);
-  return __all(ok);
-}
-
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);

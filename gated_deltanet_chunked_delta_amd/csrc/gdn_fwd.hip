@@ -22,17 +22,16 @@
 //
 // Intra-card context parallelism ("FlashQLA resource", section 3: gate-driven,
 // automatic, for long sequences and few heads).  The plan cuts each sequence
-// into segments.  Phase 1 runs every segment from a zero state (segment 0 from
-// h0), writing provisional outputs, the segment's end state b_s and
-// Lambda_s = sum over its tokens of g_t + log max(1, |1 - beta_t |k_t|^2|),
-// a bound on log ||transition||_2 since ||I - beta k k^T||_2 = max(1, |1 - beta |k|^2|).
-// Phase 3 adds, for each segment s >= 1, the effect of the true incoming state
-// H_s = b_{s-1}: delta <- H_s, and per chunk  o += scale (diag(Gam) Q delta - P W delta),
-// delta <- Gam_C delta - K^T diag(ek) W delta, until the accumulated bound
-// exp(sum Lambda) drops under 2^-24 (fp32 round-off), which the gate decay
-// makes happen after a few chunks.  H_s = b_{s-1} is exact to that bound only
-// if every interior segment decays below it; a workgroup checks that from the
-// Lambda_s values and otherwise the (sequence, head) is recomputed serially.
+// into segments, one workgroup each, all independent.  A segment that does not
+// start its sequence starts from a zero state some chunks earlier, at the
+// latest chunk wb with  sum_{c=wb}^{cb-1} Lambda_c <= ln 2^-24, where
+// Lambda_c = sum over the chunk's tokens of g_t + log max(1, |1 - beta_t |k_t|^2|)
+// bounds log ||transition||_2 (||I - beta k k^T||_2 = max(1, |1 - beta |k|^2|)).
+// Those lead-in chunks only advance the state; from chunk cb on, the state
+// differs from the true one by the true state at wb carried through chunks
+// wb..cb-1, at most 2^-24 of its norm, i.e. fp32 round-off.  Where the bound is
+// not reached (weak decay) the run starts at the sequence start from h0 and is
+// exact; the gate decay usually makes the lead-in a few chunks long.
 //
 // The same kernels, without an output, replay the forward for the backward
 // pass and store the state at every chunk start.
@@ -205,22 +204,21 @@ struct TileLoader {
 
 // OUT:  forward (writes o) vs replay (no output).  Either stores the chunk-start
 //       state when p.hs is set.
-// CORR: boundary correction -- the state is a propagated difference; the values
-//       v do not enter, outputs / stored states are incremented.
 // Waves per workgroup: 8 when the state has 128 value columns (one 16-column
 // tile per wave, two waves per SIMD), else 4.
 template <int DV>
 struct FwdWaves { static constexpr int NW = DV == 128 ? 8 : 4; };
 
-// Every chunk's T is read from p.t_in (solved chunk-parallel beforehand).
-// USAVE: every chunk's U is written to p.us (CORR: its correction added).
-template <class E, int DK, int DV, bool OUT, bool CORR, bool PREP, bool USAVE>
+// Every chunk's T and scalar record are read from p.t_in / p.rec (written by
+// the chunk-parallel T solve beforehand).
+// USAVE: every chunk's U is written to p.us.
+template <class E, int DK, int DV, bool OUT, bool PREP, bool USAVE>
 struct Chunk {
   static constexpr int NW = FwdWaves<DV>::NW;
   static constexpr int NT = NW * 64;
   static constexpr int NTW = DV / (16 * NW);  // 16-column tiles of the state per wave
   using S = FwdSmem<E, DK, DV>;
-  using Loader = TileLoader<E, DK, DV, NT, OUT, !CORR, PREP>;
+  using Loader = TileLoader<E, DK, DV, NT, OUT, true, PREP>;
 
   // One lower 16x16 tile (rt, ct) of P = (Q K^T) * M.
   __device__ __forceinline__ static void p_tile(S* sp, int rt, int ct, int g, int c16) {
@@ -241,13 +239,15 @@ struct Chunk {
 
   // Process the chunk whose tiles `ld` holds; prefetch the next chunk (if any)
   // into `ld`.  hacc: this wave's state columns (chunk start on entry, chunk end
-  // on exit).  Returns the chunk's log-bound Lambda_c.
+  // on exit).  LEAD: a lead-in chunk before the segment proper, which only
+  // advances the state (nothing is written).
   // t_in: this chunk's T; nrec: the next chunk's scalar record.
-  // us_chunk: where this chunk's U = Ut - W h goes (nullable; CORR adds its
-  // correction).
-  __device__ static float step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows,
-                               int64_t ntok0, int nrows, int h, E* hs_chunk, const float* t_in,
-                               const float* nrec, E* us_chunk, f32x4 (&hacc)[DK / 16][NTW]) {
+  // us_chunk: where this chunk's U = Ut - W h goes (nullable).
+  template <bool LEAD>
+  __device__ static void step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows, int64_t ntok0,
+                              int nrows, int h, E* hs_chunk, const float* t_in, const float* nrec, E* us_chunk,
+                              f32x4 (&hacc)[DK / 16][NTW]) {
+    constexpr bool OUTC = OUT && !LEAD, USAVEC = USAVE && !LEAD;
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA, LO = S::LO;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
@@ -258,32 +258,6 @@ struct Chunk {
     f32x4 tv[TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
-    // a correction adds to the stored U: its current pieces are requested now and
-    // consumed at the end of the chain (no load latency inside it)
-    typedef E e4_t __attribute__((__vector_size__(4 * sizeof(E))));
-    e4_t uold[4][NTW];
-    if constexpr (CORR && USAVE) {
-      const int q = (l >> 2) & 3, b = l & 3;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-          uold[rt][nt] = *reinterpret_cast<const e4_t*>(us_chunk + (n0 + 16 * nt) * CH + (16 * rt + 4 * g + b) * 16 +
-                                                        4 * q);
-    }
-    // likewise the output a correction adds to: the 16-byte row pieces this
-    // thread writes in phase 6
-    constexpr int OVEC = 16 / (int)sizeof(E), NOP = CH * (DV / OVEC) / NT;
-    typedef E ovec_t __attribute__((__vector_size__(16)));
-    ovec_t oold[NOP];
-    if constexpr (CORR && OUT) {
-#pragma unroll
-      for (int j = 0; j < NOP; ++j) {
-        const int e = tid + j * NT, r = e / (DV / OVEC), c0 = (e % (DV / OVEC)) * OVEC;
-        oold[j] = ovec_t{};
-        if (r < rows) oold[j] = *reinterpret_cast<const ovec_t*>(static_cast<const E*>(p.o) + ((tok0 + r) * H + h) * DV + c0);
-      }
-    }
 
     // ---- 1. tiles into LDS, scalars, prefetch of the next chunk
     S* sp = lds_opaque(&s0);
@@ -291,26 +265,19 @@ struct Chunk {
     ld.store(*sp);
     ld.store_rec(*sp);
     // chunk-start state out, as S (Dv x Dk) in 4 x 16 blocks: the lane's four
-    // rows of one column are contiguous.  A correction adds to the stored
-    // state: it requests the current values here and writes the sums after
-    // phase 4 (the state in registers changes only in phase 5).
-    e4_t hold[DK / 16][NTW];
-    if (hs_chunk) {
+    // rows of one column are contiguous
+    if (!LEAD && hs_chunk) {
 #pragma unroll
       for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          E* dst = hs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK);
-          if (CORR) hold[t][nt] = *reinterpret_cast<const e4_t*>(dst);
-          else st4f<E>(dst, hacc[t][nt]);
-        }
+        for (int nt = 0; nt < NTW; ++nt) st4f<E>(hs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK), hacc[t][nt]);
     }
     __syncthreads();
     sp = lds_opaque(sp);
 
     // ---- 2. for the output, the ten lower 16x16 tiles of P = (Q K^T) * M, tile j
     //         on wave j % NW (at most two tiles a wave with eight waves)
-    if constexpr (OUT) {
+    if constexpr (OUTC) {
 #pragma unroll
       for (int j = 0; j < (10 + NW - 1) / NW; ++j) {
         const int pid = w + NW * j;
@@ -326,7 +293,6 @@ struct Chunk {
     }
     __syncthreads();
     sp = lds_opaque(sp);
-    const float lam_c = sp->tail[0];  // the same value on every wave
 
     // ---- 3. the next chunk's k, v, scalar record (and q) start their way from HBM
     if (nrows > 0) {
@@ -358,42 +324,25 @@ struct Chunk {
     f32x4 u[4][NTW];
     {
       Frag<E> yv[NTW][2];
-      if (!CORR) {
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
+      for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) yv[nt][kb] = ld_frag(sp->VT, LT, n0 + 16 * nt + c16, 32 * kb);
-      }
+        for (int kb = 0; kb < 2; ++kb) yv[nt][kb] = ld_frag(sp->VT, LT, n0 + 16 * nt + c16, 32 * kb);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         Frag<E> xb[2];
-        if (!CORR) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) xb[kb] = ld_frag_scaled<E>(sp->T, LA, 16 * rt + c16, 32 * kb, sp->beta);
-        }
+        for (int kb = 0; kb < 2; ++kb) xb[kb] = ld_frag_scaled<E>(sp->T, LA, 16 * rt + c16, 32 * kb, sp->beta);
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
           u[rt][nt] = zero4();
-          if (!CORR) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) mma(u[rt][nt], xb[kb], yv[nt][kb]);
-          }
+          for (int kb = 0; kb < 2; ++kb) mma(u[rt][nt], xb[kb], yv[nt][kb]);
         }
       }
     }
     __syncthreads();
     sp = lds_opaque(sp);
-
-    if (CORR && hs_chunk) {
-#pragma unroll
-      for (int t = 0; t < DK / 16; ++t)
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          const e4_t o = hold[t][nt];
-          st4f<E>(hs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK),
-                  hacc[t][nt] + f32x4{to_f(o[0]), to_f(o[1]), to_f(o[2]), to_f(o[3])});
-        }
-    }
 
     // ---- 5. state chain: U = Ut - W h ; O = scale (diag(Gam) Q h + P U) ; h' = Gam_C h + K^T (ek * U)
     Frag<E> hf[NTW][DK / 32];
@@ -416,29 +365,19 @@ struct Chunk {
     // U out as DV/16 column blocks of [CH][16], each contiguous (a wave's
     // stores fill whole lines; rows past the end are zero: beta = 0 there);
     // the forward proper writes the rounded operand fragments it forms anyway
-    if (USAVE && (CORR || !OUT)) {
+    if (USAVEC && !OUT) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          E* blk = us_chunk + (n0 + 16 * nt) * CH;
-          if constexpr (CORR) {
-            const int q = (l >> 2) & 3, b = l & 3;
-            const e4_t o = uold[rt][nt];
-            st4f<E>(blk + (16 * rt + 4 * g + b) * 16 + 4 * q,
-                    quad_transpose(u[rt][nt]) + f32x4{to_f(o[0]), to_f(o[1]), to_f(o[2]), to_f(o[3])});
-          } else {
-            st_tile_rows<E>(blk, 16, 16 * rt, 0, u[rt][nt]);
-          }
-        }
+        for (int nt = 0; nt < NTW; ++nt) st_tile_rows<E>(us_chunk + (n0 + 16 * nt) * CH, 16, 16 * rt, 0, u[rt][nt]);
     }
-    if (OUT) {
+    if (OUTC) {
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         Frag<E> uf[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) pack_frag(uf[kb], u[2 * kb][nt], u[2 * kb + 1][nt]);
-        if (USAVE && !CORR) {
+        if (USAVEC) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) st_fragC_q<E>(us_chunk + (n0 + 16 * nt) * CH, 16, 32 * kb, 0, uf[kb]);
         }
@@ -484,56 +423,51 @@ struct Chunk {
     __syncthreads();
     sp = lds_opaque(sp);
 
-    // ---- 6. output tile out (coalesced); the next chunk's staging does not
-    //         touch sp->O.  A correction adds its tile to the stored values.
-    if constexpr (OUT) {
-#pragma unroll
-      for (int j = 0; j < NOP; ++j) {
-        const int e = tid + j * NT, r = e / (DV / OVEC), c0 = (e % (DV / OVEC)) * OVEC;
-        if (r < rows) {
-          ovec_t val;
-          val = *reinterpret_cast<const ovec_t*>(&sp->O[r * LO + c0]);
-          if constexpr (CORR) {
-#pragma unroll
-            for (int i = 0; i < OVEC; ++i) val[i] = to_e<E>(to_f(oold[j][i]) + to_f(val[i]));
-          }
-          *reinterpret_cast<ovec_t*>(static_cast<E*>(p.o) + ((tok0 + r) * H + h) * DV + c0) = val;
-        }
+    // ---- 6. output tile out (coalesced); the next chunk's staging does not touch sp->O
+    if constexpr (OUTC) {
+      constexpr int OVEC = 16 / (int)sizeof(E);
+      typedef E ovec_t __attribute__((__vector_size__(16)));
+      for (int e = tid; e < CH * (DV / OVEC); e += NT) {
+        const int r = e / (DV / OVEC), c0 = (e % (DV / OVEC)) * OVEC;
+        if (r < rows)
+          *reinterpret_cast<ovec_t*>(static_cast<E*>(p.o) + ((tok0 + r) * H + h) * DV + c0) =
+              *reinterpret_cast<const ovec_t*>(&sp->O[r * LO + c0]);
       }
     }
-    return lam_c;
   }
 
-  // Run chunks [cb, ce) of sequence (seq0, len) from the state in hacc.
-  // CORR runs stop early once the accumulated bound falls under 2^-24; the
-  // number of chunks processed is returned through *done.
-  // Issue the loads of chunk cb, the first of a run (before the state is loaded,
-  // so that the two are in flight together).
-  __device__ static void prime(Loader& ld, const FwdParams& p, int64_t seq0, int len, int64_t chunk0, int cb,
+  // Issue the loads of chunk wb, the first of a run (before the state is
+  // loaded, so that the two are in flight together).
+  __device__ static void prime(Loader& ld, const FwdParams& p, int64_t seq0, int len, int64_t chunk0, int wb,
                                int ce, int h) {
-    if (cb < ce) ld.load(p, seq0 + (int64_t)cb * CH, min(CH, len - cb * CH), h, p.rec + ((chunk0 + cb) * p.H + h) * RECF);
+    if (wb < ce) ld.load(p, seq0 + (int64_t)wb * CH, min(CH, len - wb * CH), h, p.rec + ((chunk0 + wb) * p.H + h) * RECF);
   }
-  // ld: primed for chunk cb.
-  __device__ static float run(S& s, const FwdParams& p, int64_t seq0, int len, int64_t chunk0, int cb,
-                              int ce, int h, f32x4 (&hacc)[DK / 16][NTW], int* done, Loader& ld) {
-    float lam = 0.f;
-    int c = cb;
+  // Run chunks [wb, ce) of sequence (seq0, len) from the state in hacc: chunks
+  // before cb are the lead-in (the state advances, nothing is written), chunks
+  // from cb on write their outputs.  ld: primed for chunk wb.
+  __device__ static void run(S& s, const FwdParams& p, int64_t seq0, int len, int64_t chunk0, int wb, int cb,
+                             int ce, int h, f32x4 (&hacc)[DK / 16][NTW], Loader& ld) {
     const size_t SS = (size_t)DK * DV;
     E* hs = static_cast<E*>(p.hs);
-    for (; c < ce; ++c) {
-      if (CORR && lam <= LN_EPS) break;
+    // the lead-in and the segment proper as two loops, each with its own
+    // register allocation
+    auto chunk = [&](auto lead, int c) {
       const int64_t tok0 = seq0 + (int64_t)c * CH;
       const int rows = min(CH, len - c * CH);
       const bool more = c + 1 < ce;
       const int nrows = more ? min(CH, len - (c + 1) * CH) : 0;
-      E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
-      const size_t toff = ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
-      E* usc = USAVE ? static_cast<E*>(p.us) + ((chunk0 + c) * p.H + h) * (size_t)(CH * DV) : nullptr;
+      const float* tin = p.t_in + ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
       const float* nrec = more ? p.rec + ((chunk0 + c + 1) * p.H + h) * RECF : nullptr;
-      lam += step(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, p.t_in + toff, nrec, usc, hacc);
-    }
-    if (done) *done = c - cb;
-    return lam;
+      if constexpr (decltype(lead)::value) {
+        step<true>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, nullptr, tin, nrec, nullptr, hacc);
+      } else {
+        E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
+        E* usc = USAVE ? static_cast<E*>(p.us) + ((chunk0 + c) * p.H + h) * (size_t)(CH * DV) : nullptr;
+        step<false>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, nrec, usc, hacc);
+      }
+    };
+    for (int c = wb; c < cb; ++c) chunk(std::true_type{}, c);
+    for (int c = cb; c < ce; ++c) chunk(std::false_type{}, c);
   }
 };
 
@@ -551,8 +485,7 @@ __device__ void load_state(f32x4 (&hacc)[DK / 16][DV / (16 * FwdWaves<DV>::NW)],
         hacc[t][nt][i] = src ? src[(16 * t + 4 * g + i) * DV + w * (DV / NW) + 16 * nt + c16] : 0.f;
 }
 template <class E, int DK, int DV>
-__device__ void store_state(const f32x4 (&hacc)[DK / 16][DV / (16 * FwdWaves<DV>::NW)], float* dst,
-                            const float* add, bool use_acc) {
+__device__ void store_state(const f32x4 (&hacc)[DK / 16][DV / (16 * FwdWaves<DV>::NW)], float* dst) {
   constexpr int NW = FwdWaves<DV>::NW, NTW = DV / (16 * NW);
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
 #pragma unroll
@@ -560,10 +493,7 @@ __device__ void store_state(const f32x4 (&hacc)[DK / 16][DV / (16 * FwdWaves<DV>
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = (16 * t + 4 * g + i) * DV + w * (DV / NW) + 16 * nt + c16;
-        dst[e] = (use_acc ? hacc[t][nt][i] : 0.f) + (add ? add[e] : 0.f);
-      }
+      for (int i = 0; i < 4; ++i) dst[(16 * t + 4 * g + i) * DV + w * (DV / NW) + 16 * nt + c16] = hacc[t][nt][i];
 }
 
 template <class E, int DK, int DV>
@@ -579,68 +509,30 @@ __device__ void init_smem(FwdSmem<E, DK, DV>& s) {
   __syncthreads();
 }
 
-// Phase 1: every segment from zero (segment 0 from h0).
+// One workgroup per (segment, head).  A segment that does not start its
+// sequence begins with a lead-in from a zero state over the chunks before it
+// whose log-bounds sum to ln 2^-24 or less, so that its state at the segment
+// start equals the exact one to fp32 rounding; if no such lead-in exists the
+// run starts at the sequence start from h0 (exact, and serial for that
+// segment).
 template <class E, int DK, int DV, bool OUT, bool PREP, bool USAVE>
-__global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p1(FwdParams p) {
+__global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_seg(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
   const int h = blockIdx.y, n = sd.n;
   const int nseg = p.seg_first[n + 1] - p.seg_first[n];
-  const size_t SS = (size_t)DK * DV;
-  f32x4 hacc[DK / 16][DV / (16 * FwdWaves<DV>::NW)];
-  using C = Chunk<E, DK, DV, OUT, false, PREP, USAVE>;
-  typename C::Loader ld;
-  C::prime(ld, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n], sd.c_begin, sd.c_end, h);
-  init_smem(s);
-  load_state<E, DK, DV>(hacc, (sd.s == 0 && p.h0) ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-  const float lam = C::run(s, p, p.seq.start(n), p.seq.len(n), p.chunk_first[n], sd.c_begin, sd.c_end, h, hacc,
-                           nullptr, ld);
-  if (nseg == 1) {
-    if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
-  } else {
-    store_state<E, DK, DV>(hacc, p.bstate + ((size_t)blockIdx.x * p.H + h) * SS, nullptr, true);
-    if (threadIdx.x == 0) p.lam[(size_t)blockIdx.x * p.H + h] = lam;
-  }
-}
-
-// Phase 3: boundary corrections (or the serial fallback).
-template <class E, int DK, int DV, bool OUT, bool PREP, bool USAVE>
-__global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_p3(FwdParams p) {
-  __shared__ FwdSmem<E, DK, DV> s;
-  const SegDesc sd = p.segs[blockIdx.x];
-  const int h = blockIdx.y, n = sd.n;
-  const int seg0 = p.seg_first[n];
-  const int nseg = p.seg_first[n + 1] - seg0;
-  if (nseg == 1 || sd.s == 0) return;
-  const int64_t seq0 = p.seq.start(n);
+  const int64_t seq0 = p.seq.start(n), chunk0 = p.chunk_first[n];
   const int len = p.seq.len(n);
   const size_t SS = (size_t)DK * DV;
-  const int64_t chunk0 = p.chunk_first[n];
-  const bool ok = interior_segments_decay(p.lam, seg0, nseg, p.H, h, LN_EPS);
-  if (!ok && sd.s != 1) return;
+  const int wb = sd.c_begin > 0 ? lead_in_begin(p.rec, chunk0, p.H, h, sd.c_begin) : 0;
   f32x4 hacc[DK / 16][DV / (16 * FwdWaves<DV>::NW)];
-  init_smem(s);
-  if (!ok) {
-    // Gates do not decay fast enough to cut this sequence: one workgroup redoes it serially.
-    using C = Chunk<E, DK, DV, OUT, false, PREP, USAVE>;
-    typename C::Loader ld;
-    C::prime(ld, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h);
-    load_state<E, DK, DV>(hacc, p.h0 ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-    C::run(s, p, seq0, len, chunk0, 0, (len + CH - 1) / CH, h, hacc, nullptr, ld);
-    if (p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, nullptr, true);
-    return;
-  }
-  using C = Chunk<E, DK, DV, OUT, true, PREP, USAVE>;
+  using C = Chunk<E, DK, DV, OUT, PREP, USAVE>;
   typename C::Loader ld;
-  C::prime(ld, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h);
-  load_state<E, DK, DV>(hacc, p.bstate + ((size_t)(blockIdx.x - 1) * p.H + h) * SS);
-  int done = 0;
-  C::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, h, hacc, &done, ld);
-  if (sd.s == nseg - 1 && p.hT) {
-    // hT = b_last + (the correction propagated through the whole last segment, if it got there)
-    const float* b = p.bstate + ((size_t)blockIdx.x * p.H + h) * SS;
-    store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS, b, done == sd.c_end - sd.c_begin);
-  }
+  C::prime(ld, p, seq0, len, chunk0, wb, sd.c_end, h);
+  init_smem(s);
+  load_state<E, DK, DV>(hacc, (wb == 0 && p.h0) ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
+  C::run(s, p, seq0, len, chunk0, wb, sd.c_begin, sd.c_end, h, hacc, ld);
+  if (sd.s == nseg - 1 && p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS);
 }
 
 template <class E, int DK, int DV>
@@ -648,31 +540,19 @@ hipError_t launch_fwd_t(const FwdParams& p, int nseg_total, hipStream_t st) {
   dim3 grid(nseg_total, p.H), block(64 * FwdWaves<DV>::NW);
   const bool out = p.o != nullptr;
   const bool prep = p.prep.qk_norm || p.prep.gate_act;
-  // every phase reads T (solved beforehand); the replay always writes U, the
-  // forward proper on request
-  if (!p.t_in) return hipErrorInvalidValue;
+  // T and the scalar records are solved beforehand; the replay always writes
+  // U, the forward proper on request
+  if (!p.t_in || !p.rec) return hipErrorInvalidValue;
   if (!out && !p.us) return hipErrorInvalidValue;
   const bool us = p.us != nullptr;
-  if (p.phase == 1) {
-    if (prep) {
-      if (out && us) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true, true>), grid, block, 0, st, p);
-      else if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, true, false>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, true, true>), grid, block, 0, st, p);
-    } else {
-      if (out && us) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false, true>), grid, block, 0, st, p);
-      else if (out) hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, true, false, false>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p1<E, DK, DV, false, false, true>), grid, block, 0, st, p);
-    }
+  if (prep) {
+    if (out && us) hipLaunchKernelGGL((gdn_fwd_seg<E, DK, DV, true, true, true>), grid, block, 0, st, p);
+    else if (out) hipLaunchKernelGGL((gdn_fwd_seg<E, DK, DV, true, true, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gdn_fwd_seg<E, DK, DV, false, true, true>), grid, block, 0, st, p);
   } else {
-    if (prep) {
-      if (out && us) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, true, true>), grid, block, 0, st, p);
-      else if (out) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, true, false>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, false, true, true>), grid, block, 0, st, p);
-    } else {
-      if (out && us) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, false, true>), grid, block, 0, st, p);
-      else if (out) hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, true, false, false>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gdn_fwd_p3<E, DK, DV, false, false, true>), grid, block, 0, st, p);
-    }
+    if (out && us) hipLaunchKernelGGL((gdn_fwd_seg<E, DK, DV, true, false, true>), grid, block, 0, st, p);
+    else if (out) hipLaunchKernelGGL((gdn_fwd_seg<E, DK, DV, true, false, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gdn_fwd_seg<E, DK, DV, false, false, true>), grid, block, 0, st, p);
   }
   return hipGetLastError();
 }

@@ -32,14 +32,11 @@ struct FwdParams {
   const SegDesc* segs;     // [total segments]
   const int* seg_first;    // [N+1]
   const int* chunk_first;  // [N+1]
-  float* bstate;           // [total segments][H][DK][DV] segment end states
-  float* lam;              // [total segments][H] segment log-bounds
   void* hs;                // nullable: [total chunks][H] chunk start states S, Dv x Dk in st_blk order (dtype)
   void* us;                // nullable: [total chunks][H][DV/16][CH][16] U = Ut - W h of each chunk in 16-column blocks (dtype)
   // [total chunks][H][CH][CH] fp32 row-major T = (I + diag(beta) A)^-1 of each chunk
   const float* t_in;
   const float* rec;        // [total chunks][H][RECF] scalar records
-  int phase;               // 1 = segments from zero / h0, 3 = boundary corrections
   PrepParams prep;
 };
 
@@ -81,12 +78,9 @@ struct RevParams {
   const SegDesc* segs;
   const int* seg_first;
   const int* chunk_first;
-  float* bstate;           // [total segments][H][DK][DV] segment start gradients
-  float* lam;              // [total segments][H]
   void* dhs;               // [total chunks][H] gradient at each chunk END, S-shaped, st_blk order (dtype)
   const float* t_in;       // chunk matrices T (as FwdParams)
   const float* rec;        // scalar records (as FwdParams)
-  int phase;
   PrepParams prep;
 };
 

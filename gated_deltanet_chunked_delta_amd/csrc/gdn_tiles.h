@@ -239,6 +239,44 @@ __device__ __forceinline__ void st_tile_rows(E* base, int ld, int r0, int c0, co
   st4_transposed<E>(base + (r0 + 4 * g + b) * ld + c0 + 4 * q, acc);
 }
 
+// Lead-ins of the segment runs.  The transition of the state (or of its
+// gradient) over chunks a..b-1 has norm at most exp(sum_c Lambda_c), Lambda_c
+// the chunk log-bounds of the scalar records.  A segment whose run starts from
+// a zero state that many chunks before its first (after its last, for the
+// reverse chain) has its boundary state exact to 2^-24 once the sum is at or
+// below LN_EPS.  Every lane of every wave computes the same value.
+//
+// Forward: the largest wb <= cb with sum_{c=wb}^{cb-1} Lambda_c <= LN_EPS, else
+// 0 (the run then starts at the sequence start, from h0: exact).
+__device__ __forceinline__ int lead_in_begin(const float* rec, int64_t chunk0, int H, int h, int cb) {
+  const int l = lane_id();
+  float acc = 0.f;  // sum over the chunks of earlier windows
+  for (int base = cb - 1; base >= 0; base -= 64) {
+    const int c = base - l;
+    const float lam = c >= 0 ? rec[((chunk0 + c) * H + h) * RECF + 5 * CH] : 0.f;
+    const float run = acc + wave_incl_scan(lam);  // sum over chunks c .. cb - 1
+    const unsigned long long hit = __ballot(c >= 0 && run <= LN_EPS);
+    if (hit) return base - (__ffsll((long long)hit) - 1);
+    acc = __shfl(run, 63, 64);
+  }
+  return 0;
+}
+// Reverse chain: the smallest we >= ce with sum_{c=ce}^{we-1} Lambda_c <= LN_EPS,
+// else nch (the run then starts at the sequence end, from dhT: exact).
+__device__ __forceinline__ int lead_in_end(const float* rec, int64_t chunk0, int H, int h, int ce, int nch) {
+  const int l = lane_id();
+  float acc = 0.f;
+  for (int base = ce; base < nch; base += 64) {
+    const int c = base + l;
+    const float lam = c < nch ? rec[((chunk0 + c) * H + h) * RECF + 5 * CH] : 0.f;
+    const float run = acc + wave_incl_scan(lam);  // sum over chunks ce .. c
+    const unsigned long long hit = __ballot(c < nch && run <= LN_EPS);
+    if (hit) return base + __ffsll((long long)hit);
+    acc = __shfl(run, 63, 64);
+  }
+  return nch;
+}
+
 // This thread's 16-byte piece of a chunk's scalar record (threads < RECF / 4),
 // prefetched with the chunk's tiles; store() writes it to LDS, where the
 // record's arrays lie as in memory.

@@ -5,7 +5,7 @@
 // solve" of the forward and backward kernels the "FlashQLA resource" page
 // describes in section 3).  It depends on the chunk's k, g and beta only, not on
 // the state, so it is formed here, chunk-parallel, before the serial chunk
-// chains; they, the corrections and the gradient kernel read it back instead
+// chains; they and the gradient kernel read it back instead
 // of solving on their critical path.
 //
 // One workgroup of three waves per (chunk, head) -- the column solve has three
