@@ -79,7 +79,21 @@ def test_varlen_with_empty_and_tiny_sequences(dev):
         check_bwd(x, dev, cp, "varlen-edge")
 
 
+def test_lead_in_of_varying_length(dev):
+    """Segments of one chunk whose lead-ins (after the segment, in the reverse
+    chain) differ in length, fp32: equal to the oracle and to the unsplit run."""
+    from tests.test_gpu_forward import mixed_decay
+    x = mixed_decay(gdn_inputs.generate(B=1, T=1200, H=2, Dk=64, Dv=64, dtype="f32", seed=22, h0_std=0.3,
+                                        grad=True, dhT=True), 6)
+    base = run_bwd(x, dev, -1)
+    for cp in (1, 3):
+        got, _ = check_bwd(x, dev, cp, "mixed decay")
+        for k in NAMES:
+            assert relerr(got[k], base[k]) < 1e-5, (cp, k)
+
+
 def test_slow_decay_falls_back_to_serial(dev):
+    """Gates near zero: every lead-in reaches the sequence end (from dhT)."""
     x = gdn_inputs.generate(B=1, T=640, H=2, Dk=128, Dv=128, dtype="bf16", seed=17, h0_std=0.2,
                             grad=True, dhT=True)
     x.g = (x.g * 1e-3).astype(np.float32)

@@ -95,7 +95,7 @@ def test_many_sequences(dev, nseq):
 
 def test_segment_split_is_exact(dev):
     """With fp32 arithmetic throughout, forced segment splits agree with the
-    unsplit run to fp32 rounding: the boundary correction drops nothing."""
+    unsplit run to fp32 rounding: the lead-in drops nothing."""
     x = gdn_inputs.generate(B=1, T=1000, H=2, Dk=64, Dv=64, dtype="f32", seed=3, h0_std=0.2)
     o_ref, h_ref = run_fwd(x, dev, -1)
     for cp in (1, 2, 5):
@@ -107,9 +107,30 @@ def test_segment_split_is_exact(dev):
         check_fwd(y, dev, cp, "split-bf16")
 
 
+def mixed_decay(x, seed):
+    """Scale g chunk by chunk (factors 0.01 .. 6), so that the chunks' log-bounds
+    range from about -0.05 to -30 and a segment's lead-in can be one chunk, a
+    few chunks, or reach back to the sequence start."""
+    rng = np.random.default_rng(seed)
+    T = x.g.shape[1]
+    f = rng.choice([0.01, 0.3, 1.0, 6.0], size=(T + 63) // 64)
+    x.g = (x.g * np.repeat(f, 64)[:T][None, :, None]).astype(np.float32)
+    return x
+
+
+def test_lead_in_of_varying_length(dev):
+    """Segments of one chunk whose lead-ins differ in length (mixed decay per
+    chunk), fp32: equal to the oracle and to the unsplit run."""
+    x = mixed_decay(gdn_inputs.generate(B=1, T=1200, H=2, Dk=64, Dv=64, dtype="f32", seed=21, h0_std=0.3), 5)
+    o_ref, h_ref = run_fwd(x, dev, -1)
+    for cp in (1, 3):
+        o, hT = check_fwd(x, dev, cp, "mixed decay")
+        assert relerr(o, o_ref) < 1e-5 and relerr(hT, h_ref) < 1e-5, cp
+
+
 def test_slow_decay_falls_back_to_serial(dev):
-    """Gates near zero do not decay across a segment: the boundary certificate
-    fails and the sequence is recomputed serially -- results stay exact."""
+    """Gates near zero do not decay across a segment: a segment's lead-in
+    reaches back to the sequence start (from h0) -- results stay exact."""
     x = gdn_inputs.generate(B=1, T=640, H=2, Dk=128, Dv=128, dtype="bf16", seed=4, h0_std=0.2)
     x.g = (x.g * 1e-3).astype(np.float32)
     for cp in (1, 3):
