@@ -762,13 +762,15 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       dq1[j][dt] = b[dt];
       udh[j][dt] = c[dt];
       const int dcol = d0 + 16 * dt + c16;
+      // k at the lane's four rows of key column dcol: four consecutive entries of K^T
+      const f32x4 kv4 = ld4f<E>(sKT + dcol * LT + 16 * rt + 4 * g);
+      const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&s.Gam[16 * rt + 4 * g]);
+      const f32x4 ek4 = *reinterpret_cast<const f32x4*>(&s.ek[16 * rt + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
         const float qv = frag_at(qown, 4 * j + i);
-        const float kv = to_f(sK[r * LK + dcol]);
-        rg[j][i] += scale * s.Gam[r] * qv * b[dt][i] - s.ek[r] * kv * c[dt][i];
-        lastsum += s.ek[r] * kv * c[dt][i];
+        rg[j][i] += scale * gm4[i] * qv * b[dt][i] - ek4[i] * kv4[i] * c[dt][i];
+        lastsum += ek4[i] * kv4[i] * c[dt][i];
       }
     }
   }
@@ -834,7 +836,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     const E* sGW = slotE(SQ);
     // K is re-read here: an opaque pointer keeps the compiler from holding the
     // values read in P6 in registers (or scratch) until now
-    const E* sKr = lds_opaque(sK);
+    const E* sKTr = lds_opaque(sKT);
 #pragma unroll
     for (int dt = 0; dt < CTK; ++dt) {
       Frag<E> gwf[2];
@@ -850,14 +852,16 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         f32x4 pq = zero4();  // GPM^T Q (GPM is final since P7)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) mma(pq, ld_fragT<E>(sP, LA, 16 * rt + c16, 32 * kb, 1.f), qr[kb][dt]);
+        const f32x4 kv4 = ld4f<E>(sKTr + dcol * LT + 16 * rt + 4 * g);
+        const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&s.Gam[16 * rt + 4 * g]);
+        const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&s.bg[16 * rt + 4 * g]);
+        const f32x4 ek4 = *reinterpret_cast<const f32x4*>(&s.ek[16 * rt + 4 * g]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * g + i;
-          const float kv = to_f(sKr[r * LK + dcol]);
-          const float xk = xw[i] * kv;
-          rb[j][i] += s.Gam[r] * xk;
-          rg[j][i] += s.bg[r] * xk;
-          dkacc[j][dt][i] = s.bg[r] * xw[i] + s.ek[r] * udh[j][dt][i] + pq[i];
+          const float xk = xw[i] * kv4[i];
+          rb[j][i] += gm4[i] * xk;
+          rg[j][i] += bg4[i] * xk;
+          dkacc[j][dt][i] = bg4[i] * xw[i] + ek4[i] * udh[j][dt][i] + pq[i];
         }
       }
     }
