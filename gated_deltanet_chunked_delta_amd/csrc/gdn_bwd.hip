@@ -412,7 +412,7 @@ struct alignas(16) GradSmem {
   float p7[4][CH], c7[4][CH];  // row sums of GP*P by column tile, column sums by row tile
   float c9[2][CH];             // column sums of T * (dU V^T) by row half
   float c10[2][CH];            // column sums of GA*A by row half
-  float pl[8], ph[8];
+  float ph[8];
   float GamC;
 };
 
@@ -675,9 +675,14 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 
   // per-lane partial sums of this wave's rows (row tiles 2 rh + j)
   f32x4 rg[2], rb[2];  // dgam / dbeta terms
-  float lastsum = 0.f, hdh = 0.f;
+  // e_r = ek_r k_r.(U dh'^T)_r, kept apart: it enters dgam_r with a minus sign
+  // and the last row with a plus, so dg_r gets sum_{i < r} e_i, formed as a
+  // prefix sum (adding and then cancelling it leaves a rounding residue that
+  // strong decay would make larger than dg itself)
+  f32x4 re[2];
+  float hdh = 0.f;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) { rg[j] = zero4(); rb[j] = zero4(); }
+  for (int j = 0; j < 2; ++j) { rg[j] = zero4(); rb[j] = zero4(); re[j] = zero4(); }
 
   // h and dh' down this wave's key columns (the operands of P6): requested now,
   // in flight during P5, quad-transposed in P6
@@ -769,14 +774,13 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float qv = frag_at(qown, 4 * j + i);
-        rg[j][i] += scale * gm4[i] * qv * b[dt][i] - ek4[i] * kv4[i] * c[dt][i];
-        lastsum += ek4[i] * kv4[i] * c[dt][i];
+        rg[j][i] += scale * gm4[i] * qv * b[dt][i];
+        re[j][i] += ek4[i] * kv4[i] * c[dt][i];
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) { pin(rg[j]); pin(rb[j]); }
-  pin(lastsum);
+  for (int j = 0; j < 2; ++j) { pin(rg[j]); pin(rb[j]); pin(re[j]); }
   pin(hdh);
   __syncthreads();  // Q reads done: slot Q becomes GW
   {
@@ -803,7 +807,10 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rt + 4 * g + i;
       const float gp = (c <= r) ? scale * acc[i] : 0.f;
-      const float gpp = gp * sP[r * LA + c];
+      // the diagonal entry enters row sum r and column sum r with opposite
+      // signs: left out of both, it cannot leave a rounding residue in dgam_r
+      // (which strong decay would make larger than dgam itself)
+      const float gpp = (c < r) ? gp * sP[r * LA + c] : 0.f;
       rs4[i] = gpp;
       csum += gpp;
       sP[r * LA + c] = (c <= r) ? gp * __expf(s.gam[r] - s.gam[c]) : 0.f;
@@ -1036,8 +1043,17 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     }
   }
   {
-    const float a = wave_sum(lastsum), b = wave_sum(hdh);
-    if (l == 0) { s.pl[w] = a; s.ph[w] = b; }
+    // slot T is free since P10
+    float* pe = reinterpret_cast<float*>(s.slot[ST]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f32x4 e = re[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = row16_sum(e[i]);
+      if (c16 == 0) *reinterpret_cast<f32x4*>(&pe[cw * CH + 16 * (2 * rh + j) + 4 * g]) = e;
+    }
+    const float b = wave_sum(hdh);
+    if (l == 0) s.ph[w] = b;
   }
   __syncthreads();
   store_tile<E, DV, NT>(slotE(SQ), LV, static_cast<E*>(p.dv) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
@@ -1062,13 +1078,20 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     if (r == CH - 1) {
       float extra = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < 8; ++ww) extra += s.GamC * s.ph[ww] + s.pl[ww];
+      for (int ww = 0; ww < 8; ++ww) extra += s.GamC * s.ph[ww];
       dgm += extra;
     }
-    // dg_r = sum_{r' >= r} dgam_r'  (suffix scan = prefix scan over reversed lanes)
+    const float* pe = reinterpret_cast<const float*>(s.slot[ST]);
+    float e = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) e += pe[ww * CH + r];
+    // dg_r = sum_{r' >= r} dgam_r' (suffix scan = prefix scan over reversed
+    // lanes) + sum_{i < r} e_i (exclusive prefix scan)
     const float rev = __shfl(dgm, CH - 1 - r, 64);
     const float sc = wave_incl_scan(rev);
-    const float dgv = __shfl(sc, CH - 1 - r, 64);
+    const float ei = wave_incl_scan(e);
+    const float ex = __shfl_up(ei, 1, 64);
+    const float dgv = __shfl(sc, CH - 1 - r, 64) + (r == 0 ? 0.f : ex);
     if (r < rows) {
       const int64_t si = (tok0 + r) * H + h;
       if (PREP && p.prep.gate_act) {
