@@ -1,8 +1,9 @@
 """Degenerate gates on the GPU, forward and backward against the fp64 oracle:
 beta = 0 (nothing is written: the state only decays), g = 0 with beta = 0 (the
 state is constant, so h_T equals h0 exactly), decay so strong that exp(cumsum g)
-underflows inside a chunk, and beta = 1 with unit keys (each write replaces the
-state's component along k)."""
+underflows inside a chunk, beta = 1 with unit keys (each write replaces the
+state's component along k), and beta = 2.5 (writes that expand the state
+along k, so the norm bound that sizes the lead-in has a positive term)."""
 import numpy as np
 import pytest
 
@@ -95,3 +96,24 @@ def test_split_matches_unsplit_without_decay(dev):
     o_ref, h_ref = run_fwd(x, dev, -1)
     o, hT = run_fwd(x, dev, 1)
     assert relerr(o, o_ref) < 1e-5 and relerr(hT, h_ref) < 1e-5
+
+
+def test_expanding_writes(dev):
+    """beta = 2.5 with unit keys: ||I - beta k k^T|| = 1.5, so each chunk's
+    log-bound carries 64 log 1.5 besides its decay (g = -0.485 per token leaves
+    about -5 per chunk).  A lead-in sized without that term would stop four
+    times too early; split and unsplit runs must still agree to fp32 rounding,
+    forward and backward, and both match the oracle."""
+    from tests.test_gpu_backward import NAMES, run_bwd
+    rng = np.random.default_rng(806)
+    x = base("f32", 806, T=640)
+    x.beta = np.full_like(x.beta, 2.5)
+    x.g = (-0.485 + 0.02 * rng.standard_normal(x.g.shape)).astype(np.float32)
+    o_ref, h_ref = run_fwd(x, dev, -1)
+    g_ref = run_bwd(x, dev, -1)
+    for cp in (1, 3):
+        o, hT = check_fwd(x, dev, cp, "beta=2.5")
+        assert relerr(o, o_ref) < 1e-5 and relerr(hT, h_ref) < 1e-5, cp
+        got, _ = check_bwd(x, dev, cp, "beta=2.5")
+        for k in NAMES:
+            assert relerr(got[k], g_ref[k]) < 1e-5, (cp, k)
