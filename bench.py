@@ -40,8 +40,8 @@ def kernel_models(dk, dv, esz):
     fwd:  the forward chunk algebra; reads q, k, v, g, beta and writes o.
     rev:  the state-gradient chain (diag(Gam)Q)^T dO and W^T dU; reads q, k, g, beta, dO.
     grad: the rest of the backward; reads q, k, v, dO, g, beta, writes dq, dk, dv, dbeta, dg.
-    The replay and boundary-correction launches are recomputation and count no
-    algorithmic work.
+    The replay and the lead-in chunks of the chains are recomputation and count
+    no algorithmic work.
     """
     fwd, bwd = flops_per_token_head(dk, dv)
     rev = 4 * dk * dv
