@@ -79,6 +79,24 @@ def measured_traffic(kernel, workload):
     return rec["traffic_bytes_per_launch"]
 
 
+def host_info():
+    """Threads this process may run on and the CPU model (from /proc/cpuinfo)."""
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return nproc, model
+
+
 def cpu_baseline(x_full, seconds_target=15.0):
     """Time the fp64 oracle (forward, then backward) on the first tokens of the workload."""
     from oracle import ref
@@ -99,9 +117,88 @@ def cpu_baseline(x_full, seconds_target=15.0):
         Ts = min(T, int(Ts * min(8.0, max(2.0, seconds_target / max(dt, 1e-3)))))
         dt = run(Ts)
     B, _, H, _ = x_full.q.shape
+    nproc, model = host_info()
     return {"value": B * Ts / dt, "unit": "tokens/s", "cores": ref.threads(), "kind": "oracle",
+            "nproc": nproc, "cpu_model": model,
             "sample": f"first {Ts} of {T} tokens (B={B}, all {H} heads), fp64 token recurrence forward "
                       f"then its reverse-mode backward, {dt:.1f} s"}
+
+
+def summarize_pmc(paths):
+    """Per-kernel means of rocprofv3 --pmc counter_collection.csv files (one or more passes):
+    a markdown table with every counter's mean per dispatch and, where the counters are
+    present, instructions per wave and the busy fractions of the matrix cores
+    (SQ_VALU_MFMA_BUSY_CYCLES over the kernel's cycles x 1024 SIMDs), the vector ALUs
+    (4 SQ_ACTIVE_INST_VALU over the same) and the LDS (SQ_LDS_IDX_ACTIVE over the
+    kernel's cycles x 256 CUs).  The kernel's cycles are GRBM_GUI_ACTIVE / 8: the
+    counter is summed over MI355X's eight accelerator dies (XCDs)."""
+    import csv
+    import re
+    def demangle(n):
+        # this library's kernels: _ZN3gdn[12_GLOBAL__N_1]<len><name>I<template args>EEvNS_...
+        m = re.match(r"_ZN3gdn(?:12_GLOBAL__N_1)?(\d+)(\w+)", n)
+        if not m:
+            return n
+        ln = int(m.group(1))
+        base, rest = m.group(2)[:ln], m.group(2)[ln:]
+        if not rest.startswith("I"):
+            return base
+        out = []
+        for t in re.finditer(r"DF16b|L[bi]\d+E|f(?=L|E)", rest):
+            tok = t.group(0)
+            out.append("bf16" if tok == "DF16b" else ("f32" if tok == "f" else tok[2:-1]))
+        return f"{base}<{','.join(out)}>"
+
+    vals = {}      # kernel -> counter -> [values]
+    meta = {}      # kernel -> (grid, workgroup, lds, vgpr, agpr)
+    rows = []
+    for path in paths:
+        with open(path, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    names = sorted({r["Kernel_Name"] for r in rows})
+    demangled = {n: demangle(n) for n in names}
+    if True:
+        if True:
+            for row in rows:
+                name = demangled[row["Kernel_Name"]]
+                short = re.sub(r"\(.*\)$", "", name).replace("void ", "")
+                short = re.sub(r"gdn::(?:\(anonymous namespace\)::)?", "", short)
+                short = short.replace("__hip_bfloat16", "bf16").replace("__bf16", "bf16")
+                short = short.replace("true", "1").replace("false", "0")
+                if "at::native" in name or "elementwise" in name or "fill" in name.lower():
+                    short = "torch: " + re.sub(r"<.*", "", short.split("::")[-1])
+                d = vals.setdefault(short, {})
+                d.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                meta[short] = (row.get("Grid_Size"), row.get("Workgroup_Size"), row.get("LDS_Block_Size"),
+                               row.get("VGPR_Count"), row.get("Accum_VGPR_Count"))
+    counters = sorted({c for d in vals.values() for c in d})
+    lines = ["| kernel | dispatches | grid | wg | LDS | VGPR/AGPR | " + " | ".join(counters) + " | per wave |",
+             "|---" * (6 + len(counters) + 1) + "|"]
+    for k in sorted(vals, key=lambda kk: -max(len(v) for v in vals[kk].values())):
+        d = vals[k]
+        n = max(len(v) for v in d.values())
+        mean = {c: sum(v) / len(v) for c, v in d.items()}
+        per = []
+        waves = mean.get("SQ_WAVES")
+        if waves:
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD",
+                      "SQ_INSTS_VMEM_WR"):
+                if c in mean:
+                    per.append(f"{c[9:]} {mean[c] / waves:,.0f}")
+        gui = mean.get("GRBM_GUI_ACTIVE")
+        if gui:
+            gui /= 8.0  # summed over the eight XCDs
+            per.append(f"cycles {gui:,.0f}")
+            for c, lab, units in (("SQ_VALU_MFMA_BUSY_CYCLES", "MFMA busy", 1024), ("SQ_ACTIVE_INST_VALU", "VALU busy",
+                                                                                    1024 / 4),
+                                  ("SQ_LDS_IDX_ACTIVE", "LDS busy", 256)):
+                if c in mean:
+                    per.append(f"{lab} {100 * mean[c] / (gui * units):.1f}%")
+        g, wg, lds, vg, ag = meta[k]
+        lines.append(f"| `{k}` | {n} | {g} | {wg} | {lds} | {vg}/{ag} | "
+                     + " | ".join(f"{mean[c]:,.0f}" if c in mean else "" for c in counters)
+                     + " | " + ", ".join(per) + " |")
+    return "\n".join(lines)
 
 
 def bench_decode(args, log):
@@ -183,7 +280,7 @@ def bench_decode(args, log):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="metric_32k")
     ap.add_argument("--direction", default="fwdbwd", choices=["fwdbwd", "fwd", "bwd", "decode"],
@@ -206,7 +303,17 @@ def main():
                     help="after timing, run a plain device copy (out = x * 1, fp32) of this many MiB three "
                          "times: the reference kernel that scales HBM byte counters under rocprofv3 --pmc")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-protocol", action="store_true",
+                    help="skip the per-direction timing protocol (median / min / max over --protocol-iters "
+                         "iterations, each after a 1 GiB write that flushes L2 and the last-level cache)")
+    ap.add_argument("--protocol-iters", type=int, default=30)
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="print a per-kernel markdown summary of rocprofv3 --pmc counter_collection.csv "
+                         "files and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
@@ -320,7 +427,54 @@ def main():
                    "ms_per_step": ms_v, "value": ntok * 1e3 / ms_v, "unit": "tokens/s"}
         log(f"timed {args.steps} steps with saved states")
 
+    # Timing protocol per direction: the forward alone (keeping T, as in the
+    # step), the backward alone (given that T), and both; 5 warm-ups, then the
+    # median, min and max of --protocol-iters iterations, each timed by its own
+    # event pair on the launch stream after a 1 GiB write that evicts L2 and the
+    # last-level cache (the write is enqueued before the first event).
+    protocol = None
     fwd_f, bwd_f = flops_per_token_head(dk, dv)
+    if not args.no_protocol and args.api == "abi" and args.direction == "fwdbwd":
+        log(f"timing protocol: {args.protocol_iters} iterations per direction, 1 GiB write before each")
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        kw = dict(h0=h0, cu_seqlens=cu, cu_seqlens_host=host, cp_mode=args.cp_mode, **prep_kw)
+
+        def p_fwd():
+            return gb.gdn_chunk_fwd(q, k, v, g, beta, x.scale, save_t=True, **kw)[-1]
+
+        t_kept = p_fwd()
+
+        def p_bwd():
+            gb.gdn_chunk_bwd(q, k, v, g, beta, x.scale, do, need_dh0=h0 is not None, chunk_t=t_kept, **kw)
+
+        def p_both():
+            tt = p_fwd()
+            gb.gdn_chunk_bwd(q, k, v, g, beta, x.scale, do, need_dh0=h0 is not None, chunk_t=tt, **kw)
+
+        protocol = {"method": f"5 warm-ups, then {args.protocol_iters} iterations, each after a 1 GiB device "
+                              "write (L2 and last-level cache evicted), timed by HIP events on the launch "
+                              "stream; median, min, max",
+                    "flop_per_token_head": {"fwd": fwd_f, "bwd": bwd_f, "fwdbwd": fwd_f + bwd_f}}
+        for name, fn, fl in (("fwd", p_fwd, fwd_f), ("bwd", p_bwd, bwd_f), ("fwdbwd", p_both, fwd_f + bwd_f)):
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(args.protocol_iters):
+                flush.fill_(1.0)
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_.record(stream)
+                fn()
+                b_.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a_.elapsed_time(b_))
+            med = float(np.median(ts))
+            tf = fl * ntok * H / (med * 1e-3) / 1e12
+            protocol[name] = {"median_ms": med, "min_ms": float(np.min(ts)), "max_ms": float(np.max(ts)),
+                              "tokens_per_s": ntok * 1e3 / med, "tflops": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS}
+        del flush
+        log("timing protocol done")
+
     per_th = {"fwdbwd": fwd_f + bwd_f, "fwd": fwd_f, "bwd": bwd_f}[args.direction]
     tflops = per_th * ntok * H / (ms * 1e-3) / 1e12
     kernels = {name: {"avg_ms": tot / n, "launches_per_step": n / args.steps}
@@ -358,6 +512,12 @@ def main():
         "tflops": tflops, "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "kernels": kernels, "ms_per_step_with_kernel_events": ms_prof, "roofline": roof,
     }
+    if protocol is not None:
+        out["fwd_ms"] = protocol["fwd"]["median_ms"]
+        out["bwd_ms"] = protocol["bwd"]["median_ms"]
+        out["frac_bf16_peak_fwd"] = protocol["fwd"]["frac_bf16_peak"]
+        out["frac_bf16_peak_bwd"] = protocol["bwd"]["frac_bf16_peak"]
+        out["protocol"] = protocol
     if variant is not None:
         out["variant_saved_states"] = variant
     if args.copy_mib > 0:

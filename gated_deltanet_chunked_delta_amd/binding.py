@@ -13,7 +13,9 @@ from typing import Optional, Sequence
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgdn.so")
+# GDN_LIB selects another build of the same library (for instance one whose host
+# code carries sanitizers, see build.py --sanitize); there is no other fallback.
+LIB_PATH = os.environ.get("GDN_LIB") or os.path.join(HERE, "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_E_INVALID", 2: "GDN_E_UNSUPPORTED", 3: "GDN_E_WORKSPACE", 4: "GDN_E_HIP"}
@@ -175,18 +177,28 @@ def _stream(dev):
 
 def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_seqlens_host=None,
                   output_final_state: bool = True, cp_mode: int = 0, save_states: bool = False,
-                  save_t: bool = False, qk_norm: bool = False, gate_act: bool = False, gate_scale=None):
+                  save_t: bool = False, qk_norm: bool = False, gate_act: bool = False, gate_scale=None,
+                  o=None, hT=None):
     """Forward pass.  Returns (o, hT) with hT None unless output_final_state, followed by
     states if save_states (the state at every chunk start, a flat tensor of the input
     dtype) and chunk_t if save_t (every chunk's matrix T, a flat fp32 tensor); both are
     for gdn_chunk_bwd.  qk_norm / gate_act select the in-kernel pre-processing (raw q,
-    k; gate and beta logits, see include/gdn.h)."""
+    k; gate and beta logits, see include/gdn.h).  o / hT: optional output tensors
+    to write into (else allocated)."""
     a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode,
                       qk_norm, gate_act, gate_scale)
     L = lib()
-    o = torch.empty(q.shape[:3] + (a.Dv,), dtype=q.dtype, device=q.device)
-    hT = (torch.empty((a.num_seqs, a.H, a.Dk, a.Dv), dtype=torch.float32, device=q.device)
-          if output_final_state else None)
+    if o is None:
+        o = torch.empty(q.shape[:3] + (a.Dv,), dtype=q.dtype, device=q.device)
+    _contig("o", o, q.dtype, q.device)
+    if tuple(o.shape) != tuple(q.shape[:3]) + (a.Dv,):
+        raise GDNError("o has the wrong shape")
+    if hT is None and output_final_state:
+        hT = torch.empty((a.num_seqs, a.H, a.Dk, a.Dv), dtype=torch.float32, device=q.device)
+    if hT is not None:
+        _contig("hT", hT, torch.float32, q.device)
+        if tuple(hT.shape) != (a.num_seqs, a.H, a.Dk, a.Dv):
+            raise GDNError("hT has the wrong shape")
     states = None
     if save_states:
         nb = L.gdn_chunk_states_bytes(ctypes.byref(a))

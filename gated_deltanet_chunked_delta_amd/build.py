@@ -23,30 +23,46 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INC, "-I"
          "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-    cmd = ["hipcc", "-c", *FLAGS, os.path.join(CSRC, src), "-o", obj]
+# Host-side sanitizers only (the device code is built as always): for CPU runs of
+# the argument checks and the workspace layout, with clang's ASan runtime preloaded.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, obj_dir: str = OBJ, extra=()) -> str:
+    obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
+    cmd = ["hipcc", "-c", *FLAGS, *extra, os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+    """Compile every source and link `out`.  sanitize: host code with AddressSanitizer and
+    UndefinedBehaviorSanitizer (objects in a separate folder; load with GDN_LIB=out)."""
+    obj_dir = OBJ + ("_san" if sanitize else "")
+    os.makedirs(obj_dir, exist_ok=True)
+    extra = SAN_FLAGS if sanitize else ()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = ["hipcc", "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s_: _compile(s_, obj_dir, extra), SOURCES))
+    tmp = out + ".tmp"
+    cmd = ["hipcc", "-shared", f"--offload-arch={ARCH}", "-fPIC", *(SAN_FLAGS if sanitize else ()), *objs,
+           "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(LIB)
-    return LIB
+        print(out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--sanitize", action="store_true")
+    ap.add_argument("--out", default=LIB)
+    a = ap.parse_args()
+    build(verbose=True, out=os.path.abspath(a.out), sanitize=a.sanitize)
     sys.exit(0)

@@ -52,7 +52,7 @@ struct Plan {
   bool cp = false;      // some sequence has more than one segment
   // workspace offsets (bytes)
   size_t o_chunk_first = 0, o_seg_first = 0, o_segs = 0, o_chunk_tab = 0;
-  size_t o_hs = 0, o_us = 0, o_dhs = 0, o_ts = 0, total = 0;
+  size_t o_hs = 0, o_us = 0, o_ulo = 0, o_dhs = 0, o_ts = 0, o_ep = 0, total = 0;
 };
 
 bool supported(int dtype, int Dk, int Dv) {
@@ -163,10 +163,13 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false, 
     if (!saved) {
       p.o_hs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
       p.o_us = take(esz * CHUNK * (size_t)a.Dv * std::max(1, p.nchunk) * a.H);
+      if (a.dtype == GDN_BF16) p.o_ulo = take(esz * CHUNK * (size_t)a.Dv * std::max(1, p.nchunk) * a.H);
     }
     // the chunk matrices T, solved once and read by the later kernels
     if (!t_given) p.o_ts = take(tbytes);
     p.o_dhs = take(esz * SS * (size_t)std::max(1, p.nchunk) * a.H);
+    // the reverse chain's per-wave row terms of the decay gradient
+    p.o_ep = take(sizeof(float) * gdn::EPW * CHUNK * (size_t)std::max(1, p.nchunk) * a.H);
   }
   p.total = off;
   return p;
@@ -227,9 +230,13 @@ long long count_chunks(const gdn_common_args& a) {
   return chunks;
 }
 
-// The saved-states buffer: the chunk states, then every chunk's U.
+// The saved-states buffer: the chunk states, then every chunk's U, then (bf16)
+// every chunk's U rounding residual.
 size_t states_part_bytes(const gdn_common_args& a) {
   return (size_t)count_chunks(a) * a.H * a.Dk * a.Dv * (a.dtype == GDN_BF16 ? 2 : 4);
+}
+size_t u_part_bytes(const gdn_common_args& a) {
+  return (size_t)count_chunks(a) * a.H * CHUNK * a.Dv * (a.dtype == GDN_BF16 ? 2 : 4);
 }
 
 }  // namespace
@@ -295,8 +302,7 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args) {
 size_t gdn_chunk_states_bytes(const gdn_common_args* a) {
   if (!a) { fail(GDN_E_INVALID, "null args"); return 0; }
   if (check_common(*a) != GDN_OK) return 0;
-  const size_t esz = a->dtype == GDN_BF16 ? 2 : 4;
-  return states_part_bytes(*a) + (size_t)count_chunks(*a) * a->H * CHUNK * a->Dv * esz;
+  return states_part_bytes(*a) + u_part_bytes(*a) * (a->dtype == GDN_BF16 ? 2 : 1);
 }
 
 size_t gdn_chunk_t_bytes(const gdn_common_args* a) {
@@ -323,8 +329,9 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   void* ws = a.workspace;
   gdn::SeqInfo sq = seq_info(a);
   hipError_t e = timed("plan", s, [&] {
-    return gdn::launch_plan(sq, pl.N, pl.segc, at<int>(ws, pl.o_chunk_first), at<int>(ws, pl.o_seg_first),
-                            at<gdn::SegDesc>(ws, pl.o_segs), at<int2>(ws, pl.o_chunk_tab), s);
+    return gdn::launch_plan(sq, pl.N, pl.segc, a.T, pl.nchunk, pl.nseg, at<int>(ws, pl.o_chunk_first),
+                            at<int>(ws, pl.o_seg_first), at<gdn::SegDesc>(ws, pl.o_segs),
+                            at<int2>(ws, pl.o_chunk_tab), s);
   });
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   gdn::FwdParams p{};
@@ -335,6 +342,7 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   p.chunk_first = at<int>(ws, pl.o_chunk_first);
   p.hs = args->h_save;  // nullable: the chunk states (and U) are stored only on request
   p.us = args->h_save ? static_cast<char*>(args->h_save) + states_part_bytes(a) : nullptr;
+  p.ulo = args->h_save && a.dtype == GDN_BF16 ? static_cast<char*>(p.us) + u_part_bytes(a) : nullptr;
   p.prep = prep_of(a.qk_norm, a.gate_act, a.gate_scale);
   // every chunk's T, solved chunk-parallel (into the caller's buffer when it
   // keeps T) and read by the chunk chain
@@ -380,8 +388,9 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   void* ws = a.workspace;
   gdn::SeqInfo sq = seq_info(a);
   hipError_t e = timed("plan", s, [&] {
-    return gdn::launch_plan(sq, pl.N, pl.segc, at<int>(ws, pl.o_chunk_first), at<int>(ws, pl.o_seg_first),
-                            at<gdn::SegDesc>(ws, pl.o_segs), at<int2>(ws, pl.o_chunk_tab), s);
+    return gdn::launch_plan(sq, pl.N, pl.segc, a.T, pl.nchunk, pl.nseg, at<int>(ws, pl.o_chunk_first),
+                            at<int>(ws, pl.o_seg_first), at<gdn::SegDesc>(ws, pl.o_segs),
+                            at<int2>(ws, pl.o_chunk_tab), s);
   });
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   // 1. forward replay: state at every chunk start (unless the forward saved them)
@@ -410,9 +419,11 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   if (saved) {
     p.hs = const_cast<void*>(args->h_saved);
     p.us = static_cast<char*>(const_cast<void*>(args->h_saved)) + states_part_bytes(a);
+    p.ulo = a.dtype == GDN_BF16 ? static_cast<char*>(p.us) + u_part_bytes(a) : nullptr;
   } else {
     p.hs = at<void>(ws, pl.o_hs);
     p.us = at<void>(ws, pl.o_us);
+    p.ulo = a.dtype == GDN_BF16 ? at<void>(ws, pl.o_ulo) : nullptr;
     e = timed("replay", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
     if (e != hipSuccess) return hip_fail(e, "replay launch");
   }
@@ -424,6 +435,9 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   r.dhs = at<void>(ws, pl.o_dhs);
   r.t_in = ts;
   r.rec = rec;
+  r.us = p.us;
+  r.ulo = p.ulo;
+  r.ep = at<float>(ws, pl.o_ep);
   r.prep = p.prep;
   e = timed("rev", s, [&] { return gdn::launch_rev(a.dtype, a.Dk, a.Dv, r, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "reverse launch");
@@ -431,7 +445,7 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   if (pl.nchunk > 0) {
     gdn::GradParams gp{};
     gp.q = a.q; gp.k = a.k; gp.v = a.v; gp.g = a.g; gp.beta = a.beta; gp.dout = args->do_;
-    gp.hs = p.hs; gp.dhs = r.dhs; gp.us = p.us; gp.t_in = ts;
+    gp.hs = p.hs; gp.dhs = r.dhs; gp.us = p.us; gp.t_in = ts; gp.ep = r.ep;
     gp.dq = args->dq; gp.dk = args->dk; gp.dv = args->dv; gp.dbeta = args->dbeta; gp.dg = args->dg;
     gp.scale = a.scale; gp.H = a.H; gp.seq = sq;
     gp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);

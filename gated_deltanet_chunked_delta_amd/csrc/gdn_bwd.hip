@@ -122,13 +122,35 @@ struct RevChunk {
   // t_in: this chunk's T; nrec: the next chunk's scalar record.  LEAD: a
   // lead-in chunk after the segment proper, which only advances the gradient
   // (nothing is written).
+  //
+  // Besides, for the decay gradient, the row terms e_r = ek_r u_r . (dS' k_r)
+  // (dS' = this chunk's end gradient, u_r = row r of its U) summed over this
+  // wave's value columns go to ep_chunk[w][r].  Their sum over r can be far
+  // smaller than its parts (strong decay leaves little else in dg), so both
+  // factors are carried to about 16 bits: dS' as its bf16 value plus the bf16
+  // residual (two products with K), U as the stored bf16 value plus its stored
+  // residual (us_chunk, ulo_chunk).
   template <bool LEAD>
   __device__ static void step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows, int h,
-                              E* dhs_chunk, const float* t_in, const float* nrec, f32x4 (&dh)[DK / 16][NTW]) {
+                              E* dhs_chunk, const float* t_in, const float* nrec, const E* us_chunk,
+                              const E* ulo_chunk, float* ep_chunk, f32x4 (&dh)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
+    constexpr bool LO = std::is_same<E, bf16>::value;  // U and dS' need their residuals
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
     const int n0 = w * (DV / NW);
+    // this wave's columns of U (and its residual) for the row terms, read now
+    // and used in phase 5
+    CPiece<E> uhp[4][NTW], ulp[4][NTW];
+    if constexpr (!LEAD) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          uhp[rt][nt].load(us_chunk + (n0 + 16 * nt) * CH, 16 * rt);
+          if constexpr (LO) ulp[rt][nt].load(ulo_chunk + (n0 + 16 * nt) * CH, 16 * rt);
+        }
+    }
 
     // ---- 1. gradient at the chunk end out; tiles into LDS; scalars
     S* sp = lds_opaque(&s0);
@@ -223,11 +245,14 @@ struct RevChunk {
     f32x4 du[4][NTW];
     {
       S& s = *lds_opaque(&s0);
-      Frag<E> hf[NTW][DK / 32];
+      Frag<E> hf[NTW][DK / 32], hflo[NTW][DK / 32];
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) pack_frag(hf[nt][kb], dh[2 * kb][nt], dh[2 * kb + 1][nt]);
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          pack_frag(hf[nt][kb], dh[2 * kb][nt], dh[2 * kb + 1][nt]);
+          if constexpr (LO && !LEAD) pack_frag(hflo[nt][kb], bf16_residual(dh[2 * kb][nt]), bf16_residual(dh[2 * kb + 1][nt]));
+        }
       Frag<E> yd[NTW][2];
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
@@ -242,15 +267,34 @@ struct RevChunk {
         Frag<E> xp[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) xp[kb] = ld_frag(s.PT, LT, 16 * rt + c16, 32 * kb);
+        f32x4 er = zero4();  // row terms of this lane's rows, over its columns
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
           f32x4 acc = zero4();
 #pragma unroll
           for (int kb = 0; kb < DK / 32; ++kb) mma(acc, xk[kb], hf[nt][kb]);
+          if constexpr (!LEAD) {
+            f32x4 z = acc;  // K dS'^T: this lane's rows, column n0 + 16 nt + c16
+            f32x4 u = uhp[rt][nt].get();
+            if constexpr (LO) {
+              f32x4 zl = zero4();
+#pragma unroll
+              for (int kb = 0; kb < DK / 32; ++kb) mma(zl, xk[kb], hflo[nt][kb]);
+              z = z + zl;
+              u = u + ulp[rt][nt].get();
+            }
+            er = er + u * z;
+          }
           acc = acc * e4;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) mma(acc, xp[kb], yd[nt][kb]);
           du[rt][nt] = acc;
+        }
+        if constexpr (!LEAD) {
+          er = er * e4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) er[i] = row16_sum(er[i]);
+          if (c16 == 0) *reinterpret_cast<f32x4*>(ep_chunk + w * CH + 16 * rt + 4 * g) = er;
         }
       }
       const float gc = s.tail[1];
@@ -286,6 +330,7 @@ struct RevChunk {
   __device__ static void run(S& s, const RevParams& p, int64_t seq0, int len, int64_t chunk0, int cb, int ce, int we,
                              int h, f32x4 (&dh)[DK / 16][DV / (16 * RevWaves<DV>::NW)], Loader& ld) {
     const size_t SS = (size_t)DK * DV;
+    constexpr bool LOU = std::is_same<E, bf16>::value;
     E* dhs = static_cast<E*>(p.dhs);
     // the lead-in and the segment proper as two loops, each with its own
     // register allocation
@@ -296,8 +341,14 @@ struct RevChunk {
       const int nrows = more ? min(CH, len - (c - 1) * CH) : 0;
       const float* tin = p.t_in + ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
       const float* nrec = more ? p.rec + ((chunk0 + c - 1) * p.H + h) * RECF : nullptr;
-      if constexpr (decltype(lead)::value) step<true>(s, p, ld, rows, ntok0, nrows, h, nullptr, tin, nrec, dh);
-      else step<false>(s, p, ld, rows, ntok0, nrows, h, dhs + ((chunk0 + c) * p.H + h) * SS, tin, nrec, dh);
+      if constexpr (decltype(lead)::value) {
+        step<true>(s, p, ld, rows, ntok0, nrows, h, nullptr, tin, nrec, nullptr, nullptr, nullptr, dh);
+      } else {
+        const size_t ci = (chunk0 + c) * p.H + h;
+        const E* usc = static_cast<const E*>(p.us) + ci * (CH * DV);
+        const E* ulc = LOU ? static_cast<const E*>(p.ulo) + ci * (CH * DV) : nullptr;
+        step<false>(s, p, ld, rows, ntok0, nrows, h, dhs + ci * SS, tin, nrec, usc, ulc, p.ep + ci * (EPW * CH), dh);
+      }
     };
     for (int c = we - 1; c >= ce; --c) chunk(std::true_type{}, c);
     for (int c = ce - 1; c >= cb; --c) chunk(std::false_type{}, c);
@@ -350,6 +401,7 @@ template <class E, int DK, int DV, bool PREP>
 __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_seg(RevParams p) {
   __shared__ RevSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
+  if (sd.n < 0) return;  // the plan found the device cu_seqlens inconsistent
   const int h = blockIdx.y, n = sd.n;
   const int64_t seq0 = p.seq.start(n), chunk0 = p.chunk_first[n];
   const int len = p.seq.len(n), nch = (len + CH - 1) / CH;
@@ -369,8 +421,10 @@ template <class E, int DK, int DV>
 hipError_t launch_rev_t(const RevParams& p, int nseg_total, hipStream_t st) {
   const dim3 block(64 * RevWaves<DV>::NW);
   const dim3 grid(nseg_total, p.H);
-  // T and the scalar records are solved beforehand
-  if (!p.t_in || !p.rec) return hipErrorInvalidValue;
+  // T and the scalar records are solved beforehand; U (with its bf16 residual)
+  // is stored by the forward or its replay
+  if (!p.t_in || !p.rec || !p.us || !p.ep) return hipErrorInvalidValue;
+  if (std::is_same<E, bf16>::value && !p.ulo) return hipErrorInvalidValue;
   if (p.prep.qk_norm || p.prep.gate_act) hipLaunchKernelGGL((gdn_rev_seg<E, DK, DV, true>), grid, block, 0, st, p);
   else hipLaunchKernelGGL((gdn_rev_seg<E, DK, DV, false>), grid, block, 0, st, p);
   return hipGetLastError();
@@ -510,6 +564,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int cw = w & 3, rh = w >> 2;
   const int2 ctab = p.chunk_tab[blockIdx.x];
+  if (ctab.x < 0) return;  // the plan found the device cu_seqlens inconsistent
   const int n = ctab.x, jc = ctab.y, h = blockIdx.y, H = p.H;
   const int len = p.seq.len(n);
   const int64_t tok0 = p.seq.start(n) + (int64_t)jc * CH;
@@ -528,6 +583,18 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   float* sKD = slotF(SKD);
   float* sP = slotF(SP);
   E* sDU = slotE(SDU);
+
+  // e_r = ek_r k_r.(U dh'^T)_r, the reverse chain's row terms (summed here over
+  // its waves): it enters dgam_r with a minus sign and the last row with a plus,
+  // so dg_r gets sum_{i < r} e_i, formed as a prefix sum (adding and then
+  // cancelling it leaves a rounding residue that strong decay would make larger
+  // than dg itself).  Read now, used at the end.
+  float epv[RevWaves<DV>::NW];
+  {
+    const float* ep = p.ep + ((size_t)blockIdx.x * H + h) * (EPW * CH);
+#pragma unroll
+    for (int ww = 0; ww < RevWaves<DV>::NW; ++ww) epv[ww] = w == 0 ? ep[ww * CH + l] : 0.f;
+  }
 
   // ---- P1: staging (all four tiles in flight at once; rows past the end are
   //          zero); zero T (unless given), P and the cross-wave sum arrays.
@@ -675,14 +742,9 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 
   // per-lane partial sums of this wave's rows (row tiles 2 rh + j)
   f32x4 rg[2], rb[2];  // dgam / dbeta terms
-  // e_r = ek_r k_r.(U dh'^T)_r, kept apart: it enters dgam_r with a minus sign
-  // and the last row with a plus, so dg_r gets sum_{i < r} e_i, formed as a
-  // prefix sum (adding and then cancelling it leaves a rounding residue that
-  // strong decay would make larger than dg itself)
-  f32x4 re[2];
   float hdh = 0.f;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) { rg[j] = zero4(); rb[j] = zero4(); re[j] = zero4(); }
+  for (int j = 0; j < 2; ++j) { rg[j] = zero4(); rb[j] = zero4(); }
 
   // h and dh' down this wave's key columns (the operands of P6): requested now,
   // in flight during P5, quad-transposed in P6
@@ -766,21 +828,16 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       gw[j][dt] = zero4() - a[dt];
       dq1[j][dt] = b[dt];
       udh[j][dt] = c[dt];
-      const int dcol = d0 + 16 * dt + c16;
-      // k at the lane's four rows of key column dcol: four consecutive entries of K^T
-      const f32x4 kv4 = ld4f<E>(sKT + dcol * LT + 16 * rt + 4 * g);
       const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&s.Gam[16 * rt + 4 * g]);
-      const f32x4 ek4 = *reinterpret_cast<const f32x4*>(&s.ek[16 * rt + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float qv = frag_at(qown, 4 * j + i);
         rg[j][i] += scale * gm4[i] * qv * b[dt][i];
-        re[j][i] += ek4[i] * kv4[i] * c[dt][i];
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) { pin(rg[j]); pin(rb[j]); pin(re[j]); }
+  for (int j = 0; j < 2; ++j) { pin(rg[j]); pin(rb[j]); }
   pin(hdh);
   __syncthreads();  // Q reads done: slot Q becomes GW
   {
@@ -1043,15 +1100,6 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     }
   }
   {
-    // slot T is free since P10
-    float* pe = reinterpret_cast<float*>(s.slot[ST]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      f32x4 e = re[j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) e[i] = row16_sum(e[i]);
-      if (c16 == 0) *reinterpret_cast<f32x4*>(&pe[cw * CH + 16 * (2 * rh + j) + 4 * g]) = e;
-    }
     const float b = wave_sum(hdh);
     if (l == 0) s.ph[w] = b;
   }
@@ -1081,10 +1129,9 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       for (int ww = 0; ww < 8; ++ww) extra += s.GamC * s.ph[ww];
       dgm += extra;
     }
-    const float* pe = reinterpret_cast<const float*>(s.slot[ST]);
     float e = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) e += pe[ww * CH + r];
+    for (int ww = 0; ww < RevWaves<DV>::NW; ++ww) e += epv[ww];
     // dg_r = sum_{r' >= r} dgam_r' (suffix scan = prefix scan over reversed
     // lanes) + sum_{i < r} e_i (exclusive prefix scan)
     const float rev = __shfl(dgm, CH - 1 - r, 64);

@@ -495,6 +495,46 @@ __device__ __forceinline__ void st_fragC_q<float>(float* base, int ld, int k0, i
   *reinterpret_cast<f32x4*>(p + 16 * ld) = quad_transpose(f.hi);
 }
 
+// x - bf16(x), elementwise: what rounding x to bf16 drops (x = hi + residual,
+// the residual itself rounded to bf16 when stored).
+__device__ __forceinline__ f32x4 bf16_residual(const f32x4& x) {
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = x[i] - (float)(bf16)x[i];
+  return r;
+}
+
+// The C-layout piece (rows r0+4g .. r0+4g+3 of column lane%16) of a row-major
+// E matrix with 16 columns, read as one 4-column row piece per lane and
+// quad-transposed: load() issues the read, get() returns the values as fp32.
+// All 64 lanes must take part in get().
+template <class E> struct CPiece;
+template <> struct CPiece<bf16> {
+  uint32_t x0, x1;
+  __device__ __forceinline__ void load(const bf16* blk, int r0) {
+    const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+    typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+    const u32x2 v = *reinterpret_cast<const u32x2*>(blk + (r0 + 4 * g + b) * 16 + 4 * q);
+    x0 = v[0];
+    x1 = v[1];
+  }
+  __device__ __forceinline__ f32x4 get() {
+    uint32_t a = x0, c = x1;
+    quad_transpose16(a, c);
+    const float v0 = __builtin_bit_cast(float, a << 16), v1 = __builtin_bit_cast(float, a & 0xFFFF0000u);
+    const float v2 = __builtin_bit_cast(float, c << 16), v3 = __builtin_bit_cast(float, c & 0xFFFF0000u);
+    return f32x4{v0, v1, v2, v3};
+  }
+};
+template <> struct CPiece<float> {
+  f32x4 v;
+  __device__ __forceinline__ void load(const float* blk, int r0) {
+    const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
+    v = *reinterpret_cast<const f32x4*>(blk + (r0 + 4 * g + b) * 16 + 4 * q);
+  }
+  __device__ __forceinline__ f32x4 get() const { return quad_transpose(v); }
+};
+
 // Four fp32 values of a C-layout column piece -> E, quad-transposed into a row
 // piece and stored (4 consecutive columns of row `row`).
 template <class E>

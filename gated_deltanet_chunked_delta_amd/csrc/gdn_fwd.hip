@@ -1,8 +1,9 @@
 // gdn_fwd.hip -- forward chunk loop of the gated delta rule on gfx950.
 //
-// One workgroup (4 waves, one per SIMD) owns one (segment, head): a run of
-// consecutive 64-token chunks of one sequence.  Wave w keeps columns
-// [w Dv/4, (w+1) Dv/4) of the fp32 state h = S^T (Dk x Dv) in accumulator
+// One workgroup owns one (segment, head): a run of consecutive 64-token chunks
+// of one sequence.  It has Dv/16 waves when Dv = 128 (eight, two per SIMD) and
+// four otherwise; wave w keeps the 16-column slices [16 w NTW, 16 (w+1) NTW)
+// (NTW = Dv / (16 waves)) of the fp32 state h = S^T (Dk x Dv) in accumulator
 // registers for the whole run, so
 // the serial chain U = Ut - W h, h' = Gam_C h + Kt^T U never leaves registers.
 // Everything that does not depend on h (decay cumsum, the decay-masked K K^T,
@@ -246,7 +247,7 @@ struct Chunk {
   template <bool LEAD>
   __device__ static void step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows, int64_t ntok0,
                               int nrows, int h, E* hs_chunk, const float* t_in, const float* nrec, E* us_chunk,
-                              f32x4 (&hacc)[DK / 16][NTW]) {
+                              E* ulo_chunk, f32x4 (&hacc)[DK / 16][NTW]) {
     constexpr bool OUTC = OUT && !LEAD, USAVEC = USAVE && !LEAD;
     constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA, LO = S::LO;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
@@ -365,11 +366,17 @@ struct Chunk {
     // U out as DV/16 column blocks of [CH][16], each contiguous (a wave's
     // stores fill whole lines; rows past the end are zero: beta = 0 there);
     // the forward proper writes the rounded operand fragments it forms anyway
+    // (bf16: and the residual of that rounding, for the backward's decay
+    // gradient, whose row terms u_r . (dS' k_r) can cancel far below their parts)
+    constexpr bool ULO = USAVE && std::is_same<E, bf16>::value;
     if (USAVEC && !OUT) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) st_tile_rows<E>(us_chunk + (n0 + 16 * nt) * CH, 16, 16 * rt, 0, u[rt][nt]);
+        for (int nt = 0; nt < NTW; ++nt) {
+          st_tile_rows<E>(us_chunk + (n0 + 16 * nt) * CH, 16, 16 * rt, 0, u[rt][nt]);
+          if constexpr (ULO) st_tile_rows<E>(ulo_chunk + (n0 + 16 * nt) * CH, 16, 16 * rt, 0, bf16_residual(u[rt][nt]));
+        }
     }
     if (OUTC) {
 #pragma unroll
@@ -380,6 +387,14 @@ struct Chunk {
         if (USAVEC) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) st_fragC_q<E>(us_chunk + (n0 + 16 * nt) * CH, 16, 32 * kb, 0, uf[kb]);
+          if constexpr (ULO) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              Frag<E> lf;
+              pack_frag(lf, bf16_residual(u[2 * kb][nt]), bf16_residual(u[2 * kb + 1][nt]));
+              st_fragC_q<E>(ulo_chunk + (n0 + 16 * nt) * CH, 16, 32 * kb, 0, lf);
+            }
+          }
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -459,11 +474,13 @@ struct Chunk {
       const float* tin = p.t_in + ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
       const float* nrec = more ? p.rec + ((chunk0 + c + 1) * p.H + h) * RECF : nullptr;
       if constexpr (decltype(lead)::value) {
-        step<true>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, nullptr, tin, nrec, nullptr, hacc);
+        step<true>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, nullptr, tin, nrec, nullptr, nullptr, hacc);
       } else {
         E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
-        E* usc = USAVE ? static_cast<E*>(p.us) + ((chunk0 + c) * p.H + h) * (size_t)(CH * DV) : nullptr;
-        step<false>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, nrec, usc, hacc);
+        const size_t uoff = ((chunk0 + c) * p.H + h) * (size_t)(CH * DV);
+        E* usc = USAVE ? static_cast<E*>(p.us) + uoff : nullptr;
+        E* ulc = USAVE && p.ulo ? static_cast<E*>(p.ulo) + uoff : nullptr;
+        step<false>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, nrec, usc, ulc, hacc);
       }
     };
     for (int c = wb; c < cb; ++c) chunk(std::true_type{}, c);
@@ -519,6 +536,7 @@ template <class E, int DK, int DV, bool OUT, bool PREP, bool USAVE>
 __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_seg(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
   const SegDesc sd = p.segs[blockIdx.x];
+  if (sd.n < 0) return;  // the plan found the device cu_seqlens inconsistent
   const int h = blockIdx.y, n = sd.n;
   const int nseg = p.seg_first[n + 1] - p.seg_first[n];
   const int64_t seq0 = p.seq.start(n), chunk0 = p.chunk_first[n];
@@ -545,6 +563,8 @@ hipError_t launch_fwd_t(const FwdParams& p, int nseg_total, hipStream_t st) {
   if (!p.t_in || !p.rec) return hipErrorInvalidValue;
   if (!out && !p.us) return hipErrorInvalidValue;
   const bool us = p.us != nullptr;
+  // in bf16, U's rounding residual is stored with U
+  if (std::is_same<E, bf16>::value && us && !p.ulo) return hipErrorInvalidValue;
   if (prep) {
     if (out && us) hipLaunchKernelGGL((gdn_fwd_seg<E, DK, DV, true, true, true>), grid, block, 0, st, p);
     else if (out) hipLaunchKernelGGL((gdn_fwd_seg<E, DK, DV, true, true, false>), grid, block, 0, st, p);

@@ -34,6 +34,7 @@ struct FwdParams {
   const int* chunk_first;  // [N+1]
   void* hs;                // nullable: [total chunks][H] chunk start states S, Dv x Dk in st_blk order (dtype)
   void* us;                // nullable: [total chunks][H][DV/16][CH][16] U = Ut - W h of each chunk in 16-column blocks (dtype)
+  void* ulo;               // nullable (bf16 only, with us): U - bf16(U) rounded to bf16, laid out as us
   // [total chunks][H][CH][CH] fp32 row-major T = (I + diag(beta) A)^-1 of each chunk
   const float* t_in;
   const float* rec;        // [total chunks][H][RECF] scalar records
@@ -49,6 +50,10 @@ struct FwdParams {
 // beta = 0).  Lambda_c = sum_r [g_r + log max(1, |1 - beta_r |k_r|^2|)] is the
 // chunk's log-bound on the norm of its state transition.
 constexpr int RECF = 5 * CH + 4;
+
+// Slots per chunk and head of the partial row terms e_r (RevParams::ep): one
+// per wave of the reverse chain (at most eight).
+constexpr int EPW = 8;
 
 // Every chunk's T = (I + diag(beta) strict_lower(K K^T * D))^-1, chunk-parallel.
 struct TSolveParams {
@@ -81,6 +86,14 @@ struct RevParams {
   void* dhs;               // [total chunks][H] gradient at each chunk END, S-shaped, st_blk order (dtype)
   const float* t_in;       // chunk matrices T (as FwdParams)
   const float* rec;        // scalar records (as FwdParams)
+  // Each chunk's U (us, and for bf16 its rounding residual ulo; layout as
+  // FwdParams) and, written here, the row terms
+  //   e_r = exp(gam_last - gam_r) u_r . (dS' k_r)
+  // of the decay gradient, per wave of this kernel: ep[chunk][H][EPW][CH], the
+  // partial sums over each wave's value columns (the gradient kernel adds them)
+  const void* us;
+  const void* ulo;
+  float* ep;
   PrepParams prep;
 };
 
@@ -96,6 +109,7 @@ struct GradParams {
   const void* dhs;         // chunk end state gradients
   const void* us;          // each chunk's U = Ut - W h ([total chunks][H][DV/16][CH][16] column blocks, dtype)
   const float* t_in;       // chunk matrices T (as FwdParams)
+  const float* ep;         // per-wave partial row terms e_r of the reverse chain (RevParams)
   void* dq;
   void* dk;
   void* dv;
@@ -124,8 +138,8 @@ struct DecodeParams {
   PrepParams prep;
 };
 
-hipError_t launch_plan(SeqInfo seq, int N, int segc, int* chunk_first, int* seg_first, SegDesc* segs,
-                       int2* chunk_tab, hipStream_t st);
+hipError_t launch_plan(SeqInfo seq, int N, int segc, int total_tokens, int nchunk_cap, int nseg_cap,
+                       int* chunk_first, int* seg_first, SegDesc* segs, int2* chunk_tab, hipStream_t st);
 hipError_t launch_tsolve(int dtype, int DK, const TSolveParams& p, int nchunk_total, hipStream_t st);
 hipError_t launch_fwd(int dtype, int DK, int DV, const FwdParams& p, int nseg_total, hipStream_t st);
 hipError_t launch_rev(int dtype, int DK, int DV, const RevParams& p, int nseg_total, hipStream_t st);

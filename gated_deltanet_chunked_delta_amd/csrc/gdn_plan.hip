@@ -30,11 +30,33 @@ __device__ __forceinline__ int wave_incl_scan_i(int x) {
   return x;
 }
 
-__global__ __launch_bounds__(PLAN_NT) void gdn_plan_kernel(SeqInfo seq, int N, int segc, int* chunk_first,
+// The host sized the workspace and the grids from its copy of cu_seqlens
+// (nchunk_cap chunks, nseg_cap segments).  If the device copy disagrees in a way
+// that would change those totals or reach past the packed tokens (cu[0] != 0,
+// cu[N] != total_tokens, a negative length), every table entry is marked
+// invalid (sequence index -1) and the kernels that read the tables write
+// nothing; no table is written past its capacity either way.
+__device__ void mark_invalid(int nchunk_cap, int nseg_cap, SegDesc* segs, int2* chunk_tab) {
+  for (int j = threadIdx.x; j < nseg_cap; j += PLAN_NT) segs[j] = SegDesc{-1, 0, 0, 0};
+  for (int c = threadIdx.x; c < nchunk_cap; c += PLAN_NT) chunk_tab[c] = make_int2(-1, 0);
+}
+
+__global__ __launch_bounds__(PLAN_NT) void gdn_plan_kernel(SeqInfo seq, int N, int segc, int total_tokens,
+                                                          int nchunk_cap, int nseg_cap, int* chunk_first,
                                                           int* seg_first, SegDesc* segs, int2* chunk_tab) {
   __shared__ int sc[PLAN_NT], ss[PLAN_NT];
-  __shared__ int carry_c, carry_s;
+  __shared__ int carry_c, carry_s, bad;
   const int tid = threadIdx.x;
+  if (tid == 0) bad = seq.cu && (seq.cu[0] != 0 || seq.cu[N] != total_tokens);
+  __syncthreads();
+  if (seq.cu)
+    for (int n = tid; n < N; n += PLAN_NT)
+      if (seq.len(n) < 0) bad = 1;
+  __syncthreads();
+  if (bad) {
+    mark_invalid(nchunk_cap, nseg_cap, segs, chunk_tab);
+    return;
+  }
   if (N <= PLAN_SMALL) {
     // sc[n] / ss[n]: first chunk / segment of sequence n, n <= N
     if (tid < 64) {
@@ -59,6 +81,10 @@ __global__ __launch_bounds__(PLAN_NT) void gdn_plan_kernel(SeqInfo seq, int N, i
     }
     __syncthreads();
     const int total_s = ss[N], total_c = sc[N];
+    if (total_s != nseg_cap || total_c != nchunk_cap) {
+      mark_invalid(nchunk_cap, nseg_cap, segs, chunk_tab);
+      return;
+    }
     for (int j = tid; j < total_s; j += PLAN_NT) {
       int n = 0, hi = N - 1;
       while (n < hi) {
@@ -125,6 +151,10 @@ __global__ __launch_bounds__(PLAN_NT) void gdn_plan_kernel(SeqInfo seq, int N, i
   __syncthreads();
   __threadfence();
   const int total_s = carry_s, total_c = carry_c;
+  if (total_s != nseg_cap || total_c != nchunk_cap) {
+    mark_invalid(nchunk_cap, nseg_cap, segs, chunk_tab);
+    return;
+  }
   // fill the tables: locate the owning sequence by binary search over the prefixes
   for (int j = tid; j < total_s; j += PLAN_NT) {
     int lo = 0, hi = N - 1;
@@ -154,10 +184,10 @@ __global__ __launch_bounds__(PLAN_NT) void gdn_plan_kernel(SeqInfo seq, int N, i
   }
 }
 
-hipError_t launch_plan(SeqInfo seq, int N, int segc, int* chunk_first, int* seg_first, SegDesc* segs,
-                       int2* chunk_tab, hipStream_t st) {
-  hipLaunchKernelGGL(gdn_plan_kernel, dim3(1), dim3(PLAN_NT), 0, st, seq, N, segc, chunk_first, seg_first,
-                     segs, chunk_tab);
+hipError_t launch_plan(SeqInfo seq, int N, int segc, int total_tokens, int nchunk_cap, int nseg_cap,
+                       int* chunk_first, int* seg_first, SegDesc* segs, int2* chunk_tab, hipStream_t st) {
+  hipLaunchKernelGGL(gdn_plan_kernel, dim3(1), dim3(PLAN_NT), 0, st, seq, N, segc, total_tokens, nchunk_cap,
+                     nseg_cap, chunk_first, seg_first, segs, chunk_tab);
   return hipGetLastError();
 }
 

@@ -16,8 +16,10 @@
  * segments that run side by side on one GPU; the exponential decay of the
  * gates bounds how far a segment boundary's state must be propagated
  * ("FlashQLA resource", section 3, gate-driven intra-card context parallelism;
- * section 5 for the backward pass).  The result does not depend on the split
- * beyond fp32 rounding.
+ * section 5 for the backward pass).  The split changes the result by at most
+ * 2^-24 of the norm of the state (or state gradient) at a segment boundary
+ * carried across it, so a split and an unsplit run differ at fp32 round-off
+ * level (the tests hold them to 1e-5 relative, elementwise).
  *
  * Layouts (row-major, last dimension contiguous, all pointers device memory
  * unless stated otherwise; every tensor pointer 16-byte aligned):
@@ -59,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 8
+#define GDN_ABI_VERSION 9
 
 typedef enum {
   GDN_OK = 0,
@@ -83,7 +85,14 @@ typedef struct {
   const float* h0;             /* nullable: zero initial state */
   float scale;                 /* output scale; the usual choice is Dk^-0.5 */
   const int32_t* cu_seqlens;   /* nullable device pointer [N+1] */
-  const int32_t* cu_seqlens_host; /* host copy of the same [N+1]; required with cu_seqlens */
+  const int32_t* cu_seqlens_host; /* host copy of the same [N+1]; required with cu_seqlens.  The
+                                  host copy sizes the work and the workspace; the kernels read
+                                  the device copy.  If the device copy starts at a nonzero
+                                  value, ends at a value other than T, has a negative length or
+                                  gives other chunk or segment totals than the host copy, the
+                                  call writes no output (o, hT and the gradients are left as
+                                  they were) and reads nothing past its buffers; the status is
+                                  still GDN_OK, since nothing is checked on the host side. */
   int32_t num_seqs;            /* N: len(cu_seqlens) - 1, or B when cu_seqlens is NULL */
   int32_t cp_mode;             /* intra-card sequence splitting: 0 = automatic,
                                   -1 = off (one segment per sequence and head),
@@ -140,8 +149,9 @@ size_t gdn_chunk_fwd_workspace_size(const gdn_fwd_args* args);
 size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args);
 
 /* Bytes of the saved chunk states (h_save / h_saved) for these arguments:
- * C * H * (Dk * Dv + 64 * Dv) elements of the input dtype, C = sum over
- * sequences of ceil(len / 64).  The first C * H * Dk * Dv elements are the
+ * C * H * (Dk * Dv + 64 * Dv) elements of the input dtype (bf16: C * H *
+ * (Dk * Dv + 2 * 64 * Dv)), C = sum over sequences of ceil(len / 64).  The
+ * first C * H * Dk * Dv elements are the
  * states: state (c, h) is S (= h^T, Dv x Dk) at the start of chunk c (chunks
  * numbered sequence after sequence), rounded to the dtype, stored at element
  * offset (c * H + h) * Dk * Dv in 4 x 16 blocks: S[j][i] sits at
@@ -154,6 +164,9 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args);
  * gdn_chunk_t_bytes; rows past a sequence's end are zero), stored as Dv / 16
  * column blocks of 64 x 16, each row-major and contiguous: U[r][j] sits at
  *     (j / 16) * 1024 + r * 16 + j % 16.
+ * For bf16 a third part follows, at element offset C * H * (Dk * Dv + 64 * Dv),
+ * laid out like U: bf16(U - bf16(U)), the residual of U's rounding (the
+ * backward's decay gradient takes U to about 16 bits).
  * Returns 0 and sets the error string for invalid arguments (and returns 0
  * without error when there are no tokens). */
 size_t gdn_chunk_states_bytes(const gdn_common_args* a);

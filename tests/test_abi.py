@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(L):
             "gdn_chunk_bwd_workspace_size", "gdn_last_error", "gdn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdn_abi_version() == 8
+    assert L.gdn_abi_version() == 9
 
 
 FAKE = 1 << 20  # a 16-byte aligned fake device address; never dereferenced
@@ -98,7 +98,7 @@ def test_backward_rejects_missing_gradients(L):
 def test_states_bytes(L):
     import numpy as np
     f = fwd_args()                                        # B=1, T=128, H=2, 128 x 128, bf16
-    per = (128 * 128 + 64 * 128) * 2                      # state + U per chunk and head
+    per = (128 * 128 + 2 * 64 * 128) * 2                  # state + U + U's bf16 residual per chunk and head
     assert L.gdn_chunk_states_bytes(ctypes.byref(f.a)) == 2 * 2 * per
     host = np.array([0, 1, 64, 65, 128], dtype=np.int32)  # lengths 1, 63, 1, 63: one chunk each
     f = fwd_args(cu_seqlens=FAKE, cu_seqlens_host=host.ctypes.data, num_seqs=4)

@@ -54,11 +54,11 @@ def test_decay_underflow(dev, dtype):
     """g = -30 per token: exp of the in-chunk cumsum underflows to zero within
     a few tokens; only differences of cumsums may enter the products.  dg is
     then about 1e-13 of the terms it is formed from (T = 300 ends in a partial
-    chunk, where the terms that cancel exactly are kept apart).  In bf16 its
-    largest entry comes from a single dot product over the bf16-stored U and
-    dh' of the chunk, whose sum is about a hundredth of its terms, so dg is
-    held to 5e-2 there; every other tensor, and fp32 throughout, to the usual
-    bound."""
+    chunk, where the terms that cancel exactly are kept apart), and its largest
+    entry comes from a single row term u_r . (dS' k_r) whose sum is about a
+    hundredth of its parts: with U and the chunk-end gradient dS' rounded to
+    bf16 that entry misses the bound (2.5e-2), so the kernels carry both to
+    about 16 bits there.  Every tensor is held to the usual bound."""
     from oracle import ref
     from tests.test_gpu_backward import NAMES, run_bwd
     from tests.helpers import TOL
@@ -71,10 +71,7 @@ def test_decay_underflow(dev, dtype):
         got = run_bwd(x, dev, cp)
         errs = {k: relerr(got[k], want[k]) for k in NAMES}
         print("    " + "  ".join(f"{k} {e:.3e}" for k, e in errs.items()), flush=True)
-        tol = {k: TOL[dtype] for k in NAMES}
-        if dtype == "bf16":
-            tol["dg"] = 5e-2
-        bad = {k: e for k, e in errs.items() if not e <= tol[k]}
+        bad = {k: e for k, e in errs.items() if not e <= TOL[dtype]}
         assert not bad, (cp, bad)
 
 
