@@ -79,6 +79,8 @@ def lib():
         L.gdn_chunk_fwd.restype = ctypes.c_int
         L.gdn_chunk_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
         L.gdn_chunk_bwd.restype = ctypes.c_int
+        L.gdn_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(FwdArgs), _vp]
+        L.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
         L.gdn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         L.gdn_decode_step.restype = ctypes.c_int
         L.gdn_profile_enable.argtypes = [ctypes.c_int]
@@ -178,13 +180,14 @@ def _stream(dev):
 def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_seqlens_host=None,
                   output_final_state: bool = True, cp_mode: int = 0, save_states: bool = False,
                   save_t: bool = False, qk_norm: bool = False, gate_act: bool = False, gate_scale=None,
-                  o=None, hT=None):
+                  o=None, hT=None, noalloc: bool = False):
     """Forward pass.  Returns (o, hT) with hT None unless output_final_state, followed by
     states if save_states (the state at every chunk start, a flat tensor of the input
     dtype) and chunk_t if save_t (every chunk's matrix T, a flat fp32 tensor); both are
     for gdn_chunk_bwd.  qk_norm / gate_act select the in-kernel pre-processing (raw q,
     k; gate and beta logits, see include/gdn.h).  o / hT: optional output tensors
-    to write into (else allocated)."""
+    to write into (else allocated).  noalloc: call gdn_chunk_fwd_noalloc, which
+    takes no workspace (the library's own scratch; see include/gdn.h)."""
     a, keep = _common(q, k, v, g, beta, scale, h0, cu_seqlens, cu_seqlens_host, cp_mode,
                       qk_norm, gate_act, gate_scale)
     L = lib()
@@ -210,6 +213,10 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_s
     args = FwdArgs()
     args.a = a
     args.o, args.hT, args.h_save, args.t_save = _ptr(o), _ptr(hT), _ptr(states), _ptr(chunk_t)
+    if noalloc:
+        _check(L.gdn_chunk_fwd_noalloc(ctypes.byref(args), _vp(_stream(q.device))))
+        del keep
+        return (o, hT) + ((states,) if save_states else ()) + ((chunk_t,) if save_t else ())
     nbytes = L.gdn_chunk_fwd_workspace_size(ctypes.byref(args))
     if nbytes == 0:
         _check(1)

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -193,10 +194,14 @@ hipEvent_t prof_event() {
   return e;
 }
 
+// Set while an allocation-free call runs on this thread: no timing events are
+// created for it.
+thread_local bool t_noalloc = false;
+
 // Launch through f() on stream s, bracketed by events when timing is enabled.
 template <class F>
 hipError_t timed(const char* name, hipStream_t s, F f) {
-  if (!g_prof) return f();
+  if (!g_prof || t_noalloc) return f();
   ProfRec r{name, prof_event(), prof_event()};
   const bool ok_a = r.a && hipEventRecord(r.a, s) == hipSuccess;
   hipError_t e = f();
@@ -311,7 +316,12 @@ size_t gdn_chunk_t_bytes(const gdn_common_args* a) {
   return (size_t)count_chunks(*a) * a->H * (CHUNK * CHUNK + gdn::RECF) * sizeof(float);
 }
 
-gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of the forward's own arguments (beyond check_common).
+gdn_status check_fwd(const gdn_fwd_args* args) {
   if (!args) return fail(GDN_E_INVALID, "null args");
   const gdn_common_args& a = args->a;
   gdn_status st = check_common(a);
@@ -321,12 +331,13 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   if (!aligned(args->hT, 4)) return fail(GDN_E_INVALID, "hT misaligned");
   if (!aligned(args->h_save, 16)) return fail(GDN_E_INVALID, "h_save must be 16-byte aligned");
   if (!aligned(args->t_save, 16)) return fail(GDN_E_INVALID, "t_save must be 16-byte aligned");
-  const Plan pl = make_plan(a, false, cu_count(), false, args->t_save != nullptr);
-  if (!a.workspace || a.workspace_bytes < pl.total)
-    return fail(GDN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total,
-                a.workspace ? a.workspace_bytes : (size_t)0);
+  return GDN_OK;
+}
+
+// The forward's launches with workspace ws (at least pl.total bytes).
+gdn_status fwd_launch(const gdn_fwd_args* args, const Plan& pl, void* ws, void* stream) {
+  const gdn_common_args& a = args->a;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  void* ws = a.workspace;
   gdn::SeqInfo sq = seq_info(a);
   hipError_t e = timed("plan", s, [&] {
     return gdn::launch_plan(sq, pl.N, pl.segc, a.T, pl.nchunk, pl.nseg, at<int>(ws, pl.o_chunk_first),
@@ -361,6 +372,65 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
   e = timed("fwd", s, [&] { return gdn::launch_fwd(a.dtype, a.Dk, a.Dv, p, pl.nseg, s); });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return GDN_OK;
+}
+
+// Scratch of the allocation-free forward: one copy per device, held from the
+// library's load until the process ends.  Host code never passes this name to
+// a kernel or a copy (on the host it is only a stand-in for the symbol); it
+// uses the device address hipGetSymbolAddress returns for the current device.
+constexpr size_t NOALLOC_SCRATCH = (size_t)GDN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH];
+
+// The scratch's device address on the current device, looked up once per
+// device (under a lock: concurrent first calls from several threads).
+gdn_status scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* cache[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(GDN_E_UNSUPPORTED, "device index %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    cache[dev] = ptr;
+  }
+  *out = cache[dev];
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream) {
+  gdn_status st = check_fwd(args);
+  if (st != GDN_OK) return st;
+  const gdn_common_args& a = args->a;
+  const Plan pl = make_plan(a, false, cu_count(), false, args->t_save != nullptr);
+  if (!a.workspace || a.workspace_bytes < pl.total)
+    return fail(GDN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.total,
+                a.workspace ? a.workspace_bytes : (size_t)0);
+  return fwd_launch(args, pl, a.workspace, stream);
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const gdn_fwd_args* args, void* stream) {
+  gdn_status st = check_fwd(args);
+  if (st != GDN_OK) return st;
+  const Plan pl = make_plan(args->a, false, cu_count(), false, args->t_save != nullptr);
+  if (pl.total > NOALLOC_SCRATCH)
+    return fail(GDN_E_WORKSPACE,
+                "gdn_chunk_fwd_noalloc: these arguments need %zu bytes of scratch, more than its %zu "
+                "(pass t_save, or use gdn_chunk_fwd with a workspace)", pl.total, NOALLOC_SCRATCH);
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != GDN_OK) return st;
+  t_noalloc = true;
+  st = fwd_launch(args, pl, ws, stream);
+  t_noalloc = false;
+  return st;
 }
 
 gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {

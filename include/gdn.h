@@ -193,6 +193,31 @@ size_t gdn_chunk_t_bytes(const gdn_common_args* a);
  * stream is a hipStream_t (NULL = default stream). */
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream);
 
+/* Bytes of the scratch array gdn_chunk_fwd_noalloc uses in place of a workspace. */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* gdn_chunk_fwd without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments and results as gdn_chunk_fwd, except that
+ * a.workspace / a.workspace_bytes are ignored: the work tables (and, when
+ * t_save is NULL, every chunk's T and scalar record) go to a scratch array
+ * of GDN_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on each device
+ * it runs on, from its load until the process ends.  Arguments whose
+ * gdn_chunk_fwd_workspace_size exceeds that size are rejected with
+ * GDN_E_WORKSPACE before anything is enqueued (without t_save that is about
+ * 3,700 chunk-heads, e.g. 16 heads of 15,000 tokens; with t_save the tables
+ * alone, a few bytes per chunk).  The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine, and no timing events
+ * (gdn_profile_enable does not apply to it).  Every call on one device shares
+ * that device's scratch, which keeps the last call's contents (the forward
+ * reads nothing it has not written in the same call): calls that overlap on
+ * one device -- on different streams, or from several threads without
+ * ordering -- race and give undefined results; order them on one stream.
+ * The first call on a device looks the scratch address up (not under graph
+ * capture on that device, which forbids that query in some runtimes: make one
+ * call outside capture first). */
+gdn_status gdn_chunk_fwd_noalloc(const gdn_fwd_args* args, void* stream);
+
 /* Backward: gradients of <do, o> + <dhT, hT> with respect to q, k, v, beta, g
  * and (optionally) h0.  It recomputes the forward states from the inputs
  * unless h_saved provides them, and solves for each chunk's T once unless

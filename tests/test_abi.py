@@ -190,3 +190,18 @@ def test_state_block_layout_is_a_permutation():
         flat = np.empty(Dk * Dv)
         flat[off] = S
         assert np.array_equal(unblock_states(flat, 1, 1, Dk, Dv)[0, 0], S.T)
+
+
+def test_noalloc_rejects_oversize_before_any_device_call(L):
+    """gdn_chunk_fwd_noalloc refuses arguments whose workspace exceeds its
+    scratch (GDN_NOALLOC_SCRATCH_BYTES) with GDN_E_WORKSPACE, and invalid ones
+    like gdn_chunk_fwd, before touching a device (this runs with none)."""
+    big = fwd_args(T=64 * 4096, H=16)                      # 65,536 chunk-heads: T alone needs 1.1 GiB
+    big.a.workspace = None
+    big.a.workspace_bytes = 0
+    assert L.gdn_chunk_fwd_workspace_size(ctypes.byref(big)) > (64 << 20)
+    assert L.gdn_chunk_fwd_noalloc(ctypes.byref(big), None) == 3
+    assert b"scratch" in L.gdn_last_error()
+    bad = fwd_args(Dk=96)
+    assert L.gdn_chunk_fwd_noalloc(ctypes.byref(bad), None) == 2
+    assert L.gdn_chunk_fwd_noalloc(None, None) == 1
