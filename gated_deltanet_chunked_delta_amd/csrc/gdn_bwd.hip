@@ -55,15 +55,14 @@ struct alignas(16) RevSmem {
   static constexpr int LA = CH + 4;
   E Q[CH * LQ];    // row-major, X of Q K^T
   E K[CH * LQ];    // row-major, X/Y of K K^T, X of K dh'
-  E KT[DK * LT];   // K^T, X of W^T
-  E QT[DK * LT];   // Q^T, X of (Gam Q)^T dO
+  E KT[DK * LT];   // K^T diag(beta Gam), X of W^T
+  E QT[DK * LT];   // Q^T diag(scale Gam) (zero past the sequence end), X of (Gam Q)^T dO
   E DOT[DV * LT];  // dO^T, Y of P^T dO and (Gam Q)^T dO
   E WT[DK * LT];   // -W^T
   E PT[CH * LT];   // scale * P^T
   float T[CH * LA];
   // the chunk's scalar record, as laid out in memory (tail: Lambda_c, Gam_C)
   alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], tail[4];
-  alignas(16) float sGam[CH];  // scale Gam, zero past the sequence end
 };
 
 // Waves per workgroup of the reverse chain: 8 when the state gradient has 128
@@ -86,6 +85,9 @@ struct RevChunk {
     TilePart<E, KQT, DK> kq;
     TilePart<E, NT, DV> d;
     RecordPart rec;
+    // the row scales of the transposed K (beta Gam) and Q (scale Gam, zero past
+    // the sequence end) copies, one per kq block
+    f32x4 sc[TilePart<E, KQT, DK>::NB > 0 ? TilePart<E, KQT, DK>::NB : 1];
   };
   __device__ __forceinline__ static bool q_half() { return threadIdx.x >= KQT; }
   __device__ __forceinline__ static int kq_tid() { return threadIdx.x & (KQT - 1); }
@@ -96,6 +98,17 @@ struct RevChunk {
     ld.kq.load(static_cast<const E*>(src) + (tok0 * H + h) * DK, (int64_t)H * DK, rows, kq_tid());
     ld.d.load(static_cast<const E*>(p.dout) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
     ld.rec.load(rec);
+    constexpr int NBK = TilePart<E, KQT, DK>::NB;
+    const bool qh = q_half();
+#pragma unroll
+    for (int b = 0; b < NBK; ++b) {
+      const int r0 = TilePart<E, KQT, DK>::block_row(b, kq_tid());
+      if (r0 >= 0) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(rec + (qh ? CH : 4 * CH) + r0);  // Gam or beta Gam
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ld.sc[b][i] = qh ? (r0 + i < rows ? p.scale * v[i] : 0.f) : v[i];
+      }
+    }
   }
 
   // One lower 16x16 tile (rt, ct) of scale P^T, P = (Q K^T) * M, with the rows
@@ -166,19 +179,11 @@ struct RevChunk {
     if (PREP && p.prep.qk_norm) ld.kq.normalize_rows(kq_tid());
     {
       const bool qh = q_half();
-      ld.kq.store(qh ? s1.Q : s1.K, LQ, qh ? s1.QT : s1.KT, LT, kq_tid());
+      ld.kq.store_scaledT(qh ? s1.Q : s1.K, LQ, qh ? s1.QT : s1.KT, LT, ld.sc, kq_tid());
     }
     ld.d.store(nullptr, 0, s1.DOT, LT);
     static_assert(offsetof(S, tail) == offsetof(S, gam) + 5 * CH * sizeof(float), "record layout");
     ld.rec.store(s1.gam);
-    if (tid >= CH / 4 && tid < CH / 2) {
-      // the threads that hold Gam form scale Gam, zero past the sequence end
-      const int r0 = 4 * tid - CH;
-      f32x4 sg;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sg[i] = r0 + i < rows ? p.scale * ld.rec.rv[i] : 0.f;
-      *reinterpret_cast<f32x4*>(&s1.sGam[r0]) = sg;
-    }
     __syncthreads();
 
     // ---- 2. Q K^T -> scale P^T: the ten lower 16x16 tiles, tile j on wave j % NW
@@ -228,7 +233,7 @@ struct RevChunk {
         const int dt = kt0 + dd;
         Frag<E> xk[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) xk[kb] = ld_frag_kscaled<E>(s.KT, LT, 16 * dt + c16, 32 * kb, s.bg);
+        for (int kb = 0; kb < 2; ++kb) xk[kb] = ld_frag(s.KT, LT, 16 * dt + c16, 32 * kb);
 #pragma unroll
         for (int rr = 0; rr < RTW; ++rr) {
           f32x4 acc = zero4();
@@ -308,7 +313,7 @@ struct RevChunk {
           dh[t][nt] = dh[t][nt] * gc;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            mma(dh[t][nt], ld_frag_kscaled<E>(s.QT, LT, 16 * t + c16, 32 * kb, s.sGam), yd[nt][kb]);
+            mma(dh[t][nt], ld_frag(s.QT, LT, 16 * t + c16, 32 * kb), yd[nt][kb]);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) mma(dh[t][nt], ld_frag(s.WT, LT, 16 * t + c16, 32 * kb), uf[kb]);
         }

@@ -114,22 +114,6 @@ __device__ __forceinline__ Frag<float> ld_frag8(const float* base, int ld, int r
   return f;
 }
 
-// Fragment of row `row` of an fp32 row-major LDS matrix, each k-slot multiplied
-// by kscale[k] (a diagonal matrix applied on the right), converted to E.
-template <class E>
-__device__ __forceinline__ Frag<E> ld_frag_scaled(const float* base, int ld, int row, int k0,
-                                                  const float* kscale) {
-  const int g = lane_id() >> 4;
-  const float* p = base + row * ld + k0 + 4 * g;
-  f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  f32x4 b = *reinterpret_cast<const f32x4*>(p + 16);
-  f32x4 sa = *reinterpret_cast<const f32x4*>(kscale + k0 + 4 * g);
-  f32x4 sb = *reinterpret_cast<const f32x4*>(kscale + k0 + 16 + 4 * g);
-  Frag<E> f;
-  pack_frag(f, a * sa, b * sb);
-  return f;
-}
-
 // Register operand from two accumulator tiles stacked along k (t0: k0..k0+15,
 // t1: k0+16..k0+31), each slot multiplied by a per-k scale (s0 for t0's rows,
 // s1 for t1's rows).
@@ -550,23 +534,6 @@ __device__ __forceinline__ void st4_transposed<bf16>(bf16* p, const f32x4& v) {
 template <>
 __device__ __forceinline__ void st4_transposed<float>(float* p, const f32x4& v) {
   *reinterpret_cast<f32x4*>(p) = quad_transpose(v);
-}
-
-// Row fragment of a row-major E matrix with each k-slot multiplied by kscale[k].
-template <class E>
-__device__ __forceinline__ Frag<E> ld_frag_kscaled(const E* base, int ld, int row, int k0,
-                                                   const float* kscale) {
-  const int g = lane_id() >> 4;
-  const E* p = base + row * ld + k0 + 4 * g;
-  f32x4 a, b;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    a[j] = to_f(p[j]) * kscale[k0 + 4 * g + j];
-    b[j] = to_f(p[16 + j]) * kscale[k0 + 16 + 4 * g + j];
-  }
-  Frag<E> f;
-  pack_frag(f, a, b);
-  return f;
 }
 
 // acc + sum over the eight k-slots of a[j] * b[j] (bf16 pairs on the dot

@@ -49,8 +49,7 @@ namespace gdn {
 template <class E, int DK, int DV>
 struct alignas(16) FwdSmem {
   static constexpr int LQ = ldpad<E>(DK);                 // sQ, sK, sW row stride
-  static constexpr int LT = ldpad<E>(CH);                 // transposed tiles, P
-  static constexpr int LA = CH + 4;                       // fp32 64x64 matrices
+  static constexpr int LT = ldpad<E>(CH);                 // transposed tiles, P, scaled T
   static constexpr int LO = DV + 16 / (int)sizeof(E);     // output staging (16-byte rows)
   E Q[CH * LQ];
   E K[CH * LQ];
@@ -58,7 +57,8 @@ struct alignas(16) FwdSmem {
   E VT[DV * LT];
   E W[CH * LQ];   // holds -W
   E P[CH * LT];
-  float T[CH * LA];
+  E TBG[CH * LT];  // T diag(beta Gam), the X operand of W
+  E TB[CH * LT];   // T diag(beta), the X operand of Ut
   E O[CH * LO];
   // the chunk's scalar record, as laid out in memory (tail: Lambda_c, Gam_C)
   alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], tail[4];
@@ -249,7 +249,7 @@ struct Chunk {
                               int nrows, int h, E* hs_chunk, const float* t_in, const float* nrec, E* us_chunk,
                               E* ulo_chunk, f32x4 (&hacc)[DK / 16][NTW]) {
     constexpr bool OUTC = OUT && !LEAD, USAVEC = USAVE && !LEAD;
-    constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA, LO = S::LO;
+    constexpr int LQ = S::LQ, LT = S::LT, LO = S::LO;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
     const int H = p.H;
@@ -287,10 +287,14 @@ struct Chunk {
         if (pid < 10) p_tile(sp, rt, ct, g, c16);
       }
     }
+    // T lands as its two column-scaled operands (computed in fp32, rounded once)
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
-      const int e = 4 * (tid + i * NT);
-      *reinterpret_cast<f32x4*>(&sp->T[(e / CH) * LA + e % CH]) = tv[i];
+      const int e = 4 * (tid + i * NT), r = e / CH, c = e % CH;
+      const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&sp->bg[c]);
+      const f32x4 bt4 = *reinterpret_cast<const f32x4*>(&sp->beta[c]);
+      st4f<E>(&sp->TBG[r * LT + c], tv[i] * bg4);
+      st4f<E>(&sp->TB[r * LT + c], tv[i] * bt4);
     }
     __syncthreads();
     sp = lds_opaque(sp);
@@ -309,7 +313,7 @@ struct Chunk {
       const int rt = w & 3, ct0 = (w >> 2) * CTW;
       Frag<E> xw[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) xw[kb] = ld_frag_scaled<E>(sp->T, LA, 16 * rt + c16, 32 * kb, sp->bg);
+      for (int kb = 0; kb < 2; ++kb) xw[kb] = ld_frag(sp->TBG, LT, 16 * rt + c16, 32 * kb);
 #pragma unroll
       for (int cc = 0; cc < CTW; ++cc) {
         const int ct = ct0 + cc;
@@ -333,7 +337,7 @@ struct Chunk {
       for (int rt = 0; rt < 4; ++rt) {
         Frag<E> xb[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) xb[kb] = ld_frag_scaled<E>(sp->T, LA, 16 * rt + c16, 32 * kb, sp->beta);
+        for (int kb = 0; kb < 2; ++kb) xb[kb] = ld_frag(sp->TB, LT, 16 * rt + c16, 32 * kb);
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
           u[rt][nt] = zero4();
@@ -516,12 +520,11 @@ __device__ void store_state(const f32x4 (&hacc)[DK / 16][DV / (16 * FwdWaves<DV>
 template <class E, int DK, int DV>
 __device__ void init_smem(FwdSmem<E, DK, DV>& s) {
   using Sm = FwdSmem<E, DK, DV>;
-  // Upper-triangular parts of P and T are never written by the chunk loop and
-  // must read as zero.
+  // The upper-triangular part of P is never written by the chunk loop and must
+  // read as zero.
   for (int e = threadIdx.x; e < CH * CH; e += blockDim.x) {
     const int r = e >> 6, c = e & 63;
     s.P[r * Sm::LT + c] = to_e<E>(0.f);
-    s.T[r * Sm::LA + c] = 0.f;
   }
   __syncthreads();
 }

@@ -195,6 +195,32 @@ struct TilePart {
       }
     }
   }
+  // store() with the transposed copy's rows r0 .. r0 + 3 of block b scaled by
+  // sc[b][0 .. 3] (computed in fp32, rounded once); the row-major copy is as loaded.
+  __device__ __forceinline__ void store_scaledT(E* dst, int ld, E* dstT, int ldT, const f32x4 (&sc)[NB > 0 ? NB : 1],
+                                                int tid = threadIdx.x) const {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int id = tid + b * NT;
+      if (NB * NT == NBLK || id < NBLK) {
+        const int r0 = (id / BPR) * 4, c0 = (id % BPR) * VEC;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4)
+            st4<E>(dst + (r0 + j) * ld + c0 + e, blk[b][j][e], blk[b][j][e + 1], blk[b][j][e + 2], blk[b][j][e + 3]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          st4<E>(dstT + (c0 + e) * ldT + r0, to_e<E>(to_f(blk[b][0][e]) * sc[b][0]), to_e<E>(to_f(blk[b][1][e]) * sc[b][1]),
+                 to_e<E>(to_f(blk[b][2][e]) * sc[b][2]), to_e<E>(to_f(blk[b][3][e]) * sc[b][3]));
+      }
+    }
+  }
+  // First row of each of this thread's blocks (blocks past the tile: -1).
+  __device__ __forceinline__ static int block_row(int b, int tid = threadIdx.x) {
+    const int id = tid + b * NT;
+    return (NB * NT == NBLK || id < NBLK) ? (id / BPR) * 4 : -1;
+  }
   __device__ __forceinline__ void store(E* dst, int ld, E* dstT, int ldT, int tid = threadIdx.x) const {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
