@@ -167,13 +167,12 @@ struct RevChunk {
 
     // ---- 1. gradient at the chunk end out; tiles into LDS; scalars
     S* sp = lds_opaque(&s0);
-    // stored as S (Dv x Dk) in 4 x 16 blocks: the lane's four rows of one
-    // column are contiguous
+    // stored as dh' (Dk x Dv) in 4 x 16 blocks
     if constexpr (!LEAD) {
 #pragma unroll
       for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) st4f<E>(dhs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK), dh[t][nt]);
+        for (int nt = 0; nt < NTW; ++nt) st_blk_row4<E>(dhs_chunk, 16 * t + 4 * g, n0 + 16 * nt, DV, dh[t][nt]);
     }
     S& s1 = *sp;
     if (PREP && p.prep.qk_norm) ld.kq.normalize_rows(kq_tid());
@@ -575,7 +574,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   const int64_t tok0 = p.seq.start(n) + (int64_t)jc * CH;
   const int rows = min(CH, len - jc * CH);
   const size_t SS = (size_t)DK * DV;
-  // h_c and dh'_c of this chunk, both stored as S-shaped (Dv x Dk) matrices in 4 x 16 blocks (st_blk)
+  // h_c and dh'_c of this chunk, both stored as Dk x Dv matrices in 4 x 16 blocks (st_blk)
   const E* hs = static_cast<const E*>(p.hs) + ((size_t)blockIdx.x * H + h) * SS;
   const E* dhs = static_cast<const E*>(p.dhs) + ((size_t)blockIdx.x * H + h) * SS;
   const int d0 = cw * (DK / 4), n0 = cw * (DV / 4);
@@ -605,9 +604,9 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   //          zero); zero T (unless given), P and the cross-wave sum arrays.
   //          dh' down this wave's value columns (the operand of P5) is
   //          requested after the tiles have landed and stays in flight until
-  //          P5; its products use the contiguous k-slot order (one 16-byte
-  //          read per fragment).
-  Frag<E> dk_[P5C][DK / 32];
+  //          P5, where quad transposes turn its row pieces into columns; its
+  //          products use the contiguous k-slot order.
+  RawFrag<E> dkraw[P5C][DK / 32];
   {
     const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
     const E* k = static_cast<const E*>(p.k) + (tok0 * H + h) * DK;
@@ -696,7 +695,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
   for (int nt = 0; nt < P5C; ++nt)
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) dk_[nt][kb] = ld_frag8_st(dhs, DK, p5n0 + 16 * nt + c16, 32 * kb);
+    for (int kb = 0; kb < DK / 32; ++kb) dkraw[nt][kb] = raw_fragC_q8_st<E>(dhs, DV, 32 * kb, p5n0 + 16 * nt);
 
   // ---- P2: KD = strict_lower(K K^T * D), P = (Q K^T) * M  (20 lower tiles:
   //          tile w + 8j for wave w, all fragment reads issued before the products)
@@ -751,20 +750,25 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) { rg[j] = zero4(); rb[j] = zero4(); }
 
-  // h and dh' down this wave's key columns (the operands of P6): requested now,
-  // in flight during P5, quad-transposed in P6
-  RawFrag<E> hraw[CTK][DV / 32], dhraw[CTK][DV / 32];
+  // rows of h and dh' at this wave's key columns (the operands of P6):
+  // requested now, in flight during P5
+  Frag<E> hn[CTK][DV / 32], dhn[CTK][DV / 32];
 #pragma unroll
   for (int dt = 0; dt < CTK; ++dt)
 #pragma unroll
     for (int kb = 0; kb < DV / 32; ++kb) {
-      hraw[dt][kb] = raw_fragC_q8_st<E>(hs, DK, 32 * kb, d0 + 16 * dt);
-      dhraw[dt][kb] = raw_fragC_q8_st<E>(dhs, DK, 32 * kb, d0 + 16 * dt);
+      hn[dt][kb] = ld_frag8_st(hs, DV, d0 + 16 * dt + c16, 32 * kb);
+      dhn[dt][kb] = ld_frag8_st(dhs, DV, d0 + 16 * dt + c16, 32 * kb);
     }
 
   // ---- P5: dU = diag(ek) K dh' + scale P^T dO (P5 rows and value columns)
   f32x4 du[P5R][P5C];
   {
+    Frag<E> dk_[P5C][DK / 32];
+#pragma unroll
+    for (int nt = 0; nt < P5C; ++nt)
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) dk_[nt][kb] = finish_frag(dkraw[nt][kb]);
 #pragma unroll
     for (int nt = 0; nt < P5C; ++nt) {
       Frag<E> dor[2];
@@ -795,20 +799,16 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int dt = 0; dt < CTK; ++dt) qr[kb][dt] = ld_fragC_q<E>(slotE(SQ), LK, 32 * kb, d0 + 16 * dt);
-  // (the state operands come from memory on both sides of these products, so
-  //  they use the contiguous k-slot order: one 16-byte LDS read per fragment,
-  //  each loaded once and used for both key-column tiles)
+  // (the state operands are rows of the stored h and dh', so these products
+  //  use the contiguous k-slot order: one 16-byte read per fragment, each
+  //  loaded once and used for both key-column tiles)
   f32x4 gw[2][CTK], dq1[2][CTK], udh[2][CTK];
-  Frag<E> hn[CTK][DV / 32], dhn[CTK][DV / 32];
+  // <h, dh'> over the whole state: the two row halves share each column group's part
 #pragma unroll
   for (int dt = 0; dt < CTK; ++dt)
 #pragma unroll
-    for (int kb = 0; kb < DV / 32; ++kb) {
-      hn[dt][kb] = finish_frag(hraw[dt][kb]);
-      dhn[dt][kb] = finish_frag(dhraw[dt][kb]);
-      // <h, dh'> over the whole state: the two row halves share each column group's part
+    for (int kb = 0; kb < DV / 32; ++kb)
       if ((kb & 1) == rh) hdh = frag_dot(hn[dt][kb], dhn[dt][kb], hdh);
-    }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int rt = 2 * rh + j;

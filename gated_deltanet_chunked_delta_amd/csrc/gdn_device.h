@@ -328,25 +328,37 @@ __device__ __forceinline__ void quad_transpose16(uint32_t& d0, uint32_t& d1) {
   d1 = __builtin_amdgcn_perm(x1, n1, sel);
 }
 
+// LDS transpose read (ds_read_b64_tr_b16, CDNA4).  Every lane names an 8-byte
+// piece (four 16-bit elements, 8-byte aligned); within each group of 16 lanes,
+// lane 4a + b receives element b of the pieces named by lanes a, 4 + a, 8 + a and
+// 12 + a of its group, in that order.  Reading rows r0 + L/4 at columns
+// c0 + 4 (L % 4) (lane L) therefore hands lane l the four elements
+// M[r0 + 4 (l/16) + j][c0 + l % 16], j = 0..3: one column piece of a 16 x 16
+// block, laid out as an accumulator tile holds it.
+__device__ __forceinline__ bf16x4 ds_read_tr16(const bf16* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+// The column piece above: rows r0 + 4g .. r0 + 4g + 3 of column c0 + lane%16 of
+// a row-major LDS matrix (rows 8-byte aligned, c0 a multiple of 4).
+__device__ __forceinline__ bf16x4 ld_cpiece_tr(const bf16* base, int ld, int r0, int c0) {
+  const int l = lane_id();
+  return ds_read_tr16(base + (r0 + (l >> 2)) * ld + c0 + 4 * (l & 3));
+}
+
 // Fragment whose k-slots walk down column col0 + lane%16 of a row-major E
-// matrix (rows k0+4g.., k0+16+4g..: the operand layout of an accumulator tile
-// pair), read as 4-element row pieces and turned into column pieces by quad
-// transposes.  col0 must be a multiple of 4; all 64 lanes must take part.
+// matrix in LDS (rows k0+4g.., k0+16+4g..: the operand layout of an accumulator
+// tile pair).  bf16: two transpose reads; fp32: 4-element row pieces turned
+// into column pieces by quad transposes.  col0 must be a multiple of 4; all 64
+// lanes must take part.
 template <class E>
 __device__ __forceinline__ Frag<E> ld_fragC_q(const E* base, int ld, int k0, int col0);
 template <>
 __device__ __forceinline__ Frag<bf16> ld_fragC_q<bf16>(const bf16* base, int ld, int k0, int col0) {
-  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
-  const bf16* p = base + (k0 + 4 * g + b) * ld + col0 + 4 * q;
-  typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
-  typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
-  u32x2 x = *reinterpret_cast<const u32x2*>(p);
-  u32x2 y = *reinterpret_cast<const u32x2*>(p + 16 * ld);
-  uint32_t x0 = x[0], x1 = x[1], y0 = y[0], y1 = y[1];
-  quad_transpose16(x0, x1);
-  quad_transpose16(y0, y1);
+  const bf16x4 a = ld_cpiece_tr(base, ld, k0, col0), b = ld_cpiece_tr(base, ld, k0 + 16, col0);
   Frag<bf16> f;
-  f.v = __builtin_bit_cast(bf16x8, u32x4{x0, x1, y0, y1});
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return f;
 }
 template <>
@@ -359,19 +371,19 @@ __device__ __forceinline__ Frag<float> ld_fragC_q<float>(const float* base, int 
   return f;
 }
 
-// Element offset of S[v][k] inside one stored chunk state (v < Dv value row,
-// k < Dk key column).  The Dv x Dk matrix is kept as 4 x 16 blocks, each
-// row-major and contiguous (64 elements: one 128-byte line for bf16), blocks in
-// row-major order.  Four consecutive keys of one row, eight consecutive keys of
-// one row, and four consecutive rows of a 16-key column block all fall into
-// whole lines, so the state can be read down its rows and across them (after
-// a quad transpose) with every fetched line fully used.
-__host__ __device__ constexpr int64_t st_blk(int v, int k, int DK) {
-  return ((int64_t)(v >> 2) * (DK >> 4) + (k >> 4)) * 64 + ((v & 3) << 4) + (k & 15);
+// Element offset of M[r][c] in a matrix of ncol columns kept as 4 x 16 blocks,
+// each row-major and contiguous (64 elements: one 128-byte line for bf16),
+// blocks in row-major order.  Four or eight consecutive columns of one row, and
+// the same columns of four consecutive rows, fall into whole lines, so such a
+// matrix can be read along its rows and, after a quad transpose, down its
+// columns with every fetched line fully used.  The stored chunk states are
+// h (Dk x Dv) in this layout: h[d][v] at st_blk(d, v, Dv).
+__host__ __device__ constexpr int64_t st_blk(int r, int c, int ncol) {
+  return ((int64_t)(r >> 2) * (ncol >> 4) + (c >> 4)) * 64 + ((r & 3) << 4) + (c & 15);
 }
 
-// ld_frag8 from a blocked chunk state: row v, keys k0 + 8g .. k0 + 8g + 7
-// (k0 a multiple of 16).
+// ld_frag8 from a blocked matrix of DK columns: row v, columns k0 + 8g ..
+// k0 + 8g + 7 (k0 a multiple of 16).
 __device__ __forceinline__ Frag<bf16> ld_frag8_st(const bf16* base, int DK, int v, int k0) {
   const int g = lane_id() >> 4;
   Frag<bf16> f;
@@ -534,6 +546,17 @@ __device__ __forceinline__ void st4_transposed<bf16>(bf16* p, const f32x4& v) {
 template <>
 __device__ __forceinline__ void st4_transposed<float>(float* p, const f32x4& v) {
   *reinterpret_cast<f32x4*>(p) = quad_transpose(v);
+}
+
+// Rows r0 .. r0 + 3 of column c0 + lane%16 (an accumulator tile's column
+// piece, c0 a multiple of 16) into a blocked matrix of ncol columns (st_blk):
+// quad-transposed first, so that the lane holds row r0 + lane%4 at columns
+// c0 + 4 ((lane / 4) % 4) .. + 3 and stores them as one piece.  All 64 lanes
+// must take part.
+template <class E>
+__device__ __forceinline__ void st_blk_row4(E* base, int r0, int c0, int ncol, const f32x4& x) {
+  const int l = lane_id(), q = (l >> 2) & 3, b = l & 3;
+  st4_transposed<E>(base + st_blk(r0 + b, c0 + 4 * q, ncol), x);
 }
 
 // acc + sum over the eight k-slots of a[j] * b[j] (bf16 pairs on the dot

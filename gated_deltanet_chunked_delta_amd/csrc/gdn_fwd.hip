@@ -265,13 +265,12 @@ struct Chunk {
     if (PREP && p.prep.qk_norm) ld.normalize();
     ld.store(*sp);
     ld.store_rec(*sp);
-    // chunk-start state out, as S (Dv x Dk) in 4 x 16 blocks: the lane's four
-    // rows of one column are contiguous
+    // chunk-start state out, as h (Dk x Dv) in 4 x 16 blocks
     if (!LEAD && hs_chunk) {
 #pragma unroll
       for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) st4f<E>(hs_chunk + st_blk(n0 + 16 * nt + c16, 16 * t + 4 * g, DK), hacc[t][nt]);
+        for (int nt = 0; nt < NTW; ++nt) st_blk_row4<E>(hs_chunk, 16 * t + 4 * g, n0 + 16 * nt, DV, hacc[t][nt]);
     }
     __syncthreads();
     sp = lds_opaque(sp);

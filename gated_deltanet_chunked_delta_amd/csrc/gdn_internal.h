@@ -32,7 +32,7 @@ struct FwdParams {
   const SegDesc* segs;     // [total segments]
   const int* seg_first;    // [N+1]
   const int* chunk_first;  // [N+1]
-  void* hs;                // nullable: [total chunks][H] chunk start states S, Dv x Dk in st_blk order (dtype)
+  void* hs;                // nullable: [total chunks][H] chunk start states h, Dk x Dv in st_blk order (dtype)
   void* us;                // nullable: [total chunks][H][DV/16][CH][16] U = Ut - W h of each chunk in 16-column blocks (dtype)
   void* ulo;               // nullable (bf16 only, with us): U - bf16(U) rounded to bf16, laid out as us
   // [total chunks][H][CH][CH] fp32 row-major T = (I + diag(beta) A)^-1 of each chunk
@@ -83,7 +83,7 @@ struct RevParams {
   const SegDesc* segs;
   const int* seg_first;
   const int* chunk_first;
-  void* dhs;               // [total chunks][H] gradient at each chunk END, S-shaped, st_blk order (dtype)
+  void* dhs;               // [total chunks][H] gradient at each chunk END, Dk x Dv, st_blk order (dtype)
   const float* t_in;       // chunk matrices T (as FwdParams)
   const float* rec;        // scalar records (as FwdParams)
   // Each chunk's U (us, and for bf16 its rounding residual ulo; layout as

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 9
+#define GDN_ABI_VERSION 10
 
 typedef enum {
   GDN_OK = 0,
@@ -152,10 +152,10 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args);
  * C * H * (Dk * Dv + 64 * Dv) elements of the input dtype (bf16: C * H *
  * (Dk * Dv + 2 * 64 * Dv)), C = sum over sequences of ceil(len / 64).  The
  * first C * H * Dk * Dv elements are the
- * states: state (c, h) is S (= h^T, Dv x Dk) at the start of chunk c (chunks
+ * states: state (c, h) is h (= S^T, Dk x Dv) at the start of chunk c (chunks
  * numbered sequence after sequence), rounded to the dtype, stored at element
- * offset (c * H + h) * Dk * Dv in 4 x 16 blocks: S[j][i] sits at
- *     ((j / 4) * (Dk / 16) + i / 16) * 64 + (j % 4) * 16 + i % 16
+ * offset (c * H + h) * Dk * Dv in 4 x 16 blocks: h[i][j] (key i, value j) sits at
+ *     ((i / 4) * (Dv / 16) + j / 16) * 64 + (i % 4) * 16 + j % 16
  * (each block row-major and contiguous, blocks in row-major order), so that
  * the state can be read both along and across its rows in whole cache lines.
  * Then, at element offset C * H * Dk * Dv + (c * H + h) * 64 * Dv, each

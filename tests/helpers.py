@@ -33,9 +33,8 @@ def to_np(t):
 
 def unblock_states(flat, C, H, Dk, Dv):
     """Chunk states as saved by gdn_chunk_fwd (flat, C * H * Dk * Dv elements; each
-    state S = h^T, Dv x Dk, in 4 x 16 blocks as include/gdn.h states) -> numpy
+    state h, Dk x Dv, in 4 x 16 blocks as include/gdn.h states) -> numpy
     [C, H, Dk, Dv] holding h."""
     a = np.asarray(flat, dtype=np.float64)[:C * H * Dk * Dv]
-    # [C, H, Dv/4, Dk/16, 4, 16] -> S[c, h, j, i] with j = 4 jb + jr, i = 16 ib + ir
-    S = a.reshape(C, H, Dv // 4, Dk // 16, 4, 16).transpose(0, 1, 2, 4, 3, 5).reshape(C, H, Dv, Dk)
-    return S.transpose(0, 1, 3, 2)
+    # [C, H, Dk/4, Dv/16, 4, 16] -> h[c, h, i, j] with i = 4 ib + ir, j = 16 jb + jr
+    return a.reshape(C, H, Dk // 4, Dv // 16, 4, 16).transpose(0, 1, 2, 4, 3, 5).reshape(C, H, Dk, Dv)

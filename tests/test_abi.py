@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(L):
             "gdn_chunk_bwd_workspace_size", "gdn_last_error", "gdn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdn_abi_version() == 9
+    assert L.gdn_abi_version() == 10
 
 
 FAKE = 1 << 20  # a 16-byte aligned fake device address; never dereferenced
@@ -179,17 +179,17 @@ def test_decode_empty_batch_is_a_no_op(L):
 
 
 def test_state_block_layout_is_a_permutation():
-    """The saved-state block order (include/gdn.h) maps every (j, i) of a Dv x Dk
+    """The saved-state block order (include/gdn.h) maps every (i, j) of a Dk x Dv
     state to its own offset below Dk * Dv, and unblock_states inverts it."""
     from tests.helpers import unblock_states
     for Dk, Dv in ((128, 128), (64, 128), (128, 64), (64, 64)):
-        j, i = np.meshgrid(np.arange(Dv), np.arange(Dk), indexing="ij")
-        off = ((j // 4) * (Dk // 16) + i // 16) * 64 + (j % 4) * 16 + i % 16
+        i, j = np.meshgrid(np.arange(Dk), np.arange(Dv), indexing="ij")
+        off = ((i // 4) * (Dv // 16) + j // 16) * 64 + (i % 4) * 16 + j % 16
         assert np.array_equal(np.sort(off.ravel()), np.arange(Dk * Dv))
-        S = np.random.default_rng(Dk + Dv).standard_normal((Dv, Dk))
+        h = np.random.default_rng(Dk + Dv).standard_normal((Dk, Dv))
         flat = np.empty(Dk * Dv)
-        flat[off] = S
-        assert np.array_equal(unblock_states(flat, 1, 1, Dk, Dv)[0, 0], S.T)
+        flat[off] = h
+        assert np.array_equal(unblock_states(flat, 1, 1, Dk, Dv)[0, 0], h)
 
 
 def test_noalloc_rejects_oversize_before_any_device_call(L):
