@@ -453,11 +453,11 @@ struct GradLayout {
   static constexpr int PADE = 16 / (int)sizeof(E);
   static constexpr int LK = DK + PADE;  // row-major [64][DK] E
   static constexpr int LV = DV + PADE;  // row-major [64][DV] E
-  static constexpr int LT = CH + 4;     // transposed [D][64] E
+  static constexpr int LT = CH + 4;     // transposed [D][64] E: an accumulator tile's columns as rows
   static constexpr int LA = CH + 4;     // fp32 [64][64]
   static constexpr int cmax(int a, int b) { return a > b ? a : b; }
   static constexpr int SLOT = cmax(cmax(CH * LK * (int)sizeof(E), CH * LV * (int)sizeof(E)),
-                                   cmax(DK * LT * (int)sizeof(E), CH * LA * 4));
+                                   cmax(cmax(DK, DV) * LT * (int)sizeof(E), CH * LA * 4));
   static constexpr int NSLOT = 9;
 };
 
@@ -474,29 +474,33 @@ struct alignas(16) GradSmem {
   float GamC;
 };
 
-// slot roles
-enum { SK = 0, SKT = 1, SQ = 2, SV = 3, SDO = 4, ST = 5, SKD = 6, SP = 7, SDU = 8 };
+// slot roles (each slot holds one tile at a time; the kernel's phases hand
+// them on: Q -> GW^T -> dV, U -> GT^T, dO -> dQ, KD -> dK, scale P^T ->
+// (GP * M)^T -> Z^T)
+enum { SK = 0, SE = 1, SQ = 2, SV = 3, SDO = 4, ST = 5, SKD = 6, SP = 7, SDU = 8 };
 
 // A 64 x 64 fp32 matrix in one LDS slot, kept for near-fp32 products (PFrag).
 // E = float stores it as is (row stride LA).  E = bf16 stores its bf16 hi and
 // lo parts (x = hi + lo, lo the rounded residual) as two planes of row stride
 // LP: each value is split once, when written, and fragments load ready to
-// multiply.  row(): k-slots along row r; col(): k-slots down column c0 + lane%16.
+// multiply.  row(): k-slots along row r; col(): k-slots down column c0 + lane%16;
+// cpiece(): the accumulator-tile piece at (r0, c0), as fp32.
 template <class E> struct PMat;
 template <> struct PMat<float> {
   static constexpr int LA = CH + 4;
   float* m;
   __device__ __forceinline__ explicit PMat(void* slot) : m(static_cast<float*>(slot)) {}
-  __device__ __forceinline__ void put(int r, int c, float x) const { m[r * LA + c] = x; }
   __device__ __forceinline__ void put4(int r, int c0, const f32x4& x) const {
     *reinterpret_cast<f32x4*>(&m[r * LA + c0]) = x;
   }
-  __device__ __forceinline__ float at(int r, int c) const { return m[r * LA + c]; }
-  __device__ __forceinline__ Frag<float> row_e(int r, int k0) const { return ld_frag(m, LA, r, k0); }
   __device__ __forceinline__ PFrag<float> row(int r, int k0) const { return PFrag<float>(ld_frag(m, LA, r, k0)); }
   __device__ __forceinline__ PFrag<float> col(int k0, int c0) const {
     return PFrag<float>(ld_fragT<float>(m, LA, c0 + (lane_id() & 15), k0, 1.f));
   }
+  __device__ __forceinline__ Frag<float> col_e(int k0, int c0) const {
+    return ld_fragT<float>(m, LA, c0 + (lane_id() & 15), k0, 1.f);
+  }
+  __device__ __forceinline__ f32x4 cpiece(int r0, int c0) const { return ld_cpiece<float>(m, LA, r0, c0); }
 };
 template <> struct PMat<bf16> {
   static constexpr int LP = CH + 4;  // bf16 elements per row: 8-byte aligned rows
@@ -505,30 +509,16 @@ template <> struct PMat<bf16> {
   typedef bf16 b4_t __attribute__((__vector_size__(8)));
   __device__ __forceinline__ explicit PMat(void* slot)
       : hi(static_cast<bf16*>(slot)), lo(static_cast<bf16*>(slot) + CH * LP) {}
-  __device__ __forceinline__ static void split(float x, bf16& h, bf16& l) {
-    h = (bf16)x;
-    l = (bf16)(x - (float)h);
-  }
-  __device__ __forceinline__ void put(int r, int c, float x) const {
-    bf16 h, l;
-    split(x, h, l);
-    hi[r * LP + c] = h;
-    lo[r * LP + c] = l;
-  }
   __device__ __forceinline__ void put4(int r, int c0, const f32x4& x) const {
     b4_t h, l;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      bf16 a, b;
-      split(x[i], a, b);
-      h[i] = a;
-      l[i] = b;
+      h[i] = (bf16)x[i];
+      l[i] = (bf16)(x[i] - (float)h[i]);
     }
     *reinterpret_cast<b4_t*>(&hi[r * LP + c0]) = h;
     *reinterpret_cast<b4_t*>(&lo[r * LP + c0]) = l;
   }
-  __device__ __forceinline__ float at(int r, int c) const { return (float)hi[r * LP + c] + (float)lo[r * LP + c]; }
-  __device__ __forceinline__ Frag<bf16> row_e(int r, int k0) const { return ld_frag(hi, LP, r, k0); }
   __device__ __forceinline__ PFrag<bf16> row(int r, int k0) const {
     PFrag<bf16> f;
     f.hi = ld_frag(hi, LP, r, k0);
@@ -541,6 +531,10 @@ template <> struct PMat<bf16> {
     f.lo = ld_fragC_q<bf16>(lo, LP, k0, c0);
     return f;
   }
+  __device__ __forceinline__ Frag<bf16> col_e(int k0, int c0) const { return ld_fragC_q<bf16>(hi, LP, k0, c0); }
+  __device__ __forceinline__ f32x4 cpiece(int r0, int c0) const {
+    return ld_cpiece<bf16>(hi, LP, r0, c0) + ld_cpiece<bf16>(lo, LP, r0, c0);
+  }
 };
 
 // One chunk per workgroup of 8 waves.  Wave w works on column group cw = w % 4
@@ -549,11 +543,14 @@ template <> struct PMat<bf16> {
 // waves share each SIMD and every accumulator array is half the size it would
 // be with four waves.  Sums over rows or columns that cross those halves go
 // through small LDS arrays with a single writer per entry (deterministic).
+// Accumulator tiles that later products read down their columns are stored
+// transposed (M^T row-major, the lane's four rows of a column as one piece);
+// reads across the other way use the LDS transpose loads.
 template <class E, int DK, int DV, bool PREP>
 __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   using L = GradLayout<E, DK, DV>;
   constexpr int NT = 512;
-  constexpr int LK = L::LK, LV = L::LV, LT = L::LT, LA = L::LA;
+  constexpr int LK = L::LK, LV = L::LV, LT = L::LT;
   constexpr int CTK = DK / 64, CTV = DV / 64;  // 16-wide column tiles per column group
   // P5 (dU) partition: with at least eight 16-wide value tiles every wave takes
   // its own value tiles over all four row tiles, so no two waves request the
@@ -563,7 +560,6 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   constexpr int P5C = P5ALL ? DV / 128 : CTV, P5R = P5ALL ? 4 : 2;
   __shared__ GradSmem<E, DK, DV> s;
   auto slotE = [&](int i) { return reinterpret_cast<E*>(s.slot[i]); };
-  auto slotF = [&](int i) { return reinterpret_cast<float*>(s.slot[i]); };
 
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int cw = w & 3, rh = w >> 2;
@@ -582,11 +578,10 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   const float scale = p.scale;
 
   E* sK = slotE(SK);
-  E* sKT = slotE(SKT);
-  const PMat<E> TT(s.slot[ST]);  // T^T (so that T^T's rows, the most read, load as rows)
-  float* sKD = slotF(SKD);
-  float* sP = slotF(SP);
-  E* sDU = slotE(SDU);
+  const PMat<E> Tm(s.slot[ST]);                                // T (row-major)
+  f32x4* sKD = reinterpret_cast<f32x4*>(s.slot[SKD]);           // KD: tile (rt, ct), lane l at (4 rt + ct) 64 + l
+  E* sPT = slotE(SP);                                           // scale P^T, then (GP * M)^T
+  E* sDUT = slotE(SDU);                                         // dU^T
 
   // e_r = ek_r k_r.(U dh'^T)_r, the reverse chain's row terms (summed here over
   // its waves): it enters dgam_r with a minus sign and the last row with a plus,
@@ -601,11 +596,11 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
 
   // ---- P1: staging (all four tiles in flight at once; rows past the end are
-  //          zero); zero T (unless given), P and the cross-wave sum arrays.
-  //          dh' down this wave's value columns (the operand of P5) is
-  //          requested after the tiles have landed and stays in flight until
-  //          P5, where quad transposes turn its row pieces into columns; its
-  //          products use the contiguous k-slot order.
+  //          zero); T (unless given) split into its bf16 parts; zero the
+  //          cross-wave sum arrays.  dh' down this wave's value columns (the
+  //          operand of P5) is requested after the tiles have landed and stays
+  //          in flight until P5, where quad transposes turn its row pieces into
+  //          columns; its products use the contiguous k-slot order.
   RawFrag<E> dkraw[P5C][DK / 32];
   {
     const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
@@ -636,11 +631,6 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     f32x4 tvals[TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) tvals[i] = *reinterpret_cast<const f32x4*>(tin + 4 * (tid + i * NT));
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int e = 4 * (tid + i * NT);
-      *reinterpret_cast<f32x4*>(&sP[(e >> 6) * LA + (e & 63)]) = zero4();
-    }
     for (int e = tid; e < 4 * CH; e += NT) {
       (&s.p7[0][0])[e] = 0.f;
       (&s.c7[0][0])[e] = 0.f;
@@ -669,7 +659,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       tq.normalize_rows(ht);
     }
     if (rh == 0) {
-      tk.store(sK, LK, sKT, LT, ht);
+      tk.store(sK, LK, nullptr, 0, ht);
       tq.store(slotE(SQ), LK, nullptr, 0, ht);
     } else {
 #pragma unroll
@@ -684,8 +674,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int e = 4 * (tid + i * NT);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) TT.put((e & 63) + q, e >> 6, tvals[i][q]);
+      Tm.put4(e >> 6, e & 63, tvals[i]);
     }
   }
   __syncthreads();
@@ -697,18 +686,29 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb) dkraw[nt][kb] = raw_fragC_q8_st<E>(dhs, DV, 32 * kb, p5n0 + 16 * nt);
 
-  // ---- P2: KD = strict_lower(K K^T * D), P = (Q K^T) * M  (20 lower tiles:
-  //          tile w + 8j for wave w, all fragment reads issued before the products)
+  // ---- P2: KD = strict_lower(K K^T * D) -> slot KD; P = (Q K^T) * M, kept in
+  //          fp32 registers for P7 and stored as scale P^T for P5.  Wave w
+  //          takes P tiles w and w + 8 (those P7 gives it) and KD tiles w - 2
+  //          and w + 4 (2 <= w < 6); the six zero tiles of P^T are written too.
+  f32x4 pkeep[2];
   {
     constexpr int NJ = 3;
     f32x4 acc[NJ];
     Frag<E> xr[NJ][DK / 32], xc[NJ][DK / 32];
+    auto tile = [&](int j, bool& valid, bool& isp, int& rt, int& ct) {
+      valid = j < 2 || (w >= 2 && w < 6);
+      isp = j == 0 || (j == 1 && w < 2);
+      const int tt = j == 0 ? w : (j == 1 ? (w < 2 ? w + 8 : w - 2) : w + 4);
+      rt = tt < 1 ? 0 : (tt < 3 ? 1 : (tt < 6 ? 2 : 3));
+      ct = tt - rt * (rt + 1) / 2;
+    };
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int ti = w + 8 * j, tt = ti >= 10 ? ti - 10 : ti;
-      const int rt = tt < 1 ? 0 : (tt < 3 ? 1 : (tt < 6 ? 2 : 3)), ct = tt - rt * (rt + 1) / 2;
-      const E* X = ti >= 10 ? slotE(SQ) : sK;
-      if (ti < 20) {
+      bool valid, isp;
+      int rt, ct;
+      tile(j, valid, isp, rt, ct);
+      const E* X = isp ? slotE(SQ) : sK;
+      if (valid) {
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
           xr[j][kb] = ld_frag(X, LK, 16 * rt + c16, 32 * kb);
@@ -718,28 +718,42 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
+      bool valid, isp;
+      int rt, ct;
+      tile(j, valid, isp, rt, ct);
       acc[j] = zero4();
-      if (w + 8 * j < 20) {
+      if (valid) {
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) mma(acc[j], xr[j][kb], xc[j][kb]);
       }
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int ti = w + 8 * j, tt = ti >= 10 ? ti - 10 : ti;
-      const int rt = tt < 1 ? 0 : (tt < 3 ? 1 : (tt < 6 ? 2 : 3)), ct = tt - rt * (rt + 1) / 2;
-      if (ti < 20) {
+      bool valid, isp;
+      int rt, ct;
+      tile(j, valid, isp, rt, ct);
+      if (valid) {
         const int c = 16 * ct + c16;
         const float gc = s.gam[c];
         const f32x4 gr4 = *reinterpret_cast<const f32x4*>(&s.gam[16 * rt + 4 * g]);
+        f32x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * g + i;
           const float dm = __expf(gr4[i] - gc);
-          if (ti < 10) sKD[r * LA + c] = (c < r) ? acc[j][i] * dm : 0.f;
-          else sP[r * LA + c] = (c <= r) ? acc[j][i] * dm : 0.f;
+          v[i] = (isp ? c <= r : c < r) ? acc[j][i] * dm : 0.f;
+        }
+        if (isp) {
+          if (j < 2) pkeep[j] = v;
+          st_tile_cm<E>(sPT, LT, 16 * rt, 16 * ct, v * scale);
+        } else {
+          sKD[(4 * rt + ct) * 64 + l] = v;
         }
       }
+    }
+    if (w < 6) {  // P's strictly upper tiles (rt < ct), as zero tiles of P^T
+      const int rt = w < 3 ? 0 : (w < 5 ? 1 : 2), ct = w < 3 ? w + 1 : (w < 5 ? w - 1 : 3);
+      st_tile_cm<E>(sPT, LT, 16 * rt, 16 * ct, zero4());
     }
   }
   __syncthreads();
@@ -761,9 +775,9 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       dhn[dt][kb] = ld_frag8_st(dhs, DV, d0 + 16 * dt + c16, 32 * kb);
     }
 
-  // ---- P5: dU = diag(ek) K dh' + scale P^T dO (P5 rows and value columns)
-  f32x4 du[P5R][P5C];
+  // ---- P5: dU = diag(ek) K dh' + scale P^T dO (P5 rows and value columns) -> dU^T
   {
+    f32x4 du[P5R][P5C];
     Frag<E> dk_[P5C][DK / 32];
 #pragma unroll
     for (int nt = 0; nt < P5C; ++nt)
@@ -782,15 +796,15 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         for (int kb = 0; kb < DK / 32; ++kb) mma(kd, ld_frag8(sK, LK, 16 * rt + c16, 32 * kb), dk_[nt][kb]);
         kd = kd * *reinterpret_cast<const f32x4*>(&s.ek[16 * rt + 4 * g]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(kd, ld_fragT<E>(sP, LA, 16 * rt + c16, 32 * kb, scale), dor[kb]);
+        for (int kb = 0; kb < 2; ++kb) mma(kd, ld_frag(sPT, LT, 16 * rt + c16, 32 * kb), dor[kb]);
         du[j][nt] = kd;
       }
     }
+#pragma unroll
+    for (int j = 0; j < P5R; ++j)
+#pragma unroll
+      for (int nt = 0; nt < P5C; ++nt) st_tile_cm<E>(sDUT, LT, 16 * (p5r0 + j), p5n0 + 16 * nt, du[j][nt]);
   }
-#pragma unroll
-  for (int j = 0; j < P5R; ++j)
-#pragma unroll
-    for (int nt = 0; nt < P5C; ++nt) st_tile_rows<E>(sDU, LV, 16 * (p5r0 + j), p5n0 + 16 * nt, du[j][nt]);
   __syncthreads();
 
   // ---- P6: GW = -dU h^T, dQ1 = dO h^T, Udh = U dh'^T (own rows and key columns)
@@ -817,7 +831,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     for (int dt = 0; dt < CTK; ++dt) a[dt] = b[dt] = c[dt] = zero4();
 #pragma unroll
     for (int kb = 0; kb < DV / 32; ++kb) {
-      const Frag<E> xdu = ld_frag8(sDU, LV, 16 * rt + c16, 32 * kb);
+      const Frag<E> xdu = ld_fragC_q8<E>(sDUT, LT, 32 * kb, 16 * rt);
       const Frag<E> xdo = ld_frag8(slotE(SDO), LV, 16 * rt + c16, 32 * kb);
       const Frag<E> xu = ld_frag8(slotE(SV), LV, 16 * rt + c16, 32 * kb);
 #pragma unroll
@@ -844,53 +858,54 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) { pin(rg[j]); pin(rb[j]); }
   pin(hdh);
-  __syncthreads();  // Q reads done: slot Q becomes GW
-  {
-    E* sGW = slotE(SQ);
+  __syncthreads();  // Q reads done: slot Q becomes GW^T
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int dt = 0; dt < CTK; ++dt) st_tile_rows<E>(sGW, LK, 16 * (2 * rh + j), d0 + 16 * dt, gw[j][dt]);
-  }
+    for (int dt = 0; dt < CTK; ++dt) st_tile_cm<E>(slotE(SQ), LT, 16 * (2 * rh + j), d0 + 16 * dt, gw[j][dt]);
 
-  // ---- P7: GP = scale (dO U^T) * [i <= r]; GP*P row / column sums; P -> GP * M
-  for (int ti = w; ti < 10; ti += 8) {
-    int rt = 0;
-    while ((rt + 1) * (rt + 2) / 2 <= ti) ++rt;
-    const int ct = ti - rt * (rt + 1) / 2;
-    f32x4 acc = zero4();
+  // ---- P7: GP = scale (dO U^T) * [i <= r]; GP*P row / column sums; (GP * M)^T
+  //          -> slot P (scale P^T was last read in P5)
 #pragma unroll
-    for (int kb = 0; kb < DV / 32; ++kb)
-      mma(acc, ld_frag(slotE(SDO), LV, 16 * rt + c16, 32 * kb), ld_frag(slotE(SV), LV, 16 * ct + c16, 32 * kb));
-    const int c = 16 * ct + c16;
-    f32x4 rs4;
-    float csum = 0.f;
+  for (int jj = 0; jj < 2; ++jj) {
+    const int ti = w + 8 * jj;
+    if (ti < 10) {
+      const int rt = ti < 1 ? 0 : (ti < 3 ? 1 : (ti < 6 ? 2 : 3)), ct = ti - rt * (rt + 1) / 2;
+      f32x4 acc = zero4();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * g + i;
-      const float gp = (c <= r) ? scale * acc[i] : 0.f;
-      // the diagonal entry enters row sum r and column sum r with opposite
-      // signs: left out of both, it cannot leave a rounding residue in dgam_r
-      // (which strong decay would make larger than dgam itself)
-      const float gpp = (c < r) ? gp * sP[r * LA + c] : 0.f;
-      rs4[i] = gpp;
-      csum += gpp;
-      sP[r * LA + c] = (c <= r) ? gp * __expf(s.gam[r] - s.gam[c]) : 0.f;
+      for (int kb = 0; kb < DV / 32; ++kb)
+        mma(acc, ld_frag(slotE(SDO), LV, 16 * rt + c16, 32 * kb), ld_frag(slotE(SV), LV, 16 * ct + c16, 32 * kb));
+      const int c = 16 * ct + c16;
+      const f32x4 pv = pkeep[jj];
+      f32x4 rs4, gpm;
+      float csum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        const float gp = (c <= r) ? scale * acc[i] : 0.f;
+        // the diagonal entry enters row sum r and column sum r with opposite
+        // signs: left out of both, it cannot leave a rounding residue in dgam_r
+        // (which strong decay would make larger than dgam itself)
+        const float gpp = (c < r) ? gp * pv[i] : 0.f;
+        rs4[i] = gpp;
+        csum += gpp;
+        gpm[i] = (c <= r) ? gp * __expf(s.gam[r] - s.gam[c]) : 0.f;
+      }
+      st_tile_cm<E>(sPT, LT, 16 * rt, 16 * ct, gpm);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rs4[i] = row16_sum(rs4[i]);
+      csum += __shfl_xor(csum, 16, 64);
+      csum += __shfl_xor(csum, 32, 64);
+      if (c16 == 0) *reinterpret_cast<f32x4*>(&s.p7[ct][16 * rt + 4 * g]) = rs4;
+      if (g == 0) s.c7[rt][c] = -csum;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rs4[i] = row16_sum(rs4[i]);
-    csum += __shfl_xor(csum, 16, 64);
-    csum += __shfl_xor(csum, 32, 64);
-    if (c16 == 0) *reinterpret_cast<f32x4*>(&s.p7[ct][16 * rt + 4 * g]) = rs4;
-    if (g == 0) s.c7[rt][c] = -csum;
   }
   __syncthreads();
 
   // V rows 16 cw .. 16 cw + 15, the operand of P9 (every tile of a wave there
-  // has column tile cw; slot V holds U by then): read from global now so that
-  // the loads are in flight during P8 (rows past the end are copies of the last
-  // one; beta = 0 there removes them).  Contiguous k order, one 16-byte read
-  // per fragment.
+  // has column tile cw): read from global now so that the loads are in flight
+  // during P8 (rows past the end are copies of the last one; beta = 0 there
+  // removes them).  Contiguous k order, one 16-byte read per fragment.
   Frag<E> vf[DV / 32];
   {
     const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
@@ -902,26 +917,22 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   // ---- P8: XW = T^T GW (own rows); row dots; dK partial (with GPM^T Q); dQ
   f32x4 dkacc[2][CTK];
   {
-    const E* sGW = slotE(SQ);
-    // K is re-read here: an opaque pointer keeps the compiler from holding the
-    // values read in P6 in registers (or scratch) until now
-    const E* sKTr = lds_opaque(sKT);
+    const E* sGWT = slotE(SQ);
 #pragma unroll
     for (int dt = 0; dt < CTK; ++dt) {
       Frag<E> gwf[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) gwf[kb] = ld_fragC_q<E>(sGW, LK, 32 * kb, d0 + 16 * dt);
+      for (int kb = 0; kb < 2; ++kb) gwf[kb] = ld_frag(sGWT, LT, d0 + 16 * dt + c16, 32 * kb);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int rt = 2 * rh + j;
         f32x4 xw = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(xw, TT.row_e(16 * rt + c16, 32 * kb), gwf[kb]);
-        const int dcol = d0 + 16 * dt + c16;
+        for (int kb = 0; kb < 2; ++kb) mma(xw, Tm.col_e(32 * kb, 16 * rt), gwf[kb]);
         f32x4 pq = zero4();  // GPM^T Q (GPM is final since P7)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(pq, ld_fragT<E>(sP, LA, 16 * rt + c16, 32 * kb, 1.f), qr[kb][dt]);
-        const f32x4 kv4 = ld4f<E>(sKTr + dcol * LT + 16 * rt + 4 * g);
+        for (int kb = 0; kb < 2; ++kb) mma(pq, ld_frag(sPT, LT, 16 * rt + c16, 32 * kb), qr[kb][dt]);
+        const f32x4 kv4 = ld_cpiece<E>(sK, LK, 16 * rt, d0 + 16 * dt);
         const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&s.Gam[16 * rt + 4 * g]);
         const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&s.bg[16 * rt + 4 * g]);
         const f32x4 ek4 = *reinterpret_cast<const f32x4*>(&s.ek[16 * rt + 4 * g]);
@@ -946,17 +957,18 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         f32x4 a = zero4();
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          mma(a, ld_frag_f32<E>(sP, LA, 16 * rt + c16, 32 * kb), ld_frag(sKT, LT, d0 + 16 * dt + c16, 32 * kb));
+          mma(a, ld_fragC_q<E>(sPT, LT, 32 * kb, 16 * rt), ld_fragC_q<E>(sK, LK, 32 * kb, d0 + 16 * dt));
         const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&s.Gam[16 * rt + 4 * g]);
         st_tile_rows<E>(sDQ, LK, 16 * rt, d0 + 16 * dt, dq1[j][dt] * gm4 * scale + a);
       }
   }
   __syncthreads();
 
-  // ---- P9: GT = dU V^T diag(beta) + GW K^T diag(beta Gam) -> slot V (PMat).
-  //          The dbeta term sum_c (T^T dU)[r][c] V[r][c] is the column sum
+  // ---- P9: GT = dU V^T diag(beta) + GW K^T diag(beta Gam) -> slot V as GT^T
+  //          (PMat; U was last read in P7).  The dbeta term
+  //          sum_c (T^T dU)[r][c] V[r][c] is the column sum
   //          sum_i T[i][r] (dU V^T)[i][r], taken here from the first product.
-  const PMat<E> GTm(s.slot[SV]);
+  const PMat<E> GTT(s.slot[SV]);
   {
     const int c = 16 * cw + c16;
     float tm = 0.f;
@@ -965,17 +977,19 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       const int rt = rh + 2 * j;
       f32x4 a = zero4(), b = zero4();
 #pragma unroll
-      for (int kb = 0; kb < DV / 32; ++kb) mma(a, ld_frag8(sDU, LV, 16 * rt + c16, 32 * kb), vf[kb]);
+      for (int kb = 0; kb < DV / 32; ++kb) mma(a, ld_fragC_q8<E>(sDUT, LT, 32 * kb, 16 * rt), vf[kb]);
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb)
-        mma(b, ld_frag(slotE(SQ), LK, 16 * rt + c16, 32 * kb), ld_frag(sK, LK, c, 32 * kb));
-      // U (slot V) is no longer read: every wave finished P7 before the barrier above
+        mma(b, ld_fragC_q<E>(slotE(SQ), LT, 32 * kb, 16 * rt), ld_frag(sK, LK, c, 32 * kb));
+      const f32x4 t4 = Tm.cpiece(16 * rt, 16 * cw);
+      const float bc = s.beta[c], bgc = s.bg[c];
+      f32x4 gt;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
-        GTm.put(r, c, s.beta[c] * a[i] + s.bg[c] * b[i]);
-        tm += TT.at(c, r) * a[i];
+        gt[i] = bc * a[i] + bgc * b[i];
+        tm += t4[i] * a[i];
       }
+      GTT.put4(c, 16 * rt + 4 * g, gt);
     }
     tm += __shfl_xor(tm, 16, 64);
     tm += __shfl_xor(tm, 32, 64);
@@ -983,23 +997,23 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   __syncthreads();
 
-  // ---- P10: Z = GT T^T (own row tiles, column tile cw) -> slot P (last read in
-  //           P8), GA = strict_lower(-T^T Z) (own rows); E -> S = E + E^T (slot KD)
-  // XU = T^T dU (own rows and value columns) -> dV into slot Q (GW was last read in P9)
-  // The rows of T^T for this wave's row tiles serve XU (in E) and GA (near fp32).
+  // ---- P10: Z = GT T^T (own row tiles, column tile cw) -> slot P as Z^T (last
+  //           read in P8), GA = strict_lower(-T^T Z) (own rows); E -> slot E
+  //           as E^T.  XU = T^T dU (own rows and value columns) -> dV into
+  //           slot Q (GW^T was last read in P9).  The rows of T^T for this
+  //           wave's row tiles serve XU (in E) and GA (near fp32).
   PFrag<E> ttp[2][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      ttp[j][kb] = TT.row(16 * (2 * rh + j) + c16, 32 * kb);
+    for (int kb = 0; kb < 2; ++kb) ttp[j][kb] = Tm.col(32 * kb, 16 * (2 * rh + j));
   {
     E* sDV = slotE(SQ);
 #pragma unroll
     for (int nt = 0; nt < CTV; ++nt) {
       Frag<E> duf[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) duf[kb] = ld_fragC_q<E>(sDU, LV, 32 * kb, n0 + 16 * nt);
+      for (int kb = 0; kb < 2; ++kb) duf[kb] = ld_frag(sDUT, LT, n0 + 16 * nt + c16, 32 * kb);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int rt = 2 * rh + j;
@@ -1017,15 +1031,15 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     // LDS, stored transposed so that Z's columns read back as rows
     const PMat<E> ZT(s.slot[SP]);
     {
-      PFrag<E> tcol[2];  // rows 16 cw.. of T
+      PFrag<E> trow[2];  // rows 16 cw.. of T
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) tcol[kb] = TT.col(32 * kb, 16 * cw);
+      for (int kb = 0; kb < 2; ++kb) trow[kb] = Tm.row(16 * cw + c16, 32 * kb);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int rt = 2 * rh + j;
         f32x4 z = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(z, GTm.row(16 * rt + c16, 32 * kb), tcol[kb]);
+        for (int kb = 0; kb < 2; ++kb) mma(z, GTT.col(32 * kb, 16 * rt), trow[kb]);
         ZT.put4(16 * cw + c16, 16 * rt + 4 * g, z);
       }
     }
@@ -1035,48 +1049,40 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     for (int kb = 0; kb < 2; ++kb) zf[kb] = ZT.row(16 * cw + c16, 32 * kb);
     const int c = 16 * cw + c16;
     float csum = 0.f;
-    f32x4 ga[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int rt = 2 * rh + j;
       f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) mma(acc, ttp[j][kb], zf[kb]);
+      // KD's upper tiles were never written (and are zero)
+      const f32x4 kd4 = cw <= rt ? sKD[(4 * rt + cw) * 64 + l] : zero4();
+      f32x4 ev;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
         const float gav = (c < r) ? -acc[i] : 0.f;
-        const float kd = sKD[r * LA + c];
-        const float gaa = gav * s.beta[r] * kd;
+        const float gaa = gav * s.beta[r] * kd4[i];
         rg[j][i] += gaa;
         csum += gaa;
-        rb[j][i] += gav * kd;
-        ga[j][i] = gav;
+        rb[j][i] += gav * kd4[i];
+        ev[i] = (c < r) ? s.beta[r] * gav * __expf(s.gam[r] - s.gam[c]) : 0.f;
       }
+      st_tile_cm<E>(slotE(SE), LT, 16 * rt, 16 * cw, ev);
     }
     csum += __shfl_xor(csum, 16, 64);
     csum += __shfl_xor(csum, 32, 64);
     if (g == 0) s.c10[rh][c] = -csum;
-    __syncthreads();  // every wave has read its KD entries: slot KD becomes S
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * (2 * rh + j) + 4 * g + i;
-        if (c <= r) {
-          const float ev = s.beta[r] * ga[j][i] * __expf(s.gam[r] - s.gam[c]);
-          sKD[r * LA + c] = ev;
-          if (c < r) sKD[c * LA + r] = ev;
-        }
-      }
   }
   __syncthreads();
 
-  // ---- P11: dK = dK partial + S K (own rows and key columns) -> slot K
-  //           (free since P9).  The three gradient tiles are written out after
-  //           the last barrier, so that no load of this kernel waits behind a store.
+  // ---- P11: dK = dK partial + (E + E^T) K (own rows and key columns) -> slot KD
+  //           (last read in P10).  The three gradient tiles are written out
+  //           after the last barrier, so that no load of this kernel waits
+  //           behind a store.
   {
-    E* sDK = slotE(SK);
+    E* sDK = slotE(SKD);
+    const E* sET = slotE(SE);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1084,8 +1090,11 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         const int rt = 2 * rh + j;
         f32x4 b = dkacc[j][dt];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          mma(b, ld_frag_f32<E>(sKD, LA, 16 * rt + c16, 32 * kb), ld_frag(sKT, LT, d0 + 16 * dt + c16, 32 * kb));
+        for (int kb = 0; kb < 2; ++kb) {
+          const Frag<E> kc = ld_fragC_q<E>(sK, LK, 32 * kb, d0 + 16 * dt);
+          mma(b, ld_fragC_q<E>(sET, LT, 32 * kb, 16 * rt), kc);  // rows of E
+          mma(b, ld_frag(sET, LT, 16 * rt + c16, 32 * kb), kc);   // rows of E^T
+        }
         st_tile_rows<E>(sDK, LK, 16 * rt, d0 + 16 * dt, b);
       }
   }
@@ -1114,11 +1123,11 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     // gradients with respect to the raw q and k (the kernel saw them normalised)
     store_tile_unnorm<E, DK, NT>(slotE(SDO), LK, static_cast<const E*>(p.q) + (tok0 * H + h) * DK, (int64_t)H * DK,
                                  static_cast<E*>(p.dq) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
-    store_tile_unnorm<E, DK, NT>(slotE(SK), LK, static_cast<const E*>(p.k) + (tok0 * H + h) * DK, (int64_t)H * DK,
+    store_tile_unnorm<E, DK, NT>(slotE(SKD), LK, static_cast<const E*>(p.k) + (tok0 * H + h) * DK, (int64_t)H * DK,
                                  static_cast<E*>(p.dk) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
   } else {
     store_tile<E, DK, NT>(slotE(SDO), LK, static_cast<E*>(p.dq) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
-    store_tile<E, DK, NT>(slotE(SK), LK, static_cast<E*>(p.dk) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
+    store_tile<E, DK, NT>(slotE(SKD), LK, static_cast<E*>(p.dk) + (tok0 * H + h) * DK, (int64_t)H * DK, rows);
   }
   if (w == 0) {
     const int r = l;

@@ -371,6 +371,56 @@ __device__ __forceinline__ Frag<float> ld_fragC_q<float>(const float* base, int 
   return f;
 }
 
+// ld_fragC_q in the contiguous k-slot order (pairs with ld_frag8): k-slots
+// k0 + 8g .. k0 + 8g + 7 down column col0 + lane%16 of a row-major LDS matrix.
+template <class E>
+__device__ __forceinline__ Frag<E> ld_fragC_q8(const E* base, int ld, int k0, int col0);
+template <>
+__device__ __forceinline__ Frag<bf16> ld_fragC_q8<bf16>(const bf16* base, int ld, int k0, int col0) {
+  const int l = lane_id();
+  const bf16* p = base + (k0 + 8 * (l >> 4) + ((l & 15) >> 2)) * ld + col0 + 4 * (l & 3);
+  const bf16x4 a = ds_read_tr16(p), b = ds_read_tr16(p + 4 * ld);
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> ld_fragC_q8<float>(const float* base, int ld, int k0, int col0) {
+  const int l = lane_id();
+  const float* p = base + (k0 + 8 * (l >> 4)) * ld + col0 + (l & 15);
+  Frag<float> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f.lo[j] = p[j * ld];
+    f.hi[j] = p[(4 + j) * ld];
+  }
+  return f;
+}
+
+// Rows r0 + 4g .. r0 + 4g + 3 of column c0 + lane%16 of a row-major LDS
+// matrix, as fp32: the piece of an accumulator tile at (r0, c0).
+template <class E>
+__device__ __forceinline__ f32x4 ld_cpiece(const E* base, int ld, int r0, int c0);
+template <>
+__device__ __forceinline__ f32x4 ld_cpiece<bf16>(const bf16* base, int ld, int r0, int c0) {
+  const bf16x4 v = ld_cpiece_tr(base, ld, r0, c0);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+template <>
+__device__ __forceinline__ f32x4 ld_cpiece<float>(const float* base, int ld, int r0, int c0) {
+  const int l = lane_id();
+  const float* p = base + (r0 + 4 * (l >> 4)) * ld + c0 + (l & 15);
+  return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+
+// An accumulator tile (rows r0.., columns c0..) stored transposed, into the
+// row-major matrix M^T: the lane's four rows of its column are one piece.
+template <class E>
+__device__ __forceinline__ void st_tile_cm(E* baseT, int ldT, int r0, int c0, const f32x4& acc) {
+  const int l = lane_id();
+  st4f<E>(baseT + (c0 + (l & 15)) * ldT + r0 + 4 * (l >> 4), acc);
+}
+
 // Element offset of M[r][c] in a matrix of ncol columns kept as 4 x 16 blocks,
 // each row-major and contiguous (64 elements: one 128-byte line for bf16),
 // blocks in row-major order.  Four or eight consecutive columns of one row, and
