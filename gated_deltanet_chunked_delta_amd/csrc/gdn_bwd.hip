@@ -475,9 +475,9 @@ struct alignas(16) GradSmem {
 };
 
 // slot roles (each slot holds one tile at a time; the kernel's phases hand
-// them on: Q -> GW^T -> dV, U -> GT^T, dO -> dQ, KD -> dK, scale P^T ->
-// (GP * M)^T -> Z^T)
-enum { SK = 0, SE = 1, SQ = 2, SV = 3, SDO = 4, ST = 5, SKD = 6, SP = 7, SDU = 8 };
+// them on: Q -> GW^T -> dV, U -> GT^T, dO -> dQ, KD -> dK, scale P^T -> Z^T,
+// dU^T -> E^T; slot GP holds (GP * M)^T)
+enum { SK = 0, SGP = 1, SQ = 2, SV = 3, SDO = 4, ST = 5, SKD = 6, SP = 7, SDU = 8 };
 
 // A 64 x 64 fp32 matrix in one LDS slot, kept for near-fp32 products (PFrag).
 // E = float stores it as is (row stride LA).  E = bf16 stores its bf16 hi and
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   E* sK = slotE(SK);
   const PMat<E> Tm(s.slot[ST]);                                // T (row-major)
   f32x4* sKD = reinterpret_cast<f32x4*>(s.slot[SKD]);           // KD: tile (rt, ct), lane l at (4 rt + ct) 64 + l
-  E* sPT = slotE(SP);                                           // scale P^T, then (GP * M)^T
+  E* sPT = slotE(SP);                                           // scale P^T
   E* sDUT = slotE(SDU);                                         // dU^T
 
   // e_r = ek_r k_r.(U dh'^T)_r, the reverse chain's row terms (summed here over
@@ -775,7 +775,10 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       dhn[dt][kb] = ld_frag8_st(dhs, DV, d0 + 16 * dt + c16, 32 * kb);
     }
 
-  // ---- P5: dU = diag(ek) K dh' + scale P^T dO (P5 rows and value columns) -> dU^T
+  // ---- P5: dU = diag(ek) K dh' + scale P^T dO (P5 rows and value columns) -> dU^T;
+  //          GP = scale (dO U^T) * [i <= r] (tiles w, w + 8): GP*P row / column
+  //          sums, (GP * M)^T -> slot GP; Q down the own key columns
+  Frag<E> qr[2][CTK];
   {
     f32x4 du[P5R][P5C];
     Frag<E> dk_[P5C][DK / 32];
@@ -805,14 +808,52 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
       for (int nt = 0; nt < P5C; ++nt) st_tile_cm<E>(sDUT, LT, 16 * (p5r0 + j), p5n0 + 16 * nt, du[j][nt]);
   }
-  __syncthreads();
-
-  // ---- P6: GW = -dU h^T, dQ1 = dO h^T, Udh = U dh'^T (own rows and key columns)
-  Frag<E> qr[2][CTK];  // Q down the own key columns, all rows
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int ti = w + 8 * jj;
+    if (ti < 10) {
+      const int rt = ti < 1 ? 0 : (ti < 3 ? 1 : (ti < 6 ? 2 : 3)), ct = ti - rt * (rt + 1) / 2;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < DV / 32; ++kb)
+        mma(acc, ld_frag(slotE(SDO), LV, 16 * rt + c16, 32 * kb), ld_frag(slotE(SV), LV, 16 * ct + c16, 32 * kb));
+      const int c = 16 * ct + c16;
+      const f32x4 pv = pkeep[jj];
+      f32x4 rs4, gpm;
+      float csum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        const float gp = (c <= r) ? scale * acc[i] : 0.f;
+        // the diagonal entry enters row sum r and column sum r with opposite
+        // signs: left out of both, it cannot leave a rounding residue in dgam_r
+        // (which strong decay would make larger than dgam itself)
+        const float gpp = (c < r) ? gp * pv[i] : 0.f;
+        rs4[i] = gpp;
+        csum += gpp;
+        gpm[i] = (c <= r) ? gp * __expf(s.gam[r] - s.gam[c]) : 0.f;
+      }
+      st_tile_cm<E>(slotE(SGP), LT, 16 * rt, 16 * ct, gpm);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rs4[i] = row16_sum(rs4[i]);
+      csum += __shfl_xor(csum, 16, 64);
+      csum += __shfl_xor(csum, 32, 64);
+      if (c16 == 0) *reinterpret_cast<f32x4*>(&s.p7[ct][16 * rt + 4 * g]) = rs4;
+      if (g == 0) s.c7[rt][c] = -csum;
+    }
+  }
+  if (w < 6) {  // the strictly upper tiles of (GP * M)^T are zero
+    const int rt = w < 3 ? 0 : (w < 5 ? 1 : 2), ct = w < 3 ? w + 1 : (w < 5 ? w - 1 : 3);
+    st_tile_cm<E>(slotE(SGP), LT, 16 * rt, 16 * ct, zero4());
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int dt = 0; dt < CTK; ++dt) qr[kb][dt] = ld_fragC_q<E>(slotE(SQ), LK, 32 * kb, d0 + 16 * dt);
+  __syncthreads();
+
+  // ---- P6: GW = -dU h^T, dQ1 = dO h^T, Udh = U dh'^T (own rows and key columns);
+  //          GW -> slot Q as GW^T (Q was last read in P5)
   // (the state operands are rows of the stored h and dh', so these products
   //  use the contiguous k-slot order: one 16-byte read per fragment, each
   //  loaded once and used for both key-column tiles)
@@ -858,54 +899,17 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) { pin(rg[j]); pin(rb[j]); }
   pin(hdh);
-  __syncthreads();  // Q reads done: slot Q becomes GW^T
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int dt = 0; dt < CTK; ++dt) st_tile_cm<E>(slotE(SQ), LT, 16 * (2 * rh + j), d0 + 16 * dt, gw[j][dt]);
-
-  // ---- P7: GP = scale (dO U^T) * [i <= r]; GP*P row / column sums; (GP * M)^T
-  //          -> slot P (scale P^T was last read in P5)
-#pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const int ti = w + 8 * jj;
-    if (ti < 10) {
-      const int rt = ti < 1 ? 0 : (ti < 3 ? 1 : (ti < 6 ? 2 : 3)), ct = ti - rt * (rt + 1) / 2;
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < DV / 32; ++kb)
-        mma(acc, ld_frag(slotE(SDO), LV, 16 * rt + c16, 32 * kb), ld_frag(slotE(SV), LV, 16 * ct + c16, 32 * kb));
-      const int c = 16 * ct + c16;
-      const f32x4 pv = pkeep[jj];
-      f32x4 rs4, gpm;
-      float csum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
-        const float gp = (c <= r) ? scale * acc[i] : 0.f;
-        // the diagonal entry enters row sum r and column sum r with opposite
-        // signs: left out of both, it cannot leave a rounding residue in dgam_r
-        // (which strong decay would make larger than dgam itself)
-        const float gpp = (c < r) ? gp * pv[i] : 0.f;
-        rs4[i] = gpp;
-        csum += gpp;
-        gpm[i] = (c <= r) ? gp * __expf(s.gam[r] - s.gam[c]) : 0.f;
-      }
-      st_tile_cm<E>(sPT, LT, 16 * rt, 16 * ct, gpm);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rs4[i] = row16_sum(rs4[i]);
-      csum += __shfl_xor(csum, 16, 64);
-      csum += __shfl_xor(csum, 32, 64);
-      if (c16 == 0) *reinterpret_cast<f32x4*>(&s.p7[ct][16 * rt + 4 * g]) = rs4;
-      if (g == 0) s.c7[rt][c] = -csum;
-    }
-  }
   __syncthreads();
 
-  // V rows 16 cw .. 16 cw + 15, the operand of P9 (every tile of a wave there
+  // V rows 16 cw .. 16 cw + 15, the operand of GT (every tile of a wave there
   // has column tile cw): read from global now so that the loads are in flight
-  // during P8 (rows past the end are copies of the last one; beta = 0 there
-  // removes them).  Contiguous k order, one 16-byte read per fragment.
+  // during the first half of P8 (rows past the end are copies of the last one;
+  // beta = 0 there removes them).  Contiguous k order, one 16-byte read per
+  // fragment.
   Frag<E> vf[DV / 32];
   {
     const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
@@ -914,7 +918,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     for (int kb = 0; kb < DV / 32; ++kb) vf[kb] = ld_frag8(v + (int64_t)vrow * H * DV, 0, 0, 32 * kb);
   }
 
-  // ---- P8: XW = T^T GW (own rows); row dots; dK partial (with GPM^T Q); dQ
+  // ---- P8: XW = T^T GW (own rows); row dots; dK partial (with GPM^T Q); dQ;
+  //          then GT
   f32x4 dkacc[2][CTK];
   {
     const E* sGWT = slotE(SQ);
@@ -931,7 +936,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         for (int kb = 0; kb < 2; ++kb) mma(xw, Tm.col_e(32 * kb, 16 * rt), gwf[kb]);
         f32x4 pq = zero4();  // GPM^T Q (GPM is final since P7)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(pq, ld_frag(sPT, LT, 16 * rt + c16, 32 * kb), qr[kb][dt]);
+        for (int kb = 0; kb < 2; ++kb) mma(pq, ld_frag(slotE(SGP), LT, 16 * rt + c16, 32 * kb), qr[kb][dt]);
         const f32x4 kv4 = ld_cpiece<E>(sK, LK, 16 * rt, d0 + 16 * dt);
         const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&s.Gam[16 * rt + 4 * g]);
         const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&s.bg[16 * rt + 4 * g]);
@@ -946,7 +951,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       }
     }
   }
-  // dQ = scale diag(Gam) dQ1 + GPM K, final here (slot dO was last read in P7)
+  // dQ = scale diag(Gam) dQ1 + GPM K, final here (slot dO was last read in P6)
   {
     E* sDQ = slotE(SDO);
 #pragma unroll
@@ -957,15 +962,14 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         f32x4 a = zero4();
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          mma(a, ld_fragC_q<E>(sPT, LT, 32 * kb, 16 * rt), ld_fragC_q<E>(sK, LK, 32 * kb, d0 + 16 * dt));
+          mma(a, ld_fragC_q<E>(slotE(SGP), LT, 32 * kb, 16 * rt), ld_fragC_q<E>(sK, LK, 32 * kb, d0 + 16 * dt));
         const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&s.Gam[16 * rt + 4 * g]);
         st_tile_rows<E>(sDQ, LK, 16 * rt, d0 + 16 * dt, dq1[j][dt] * gm4 * scale + a);
       }
   }
-  __syncthreads();
 
-  // ---- P9: GT = dU V^T diag(beta) + GW K^T diag(beta Gam) -> slot V as GT^T
-  //          (PMat; U was last read in P7).  The dbeta term
+  // ---- P9 (same phase): GT = dU V^T diag(beta) + GW K^T diag(beta Gam) -> slot
+  //          V as GT^T (PMat; U was last read in P6).  The dbeta term
   //          sum_c (T^T dU)[r][c] V[r][c] is the column sum
   //          sum_i T[i][r] (dU V^T)[i][r], taken here from the first product.
   const PMat<E> GTT(s.slot[SV]);
@@ -998,8 +1002,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   __syncthreads();
 
   // ---- P10: Z = GT T^T (own row tiles, column tile cw) -> slot P as Z^T (last
-  //           read in P8), GA = strict_lower(-T^T Z) (own rows); E -> slot E
-  //           as E^T.  XU = T^T dU (own rows and value columns) -> dV into
+  //           read in P5), GA = strict_lower(-T^T Z) (own rows); E -> slot dU
+  //           as E^T (dU^T is last read before the barrier in the middle).  XU = T^T dU (own rows and value columns) -> dV into
   //           slot Q (GW^T was last read in P9).  The rows of T^T for this
   //           wave's row tiles serve XU (in E) and GA (near fp32).
   PFrag<E> ttp[2][2];
@@ -1068,7 +1072,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
         rb[j][i] += gav * kd4[i];
         ev[i] = (c < r) ? s.beta[r] * gav * __expf(s.gam[r] - s.gam[c]) : 0.f;
       }
-      st_tile_cm<E>(slotE(SE), LT, 16 * rt, 16 * cw, ev);
+      st_tile_cm<E>(sDUT, LT, 16 * rt, 16 * cw, ev);
     }
     csum += __shfl_xor(csum, 16, 64);
     csum += __shfl_xor(csum, 32, 64);
@@ -1082,7 +1086,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   //           behind a store.
   {
     E* sDK = slotE(SKD);
-    const E* sET = slotE(SE);
+    const E* sET = sDUT;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
