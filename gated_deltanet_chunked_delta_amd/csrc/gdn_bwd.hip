@@ -583,26 +583,26 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   E* sPT = slotE(SP);                                           // scale P^T
   E* sDUT = slotE(SDU);                                         // dU^T
 
-  // e_r = ek_r k_r.(U dh'^T)_r, the reverse chain's row terms (summed here over
-  // its waves): it enters dgam_r with a minus sign and the last row with a plus,
-  // so dg_r gets sum_{i < r} e_i, formed as a prefix sum (adding and then
-  // cancelling it leaves a rounding residue that strong decay would make larger
-  // than dg itself).  Read now, used at the end.
-  float epv[RevWaves<DV>::NW];
+  // ---- P1: staging, in the order the phases need it: the scalar record (wave
+  //          0) and K, Q (waves 0..3 and 4..7) are requested first and stored
+  //          before the first barrier; U, dO (waves 0..3 and 4..7) and T stay
+  //          in flight during P2 and are stored at its end.  Rows past the end
+  //          are zero.
+  const int ht = tid & (NT / 2 - 1);
+  typedef E vec_t __attribute__((__vector_size__(16)));
+  constexpr int UVEC = 16 / (int)sizeof(E), UPC = CH * DV / UVEC / (NT / 2);  // U pieces per thread
+  constexpr int TPT = CH * CH / (4 * NT);
+  vec_t upc[UPC];
+  TilePart<E, NT / 2, DV> td;
+  f32x4 tvals[TPT];
   {
-    const float* ep = p.ep + ((size_t)blockIdx.x * H + h) * (EPW * CH);
-#pragma unroll
-    for (int ww = 0; ww < RevWaves<DV>::NW; ++ww) epv[ww] = w == 0 ? ep[ww * CH + l] : 0.f;
-  }
-
-  // ---- P1: staging (all four tiles in flight at once; rows past the end are
-  //          zero); T (unless given) split into its bf16 parts; zero the
-  //          cross-wave sum arrays.  dh' down this wave's value columns (the
-  //          operand of P5) is requested after the tiles have landed and stays
-  //          in flight until P5, where quad transposes turn its row pieces into
-  //          columns; its products use the contiguous k-slot order.
-  RawFrag<E> dkraw[P5C][DK / 32];
-  {
+    float gr = 0.f, bt = 0.f;
+    const bool valid = l < rows;
+    if (w == 0 && valid) {
+      const int64_t si = (tok0 + l) * H + h;
+      gr = p.g[si];
+      bt = to_f(static_cast<const E*>(p.beta)[si]);
+    }
     const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
     const E* k = static_cast<const E*>(p.k) + (tok0 * H + h) * DK;
     // U of this chunk as the forward (or its replay) formed it: DV/16 column
@@ -610,25 +610,15 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     // of the whole [CH x DV] matrix sits at element 16 i / sizeof(E)
     const E* u = static_cast<const E*>(p.us) + ((size_t)blockIdx.x * H + h) * (CH * DV);
     const E* d = static_cast<const E*>(p.dout) + (tok0 * H + h) * DV;
-    // waves 0..3 bring K and Q, waves 4..7 U and dO
-    const int ht = tid & (NT / 2 - 1);
-    TilePart<E, NT / 2, DK> tk, tq;
-    TilePart<E, NT / 2, DV> td;
-    typedef E vec_t __attribute__((__vector_size__(16)));
-    constexpr int UVEC = 16 / (int)sizeof(E), UPC = CH * DV / UVEC / (NT / 2);  // pieces per thread
-    vec_t upc[UPC];
+    TilePart<E, NT / 2, DK> tkq;
+    tkq.template load<true>(rh == 0 ? k : q, (int64_t)H * DK, rows, ht);
     if (rh == 0) {
-      tk.template load<true>(k, (int64_t)H * DK, rows, ht);
-      tq.template load<true>(q, (int64_t)H * DK, rows, ht);
-    } else {
 #pragma unroll
       for (int i = 0; i < UPC; ++i) upc[i] = *reinterpret_cast<const vec_t*>(u + (ht + i * (NT / 2)) * UVEC);
+    } else {
       td.template load<true>(d, (int64_t)H * DV, rows, ht);
     }
-    // T (requested after the tiles)
-    constexpr int TPT = CH * CH / (4 * NT);
     const float* tin = p.t_in + ((size_t)blockIdx.x * H + h) * (CH * CH);
-    f32x4 tvals[TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) tvals[i] = *reinterpret_cast<const f32x4*>(tin + 4 * (tid + i * NT));
     for (int e = tid; e < 4 * CH; e += NT) {
@@ -636,10 +626,6 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       (&s.c7[0][0])[e] = 0.f;
     }
     if (w == 0) {
-      const bool valid = l < rows;
-      const int64_t si = (tok0 + l) * H + h;
-      float gr = valid ? p.g[si] : 0.f;
-      float bt = valid ? to_f(static_cast<const E*>(p.beta)[si]) : 0.f;
       if (PREP && p.prep.gate_act && valid) {
         gr = -(p.prep.gate_scale ? p.prep.gate_scale[h] : 1.f) * softplus_f(gr);
         bt = sigmoid_f(bt);
@@ -654,33 +640,14 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       s.bg[l] = bt * Gm;
       if (l == 0) s.GamC = __expf(gC);
     }
-    if (PREP && p.prep.qk_norm && rh == 0) {
-      tk.normalize_rows(ht);
-      tq.normalize_rows(ht);
-    }
-    if (rh == 0) {
-      tk.store(sK, LK, nullptr, 0, ht);
-      tq.store(slotE(SQ), LK, nullptr, 0, ht);
-    } else {
-#pragma unroll
-      for (int i = 0; i < UPC; ++i) {
-        const int pc = ht + i * (NT / 2);            // piece index
-        const int blk = pc / (CH * 16 / UVEC);       // column block
-        const int r = (pc % (CH * 16 / UVEC)) / (16 / UVEC), c = blk * 16 + (pc % (16 / UVEC)) * UVEC;
-        *reinterpret_cast<vec_t*>(slotE(SV) + r * LV + c) = upc[i];
-      }
-      td.store(slotE(SDO), LV, nullptr, 0, ht);
-    }
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int e = 4 * (tid + i * NT);
-      Tm.put4(e >> 6, e & 63, tvals[i]);
-    }
+    if (PREP && p.prep.qk_norm) tkq.normalize_rows(ht);
+    tkq.store(rh == 0 ? sK : slotE(SQ), LK, nullptr, 0, ht);
   }
   __syncthreads();
-  // dh' down this wave's P5 value columns, requested only now: every
-  // workgroup stages its tiles at about the same time, and the tiles arrive
-  // sooner without the state queued beside them
+  // dh' down this wave's P5 value columns, requested now (behind the tiles
+  // still in flight): quad transposes in P5 turn its row pieces into columns;
+  // its products use the contiguous k-slot order
+  RawFrag<E> dkraw[P5C][DK / 32];
 #pragma unroll
   for (int nt = 0; nt < P5C; ++nt)
 #pragma unroll
@@ -755,6 +722,23 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       const int rt = w < 3 ? 0 : (w < 5 ? 1 : 2), ct = w < 3 ? w + 1 : (w < 5 ? w - 1 : 3);
       st_tile_cm<E>(sPT, LT, 16 * rt, 16 * ct, zero4());
     }
+  }
+  // the rest of the staging: U, dO and T (split into its bf16 parts)
+  if (rh == 0) {
+#pragma unroll
+    for (int i = 0; i < UPC; ++i) {
+      const int pc = ht + i * (NT / 2);            // piece index
+      const int blk = pc / (CH * 16 / UVEC);       // column block
+      const int r = (pc % (CH * 16 / UVEC)) / (16 / UVEC), c = blk * 16 + (pc % (16 / UVEC)) * UVEC;
+      *reinterpret_cast<vec_t*>(slotE(SV) + r * LV + c) = upc[i];
+    }
+  } else {
+    td.store(slotE(SDO), LV, nullptr, 0, ht);
+  }
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int e = 4 * (tid + i * NT);
+    Tm.put4(e >> 6, e & 63, tvals[i]);
   }
   __syncthreads();
 
@@ -1079,6 +1063,18 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     if (g == 0) s.c10[rh][c] = -csum;
   }
   __syncthreads();
+
+  // e_r = ek_r k_r.(U dh'^T)_r, the reverse chain's row terms (summed here over
+  // its waves): it enters dgam_r with a minus sign and the last row with a plus,
+  // so dg_r gets sum_{i < r} e_i, formed as a prefix sum (adding and then
+  // cancelling it leaves a rounding residue that strong decay would make larger
+  // than dg itself).  Wave 0's, for the end.
+  float epv[RevWaves<DV>::NW];
+  {
+    const float* ep = p.ep + ((size_t)blockIdx.x * H + h) * (EPW * CH);
+#pragma unroll
+    for (int ww = 0; ww < RevWaves<DV>::NW; ++ww) epv[ww] = w == 0 ? ep[ww * CH + l] : 0.f;
+  }
 
   // ---- P11: dK = dK partial + (E + E^T) K (own rows and key columns) -> slot KD
   //           (last read in P10).  The three gradient tiles are written out
