@@ -189,8 +189,12 @@ size_t gdn_chunk_states_bytes(const gdn_common_args* a);
  * without error when there are no tokens). */
 size_t gdn_chunk_t_bytes(const gdn_common_args* a);
 
-/* Forward: o and (optionally) hT, the chunk states and the chunk matrices T.
- * stream is a hipStream_t (NULL = default stream). */
+/* Forward: o and (optionally) hT, the chunk states and the chunk matrices T
+ * -- the chunked prefill forward pass ("FlashQLA resource", section 2 "What It
+ * Actually Is", and section 3 for the reformulated chunk form and the
+ * intra-card splitting; "Qwen's FlashQLA targets the expensive bit of
+ * long-context AI", section "What happened").  stream is a hipStream_t (NULL =
+ * default stream). */
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream);
 
 /* Bytes of the scratch array gdn_chunk_fwd_noalloc uses in place of a workspace. */
@@ -219,9 +223,12 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* args, void* stream);
 gdn_status gdn_chunk_fwd_noalloc(const gdn_fwd_args* args, void* stream);
 
 /* Backward: gradients of <do, o> + <dhT, hT> with respect to q, k, v, beta, g
- * and (optionally) h0.  It recomputes the forward states from the inputs
- * unless h_saved provides them, and solves for each chunk's T once unless
- * t_saved provides them. */
+ * and (optionally) h0 -- the matching backward pass ("FlashQLA resource",
+ * section 2, and section 5 for its intra-card splitting; "Qwen's FlashQLA
+ * targets the expensive bit of long-context AI", section "What happened").  It
+ * recomputes the forward states from the inputs unless h_saved provides them,
+ * and solves for each chunk's T once unless t_saved provides them.  stream as
+ * for gdn_chunk_fwd. */
 gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream);
 
 /* One recurrent decode step: every listed sequence takes one new token and
