@@ -46,15 +46,23 @@
 
 namespace gdn {
 
+// Every tile is row-major.  Products that need the columns of K or V read them
+// with LDS transpose loads, from copies whose bf16 rows are padded by 16
+// elements (which keeps the transpose loads free of bank conflicts); the
+// tiles read along their rows (Q, W, P, T, and K once more for Q K^T) are
+// padded by 4, where 8-byte row reads run at full rate and 16 would not.
 template <class E, int DK, int DV>
 struct alignas(16) FwdSmem {
-  static constexpr int LQ = ldpad<E>(DK);                 // sQ, sK, sW row stride
-  static constexpr int LT = ldpad<E>(CH);                 // transposed tiles, P, scaled T
+  static constexpr int LQ = ldpad<E>(DK);                 // sQ, sKR, sW row stride
+  static constexpr int LT = ldpad<E>(CH);                 // P, scaled T
   static constexpr int LO = DV + 16 / (int)sizeof(E);     // output staging (16-byte rows)
+  static constexpr int PADC = sizeof(E) == 2 ? 16 : 4;    // tiles read through transpose loads
+  static constexpr int LK = DK + PADC;
+  static constexpr int LV = DV + PADC;
   E Q[CH * LQ];
-  E K[CH * LQ];
-  E KT[DK * LT];
-  E VT[DV * LT];
+  E KR[CH * LQ];  // K, for its rows
+  E K[CH * LK];   // K, for its columns
+  E V[CH * LV];
   E W[CH * LQ];   // holds -W
   E P[CH * LT];
   E TBG[CH * LT];  // T diag(beta Gam), the X operand of W
@@ -68,8 +76,8 @@ struct alignas(16) FwdSmem {
 
 // The raw tiles of one chunk, held in registers between the global load and
 // the LDS store so that the next chunk's loads overlap the current chunk's
-// compute.  K and V move as 4-row x 16-byte blocks (K is stored row-major and
-// transposed, V transposed); Q as single 16-byte vectors (row-major).
+// compute.  K and V move as 4-row x 16-byte blocks, Q as single 16-byte
+// vectors, all stored row-major (K twice, at the two strides).
 template <class E, int DK, int DV, int NT, bool NEED_Q, bool NEED_V, bool PREP>
 struct TileLoader {
   static constexpr int VEC = 16 / (int)sizeof(E);
@@ -174,18 +182,18 @@ struct TileLoader {
         const int loc = isk ? id : id - NBK;
         const int D = isk ? DK : DV;
         const int r0 = (loc / (D / VEC)) * 4, c0 = (loc % (D / VEC)) * VEC;
-        E* dT = isk ? s.KT : s.VT;
-        if (isk) {
+        E* dst = isk ? s.K : s.V;
+        const int ld = isk ? S::LK : S::LV;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<vec_t*>(dst + (r0 + j) * ld + c0) = blk[b][j];
+        if (NEED_Q && isk) {  // the row copy serves Q K^T, which only the forward proper forms
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < VEC; e += 4)
-              st4<E>(s.K + (r0 + j) * S::LQ + c0 + e, blk[b][j][e], blk[b][j][e + 1], blk[b][j][e + 2],
+              st4<E>(s.KR + (r0 + j) * S::LQ + c0 + e, blk[b][j][e], blk[b][j][e + 1], blk[b][j][e + 2],
                      blk[b][j][e + 3]);
         }
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          st4<E>(dT + (c0 + e) * S::LT + r0, blk[b][0][e], blk[b][1][e], blk[b][2][e], blk[b][3][e]);
       }
     }
 #pragma unroll
@@ -227,7 +235,7 @@ struct Chunk {
     f32x4 acc = zero4();
 #pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb)
-      mma(acc, ld_frag(sp->Q, LQ, 16 * rt + c16, 32 * kb), ld_frag(sp->K, LQ, 16 * ct + c16, 32 * kb));
+      mma(acc, ld_frag(sp->Q, LQ, 16 * rt + c16, 32 * kb), ld_frag(sp->KR, LQ, 16 * ct + c16, 32 * kb));
     const f32x4 gr4 = *reinterpret_cast<const f32x4*>(&sp->gam[16 * rt + 4 * g]);
     const int c = 16 * ct + c16;
     const float gc = sp->gam[c];
@@ -318,7 +326,7 @@ struct Chunk {
         const int ct = ct0 + cc;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(acc, xw[kb], ld_frag(sp->KT, LT, 16 * ct + c16, 32 * kb));
+        for (int kb = 0; kb < 2; ++kb) mma(acc, xw[kb], ld_fragC_q<E>(sp->K, S::LK, 32 * kb, 16 * ct));
 #pragma unroll
         for (int i = 0; i < 4; ++i) sp->W[(16 * rt + 4 * g + i) * LQ + 16 * ct + c16] = to_e<E>(-acc[i]);
       }
@@ -331,7 +339,7 @@ struct Chunk {
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) yv[nt][kb] = ld_frag(sp->VT, LT, n0 + 16 * nt + c16, 32 * kb);
+        for (int kb = 0; kb < 2; ++kb) yv[nt][kb] = ld_fragC_q<E>(sp->V, S::LV, 32 * kb, n0 + 16 * nt);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         Frag<E> xb[2];
@@ -434,7 +442,7 @@ struct Chunk {
         for (int t = 0; t < DK / 16; ++t) {
           hacc[t][nt] = hacc[t][nt] * gc;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) mma(hacc[t][nt], ld_frag(sp->KT, LT, 16 * t + c16, 32 * kb), us[kb]);
+          for (int kb = 0; kb < 2; ++kb) mma(hacc[t][nt], ld_fragC_q<E>(sp->K, S::LK, 32 * kb, 16 * t), us[kb]);
         }
       }
     }
