@@ -48,19 +48,25 @@ namespace gdn {
 
 // ======================================================================== reverse chain
 
+// Every staged tile is row-major.  Products that need the columns of K, of
+// diag(scale Gam) Q or of dO read them with LDS transpose loads, from copies
+// whose bf16 rows are padded by 16 elements (conflict-free for transpose
+// loads); tiles read along their rows are padded by 4 (where 8-byte row reads
+// run at full rate).
 template <class E, int DK, int DV>
 struct alignas(16) RevSmem {
   static constexpr int LQ = ldpad<E>(DK);
   static constexpr int LT = ldpad<E>(CH);
-  static constexpr int LA = CH + 4;
+  static constexpr int PADC = sizeof(E) == 2 ? 16 : 4;
+  static constexpr int LKC = DK + PADC, LDO = DV + PADC;
   E Q[CH * LQ];    // row-major, X of Q K^T
   E K[CH * LQ];    // row-major, X/Y of K K^T, X of K dh'
-  E KT[DK * LT];   // K^T diag(beta Gam), X of W^T
-  E QT[DK * LT];   // Q^T diag(scale Gam) (zero past the sequence end), X of (Gam Q)^T dO
-  E DOT[DV * LT];  // dO^T, Y of P^T dO and (Gam Q)^T dO
+  E KC[CH * LKC];  // K again, read down its columns (X of W^T)
+  E QS[CH * LKC];  // diag(scale Gam) Q (zero past the sequence end), read down its columns (X of (Gam Q)^T dO)
+  E DO[CH * LDO];  // dO, read down its columns (Y of P^T dO and (Gam Q)^T dO)
   E WT[DK * LT];   // -W^T
   E PT[CH * LT];   // scale * P^T
-  float T[CH * LA];
+  E TBG[CH * LT];  // T diag(beta Gam), Y of W^T
   // the chunk's scalar record, as laid out in memory (tail: Lambda_c, Gam_C)
   alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], tail[4];
 };
@@ -85,8 +91,8 @@ struct RevChunk {
     TilePart<E, KQT, DK> kq;
     TilePart<E, NT, DV> d;
     RecordPart rec;
-    // the row scales of the transposed K (beta Gam) and Q (scale Gam, zero past
-    // the sequence end) copies, one per kq block
+    // the row scales of the second Q copy (scale Gam, zero past the sequence
+    // end), one per kq block
     f32x4 sc[TilePart<E, KQT, DK>::NB > 0 ? TilePart<E, KQT, DK>::NB : 1];
   };
   __device__ __forceinline__ static bool q_half() { return threadIdx.x >= KQT; }
@@ -104,9 +110,9 @@ struct RevChunk {
     for (int b = 0; b < NBK; ++b) {
       const int r0 = TilePart<E, KQT, DK>::block_row(b, kq_tid());
       if (r0 >= 0) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(rec + (qh ? CH : 4 * CH) + r0);  // Gam or beta Gam
+        const f32x4 v = *reinterpret_cast<const f32x4*>(rec + CH + r0);  // Gam
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ld.sc[b][i] = qh ? (r0 + i < rows ? p.scale * v[i] : 0.f) : v[i];
+        for (int i = 0; i < 4; ++i) ld.sc[b][i] = qh && r0 + i < rows ? p.scale * v[i] : 0.f;
       }
     }
   }
@@ -126,8 +132,9 @@ struct RevChunk {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rt + 4 * g + i;
-      sp->PT[c * LT + r] = to_e<E>((c <= r && r < rows) ? p.scale * acc[i] * __expf(gr4[i] - gc) : 0.f);
+      acc[i] = (c <= r && r < rows) ? p.scale * acc[i] * __expf(gr4[i] - gc) : 0.f;
     }
+    st_tile_cm<E>(sp->PT, LT, 16 * rt, 16 * ct, acc);
   }
 
   // dh: gradient at the chunk end on entry, at the chunk start on exit.
@@ -147,7 +154,7 @@ struct RevChunk {
   __device__ static void step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows, int h,
                               E* dhs_chunk, const float* t_in, const float* nrec, const E* us_chunk,
                               const E* ulo_chunk, float* ep_chunk, f32x4 (&dh)[DK / 16][NTW]) {
-    constexpr int LQ = S::LQ, LT = S::LT, LA = S::LA;
+    constexpr int LQ = S::LQ, LT = S::LT;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     constexpr bool LO = std::is_same<E, bf16>::value;  // U and dS' need their residuals
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
@@ -178,9 +185,10 @@ struct RevChunk {
     if (PREP && p.prep.qk_norm) ld.kq.normalize_rows(kq_tid());
     {
       const bool qh = q_half();
-      ld.kq.store_scaledT(qh ? s1.Q : s1.K, LQ, qh ? s1.QT : s1.KT, LT, ld.sc, kq_tid());
+      if (qh) ld.kq.template store_rows2<true>(s1.Q, LQ, s1.QS, S::LKC, ld.sc, kq_tid());
+      else ld.kq.template store_rows2<false>(s1.K, LQ, s1.KC, S::LKC, ld.sc, kq_tid());
     }
-    ld.d.store(nullptr, 0, s1.DOT, LT);
+    ld.d.store_rows16(s1.DO, S::LDO);
     static_assert(offsetof(S, tail) == offsetof(S, gam) + 5 * CH * sizeof(float), "record layout");
     ld.rec.store(s1.gam);
     __syncthreads();
@@ -206,7 +214,8 @@ struct RevChunk {
 #pragma unroll
       for (int i = 0; i < TPT; ++i) {
         const int e = 4 * (tid + i * NT);
-        *reinterpret_cast<f32x4*>(&s.T[(e / CH) * LA + e % CH]) = tv[i];
+        const int r = e / CH, c = e % CH;
+        st4f<E>(&s.TBG[r * LT + c], tv[i] * *reinterpret_cast<const f32x4*>(&s.bg[c]));
       }
     }
     __syncthreads();
@@ -226,13 +235,13 @@ struct RevChunk {
 #pragma unroll
       for (int rr = 0; rr < RTW; ++rr)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) yt[rr][kb] = ld_frag_f32<E>(s.T, LA, 16 * (rt0 + rr) + c16, 32 * kb);
+        for (int kb = 0; kb < 2; ++kb) yt[rr][kb] = ld_frag(s.TBG, LT, 16 * (rt0 + rr) + c16, 32 * kb);
 #pragma unroll
       for (int dd = 0; dd < KTW; ++dd) {
         const int dt = kt0 + dd;
         Frag<E> xk[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) xk[kb] = ld_frag(s.KT, LT, 16 * dt + c16, 32 * kb);
+        for (int kb = 0; kb < 2; ++kb) xk[kb] = ld_fragC_q<E>(s.KC, S::LKC, 32 * kb, 16 * dt);
 #pragma unroll
         for (int rr = 0; rr < RTW; ++rr) {
           f32x4 acc = zero4();
@@ -261,7 +270,7 @@ struct RevChunk {
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) yd[nt][kb] = ld_frag(s.DOT, LT, n0 + 16 * nt + c16, 32 * kb);
+        for (int kb = 0; kb < 2; ++kb) yd[nt][kb] = ld_fragC_q<E>(s.DO, S::LDO, 32 * kb, n0 + 16 * nt);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         Frag<E> xk[DK / 32];
@@ -312,7 +321,7 @@ struct RevChunk {
           dh[t][nt] = dh[t][nt] * gc;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            mma(dh[t][nt], ld_frag(s.QT, LT, 16 * t + c16, 32 * kb), yd[nt][kb]);
+            mma(dh[t][nt], ld_fragC_q<E>(s.QS, S::LKC, 32 * kb, 16 * t), yd[nt][kb]);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) mma(dh[t][nt], ld_frag(s.WT, LT, 16 * t + c16, 32 * kb), uf[kb]);
         }
@@ -389,11 +398,8 @@ __device__ void rev_store(const f32x4 (&acc)[DK / 16][DV / (16 * RevWaves<DV>::N
 template <class E, int DK, int DV>
 __device__ void rev_init_smem(RevSmem<E, DK, DV>& s) {
   using Sm = RevSmem<E, DK, DV>;
-  // T's strictly-upper blocks and the tiles of P^T above the diagonal are never written
-  for (int e = threadIdx.x; e < CH * CH; e += blockDim.x) {
-    s.T[(e >> 6) * Sm::LA + (e & 63)] = 0.f;
-    s.PT[(e >> 6) * Sm::LT + (e & 63)] = to_e<E>(0.f);
-  }
+  // the tiles of P^T above the diagonal are never written
+  for (int e = threadIdx.x; e < CH * CH; e += blockDim.x) s.PT[(e >> 6) * Sm::LT + (e & 63)] = to_e<E>(0.f);
   __syncthreads();
 }
 

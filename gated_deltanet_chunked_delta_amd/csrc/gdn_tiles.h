@@ -195,24 +195,42 @@ struct TilePart {
       }
     }
   }
-  // store() with the transposed copy's rows r0 .. r0 + 3 of block b scaled by
-  // sc[b][0 .. 3] (computed in fp32, rounded once); the row-major copy is as loaded.
-  __device__ __forceinline__ void store_scaledT(E* dst, int ld, E* dstT, int ldT, const f32x4 (&sc)[NB > 0 ? NB : 1],
-                                                int tid = threadIdx.x) const {
+  // The tile row-major twice: as loaded at dst (8-byte stores, any stride)
+  // and at dst2 (16-byte stores: ld2 * sizeof(E) a multiple of 16), the rows
+  // r0 .. r0 + 3 of block b of the second copy scaled by sc[b][0 .. 3] when
+  // SCALE2 (computed in fp32, rounded once).
+  template <bool SCALE2>
+  __device__ __forceinline__ void store_rows2(E* dst, int ld, E* dst2, int ld2, const f32x4 (&sc)[NB > 0 ? NB : 1],
+                                              int tid = threadIdx.x) const {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int id = tid + b * NT;
       if (NB * NT == NBLK || id < NBLK) {
         const int r0 = (id / BPR) * 4, c0 = (id % BPR) * VEC;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
 #pragma unroll
           for (int e = 0; e < VEC; e += 4)
             st4<E>(dst + (r0 + j) * ld + c0 + e, blk[b][j][e], blk[b][j][e + 1], blk[b][j][e + 2], blk[b][j][e + 3]);
+          vec_t v = blk[b][j];
+          if (SCALE2) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          st4<E>(dstT + (c0 + e) * ldT + r0, to_e<E>(to_f(blk[b][0][e]) * sc[b][0]), to_e<E>(to_f(blk[b][1][e]) * sc[b][1]),
-                 to_e<E>(to_f(blk[b][2][e]) * sc[b][2]), to_e<E>(to_f(blk[b][3][e]) * sc[b][3]));
+            for (int e = 0; e < VEC; ++e) v[e] = to_e<E>(to_f(v[e]) * sc[b][j]);
+          }
+          *reinterpret_cast<vec_t*>(dst2 + (r0 + j) * ld2 + c0) = v;
+        }
+      }
+    }
+  }
+  // The tile row-major with 16-byte stores (ld * sizeof(E) a multiple of 16).
+  __device__ __forceinline__ void store_rows16(E* dst, int ld, int tid = threadIdx.x) const {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int id = tid + b * NT;
+      if (NB * NT == NBLK || id < NBLK) {
+        const int r0 = (id / BPR) * 4, c0 = (id % BPR) * VEC;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<vec_t*>(dst + (r0 + j) * ld + c0) = blk[b][j];
       }
     }
   }
