@@ -87,33 +87,37 @@ struct RevChunk {
   // the first half of the threads holds K and the second half Q (one register
   // set, kq), and dO sits on the first NT / 2 * (DV / DK) threads.
   static constexpr int KQT = NT / 2;  // threads per K (or Q) tile
+  static constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
+  static_assert(TPT * 4 * NT == CH * CH && (4 * NT) % CH == 0, "whole rows of T per pass");
   struct Loader {
     TilePart<E, KQT, DK> kq;
     TilePart<E, NT, DV> d;
     RecordPart rec;
-    // the row scales of the second Q copy (scale Gam, zero past the sequence
-    // end), one per kq block
+    // this thread's pieces of T (piece i at element 4 (tid + i NT)) and beta Gam
+    // of their columns (the same columns for every piece)
+    f32x4 tv[TPT], tbg;
+    // Gam of the rows of each kq block (Q half), as loaded: the scaling waits
+    // for the staging, so that nothing waits for these loads meanwhile
     f32x4 sc[TilePart<E, KQT, DK>::NB > 0 ? TilePart<E, KQT, DK>::NB : 1];
   };
   __device__ __forceinline__ static bool q_half() { return threadIdx.x >= KQT; }
   __device__ __forceinline__ static int kq_tid() { return threadIdx.x & (KQT - 1); }
 
-  __device__ static void issue(Loader& ld, const RevParams& p, int64_t tok0, int rows, int h, const float* rec) {
+  __device__ static void issue(Loader& ld, const RevParams& p, int64_t tok0, int rows, int h, const float* rec,
+                              const float* t) {
     const int H = p.H;
     const void* src = q_half() ? p.q : p.k;
     ld.kq.load(static_cast<const E*>(src) + (tok0 * H + h) * DK, (int64_t)H * DK, rows, kq_tid());
     ld.d.load(static_cast<const E*>(p.dout) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
     ld.rec.load(rec);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) ld.tv[i] = *reinterpret_cast<const f32x4*>(t + 4 * (threadIdx.x + i * NT));
+    ld.tbg = *reinterpret_cast<const f32x4*>(rec + 4 * CH + (4 * threadIdx.x) % CH);
     constexpr int NBK = TilePart<E, KQT, DK>::NB;
-    const bool qh = q_half();
 #pragma unroll
     for (int b = 0; b < NBK; ++b) {
       const int r0 = TilePart<E, KQT, DK>::block_row(b, kq_tid());
-      if (r0 >= 0) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(rec + CH + r0);  // Gam
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ld.sc[b][i] = qh && r0 + i < rows ? p.scale * v[i] : 0.f;
-      }
+      if (q_half() && r0 >= 0) ld.sc[b] = *reinterpret_cast<const f32x4*>(rec + CH + r0);  // Gam
     }
   }
 
@@ -138,8 +142,8 @@ struct RevChunk {
   }
 
   // dh: gradient at the chunk end on entry, at the chunk start on exit.
-  // Prefetches chunk (ntok0, nrows) into ld (nrows = 0: none).  Returns Lambda_c.
-  // t_in: this chunk's T; nrec: the next chunk's scalar record.  LEAD: a
+  // Prefetches chunk (ntok0, nrows) into ld (nrows = 0: none).
+  // nt_in, nrec: the next chunk's T and scalar record.  LEAD: a
   // lead-in chunk after the segment proper, which only advances the gradient
   // (nothing is written).
   //
@@ -152,10 +156,9 @@ struct RevChunk {
   // residual (us_chunk, ulo_chunk).
   template <bool LEAD>
   __device__ static void step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows, int h,
-                              E* dhs_chunk, const float* t_in, const float* nrec, const E* us_chunk,
+                              E* dhs_chunk, const float* nt_in, const float* nrec, const E* us_chunk,
                               const E* ulo_chunk, float* ep_chunk, f32x4 (&dh)[DK / 16][NTW]) {
     constexpr int LQ = S::LQ, LT = S::LT;
-    constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     constexpr bool LO = std::is_same<E, bf16>::value;  // U and dS' need their residuals
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
     const int n0 = w * (DV / NW);
@@ -183,22 +186,36 @@ struct RevChunk {
     }
     S& s1 = *sp;
     if (PREP && p.prep.qk_norm) ld.kq.normalize_rows(kq_tid());
-    {
-      const bool qh = q_half();
-      if (qh) ld.kq.template store_rows2<true>(s1.Q, LQ, s1.QS, S::LKC, ld.sc, kq_tid());
-      else ld.kq.template store_rows2<false>(s1.K, LQ, s1.KC, S::LKC, ld.sc, kq_tid());
+    if (q_half()) {
+      // the second Q copy's row scales: scale Gam, zero past the sequence end
+      constexpr int NBK = TilePart<E, KQT, DK>::NB;
+      f32x4 sc[NBK > 0 ? NBK : 1];
+#pragma unroll
+      for (int b = 0; b < NBK; ++b) {
+        const int r0 = TilePart<E, KQT, DK>::block_row(b, kq_tid());
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[b][i] = r0 + i < rows ? p.scale * ld.sc[b][i] : 0.f;
+      }
+      ld.kq.template store_rows2<true>(s1.Q, LQ, s1.QS, S::LKC, sc, kq_tid());
+    } else {
+      ld.kq.template store_rows2<false>(s1.K, LQ, s1.KC, S::LKC, ld.sc, kq_tid());
     }
     ld.d.store_rows16(s1.DO, S::LDO);
+    // T lands as T diag(beta Gam) (computed in fp32, rounded once)
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int e = 4 * (tid + i * NT), r = e / CH, c = e % CH;
+      st4f<E>(&s1.TBG[r * LT + c], ld.tv[i] * ld.tbg);
+    }
     static_assert(offsetof(S, tail) == offsetof(S, gam) + 5 * CH * sizeof(float), "record layout");
     ld.rec.store(s1.gam);
     __syncthreads();
 
-    // ---- 2. Q K^T -> scale P^T: the ten lower 16x16 tiles, tile j on wave j % NW
-    //         (at most two tiles a wave with eight waves).  T is requested now,
-    //         past the staging, and lands in LDS at the end of this phase.
-    f32x4 tv[TPT];
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
+    // ---- 2. the next chunk's tiles, T and record start their way from HBM
+    if (nrows > 0) issue(ld, p, ntok0, nrows, h, nrec, nt_in);
+
+    // ---- 3. Q K^T -> scale P^T: the ten lower 16x16 tiles, tile j on wave j % NW
+    //         (at most two tiles a wave with eight waves)
     {
       S* sq = lds_opaque(&s0);
 #pragma unroll
@@ -209,19 +226,7 @@ struct RevChunk {
         if (pid < 10) pt_tile(sq, p, rt, ct, g, c16, rows);
       }
     }
-    {
-      S& s = *lds_opaque(&s0);
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) {
-        const int e = 4 * (tid + i * NT);
-        const int r = e / CH, c = e % CH;
-        st4f<E>(&s.TBG[r * LT + c], tv[i] * *reinterpret_cast<const f32x4*>(&s.bg[c]));
-      }
-    }
-    __syncthreads();
-
-    // ---- 3. the next chunk's tiles start their way from HBM
-    if (nrows > 0) issue(ld, p, ntok0, nrows, h, nrec);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- 4. -W^T = -K^T diag(beta Gam) T^T: (Dk/16) x 4 tiles, KTW key tiles x
     //         RTW chunk-row tiles per wave
@@ -242,13 +247,14 @@ struct RevChunk {
         Frag<E> xk[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) xk[kb] = ld_fragC_q<E>(s.KC, S::LKC, 32 * kb, 16 * dt);
+        // W itself (chunk rows, key columns), stored transposed: each lane
+        // writes four consecutive entries of a row of -W^T at once
 #pragma unroll
         for (int rr = 0; rr < RTW; ++rr) {
           f32x4 acc = zero4();
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) mma(acc, xk[kb], yt[rr][kb]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s.WT[(16 * dt + 4 * g + i) * LT + 16 * (rt0 + rr) + c16] = to_e<E>(-acc[i]);
+          for (int kb = 0; kb < 2; ++kb) mma(acc, yt[rr][kb], xk[kb]);
+          st_tile_cm<E>(s.WT, LT, 16 * (rt0 + rr), 16 * dt, -acc);
         }
       }
     }
@@ -335,7 +341,9 @@ struct RevChunk {
   __device__ static void prime(Loader& ld, const RevParams& p, int64_t seq0, int len, int64_t chunk0, int cb, int we,
                                int h) {
     const int c = we - 1;
-    if (c >= cb) issue(ld, p, seq0 + (int64_t)c * CH, min(CH, len - c * CH), h, p.rec + ((chunk0 + c) * p.H + h) * RECF);
+    if (c >= cb)
+      issue(ld, p, seq0 + (int64_t)c * CH, min(CH, len - c * CH), h, p.rec + ((chunk0 + c) * p.H + h) * RECF,
+            p.t_in + ((chunk0 + c) * p.H + h) * (size_t)(CH * CH));
   }
   // Chunks we-1 down to cb from the gradient in dh: chunks at or after ce are
   // the lead-in (the gradient advances, nothing is written), chunks below ce
@@ -352,15 +360,15 @@ struct RevChunk {
       const bool more = c - 1 >= cb;
       const int64_t ntok0 = seq0 + (int64_t)(c - 1) * CH;
       const int nrows = more ? min(CH, len - (c - 1) * CH) : 0;
-      const float* tin = p.t_in + ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
+      const float* ntin = more ? p.t_in + ((chunk0 + c - 1) * p.H + h) * (size_t)(CH * CH) : nullptr;
       const float* nrec = more ? p.rec + ((chunk0 + c - 1) * p.H + h) * RECF : nullptr;
       if constexpr (decltype(lead)::value) {
-        step<true>(s, p, ld, rows, ntok0, nrows, h, nullptr, tin, nrec, nullptr, nullptr, nullptr, dh);
+        step<true>(s, p, ld, rows, ntok0, nrows, h, nullptr, ntin, nrec, nullptr, nullptr, nullptr, dh);
       } else {
         const size_t ci = (chunk0 + c) * p.H + h;
         const E* usc = static_cast<const E*>(p.us) + ci * (CH * DV);
         const E* ulc = LOU ? static_cast<const E*>(p.ulo) + ci * (CH * DV) : nullptr;
-        step<false>(s, p, ld, rows, ntok0, nrows, h, dhs + ci * SS, tin, nrec, usc, ulc, p.ep + ci * (EPW * CH), dh);
+        step<false>(s, p, ld, rows, ntok0, nrows, h, dhs + ci * SS, ntin, nrec, usc, ulc, p.ep + ci * (EPW * CH), dh);
       }
     };
     for (int c = we - 1; c >= ce; --c) chunk(std::true_type{}, c);

@@ -229,21 +229,24 @@ struct Chunk {
   using S = FwdSmem<E, DK, DV>;
   using Loader = TileLoader<E, DK, DV, NT, OUT, true, PREP>;
 
-  // One lower 16x16 tile (rt, ct) of P = (Q K^T) * M.
+  // One lower 16x16 tile (rt, ct) of P = (Q K^T) * M, formed transposed (key
+  // rows, query columns) so that each lane stores four consecutive entries of
+  // a row of P at once.
   __device__ __forceinline__ static void p_tile(S* sp, int rt, int ct, int g, int c16) {
     constexpr int LQ = S::LQ, LT = S::LT;
     f32x4 acc = zero4();
 #pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb)
-      mma(acc, ld_frag(sp->Q, LQ, 16 * rt + c16, 32 * kb), ld_frag(sp->KR, LQ, 16 * ct + c16, 32 * kb));
-    const f32x4 gr4 = *reinterpret_cast<const f32x4*>(&sp->gam[16 * rt + 4 * g]);
-    const int c = 16 * ct + c16;
-    const float gc = sp->gam[c];
+      mma(acc, ld_frag(sp->KR, LQ, 16 * ct + c16, 32 * kb), ld_frag(sp->Q, LQ, 16 * rt + c16, 32 * kb));
+    const f32x4 gc4 = *reinterpret_cast<const f32x4*>(&sp->gam[16 * ct + 4 * g]);
+    const int r = 16 * rt + c16;
+    const float gr = sp->gam[r];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * g + i;
-      sp->P[r * LT + c] = to_e<E>((c <= r) ? acc[i] * __expf(gr4[i] - gc) : 0.f);
+      const int c = 16 * ct + 4 * g + i;
+      acc[i] = (c <= r) ? acc[i] * __expf(gr - gc4[i]) : 0.f;
     }
+    st_tile_cm<E>(sp->P, LT, 16 * ct, 16 * rt, acc);
   }
 
   // Process the chunk whose tiles `ld` holds; prefetch the next chunk (if any)
@@ -321,14 +324,15 @@ struct Chunk {
       Frag<E> xw[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) xw[kb] = ld_frag(sp->TBG, LT, 16 * rt + c16, 32 * kb);
+      // formed transposed (key rows), so each lane stores four consecutive
+      // entries of a row of -W at once
 #pragma unroll
       for (int cc = 0; cc < CTW; ++cc) {
         const int ct = ct0 + cc;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(acc, xw[kb], ld_fragC_q<E>(sp->K, S::LK, 32 * kb, 16 * ct));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sp->W[(16 * rt + 4 * g + i) * LQ + 16 * ct + c16] = to_e<E>(-acc[i]);
+        for (int kb = 0; kb < 2; ++kb) mma(acc, ld_fragC_q<E>(sp->K, S::LK, 32 * kb, 16 * ct), xw[kb]);
+        st_tile_cm<E>(sp->W, LQ, 16 * ct, 16 * rt, -acc);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -407,19 +411,17 @@ struct Chunk {
             }
           }
         }
+        // O^T = scale (h^T Q^T diag(Gam) + U^T P^T): value rows, chunk-row
+        // columns, so each lane stores four consecutive entries of a row of O
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           f32x4 o = zero4();
 #pragma unroll
-          for (int kb = 0; kb < DK / 32; ++kb) mma(o, ld_frag(sp->Q, LQ, 16 * rt + c16, 32 * kb), hf[nt][kb]);
-          const f32x4 gm4 = *reinterpret_cast<const f32x4*>(&sp->Gam[16 * rt + 4 * g]);
-          o = o * gm4;
+          for (int kb = 0; kb < DK / 32; ++kb) mma(o, hf[nt][kb], ld_frag(sp->Q, LQ, 16 * rt + c16, 32 * kb));
+          o = o * sp->Gam[16 * rt + c16];
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) mma(o, ld_frag(sp->P, LT, 16 * rt + c16, 32 * kb), uf[kb]);
-          o = o * p.scale;
-          const int col = n0 + 16 * nt + c16;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sp->O[(16 * rt + 4 * g + i) * LO + col] = to_e<E>(o[i]);
+          for (int kb = 0; kb < 2; ++kb) mma(o, uf[kb], ld_frag(sp->P, LT, 16 * rt + c16, 32 * kb));
+          st_tile_cm<E>(sp->O, LO, n0 + 16 * nt, 16 * rt, o * p.scale);
         }
       }
     }
