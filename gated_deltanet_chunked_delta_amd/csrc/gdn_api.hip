@@ -515,7 +515,7 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
   if (pl.nchunk > 0) {
     gdn::GradParams gp{};
     gp.q = a.q; gp.k = a.k; gp.v = a.v; gp.g = a.g; gp.beta = a.beta; gp.dout = args->do_;
-    gp.hs = p.hs; gp.dhs = r.dhs; gp.us = p.us; gp.t_in = ts; gp.ep = r.ep;
+    gp.hs = p.hs; gp.dhs = r.dhs; gp.us = p.us; gp.t_in = ts; gp.rec = rec; gp.ep = r.ep;
     gp.dq = args->dq; gp.dk = args->dk; gp.dv = args->dv; gp.dbeta = args->dbeta; gp.dg = args->dg;
     gp.scale = a.scale; gp.H = a.H; gp.seq = sq;
     gp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);

@@ -479,13 +479,13 @@ template <class E, int DK, int DV>
 struct alignas(16) GradSmem {
   using L = GradLayout<E, DK, DV>;
   alignas(16) char slot[L::NSLOT][L::SLOT];
-  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH];
+  // the chunk's scalar record, as laid out in memory (tail: Lambda_c, Gam_C)
+  alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], tail[4];
   float pg[4][CH], pb[4][CH];  // row sums of the per-wave dgam / dbeta terms, by column group
   float p7[4][CH], c7[4][CH];  // row sums of GP*P by column tile, column sums by row tile
   float c9[2][CH];             // column sums of T * (dU V^T) by row half
   float c10[2][CH];            // column sums of GA*A by row half
   float ph[8];
-  float GamC;
 };
 
 // slot roles (each slot holds one tile at a time; the kernel's phases hand
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int cw = w & 3, rh = w >> 2;
-  const int2 ctab = p.chunk_tab[blockIdx.x];
+  const int2 ctab = p.seq.chunk_of(p.chunk_tab, blockIdx.x);
   if (ctab.x < 0) return;  // the plan found the device cu_seqlens inconsistent
   const int n = ctab.x, jc = ctab.y, h = blockIdx.y, H = p.H;
   const int len = p.seq.len(n);
@@ -597,40 +597,43 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   E* sPT = slotE(SP);                                           // scale P^T
   E* sDUT = slotE(SDU);                                         // dU^T
 
-  // ---- P1: staging, in the order the phases need it: the scalar record (wave
-  //          0) and K, Q (waves 0..3 and 4..7) are requested first and stored
-  //          before the first barrier; U, dO (waves 0..3 and 4..7) and T stay
-  //          in flight during P2 and are stored at its end.  Rows past the end
-  //          are zero.
+  // ---- P1: staging, in the order the phases need it: the chunk's scalar
+  //          record (written by the T solve: decay cumsum and exponentials,
+  //          beta, beta Gam, Gam_C) and K, Q (waves 0..3 and 4..7) are
+  //          requested first and stored before the first barrier; U, dO (waves
+  //          0..3 and 4..7) and T stay in flight during P2 and are stored at
+  //          its end.  Rows past the end are zero.  Every load is issued by
+  //          every lane (rows past the end read the last row and are zeroed
+  //          when stored), so that the compiler knows how many loads are in
+  //          flight behind each one it waits for; with loads under branches
+  //          it waited for all of them.
   const int ht = tid & (NT / 2 - 1);
   typedef E vec_t __attribute__((__vector_size__(16)));
   constexpr int UVEC = 16 / (int)sizeof(E), UPC = CH * DV / UVEC / (NT / 2);  // U pieces per thread
   constexpr int TPT = CH * CH / (4 * NT);
-  vec_t upc[UPC];
-  TilePart<E, NT / 2, DV> td;
+  vec_t upc[UPC];  // U (waves 0..3) or dO (waves 4..7)
   f32x4 tvals[TPT];
   {
-    float gr = 0.f, bt = 0.f;
-    const bool valid = l < rows;
-    if (w == 0 && valid) {
-      const int64_t si = (tok0 + l) * H + h;
-      gr = p.g[si];
-      bt = to_f(static_cast<const E*>(p.beta)[si]);
-    }
+    using GS = GradSmem<E, DK, DV>;
+    static_assert(offsetof(GS, tail) == offsetof(GS, gam) + 5 * CH * sizeof(float), "record layout");
+    const f32x4 rv =
+        *reinterpret_cast<const f32x4*>(p.rec + ((size_t)blockIdx.x * H + h) * RECF + 4 * min(tid, RECF / 4 - 1));
     const E* q = static_cast<const E*>(p.q) + (tok0 * H + h) * DK;
     const E* k = static_cast<const E*>(p.k) + (tok0 * H + h) * DK;
     // U of this chunk as the forward (or its replay) formed it: DV/16 column
     // blocks of [CH][16], zero past the end; contiguous, so 16-byte piece i
-    // of the whole [CH x DV] matrix sits at element 16 i / sizeof(E)
+    // of the whole [CH x DV] matrix sits at element 16 i / sizeof(E).  dO by
+    // rows, 16-byte piece i at row i / (DV / UVEC).
     const E* u = static_cast<const E*>(p.us) + ((size_t)blockIdx.x * H + h) * (CH * DV);
     const E* d = static_cast<const E*>(p.dout) + (tok0 * H + h) * DV;
     TilePart<E, NT / 2, DK> tkq;
-    tkq.template load<true>(rh == 0 ? k : q, (int64_t)H * DK, rows, ht);
-    if (rh == 0) {
+    tkq.template load<false>(rh == 0 ? k : q, (int64_t)H * DK, rows, ht);
 #pragma unroll
-      for (int i = 0; i < UPC; ++i) upc[i] = *reinterpret_cast<const vec_t*>(u + (ht + i * (NT / 2)) * UVEC);
-    } else {
-      td.template load<true>(d, (int64_t)H * DV, rows, ht);
+    for (int i = 0; i < UPC; ++i) {
+      const int pc = ht + i * (NT / 2);
+      const int rd = min(pc / (DV / UVEC), rows - 1), cd = pc % (DV / UVEC);
+      const E* src = rh == 0 ? u + pc * UVEC : d + (int64_t)rd * H * DV + cd * UVEC;
+      upc[i] = *reinterpret_cast<const vec_t*>(src);
     }
     const float* tin = p.t_in + ((size_t)blockIdx.x * H + h) * (CH * CH);
 #pragma unroll
@@ -639,23 +642,9 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       (&s.p7[0][0])[e] = 0.f;
       (&s.c7[0][0])[e] = 0.f;
     }
-    if (w == 0) {
-      if (PREP && p.prep.gate_act && valid) {
-        gr = -(p.prep.gate_scale ? p.prep.gate_scale[h] : 1.f) * softplus_f(gr);
-        bt = sigmoid_f(bt);
-      }
-      const float gm = wave_incl_scan(gr);
-      const float gC = __shfl(gm, 63, 64);
-      const float Gm = __expf(gm);
-      s.gam[l] = gm;
-      s.Gam[l] = Gm;
-      s.ek[l] = __expf(gC - gm);
-      s.beta[l] = bt;
-      s.bg[l] = bt * Gm;
-      if (l == 0) s.GamC = __expf(gC);
-    }
+    if (tid < RECF / 4) *reinterpret_cast<f32x4*>(&s.gam[4 * tid]) = rv;
     if (PREP && p.prep.qk_norm) tkq.normalize_rows(ht);
-    tkq.store(rh == 0 ? sK : slotE(SQ), LK, nullptr, 0, ht);
+    tkq.store_zrows(rh == 0 ? sK : slotE(SQ), LK, rows, ht);
   }
   __syncthreads();
   // dh' down this wave's P5 value columns, requested now (behind the tiles
@@ -747,7 +736,12 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       *reinterpret_cast<vec_t*>(slotE(SV) + r * LV + c) = upc[i];
     }
   } else {
-    td.store(slotE(SDO), LV, nullptr, 0, ht);
+#pragma unroll
+    for (int i = 0; i < UPC; ++i) {
+      const int pc = ht + i * (NT / 2);
+      const int r = pc / (DV / UVEC), c = (pc % (DV / UVEC)) * UVEC;
+      *reinterpret_cast<vec_t*>(slotE(SDO) + r * LV + c) = r < rows ? upc[i] : vec_t{};
+    }
   }
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
@@ -1154,7 +1148,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     if (r == CH - 1) {
       float extra = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < 8; ++ww) extra += s.GamC * s.ph[ww];
+      for (int ww = 0; ww < 8; ++ww) extra += s.tail[1] * s.ph[ww];
       dgm += extra;
     }
     float e = 0.f;
@@ -1185,6 +1179,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 
 template <class E, int DK, int DV>
 hipError_t launch_grad_t(const GradParams& p, int nchunk_total, hipStream_t st) {
+  // the scalar records and T are solved beforehand (as for the chains)
+  if (!p.t_in || !p.rec || !p.us || !p.ep) return hipErrorInvalidValue;
   if (p.prep.qk_norm || p.prep.gate_act)
     hipLaunchKernelGGL((gdn_grad_kernel<E, DK, DV, true>), dim3(nchunk_total, p.H), dim3(512), 0, st, p);
   else

@@ -662,6 +662,14 @@ struct SeqInfo {
   int T;               // tokens per sequence when cu == nullptr
   __device__ __forceinline__ int64_t start(int n) const { return cu ? (int64_t)cu[n] : (int64_t)n * T; }
   __device__ __forceinline__ int len(int n) const { return cu ? cu[n + 1] - cu[n] : T; }
+  // (sequence, chunk within it) of global chunk c: computed for sequences of
+  // one length (no load in front of a workgroup's first requests), else the
+  // plan's table
+  __device__ __forceinline__ int2 chunk_of(const int2* tab, int c) const {
+    if (cu) return tab[c];
+    const int nch = max(1, (T + CH - 1) / CH);
+    return make_int2(c / nch, c % nch);
+  }
 };
 
 }  // namespace gdn

@@ -109,6 +109,7 @@ struct GradParams {
   const void* dhs;         // chunk end state gradients
   const void* us;          // each chunk's U = Ut - W h ([total chunks][H][DV/16][CH][16] column blocks, dtype)
   const float* t_in;       // chunk matrices T (as FwdParams)
+  const float* rec;        // scalar records (as FwdParams)
   const float* ep;         // per-wave partial row terms e_r of the reverse chain (RevParams)
   void* dq;
   void* dk;

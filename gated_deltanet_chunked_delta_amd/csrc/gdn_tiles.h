@@ -239,6 +239,23 @@ struct TilePart {
     const int id = tid + b * NT;
     return (NB * NT == NBLK || id < NBLK) ? (id / BPR) * 4 : -1;
   }
+  // The tile row-major at dst (8-byte stores), rows at or past `rows` as
+  // zeros (for a tile loaded without ZFILL, whose extra rows repeat the last).
+  __device__ __forceinline__ void store_zrows(E* dst, int ld, int rows, int tid = threadIdx.x) const {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int id = tid + b * NT;
+      if (NB * NT == NBLK || id < NBLK) {
+        const int r0 = (id / BPR) * 4, c0 = (id % BPR) * VEC;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const vec_t v = r0 + j < rows ? blk[b][j] : vec_t{};
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4) st4<E>(dst + (r0 + j) * ld + c0 + e, v[e], v[e + 1], v[e + 2], v[e + 3]);
+        }
+      }
+    }
+  }
   __device__ __forceinline__ void store(E* dst, int ld, E* dstT, int ldT, int tid = threadIdx.x) const {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {

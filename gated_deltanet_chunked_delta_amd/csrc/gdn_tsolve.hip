@@ -42,7 +42,7 @@ __global__ __launch_bounds__(192) void gdn_tsolve(TSolveParams p) {
   constexpr int LK = S::LK, LA = S::LA;
   __shared__ S s;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
-  const int2 ct = p.chunk_tab[blockIdx.x];
+  const int2 ct = p.seq.chunk_of(p.chunk_tab, blockIdx.x);
   if (ct.x < 0) return;  // the plan found the device cu_seqlens inconsistent
   const int n = ct.x, h = blockIdx.y, H = p.H;
   const int64_t tok0 = p.seq.start(n) + (int64_t)ct.y * CH;
