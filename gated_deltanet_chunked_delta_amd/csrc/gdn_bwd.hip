@@ -843,6 +843,18 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
     for (int dt = 0; dt < CTK; ++dt) qr[kb][dt] = ld_fragC_q<E>(slotE(SQ), LK, 32 * kb, d0 + 16 * dt);
   __syncthreads();
+  // V rows 16 cw .. 16 cw + 15, the operand of GT in P9 (every tile of a wave
+  // there has column tile cw): requested here, so that the loads are in
+  // flight during P6 and P8 (rows past the end are copies of the last one;
+  // beta = 0 there removes them).  Contiguous k order, one 16-byte read per
+  // fragment.
+  Frag<E> vf[DV / 32];
+  {
+    const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
+    const int vrow = min(16 * cw + c16, rows - 1);
+#pragma unroll
+    for (int kb = 0; kb < DV / 32; ++kb) vf[kb] = ld_frag8(v + (int64_t)vrow * H * DV, 0, 0, 32 * kb);
+  }
 
   // ---- P6: GW = -dU h^T, dQ1 = dO h^T, Udh = U dh'^T (own rows and key columns);
   //          GW -> slot Q as GW^T (Q was last read in P5)
@@ -896,19 +908,6 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
     for (int dt = 0; dt < CTK; ++dt) st_tile_cm<E>(slotE(SQ), LT, 16 * (2 * rh + j), d0 + 16 * dt, gw[j][dt]);
   __syncthreads();
-
-  // V rows 16 cw .. 16 cw + 15, the operand of GT (every tile of a wave there
-  // has column tile cw): read from global now so that the loads are in flight
-  // during the first half of P8 (rows past the end are copies of the last one;
-  // beta = 0 there removes them).  Contiguous k order, one 16-byte read per
-  // fragment.
-  Frag<E> vf[DV / 32];
-  {
-    const E* v = static_cast<const E*>(p.v) + (tok0 * H + h) * DV;
-    const int vrow = min(16 * cw + c16, rows - 1);
-#pragma unroll
-    for (int kb = 0; kb < DV / 32; ++kb) vf[kb] = ld_frag8(v + (int64_t)vrow * H * DV, 0, 0, 32 * kb);
-  }
 
   // ---- P8: XW = T^T GW (own rows); row dots; dK partial (with GPM^T Q); dQ;
   //          then GT
@@ -1076,12 +1075,13 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   // its waves): it enters dgam_r with a minus sign and the last row with a plus,
   // so dg_r gets sum_{i < r} e_i, formed as a prefix sum (adding and then
   // cancelling it leaves a rounding residue that strong decay would make larger
-  // than dg itself).  Wave 0's, for the end.
+  // than dg itself).  Every wave loads them (a branch around the loads made
+  // the compiler wait for them at once); wave 0 uses them at the end.
   float epv[RevWaves<DV>::NW];
   {
     const float* ep = p.ep + ((size_t)blockIdx.x * H + h) * (EPW * CH);
 #pragma unroll
-    for (int ww = 0; ww < RevWaves<DV>::NW; ++ww) epv[ww] = w == 0 ? ep[ww * CH + l] : 0.f;
+    for (int ww = 0; ww < RevWaves<DV>::NW; ++ww) epv[ww] = ep[ww * CH + l];
   }
 
   // ---- P11: dK = dK partial + (E + E^T) K (own rows and key columns) -> slot KD
