@@ -376,7 +376,6 @@ struct Chunk {
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) mma(u[rt][nt], xw[kb], hf[nt][kb]);
     }
-    __builtin_amdgcn_sched_barrier(0);
     sp = lds_opaque(sp);
     // U out as DV/16 column blocks of [CH][16], each contiguous (a wave's
     // stores fill whole lines; rows past the end are zero: beta = 0 there);
@@ -425,7 +424,6 @@ struct Chunk {
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
     sp = lds_opaque(sp);
     {
       const float gc = sp->tail[1];
