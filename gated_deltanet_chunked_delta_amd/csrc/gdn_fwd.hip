@@ -376,7 +376,6 @@ struct Chunk {
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) mma(u[rt][nt], xw[kb], hf[nt][kb]);
     }
-    sp = lds_opaque(sp);
     // U out as DV/16 column blocks of [CH][16], each contiguous (a wave's
     // stores fill whole lines; rows past the end are zero: beta = 0 there);
     // the forward proper writes the rounded operand fragments it forms anyway
@@ -424,7 +423,6 @@ struct Chunk {
         }
       }
     }
-    sp = lds_opaque(sp);
     {
       const float gc = sp->tail[1];
       f32x4 e0[2], e1[2];
