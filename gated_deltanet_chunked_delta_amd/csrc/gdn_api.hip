@@ -219,11 +219,24 @@ gdn_status hip_fail(hipError_t e, const char* what) {
   return fail(GDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-gdn::SeqInfo seq_info(const gdn_common_args& a) {
+gdn::SeqInfo seq_info(const gdn_common_args& a, int segc) {
   gdn::SeqInfo s;
   s.cu = a.cu_seqlens;
   s.T = a.T;
+  s.segc = segc;
   return s;
+}
+
+// The plan kernel fills the work tables from the device cu_seqlens; for
+// sequences of one length (no cu_seqlens) the kernels compute the same tables
+// themselves and it does not run.
+hipError_t plan_tables(const gdn_common_args& a, const Plan& pl, const gdn::SeqInfo& sq, void* ws, hipStream_t s) {
+  if (!sq.cu) return hipSuccess;
+  return timed("plan", s, [&] {
+    return gdn::launch_plan(sq, pl.N, pl.segc, a.T, pl.nchunk, pl.nseg, at<int>(ws, pl.o_chunk_first),
+                            at<int>(ws, pl.o_seg_first), at<gdn::SegDesc>(ws, pl.o_segs),
+                            at<int2>(ws, pl.o_chunk_tab), s);
+  });
 }
 
 long long count_chunks(const gdn_common_args& a) {
@@ -338,12 +351,8 @@ gdn_status check_fwd(const gdn_fwd_args* args) {
 gdn_status fwd_launch(const gdn_fwd_args* args, const Plan& pl, void* ws, void* stream) {
   const gdn_common_args& a = args->a;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  gdn::SeqInfo sq = seq_info(a);
-  hipError_t e = timed("plan", s, [&] {
-    return gdn::launch_plan(sq, pl.N, pl.segc, a.T, pl.nchunk, pl.nseg, at<int>(ws, pl.o_chunk_first),
-                            at<int>(ws, pl.o_seg_first), at<gdn::SegDesc>(ws, pl.o_segs),
-                            at<int2>(ws, pl.o_chunk_tab), s);
-  });
+  gdn::SeqInfo sq = seq_info(a, pl.segc);
+  hipError_t e = plan_tables(a, pl, sq, ws, s);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   gdn::FwdParams p{};
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta; p.h0 = a.h0;
@@ -456,12 +465,8 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
                 a.workspace ? a.workspace_bytes : (size_t)0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* ws = a.workspace;
-  gdn::SeqInfo sq = seq_info(a);
-  hipError_t e = timed("plan", s, [&] {
-    return gdn::launch_plan(sq, pl.N, pl.segc, a.T, pl.nchunk, pl.nseg, at<int>(ws, pl.o_chunk_first),
-                            at<int>(ws, pl.o_seg_first), at<gdn::SegDesc>(ws, pl.o_segs),
-                            at<int2>(ws, pl.o_chunk_tab), s);
-  });
+  gdn::SeqInfo sq = seq_info(a, pl.segc);
+  hipError_t e = plan_tables(a, pl, sq, ws, s);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   // 1. forward replay: state at every chunk start (unless the forward saved them)
   gdn::FwdParams p{};

@@ -418,10 +418,10 @@ __device__ void rev_init_smem(RevSmem<E, DK, DV>& s) {
 template <class E, int DK, int DV, bool PREP>
 __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_seg(RevParams p) {
   __shared__ RevSmem<E, DK, DV> s;
-  const SegDesc sd = p.segs[blockIdx.x];
+  const SegDesc sd = p.seq.seg_of(p.segs, blockIdx.x);
   if (sd.n < 0) return;  // the plan found the device cu_seqlens inconsistent
   const int h = blockIdx.y, n = sd.n;
-  const int64_t seq0 = p.seq.start(n), chunk0 = p.chunk_first[n];
+  const int64_t seq0 = p.seq.start(n), chunk0 = p.seq.first_chunk(p.chunk_first, n);
   const int len = p.seq.len(n), nch = (len + CH - 1) / CH;
   const size_t SS = (size_t)DK * DV;
   const int we = sd.c_end < nch ? lead_in_end(p.rec, chunk0, p.H, h, sd.c_end, nch) : nch;

@@ -660,6 +660,7 @@ struct SegDesc {
 struct SeqInfo {
   const int32_t* cu;   // device cu_seqlens [N+1] or nullptr for uniform length T
   int T;               // tokens per sequence when cu == nullptr
+  int segc;            // chunks per segment (the plan's)
   __device__ __forceinline__ int64_t start(int n) const { return cu ? (int64_t)cu[n] : (int64_t)n * T; }
   __device__ __forceinline__ int len(int n) const { return cu ? cu[n + 1] - cu[n] : T; }
   // (sequence, chunk within it) of global chunk c: computed for sequences of
@@ -669,6 +670,25 @@ struct SeqInfo {
     if (cu) return tab[c];
     const int nch = max(1, (T + CH - 1) / CH);
     return make_int2(c / nch, c % nch);
+  }
+  // The plan's tables, computed the same way for sequences of one length
+  // (ceil(T / CH) chunks each, cut into segments of segc chunks; an empty
+  // sequence has one segment without chunks), so that no plan runs for them.
+  __device__ __forceinline__ int nseg_per_seq() const {
+    const int nch = (T + CH - 1) / CH;
+    return nch == 0 ? 1 : (nch + segc - 1) / segc;
+  }
+  __device__ __forceinline__ SegDesc seg_of(const SegDesc* tab, int j) const {
+    if (cu) return tab[j];
+    const int nch = (T + CH - 1) / CH, ns = nseg_per_seq();
+    const int n = j / ns, s = j % ns;
+    return SegDesc{n, min(nch, s * segc), min(nch, (s + 1) * segc), s};
+  }
+  __device__ __forceinline__ int nseg_of(const int* seg_first, int n) const {
+    return cu ? seg_first[n + 1] - seg_first[n] : nseg_per_seq();
+  }
+  __device__ __forceinline__ int64_t first_chunk(const int* chunk_first, int n) const {
+    return cu ? chunk_first[n] : (int64_t)n * ((T + CH - 1) / CH);
   }
 };
 

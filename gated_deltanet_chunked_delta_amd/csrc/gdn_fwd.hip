@@ -543,11 +543,11 @@ __device__ void init_smem(FwdSmem<E, DK, DV>& s) {
 template <class E, int DK, int DV, bool OUT, bool PREP, bool USAVE>
 __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_seg(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
-  const SegDesc sd = p.segs[blockIdx.x];
+  const SegDesc sd = p.seq.seg_of(p.segs, blockIdx.x);
   if (sd.n < 0) return;  // the plan found the device cu_seqlens inconsistent
   const int h = blockIdx.y, n = sd.n;
-  const int nseg = p.seg_first[n + 1] - p.seg_first[n];
-  const int64_t seq0 = p.seq.start(n), chunk0 = p.chunk_first[n];
+  const int nseg = p.seq.nseg_of(p.seg_first, n);
+  const int64_t seq0 = p.seq.start(n), chunk0 = p.seq.first_chunk(p.chunk_first, n);
   const int len = p.seq.len(n);
   const size_t SS = (size_t)DK * DV;
   const int wb = sd.c_begin > 0 ? lead_in_begin(p.rec, chunk0, p.H, h, sd.c_begin) : 0;
