@@ -277,6 +277,74 @@ def bench_decode(args, log):
     print(json.dumps(out))
 
 
+# Phase names of the instrumented kernels' clocks (the order of their slots).
+CLOCK_PHASES = {
+    "fwd": ["before the first chunk", "staging", "P; T lands", "-W, Ut", "state chain (U, O, h')", "output stores",
+            "after the last chunk"],
+    "rev": ["before the first chunk", "staging (T lands)", "scale P^T, -W^T", "dU, state-gradient update",
+            "after the last chunk"],
+    "grad": ["", "staging (K, Q, record)", "K K^T * D and P; U, dO, T land", "dU, G_P", "G_W, dQ1, U dh'^T",
+             "X_W, dQ, G_T", "Z", "G_A, E", "dK, row sums", "gradient stores"],
+}
+
+
+def phase_clock_report(lib, config):
+    """Markdown tables of the per-phase shader-clock cycles that the instrumented
+    library recorded for the last launch of each kernel (wave 0 of each of the
+    first 512 workgroups; the barriers keep a workgroup's waves in step)."""
+    import ctypes
+    for fn in ("gdn_clock_read_fwd", "gdn_clock_read_rev", "gdn_clock_read_grad"):
+        if not hasattr(lib, fn):
+            sys.exit("--phase-clock needs the instrumented library: python -m gated_deltanet_chunked_delta_amd.build "
+                     "--phase-clock, then GDN_LIB=gated_deltanet_chunked_delta_amd/libgdn_clock.so")
+    blocks = 512
+    fwd = np.zeros((2, blocks, 8, 8), dtype=np.uint32)
+    rev = np.zeros((blocks, 8, 8), dtype=np.uint32)
+    grad = np.zeros((blocks, 8, 10), dtype=np.uint32)
+    for fn, buf in (("gdn_clock_read_fwd", fwd), ("gdn_clock_read_rev", rev), ("gdn_clock_read_grad", grad)):
+        f = getattr(lib, fn)
+        f.argtypes = [ctypes.c_void_p]
+        if f(buf.ctypes.data) != 0:
+            sys.exit(f"{fn} failed")
+    out = [f"Phase clock, workload {config}: shader-clock cycles (s_memtime), wave 0 of each recorded workgroup.", ""]
+
+    def chain(name, rec, phases):
+        w0 = rec[:, 0, :].astype(np.float64)
+        used = w0[:, 7] > 0
+        w0 = w0[used]
+        nch = w0[:, 7]
+        total = w0[:, :len(phases)].sum(1)
+        out.append(f"**{name}** ({used.sum()} workgroups, {nch.mean():.1f} chunks each on average; "
+                   f"workgroup cycles median {np.median(total):,.0f}, max {total.max():,.0f})")
+        out.append("")
+        out.append("| phase | cycles per chunk (mean over workgroups) | share |")
+        out.append("|---|---|---|")
+        per = [w0[:, i].sum() / nch.sum() for i in range(len(phases))]
+        for i, ph in enumerate(phases):
+            if 1 <= i <= len(phases) - 2:
+                out.append(f"| {i} {ph} | {per[i]:,.0f} | {per[i] / sum(per[1:len(phases) - 1]):.0%} |")
+            else:
+                out.append(f"| {i} {ph} (per workgroup) | {w0[:, i].mean():,.0f} | |")
+        out.append("")
+
+    chain("forward (`gdn_fwd_seg<...,1,0,0>`)", fwd[0], CLOCK_PHASES["fwd"])
+    chain("replay (`gdn_fwd_seg<...,0,0,1>`)", fwd[1], CLOCK_PHASES["fwd"])
+    chain("reverse chain (`gdn_rev_seg`)", rev, CLOCK_PHASES["rev"])
+    w0 = grad[:, 0, :].astype(np.float64)
+    used = w0[:, 1:].sum(1) > 0
+    w0 = w0[used]
+    total = w0[:, 1:].sum(1)
+    out.append(f"**gradient kernel (`gdn_grad_kernel`)** ({used.sum()} workgroups, one chunk each; cycles median "
+               f"{np.median(total):,.0f}, max {total.max():,.0f})")
+    out.append("")
+    out.append("| phase | cycles (median over workgroups) | share |")
+    out.append("|---|---|---|")
+    med = [np.median(w0[:, i]) for i in range(10)]
+    for i in range(1, 10):
+        out.append(f"| {i} {CLOCK_PHASES['grad'][i]} | {med[i]:,.0f} | {med[i] / sum(med[1:]):.0%} |")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +375,10 @@ def main():
                     help="skip the per-direction timing protocol (median / min / max over --protocol-iters "
                          "iterations, each after a 1 GiB write that flushes L2 and the last-level cache)")
     ap.add_argument("--protocol-iters", type=int, default=30)
+    ap.add_argument("--phase-clock", action="store_true",
+                    help="with the instrumented library (python -m gated_deltanet_chunked_delta_amd.build "
+                         "--phase-clock; GDN_LIB=gated_deltanet_chunked_delta_amd/libgdn_clock.so): run the step "
+                         "and print each kernel's cycles per phase (per chunk for the chains) as markdown")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
                     help="print a per-kernel markdown summary of rocprofv3 --pmc counter_collection.csv "
                          "files and exit (no GPU needed)")
@@ -387,6 +459,13 @@ def main():
                              **prep_kw)
 
     stream = torch.cuda.current_stream(dev)
+
+    if args.phase_clock:
+        for _ in range(max(1, args.warmup)):
+            step()
+        torch.cuda.synchronize()
+        print(phase_clock_report(gb.lib(), args.config))
+        return
 
     def timed_run(profile):
         for _ in range(args.warmup):

@@ -14,6 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
+# The same kernels with per-phase cycle counters (bench.py --phase-clock)
+LIB_CLOCK = os.path.join(HERE, "libgdn_clock.so")
 OBJ = os.path.join(HERE, "_build")
 SOURCES = ["gdn_api.hip", "gdn_plan.hip", "gdn_tsolve.hip", "gdn_fwd.hip", "gdn_bwd.hip", "gdn_decode.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
@@ -38,12 +40,14 @@ def _compile(src: str, obj_dir: str = OBJ, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False, phase_clock: bool = False) -> str:
     """Compile every source and link `out`.  sanitize: host code with AddressSanitizer and
-    UndefinedBehaviorSanitizer (objects in a separate folder; load with GDN_LIB=out)."""
-    obj_dir = OBJ + ("_san" if sanitize else "")
+    UndefinedBehaviorSanitizer (objects in a separate folder; load with GDN_LIB=out).
+    phase_clock: the kernels also sum the shader clock per phase of each workgroup
+    (GDN_PHASE_CLOCK; objects in a separate folder, default output LIB_CLOCK)."""
+    obj_dir = OBJ + ("_san" if sanitize else "") + ("_clock" if phase_clock else "")
     os.makedirs(obj_dir, exist_ok=True)
-    extra = SAN_FLAGS if sanitize else ()
+    extra = (SAN_FLAGS if sanitize else ()) + (("-DGDN_PHASE_CLOCK",) if phase_clock else ())
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s_: _compile(s_, obj_dir, extra), SOURCES))
     tmp = out + ".tmp"
@@ -62,7 +66,9 @@ if __name__ == "__main__":
     import argparse
     ap = argparse.ArgumentParser()
     ap.add_argument("--sanitize", action="store_true")
-    ap.add_argument("--out", default=LIB)
+    ap.add_argument("--phase-clock", action="store_true")
+    ap.add_argument("--out", default=None)
     a = ap.parse_args()
-    build(verbose=True, out=os.path.abspath(a.out), sanitize=a.sanitize)
+    out = a.out or (LIB_CLOCK if a.phase_clock else LIB)
+    build(verbose=True, out=os.path.abspath(out), sanitize=a.sanitize, phase_clock=a.phase_clock)
     sys.exit(0)

@@ -71,6 +71,13 @@ struct alignas(16) RevSmem {
   alignas(16) float gam[CH], Gam[CH], ek[CH], beta[CH], bg[CH], tail[4];
 };
 
+// Phases of the reverse chain's phase clock: 0 before the first chunk; per
+// chunk 1 staging, 2 scale P^T and -W^T, 3 dU and the state-gradient update;
+// 4 after the last chunk; slot 7 counts the chunks run.
+using RevClock = PhaseClock<8>;
+// [workgroup][wave][phase] (an instrumented build only)
+__device__ uint32_t gdn_clock_rev[kPhaseClock ? CLOCK_BLOCKS : 1][8 * 8];
+
 // Waves per workgroup of the reverse chain: 8 when the state gradient has 128
 // value columns (one 16-column tile per wave, two waves per SIMD), else 4.
 template <int DV>
@@ -157,7 +164,7 @@ struct RevChunk {
   template <bool LEAD>
   __device__ static void step(S& s0, const RevParams& p, Loader& ld, int rows, int64_t ntok0, int nrows, int h,
                               E* dhs_chunk, const float* nt_in, const float* nrec, const E* us_chunk,
-                              const E* ulo_chunk, float* ep_chunk, f32x4 (&dh)[DK / 16][NTW]) {
+                              const E* ulo_chunk, float* ep_chunk, f32x4 (&dh)[DK / 16][NTW], RevClock& clk) {
     constexpr int LQ = S::LQ, LT = S::LT;
     constexpr bool LO = std::is_same<E, bf16>::value;  // U and dS' need their residuals
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
@@ -210,6 +217,7 @@ struct RevChunk {
     static_assert(offsetof(S, tail) == offsetof(S, gam) + 5 * CH * sizeof(float), "record layout");
     ld.rec.store(s1.gam);
     __syncthreads();
+    clk.mark(1);
 
     // ---- 2. the next chunk's tiles, T and record start their way from HBM
     if (nrows > 0) issue(ld, p, ntok0, nrows, h, nrec, nt_in);
@@ -259,6 +267,7 @@ struct RevChunk {
       }
     }
     __syncthreads();
+    clk.mark(2);
 
     // ---- 5. dU = diag(ek) K dh' + scale P^T dO ;  dh = Gam_C dh' + scale (Gam Q)^T dO - W^T dU
     f32x4 du[4][NTW];
@@ -334,6 +343,7 @@ struct RevChunk {
       }
     }
     __syncthreads();
+    clk.mark(3);
   }
 
   // Issue the loads of chunk we - 1, the first of a run (before the state
@@ -349,7 +359,7 @@ struct RevChunk {
   // the lead-in (the gradient advances, nothing is written), chunks below ce
   // write their chunk-end gradients.  ld: primed for chunk we - 1.
   __device__ static void run(S& s, const RevParams& p, int64_t seq0, int len, int64_t chunk0, int cb, int ce, int we,
-                             int h, f32x4 (&dh)[DK / 16][DV / (16 * RevWaves<DV>::NW)], Loader& ld) {
+                             int h, f32x4 (&dh)[DK / 16][DV / (16 * RevWaves<DV>::NW)], Loader& ld, RevClock& clk) {
     const size_t SS = (size_t)DK * DV;
     constexpr bool LOU = std::is_same<E, bf16>::value;
     E* dhs = static_cast<E*>(p.dhs);
@@ -363,16 +373,18 @@ struct RevChunk {
       const float* ntin = more ? p.t_in + ((chunk0 + c - 1) * p.H + h) * (size_t)(CH * CH) : nullptr;
       const float* nrec = more ? p.rec + ((chunk0 + c - 1) * p.H + h) * RECF : nullptr;
       if constexpr (decltype(lead)::value) {
-        step<true>(s, p, ld, rows, ntok0, nrows, h, nullptr, ntin, nrec, nullptr, nullptr, nullptr, dh);
+        step<true>(s, p, ld, rows, ntok0, nrows, h, nullptr, ntin, nrec, nullptr, nullptr, nullptr, dh, clk);
       } else {
         const size_t ci = (chunk0 + c) * p.H + h;
         const E* usc = static_cast<const E*>(p.us) + ci * (CH * DV);
         const E* ulc = LOU ? static_cast<const E*>(p.ulo) + ci * (CH * DV) : nullptr;
-        step<false>(s, p, ld, rows, ntok0, nrows, h, dhs + ci * SS, ntin, nrec, usc, ulc, p.ep + ci * (EPW * CH), dh);
+        step<false>(s, p, ld, rows, ntok0, nrows, h, dhs + ci * SS, ntin, nrec, usc, ulc, p.ep + ci * (EPW * CH), dh,
+                    clk);
       }
     };
     for (int c = we - 1; c >= ce; --c) chunk(std::true_type{}, c);
     for (int c = ce - 1; c >= cb; --c) chunk(std::false_type{}, c);
+    clk.set(7, we - cb);
   }
 };
 
@@ -418,6 +430,8 @@ __device__ void rev_init_smem(RevSmem<E, DK, DV>& s) {
 template <class E, int DK, int DV, bool PREP>
 __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_seg(RevParams p) {
   __shared__ RevSmem<E, DK, DV> s;
+  RevClock clk;
+  clk.start();
   const SegDesc sd = p.seq.seg_of(p.segs, blockIdx.x);
   if (sd.n < 0) return;  // the plan found the device cu_seqlens inconsistent
   const int h = blockIdx.y, n = sd.n;
@@ -431,8 +445,14 @@ __global__ __launch_bounds__(64 * RevWaves<DV>::NW) void gdn_rev_seg(RevParams p
   C::prime(ld, p, seq0, len, chunk0, sd.c_begin, we, h);
   rev_init_smem(s);
   rev_load<E, DK, DV>(dh, (we == nch && p.dhT) ? p.dhT + ((size_t)n * p.H + h) * SS : nullptr);
-  C::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, we, h, dh, ld);
+  clk.mark(0);
+  C::run(s, p, seq0, len, chunk0, sd.c_begin, sd.c_end, we, h, dh, ld, clk);
   if (sd.c_begin == 0 && p.dh0) rev_store<E, DK, DV>(dh, p.dh0 + ((size_t)n * p.H + h) * SS);
+  if constexpr (kPhaseClock) {
+    clk.mark(4);
+    const int blk = blockIdx.x + blockIdx.y * gridDim.x;
+    if (blk < CLOCK_BLOCKS) clk.flush(gdn_clock_rev[blk]);
+  }
 }
 
 template <class E, int DK, int DV>
@@ -560,8 +580,17 @@ template <> struct PMat<bf16> {
 // Accumulator tiles that later products read down their columns are stored
 // transposed (M^T row-major, the lane's four rows of a column as one piece);
 // reads across the other way use the LDS transpose loads.
+// Phases of the gradient kernel's phase clock: one per barrier interval (1
+// staging, 2 K K^T * D and P, 3 dU and G_P, 4 G_W / dQ1 / U dh'^T, 5 X_W / dQ /
+// G_T, 6 Z, 7 G_A and E, 8 dK and the row sums), 9 the final stores.
+using GradClock = PhaseClock<10>;
+// [workgroup][wave][phase] (an instrumented build only)
+__device__ uint32_t gdn_clock_grad[kPhaseClock ? CLOCK_BLOCKS : 1][8 * 10];
+
 template <class E, int DK, int DV, bool PREP>
 __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
+  GradClock clk;
+  clk.start();
   using L = GradLayout<E, DK, DV>;
   constexpr int NT = 512;
   constexpr int LK = L::LK, LV = L::LV, LT = L::LT;
@@ -647,6 +676,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     tkq.store_zrows(rh == 0 ? sK : slotE(SQ), LK, rows, ht);
   }
   __syncthreads();
+  clk.mark(1);
   // dh' down this wave's P5 value columns, requested now (behind the tiles
   // still in flight): quad transposes in P5 turn its row pieces into columns;
   // its products use the contiguous k-slot order
@@ -749,6 +779,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     Tm.put4(e >> 6, e & 63, tvals[i]);
   }
   __syncthreads();
+  clk.mark(2);
 
   // per-lane partial sums of this wave's rows (row tiles 2 rh + j)
   f32x4 rg[2], rb[2];  // dgam / dbeta terms
@@ -843,6 +874,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
     for (int dt = 0; dt < CTK; ++dt) qr[kb][dt] = ld_fragC_q<E>(slotE(SQ), LK, 32 * kb, d0 + 16 * dt);
   __syncthreads();
+  clk.mark(3);
   // V rows 16 cw .. 16 cw + 15, the operand of GT in P9 (every tile of a wave
   // there has column tile cw): requested here, so that the loads are in
   // flight during P6 and P8 (rows past the end are copies of the last one;
@@ -908,6 +940,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
 #pragma unroll
     for (int dt = 0; dt < CTK; ++dt) st_tile_cm<E>(slotE(SQ), LT, 16 * (2 * rh + j), d0 + 16 * dt, gw[j][dt]);
   __syncthreads();
+  clk.mark(4);
 
   // ---- P8: XW = T^T GW (own rows); row dots; dK partial (with GPM^T Q); dQ;
   //          then GT
@@ -991,6 +1024,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     if (g == 0) s.c9[rh][c] = tm;
   }
   __syncthreads();
+  clk.mark(5);
 
   // ---- P10: Z = GT T^T (own row tiles, column tile cw) -> slot P as Z^T (last
   //           read in P5), GA = strict_lower(-T^T Z) (own rows); E -> slot dU
@@ -1039,6 +1073,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       }
     }
     __syncthreads();
+    clk.mark(6);
     PFrag<E> zf[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) zf[kb] = ZT.row(16 * cw + c16, 32 * kb);
@@ -1070,6 +1105,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     if (g == 0) s.c10[rh][c] = -csum;
   }
   __syncthreads();
+  clk.mark(7);
 
   // e_r = ek_r k_r.(U dh'^T)_r, the reverse chain's row terms (summed here over
   // its waves): it enters dgam_r with a minus sign and the last row with a plus,
@@ -1126,6 +1162,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     if (l == 0) s.ph[w] = b;
   }
   __syncthreads();
+  clk.mark(8);
   store_tile<E, DV, NT>(slotE(SQ), LV, static_cast<E*>(p.dv) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
   if (PREP && p.prep.qk_norm) {
     // gradients with respect to the raw q and k (the kernel saw them normalised)
@@ -1175,6 +1212,11 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       }
     }
   }
+  if constexpr (kPhaseClock) {
+    clk.mark(9);
+    const int blk = blockIdx.x + blockIdx.y * gridDim.x;
+    if (blk < CLOCK_BLOCKS) clk.flush(gdn_clock_grad[blk]);
+  }
 }
 
 template <class E, int DK, int DV>
@@ -1201,3 +1243,15 @@ hipError_t launch_grad(int dtype, int DK, int DV, const GradParams& p, int nchun
 }
 
 }  // namespace gdn
+
+#ifdef GDN_PHASE_CLOCK
+// The reverse chain's ([CLOCK_BLOCKS][8 waves][8 phases]) and the gradient
+// kernel's ([CLOCK_BLOCKS][8 waves][10 phases]) phase clocks, uint32 cycles, to
+// host memory; an instrumented build only.
+extern "C" int gdn_clock_read_rev(uint32_t* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn::gdn_clock_rev), sizeof(gdn::gdn_clock_rev));
+}
+extern "C" int gdn_clock_read_grad(uint32_t* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn::gdn_clock_grad), sizeof(gdn::gdn_clock_grad));
+}
+#endif

@@ -59,6 +59,51 @@ __device__ __forceinline__ T* lds_opaque(T* p) {
 
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// Cycles per phase of a workgroup, for an instrumented build only (compiled
+// with GDN_PHASE_CLOCK; otherwise every call is empty).  Each wave reads the
+// shader clock (s_memtime) at mark(i) and adds the cycles since its previous
+// mark to phase i; the sums stay in registers until flush(), which lane 0
+// writes out once at the end, so that no store enters the phases measured.
+#ifdef GDN_PHASE_CLOCK
+constexpr bool kPhaseClock = true;
+#else
+constexpr bool kPhaseClock = false;
+#endif
+template <int NPH>
+struct PhaseClock {
+  uint64_t last;
+  uint32_t acc[NPH];
+  __device__ __forceinline__ void start() {
+    if constexpr (kPhaseClock) {
+#pragma unroll
+      for (int i = 0; i < NPH; ++i) acc[i] = 0;
+      last = __builtin_amdgcn_s_memtime();
+    }
+  }
+  __device__ __forceinline__ void mark(int i) {
+    if constexpr (kPhaseClock) {
+      const uint64_t t = __builtin_amdgcn_s_memtime();
+      acc[i] += (uint32_t)(t - last);
+      last = t;
+    }
+  }
+  // a count kept in slot i instead of cycles (the chunks a chain ran)
+  __device__ __forceinline__ void set(int i, uint32_t v) {
+    if constexpr (kPhaseClock) acc[i] = v;
+  }
+  // dst: this workgroup's [waves][NPH] record
+  __device__ __forceinline__ void flush(uint32_t* dst) const {
+    if constexpr (kPhaseClock) {
+      if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int i = 0; i < NPH; ++i) dst[wave_id() * NPH + i] = acc[i];
+      }
+    }
+  }
+};
+// Workgroups whose phase cycles are kept (the first ones of the grid).
+constexpr int CLOCK_BLOCKS = 512;
+
 // ---------------------------------------------------------------------------
 // Operand fragments: eight k-slots per lane.
 template <class E> struct Frag;

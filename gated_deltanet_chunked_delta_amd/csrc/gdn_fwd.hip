@@ -211,6 +211,13 @@ struct TileLoader {
 
 // ------------------------------------------------------------------ one chunk
 
+// Phases of the forward's phase clock: 0 before the first chunk; per chunk 1
+// staging, 2 P and T's landing, 3 -W and Ut, 4 the state chain, 5 the output
+// stores; 6 after the last chunk; slot 7 counts the chunks run.
+using FwdClock = PhaseClock<8>;
+// [forward, replay][workgroup][wave][phase] (an instrumented build only)
+__device__ uint32_t gdn_clock_fwd[kPhaseClock ? 2 : 1][kPhaseClock ? CLOCK_BLOCKS : 1][8 * 8];
+
 // OUT:  forward (writes o) vs replay (no output).  Either stores the chunk-start
 //       state when p.hs is set.
 // Waves per workgroup: 8 when the state has 128 value columns (one 16-column
@@ -258,7 +265,7 @@ struct Chunk {
   template <bool LEAD>
   __device__ static void step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows, int64_t ntok0,
                               int nrows, int h, E* hs_chunk, const float* t_in, const float* nrec, E* us_chunk,
-                              E* ulo_chunk, f32x4 (&hacc)[DK / 16][NTW]) {
+                              E* ulo_chunk, f32x4 (&hacc)[DK / 16][NTW], FwdClock& clk) {
     constexpr bool OUTC = OUT && !LEAD, USAVEC = USAVE && !LEAD;
     constexpr int LQ = S::LQ, LT = S::LT, LO = S::LO;
     constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
@@ -284,6 +291,7 @@ struct Chunk {
         for (int nt = 0; nt < NTW; ++nt) st_blk_row4<E>(hs_chunk, 16 * t + 4 * g, n0 + 16 * nt, DV, hacc[t][nt]);
     }
     __syncthreads();
+    clk.mark(1);
     sp = lds_opaque(sp);
 
     // ---- 2. for the output, the ten lower 16x16 tiles of P = (Q K^T) * M, tile j
@@ -307,6 +315,7 @@ struct Chunk {
       st4f<E>(&sp->TB[r * LT + c], tv[i] * bt4);
     }
     __syncthreads();
+    clk.mark(2);
     sp = lds_opaque(sp);
 
     // ---- 3. the next chunk's k, v, scalar record (and q) start their way from HBM
@@ -358,6 +367,7 @@ struct Chunk {
       }
     }
     __syncthreads();
+    clk.mark(3);
     sp = lds_opaque(sp);
 
     // ---- 5. state chain: U = Ut - W h ; O = scale (diag(Gam) Q h + P U) ; h' = Gam_C h + K^T (ek * U)
@@ -445,6 +455,7 @@ struct Chunk {
       }
     }
     __syncthreads();
+    clk.mark(4);
     sp = lds_opaque(sp);
 
     // ---- 6. output tile out (coalesced); the next chunk's staging does not touch sp->O
@@ -458,6 +469,7 @@ struct Chunk {
               *reinterpret_cast<const ovec_t*>(&sp->O[r * LO + c0]);
       }
     }
+    clk.mark(5);
   }
 
   // Issue the loads of chunk wb, the first of a run (before the state is
@@ -470,7 +482,7 @@ struct Chunk {
   // before cb are the lead-in (the state advances, nothing is written), chunks
   // from cb on write their outputs.  ld: primed for chunk wb.
   __device__ static void run(S& s, const FwdParams& p, int64_t seq0, int len, int64_t chunk0, int wb, int cb,
-                             int ce, int h, f32x4 (&hacc)[DK / 16][NTW], Loader& ld) {
+                             int ce, int h, f32x4 (&hacc)[DK / 16][NTW], Loader& ld, FwdClock& clk) {
     const size_t SS = (size_t)DK * DV;
     E* hs = static_cast<E*>(p.hs);
     // the lead-in and the segment proper as two loops, each with its own
@@ -483,17 +495,18 @@ struct Chunk {
       const float* tin = p.t_in + ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
       const float* nrec = more ? p.rec + ((chunk0 + c + 1) * p.H + h) * RECF : nullptr;
       if constexpr (decltype(lead)::value) {
-        step<true>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, nullptr, tin, nrec, nullptr, nullptr, hacc);
+        step<true>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, nullptr, tin, nrec, nullptr, nullptr, hacc, clk);
       } else {
         E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
         const size_t uoff = ((chunk0 + c) * p.H + h) * (size_t)(CH * DV);
         E* usc = USAVE ? static_cast<E*>(p.us) + uoff : nullptr;
         E* ulc = USAVE && p.ulo ? static_cast<E*>(p.ulo) + uoff : nullptr;
-        step<false>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, nrec, usc, ulc, hacc);
+        step<false>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, nrec, usc, ulc, hacc, clk);
       }
     };
     for (int c = wb; c < cb; ++c) chunk(std::true_type{}, c);
     for (int c = cb; c < ce; ++c) chunk(std::false_type{}, c);
+    clk.set(7, ce - wb);
   }
 };
 
@@ -543,6 +556,8 @@ __device__ void init_smem(FwdSmem<E, DK, DV>& s) {
 template <class E, int DK, int DV, bool OUT, bool PREP, bool USAVE>
 __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_seg(FwdParams p) {
   __shared__ FwdSmem<E, DK, DV> s;
+  FwdClock clk;
+  clk.start();
   const SegDesc sd = p.seq.seg_of(p.segs, blockIdx.x);
   if (sd.n < 0) return;  // the plan found the device cu_seqlens inconsistent
   const int h = blockIdx.y, n = sd.n;
@@ -557,8 +572,14 @@ __global__ __launch_bounds__(64 * FwdWaves<DV>::NW) void gdn_fwd_seg(FwdParams p
   C::prime(ld, p, seq0, len, chunk0, wb, sd.c_end, h);
   init_smem(s);
   load_state<E, DK, DV>(hacc, (wb == 0 && p.h0) ? p.h0 + ((size_t)n * p.H + h) * SS : nullptr);
-  C::run(s, p, seq0, len, chunk0, wb, sd.c_begin, sd.c_end, h, hacc, ld);
+  clk.mark(0);
+  C::run(s, p, seq0, len, chunk0, wb, sd.c_begin, sd.c_end, h, hacc, ld, clk);
   if (sd.s == nseg - 1 && p.hT) store_state<E, DK, DV>(hacc, p.hT + ((size_t)n * p.H + h) * SS);
+  if constexpr (kPhaseClock) {
+    clk.mark(6);
+    const int blk = blockIdx.x + blockIdx.y * gridDim.x;
+    if (blk < CLOCK_BLOCKS) clk.flush(gdn_clock_fwd[OUT ? 0 : 1][blk]);
+  }
 }
 
 template <class E, int DK, int DV>
@@ -598,3 +619,11 @@ hipError_t launch_fwd(int dtype, int DK, int DV, const FwdParams& p, int nseg_to
 }
 
 }  // namespace gdn
+
+#ifdef GDN_PHASE_CLOCK
+// The forward's and the replay's phase clocks ([2][CLOCK_BLOCKS][8 waves][8
+// phases] uint32 cycles) to host memory; an instrumented build only.
+extern "C" int gdn_clock_read_fwd(uint32_t* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn::gdn_clock_fwd), sizeof(gdn::gdn_clock_fwd));
+}
+#endif
