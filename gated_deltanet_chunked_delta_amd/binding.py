@@ -183,7 +183,8 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale: float, h0=None, cu_seqlens=None, cu_s
                   o=None, hT=None, noalloc: bool = False):
     """Forward pass.  Returns (o, hT) with hT None unless output_final_state, followed by
     states if save_states (the state at every chunk start, a flat tensor of the input
-    dtype) and chunk_t if save_t (every chunk's matrix T, a flat fp32 tensor); both are
+    dtype) and chunk_t if save_t (every chunk's matrix T, a flat fp32 tensor laid out as
+    gdn_chunk_t_bytes in include/gdn.h describes); both are
     for gdn_chunk_bwd.  qk_norm / gate_act select the in-kernel pre-processing (raw q,
     k; gate and beta logits, see include/gdn.h).  o / hT: optional output tensors
     to write into (else allocated).  noalloc: call gdn_chunk_fwd_noalloc, which

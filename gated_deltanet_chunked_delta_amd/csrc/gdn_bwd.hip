@@ -94,15 +94,14 @@ struct RevChunk {
   // the first half of the threads holds K and the second half Q (one register
   // set, kq), and dO sits on the first NT / 2 * (DV / DK) threads.
   static constexpr int KQT = NT / 2;  // threads per K (or Q) tile
-  static constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
-  static_assert(TPT * 4 * NT == CH * CH && (4 * NT) % CH == 0, "whole rows of T per pass");
   struct Loader {
     TilePart<E, KQT, DK> kq;
     TilePart<E, NT, DV> d;
     RecordPart rec;
-    // this thread's pieces of T (piece i at element 4 (tid + i NT)) and beta Gam
-    // of their columns (the same columns for every piece)
-    f32x4 tv[TPT], tbg;
+    // this thread's pieces of T (its bf16 value plane for bf16 inputs) and
+    // beta Gam of their 8 columns (the same columns for every piece)
+    TPart<E, NT> t;
+    f32x4 tbg[2];
     // Gam of the rows of each kq block (Q half), as loaded: the scaling waits
     // for the staging, so that nothing waits for these loads meanwhile
     f32x4 sc[TilePart<E, KQT, DK>::NB > 0 ? TilePart<E, KQT, DK>::NB : 1];
@@ -117,9 +116,10 @@ struct RevChunk {
     ld.kq.load(static_cast<const E*>(src) + (tok0 * H + h) * DK, (int64_t)H * DK, rows, kq_tid());
     ld.d.load(static_cast<const E*>(p.dout) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
     ld.rec.load(rec);
+    ld.t.load(t);
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) ld.tv[i] = *reinterpret_cast<const f32x4*>(t + 4 * (threadIdx.x + i * NT));
-    ld.tbg = *reinterpret_cast<const f32x4*>(rec + 4 * CH + (4 * threadIdx.x) % CH);
+    for (int j = 0; j < 2; ++j)
+      ld.tbg[j] = *reinterpret_cast<const f32x4*>(rec + 4 * CH + (8 * threadIdx.x) % CH + 4 * j);
     constexpr int NBK = TilePart<E, KQT, DK>::NB;
 #pragma unroll
     for (int b = 0; b < NBK; ++b) {
@@ -208,12 +208,14 @@ struct RevChunk {
       ld.kq.template store_rows2<false>(s1.K, LQ, s1.KC, S::LKC, ld.sc, kq_tid());
     }
     ld.d.store_rows16(s1.DO, S::LDO);
-    // T lands as T diag(beta Gam) (computed in fp32, rounded once)
+    // T lands as T diag(beta Gam) (scaled in fp32, rounded once)
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int e = 4 * (tid + i * NT), r = e / CH, c = e % CH;
-      st4f<E>(&s1.TBG[r * LT + c], ld.tv[i] * ld.tbg);
-    }
+    for (int i = 0; i < TPart<E, NT>::NP; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = 8 * (tid + i * NT) + 4 * j, r = e / CH, c = e % CH;
+        st4f<E>(&s1.TBG[r * LT + c], ld.t.get(i, j) * ld.tbg[j]);
+      }
     static_assert(offsetof(S, tail) == offsetof(S, gam) + 5 * CH * sizeof(float), "record layout");
     ld.rec.store(s1.gam);
     __syncthreads();
@@ -569,6 +571,54 @@ template <> struct PMat<bf16> {
   __device__ __forceinline__ f32x4 cpiece(int r0, int c0) const {
     return ld_cpiece<bf16>(hi, LP, r0, c0) + ld_cpiece<bf16>(lo, LP, r0, c0);
   }
+  // 8 consecutive elements of row r from c0, already split into their parts
+  __device__ __forceinline__ void put8(int r, int c0, const bf16x8& h, const bf16x8& l) const {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *reinterpret_cast<b4_t*>(&hi[r * LP + c0 + 4 * j]) = b4_t{h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]};
+      *reinterpret_cast<b4_t*>(&lo[r * LP + c0 + 4 * j]) = b4_t{l[4 * j], l[4 * j + 1], l[4 * j + 2], l[4 * j + 3]};
+    }
+  }
+};
+
+// One thread's share of a chunk's T on its way from global memory (as the T
+// solve stores it) into a PMat: fp32 pieces, or for bf16 inputs the stored
+// value and residual planes, which are already the PMat's two parts.
+template <class E, int NT> struct TStage;
+template <int NT> struct TStage<float, NT> {
+  static constexpr int NP = CH * CH / (4 * NT);
+  f32x4 v[NP];
+  __device__ __forceinline__ void load(const float* t, int tid) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) v[i] = *reinterpret_cast<const f32x4*>(t + 4 * (tid + i * NT));
+  }
+  __device__ __forceinline__ void put(const PMat<float>& m, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int e = 4 * (tid + i * NT);
+      m.put4(e / CH, e % CH, v[i]);
+    }
+  }
+};
+template <int NT> struct TStage<bf16, NT> {
+  static constexpr int NP = CH * CH / (8 * NT);
+  static_assert(NP * 8 * NT == CH * CH, "whole pieces of T per thread");
+  bf16x8 h[NP], l[NP];
+  __device__ __forceinline__ void load(const float* t, int tid) {
+    const bf16* b = reinterpret_cast<const bf16*>(t);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      h[i] = *reinterpret_cast<const bf16x8*>(b + 8 * (tid + i * NT));
+      l[i] = *reinterpret_cast<const bf16x8*>(b + CH * CH + 8 * (tid + i * NT));
+    }
+  }
+  __device__ __forceinline__ void put(const PMat<bf16>& m, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int e = 8 * (tid + i * NT);
+      m.put8(e / CH, e % CH, h[i], l[i]);
+    }
+  }
 };
 
 // One chunk per workgroup of 8 waves.  Wave w works on column group cw = w % 4
@@ -639,9 +689,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   const int ht = tid & (NT / 2 - 1);
   typedef E vec_t __attribute__((__vector_size__(16)));
   constexpr int UVEC = 16 / (int)sizeof(E), UPC = CH * DV / UVEC / (NT / 2);  // U pieces per thread
-  constexpr int TPT = CH * CH / (4 * NT);
   vec_t upc[UPC];  // U (waves 0..3) or dO (waves 4..7)
-  f32x4 tvals[TPT];
+  TStage<E, NT> tst;
   {
     using GS = GradSmem<E, DK, DV>;
     static_assert(offsetof(GS, tail) == offsetof(GS, gam) + 5 * CH * sizeof(float), "record layout");
@@ -664,9 +713,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       const E* src = rh == 0 ? u + pc * UVEC : d + (int64_t)rd * H * DV + cd * UVEC;
       upc[i] = *reinterpret_cast<const vec_t*>(src);
     }
-    const float* tin = p.t_in + ((size_t)blockIdx.x * H + h) * (CH * CH);
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) tvals[i] = *reinterpret_cast<const f32x4*>(tin + 4 * (tid + i * NT));
+    tst.load(p.t_in + ((size_t)blockIdx.x * H + h) * (CH * CH), tid);
     for (int e = tid; e < 4 * CH; e += NT) {
       (&s.p7[0][0])[e] = 0.f;
       (&s.c7[0][0])[e] = 0.f;
@@ -773,11 +820,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       *reinterpret_cast<vec_t*>(slotE(SDO) + r * LV + c) = r < rows ? upc[i] : vec_t{};
     }
   }
-#pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int e = 4 * (tid + i * NT);
-    Tm.put4(e >> 6, e & 63, tvals[i]);
-  }
+  tst.put(Tm, tid);
   __syncthreads();
   clk.mark(2);
 

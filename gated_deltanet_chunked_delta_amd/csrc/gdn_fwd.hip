@@ -268,15 +268,14 @@ struct Chunk {
                               E* ulo_chunk, f32x4 (&hacc)[DK / 16][NTW], FwdClock& clk) {
     constexpr bool OUTC = OUT && !LEAD, USAVEC = USAVE && !LEAD;
     constexpr int LQ = S::LQ, LT = S::LT, LO = S::LO;
-    constexpr int TPT = CH * CH / (4 * NT);  // 4-float pieces of T per thread
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
     const int H = p.H;
     const int n0 = w * (DV / NW);  // first state column of this wave
 
-    // T is requested first and lands in LDS at the end of phase 2
-    f32x4 tv[TPT];
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) tv[i] = *reinterpret_cast<const f32x4*>(t_in + 4 * (tid + i * NT));
+    // T (its bf16 value plane for bf16 inputs) is requested first and lands
+    // in LDS at the end of phase 2
+    TPart<E, NT> tp;
+    tp.load(t_in);
 
     // ---- 1. tiles into LDS, scalars, prefetch of the next chunk
     S* sp = lds_opaque(&s0);
@@ -305,15 +304,18 @@ struct Chunk {
         if (pid < 10) p_tile(sp, rt, ct, g, c16);
       }
     }
-    // T lands as its two column-scaled operands (computed in fp32, rounded once)
+    // T lands as its two column-scaled operands (scaled in fp32, rounded once)
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int e = 4 * (tid + i * NT), r = e / CH, c = e % CH;
-      const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&sp->bg[c]);
-      const f32x4 bt4 = *reinterpret_cast<const f32x4*>(&sp->beta[c]);
-      st4f<E>(&sp->TBG[r * LT + c], tv[i] * bg4);
-      st4f<E>(&sp->TB[r * LT + c], tv[i] * bt4);
-    }
+    for (int i = 0; i < TPart<E, NT>::NP; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = 8 * (tid + i * NT) + 4 * j, r = e / CH, c = e % CH;
+        const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&sp->bg[c]);
+        const f32x4 bt4 = *reinterpret_cast<const f32x4*>(&sp->beta[c]);
+        const f32x4 tv = tp.get(i, j);
+        st4f<E>(&sp->TBG[r * LT + c], tv * bg4);
+        st4f<E>(&sp->TB[r * LT + c], tv * bt4);
+      }
     __syncthreads();
     clk.mark(2);
     sp = lds_opaque(sp);

@@ -338,6 +338,47 @@ __device__ __forceinline__ int lead_in_end(const float* rec, int64_t chunk0, int
   return nch;
 }
 
+// A chunk's T as the T solve stores it (one 16 KiB entry per chunk and head):
+// fp32 64 x 64 row-major for fp32 inputs; for bf16 inputs two bf16 64 x 64
+// row-major planes, the value rounded to bf16 (the "hi" plane) and then the
+// residual T - hi rounded to bf16 (the "lo" plane), so that hi + lo carries T
+// to about 16 bits.  The chains use T only as a bf16 matrix-core operand
+// (scaled by a column factor and rounded) and read the hi plane alone; the
+// gradient kernel's near-fp32 products read both.
+//
+// TPart: one thread's share of the chunk's (hi) T, in pieces of 8 consecutive
+// elements, piece i at element 8 (tid + i NT); get(i, j) gives elements
+// 8 (tid + i NT) + 4 j .. + 3 as fp32.
+template <class E, int NT>
+struct TPart;
+template <int NT>
+struct TPart<float, NT> {
+  static constexpr int NP = CH * CH / (8 * NT);
+  static_assert(NP * 8 * NT == CH * CH && (8 * NT) % CH == 0, "whole rows of T per pass");
+  f32x4 v[NP][2];
+  __device__ __forceinline__ void load(const float* t, int tid = threadIdx.x) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) v[i][j] = *reinterpret_cast<const f32x4*>(t + 8 * (tid + i * NT) + 4 * j);
+  }
+  __device__ __forceinline__ f32x4 get(int i, int j) const { return v[i][j]; }
+};
+template <int NT>
+struct TPart<bf16, NT> {
+  static constexpr int NP = CH * CH / (8 * NT);
+  static_assert(NP * 8 * NT == CH * CH && (8 * NT) % CH == 0, "whole rows of T per pass");
+  bf16x8 v[NP];
+  __device__ __forceinline__ void load(const float* t, int tid = threadIdx.x) {
+    const bf16* hi = reinterpret_cast<const bf16*>(t);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) v[i] = *reinterpret_cast<const bf16x8*>(hi + 8 * (tid + i * NT));
+  }
+  __device__ __forceinline__ f32x4 get(int i, int j) const {
+    return f32x4{(float)v[i][4 * j], (float)v[i][4 * j + 1], (float)v[i][4 * j + 2], (float)v[i][4 * j + 3]};
+  }
+};
+
 // This thread's 16-byte piece of a chunk's scalar record (threads < RECF / 4),
 // prefetched with the chunk's tiles; store() writes it to LDS, where the
 // record's arrays lie as in memory.

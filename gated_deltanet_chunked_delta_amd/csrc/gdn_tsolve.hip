@@ -142,9 +142,23 @@ __global__ __launch_bounds__(192) void gdn_tsolve(TSolveParams p) {
   __syncthreads();
   solve_columns(s.KD, sT, w, s.beta);
   __syncthreads();
+  // out as fp32 (fp32 inputs) or as its bf16 value and residual planes
   float* dst = p.t_out + ((size_t)blockIdx.x * H + h) * (CH * CH);
-  for (int e = 4 * tid; e < CH * CH; e += 4 * NT)
-    *reinterpret_cast<f32x4*>(dst + e) = *reinterpret_cast<const f32x4*>(&sT[(e >> 6) * LA + (e & 63)]);
+  for (int e = 4 * tid; e < CH * CH; e += 4 * NT) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(&sT[(e >> 6) * LA + (e & 63)]);
+    if constexpr (std::is_same<E, bf16>::value) {
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = (bf16)x[i];
+        lo[i] = (bf16)(x[i] - (float)hi[i]);
+      }
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(dst) + e) = hi;
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(dst) + CH * CH + e) = lo;
+    } else {
+      *reinterpret_cast<f32x4*>(dst + e) = x;
+    }
+  }
 }
 
 template <class E, int DK>

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 10
+#define GDN_ABI_VERSION 11
 
 typedef enum {
   GDN_OK = 0,
@@ -172,14 +172,18 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_bwd_args* args);
 size_t gdn_chunk_states_bytes(const gdn_common_args* a);
 
 /* Bytes of the saved chunk matrices (t_save / t_saved): C * H * (64 * 64 + 324)
- * fp32 values, C as above.  Entry (c, h) at element offset (c * H + h) * 4096 is
- * the 64 x 64 row-major lower-triangular matrix
+ * fp32 values, C as above.  Entry (c, h), 16 KiB at element offset
+ * (c * H + h) * 4096, holds the 64 x 64 row-major lower-triangular matrix
  *     T = (I + diag(beta) strict_lower((K K^T) * D))^-1,   D[r][i] = exp(G_r - G_i),
  * of chunk c and head h (K: the chunk's 64 keys as rows, after the optional
  * normalisation; beta after the optional activation; G_r the running sum of
  * g over the chunk up to row r), the inverse of the chunk's unit lower-
  * triangular system in the WY/UT form ("FlashQLA resource", section 3).  Rows
- * past a sequence's end have beta = 0 (rows of the identity).  After the
+ * past a sequence's end have beta = 0 (rows of the identity).  For fp32 inputs
+ * the entry is T in fp32; for bf16 inputs it is two 64 x 64 row-major bf16
+ * planes, T rounded to bf16 and then the residual T - that value rounded to
+ * bf16 (their sum carries T to about 16 significant bits; the forward and
+ * reverse state chains read the first plane only).  After the
  * C * H matrices, at element offset C * H * 4096 + (c * H + h) * 324, the
  * chunk's scalar record (g, beta after the optional activation; rows past a
  * sequence end have g = beta = 0): G_r (64 values), exp(G_r), exp(G_63 - G_r),
