@@ -525,6 +525,7 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* args, void* stream) {
     gp.scale = a.scale; gp.H = a.H; gp.seq = sq;
     gp.chunk_tab = at<int2>(ws, pl.o_chunk_tab);
     gp.prep = p.prep;
+    gp.nwg = cu_count();
     e = timed("grad", s, [&] { return gdn::launch_grad(a.dtype, a.Dk, a.Dv, gp, pl.nchunk, s); });
     if (e != hipSuccess) return hip_fail(e, "gradient launch");
   }

@@ -621,6 +621,52 @@ template <int NT> struct TStage<bf16, NT> {
   }
 };
 
+// Requests into L2 the inputs that the staging of workgroup b + nwg reads (b
+// this workgroup's linear index, nwg the compute units; the last workgroups
+// take the last one): its scalar record, K, Q, dO (sequences of one length;
+// with cu_seqlens only the chunk-indexed inputs), U and T, one 4-byte load
+// per 64-byte piece, folded into the returned value.  The LDS holds one
+// workgroup per compute unit and workgroups are dealt to the XCDs round-robin,
+// so that workgroup runs on this XCD and starts about when this one ends:
+// its staging then reads from L2.
+template <class E, int DK, int DV>
+__device__ __forceinline__ uint32_t l2_prefetch_next(const GradParams& p, int tid) {
+  constexpr int NT = 512;
+  constexpr int KP = DK * (int)sizeof(E) / 64, VP = DV * (int)sizeof(E) / 64;  // pieces per row
+  constexpr int NK = CH * KP, NDO = CH * VP, NU = CH * DV * (int)sizeof(E) / 64, NTP = CH * CH * 4 / 64,
+                NR = (RECF * 4 + 63) / 64;
+  constexpr int O_Q = NK, O_DO = 2 * NK, O_U = O_DO + NDO, O_T = O_U + NU, O_R = O_T + NTP, NPF = O_R + NR;
+  const int nlin = gridDim.x * gridDim.y;
+  const int tgt = min((int)(blockIdx.x + blockIdx.y * gridDim.x) + p.nwg, nlin - 1);
+  const int ci = tgt % gridDim.x, h = tgt / gridDim.x, H = p.H;
+  const bool tok = p.seq.cu == nullptr;  // token-indexed inputs without a table load
+  const int2 ct = tok ? p.seq.chunk_of(nullptr, ci) : make_int2(0, 0);
+  const int64_t tok0 = (int64_t)ct.x * p.seq.T + (int64_t)ct.y * CH;
+  const int rmax = min(CH, p.seq.T - ct.y * CH) - 1;
+  const size_t cb = (size_t)ci * H + h;
+  const char* kb = static_cast<const char*>(p.k) + (tok0 * H + h) * DK * sizeof(E);
+  const char* qb = static_cast<const char*>(p.q) + (tok0 * H + h) * DK * sizeof(E);
+  const char* db = static_cast<const char*>(p.dout) + (tok0 * H + h) * DV * sizeof(E);
+  const char* ub = static_cast<const char*>(p.us) + cb * (CH * DV * sizeof(E));
+  const char* tb = reinterpret_cast<const char*>(p.t_in + cb * (CH * CH));
+  const char* rb = reinterpret_cast<const char*>(p.rec + cb * RECF);
+  uint32_t acc = 0;
+#pragma unroll
+  for (int j = 0; j < (NPF + NT - 1) / NT; ++j) {
+    int i = min(tid + j * NT, NPF - 1);
+    if (!tok && i < O_U) i = O_U + i % NU;
+    const char* a;
+    if (i < O_Q) a = kb + (int64_t)min(i / KP, rmax) * H * DK * sizeof(E) + (i % KP) * 64;
+    else if (i < O_DO) a = qb + (int64_t)min((i - O_Q) / KP, rmax) * H * DK * sizeof(E) + ((i - O_Q) % KP) * 64;
+    else if (i < O_U) a = db + (int64_t)min((i - O_DO) / VP, rmax) * H * DV * sizeof(E) + ((i - O_DO) % VP) * 64;
+    else if (i < O_T) a = ub + (i - O_U) * 64;
+    else if (i < O_R) a = tb + (i - O_T) * 64;
+    else a = rb + min((i - O_R) * 64, RECF * 4 - 4);
+    acc ^= *reinterpret_cast<const uint32_t*>(a);
+  }
+  return acc;
+}
+
 // One chunk per workgroup of 8 waves.  Wave w works on column group cw = w % 4
 // (key columns [cw Dk/4, (cw+1) Dk/4), value columns [cw Dv/4, ...)) and row
 // half rh = w / 4 (row tiles 2 rh, 2 rh + 1) of every per-row product, so two
@@ -1069,6 +1115,8 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   __syncthreads();
   clk.mark(5);
 
+  uint32_t pf;  // the prefetch below, folded; consumed after the last barrier
+
   // ---- P10: Z = GT T^T (own row tiles, column tile cw) -> slot P as Z^T (last
   //           read in P5), GA = strict_lower(-T^T Z) (own rows); E -> slot dU
   //           as E^T (dU^T is last read before the barrier in the middle).  XU = T^T dU (own rows and value columns) -> dV into
@@ -1117,6 +1165,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     }
     __syncthreads();
     clk.mark(6);
+    pf = l2_prefetch_next<E, DK, DV>(p, tid);
     PFrag<E> zf[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) zf[kb] = ZT.row(16 * cw + c16, 32 * kb);
@@ -1206,6 +1255,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   __syncthreads();
   clk.mark(8);
+  asm volatile("" ::"v"(pf));  // the prefetch's loads end here (no store is in flight yet)
   store_tile<E, DV, NT>(slotE(SQ), LV, static_cast<E*>(p.dv) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
   if (PREP && p.prep.qk_norm) {
     // gradients with respect to the raw q and k (the kernel saw them normalised)

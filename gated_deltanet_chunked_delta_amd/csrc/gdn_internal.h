@@ -121,6 +121,7 @@ struct GradParams {
   SeqInfo seq;
   const int2* chunk_tab;   // [total chunks] (sequence, chunk index within it)
   PrepParams prep;
+  int nwg;                 // compute units (workgroups resident at once: one per compute unit)
 };
 
 // One recurrent decode step: N sequences x H heads, one token each.
