@@ -256,16 +256,62 @@ struct Chunk {
     st_tile_cm<E>(sp->P, LT, 16 * ct, 16 * rt, acc);
   }
 
+  // A chunk's stores that wait for the next chunk: its U (the replay, from
+  // registers) and its output tile (the forward proper, from LDS, where the
+  // next chunk writes O only in its state-chain phase).  Loads and stores share
+  // one counter, and once both are in flight the compiler's wait for a load
+  // waits for every store as well; the next chunk's tiles are waited for at its
+  // very start, so stores issued at the end of a chunk would be waited for
+  // there in full.  Held back to just after the next chunk's T lands (its
+  // last load wait before the state chain), they complete during the chain.
+  struct Held {
+    f32x4 u[4][NTW];
+    E* us = nullptr;   // where the held U goes (none held: nullptr)
+    E* ulo = nullptr;  // and its rounding residual (bf16)
+    int64_t otok0 = 0;
+    int orows = 0;     // rows of the held output tile (none held: 0)
+  };
+  __device__ static void flush(S* sp, const FwdParams& p, Held& hd, int h) {
+    constexpr bool ULO = USAVE && std::is_same<E, bf16>::value;
+    const int tid = threadIdx.x, n0 = wave_id() * (DV / NW);
+    if constexpr (USAVE && !OUT) {
+      // U as DV/16 column blocks of [CH][16], each contiguous (a wave's stores
+      // fill whole lines; rows past the end are zero: beta = 0 there)
+      if (hd.us) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) {
+            st_tile_rows<E>(hd.us + (n0 + 16 * nt) * CH, 16, 16 * rt, 0, hd.u[rt][nt]);
+            if constexpr (ULO) st_tile_rows<E>(hd.ulo + (n0 + 16 * nt) * CH, 16, 16 * rt, 0, bf16_residual(hd.u[rt][nt]));
+          }
+        hd.us = nullptr;
+      }
+    }
+    if constexpr (OUT) {
+      // the output tile, coalesced
+      constexpr int OVEC = 16 / (int)sizeof(E), LO = S::LO;
+      typedef E ovec_t __attribute__((__vector_size__(16)));
+      for (int e = tid; e < hd.orows * (DV / OVEC); e += NT) {
+        const int r = e / (DV / OVEC), c0 = (e % (DV / OVEC)) * OVEC;
+        *reinterpret_cast<ovec_t*>(static_cast<E*>(p.o) + ((hd.otok0 + r) * p.H + h) * DV + c0) =
+            *reinterpret_cast<const ovec_t*>(&sp->O[r * LO + c0]);
+      }
+      hd.orows = 0;
+    }
+  }
+
   // Process the chunk whose tiles `ld` holds; prefetch the next chunk (if any)
   // into `ld`.  hacc: this wave's state columns (chunk start on entry, chunk end
   // on exit).  LEAD: a lead-in chunk before the segment proper, which only
   // advances the state (nothing is written).
   // t_in: this chunk's T; nrec: the next chunk's scalar record.
-  // us_chunk: where this chunk's U = Ut - W h goes (nullable).
+  // us_chunk: where this chunk's U = Ut - W h goes (nullable).  hd: the
+  // previous chunk's held stores (issued here), then this chunk's.
   template <bool LEAD>
   __device__ static void step(S& s0, const FwdParams& p, Loader& ld, int64_t tok0, int rows, int64_t ntok0,
                               int nrows, int h, E* hs_chunk, const float* t_in, const float* nrec, E* us_chunk,
-                              E* ulo_chunk, f32x4 (&hacc)[DK / 16][NTW], FwdClock& clk) {
+                              E* ulo_chunk, f32x4 (&hacc)[DK / 16][NTW], Held& hd, FwdClock& clk) {
     constexpr bool OUTC = OUT && !LEAD, USAVEC = USAVE && !LEAD;
     constexpr int LQ = S::LQ, LT = S::LT, LO = S::LO;
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
@@ -282,13 +328,6 @@ struct Chunk {
     if (PREP && p.prep.qk_norm) ld.normalize();
     ld.store(*sp);
     ld.store_rec(*sp);
-    // chunk-start state out, as h (Dk x Dv) in 4 x 16 blocks
-    if (!LEAD && hs_chunk) {
-#pragma unroll
-      for (int t = 0; t < DK / 16; ++t)
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) st_blk_row4<E>(hs_chunk, 16 * t + 4 * g, n0 + 16 * nt, DV, hacc[t][nt]);
-    }
     __syncthreads();
     clk.mark(1);
     sp = lds_opaque(sp);
@@ -316,6 +355,17 @@ struct Chunk {
         st4f<E>(&sp->TBG[r * LT + c], tv * bg4);
         st4f<E>(&sp->TB[r * LT + c], tv * bt4);
       }
+    if constexpr (!LEAD) {
+      // the stores held back from the previous chunk, and the chunk-start
+      // state, as h (Dk x Dv) in 4 x 16 blocks
+      flush(sp, p, hd, h);
+      if (hs_chunk) {
+#pragma unroll
+        for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) st_blk_row4<E>(hs_chunk, 16 * t + 4 * g, n0 + 16 * nt, DV, hacc[t][nt]);
+      }
+    }
     __syncthreads();
     clk.mark(2);
     sp = lds_opaque(sp);
@@ -388,20 +438,18 @@ struct Chunk {
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) mma(u[rt][nt], xw[kb], hf[nt][kb]);
     }
-    // U out as DV/16 column blocks of [CH][16], each contiguous (a wave's
-    // stores fill whole lines; rows past the end are zero: beta = 0 there);
-    // the forward proper writes the rounded operand fragments it forms anyway
-    // (bf16: and the residual of that rounding, for the backward's decay
-    // gradient, whose row terms u_r . (dS' k_r) can cancel far below their parts)
+    // U out (held for the next chunk; flush); the forward proper writes the
+    // rounded operand fragments it forms anyway (bf16: and the residual of
+    // that rounding, for the backward's decay gradient, whose row terms
+    // u_r . (dS' k_r) can cancel far below their parts)
     constexpr bool ULO = USAVE && std::is_same<E, bf16>::value;
     if (USAVEC && !OUT) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          st_tile_rows<E>(us_chunk + (n0 + 16 * nt) * CH, 16, 16 * rt, 0, u[rt][nt]);
-          if constexpr (ULO) st_tile_rows<E>(ulo_chunk + (n0 + 16 * nt) * CH, 16, 16 * rt, 0, bf16_residual(u[rt][nt]));
-        }
+        for (int nt = 0; nt < NTW; ++nt) hd.u[rt][nt] = u[rt][nt];
+      hd.us = us_chunk;
+      hd.ulo = ulo_chunk;
     }
     if (OUTC) {
 #pragma unroll
@@ -460,16 +508,10 @@ struct Chunk {
     clk.mark(4);
     sp = lds_opaque(sp);
 
-    // ---- 6. output tile out (coalesced); the next chunk's staging does not touch sp->O
+    // ---- 6. the output tile stays in LDS until the next chunk (flush)
     if constexpr (OUTC) {
-      constexpr int OVEC = 16 / (int)sizeof(E);
-      typedef E ovec_t __attribute__((__vector_size__(16)));
-      for (int e = tid; e < CH * (DV / OVEC); e += NT) {
-        const int r = e / (DV / OVEC), c0 = (e % (DV / OVEC)) * OVEC;
-        if (r < rows)
-          *reinterpret_cast<ovec_t*>(static_cast<E*>(p.o) + ((tok0 + r) * H + h) * DV + c0) =
-              *reinterpret_cast<const ovec_t*>(&sp->O[r * LO + c0]);
-      }
+      hd.otok0 = tok0;
+      hd.orows = rows;
     }
     clk.mark(5);
   }
@@ -487,6 +529,7 @@ struct Chunk {
                              int ce, int h, f32x4 (&hacc)[DK / 16][NTW], Loader& ld, FwdClock& clk) {
     const size_t SS = (size_t)DK * DV;
     E* hs = static_cast<E*>(p.hs);
+    Held hd;
     // the lead-in and the segment proper as two loops, each with its own
     // register allocation
     auto chunk = [&](auto lead, int c) {
@@ -497,17 +540,18 @@ struct Chunk {
       const float* tin = p.t_in + ((chunk0 + c) * p.H + h) * (size_t)(CH * CH);
       const float* nrec = more ? p.rec + ((chunk0 + c + 1) * p.H + h) * RECF : nullptr;
       if constexpr (decltype(lead)::value) {
-        step<true>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, nullptr, tin, nrec, nullptr, nullptr, hacc, clk);
+        step<true>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, nullptr, tin, nrec, nullptr, nullptr, hacc, hd, clk);
       } else {
         E* hsc = hs ? hs + ((chunk0 + c) * p.H + h) * SS : nullptr;
         const size_t uoff = ((chunk0 + c) * p.H + h) * (size_t)(CH * DV);
         E* usc = USAVE ? static_cast<E*>(p.us) + uoff : nullptr;
         E* ulc = USAVE && p.ulo ? static_cast<E*>(p.ulo) + uoff : nullptr;
-        step<false>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, nrec, usc, ulc, hacc, clk);
+        step<false>(s, p, ld, tok0, rows, tok0 + CH, nrows, h, hsc, tin, nrec, usc, ulc, hacc, hd, clk);
       }
     };
     for (int c = wb; c < cb; ++c) chunk(std::true_type{}, c);
     for (int c = cb; c < ce; ++c) chunk(std::false_type{}, c);
+    flush(lds_opaque(&s), p, hd, h);  // the last chunk's (after its final barrier)
     clk.set(7, ce - wb);
   }
 };
