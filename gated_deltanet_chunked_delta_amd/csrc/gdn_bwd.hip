@@ -1255,7 +1255,13 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   }
   __syncthreads();
   clk.mark(8);
-  asm volatile("" ::"v"(pf));  // the prefetch's loads end here (no store is in flight yet)
+  // The prefetch's loads and the row terms e end here, before the first
+  // store: a wait for a load issued before a store waits for that store too,
+  // and wave 0's sums below would otherwise wait for the tiles' stores.
+  float esum = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < RevWaves<DV>::NW; ++ww) esum += epv[ww];
+  asm volatile("" ::"v"(pf), "v"(esum));
   store_tile<E, DV, NT>(slotE(SQ), LV, static_cast<E*>(p.dv) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
   if (PREP && p.prep.qk_norm) {
     // gradients with respect to the raw q and k (the kernel saw them normalised)
@@ -1281,9 +1287,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
       for (int ww = 0; ww < 8; ++ww) extra += s.tail[1] * s.ph[ww];
       dgm += extra;
     }
-    float e = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < RevWaves<DV>::NW; ++ww) e += epv[ww];
+    const float e = esum;
     // dg_r = sum_{r' >= r} dgam_r' (suffix scan = prefix scan over reversed
     // lanes) + sum_{i < r} e_i (exclusive prefix scan)
     const float rev = __shfl(dgm, CH - 1 - r, 64);
