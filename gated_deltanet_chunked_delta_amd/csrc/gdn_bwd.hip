@@ -625,16 +625,17 @@ template <int NT> struct TStage<bf16, NT> {
 // this workgroup's linear index, nwg the compute units; the last workgroups
 // take the last one): its scalar record, K, Q, dO (sequences of one length;
 // with cu_seqlens only the chunk-indexed inputs), U and T, one 4-byte load
-// per 64-byte piece, folded into the returned value.  The LDS holds one
+// per 128-byte L2 line (a miss fills the whole line: one load per 64 bytes
+// measured no faster), folded into the returned value.  The LDS holds one
 // workgroup per compute unit and workgroups are dealt to the XCDs round-robin,
 // so that workgroup runs on this XCD and starts about when this one ends:
 // its staging then reads from L2.
 template <class E, int DK, int DV>
 __device__ __forceinline__ uint32_t l2_prefetch_next(const GradParams& p, int tid) {
   constexpr int NT = 512;
-  constexpr int KP = DK * (int)sizeof(E) / 64, VP = DV * (int)sizeof(E) / 64;  // pieces per row
-  constexpr int NK = CH * KP, NDO = CH * VP, NU = CH * DV * (int)sizeof(E) / 64, NTP = CH * CH * 4 / 64,
-                NR = (RECF * 4 + 63) / 64;
+  constexpr int KP = DK * (int)sizeof(E) / 128, VP = DV * (int)sizeof(E) / 128;  // pieces per row
+  constexpr int NK = CH * KP, NDO = CH * VP, NU = CH * DV * (int)sizeof(E) / 128, NTP = CH * CH * 4 / 128,
+                NR = (RECF * 4 + 127) / 128;
   constexpr int O_Q = NK, O_DO = 2 * NK, O_U = O_DO + NDO, O_T = O_U + NU, O_R = O_T + NTP, NPF = O_R + NR;
   const int nlin = gridDim.x * gridDim.y;
   const int tgt = min((int)(blockIdx.x + blockIdx.y * gridDim.x) + p.nwg, nlin - 1);
@@ -656,12 +657,12 @@ __device__ __forceinline__ uint32_t l2_prefetch_next(const GradParams& p, int ti
     int i = min(tid + j * NT, NPF - 1);
     if (!tok && i < O_U) i = O_U + i % NU;
     const char* a;
-    if (i < O_Q) a = kb + (int64_t)min(i / KP, rmax) * H * DK * sizeof(E) + (i % KP) * 64;
-    else if (i < O_DO) a = qb + (int64_t)min((i - O_Q) / KP, rmax) * H * DK * sizeof(E) + ((i - O_Q) % KP) * 64;
-    else if (i < O_U) a = db + (int64_t)min((i - O_DO) / VP, rmax) * H * DV * sizeof(E) + ((i - O_DO) % VP) * 64;
-    else if (i < O_T) a = ub + (i - O_U) * 64;
-    else if (i < O_R) a = tb + (i - O_T) * 64;
-    else a = rb + min((i - O_R) * 64, RECF * 4 - 4);
+    if (i < O_Q) a = kb + (int64_t)min(i / KP, rmax) * H * DK * sizeof(E) + (i % KP) * 128;
+    else if (i < O_DO) a = qb + (int64_t)min((i - O_Q) / KP, rmax) * H * DK * sizeof(E) + ((i - O_Q) % KP) * 128;
+    else if (i < O_U) a = db + (int64_t)min((i - O_DO) / VP, rmax) * H * DV * sizeof(E) + ((i - O_DO) % VP) * 128;
+    else if (i < O_T) a = ub + (i - O_U) * 128;
+    else if (i < O_R) a = tb + (i - O_T) * 128;
+    else a = rb + min((i - O_R) * 128, RECF * 4 - 4);
     acc ^= *reinterpret_cast<const uint32_t*>(a);
   }
   return acc;
