@@ -53,15 +53,21 @@ def kernel_models(dk, dv, esz):
 
 
 def kernel_sources_sha256():
-    """Digest of the HIP sources (the key under which measured counters stay valid)."""
+    """Digest of the HIP sources (the key under which measured counters stay
+    valid): their code, with comments and blank space removed, so that a
+    comment edit keeps the counters; any change to the code drops them."""
     import glob
     import hashlib
+    import re
     h = hashlib.sha256()
     d = os.path.join(ROOT, "gated_deltanet_chunked_delta_amd", "csrc")
     for f in sorted(glob.glob(os.path.join(d, "*.hip")) + glob.glob(os.path.join(d, "*.h"))):
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)  # block comments
+        src = re.sub(r"//[^\n]*", " ", src)                # line comments
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 

@@ -1257,8 +1257,9 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
   __syncthreads();
   clk.mark(8);
   // The prefetch's loads and the row terms e end here, before the first
-  // store: a wait for a load issued before a store waits for that store too,
-  // and wave 0's sums below would otherwise wait for the tiles' stores.
+  // store: the compiler cannot count the stores of the tile loops below (their
+  // trip count depends on the rows), so a wait after them for a load issued
+  // before them waited for every one of them too (wave 0's sums did).
   float esum = 0.f;
 #pragma unroll
   for (int ww = 0; ww < RevWaves<DV>::NW; ++ww) esum += epv[ww];

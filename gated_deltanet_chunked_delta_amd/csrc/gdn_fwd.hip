@@ -258,12 +258,13 @@ struct Chunk {
 
   // A chunk's stores that wait for the next chunk: its U (the replay, from
   // registers) and its output tile (the forward proper, from LDS, where the
-  // next chunk writes O only in its state-chain phase).  Loads and stores share
-  // one counter, and once both are in flight the compiler's wait for a load
-  // waits for every store as well; the next chunk's tiles are waited for at its
-  // very start, so stores issued at the end of a chunk would be waited for
-  // there in full.  Held back to just after the next chunk's T lands (its
-  // last load wait before the state chain), they complete during the chain.
+  // next chunk writes O only in its state-chain phase).  Loads and stores
+  // retire through one counter, and at the next chunk's start the compiler's
+  // wait for the prefetched tiles also covered the stores issued after them
+  // (it cannot count the stores of a loop iteration exactly), so stores issued
+  // at the end of a chunk were waited for there in full.  Held back to just
+  // after the next chunk's T lands (its last load wait before the state
+  // chain), they complete during the chain.
   struct Held {
     f32x4 u[4][NTW];
     E* us = nullptr;   // where the held U goes (none held: nullptr)
