@@ -625,8 +625,8 @@ template <int NT> struct TStage<bf16, NT> {
 // this workgroup's linear index, nwg the compute units; the last workgroups
 // take the last one): its scalar record, K, Q, dO (sequences of one length;
 // with cu_seqlens only the chunk-indexed inputs), U and T, one 4-byte load
-// per 128-byte L2 line (a miss fills the whole line: one load per 64 bytes
-// measured no faster), folded into the returned value.  The LDS holds one
+// per 128-byte L2 line (one load per 64 bytes measured no faster), folded into
+// the returned value.  The LDS holds one
 // workgroup per compute unit and workgroups are dealt to the XCDs round-robin,
 // so that workgroup runs on this XCD and starts about when this one ends:
 // its staging then reads from L2.
