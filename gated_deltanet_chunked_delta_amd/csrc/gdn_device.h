@@ -260,6 +260,16 @@ template <>
 __device__ __forceinline__ f32x4 ld4f<float>(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
+// A store of data that the storing kernel never reads back (its output, or a
+// buffer that a later kernel reads from HBM anyway): non-temporal.  The chain
+// kernels' state stores and the T solve's store of T use it (the chains ran
+// shorter with it); the gradient kernel's stores of dq, dk, dv ran slower with
+// it and are plain stores.
+template <class V>
+__device__ __forceinline__ void st_out(V* p, const V& v) {
+  __builtin_nontemporal_store(v, p);
+}
+
 template <class E>
 __device__ __forceinline__ void st4f(E* p, const f32x4& v);
 template <>
@@ -628,19 +638,19 @@ template <> struct CPiece<float> {
 
 // Four fp32 values of a C-layout column piece -> E, quad-transposed into a row
 // piece and stored (4 consecutive columns of row `row`).
-template <class E>
-__device__ __forceinline__ void st4_transposed(E* p, const f32x4& v);
-template <>
-__device__ __forceinline__ void st4_transposed<bf16>(bf16* p, const f32x4& v) {
-  typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
-  u32x2 x = __builtin_bit_cast(u32x2, bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]});
-  uint32_t x0 = x[0], x1 = x[1];
-  quad_transpose16(x0, x1);
-  *reinterpret_cast<u32x2*>(p) = u32x2{x0, x1};
-}
-template <>
-__device__ __forceinline__ void st4_transposed<float>(float* p, const f32x4& v) {
-  *reinterpret_cast<f32x4*>(p) = quad_transpose(v);
+template <class E, bool NTS = false>
+__device__ __forceinline__ void st4_transposed(E* p, const f32x4& v) {
+  if constexpr (sizeof(E) == 2) {
+    typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+    u32x2 x = __builtin_bit_cast(u32x2, bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]});
+    uint32_t x0 = x[0], x1 = x[1];
+    quad_transpose16(x0, x1);
+    if constexpr (NTS) st_out(reinterpret_cast<u32x2*>(p), u32x2{x0, x1});
+    else *reinterpret_cast<u32x2*>(p) = u32x2{x0, x1};
+  } else {
+    if constexpr (NTS) st_out(reinterpret_cast<f32x4*>(p), quad_transpose(v));
+    else *reinterpret_cast<f32x4*>(p) = quad_transpose(v);
+  }
 }
 
 // Rows r0 .. r0 + 3 of column c0 + lane%16 (an accumulator tile's column
@@ -651,7 +661,7 @@ __device__ __forceinline__ void st4_transposed<float>(float* p, const f32x4& v) 
 template <class E>
 __device__ __forceinline__ void st_blk_row4(E* base, int r0, int c0, int ncol, const f32x4& x) {
   const int l = lane_id(), q = (l >> 2) & 3, b = l & 3;
-  st4_transposed<E>(base + st_blk(r0 + b, c0 + 4 * q, ncol), x);
+  st4_transposed<E, true>(base + st_blk(r0 + b, c0 + 4 * q, ncol), x);
 }
 
 // acc + sum over the eight k-slots of a[j] * b[j] (bf16 pairs on the dot

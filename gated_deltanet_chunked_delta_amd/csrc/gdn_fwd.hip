@@ -295,8 +295,8 @@ struct Chunk {
       typedef E ovec_t __attribute__((__vector_size__(16)));
       for (int e = tid; e < hd.orows * (DV / OVEC); e += NT) {
         const int r = e / (DV / OVEC), c0 = (e % (DV / OVEC)) * OVEC;
-        *reinterpret_cast<ovec_t*>(static_cast<E*>(p.o) + ((hd.otok0 + r) * p.H + h) * DV + c0) =
-            *reinterpret_cast<const ovec_t*>(&sp->O[r * LO + c0]);
+        st_out(reinterpret_cast<ovec_t*>(static_cast<E*>(p.o) + ((hd.otok0 + r) * p.H + h) * DV + c0),
+               *reinterpret_cast<const ovec_t*>(&sp->O[r * LO + c0]));
       }
       hd.orows = 0;
     }

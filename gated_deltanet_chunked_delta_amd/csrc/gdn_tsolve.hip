@@ -153,10 +153,10 @@ __global__ __launch_bounds__(192) void gdn_tsolve(TSolveParams p) {
         hi[i] = (bf16)x[i];
         lo[i] = (bf16)(x[i] - (float)hi[i]);
       }
-      *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(dst) + e) = hi;
-      *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(dst) + CH * CH + e) = lo;
+      st_out(reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(dst) + e), hi);
+      st_out(reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(dst) + CH * CH + e), lo);
     } else {
-      *reinterpret_cast<f32x4*>(dst + e) = x;
+      st_out(reinterpret_cast<f32x4*>(dst + e), x);
     }
   }
 }
