@@ -113,10 +113,13 @@ struct RevChunk {
                               const float* t) {
     const int H = p.H;
     const void* src = q_half() ? p.q : p.k;
-    ld.kq.load(static_cast<const E*>(src) + (tok0 * H + h) * DK, (int64_t)H * DK, rows, kq_tid());
-    ld.d.load(static_cast<const E*>(p.dout) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
+    // every load of the prefetch is non-temporal: the chain ran shorter so
+    // (the forward chain did not)
+    ld.kq.template load<false, true>(static_cast<const E*>(src) + (tok0 * H + h) * DK, (int64_t)H * DK, rows,
+                                     kq_tid());
+    ld.d.template load<false, true>(static_cast<const E*>(p.dout) + (tok0 * H + h) * DV, (int64_t)H * DV, rows);
     ld.rec.load(rec);
-    ld.t.load(t);
+    ld.t.template load<true>(t);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       ld.tbg[j] = *reinterpret_cast<const f32x4*>(rec + 4 * CH + (8 * threadIdx.x) % CH + 4 * j);
@@ -177,8 +180,8 @@ struct RevChunk {
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
-          uhp[rt][nt].load(us_chunk + (n0 + 16 * nt) * CH, 16 * rt);
-          if constexpr (LO) ulp[rt][nt].load(ulo_chunk + (n0 + 16 * nt) * CH, 16 * rt);
+          uhp[rt][nt].template load<true>(us_chunk + (n0 + 16 * nt) * CH, 16 * rt);
+          if constexpr (LO) ulp[rt][nt].template load<true>(ulo_chunk + (n0 + 16 * nt) * CH, 16 * rt);
         }
     }
 
@@ -324,7 +327,7 @@ struct RevChunk {
           er = er * e4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) er[i] = row16_sum(er[i]);
-          if (c16 == 0) *reinterpret_cast<f32x4*>(ep_chunk + w * CH + 16 * rt + 4 * g) = er;
+          if (c16 == 0) st_out(reinterpret_cast<f32x4*>(ep_chunk + w * CH + 16 * rt + 4 * g), er);
         }
       }
       const float gc = s.tail[1];
@@ -752,7 +755,7 @@ __global__ __launch_bounds__(512) void gdn_grad_kernel(GradParams p) {
     const E* u = static_cast<const E*>(p.us) + ((size_t)blockIdx.x * H + h) * (CH * DV);
     const E* d = static_cast<const E*>(p.dout) + (tok0 * H + h) * DV;
     TilePart<E, NT / 2, DK> tkq;
-    tkq.template load<false>(rh == 0 ? k : q, (int64_t)H * DK, rows, ht);
+    tkq.template load<false, true>(rh == 0 ? k : q, (int64_t)H * DK, rows, ht);
 #pragma unroll
     for (int i = 0; i < UPC; ++i) {
       const int pc = ht + i * (NT / 2);

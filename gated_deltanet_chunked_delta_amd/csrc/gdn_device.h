@@ -573,27 +573,33 @@ __device__ __forceinline__ Frag<float> ld_fragC_q8_st<float>(const float* base, 
 // The inverse of ld_fragC_q: a fragment whose k-slots walk down column
 // col0 + lane%16 (rows k0+4g.., k0+16+4g..) stored into a row-major E matrix as
 // two quad-transposed 4-column row pieces.  All 64 lanes must take part.
-template <class E>
-__device__ __forceinline__ void st_fragC_q(E* base, int ld, int k0, int col0, const Frag<E>& f);
-template <>
-__device__ __forceinline__ void st_fragC_q<bf16>(bf16* base, int ld, int k0, int col0, const Frag<bf16>& f) {
+template <class E, bool NTS = false>
+__device__ __forceinline__ void st_fragC_q(E* base, int ld, int k0, int col0, const Frag<E>& f) {
   const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
-  typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
-  typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
-  const u32x4 v = __builtin_bit_cast(u32x4, f.v);
-  uint32_t x0 = v[0], x1 = v[1], y0 = v[2], y1 = v[3];
-  quad_transpose16(x0, x1);
-  quad_transpose16(y0, y1);
-  bf16* p = base + (k0 + 4 * g + b) * ld + col0 + 4 * q;
-  *reinterpret_cast<u32x2*>(p) = u32x2{x0, x1};
-  *reinterpret_cast<u32x2*>(p + 16 * ld) = u32x2{y0, y1};
-}
-template <>
-__device__ __forceinline__ void st_fragC_q<float>(float* base, int ld, int k0, int col0, const Frag<float>& f) {
-  const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
-  float* p = base + (k0 + 4 * g + b) * ld + col0 + 4 * q;
-  *reinterpret_cast<f32x4*>(p) = quad_transpose(f.lo);
-  *reinterpret_cast<f32x4*>(p + 16 * ld) = quad_transpose(f.hi);
+  E* p = base + (k0 + 4 * g + b) * ld + col0 + 4 * q;
+  if constexpr (sizeof(E) == 2) {
+    typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+    typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+    const u32x4 v = __builtin_bit_cast(u32x4, f.v);
+    uint32_t x0 = v[0], x1 = v[1], y0 = v[2], y1 = v[3];
+    quad_transpose16(x0, x1);
+    quad_transpose16(y0, y1);
+    if constexpr (NTS) {
+      st_out(reinterpret_cast<u32x2*>(p), u32x2{x0, x1});
+      st_out(reinterpret_cast<u32x2*>(p + 16 * ld), u32x2{y0, y1});
+    } else {
+      *reinterpret_cast<u32x2*>(p) = u32x2{x0, x1};
+      *reinterpret_cast<u32x2*>(p + 16 * ld) = u32x2{y0, y1};
+    }
+  } else {
+    if constexpr (NTS) {
+      st_out(reinterpret_cast<f32x4*>(p), quad_transpose(f.lo));
+      st_out(reinterpret_cast<f32x4*>(p + 16 * ld), quad_transpose(f.hi));
+    } else {
+      *reinterpret_cast<f32x4*>(p) = quad_transpose(f.lo);
+      *reinterpret_cast<f32x4*>(p + 16 * ld) = quad_transpose(f.hi);
+    }
+  }
 }
 
 // x - bf16(x), elementwise: what rounding x to bf16 drops (x = hi + residual,
@@ -612,10 +618,12 @@ __device__ __forceinline__ f32x4 bf16_residual(const f32x4& x) {
 template <class E> struct CPiece;
 template <> struct CPiece<bf16> {
   uint32_t x0, x1;
+  template <bool NTL = false>
   __device__ __forceinline__ void load(const bf16* blk, int r0) {
     const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
     typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
-    const u32x2 v = *reinterpret_cast<const u32x2*>(blk + (r0 + 4 * g + b) * 16 + 4 * q);
+    const u32x2* p = reinterpret_cast<const u32x2*>(blk + (r0 + 4 * g + b) * 16 + 4 * q);
+    const u32x2 v = NTL ? __builtin_nontemporal_load(p) : *p;
     x0 = v[0];
     x1 = v[1];
   }
@@ -629,9 +637,11 @@ template <> struct CPiece<bf16> {
 };
 template <> struct CPiece<float> {
   f32x4 v;
+  template <bool NTL = false>
   __device__ __forceinline__ void load(const float* blk, int r0) {
     const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
-    v = *reinterpret_cast<const f32x4*>(blk + (r0 + 4 * g + b) * 16 + 4 * q);
+    const f32x4* p = reinterpret_cast<const f32x4*>(blk + (r0 + 4 * g + b) * 16 + 4 * q);
+    v = NTL ? __builtin_nontemporal_load(p) : *p;
   }
   __device__ __forceinline__ f32x4 get() const { return quad_transpose(v); }
 };

@@ -145,12 +145,18 @@ struct TilePart {
   static constexpr int BPR = D > 0 ? D / VEC : 1;  // blocks per 4-row group
   typedef E vec_t __attribute__((__vector_size__(16)));
   vec_t blk[NB > 0 ? NB : 1][4];
+  template <bool NTL>
+  __device__ __forceinline__ static vec_t ld_vec(const char* p) {
+    if constexpr (NTL) return __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(p));
+    else return *reinterpret_cast<const vec_t*>(p);
+  }
 
   // ZFILL: rows at or past `rows` become zero instead of copies of the last row.
   // src is the same for every lane; each load is addressed as src + a 32-bit
   // byte offset (the host keeps 64 rows of a tile under 2 GiB), one address
   // register per load.
-  template <bool ZFILL = false>
+  // NTL: non-temporal loads.
+  template <bool ZFILL = false, bool NTL = false>
   __device__ __forceinline__ void load(const E* src, int64_t gld, int rows, int tid = threadIdx.x) {
     const char* base = reinterpret_cast<const char*>(src);
     const uint32_t ldb = (uint32_t)gld * (uint32_t)sizeof(E);
@@ -164,9 +170,9 @@ struct TilePart {
         for (int j = 0; j < 4; ++j) {
           if (ZFILL) {
             blk[b][j] = vec_t{};
-            if (r0 + j < rows) blk[b][j] = *reinterpret_cast<const vec_t*>(base + ((uint32_t)(r0 + j) * ldb + cb));
+            if (r0 + j < rows) blk[b][j] = ld_vec<NTL>(base + ((uint32_t)(r0 + j) * ldb + cb));
           } else {
-            blk[b][j] = *reinterpret_cast<const vec_t*>(base + ((uint32_t)min(r0 + j, rows - 1) * ldb + cb));
+            blk[b][j] = ld_vec<NTL>(base + ((uint32_t)min(r0 + j, rows - 1) * ldb + cb));
           }
         }
       }
@@ -294,10 +300,10 @@ __device__ __forceinline__ void store_tile(const E* src, int ld, E* dst, int64_t
 // Write a C-layout accumulator tile (lane: rows r0+4g..+3 of column c0+lane%16)
 // into a row-major E matrix, four consecutive columns per lane after a quad
 // transpose.
-template <class E>
+template <class E, bool NTS = false>
 __device__ __forceinline__ void st_tile_rows(E* base, int ld, int r0, int c0, const f32x4& acc) {
   const int l = lane_id(), g = l >> 4, q = (l >> 2) & 3, b = l & 3;
-  st4_transposed<E>(base + (r0 + 4 * g + b) * ld + c0 + 4 * q, acc);
+  st4_transposed<E, NTS>(base + (r0 + 4 * g + b) * ld + c0 + 4 * q, acc);
 }
 
 // Lead-ins of the segment runs.  The transition of the state (or of its
@@ -356,11 +362,15 @@ struct TPart<float, NT> {
   static constexpr int NP = CH * CH / (8 * NT);
   static_assert(NP * 8 * NT == CH * CH && (8 * NT) % CH == 0, "whole rows of T per pass");
   f32x4 v[NP][2];
+  template <bool NTL = false>
   __device__ __forceinline__ void load(const float* t, int tid = threadIdx.x) {
 #pragma unroll
     for (int i = 0; i < NP; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) v[i][j] = *reinterpret_cast<const f32x4*>(t + 8 * (tid + i * NT) + 4 * j);
+      for (int j = 0; j < 2; ++j) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(t + 8 * (tid + i * NT) + 4 * j);
+        v[i][j] = NTL ? __builtin_nontemporal_load(p) : *p;
+      }
   }
   __device__ __forceinline__ f32x4 get(int i, int j) const { return v[i][j]; }
 };
@@ -369,10 +379,14 @@ struct TPart<bf16, NT> {
   static constexpr int NP = CH * CH / (8 * NT);
   static_assert(NP * 8 * NT == CH * CH && (8 * NT) % CH == 0, "whole rows of T per pass");
   bf16x8 v[NP];
+  template <bool NTL = false>
   __device__ __forceinline__ void load(const float* t, int tid = threadIdx.x) {
     const bf16* hi = reinterpret_cast<const bf16*>(t);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) v[i] = *reinterpret_cast<const bf16x8*>(hi + 8 * (tid + i * NT));
+    for (int i = 0; i < NP; ++i) {
+      const bf16x8* p = reinterpret_cast<const bf16x8*>(hi + 8 * (tid + i * NT));
+      v[i] = NTL ? __builtin_nontemporal_load(p) : *p;
+    }
   }
   __device__ __forceinline__ f32x4 get(int i, int j) const {
     return f32x4{(float)v[i][4 * j], (float)v[i][4 * j + 1], (float)v[i][4 * j + 2], (float)v[i][4 * j + 3]};
