@@ -77,7 +77,9 @@ struct alignas(16) FwdSmem {
 // The raw tiles of one chunk, held in registers between the global load and
 // the LDS store so that the next chunk's loads overlap the current chunk's
 // compute.  K and V move as 4-row x 16-byte blocks, Q as single 16-byte
-// vectors, all stored row-major (K twice, at the two strides).
+// vectors, all stored row-major (K twice, at the two strides).  The loads, and
+// those of T, are non-temporal: the forward ran shorter so, the replay much
+// shorter.
 template <class E, int DK, int DV, int NT, bool NEED_Q, bool NEED_V, bool PREP>
 struct TileLoader {
   static constexpr int VEC = 16 / (int)sizeof(E);
@@ -109,7 +111,8 @@ struct TileLoader {
         const E* src = static_cast<const E*>(isk ? p.k : p.v) + (tok0 * H + h) * D + c0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (r0 + j < rows) blk[b][j] = *reinterpret_cast<const vec_t*>(src + (int64_t)(r0 + j) * H * D);
+          if (r0 + j < rows)
+            blk[b][j] = __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(src + (int64_t)(r0 + j) * H * D));
           else
             for (int e = 0; e < VEC; ++e) blk[b][j][e] = (E)0.f;
         }
@@ -125,7 +128,9 @@ struct TileLoader {
       const int id = threadIdx.x + v * NT;
       if (id < CH * (DK / VEC)) {
         const int r = id / (DK / VEC), c0 = (id % (DK / VEC)) * VEC;
-        if (r < rows) qv[v] = *reinterpret_cast<const vec_t*>(static_cast<const E*>(p.q) + ((tok0 + r) * H + h) * DK + c0);
+        if (r < rows)
+          qv[v] = __builtin_nontemporal_load(
+              reinterpret_cast<const vec_t*>(static_cast<const E*>(p.q) + ((tok0 + r) * H + h) * DK + c0));
         else
           for (int e = 0; e < VEC; ++e) qv[v][e] = (E)0.f;
       }
@@ -322,7 +327,7 @@ struct Chunk {
     // T (its bf16 value plane for bf16 inputs) is requested first and lands
     // in LDS at the end of phase 2
     TPart<E, NT> tp;
-    tp.load(t_in);
+    tp.template load<true>(t_in);
 
     // ---- 1. tiles into LDS, scalars, prefetch of the next chunk
     S* sp = lds_opaque(&s0);
