@@ -144,6 +144,33 @@ Plan make_plan(const gdn_common_args& a, bool bwd, int cus, bool saved = false, 
     const long long per = (work + cus - 1) / std::max(1, cus);
     p.segc = (int)std::max<long long>(8, per);
     p.segc = std::max(1, std::min(p.segc, std::max(1, maxc)));
+    // Sequences of several lengths round up to more workgroups than compute
+    // units, and the chains then run in two rounds.  Among longer segments,
+    // take the one that minimises rounds x chunks per segment (the chain
+    // time of the slowest compute unit), when there are only a few rounds.
+    const int ncu = std::max(1, cus);
+    auto rounds = [&](int sc) {
+      long long w = 0;
+      for (int n = 0; n < p.N; ++n) w += nch[n] == 0 ? 1 : (nch[n] + sc - 1) / sc;
+      return (w * a.H + ncu - 1) / ncu;
+    };
+    const long long r0 = rounds(p.segc);
+    if (r0 > 1 && r0 <= 8) {
+      long long best = r0 * p.segc;
+      int bestc = p.segc;
+      for (long long r = r0 - 1; r >= 1; --r) {
+        // the shortest segment length (up to the longest sequence) with at most r rounds
+        int lo = bestc, hi = std::max(1, maxc);
+        if (rounds(hi) > r) break;
+        while (lo < hi) {
+          const int mid = lo + (hi - lo) / 2;
+          if (rounds(mid) <= r) hi = mid;
+          else lo = mid + 1;
+        }
+        if (r * lo < best) { best = r * lo; bestc = lo; }
+      }
+      p.segc = bestc;
+    }
   }
   long long nseg = 0;
   for (int n = 0; n < p.N; ++n) nseg += nch[n] == 0 ? 1 : (nch[n] + p.segc - 1) / p.segc;
